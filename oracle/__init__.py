@@ -1,0 +1,131 @@
+"""CPU oracle for the speculative-sampling verify step (fp64, plain C).
+
+TEST INFRASTRUCTURE: only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The GPU library
+never calls it and shares no code with it.
+
+The arithmetic lives in ``sv_oracle.c`` (see its header for the page
+citations and the readings R1-R12 of the points the pages leave open); this
+module only loads the compiled library and marshals numpy arrays.
+
+Every function here is pinned by ``tests/test_oracle_*.py`` against closed
+forms, exact enumeration on tiny vocabularies, hand-worked fixtures under
+``tests/golden/`` and a Monte-Carlo chi-square test.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sv_oracle.c")
+_LIB = os.path.join(_HERE, "libsv_oracle.so")
+
+PARAMS_DTYPE = np.dtype(
+    [("temperature", "<f4"), ("top_k", "<i4"), ("top_p", "<f4"), ("reserved", "<i4")]
+)
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_LIB):
+        cmd = [
+            "gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+            "-shared", "-fPIC", "-o", _LIB + ".tmp", _SRC, "-lm",
+        ]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        lib.sv_oracle_verify.restype = ctypes.c_int
+        lib.sv_oracle_verify.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ]
+        lib.sv_oracle_dist.restype = ctypes.c_int
+        lib.sv_oracle_dist.argtypes = [
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_double,
+            ctypes.c_void_p, ctypes.c_void_p,
+        ]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def verify(target, draft, tokens, draft_len, params, uniforms, *, dtype="f32",
+           nthreads: int = 0):
+    """Run the oracle on host arrays.
+
+    target: [B, K+1, V] float32 (dtype="f32") or uint16 bf16 bit patterns
+    (dtype="bf16"); draft: [B, K, V] same dtype; tokens [B, K] int32;
+    draft_len [B] int32 or None; params [B] PARAMS_DTYPE; uniforms [B, K+1]
+    float32.  Returns (out_tokens [B, K+1], accept_len [B], diag [B, K+1, 4],
+    cut_margin [B], threads_used).
+    """
+    lib = _load()
+    code = {"f32": 0, "bf16": 1}[dtype]
+    target = np.ascontiguousarray(target)
+    B, K1, V = target.shape
+    K = K1 - 1
+    want = np.float32 if code == 0 else np.uint16
+    if target.dtype != want:
+        raise TypeError(f"target must be {want.__name__} for dtype={dtype}")
+    if K > 0:
+        draft = np.ascontiguousarray(draft)
+        if draft.shape != (B, K, V) or draft.dtype != want:
+            raise TypeError("draft must be [B, K, V] of the same dtype as target")
+    else:
+        draft = None
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32).reshape(B, max(K, 0))
+    if tokens.size == 0:
+        tokens = np.zeros((B, 1), np.int32)
+    if draft_len is not None:
+        draft_len = np.ascontiguousarray(draft_len, dtype=np.int32).reshape(B)
+    params = np.ascontiguousarray(params)
+    if params.dtype != PARAMS_DTYPE or params.shape != (B,):
+        raise TypeError("params must be [B] of PARAMS_DTYPE")
+    uniforms = np.ascontiguousarray(uniforms, dtype=np.float32).reshape(B, K + 1)
+    out_tok = np.empty((B, K + 1), np.int32)
+    acc = np.empty(B, np.int32)
+    diag = np.empty((B, K + 1, 4), np.float64)
+    cut = np.empty(B, np.float64)
+    used = lib.sv_oracle_verify(
+        _ptr(target), _ptr(draft), code, B, K, V, V, V, _ptr(tokens), _ptr(draft_len),
+        _ptr(params), _ptr(uniforms), _ptr(out_tok), _ptr(acc), _ptr(diag), _ptr(cut),
+        int(nthreads),
+    )
+    if used < 0:
+        raise ValueError("sv_oracle_verify rejected its arguments")
+    return out_tok, acc, diag, cut, used
+
+
+def dist(logits, temperature: float, top_k: int, top_p: float):
+    """Truncated tempered distribution of one fp64 logits row (T > 0).
+
+    Returns (prob [V] float64, cut_margin)."""
+    lib = _load()
+    x = np.ascontiguousarray(logits, dtype=np.float64).reshape(-1)
+    prob = np.empty_like(x)
+    cm = ctypes.c_double(0.0)
+    rc = lib.sv_oracle_dist(_ptr(x), x.size, float(temperature), int(top_k), float(top_p),
+                            _ptr(prob), ctypes.addressof(cm))
+    if rc != 0:
+        raise ValueError("distribution undefined (T <= 0 or no finite logit)")
+    return prob, cm.value
