@@ -1,0 +1,128 @@
+/*
+ * sv.h — C ABI of the speculative-sampling verify library (libsv.so, gfx950).
+ *
+ * The operation (web pages, cited by title and section):
+ *   - deniz.in, "Üç düzeltmeden sonra Qwen3.5 ve Qwen3.6 MTP head, Apple
+ *     Silicon'da 1.4 kata ulaştı", section "Örnekleme altında doğrulama
+ *     yanlıştı": a greedy row accepts a draft token iff it equals the target
+ *     argmax; a sampling row accepts draft token x with probability
+ *     min(1, p(x)/q(x)) and, on rejection, draws a replacement from the
+ *     clipped and rescaled difference (p - q)+.
+ *   - same page, section "Kesme her iki tarafta eşleşmek zorunda": target and
+ *     draft distributions get the same temperature / top_k / top_p treatment.
+ *   - "MTPLX：让模型用上自己的 MTP 头——Apple Silicon 上的原生投机解码",
+ *     section 3.3: the same accept / residual rule, which leaves the output
+ *     law equal to plain decoding from the target.
+ *   - tinycto.tv, "Spekülatif Kod Çözme (Speculative Decoding)…", section
+ *     "1. Temel Çalışma Mekanizması": drafts are tested in order and the first
+ *     rejection ends the row; section "Yaygın Yanılgılar": target and draft
+ *     share one vocabulary (one V here).
+ *   - "Apple Silikon İçin Cihaz Üstü Çıkarımı Optimize Etme", section
+ *     "Kelime parçacığı devrini GPU üzerinde tutun": the chosen token stays in
+ *     device memory for the next step; this library never copies results to
+ *     the host.
+ *
+ * Readings of points the pages leave open (the oracle uses the same ones):
+ *   temperature first, then top_k (ranking by logit descending, token id
+ *   ascending), renormalise, then the top_p walk over the renormalised top_k
+ *   keeping every token whose preceding mass is < top_p (top_p >= 1: no cut),
+ *   renormalise.  top_k <= 0 or >= V disables top_k.  T == 0 is a greedy row.
+ *   Accept iff u < a (strict).  The inverse CDF of the final draw walks token
+ *   ids in ascending order and returns the first id with u*W < running sum.
+ *   Residual mass W <= 0 falls back to p.  When all L drafts are accepted a
+ *   bonus token is drawn from the target row at position L.
+ */
+#ifndef SV_H
+#define SV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest top_k served by the in-register top-k path.  Rows with
+ * SV_MAX_TOP_K < top_k < V are reported as unsupported (accept length -2). */
+#define SV_MAX_TOP_K 64
+
+enum { SV_F32 = 0, SV_BF16 = 1 };
+
+enum {
+    SV_OK = 0,
+    SV_EINVAL = -1,     /* null required pointer, bad size, dtype or stride   */
+    SV_EWORKSPACE = -2, /* workspace missing or smaller than sv_workspace_bytes */
+    SV_EHIP = -3        /* a HIP launch failed; sv_strerror gives the reason   */
+};
+
+/* Per-row sampler parameters, 16 bytes, one per batch row (device memory).
+ * temperature: 0 = greedy, > 0 finite = sampling; anything else is a row
+ * error.  top_k: <= 0 or >= V disables.  top_p: > 0; >= 1 disables. */
+typedef struct {
+    float temperature;
+    int32_t top_k;
+    float top_p;
+    int32_t reserved;
+} sv_sampler_params;
+
+/* Host-side descriptor of shapes, layout, stream and scratch. */
+typedef struct {
+    int32_t batch;     /* B >= 1                                              */
+    int32_t max_draft; /* K >= 1 (drafted positions per row)                  */
+    int32_t vocab;     /* V >= 2, shared by target and draft                  */
+    int32_t dtype;     /* SV_F32 or SV_BF16, same for both logits tensors     */
+    int64_t target_row_stride; /* elements between consecutive (b, k) rows; 0 => V */
+    int64_t draft_row_stride;  /* same for the draft tensor; 0 => V             */
+    void* stream;              /* hipStream_t to enqueue on; NULL => default    */
+    void* workspace;           /* caller-owned device scratch                   */
+    size_t workspace_bytes;    /* >= sv_workspace_bytes(...)                    */
+    double* diag; /* optional device [B][K+1][4] fp64, NULL => not written.
+                     Slots 0..K-1: (p(x), q(x), a, |u - a|) of each evaluated
+                     accept test; slot K: (probability of the drawn token under
+                     the final distribution, lower CDF edge, upper CDF edge,
+                     margin of u to the nearer edge).  NaN where not evaluated
+                     and on greedy rows. */
+} sv_config;
+
+/* Bytes of device workspace sv_verify needs for this shape.  Pure function
+ * of its arguments; 0 on invalid arguments. */
+size_t sv_workspace_bytes(int32_t batch, int32_t max_draft, int32_t vocab, int32_t dtype);
+
+/*
+ * Enqueue one verify step on cfg->stream.  All pointers except cfg are
+ * device pointers owned by the caller; inputs must stay alive and unchanged
+ * until the stream work completes, outputs must not alias inputs.  The call
+ * never synchronises, never reads device memory on the host and keeps no
+ * pointer after it returns.  Calls that share a workspace must be ordered on
+ * one stream.
+ *
+ *   target_logits  [B][K+1] rows of V logits (row r at r*target_row_stride)
+ *   draft_logits   [B][K]   rows of V logits (row r at r*draft_row_stride)
+ *   draft_tokens   [B][K] int32; only the first draft_len[b] are read
+ *   draft_len      [B] int32 in [0, K], or NULL (= K for every row)
+ *   sampler_params [B] sv_sampler_params
+ *   uniforms       [B][K+1] fp32 in [0, 1): column k is the accept test of
+ *                  draft position k, column K the single final draw
+ *   out_tokens     [B][K+1] int32: accepted drafts, then the resampled /
+ *                  bonus / argmax token, then -1 padding
+ *   out_accept_len [B] int32: drafts accepted; -1 for a row with invalid
+ *                  data (bad params, draft_len, token id, or a distribution
+ *                  with no finite logit), -2 for a row this build does not
+ *                  serve (SV_MAX_TOP_K < top_k < V); such rows get tokens -1.
+ *
+ * Returns SV_OK once the work is enqueued, or a negative SV_E* code (nothing
+ * is enqueued then).  Identical inputs give bitwise-identical outputs.
+ */
+int sv_verify(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+              const int32_t* draft_len, const sv_sampler_params* sampler_params,
+              const float* uniforms, int32_t* out_tokens, int32_t* out_accept_len,
+              const sv_config* cfg);
+
+/* Static description of an error code (the last HIP error for SV_EHIP). */
+const char* sv_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SV_H */

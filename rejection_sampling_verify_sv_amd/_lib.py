@@ -1,0 +1,163 @@
+"""ctypes binding of libsv.so (the C ABI in include/sv.h).
+
+Argument marshalling only: every step of the verify computation runs in the
+HIP kernels of the library.  Torch supplies device memory and the stream.
+There is no fallback: if the library is missing or the tensors are not on a
+GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsv.so")
+
+SV_F32, SV_BF16 = 0, 1
+SV_MAX_TOP_K = 64
+ERRORS = {0: "SV_OK", -1: "SV_EINVAL", -2: "SV_EWORKSPACE", -3: "SV_EHIP"}
+EXPORTED = ("sv_verify", "sv_workspace_bytes", "sv_strerror")
+
+
+class SvConfig(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("max_draft", ctypes.c_int32),
+        ("vocab", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("target_row_stride", ctypes.c_int64),
+        ("draft_row_stride", ctypes.c_int64),
+        ("stream", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("diag", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libsv.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with __graft_entry__.build() (hipcc, gfx950)")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.sv_workspace_bytes.restype = ctypes.c_size_t
+        lib.sv_workspace_bytes.argtypes = [ctypes.c_int32] * 4
+        lib.sv_verify.restype = ctypes.c_int
+        lib.sv_verify.argtypes = [ctypes.c_void_p] * 8 + [ctypes.POINTER(SvConfig)]
+        lib.sv_strerror.restype = ctypes.c_char_p
+        lib.sv_strerror.argtypes = [ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def workspace_bytes(batch: int, max_draft: int, vocab: int, dtype: int) -> int:
+    return int(load().sv_workspace_bytes(batch, max_draft, vocab, dtype))
+
+
+def params_tensor(params, device) -> torch.Tensor:
+    """Sampler parameters as a [B, 4] int32 device tensor holding the 16-byte
+    {float temperature, int32 top_k, float top_p, int32 reserved} records.
+    Accepts a numpy structured array or an existing [B, 4] int32 tensor."""
+    if isinstance(params, torch.Tensor):
+        if params.dtype != torch.int32 or params.dim() != 2 or params.shape[1] != 4:
+            raise TypeError("params tensor must be [B, 4] int32")
+        return params.to(device).contiguous()
+    arr = np.ascontiguousarray(params)
+    if arr.dtype.itemsize != 16:
+        raise TypeError("params must be 16-byte records")
+    raw = arr.view(np.int32).reshape(-1, 4)
+    return torch.from_numpy(raw.copy()).to(device)
+
+
+def _rows_layout(t: torch.Tensor, nrows: int):
+    """(tensor, row_stride) such that row r = (b, k) starts at r * stride."""
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(0) != t.shape[1] * t.stride(1):
+        t = t.contiguous()
+    return t, t.stride(1)
+
+
+def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+           draft_len: torch.Tensor | None, params, uniforms: torch.Tensor, *,
+           diag: bool = False, workspace: torch.Tensor | None = None,
+           out_tokens: torch.Tensor | None = None, out_accept_len: torch.Tensor | None = None,
+           stream: torch.cuda.Stream | None = None):
+    """Enqueue one verify step; returns (out_tokens, out_accept_len, diag|None).
+
+    target [B, K+1, V], draft [B, K, V]: float32 or bfloat16 CUDA tensors.
+    draft_tokens [B, K] int32; draft_len [B] int32 or None; params as in
+    params_tensor(); uniforms [B, K+1] float32.  Nothing is synchronised.
+    """
+    lib = load()
+    if not target.is_cuda:
+        raise RuntimeError("verify needs GPU tensors (no CPU path exists)")
+    dev = target.device
+    if target.dtype == torch.float32:
+        code = SV_F32
+    elif target.dtype == torch.bfloat16:
+        code = SV_BF16
+    else:
+        raise TypeError("logits must be float32 or bfloat16")
+    if draft.dtype != target.dtype or draft.device != dev:
+        raise TypeError("draft must match target's dtype and device")
+    B, K1, V = target.shape
+    K = K1 - 1
+    if tuple(draft.shape) != (B, K, V):
+        raise ValueError(f"draft shape {tuple(draft.shape)} != {(B, K, V)}")
+    target, ts = _rows_layout(target, B * K1)
+    draft, ds = _rows_layout(draft, B * K)
+    tok = draft_tokens.to(dev, torch.int32).contiguous()
+    if tuple(tok.shape) != (B, K):
+        raise ValueError("draft_tokens must be [B, K]")
+    dl = None
+    if draft_len is not None:
+        dl = draft_len.to(dev, torch.int32).contiguous()
+        if tuple(dl.shape) != (B,):
+            raise ValueError("draft_len must be [B]")
+    prm = params_tensor(params, dev)
+    if prm.shape[0] != B:
+        raise ValueError("params must have B rows")
+    uni = uniforms.to(dev, torch.float32).contiguous()
+    if tuple(uni.shape) != (B, K1):
+        raise ValueError("uniforms must be [B, K+1]")
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K1), dtype=torch.int32, device=dev)
+    if out_accept_len is None:
+        out_accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    dg = torch.empty((B, K1, 4), dtype=torch.float64, device=dev) if diag else None
+    need = workspace_bytes(B, K, V, code)
+    if need == 0:
+        raise ValueError("invalid shape for sv_verify")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    wptr = workspace.data_ptr()
+    pad = (-wptr) % 256
+    cfg = SvConfig()
+    cfg.batch, cfg.max_draft, cfg.vocab, cfg.dtype = B, K, V, code
+    cfg.target_row_stride, cfg.draft_row_stride = ts, ds
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    cfg.stream = st.cuda_stream
+    cfg.workspace = wptr + pad
+    cfg.workspace_bytes = workspace.numel() * workspace.element_size() - pad
+    cfg.diag = dg.data_ptr() if dg is not None else None
+    rc = lib.sv_verify(target.data_ptr(), draft.data_ptr(), tok.data_ptr(),
+                       dl.data_ptr() if dl is not None else None, prm.data_ptr(),
+                       uni.data_ptr(), out_tokens.data_ptr(), out_accept_len.data_ptr(),
+                       ctypes.byref(cfg))
+    if rc != 0:
+        raise RuntimeError(f"sv_verify failed: {ERRORS.get(rc, rc)}: "
+                           f"{lib.sv_strerror(rc).decode()}")
+    if stream is not None:
+        # temporaries were allocated on the current stream; keep them alive
+        # until the work enqueued on `stream` has finished
+        for t in (target, draft, tok, dl, prm, uni, workspace, out_tokens, out_accept_len, dg):
+            if t is not None:
+                t.record_stream(st)
+    return out_tokens, out_accept_len, dg

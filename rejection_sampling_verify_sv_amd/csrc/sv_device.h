@@ -1,0 +1,235 @@
+// sv_device.h — device-side types and helpers shared by the verify kernels.
+//
+// Layout conventions (gfx950, wave64):
+//   * one workgroup = 256 threads = 4 waves;
+//   * a "tile" is what one workgroup reads in one step: every thread issues
+//     kLoads 16-byte loads, consecutive lanes read consecutive 16-byte vectors
+//     (fully coalesced), so a tile is 16 KiB of logits (4096 fp32 or 8192 bf16);
+//   * a "segment" is a run of whole tiles of one logits row handled by one
+//     workgroup; a row is split into nseg segments so that small batches still
+//     fill the 256 compute units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sv.h"
+
+namespace sv {
+
+constexpr int kThreads = 256;
+constexpr int kWave = 64;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kMaxTopK = SV_MAX_TOP_K;
+constexpr int kLoads = 4;    // 16-byte loads per thread per tile
+constexpr int kCandCap = 1024;  // candidate slots per merge round
+constexpr int kMergeBuf = 2048; // pow2 >= kCandCap + kMaxTopK
+
+enum RowClass : int32_t {
+    CLS_GREEDY = 0,
+    CLS_TOPK = 1,
+    CLS_FULL = 2,     // no top_k, no top_p cut: softmax over all V
+    CLS_NUCLEUS = 3,  // no top_k, top_p < 1 over all V
+    CLS_ERROR = -1,
+    CLS_UNSUP = -2,
+};
+
+enum RowStatus : int32_t { ST_LIVE = 0, ST_DONE = 1, ST_SAMPLE = 2, ST_ERROR = 3 };
+enum Need : int32_t { NEED_NONE = 0, NEED_RESID = 1, NEED_BONUS = 2 };
+
+// Per-row bookkeeping kept in the workspace (80 bytes).
+struct RowInfo {
+    int32_t cls, L, status, acc;
+    int32_t kpos, need, k_eff, flags;
+    float T, top_p;
+    int32_t pad0, pad1;
+    double mt, zt, md, zd;  // full-vocab stats (max, sum-exp) at position kpos
+};
+static_assert(sizeof(RowInfo) == 80, "RowInfo layout");
+
+// One segment's result for one (row, side): either a descending top-k key
+// list (zero-padded) or, for full-vocab rows, {max, sum-exp relative to max}.
+struct PartSlot {
+    uint64_t keys[kMaxTopK];
+};
+struct FullStat {
+    float m;
+    float pad;
+    double s;
+};
+
+template <int DT>
+struct Elt;
+template <>
+struct Elt<SV_F32> {
+    static constexpr int kVec = 4;
+    static constexpr int kSize = 4;
+};
+template <>
+struct Elt<SV_BF16> {
+    static constexpr int kVec = 8;
+    static constexpr int kSize = 2;
+};
+
+template <int DT>
+struct TileShape {
+    static constexpr int kVec = Elt<DT>::kVec;
+    static constexpr int kE = kLoads * kVec;      // elements per thread
+    static constexpr int kTile = kThreads * kE;   // elements per tile
+};
+
+// ---- ranking key ---------------------------------------------------------
+// key = (order-preserving image of the logit) << 32 | (0xFFFFFFFF - id):
+// a larger key is a higher logit, and among equal logits the lower id.
+// -0.0 is folded onto +0.0 so the two compare equal, as they do in fp64.
+// Key 0 is below every real token (the image of -inf is 0x007FFFFF).
+__device__ __forceinline__ uint32_t ord32(float f) {
+    uint32_t b = __float_as_uint(f);
+    b = (b == 0x80000000u) ? 0u : b;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t make_key(float f, uint32_t id) {
+    return ((uint64_t)ord32(f) << 32) | (uint64_t)(0xFFFFFFFFu - id);
+}
+__device__ __forceinline__ float key_logit(uint64_t k) {
+    uint32_t o = (uint32_t)(k >> 32);
+    uint32_t b = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+    return __uint_as_float(b);
+}
+__device__ __forceinline__ uint32_t key_id(uint64_t k) { return 0xFFFFFFFFu - (uint32_t)k; }
+
+// ---- loads ---------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int DT>
+__device__ __forceinline__ float load_one(const void* row, int64_t i) {
+    if constexpr (DT == SV_F32) {
+        return static_cast<const float*>(row)[i];
+    } else {
+        uint32_t h = static_cast<const uint16_t*>(row)[i];
+        return __uint_as_float(h << 16);
+    }
+}
+
+// Load one tile starting at element `start` into v[].  Element v[j*kVec+e]
+// has id start + (j*kThreads + tid)*kVec + e, so a thread's elements are in
+// ascending id order.  When `full` is false, elements at or past `end` read
+// as -inf and must be masked by the caller with elem_id() < end.
+template <int DT, bool kAligned>
+__device__ __forceinline__ void load_tile(const void* row, int64_t start, int64_t end, bool full,
+                                          float (&v)[TileShape<DT>::kE]) {
+    constexpr int kVec = Elt<DT>::kVec;
+    const int tid = threadIdx.x;
+    if (kAligned && full) {
+#pragma unroll
+        for (int j = 0; j < kLoads; j++) {
+            const int64_t off = start + (int64_t)(j * kThreads + tid) * kVec;
+            if constexpr (DT == SV_F32) {
+                const f32x4 q = __builtin_nontemporal_load(
+                    reinterpret_cast<const f32x4*>(static_cast<const float*>(row) + off));
+                v[j * 4 + 0] = q.x;
+                v[j * 4 + 1] = q.y;
+                v[j * 4 + 2] = q.z;
+                v[j * 4 + 3] = q.w;
+            } else {
+                const u32x4 q = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(row) + off));
+                v[j * 8 + 0] = bf16_lo(q.x);
+                v[j * 8 + 1] = bf16_hi(q.x);
+                v[j * 8 + 2] = bf16_lo(q.y);
+                v[j * 8 + 3] = bf16_hi(q.y);
+                v[j * 8 + 4] = bf16_lo(q.z);
+                v[j * 8 + 5] = bf16_hi(q.z);
+                v[j * 8 + 6] = bf16_lo(q.w);
+                v[j * 8 + 7] = bf16_hi(q.w);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kLoads; j++) {
+#pragma unroll
+            for (int e = 0; e < kVec; e++) {
+                const int64_t i = start + (int64_t)(j * kThreads + tid) * kVec + e;
+                v[j * kVec + e] = (i < end) ? load_one<DT>(row, i) : -INFINITY;
+            }
+        }
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ int64_t elem_id(int64_t start, int idx) {
+    constexpr int kVec = Elt<DT>::kVec;
+    const int j = idx / kVec, e = idx % kVec;
+    return start + (int64_t)(j * kThreads + (int)threadIdx.x) * kVec + e;
+}
+
+// ---- wave / block reductions -------------------------------------------
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        uint64_t w = __shfl_xor(v, o, kWave);
+        v = w > v ? w : v;
+    }
+    return v;
+}
+
+// Block-wide max of a u64; every thread gets the result.  `tmp` holds kWaves.
+__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* tmp) {
+    v = wave_max_u64(v);
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    __syncthreads();
+    if (lane == 0) tmp[w] = v;
+    __syncthreads();
+    uint64_t r = tmp[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; i++) r = tmp[i] > r ? tmp[i] : r;
+    return r;
+}
+
+// Bitonic sort (descending) of n = power of two u64 keys in LDS.
+__device__ inline void block_sort_desc(uint64_t* s, int n) {
+    for (int size = 2; size <= n; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = threadIdx.x; i < (n >> 1); i += kThreads) {
+                const int lo = 2 * i - (i & (stride - 1));
+                const int hi = lo + stride;
+                const bool desc = (lo & size) == 0;
+                const uint64_t a = s[lo], b = s[hi];
+                if ((a < b) == desc) {
+                    s[lo] = b;
+                    s[hi] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// Bitonic sort (descending) of one u64 per lane across a wave.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
+    const int lane = threadIdx.x % kWave;
+#pragma unroll
+    for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const uint64_t o = __shfl_xor(v, stride, kWave);
+            const bool dir = (lane & size) == 0;       // descending block
+            const bool lower = (lane & stride) == 0;   // lower index of the pair
+            const bool keep_max = (lower == dir);
+            v = keep_max ? (o > v ? o : v) : (o < v ? o : v);
+        }
+    }
+    return v;
+}
+
+__device__ __forceinline__ int pow2_ceil(int n) {
+    int p = 1;
+    while (p < n) p <<= 1;
+    return p;
+}
+
+}  // namespace sv

@@ -1,0 +1,258 @@
+// sv_sample.h — the final draw for full-vocab rows (inverse CDF over V).
+//
+// Rows that ended at position kpos with a rejection draw from the normalised
+// residual (p - q)+ (deniz.in "Üç düzeltmeden sonra…", section "Örnekleme
+// altında doğrulama yanlıştı"; "MTPLX…" section 3.3); rows whose drafts were
+// all accepted draw the bonus token from p at position L.  The walk is in
+// ascending token id (the reading used throughout this library).
+//
+// Two steps:
+//   sample_sums_kernel  one workgroup per (row, chunk of one tile): the chunk's
+//                       residual mass and p mass, fp64, fixed reduction tree;
+//   sample_pick_kernel  one workgroup per row: running sum over the chunk
+//                       masses, then a block-wide fp64 prefix scan inside the
+//                       chosen chunk to find the token.
+// Terms use the same exp2 formulation as the row pass that produced the
+// normalisers, so (p - q)+ is formed from consistent p and q.
+#pragma once
+
+#include "sv_decide.h"
+
+namespace sv {
+
+__device__ __forceinline__ float exp2_coef(float T) {
+    float c = (float)(1.4426950408889634 / (double)T);
+    return fminf(c, 3.0e38f);
+}
+
+template <int DT, bool kAligned>
+__global__ __launch_bounds__(kThreads) void sample_sums_kernel(StepArgs a) {
+    using TS = TileShape<DT>;
+    const int b = blockIdx.x / a.nch, ch = blockIdx.x % a.nch;
+    const RowInfo& ri = a.rows[b];
+    if (ri.status != ST_SAMPLE) return;
+    const int kpos = ri.kpos;
+    const bool resid = ri.need == NEED_RESID;
+    const float c = exp2_coef(ri.T);
+    const float mt = (float)ri.mt, md = (float)ri.md;
+    const double zt = ri.zt, zd = ri.zd;
+    const char* trow = static_cast<const char*>(a.target) +
+                       ((int64_t)b * (a.K + 1) + kpos) * a.t_stride * Elt<DT>::kSize;
+    const char* drow = static_cast<const char*>(a.draft) +
+                       ((int64_t)b * a.K + kpos) * a.d_stride * Elt<DT>::kSize;
+    const int64_t start = (int64_t)ch * TS::kTile;
+    const int64_t end = (start + TS::kTile < a.V) ? start + TS::kTile : a.V;
+    const bool full = start + TS::kTile <= a.V;
+    float vt[TS::kE], vd[TS::kE];
+    load_tile<DT, kAligned>(trow, start, end, full, vt);
+    if (resid) load_tile<DT, kAligned>(drow, start, end, full, vd);
+    double sr = 0.0, sp = 0.0;
+#pragma unroll
+    for (int i = 0; i < TS::kE; i++) {
+        if (elem_id<DT>(start, i) >= end) continue;
+        const float ep = exp2f((vt[i] - mt) * c);
+        sp += (double)ep;
+        if (resid) {
+            const float eq = exp2f((vd[i] - md) * c);
+            const double d = (double)ep / zt - (double)eq / zd;
+            sr += d > 0.0 ? d : 0.0;
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        sr += __shfl_xor(sr, o, kWave);
+        sp += __shfl_xor(sp, o, kWave);
+    }
+    __shared__ double red[2][kWaves];
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    if (lane == 0) {
+        red[0][w] = sr;
+        red[1][w] = sp;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double r0 = 0.0, r1 = 0.0;
+        for (int i = 0; i < kWaves; i++) {
+            r0 += red[0][i];
+            r1 += red[1][i];
+        }
+        double2 out;
+        out.x = r0;
+        out.y = r1;
+        a.chunks[(int64_t)b * a.nch + ch] = out;
+    }
+}
+
+// Block-wide exclusive prefix sum of one double per thread (fixed order).
+__device__ inline double block_exclusive_scan(double v, double* tmp /* kWaves */,
+                                              double* total) {
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    double incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
+    }
+    __syncthreads();
+    if (lane == kWave - 1) tmp[w] = incl;
+    __syncthreads();
+    double off = 0.0, tot = 0.0;
+    for (int i = 0; i < kWaves; i++) {
+        if (i < w) off += tmp[i];
+        tot += tmp[i];
+    }
+    *total = tot;
+    return off + incl - v;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void sample_pick_kernel(StepArgs a) {
+    using TS = TileShape<DT>;
+    constexpr int kE = TS::kE;
+    const int b = blockIdx.x;
+    const RowInfo ri = a.rows[b];
+    if (ri.status != ST_SAMPLE) return;
+    __shared__ int s_chunk, s_use_r, s_best, s_last;
+    __shared__ double s_base, s_W, s_target;
+    __shared__ double s_tmp[kWaves];
+    __shared__ double s_lo, s_hi, s_wy;
+    const bool resid = ri.need == NEED_RESID;
+    const double u = (double)a.uniforms[(int64_t)b * (a.K + 1) + a.K];
+    if (threadIdx.x == 0) {
+        const double2* cs = a.chunks + (int64_t)b * a.nch;
+        double Wr = 0.0, Wp = 0.0;
+        for (int c = 0; c < a.nch; c++) {
+            Wr += cs[c].x;
+            Wp += cs[c].y;
+        }
+        const int use_r = resid && Wr > 0.0;
+        const double W = use_r ? Wr : Wp;
+        const double target = u * W;
+        double S = 0.0, base = 0.0;
+        int chosen = -1, last = -1;
+        double last_base = 0.0;
+        for (int c = 0; c < a.nch; c++) {
+            const double wc = use_r ? cs[c].x : cs[c].y;
+            if (!(wc > 0.0)) continue;
+            const double before = S;
+            S += wc;
+            last = c;
+            last_base = before;
+            if (target < S) {
+                chosen = c;
+                base = before;
+                break;
+            }
+        }
+        if (chosen < 0) {
+            chosen = last;
+            base = last_base;
+        }
+        s_chunk = chosen;
+        s_use_r = use_r;
+        s_base = base;
+        s_W = W;
+        s_target = target;
+        s_best = 0x7FFFFFFF;
+        s_last = -1;
+        s_lo = s_hi = s_wy = 0.0;
+    }
+    __syncthreads();
+    if (s_chunk < 0) {  // no positive mass anywhere: only reachable on corrupt stats
+        if (threadIdx.x == 0) {
+            a.out_acc[b] = -1;
+            a.rows[b].status = ST_ERROR;
+        }
+        return;
+    }
+    const int kpos = ri.kpos;
+    const float c = exp2_coef(ri.T);
+    const float mt = (float)ri.mt, md = (float)ri.md;
+    const double zt = ri.zt, zd = ri.zd;
+    const bool use_r = s_use_r;
+    const char* trow = static_cast<const char*>(a.target) +
+                       ((int64_t)b * (a.K + 1) + kpos) * a.t_stride * Elt<DT>::kSize;
+    const char* drow = static_cast<const char*>(a.draft) +
+                       ((int64_t)b * a.K + kpos) * a.d_stride * Elt<DT>::kSize;
+    // thread t owns the contiguous run [start + t*kE, start + (t+1)*kE)
+    const int64_t cstart = (int64_t)s_chunk * TS::kTile;
+    const int64_t r0 = cstart + (int64_t)threadIdx.x * kE;
+    double w[kE];
+    double mine = 0.0;
+#pragma unroll
+    for (int i = 0; i < kE; i++) {
+        const int64_t id = r0 + i;
+        double wi = 0.0;
+        if (id < a.V && id < cstart + TS::kTile) {
+            const float ep = exp2f((load_one<DT>(trow, id) - mt) * c);
+            if (use_r) {
+                const float eq = exp2f((load_one<DT>(drow, id) - md) * c);
+                const double d = (double)ep / zt - (double)eq / zd;
+                wi = d > 0.0 ? d : 0.0;
+            } else {
+                wi = (double)ep;
+            }
+        }
+        w[i] = wi;
+        mine += wi;
+    }
+    double total;
+    const double off = block_exclusive_scan(mine, s_tmp, &total);
+    const double target = s_target;
+    double S = s_base + off;
+    int found = -1;
+    double f_before = 0.0, f_after = 0.0, f_w = 0.0;
+    int lastpos = -1;
+    double l_before = 0.0, l_after = 0.0, l_w = 0.0;
+#pragma unroll
+    for (int i = 0; i < kE; i++) {
+        if (!(w[i] > 0.0)) continue;
+        const double before = S;
+        S += w[i];
+        lastpos = i;
+        l_before = before;
+        l_after = S;
+        l_w = w[i];
+        if (found < 0 && target < S) {
+            found = i;
+            f_before = before;
+            f_after = S;
+            f_w = w[i];
+        }
+    }
+    if (found >= 0) atomicMin(&s_best, (int)(r0 + found));
+    // rounding can push the target past this chunk's own running sums; then
+    // the chunk's last positive-weight token is taken (margin reported as 0)
+    if (lastpos >= 0) atomicMax(&s_last, (int)(r0 + lastpos));
+    __syncthreads();
+    const bool fallback = s_best == 0x7FFFFFFF;
+    const int y = fallback ? s_last : s_best;
+    if (!fallback && found >= 0 && (int)(r0 + found) == y) {
+        s_lo = f_before;
+        s_hi = f_after;
+        s_wy = f_w;
+    } else if (fallback && lastpos >= 0 && (int)(r0 + lastpos) == y) {
+        s_lo = l_before;
+        s_hi = l_after;
+        s_wy = l_w;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const double W = s_W;
+        if (a.diag) {
+            double* dg = a.diag + (int64_t)b * 4 * (a.K + 1) + 4 * a.K;
+            const double lo = s_lo / W, hi = s_hi / W;
+            const double d1 = u - lo, d2 = hi - u;
+            dg[0] = s_wy / W;
+            dg[1] = lo;
+            dg[2] = hi;
+            dg[3] = fallback ? 0.0 : (d1 < d2 ? d1 : d2);
+        }
+        if (y < 0)
+            a.rows[b].status = ST_ERROR;  // no positive weight: cannot happen for a chosen chunk
+        else
+            emit_row(a, b, kpos, y);
+    }
+}
+
+}  // namespace sv

@@ -287,3 +287,22 @@ def custom(target_f32: np.ndarray, draft_f32: np.ndarray, tokens, draft_len, par
                     np.ascontiguousarray(tokens, dtype=np.int32).reshape(B, K1 - 1),
                     np.ascontiguousarray(draft_len, dtype=np.int32).reshape(B),
                     np.ascontiguousarray(params), np.ascontiguousarray(uniforms, np.float32))
+
+
+def to_torch(wl: Workload, device):
+    """Device tensors (target, draft, tokens, draft_len, params [B,4] int32,
+    uniforms) for a workload; bf16 bit patterns are reinterpreted, not
+    converted."""
+    import torch
+
+    if wl.dtype == "f32":
+        t = torch.from_numpy(np.ascontiguousarray(wl.target)).to(device)
+        d = torch.from_numpy(np.ascontiguousarray(wl.draft)).to(device)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(wl.target).view(np.int16)).to(device)
+        d = torch.from_numpy(np.ascontiguousarray(wl.draft).view(np.int16)).to(device)
+        t, d = t.view(torch.bfloat16), d.view(torch.bfloat16)
+    prm = torch.from_numpy(np.ascontiguousarray(wl.params).view(np.int32).reshape(-1, 4).copy())
+    return (t, d, torch.from_numpy(wl.tokens).to(device),
+            torch.from_numpy(wl.draft_len).to(device), prm.to(device),
+            torch.from_numpy(wl.uniforms).to(device))

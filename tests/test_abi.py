@@ -1,0 +1,62 @@
+"""The C ABI library loads and exports every function include/sv.h declares;
+host-side argument checks reject bad input without touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "sv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from rejection_sampling_verify_sv_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from rejection_sampling_verify_sv_amd import build
+        build.build()
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) >= {"sv_verify", "sv_workspace_bytes", "sv_strerror"}
+    for n in names:
+        assert hasattr(lib, n), f"libsv.so does not export {n}"
+
+
+def test_workspace_bytes_is_pure_and_validates(lib):
+    from rejection_sampling_verify_sv_amd import _lib
+    f = _lib.workspace_bytes
+    assert f(1024, 3, 151936, 0) > 0
+    assert f(1024, 3, 151936, 0) == f(1024, 3, 151936, 0)
+    for bad in [(0, 3, 100, 0), (4, 0, 100, 0), (4, 3, 1, 0), (4, 3, 100, 7)]:
+        assert f(*bad) == 0
+
+
+def test_verify_rejects_bad_arguments_on_host(lib):
+    from rejection_sampling_verify_sv_amd import _lib
+    cfg = _lib.SvConfig()
+    cfg.batch, cfg.max_draft, cfg.vocab, cfg.dtype = 2, 1, 100, 0
+    dummy = ctypes.c_void_p(0x1000)
+    args = [dummy] * 8
+    assert lib.sv_verify(*args, None) == -1           # no config
+    bad = list(args)
+    bad[0] = None
+    assert lib.sv_verify(*bad, ctypes.byref(cfg)) == -1  # null target
+    cfg.target_row_stride = 50                           # stride < V
+    assert lib.sv_verify(*args, ctypes.byref(cfg)) == -1
+    cfg.target_row_stride = 0
+    cfg.workspace = None                                 # no workspace
+    assert lib.sv_verify(*args, ctypes.byref(cfg)) == -2
+    cfg.workspace = 0x1000
+    cfg.workspace_bytes = 16
+    assert lib.sv_verify(*args, ctypes.byref(cfg)) == -2
+    assert b"workspace" in lib.sv_strerror(-2)
+    assert lib.sv_strerror(0) == b"ok"

@@ -1,0 +1,165 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every test builds seeded inputs with the shared input module, runs libsv.so on
+cuda:0 and the oracle on the host, and applies the bar of tests/parity.py:
+identical tokens and accept lengths except rows whose outcome was decided by a
+uniform within 1e-5 of a threshold (counted), diagnostics within 1e-5.
+Full-size recipes are checked on a seeded sample of rows that the oracle can
+compute one by one; smaller sizes are checked on every row.
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+from rejection_sampling_verify_sv_amd import workloads
+from rejection_sampling_verify_sv_amd.workloads import PARAMS_DTYPE
+from tests.parity import compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need cuda:0"
+    import rejection_sampling_verify_sv_amd as sv
+
+    sv.load()
+    return torch.device("cuda:0")
+
+
+def run_gpu(wl, dev, diag=True):
+    import torch
+
+    import rejection_sampling_verify_sv_amd as sv
+
+    tok, acc, dg = sv.verify(*workloads.to_torch(wl, dev), diag=diag)
+    torch.cuda.synchronize()
+    return (tok.cpu().numpy(), acc.cpu().numpy(),
+            dg.cpu().numpy() if dg is not None else None)
+
+
+def run_oracle(oracle_mod, wl, rows=None):
+    if rows is None:
+        return oracle_mod.verify(wl.target, wl.draft, wl.tokens, wl.draft_len, wl.params,
+                                 wl.uniforms, dtype=wl.dtype)
+    rows = np.asarray(rows)
+    return oracle_mod.verify(wl.target[rows], wl.draft[rows], wl.tokens[rows],
+                             wl.draft_len[rows], wl.params[rows], wl.uniforms[rows],
+                             dtype=wl.dtype)
+
+
+def check(oracle_mod, wl, dev, rows=None, label=""):
+    _say(f"[gpu] {label or wl.name}: B={wl.B} K={wl.K} V={wl.V} {wl.dtype}")
+    g_tok, g_acc, g_diag = run_gpu(wl, dev)
+    ref = run_oracle(oracle_mod, wl, rows)
+    rep = compare(g_tok, g_acc, g_diag, ref, rows)
+    _say(f"[gpu] {label or wl.name}: {rep.describe()}")
+    assert rep.ok, rep.describe()
+    return rep, g_tok, g_acc
+
+
+RECIPES = [
+    # name, batch, vocab, oracle sample size (None = every row)
+    ("tiny_v1000", 10000, None, None),
+    ("decode_b1", None, None, None),
+    ("mixed_greedy_b64", None, None, None),
+    ("fullvocab_ragged_b256", None, None, 40),
+    ("mixed_samplers_b1024", None, None, 48),
+]
+
+
+@pytest.mark.parametrize("name,batch,vocab,sample", RECIPES, ids=[r[0] for r in RECIPES])
+def test_recipe_parity(oracle_mod, dev, name, batch, vocab, sample):
+    wl = workloads.make(name, batch=batch, vocab=vocab, poison=(name == "fullvocab_ragged_b256"))
+    rows = None
+    if sample is not None:
+        rows = np.sort(np.random.default_rng(7).choice(wl.B, size=sample, replace=False))
+    rep, _, _ = check(oracle_mod, wl, dev, rows)
+    assert rep.compared > 0
+
+
+@pytest.mark.parametrize("name", ["mixed_greedy_b64", "fullvocab_ragged_b256",
+                                  "mixed_samplers_b1024"])
+def test_recipe_small_vocab_every_row(oracle_mod, dev, name):
+    # same recipes at a vocabulary the oracle finishes quickly on every row;
+    # 20011 is not a multiple of any tile, so the ragged tail is exercised
+    wl = workloads.make(name, batch=96, vocab=20011)
+    check(oracle_mod, wl, dev, label=f"{name}@V=20011")
+
+
+def _random_case(rng, B, K, V, dtype, T, top_k, top_p, scale=2.0, quant=None, draft_len=None):
+    t = rng.normal(0, scale, (B, K + 1, V))
+    d = t[:, :K] * 0.8 + rng.normal(0, scale * 0.6, (B, K, V))
+    if quant:
+        t, d = np.round(t * quant) / quant, np.round(d * quant) / quant
+    prm = np.zeros(B, PARAMS_DTYPE)
+    prm["temperature"], prm["top_k"], prm["top_p"] = T, top_k, top_p
+    L = np.full(B, K, np.int32) if draft_len is None else draft_len
+    tok = np.zeros((B, K), np.int32)
+    for b in range(B):
+        for k in range(K):
+            tok[b, k] = int(np.argmax(d[b, k] / max(T, 1e-3) + rng.gumbel(size=V)))
+    u = rng.random((B, K + 1), dtype=np.float32)
+    return workloads.custom(t, d, tok, L, prm, u, dtype=dtype)
+
+
+EDGE = [
+    # label, B, K, V, dtype, T, top_k, top_p, extra
+    ("tiny_vocab_topk", 64, 2, 7, "f32", 1.0, 3, 0.9, {}),
+    ("vocab_below_tile_bf16", 64, 3, 5000, "bf16", 0.8, 20, 0.95, {}),
+    ("ragged_tail_f32", 64, 2, 12345, "f32", 1.0, 50, 0.9, {}),
+    ("top_k_64", 48, 2, 30000, "f32", 1.0, 64, 1.0, {}),
+    ("top_k_1", 48, 2, 30000, "bf16", 0.7, 1, 0.5, {}),
+    ("heavy_ties_bf16", 48, 3, 40000, "bf16", 1.0, 20, 0.95, {"quant": 2}),
+    ("all_equal_logits", 16, 2, 9000, "f32", 1.0, 10, 1.0, {"scale": 0.0}),
+    ("full_vocab_untruncated_f32", 48, 3, 30011, "f32", 0.9, 0, 1.0, {}),
+    ("full_vocab_top_k_ge_V", 32, 2, 3000, "bf16", 1.1, 3000, 1.0, {}),
+    ("greedy_rows", 64, 4, 50000, "bf16", 0.0, 20, 0.95, {"quant": 4}),
+]
+
+
+@pytest.mark.parametrize("label,B,K,V,dtype,T,top_k,top_p,extra", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(oracle_mod, dev, label, B, K, V, dtype, T, top_k, top_p, extra):
+    rng = np.random.default_rng(zlib.crc32(label.encode()))
+    wl = _random_case(rng, B, K, V, dtype, T, top_k, top_p, **extra)
+    check(oracle_mod, wl, dev, label=label)
+
+
+def test_ragged_draft_len_and_zero(oracle_mod, dev):
+    rng = np.random.default_rng(5)
+    L = rng.integers(0, 4, 80).astype(np.int32)
+    wl = _random_case(rng, 80, 3, 20000, "bf16", 1.0, 20, 0.9, draft_len=L)
+    check(oracle_mod, wl, dev, label="ragged_draft_len")
+
+
+def test_invalid_rows(oracle_mod, dev):
+    rng = np.random.default_rng(6)
+    wl = _random_case(rng, 12, 2, 3000, "f32", 1.0, 20, 0.9)
+    wl.params["temperature"][1] = -1.0
+    wl.params["temperature"][2] = np.nan
+    wl.params["top_p"][3] = 0.0
+    wl.draft_len[4] = 3
+    wl.tokens[5, 1] = 3000
+    wl.tokens[6, 0] = -4
+    wl.draft_len[7] = -1
+    wl.target[8, :, :] = -np.inf
+    rep, g_tok, g_acc = check(oracle_mod, wl, dev, label="invalid_rows")
+    assert g_acc[1:9].tolist() == [-1] * 8
+    assert (g_tok[1:9] == -1).all()
+
+
+def test_deterministic(dev):
+    wl = workloads.make("mixed_samplers_b1024", batch=128, vocab=30011)
+    a = run_gpu(wl, dev)
+    b = run_gpu(wl, dev)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y, equal_nan=True)
