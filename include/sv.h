@@ -118,6 +118,27 @@ int sv_verify(const void* target_logits, const void* draft_logits, const int32_t
               const float* uniforms, int32_t* out_tokens, int32_t* out_accept_len,
               const sv_config* cfg);
 
+/*
+ * Same as sv_verify, and additionally records events[i] (hipEvent_t, created
+ * by the caller) on cfg->stream just before kernel launch i of the step and
+ * events[sv_launch_count(K)] after the last one, so the caller can time each
+ * kernel with hipEventElapsedTime.  n_events must be >= sv_launch_count(K)+1.
+ * For measuring kernels against the sustainable read rate of the part, the
+ * method of "Apple Silikon İçin Cihaz Üstü Çıkarımı Optimize Etme", section
+ * "Daha fazla optimizasyonun sınırları".
+ */
+int sv_verify_profiled(const void* target_logits, const void* draft_logits,
+                       const int32_t* draft_tokens, const int32_t* draft_len,
+                       const sv_sampler_params* sampler_params, const float* uniforms,
+                       int32_t* out_tokens, int32_t* out_accept_len, const sv_config* cfg,
+                       void* const* events, int32_t n_events);
+
+/* Number of kernel launches in one step for max_draft K (0 if K < 1), and
+ * the name of launch i ("plan", "rowpass", "decide", ...; NULL if out of
+ * range).  Static strings, host only. */
+int32_t sv_launch_count(int32_t max_draft);
+const char* sv_launch_name(int32_t max_draft, int32_t i);
+
 /* Static description of an error code (the last HIP error for SV_EHIP). */
 const char* sv_strerror(int code);
 

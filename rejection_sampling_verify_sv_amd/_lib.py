@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libsv.so")
 SV_F32, SV_BF16 = 0, 1
 SV_MAX_TOP_K = 64
 ERRORS = {0: "SV_OK", -1: "SV_EINVAL", -2: "SV_EWORKSPACE", -3: "SV_EHIP"}
-EXPORTED = ("sv_verify", "sv_workspace_bytes", "sv_strerror")
+EXPORTED = ("sv_verify", "sv_verify_profiled", "sv_workspace_bytes", "sv_strerror",
+            "sv_launch_count", "sv_launch_name")
 
 
 class SvConfig(ctypes.Structure):
@@ -52,14 +53,27 @@ def load() -> ctypes.CDLL:
         lib.sv_workspace_bytes.argtypes = [ctypes.c_int32] * 4
         lib.sv_verify.restype = ctypes.c_int
         lib.sv_verify.argtypes = [ctypes.c_void_p] * 8 + [ctypes.POINTER(SvConfig)]
+        lib.sv_verify_profiled.restype = ctypes.c_int
+        lib.sv_verify_profiled.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.POINTER(SvConfig)]
+                                           + [ctypes.c_void_p, ctypes.c_int32])
         lib.sv_strerror.restype = ctypes.c_char_p
         lib.sv_strerror.argtypes = [ctypes.c_int]
+        lib.sv_launch_count.restype = ctypes.c_int32
+        lib.sv_launch_count.argtypes = [ctypes.c_int32]
+        lib.sv_launch_name.restype = ctypes.c_char_p
+        lib.sv_launch_name.argtypes = [ctypes.c_int32, ctypes.c_int32]
         _lib = lib
     return _lib
 
 
 def workspace_bytes(batch: int, max_draft: int, vocab: int, dtype: int) -> int:
     return int(load().sv_workspace_bytes(batch, max_draft, vocab, dtype))
+
+
+def launch_names(max_draft: int) -> list:
+    lib = load()
+    return [lib.sv_launch_name(max_draft, i).decode()
+            for i in range(lib.sv_launch_count(max_draft))]
 
 
 def params_tensor(params, device) -> torch.Tensor:
@@ -88,7 +102,7 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
            draft_len: torch.Tensor | None, params, uniforms: torch.Tensor, *,
            diag: bool = False, workspace: torch.Tensor | None = None,
            out_tokens: torch.Tensor | None = None, out_accept_len: torch.Tensor | None = None,
-           stream: torch.cuda.Stream | None = None):
+           stream: torch.cuda.Stream | None = None, events=None):
     """Enqueue one verify step; returns (out_tokens, out_accept_len, diag|None).
 
     target [B, K+1, V], draft [B, K, V]: float32 or bfloat16 CUDA tensors.
@@ -147,10 +161,13 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
     cfg.workspace = wptr + pad
     cfg.workspace_bytes = workspace.numel() * workspace.element_size() - pad
     cfg.diag = dg.data_ptr() if dg is not None else None
-    rc = lib.sv_verify(target.data_ptr(), draft.data_ptr(), tok.data_ptr(),
-                       dl.data_ptr() if dl is not None else None, prm.data_ptr(),
-                       uni.data_ptr(), out_tokens.data_ptr(), out_accept_len.data_ptr(),
-                       ctypes.byref(cfg))
+    args = (target.data_ptr(), draft.data_ptr(), tok.data_ptr(),
+            dl.data_ptr() if dl is not None else None, prm.data_ptr(), uni.data_ptr(),
+            out_tokens.data_ptr(), out_accept_len.data_ptr(), ctypes.byref(cfg))
+    if events is None:
+        rc = lib.sv_verify(*args)
+    else:  # events: a ctypes array of hipEvent_t handles (see sv_verify_profiled)
+        rc = lib.sv_verify_profiled(*args, ctypes.cast(events, ctypes.c_void_p), len(events))
     if rc != 0:
         raise RuntimeError(f"sv_verify failed: {ERRORS.get(rc, rc)}: "
                            f"{lib.sv_strerror(rc).decode()}")

@@ -37,6 +37,8 @@ struct StepArgs {
     int32_t* out_tokens;
     int32_t* out_acc;
     double* diag;
+    FnUnit* fn_unit;    // [B*2] nucleus cut of the current position
+    const double* ebk;  // [kNB] e^(-b/32)
 };
 
 __device__ inline void diag_nan_row(double* diag, int b, int K) {
@@ -63,6 +65,17 @@ __device__ inline void fail_row(const StepArgs& a, int b) {
         int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
         for (int j = 0; j <= a.K; j++) o[j] = -1;
         a.out_acc[b] = -1;
+        a.rows[b].status = ST_ERROR;
+    }
+}
+
+// Row the build does not serve (boundary bucket over capacity): -2.
+__device__ inline void unsup_row(const StepArgs& a, int b) {
+    diag_nan_row(a.diag, b, a.K);
+    if (threadIdx.x == 0) {
+        int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
+        for (int j = 0; j <= a.K; j++) o[j] = -1;
+        a.out_acc[b] = -2;
         a.rows[b].status = ST_ERROR;
     }
 }
@@ -352,6 +365,79 @@ __device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri) 
     if (s_fail) fail_row(a, b);
 }
 
+// Nucleus rows: p(x) = [key(x) >= tau] w(x) / Z_S with the exact masses of
+// the cut computed by the nucleus kernels for this position.
+template <int DT>
+__device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& ri) {
+    __shared__ int s_fail;  // 0 ok, 1 invalid data, 2 not served
+    if (threadIdx.x == 0) {
+        s_fail = 0;
+        const double invT = 1.0 / (double)ri.T;
+        const FnUnit ut = a.fn_unit[b * 2];
+        RowInfo& w = a.rows[b];
+        if (ut.status != 0) {
+            s_fail = ut.status == 1 ? 2 : 1;
+        } else if (k == ri.L) {
+            w.need = NEED_BONUS;
+            w.kpos = k;
+            w.mt = (double)ut.m;
+            w.zt = ut.Zs;
+            w.tau_t = ut.tau;
+            w.status = ST_SAMPLE;
+        } else {
+            const FnUnit ud = a.fn_unit[b * 2 + 1];
+            if (ud.status != 0) {
+                s_fail = ud.status == 1 ? 2 : 1;
+            } else {
+                const int x = a.tokens[(int64_t)b * a.K + k];
+                const char* trow = static_cast<const char*>(a.target) +
+                                   ((int64_t)b * (a.K + 1) + k) * a.t_stride * Elt<DT>::kSize;
+                const char* drow = static_cast<const char*>(a.draft) +
+                                   ((int64_t)b * a.K + k) * a.d_stride * Elt<DT>::kSize;
+                const float lx = load_one<DT>(trow, x);
+                const float ld = load_one<DT>(drow, x);
+                const double px = (make_key(lx, (uint32_t)x) >= ut.tau)
+                                      ? fn_weight(lx, ut.m, invT, a.ebk) / ut.Zs : 0.0;
+                const double qx = (make_key(ld, (uint32_t)x) >= ud.tau)
+                                      ? fn_weight(ld, ud.m, invT, a.ebk) / ud.Zs : 0.0;
+                double acc;
+                if (qx > 0.0) {
+                    acc = px / qx;
+                    if (acc > 1.0) acc = 1.0;
+                } else {
+                    acc = (px > 0.0) ? 1.0 : 0.0;
+                }
+                const double uk = (double)a.uniforms[(int64_t)b * (a.K + 1) + k];
+                if (a.diag) {
+                    double* dg = a.diag + (int64_t)b * 4 * (a.K + 1);
+                    dg[4 * k + 0] = px;
+                    dg[4 * k + 1] = qx;
+                    dg[4 * k + 2] = acc;
+                    dg[4 * k + 3] = fabs(uk - acc);
+                }
+                if (uk < acc) {
+                    w.acc = k + 1;
+                } else {
+                    w.need = NEED_RESID;
+                    w.kpos = k;
+                    w.mt = (double)ut.m;
+                    w.zt = ut.Zs;
+                    w.tau_t = ut.tau;
+                    w.md = (double)ud.m;
+                    w.zd = ud.Zs;
+                    w.tau_d = ud.tau;
+                    w.status = ST_SAMPLE;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (s_fail == 1)
+        fail_row(a, b);
+    else if (s_fail == 2)
+        unsup_row(a, b);
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void decide_kernel(StepArgs a, int k) {
     const int b = blockIdx.x;
@@ -361,6 +447,8 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(StepArgs a, int k) {
         decide_greedy(a, b, k, ri);
     else if (ri.cls == CLS_TOPK)
         decide_topk(a, b, k, ri);
+    else if (ri.cls == CLS_NUCLEUS)
+        decide_nucleus<DT>(a, b, k, ri);
     else
         decide_full<DT>(a, b, k, ri);
 }
@@ -391,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(StepArgs a, int B, const
     else if (tk > 0 && tk < a.V)
         cls = (tk <= kMaxTopK) ? CLS_TOPK : CLS_UNSUP;
     else
-        cls = (tp < 1.f) ? CLS_UNSUP : CLS_FULL;
+        cls = (tp < 1.f) ? CLS_NUCLEUS : CLS_FULL;
     RowInfo ri;
     ri.cls = cls;
     ri.L = L;
@@ -405,6 +493,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(StepArgs a, int B, const
     ri.top_p = tp;
     ri.pad0 = ri.pad1 = 0;
     ri.mt = ri.zt = ri.md = ri.zd = 0.0;
+    ri.tau_t = ri.tau_d = 0ull;
     a.rows[b] = ri;
     int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
     for (int j = 0; j <= a.K; j++) o[j] = -1;

@@ -37,15 +37,16 @@ enum RowClass : int32_t {
 enum RowStatus : int32_t { ST_LIVE = 0, ST_DONE = 1, ST_SAMPLE = 2, ST_ERROR = 3 };
 enum Need : int32_t { NEED_NONE = 0, NEED_RESID = 1, NEED_BONUS = 2 };
 
-// Per-row bookkeeping kept in the workspace (80 bytes).
+// Per-row bookkeeping kept in the workspace (96 bytes).
 struct RowInfo {
     int32_t cls, L, status, acc;
     int32_t kpos, need, k_eff, flags;
     float T, top_p;
     int32_t pad0, pad1;
-    double mt, zt, md, zd;  // full-vocab stats (max, sum-exp) at position kpos
+    double mt, zt, md, zd;   // full-vocab stats (max, normaliser) at position kpos
+    uint64_t tau_t, tau_d;   // nucleus rows: key of the last kept token
 };
-static_assert(sizeof(RowInfo) == 80, "RowInfo layout");
+static_assert(sizeof(RowInfo) == 96, "RowInfo layout");
 
 // One segment's result for one (row, side): either a descending top-k key
 // list (zero-padded) or, for full-vocab rows, {max, sum-exp relative to max}.
@@ -57,6 +58,69 @@ struct FullStat {
     float pad;
     double s;
 };
+
+// ---- exact masses for the full-vocab nucleus cut ---------------------------
+constexpr int kNB = 2048;           // buckets of width 1/32 in z, z < 64
+constexpr int kCollectCap = 4096;   // boundary-bucket tokens resolved per unit
+
+// Per (row, side) state of the nucleus cut at the current position.
+struct FnUnit {
+    double Z;        // total mass (relative to the row max)
+    double Mabove;   // mass of the buckets before the boundary bucket
+    double Zs;       // kept mass
+    uint64_t tau;    // key of the last kept token
+    float m;         // row max
+    int32_t beta;    // boundary bucket
+    int32_t count;   // tokens in the boundary bucket (histogram)
+    int32_t ncoll;   // tokens appended by the collect pass
+    int32_t status;  // 0 ok, 1 boundary bucket too large to resolve
+    int32_t pad;
+};
+
+// e^(-d) for d in [0, 1/32): Taylor series to degree 8.
+__device__ __forceinline__ double exp_neg_small(double d) {
+    double p = 1.0 / 40320.0;
+    p = fma(p, -d, 1.0 / 5040.0);
+    p = fma(p, -d, 1.0 / 720.0);
+    p = fma(p, -d, 1.0 / 120.0);
+    p = fma(p, -d, 1.0 / 24.0);
+    p = fma(p, -d, 1.0 / 6.0);
+    p = fma(p, -d, 0.5);
+    p = fma(p, -d, 1.0);
+    p = fma(p, -d, 1.0);
+    return p;
+}
+
+// Bucket of a logit (kNB = tail) and its in-bucket offset; identical in every
+// pass so that the histogram, the collect pass and the resolve agree.
+__device__ __forceinline__ int fn_bucket(float l, float m, double invT, double* d) {
+    const double z = ((double)m - (double)l) * invT;
+    if (!(z < 64.0)) {
+        *d = 0.0;
+        return kNB;
+    }
+    const int b = (int)(z * 32.0);
+    *d = z - (double)b * (1.0 / 32.0);
+    return b;
+}
+
+// Exact-mass weight of a logit (0 for the dropped tail).
+__device__ __forceinline__ double fn_weight(float l, float m, double invT, const double* ebk) {
+    double d;
+    const int b = fn_bucket(l, m, invT, &d);
+    return b < kNB ? ebk[b] * exp_neg_small(d) : 0.0;
+}
+
+__device__ __forceinline__ void fixed80(double e, uint64_t* hi, uint64_t* lo) {
+    const double t = e * 1099511627776.0;  // 2^40
+    const double h = floor(t);
+    *hi = (uint64_t)h;
+    *lo = (uint64_t)((t - h) * 1099511627776.0);
+}
+
+__device__ __forceinline__ double unfixed80(uint64_t hi, uint64_t lo) {
+    return (double)hi * 9.094947017729282e-13 + (double)lo * 8.271806125530277e-25;
+}
 
 template <int DT>
 struct Elt;
@@ -188,6 +252,28 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* tmp) {
 #pragma unroll
     for (int i = 1; i < kWaves; i++) r = tmp[i] > r ? tmp[i] : r;
     return r;
+}
+
+// Block-wide exclusive prefix sum of one double per thread (fixed order).
+__device__ inline double block_exclusive_scan(double v, double* tmp /* kWaves */,
+                                              double* total) {
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    double incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
+    }
+    __syncthreads();
+    if (lane == kWave - 1) tmp[w] = incl;
+    __syncthreads();
+    double off = 0.0, tot = 0.0;
+    for (int i = 0; i < kWaves; i++) {
+        if (i < w) off += tmp[i];
+        tot += tmp[i];
+    }
+    *total = tot;
+    return off + incl - v;
 }
 
 // Bitonic sort (descending) of n = power of two u64 keys in LDS.

@@ -23,7 +23,8 @@ struct TopkSmem {
     uint64_t list[kMaxTopK];
     uint64_t buf[kMergeBuf];
     uint64_t red[kWaves];
-    uint64_t thr;
+    uint64_t thr;    // k-th key of the merged list (0 until it holds k keys)
+    uint64_t floor;  // lower bound from the segment's first tile
     int ncand;
     int nlist;
 };
@@ -64,6 +65,7 @@ __device__ void rowpass_topk(const void* row, int64_t start, int64_t end, int k_
         sm.ncand = 0;
         sm.nlist = 0;
         sm.thr = 0ull;
+        sm.floor = 0ull;
     }
     __syncthreads();
     float v[TS::kE];
@@ -76,9 +78,10 @@ __device__ void rowpass_topk(const void* row, int64_t start, int64_t end, int k_
         for (int i = 0; i < TS::kE; i++) vmax = fmaxf(vmax, v[i]);
         uint64_t own_thr;
         if (t0 == start) {
-            // Per-wave lower bound: the k-th largest of the lanes' best keys
-            // (k distinct elements of this wave reach it, so every element of
-            // the wave's top-k does too).
+            // Lower bound for the segment's k-th key: in each wave, the k-th
+            // largest of the lanes' best keys is reached by k distinct
+            // elements, so the segment's k-th key is at least the largest of
+            // these per-wave values.  Keys below it are never candidates.
             uint64_t best = 0ull;
 #pragma unroll
             for (int i = 0; i < TS::kE; i++) {
@@ -87,9 +90,16 @@ __device__ void rowpass_topk(const void* row, int64_t start, int64_t end, int k_
             }
             const uint64_t sorted = wave_sort_desc(best);
             const uint64_t theta = __shfl(sorted, k_eff - 1, kWave);
-            own_thr = theta > 0ull ? theta - 1ull : 0ull;
+            if (threadIdx.x % kWave == 0) sm.red[threadIdx.x / kWave] = theta;
+            __syncthreads();
+            uint64_t th = sm.red[0];
+#pragma unroll
+            for (int w = 1; w < kWaves; w++) th = sm.red[w] > th ? sm.red[w] : th;
+            own_thr = th > 0ull ? th - 1ull : 0ull;
+            __syncthreads();
+            if (threadIdx.x == 0) sm.floor = own_thr;
         } else {
-            own_thr = sm.thr;
+            own_thr = sm.thr > sm.floor ? sm.thr : sm.floor;
         }
         uint32_t pend = 0u;
         {

@@ -25,6 +25,57 @@ __device__ __forceinline__ float exp2_coef(float T) {
     return fminf(c, 3.0e38f);
 }
 
+// Draw weights of token `id` for a row that ended at kpos: the residual
+// (p - q)+ and the target weight (unnormalised exp2 terms on untruncated rows,
+// exact cut masses over Z_S on nucleus rows).
+struct DrawCtx {
+    bool nucleus, resid;
+    float mt, md, c;
+    double zt, zd, invT;
+    uint64_t tau_t, tau_d;
+};
+
+__device__ __forceinline__ DrawCtx draw_ctx(const RowInfo& ri) {
+    DrawCtx x;
+    x.nucleus = ri.cls == CLS_NUCLEUS;
+    x.resid = ri.need == NEED_RESID;
+    x.mt = (float)ri.mt;
+    x.md = (float)ri.md;
+    x.c = exp2_coef(ri.T);
+    x.zt = ri.zt;
+    x.zd = ri.zd;
+    x.invT = 1.0 / (double)ri.T;
+    x.tau_t = ri.tau_t;
+    x.tau_d = ri.tau_d;
+    return x;
+}
+
+__device__ __forceinline__ void draw_weights(const DrawCtx& x, float lt, float ld, uint32_t id,
+                                             const double* ebk, double* wr, double* wp) {
+    if (x.nucleus) {
+        const double p = (make_key(lt, id) >= x.tau_t) ? fn_weight(lt, x.mt, x.invT, ebk) / x.zt : 0.0;
+        *wp = p;
+        if (x.resid) {
+            const double q =
+                (make_key(ld, id) >= x.tau_d) ? fn_weight(ld, x.md, x.invT, ebk) / x.zd : 0.0;
+            const double d = p - q;
+            *wr = d > 0.0 ? d : 0.0;
+        } else {
+            *wr = 0.0;
+        }
+    } else {
+        const float ep = exp2f((lt - x.mt) * x.c);
+        *wp = (double)ep;
+        if (x.resid) {
+            const float eq = exp2f((ld - x.md) * x.c);
+            const double d = (double)ep / x.zt - (double)eq / x.zd;
+            *wr = d > 0.0 ? d : 0.0;
+        } else {
+            *wr = 0.0;
+        }
+    }
+}
+
 template <int DT, bool kAligned>
 __global__ __launch_bounds__(kThreads) void sample_sums_kernel(StepArgs a) {
     using TS = TileShape<DT>;
@@ -32,10 +83,7 @@ __global__ __launch_bounds__(kThreads) void sample_sums_kernel(StepArgs a) {
     const RowInfo& ri = a.rows[b];
     if (ri.status != ST_SAMPLE) return;
     const int kpos = ri.kpos;
-    const bool resid = ri.need == NEED_RESID;
-    const float c = exp2_coef(ri.T);
-    const float mt = (float)ri.mt, md = (float)ri.md;
-    const double zt = ri.zt, zd = ri.zd;
+    const DrawCtx x = draw_ctx(ri);
     const char* trow = static_cast<const char*>(a.target) +
                        ((int64_t)b * (a.K + 1) + kpos) * a.t_stride * Elt<DT>::kSize;
     const char* drow = static_cast<const char*>(a.draft) +
@@ -45,18 +93,16 @@ __global__ __launch_bounds__(kThreads) void sample_sums_kernel(StepArgs a) {
     const bool full = start + TS::kTile <= a.V;
     float vt[TS::kE], vd[TS::kE];
     load_tile<DT, kAligned>(trow, start, end, full, vt);
-    if (resid) load_tile<DT, kAligned>(drow, start, end, full, vd);
+    if (x.resid) load_tile<DT, kAligned>(drow, start, end, full, vd);
     double sr = 0.0, sp = 0.0;
 #pragma unroll
     for (int i = 0; i < TS::kE; i++) {
-        if (elem_id<DT>(start, i) >= end) continue;
-        const float ep = exp2f((vt[i] - mt) * c);
-        sp += (double)ep;
-        if (resid) {
-            const float eq = exp2f((vd[i] - md) * c);
-            const double d = (double)ep / zt - (double)eq / zd;
-            sr += d > 0.0 ? d : 0.0;
-        }
+        const int64_t id = elem_id<DT>(start, i);
+        if (id >= end) continue;
+        double wr, wp;
+        draw_weights(x, vt[i], x.resid ? vd[i] : 0.f, (uint32_t)id, a.ebk, &wr, &wp);
+        sr += wr;
+        sp += wp;
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -81,28 +127,6 @@ __global__ __launch_bounds__(kThreads) void sample_sums_kernel(StepArgs a) {
         out.y = r1;
         a.chunks[(int64_t)b * a.nch + ch] = out;
     }
-}
-
-// Block-wide exclusive prefix sum of one double per thread (fixed order).
-__device__ inline double block_exclusive_scan(double v, double* tmp /* kWaves */,
-                                              double* total) {
-    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-    double incl = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const double t = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += t;
-    }
-    __syncthreads();
-    if (lane == kWave - 1) tmp[w] = incl;
-    __syncthreads();
-    double off = 0.0, tot = 0.0;
-    for (int i = 0; i < kWaves; i++) {
-        if (i < w) off += tmp[i];
-        tot += tmp[i];
-    }
-    *total = tot;
-    return off + incl - v;
 }
 
 template <int DT>
@@ -166,9 +190,7 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(StepArgs a) {
         return;
     }
     const int kpos = ri.kpos;
-    const float c = exp2_coef(ri.T);
-    const float mt = (float)ri.mt, md = (float)ri.md;
-    const double zt = ri.zt, zd = ri.zd;
+    const DrawCtx x = draw_ctx(ri);
     const bool use_r = s_use_r;
     const char* trow = static_cast<const char*>(a.target) +
                        ((int64_t)b * (a.K + 1) + kpos) * a.t_stride * Elt<DT>::kSize;
@@ -184,14 +206,10 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(StepArgs a) {
         const int64_t id = r0 + i;
         double wi = 0.0;
         if (id < a.V && id < cstart + TS::kTile) {
-            const float ep = exp2f((load_one<DT>(trow, id) - mt) * c);
-            if (use_r) {
-                const float eq = exp2f((load_one<DT>(drow, id) - md) * c);
-                const double d = (double)ep / zt - (double)eq / zd;
-                wi = d > 0.0 ? d : 0.0;
-            } else {
-                wi = (double)ep;
-            }
+            double wr, wp;
+            draw_weights(x, load_one<DT>(trow, id), x.resid ? load_one<DT>(drow, id) : 0.f,
+                         (uint32_t)id, a.ebk, &wr, &wp);
+            wi = use_r ? wr : wp;
         }
         w[i] = wi;
         mine += wi;

@@ -85,6 +85,7 @@ def test_recipe_parity(oracle_mod, dev, name, batch, vocab, sample):
         rows = np.sort(np.random.default_rng(7).choice(wl.B, size=sample, replace=False))
     rep, _, _ = check(oracle_mod, wl, dev, rows)
     assert rep.compared > 0
+    assert rep.unsupported == 0
 
 
 @pytest.mark.parametrize("name", ["mixed_greedy_b64", "fullvocab_ragged_b256",
@@ -124,6 +125,12 @@ EDGE = [
     ("full_vocab_untruncated_f32", 48, 3, 30011, "f32", 0.9, 0, 1.0, {}),
     ("full_vocab_top_k_ge_V", 32, 2, 3000, "bf16", 1.1, 3000, 1.0, {}),
     ("greedy_rows", 64, 4, 50000, "bf16", 0.0, 20, 0.95, {"quant": 4}),
+    ("nucleus_f32", 64, 3, 30011, "f32", 1.0, 0, 0.9, {}),
+    ("nucleus_bf16_ties", 64, 2, 50000, "bf16", 0.7, 0, 0.95, {"quant": 4}),
+    ("nucleus_low_T", 48, 2, 20000, "f32", 0.3, 0, 0.8, {}),
+    ("nucleus_tiny_top_p", 32, 2, 10000, "f32", 1.0, 0, 1e-3, {}),
+    ("nucleus_all_equal", 16, 2, 3000, "f32", 1.0, 0, 0.5, {"scale": 0.0}),
+    ("nucleus_top_k_ge_V", 32, 2, 4000, "bf16", 1.2, 5000, 0.7, {}),
 ]
 
 
