@@ -68,7 +68,7 @@ typedef struct {
 /* Host-side descriptor of shapes, layout, stream and scratch. */
 typedef struct {
     int32_t batch;     /* B >= 1                                              */
-    int32_t max_draft; /* K >= 1 (drafted positions per row)                  */
+    int32_t max_draft; /* 1 <= K <= 1024 (drafted positions per row)         */
     int32_t vocab;     /* V >= 2, shared by target and draft                  */
     int32_t dtype;     /* SV_F32 or SV_BF16, same for both logits tensors     */
     int64_t target_row_stride; /* elements between consecutive (b, k) rows; 0 => V */

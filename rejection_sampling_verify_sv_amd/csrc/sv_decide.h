@@ -1,16 +1,18 @@
-// sv_decide.h — per-row decision at one draft position.
+// sv_decide.h — per-row decision at one draft position, and row set-up.
 //
-// After the row pass of position k, one workgroup per live row:
+// After the row pass (and, for nucleus rows, the nucleus cut) of position k,
+// one wave per live row:
 //   * merges the segment records of the target (and draft) row;
-//   * top-k rows: sorts the <= 64 survivors, applies temperature, the top_p
-//     walk over the renormalised top-k and renormalisation, all in fp64 and
-//     in the same summation order as the definition; then runs the accept
-//     test and, if the row ends here, the residual or bonus draw over the
-//     <= 64 kept tokens in ascending id order;
+//   * top-k rows: applies temperature, the top_p walk over the renormalised
+//     top-k and renormalisation in fp64 across the lanes (lane j holds the
+//     j-th ranked token); then runs the accept test and, if the row ends here,
+//     the residual or bonus draw over the <= 64 kept tokens in ascending id
+//     order;
 //   * greedy rows: compares the draft token with the target argmax;
-//   * full-vocab rows: forms p(x), q(x) from {max, sum-exp} and the two
-//     gathered logits, runs the accept test and, if the row ends here, hands
-//     the draw to the full-vocab sampler (sv_sample.h).
+//   * full-vocab rows: forms p(x), q(x) from {max, sum-exp} (untruncated) or
+//     from the exact nucleus cut, runs the accept test and, if the row ends
+//     here, queues the draw for the full-vocab sampler (sv_sample.h).
+// A row that accepts and continues lists its units for position k+1.
 //
 // Rule sources: deniz.in "Üç düzeltmeden sonra Qwen3.5 ve Qwen3.6 MTP head…",
 // sections "Örnekleme altında doğrulama yanlıştı" (greedy check; accept with
@@ -24,30 +26,16 @@
 
 namespace sv {
 
-struct StepArgs {
-    const void* target;
-    const void* draft;
-    int64_t t_stride, d_stride;
-    int K, V, nseg, nch;
-    const int32_t* tokens;
-    const float* uniforms;
-    RowInfo* rows;
-    const PartSlot* parts;
-    double2* chunks;
-    int32_t* out_tokens;
-    int32_t* out_acc;
-    double* diag;
-    FnUnit* fn_unit;    // [B*2] nucleus cut of the current position
-    const double* ebk;  // [kNB] e^(-b/32)
-};
+constexpr int kDecideThreads = kWave;  // one wave per row
 
 __device__ inline void diag_nan_row(double* diag, int b, int K) {
     if (!diag) return;
     double* d = diag + (int64_t)b * 4 * (K + 1);
-    for (int i = threadIdx.x; i < 4 * (K + 1); i += kThreads) d[i] = __longlong_as_double(0x7FF8000000000000ll);
+    for (int i = lane_id(); i < 4 * (K + 1); i += kWave)
+        d[i] = __longlong_as_double(0x7FF8000000000000ll);
 }
 
-// Single thread: write accepted drafts + final token, close the row.
+// One lane: write accepted drafts + final token, close the row.
 __device__ inline void emit_row(const StepArgs& a, int b, int acc, int y) {
     int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
     const int32_t* t = a.tokens + (int64_t)b * a.K;
@@ -58,408 +46,390 @@ __device__ inline void emit_row(const StepArgs& a, int b, int acc, int y) {
     a.rows[b].status = ST_DONE;
 }
 
-__device__ inline void fail_row(const StepArgs& a, int b) {
-    // every thread of the block calls this (uniform)
+// Every lane of the wave calls these (the diagnostics are cleared in parallel).
+__device__ inline void close_row_invalid(const StepArgs& a, int b, int code) {
     diag_nan_row(a.diag, b, a.K);
-    if (threadIdx.x == 0) {
+    if (lane_id() == 0) {
         int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
         for (int j = 0; j <= a.K; j++) o[j] = -1;
-        a.out_acc[b] = -1;
+        a.out_acc[b] = code;  // -1 invalid data, -2 not served
         a.rows[b].status = ST_ERROR;
     }
 }
 
-// Row the build does not serve (boundary bucket over capacity): -2.
-__device__ inline void unsup_row(const StepArgs& a, int b) {
-    diag_nan_row(a.diag, b, a.K);
-    if (threadIdx.x == 0) {
-        int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
-        for (int j = 0; j <= a.K; j++) o[j] = -1;
-        a.out_acc[b] = -2;
-        a.rows[b].status = ST_ERROR;
+// ---- wave arithmetic in a fixed order -------------------------------------
+// Sum over the wave, computed in one fixed tree and broadcast from lane 0,
+// so every lane holds the same bits.
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_down(v, o, kWave);
+    return __shfl(v, 0, kWave);
+}
+
+__device__ __forceinline__ double wave_incl_scan(double v) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double t = __shfl_up(v, o, kWave);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Index of the first lane where pred holds, or -1.
+__device__ __forceinline__ int first_lane(bool pred) {
+    const uint64_t m = __ballot(pred);
+    return m ? __ffsll((unsigned long long)m) - 1 : -1;
+}
+
+// Top-64 keys (descending, lane j = j-th) of one unit from its segments.
+__device__ __forceinline__ uint64_t unit_top(const PartSlot* parts, int li, int nseg) {
+    const PartSlot* s = parts + (int64_t)li * nseg;
+    uint64_t acc = s[0].keys[lane_id()];
+    for (int i = 1; i < nseg; i++) acc = wave_merge_top(acc, s[i].keys[lane_id()]);
+    return acc;
+}
+
+// Truncated distribution over a ranked list (lane j = j-th ranked token):
+// temperature, top_k (first k_eff lanes), renormalise, keep while the mass
+// before the token is < top_p, renormalise.  Returns false when the best
+// logit is -inf (no finite logit).
+__device__ bool topk_dist_wave(uint64_t key, int k_eff, double T, double top_p, double* p,
+                               bool* keep) {
+    const int lane = lane_id();
+    const bool valid = lane < k_eff;
+    const double l = (double)key_logit(key);
+    const double l0 = __shfl(l, 0, kWave);
+    if (!(l0 > -INFINITY)) return false;
+    const double w = valid ? exp((l - l0) / T) : 0.0;
+    int nkeep = k_eff;
+    if (top_p < 1.0) {
+        const double zk = wave_sum(w);
+        const double P = w / zk;
+        const double up = __shfl_up(wave_incl_scan(P), 1, kWave);
+        const double mass_before = lane == 0 ? 0.0 : up;
+        const int f = first_lane(valid && !(mass_before < top_p));
+        nkeep = f < 0 ? k_eff : f;
+    }
+    *keep = lane < nkeep;
+    const double zs = wave_sum(*keep ? w : 0.0);
+    *p = *keep ? w / zs : 0.0;
+    return true;
+}
+
+__device__ __forceinline__ double lookup_lane(bool keep, int id, double p, int token) {
+    const int j = first_lane(keep && id == token);
+    return j < 0 ? 0.0 : __shfl(p, j, kWave);
+}
+
+__device__ __forceinline__ double accept_prob(double px, double qx) {
+    if (qx > 0.0) {
+        const double a = px / qx;
+        return a > 1.0 ? 1.0 : a;
+    }
+    return (px > 0.0) ? 1.0 : 0.0;
+}
+
+__device__ __forceinline__ void write_accept_diag(const StepArgs& a, int b, int k, double px,
+                                                  double qx, double acc, double uk) {
+    if (a.diag && lane_id() == 0) {
+        double* dg = a.diag + (int64_t)b * 4 * (a.K + 1);
+        dg[4 * k + 0] = px;
+        dg[4 * k + 1] = qx;
+        dg[4 * k + 2] = acc;
+        dg[4 * k + 3] = fabs(uk - acc);
     }
 }
 
-// Inverse CDF over n weights listed in ascending id order (single thread).
-// Returns the index of the first positive weight whose running sum exceeds
-// u * W; writes the bin edges as fractions of W and the margin of u.
-__device__ inline int invcdf_small(const double* w, int n, double u, double* lo, double* hi,
-                                   double* margin, double* Wout) {
-    double W = 0.0;
-    for (int j = 0; j < n; j++) W += w[j];
-    *Wout = W;
-    const double target = u * W;
-    double S = 0.0, last_before = 0.0;
-    int last = -1;
-    for (int j = 0; j < n; j++) {
-        if (!(w[j] > 0.0)) continue;
-        const double before = S;
-        S += w[j];
-        last = j;
-        last_before = before;
-        if (target < S) {
-            *lo = before / W;
-            *hi = S / W;
-            const double d1 = u - *lo, d2 = *hi - u;
-            *margin = d1 < d2 ? d1 : d2;
-            return j;
-        }
+// Row b accepted the draft at position k: continue at k+1.
+__device__ inline void continue_row(const StepArgs& a, int b, int k) {
+    if (lane_id() == 0) {
+        RowInfo& w = a.rows[b];
+        w.acc = k + 1;
+        append_units(a, b, k + 1, w);
     }
-    *lo = last_before / W;
-    *hi = 1.0;
-    *margin = 0.0;
-    return last;
 }
 
-struct TopkDecideSmem {
-    uint64_t buf[64 * kMaxTopK];
-    uint64_t top[2][kMaxTopK];
-    double w[2][kMaxTopK];
-    double prob[2][kMaxTopK];
-    int id[2][kMaxTopK];
-    int keep[2];
-    // residual / bonus, ascending id
-    double sw[kMaxTopK];
-    double sp[kMaxTopK];
-    int sid[kMaxTopK];
-    int err;
-};
-
-// Merge nseg descending lists of one side into the block-wide top k_eff.
-__device__ inline void merge_side(TopkDecideSmem& sm, const PartSlot* slots, int nseg, int k_eff,
-                                  int side) {
-    if (nseg == 1) {
-        for (int i = threadIdx.x; i < k_eff; i += kThreads) sm.top[side][i] = slots[0].keys[i];
-        __syncthreads();
-        return;
-    }
-    const int n = nseg * k_eff;
-    const int P = pow2_ceil(n);
-    for (int i = threadIdx.x; i < P; i += kThreads) {
-        uint64_t key = 0ull;
-        if (i < n) key = slots[i / k_eff].keys[i % k_eff];
-        sm.buf[i] = key;
-    }
-    __syncthreads();
-    block_sort_desc(sm.buf, P);
-    for (int i = threadIdx.x; i < k_eff; i += kThreads) sm.top[side][i] = sm.buf[i];
-    __syncthreads();
+// Row b ends at position k with a draw over the full vocabulary.
+__device__ inline void queue_draw(const StepArgs& a, int b) {
+    const int i = atomicAdd(&a.pos[a.K + 1].n_sample, 1);
+    a.slist[i] = b;
+    a.rows[b].status = ST_SAMPLE;
 }
 
-// Wave 0 builds the truncated distribution of one side from its sorted keys.
-__device__ inline void topk_dist(TopkDecideSmem& sm, int side, int k_eff, double T, double top_p) {
-    const int lane = threadIdx.x;
-    if (lane < kWave) {
-        const double l0 = (double)key_logit(sm.top[side][0]);
-        if (lane < k_eff) {
-            const uint64_t key = sm.top[side][lane];
-            const double l = (double)key_logit(key);
-            sm.w[side][lane] = exp((l - l0) / T);
-            sm.id[side][lane] = (int)key_id(key);
-        }
-        if (lane == 0 && !(l0 > -INFINITY)) sm.err = 1;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0 && !sm.err) {
-        const double* w = sm.w[side];
-        double zk = 0.0;
-        for (int j = 0; j < k_eff; j++) zk += w[j];
-        int keep = k_eff;
-        if (top_p < 1.0) {
-            double cum = 0.0;
-            keep = 0;
-            while (keep < k_eff && cum < top_p) {
-                cum += w[keep] / zk;
-                keep++;
-            }
-        }
-        double zs = 0.0;
-        for (int j = 0; j < keep; j++) zs += w[j];
-        for (int j = 0; j < k_eff; j++) sm.prob[side][j] = (j < keep) ? w[j] / zs : 0.0;
-        sm.keep[side] = keep;
-    }
-    __syncthreads();
-}
-
-__device__ inline double lookup_prob(const TopkDecideSmem& sm, int side, int token) {
-    double p = 0.0;
-    for (int j = 0; j < sm.keep[side]; j++)
-        if (sm.id[side][j] == token) p = sm.prob[side][j];
-    return p;
-}
-
-__device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri) {
-    __shared__ TopkDecideSmem sm;
+__device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, int nseg) {
+    __shared__ double s_w[kWave];
+    __shared__ double s_p[kWave];
+    __shared__ int s_id[kWave];
+    const int lane = lane_id();
     const int k_eff = ri.k_eff;
     const double T = (double)ri.T, top_p = (double)ri.top_p;
     const bool has_draft = k < ri.L;
-    if (threadIdx.x == 0) sm.err = 0;
-    const PartSlot* base = a.parts + (int64_t)b * 2 * a.nseg;
-    merge_side(sm, base, a.nseg, k_eff, 0);
-    if (has_draft) merge_side(sm, base + a.nseg, a.nseg, k_eff, 1);
-    topk_dist(sm, 0, k_eff, T, top_p);
-    if (has_draft) topk_dist(sm, 1, k_eff, T, top_p);
-    if (sm.err) {
-        fail_row(a, b);
+    const uint64_t kt = unit_top(a.parts, ri.li_t, nseg);
+    double p;
+    bool keep_p;
+    if (!topk_dist_wave(kt, k_eff, T, top_p, &p, &keep_p)) {
+        close_row_invalid(a, b, -1);
         return;
     }
+    const int id_p = (int)key_id(kt);
     const float* u = a.uniforms + (int64_t)b * (a.K + 1);
-    double* dg = a.diag ? a.diag + (int64_t)b * 4 * (a.K + 1) : nullptr;
-    bool final_draw = true;
-    bool use_resid = false;
+    double q = 0.0;
+    bool keep_q = false;
+    int id_q = -1;
     if (has_draft) {
-        __shared__ int s_accept;
-        if (threadIdx.x == 0) {
-            const int x = a.tokens[(int64_t)b * a.K + k];
-            const double px = lookup_prob(sm, 0, x), qx = lookup_prob(sm, 1, x);
-            double acc;
-            if (qx > 0.0) {
-                acc = px / qx;
-                if (acc > 1.0) acc = 1.0;
-            } else {
-                acc = (px > 0.0) ? 1.0 : 0.0;
-            }
-            const double uk = (double)u[k];
-            if (dg) {
-                dg[4 * k + 0] = px;
-                dg[4 * k + 1] = qx;
-                dg[4 * k + 2] = acc;
-                dg[4 * k + 3] = fabs(uk - acc);
-            }
-            s_accept = uk < acc;
-            if (s_accept) a.rows[b].acc = k + 1;
+        const uint64_t kd = unit_top(a.parts, ri.li_d, nseg);
+        if (!topk_dist_wave(kd, k_eff, T, top_p, &q, &keep_q)) {
+            close_row_invalid(a, b, -1);
+            return;
         }
-        __syncthreads();
-        if (s_accept) return;
-        use_resid = true;
+        id_q = (int)key_id(kd);
+        const int x = a.tokens[(int64_t)b * a.K + k];
+        const double px = lookup_lane(keep_p, id_p, p, x);
+        const double qx = lookup_lane(keep_q, id_q, q, x);
+        const double acc = accept_prob(px, qx);
+        const double uk = (double)u[k];
+        write_accept_diag(a, b, k, px, qx, acc, uk);
+        if (uk < acc) {
+            continue_row(a, b, k);
+            return;
+        }
     }
-    if (!final_draw) return;
-    // weights over p's kept set in ascending id order (rank by id)
-    const int kp = sm.keep[0];
-    if (threadIdx.x < kp) {
-        const int j = threadIdx.x;
-        const int id = sm.id[0][j];
-        int rank = 0;
-        for (int i = 0; i < kp; i++) rank += sm.id[0][i] < id;
-        const double pj = sm.prob[0][j];
-        double wj = pj;
-        if (use_resid) {
-            const double qj = lookup_prob(sm, 1, id);
-            const double d = pj - qj;
-            wj = d > 0.0 ? d : 0.0;
-        }
-        sm.sid[rank] = id;
-        sm.sw[rank] = wj;
-        sm.sp[rank] = pj;
+    // Final draw over p's kept tokens in ascending id order: the residual
+    // (p - q)+ after a rejection, p itself for the bonus token.
+    double qj = 0.0;
+    int rank = 0;
+    for (int s = 0; s < kWave; s++) {
+        const int ids = __shfl(id_q, s, kWave);
+        const double qs = __shfl(q, s, kWave);
+        const bool ks = __shfl((int)keep_q, s, kWave) != 0;
+        if (ks && ids == id_p) qj = qs;
+        const int idp = __shfl(id_p, s, kWave);
+        const bool kp = __shfl((int)keep_p, s, kWave) != 0;
+        rank += (kp && idp < id_p) ? 1 : 0;
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const double uf = (double)u[a.K];
-        double lo, hi, mg, W;
-        const double* w = sm.sw;
-        if (use_resid) {
-            double Wr = 0.0;
-            for (int j = 0; j < kp; j++) Wr += sm.sw[j];
-            if (!(Wr > 0.0)) w = sm.sp;
-        }
-        const int j = invcdf_small(w, kp, uf, &lo, &hi, &mg, &W);
-        const int y = sm.sid[j];
-        if (dg) {
-            dg[4 * a.K + 0] = use_resid ? w[j] / W : sm.sp[j];
-            dg[4 * a.K + 1] = lo;
-            dg[4 * a.K + 2] = hi;
-            dg[4 * a.K + 3] = mg;
+    if (keep_p) {
+        const double d = p - qj;
+        s_w[rank] = has_draft ? (d > 0.0 ? d : 0.0) : p;
+        s_p[rank] = p;
+        s_id[rank] = id_p;
+    }
+    wave_lds_sync();
+    const int kp = __popcll(__ballot(keep_p));
+    double wr = lane < kp ? s_w[lane] : 0.0;
+    const double pr = lane < kp ? s_p[lane] : 0.0;
+    const int idr = lane < kp ? s_id[lane] : -1;
+    double W = wave_sum(wr);
+    const bool fallback = has_draft && !(W > 0.0);
+    if (fallback) {  // p == q up to rounding: draw from p
+        wr = pr;
+        W = wave_sum(wr);
+    }
+    const double uf = (double)u[a.K];
+    const double target = uf * W;
+    const double incl = wave_incl_scan(wr);
+    const double excl_raw = __shfl_up(incl, 1, kWave);
+    const double excl = lane == 0 ? 0.0 : excl_raw;
+    int j = first_lane(wr > 0.0 && target < incl);
+    double margin_scale = 1.0;
+    if (j < 0) {  // not reachable for u < 1; keeps the function total
+        const uint64_t pos = __ballot(wr > 0.0);
+        j = 63 - __clzll((unsigned long long)pos);
+        margin_scale = 0.0;
+    }
+    const int y = __shfl(idr, j, kWave);
+    const double lo = __shfl(excl, j, kWave) / W;
+    const double hi = (margin_scale == 0.0) ? 1.0 : __shfl(incl, j, kWave) / W;
+    const double wy = __shfl(wr, j, kWave);
+    const double py = __shfl(pr, j, kWave);
+    if (lane == 0) {
+        if (a.diag) {
+            double* dg = a.diag + (int64_t)b * 4 * (a.K + 1) + 4 * a.K;
+            const double d1 = uf - lo, d2 = hi - uf;
+            dg[0] = has_draft ? wy / W : py;
+            dg[1] = lo;
+            dg[2] = hi;
+            dg[3] = margin_scale * (d1 < d2 ? d1 : d2);
         }
         emit_row(a, b, k, y);
     }
 }
 
-__device__ void decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri) {
-    if (threadIdx.x != 0) return;
-    const PartSlot* base = a.parts + (int64_t)b * 2 * a.nseg;
+__device__ void decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri, int nseg) {
+    const int lane = lane_id();
+    const PartSlot* s = a.parts + (int64_t)ri.li_t * nseg;
     uint64_t best = 0ull;
-    for (int s = 0; s < a.nseg; s++) best = base[s].keys[0] > best ? base[s].keys[0] : best;
+    for (int i = lane; i < nseg; i += kWave) best = s[i].keys[0] > best ? s[i].keys[0] : best;
+    best = wave_max_u64(best);
     const int g = (int)key_id(best);
     if (k < ri.L && a.tokens[(int64_t)b * a.K + k] == g) {
-        a.rows[b].acc = k + 1;
+        continue_row(a, b, k);
         return;
     }
-    emit_row(a, b, k, g);
+    if (lane == 0) emit_row(a, b, k, g);
 }
 
-// {max, sum-exp} of one full-vocab row from its segment records.
-__device__ inline void full_stats(const PartSlot* slots, int nseg, double invT, double* m,
+// {max, sum-exp} of one full-vocab unit from its segment records (lanes
+// combine in a fixed tree; lane 0's result is broadcast).
+__device__ inline void full_stats(const PartSlot* parts, int li, int nseg, double invT, double* m,
                                   double* z) {
+    const int lane = lane_id();
     float mm = -INFINITY;
     double ss = 0.0;
-    for (int s = 0; s < nseg; s++) {
-        const FullStat* fs = reinterpret_cast<const FullStat*>(slots + s);
+    const PartSlot* s = parts + (int64_t)li * nseg;
+    for (int i = lane; i < nseg; i += kWave) {
+        const FullStat* fs = reinterpret_cast<const FullStat*>(s + i);
         ms_combine(mm, ss, fs->m, fs->s, invT);
     }
-    *m = (double)mm;
-    *z = ss;
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        const float m2 = __shfl_down(mm, o, kWave);
+        const double s2 = __shfl_down(ss, o, kWave);
+        if (lane + o < kWave) ms_combine(mm, ss, m2, s2, invT);
+    }
+    *m = (double)__shfl(mm, 0, kWave);
+    *z = __shfl(ss, 0, kWave);
 }
 
 template <int DT>
-__device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri) {
-    __shared__ int s_fail;
-    if (threadIdx.x == 0) {
-        s_fail = 0;
-        const double T = (double)ri.T, invT = 1.0 / T;
-        const PartSlot* base = a.parts + (int64_t)b * 2 * a.nseg;
-        double mt, zt, md = 0.0, zd = 0.0;
-        full_stats(base, a.nseg, invT, &mt, &zt);
-        RowInfo& w = a.rows[b];
-        if (!(mt > -INFINITY)) {
-            s_fail = 1;
-        } else if (k == ri.L) {
+__device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri, int nseg) {
+    const double T = (double)ri.T, invT = 1.0 / T;
+    double mt, zt, md = 0.0, zd = 0.0;
+    full_stats(a.parts, ri.li_t, nseg, invT, &mt, &zt);
+    if (!(mt > -INFINITY)) {
+        close_row_invalid(a, b, -1);
+        return;
+    }
+    if (k == ri.L) {
+        if (lane_id() == 0) {
+            RowInfo& w = a.rows[b];
             w.need = NEED_BONUS;
             w.kpos = k;
             w.mt = mt;
             w.zt = zt;
-            w.status = ST_SAMPLE;
-        } else {
-            full_stats(base + a.nseg, a.nseg, invT, &md, &zd);
-            if (!(md > -INFINITY)) {
-                s_fail = 1;
-            } else {
-                const int x = a.tokens[(int64_t)b * a.K + k];
-                const char* trow = static_cast<const char*>(a.target) +
-                                   ((int64_t)b * (a.K + 1) + k) * a.t_stride * Elt<DT>::kSize;
-                const char* drow = static_cast<const char*>(a.draft) +
-                                   ((int64_t)b * a.K + k) * a.d_stride * Elt<DT>::kSize;
-                const double lx = (double)load_one<DT>(trow, x);
-                const double ld = (double)load_one<DT>(drow, x);
-                const double px = exp((lx - mt) / T) / zt;
-                const double qx = exp((ld - md) / T) / zd;
-                double acc;
-                if (qx > 0.0) {
-                    acc = px / qx;
-                    if (acc > 1.0) acc = 1.0;
-                } else {
-                    acc = (px > 0.0) ? 1.0 : 0.0;
-                }
-                const double uk = (double)a.uniforms[(int64_t)b * (a.K + 1) + k];
-                if (a.diag) {
-                    double* dg = a.diag + (int64_t)b * 4 * (a.K + 1);
-                    dg[4 * k + 0] = px;
-                    dg[4 * k + 1] = qx;
-                    dg[4 * k + 2] = acc;
-                    dg[4 * k + 3] = fabs(uk - acc);
-                }
-                if (uk < acc) {
-                    w.acc = k + 1;
-                } else {
-                    w.need = NEED_RESID;
-                    w.kpos = k;
-                    w.mt = mt;
-                    w.zt = zt;
-                    w.md = md;
-                    w.zd = zd;
-                    w.status = ST_SAMPLE;
-                }
-            }
+            queue_draw(a, b);
         }
+        return;
     }
-    __syncthreads();
-    if (s_fail) fail_row(a, b);
+    full_stats(a.parts, ri.li_d, nseg, invT, &md, &zd);
+    if (!(md > -INFINITY)) {
+        close_row_invalid(a, b, -1);
+        return;
+    }
+    if (lane_id() != 0) return;
+    const int x = a.tokens[(int64_t)b * a.K + k];
+    const double lx = (double)load_one<DT>(unit_row<DT>(a, b, 0, k), x);
+    const double ld = (double)load_one<DT>(unit_row<DT>(a, b, 1, k), x);
+    const double px = exp((lx - mt) / T) / zt;
+    const double qx = exp((ld - md) / T) / zd;
+    const double acc = accept_prob(px, qx);
+    const double uk = (double)a.uniforms[(int64_t)b * (a.K + 1) + k];
+    write_accept_diag(a, b, k, px, qx, acc, uk);
+    RowInfo& w = a.rows[b];
+    if (uk < acc) {
+        w.acc = k + 1;
+        append_units(a, b, k + 1, w);
+    } else {
+        w.need = NEED_RESID;
+        w.kpos = k;
+        w.mt = mt;
+        w.zt = zt;
+        w.md = md;
+        w.zd = zd;
+        queue_draw(a, b);
+    }
 }
 
 // Nucleus rows: p(x) = [key(x) >= tau] w(x) / Z_S with the exact masses of
 // the cut computed by the nucleus kernels for this position.
 template <int DT>
 __device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& ri) {
-    __shared__ int s_fail;  // 0 ok, 1 invalid data, 2 not served
-    if (threadIdx.x == 0) {
-        s_fail = 0;
-        const double invT = 1.0 / (double)ri.T;
-        const FnUnit ut = a.fn_unit[b * 2];
-        RowInfo& w = a.rows[b];
-        if (ut.status != 0) {
-            s_fail = ut.status == 1 ? 2 : 1;
-        } else if (k == ri.L) {
-            w.need = NEED_BONUS;
-            w.kpos = k;
-            w.mt = (double)ut.m;
-            w.zt = ut.Zs;
-            w.tau_t = ut.tau;
-            w.status = ST_SAMPLE;
-        } else {
-            const FnUnit ud = a.fn_unit[b * 2 + 1];
-            if (ud.status != 0) {
-                s_fail = ud.status == 1 ? 2 : 1;
-            } else {
-                const int x = a.tokens[(int64_t)b * a.K + k];
-                const char* trow = static_cast<const char*>(a.target) +
-                                   ((int64_t)b * (a.K + 1) + k) * a.t_stride * Elt<DT>::kSize;
-                const char* drow = static_cast<const char*>(a.draft) +
-                                   ((int64_t)b * a.K + k) * a.d_stride * Elt<DT>::kSize;
-                const float lx = load_one<DT>(trow, x);
-                const float ld = load_one<DT>(drow, x);
-                const double px = (make_key(lx, (uint32_t)x) >= ut.tau)
-                                      ? fn_weight(lx, ut.m, invT, a.ebk) / ut.Zs : 0.0;
-                const double qx = (make_key(ld, (uint32_t)x) >= ud.tau)
-                                      ? fn_weight(ld, ud.m, invT, a.ebk) / ud.Zs : 0.0;
-                double acc;
-                if (qx > 0.0) {
-                    acc = px / qx;
-                    if (acc > 1.0) acc = 1.0;
-                } else {
-                    acc = (px > 0.0) ? 1.0 : 0.0;
-                }
-                const double uk = (double)a.uniforms[(int64_t)b * (a.K + 1) + k];
-                if (a.diag) {
-                    double* dg = a.diag + (int64_t)b * 4 * (a.K + 1);
-                    dg[4 * k + 0] = px;
-                    dg[4 * k + 1] = qx;
-                    dg[4 * k + 2] = acc;
-                    dg[4 * k + 3] = fabs(uk - acc);
-                }
-                if (uk < acc) {
-                    w.acc = k + 1;
-                } else {
-                    w.need = NEED_RESID;
-                    w.kpos = k;
-                    w.mt = (double)ut.m;
-                    w.zt = ut.Zs;
-                    w.tau_t = ut.tau;
-                    w.md = (double)ud.m;
-                    w.zd = ud.Zs;
-                    w.tau_d = ud.tau;
-                    w.status = ST_SAMPLE;
-                }
-            }
-        }
+    const FnUnit ut = a.fn_unit[b * 2];
+    const bool has_draft = k < ri.L;
+    FnUnit ud;
+    ud.status = 0;
+    if (has_draft) ud = a.fn_unit[b * 2 + 1];
+    const int st = ut.status != 0 ? ut.status : (has_draft ? ud.status : 0);
+    if (st != 0) {
+        close_row_invalid(a, b, st == 1 ? -2 : -1);
+        return;
     }
-    __syncthreads();
-    if (s_fail == 1)
-        fail_row(a, b);
-    else if (s_fail == 2)
-        unsup_row(a, b);
+    if (lane_id() != 0) return;
+    RowInfo& w = a.rows[b];
+    if (!has_draft) {
+        w.need = NEED_BONUS;
+        w.kpos = k;
+        w.mt = (double)ut.m;
+        w.zt = ut.Zs;
+        w.tau_t = ut.tau;
+        queue_draw(a, b);
+        return;
+    }
+    const double invT = 1.0 / (double)ri.T;
+    const int x = a.tokens[(int64_t)b * a.K + k];
+    const float lx = load_one<DT>(unit_row<DT>(a, b, 0, k), x);
+    const float ld = load_one<DT>(unit_row<DT>(a, b, 1, k), x);
+    const double px =
+        (make_key(lx, (uint32_t)x) >= ut.tau) ? fn_weight(lx, ut.m, invT, a.ebk) / ut.Zs : 0.0;
+    const double qx =
+        (make_key(ld, (uint32_t)x) >= ud.tau) ? fn_weight(ld, ud.m, invT, a.ebk) / ud.Zs : 0.0;
+    const double acc = accept_prob(px, qx);
+    const double uk = (double)a.uniforms[(int64_t)b * (a.K + 1) + k];
+    write_accept_diag(a, b, k, px, qx, acc, uk);
+    if (uk < acc) {
+        w.acc = k + 1;
+        append_units(a, b, k + 1, w);
+    } else {
+        w.need = NEED_RESID;
+        w.kpos = k;
+        w.mt = (double)ut.m;
+        w.zt = ut.Zs;
+        w.tau_t = ut.tau;
+        w.md = (double)ud.m;
+        w.zd = ud.Zs;
+        w.tau_d = ud.tau;
+        queue_draw(a, b);
+    }
 }
 
+// One wave per row; rows not live at position k return at once.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void decide_kernel(StepArgs a, int k) {
+__global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepArgs a, int k) {
     const int b = blockIdx.x;
     const RowInfo ri = a.rows[b];
     if (ri.status != ST_LIVE || k > ri.L) return;
+    int nseg, tps;
+    seg_plan(a.pos[k].n_units, a.ntiles, &nseg, &tps);
     if (ri.cls == CLS_GREEDY)
-        decide_greedy(a, b, k, ri);
+        decide_greedy(a, b, k, ri, nseg);
     else if (ri.cls == CLS_TOPK)
-        decide_topk(a, b, k, ri);
+        decide_topk(a, b, k, ri, nseg);
     else if (ri.cls == CLS_NUCLEUS)
         decide_nucleus<DT>(a, b, k, ri);
     else
-        decide_full<DT>(a, b, k, ri);
+        decide_full<DT>(a, b, k, ri, nseg);
 }
 
-// Row classification and output initialisation (one thread per row).
-// A row is invalid when T is negative, NaN or infinite, top_p is not > 0,
-// draft_len is outside [0, K] or a read draft token is outside [0, V).
-__global__ __launch_bounds__(kThreads) void plan_kernel(StepArgs a, int B, const int32_t* draft_len,
+// Zero the work counters and write the e^(-b/32) table (once per call).
+__global__ __launch_bounds__(kThreads) void init_kernel(StepArgs a, double* ebk) {
+    const int i = blockIdx.x * kThreads + threadIdx.x;
+    if (i < a.K + 2) {
+        a.pos[i].n_units = 0;
+        a.pos[i].n_fn = 0;
+        a.pos[i].n_sample = 0;
+        a.pos[i].pad = 0;
+    }
+    if (i < kNB) ebk[i] = exp(-(double)i / 32.0);
+}
+
+// Row classification, output initialisation and the position-0 unit lists
+// (one thread per row).  A row is invalid when T is negative, NaN or
+// infinite, top_p is not > 0, draft_len is outside [0, K] or a read draft
+// token is outside [0, V).
+__global__ __launch_bounds__(kThreads) void plan_kernel(StepArgs a, const int32_t* draft_len,
                                                         const sv_sampler_params* params) {
     const int b = blockIdx.x * kThreads + threadIdx.x;
-    if (b >= B) return;
+    if (b >= a.B) return;
     const sv_sampler_params prm = params[b];
     const int L = draft_len ? draft_len[b] : a.K;
     const float T = prm.temperature, tp = prm.top_p;
@@ -491,9 +461,10 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(StepArgs a, int B, const
     ri.flags = 0;
     ri.T = T;
     ri.top_p = tp;
-    ri.pad0 = ri.pad1 = 0;
+    ri.li_t = ri.li_d = -1;
     ri.mt = ri.zt = ri.md = ri.zd = 0.0;
     ri.tau_t = ri.tau_d = 0ull;
+    if (cls >= 0) append_units(a, b, 0, ri);
     a.rows[b] = ri;
     int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
     for (int j = 0; j <= a.K; j++) o[j] = -1;

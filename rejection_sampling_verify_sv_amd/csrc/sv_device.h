@@ -5,9 +5,13 @@
 //   * a "tile" is what one workgroup reads in one step: every thread issues
 //     kLoads 16-byte loads, consecutive lanes read consecutive 16-byte vectors
 //     (fully coalesced), so a tile is 16 KiB of logits (4096 fp32 or 8192 bf16);
-//   * a "segment" is a run of whole tiles of one logits row handled by one
-//     workgroup; a row is split into nseg segments so that small batches still
-//     fill the 256 compute units.
+//     tiles are double-buffered, so two tiles per workgroup are in flight;
+//   * a "unit" is one logits row to stream: (batch row b, side), side 0 = the
+//     target row, side 1 = the draft row of the current position;
+//   * a "segment" is a run of whole tiles of one unit handled by one workgroup.
+//     Units live at a position are listed on the device; the number of
+//     segments per unit is chosen from that count so every position keeps the
+//     256 compute units busy even after most rows have stopped.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,9 +25,11 @@ constexpr int kThreads = 256;
 constexpr int kWave = 64;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxTopK = SV_MAX_TOP_K;
-constexpr int kLoads = 4;    // 16-byte loads per thread per tile
-constexpr int kCandCap = 1024;  // candidate slots per merge round
-constexpr int kMergeBuf = 2048; // pow2 >= kCandCap + kMaxTopK
+constexpr int kLoads = 4;          // 16-byte loads per thread per tile
+constexpr int kGrid = 2048;        // workgroups of a streaming launch (grid-stride)
+constexpr int kTargetItems = 4096; // segments wanted per streaming launch
+constexpr int kMaxSeg = 64;        // segments per unit (decide merges <= 64 lists)
+constexpr int kCandBuf = 128;      // per-wave candidate buffer (top-k select)
 
 enum RowClass : int32_t {
     CLS_GREEDY = 0,
@@ -42,14 +48,23 @@ struct RowInfo {
     int32_t cls, L, status, acc;
     int32_t kpos, need, k_eff, flags;
     float T, top_p;
-    int32_t pad0, pad1;
+    int32_t li_t, li_d;      // list index of the target / draft unit at the current position
     double mt, zt, md, zd;   // full-vocab stats (max, normaliser) at position kpos
     uint64_t tau_t, tau_d;   // nucleus rows: key of the last kept token
 };
 static_assert(sizeof(RowInfo) == 96, "RowInfo layout");
 
-// One segment's result for one (row, side): either a descending top-k key
-// list (zero-padded) or, for full-vocab rows, {max, sum-exp relative to max}.
+// Work counters of one position (units to stream, nucleus units, rows to
+// draw from at the end).
+struct PosDesc {
+    int32_t n_units;
+    int32_t n_fn;
+    int32_t n_sample;
+    int32_t pad;
+};
+
+// One segment's result: either a descending top-k key list (zero-padded)
+// or, for full-vocab rows, {max, sum-exp relative to max}.
 struct PartSlot {
     uint64_t keys[kMaxTopK];
 };
@@ -73,7 +88,7 @@ struct FnUnit {
     int32_t beta;    // boundary bucket
     int32_t count;   // tokens in the boundary bucket (histogram)
     int32_t ncoll;   // tokens appended by the collect pass
-    int32_t status;  // 0 ok, 1 boundary bucket too large to resolve
+    int32_t status;  // 0 ok, 1 boundary bucket too large to resolve, 2 no finite logit
     int32_t pad;
 };
 
@@ -122,6 +137,7 @@ __device__ __forceinline__ double unfixed80(uint64_t hi, uint64_t lo) {
     return (double)hi * 9.094947017729282e-13 + (double)lo * 8.271806125530277e-25;
 }
 
+// ---- element types and tiles ----------------------------------------------
 template <int DT>
 struct Elt;
 template <>
@@ -162,9 +178,17 @@ __device__ __forceinline__ float key_logit(uint64_t k) {
 }
 __device__ __forceinline__ uint32_t key_id(uint64_t k) { return 0xFFFFFFFFu - (uint32_t)k; }
 
+// Logit below which no key can exceed `thr` (the id decides on equality).
+__device__ __forceinline__ float thr_floor(uint64_t thr) {
+    return ((uint32_t)(thr >> 32) < 0x007FFFFFu) ? -INFINITY : key_logit(thr);
+}
+
 // ---- loads ---------------------------------------------------------------
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct RawTile {
+    u32x4 q[kLoads];
+};
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -179,51 +203,55 @@ __device__ __forceinline__ float load_one(const void* row, int64_t i) {
     }
 }
 
-// Load one tile starting at element `start` into v[].  Element v[j*kVec+e]
-// has id start + (j*kThreads + tid)*kVec + e, so a thread's elements are in
-// ascending id order.  When `full` is false, elements at or past `end` read
-// as -inf and must be masked by the caller with elem_id() < end.
-template <int DT, bool kAligned>
-__device__ __forceinline__ void load_tile(const void* row, int64_t start, int64_t end, bool full,
-                                          float (&v)[TileShape<DT>::kE]) {
-    constexpr int kVec = Elt<DT>::kVec;
-    const int tid = threadIdx.x;
-    if (kAligned && full) {
+// Issue the 16-byte loads of one full tile (row 16-byte aligned).
+template <int DT>
+__device__ __forceinline__ void issue_tile(const void* row, int64_t t0, RawTile& r) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const char*>(row) +
+                                                    t0 * Elt<DT>::kSize);
 #pragma unroll
-        for (int j = 0; j < kLoads; j++) {
-            const int64_t off = start + (int64_t)(j * kThreads + tid) * kVec;
-            if constexpr (DT == SV_F32) {
-                const f32x4 q = __builtin_nontemporal_load(
-                    reinterpret_cast<const f32x4*>(static_cast<const float*>(row) + off));
-                v[j * 4 + 0] = q.x;
-                v[j * 4 + 1] = q.y;
-                v[j * 4 + 2] = q.z;
-                v[j * 4 + 3] = q.w;
-            } else {
-                const u32x4 q = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(row) + off));
-                v[j * 8 + 0] = bf16_lo(q.x);
-                v[j * 8 + 1] = bf16_hi(q.x);
-                v[j * 8 + 2] = bf16_lo(q.y);
-                v[j * 8 + 3] = bf16_hi(q.y);
-                v[j * 8 + 4] = bf16_lo(q.z);
-                v[j * 8 + 5] = bf16_hi(q.z);
-                v[j * 8 + 6] = bf16_lo(q.w);
-                v[j * 8 + 7] = bf16_hi(q.w);
-            }
-        }
-    } else {
+    for (int j = 0; j < kLoads; j++)
+        r.q[j] = __builtin_nontemporal_load(p + j * kThreads + (int)threadIdx.x);
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack_tile(const RawTile& r, float (&v)[TileShape<DT>::kE]) {
 #pragma unroll
-        for (int j = 0; j < kLoads; j++) {
-#pragma unroll
-            for (int e = 0; e < kVec; e++) {
-                const int64_t i = start + (int64_t)(j * kThreads + tid) * kVec + e;
-                v[j * kVec + e] = (i < end) ? load_one<DT>(row, i) : -INFINITY;
-            }
+    for (int j = 0; j < kLoads; j++) {
+        if constexpr (DT == SV_F32) {
+            v[j * 4 + 0] = __uint_as_float(r.q[j].x);
+            v[j * 4 + 1] = __uint_as_float(r.q[j].y);
+            v[j * 4 + 2] = __uint_as_float(r.q[j].z);
+            v[j * 4 + 3] = __uint_as_float(r.q[j].w);
+        } else {
+            v[j * 8 + 0] = bf16_lo(r.q[j].x);
+            v[j * 8 + 1] = bf16_hi(r.q[j].x);
+            v[j * 8 + 2] = bf16_lo(r.q[j].y);
+            v[j * 8 + 3] = bf16_hi(r.q[j].y);
+            v[j * 8 + 4] = bf16_lo(r.q[j].z);
+            v[j * 8 + 5] = bf16_hi(r.q[j].z);
+            v[j * 8 + 6] = bf16_lo(r.q[j].w);
+            v[j * 8 + 7] = bf16_hi(r.q[j].w);
         }
     }
 }
 
+// Element-wise load of a tile; elements at or past `end` read as -inf.
+template <int DT>
+__device__ __forceinline__ void load_tile_partial(const void* row, int64_t start, int64_t end,
+                                                  float (&v)[TileShape<DT>::kE]) {
+    constexpr int kVec = Elt<DT>::kVec;
+#pragma unroll
+    for (int j = 0; j < kLoads; j++) {
+#pragma unroll
+        for (int e = 0; e < kVec; e++) {
+            const int64_t i = start + (int64_t)(j * kThreads + (int)threadIdx.x) * kVec + e;
+            v[j * kVec + e] = (i < end) ? load_one<DT>(row, i) : -INFINITY;
+        }
+    }
+}
+
+// Id of element v[idx] of the tile starting at t0: the thread's elements are
+// in ascending id order.
 template <int DT>
 __device__ __forceinline__ int64_t elem_id(int64_t start, int idx) {
     constexpr int kVec = Elt<DT>::kVec;
@@ -231,7 +259,72 @@ __device__ __forceinline__ int64_t elem_id(int64_t start, int idx) {
     return start + (int64_t)(j * kThreads + (int)threadIdx.x) * kVec + e;
 }
 
-// ---- wave / block reductions -------------------------------------------
+// Stream the elements [start, end) of a row (start tile-aligned) through
+// body(v, t0, full).  Full tiles are double-buffered: the loads of tile t+1
+// are in flight while tile t is processed.  The ragged tail, and every tile
+// of a row that is not 16-byte aligned, is loaded element by element.
+// `body` must not contain workgroup barriers (they would drain the loads).
+template <int DT, bool kAligned, class Body>
+__device__ __forceinline__ void stream_range(const void* row, int64_t start, int64_t end,
+                                             Body&& body) {
+    using TS = TileShape<DT>;
+    float v[TS::kE];
+    int64_t t0 = start;
+    if constexpr (kAligned) {
+        const int64_t full_end = start + ((end - start) / TS::kTile) * TS::kTile;
+        if (t0 < full_end) {
+            RawTile A, B;
+            issue_tile<DT>(row, t0, A);
+            while (true) {
+                const bool moreB = t0 + TS::kTile < full_end;
+                if (moreB) issue_tile<DT>(row, t0 + TS::kTile, B);
+                unpack_tile<DT>(A, v);
+                body(v, t0, true);
+                t0 += TS::kTile;
+                if (!moreB) break;
+                const bool moreA = t0 + TS::kTile < full_end;
+                if (moreA) issue_tile<DT>(row, t0 + TS::kTile, A);
+                unpack_tile<DT>(B, v);
+                body(v, t0, true);
+                t0 += TS::kTile;
+                if (!moreA) break;
+            }
+        }
+    }
+    while (t0 < end) {
+        load_tile_partial<DT>(row, t0, end, v);
+        body(v, t0, t0 + TS::kTile <= end);
+        t0 += TS::kTile;
+    }
+}
+
+// ---- segmentation of a position's units ----------------------------------
+// nseg segments of tps tiles per unit, chosen from the number of units so a
+// launch has about kTargetItems segments.  Every kernel that touches the
+// segments of a list derives them from the same count with this function.
+__host__ __device__ __forceinline__ void seg_plan(int n_units, int ntiles, int* nseg, int* tps) {
+    int s = n_units > 0 ? kTargetItems / n_units : 1;
+    const int cap = ntiles < kMaxSeg ? ntiles : kMaxSeg;
+    if (s > cap) s = cap;
+    if (s < 1) s = 1;
+    const int t = (ntiles + s - 1) / s;
+    *tps = t;
+    *nseg = (ntiles + t - 1) / t;
+}
+
+// ---- wave / block helpers -------------------------------------------------
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+__device__ __forceinline__ int wave_id() { return (int)(threadIdx.x / kWave); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
+
+// Order this wave's LDS accesses (writes by some lanes, reads by others).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -244,9 +337,8 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 // Block-wide max of a u64; every thread gets the result.  `tmp` holds kWaves.
 __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* tmp) {
     v = wave_max_u64(v);
-    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
     __syncthreads();
-    if (lane == 0) tmp[w] = v;
+    if (lane_id() == 0) tmp[wave_id()] = v;
     __syncthreads();
     uint64_t r = tmp[0];
 #pragma unroll
@@ -254,10 +346,43 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* tmp) {
     return r;
 }
 
+// Bitonic sort (descending) of one u64 per lane across a wave.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const uint64_t o = __shfl_xor(v, stride, kWave);
+            const bool dir = (lane & size) == 0;       // descending block
+            const bool lower = (lane & stride) == 0;   // lower index of the pair
+            const bool keep_max = (lower == dir);
+            v = keep_max ? (o > v ? o : v) : (o < v ? o : v);
+        }
+    }
+    return v;
+}
+
+// Top 64 of two descending 64-lists (one entry per lane), descending.
+// max(a_j, b_{63-j}) holds the 64 largest of the union as a bitonic
+// sequence; six half-cleaner stages sort it.
+__device__ __forceinline__ uint64_t wave_merge_top(uint64_t a, uint64_t b) {
+    const int lane = lane_id();
+    const uint64_t br = __shfl(b, kWave - 1 - lane, kWave);
+    uint64_t v = a > br ? a : br;
+#pragma unroll
+    for (int stride = kWave / 2; stride > 0; stride >>= 1) {
+        const uint64_t o = __shfl_xor(v, stride, kWave);
+        const bool lower = (lane & stride) == 0;
+        v = lower ? (o > v ? o : v) : (o < v ? o : v);
+    }
+    return v;
+}
+
 // Block-wide exclusive prefix sum of one double per thread (fixed order).
 __device__ inline double block_exclusive_scan(double v, double* tmp /* kWaves */,
                                               double* total) {
-    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    const int lane = lane_id(), w = wave_id();
     double incl = v;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -295,27 +420,62 @@ __device__ inline void block_sort_desc(uint64_t* s, int n) {
     }
 }
 
-// Bitonic sort (descending) of one u64 per lane across a wave.
-__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
-    const int lane = threadIdx.x % kWave;
-#pragma unroll
-    for (int size = 2; size <= kWave; size <<= 1) {
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const uint64_t o = __shfl_xor(v, stride, kWave);
-            const bool dir = (lane & size) == 0;       // descending block
-            const bool lower = (lane & stride) == 0;   // lower index of the pair
-            const bool keep_max = (lower == dir);
-            v = keep_max ? (o > v ? o : v) : (o < v ? o : v);
-        }
-    }
-    return v;
-}
-
 __device__ __forceinline__ int pow2_ceil(int n) {
     int p = 1;
     while (p < n) p <<= 1;
     return p;
+}
+
+// ---- arguments shared by the step kernels ---------------------------------
+struct StepArgs {
+    const void* target;
+    const void* draft;
+    int64_t t_stride, d_stride;
+    int B, K, V, ntiles;
+    const int32_t* tokens;
+    const float* uniforms;
+    RowInfo* rows;
+    PartSlot* parts;       // segment records of the current position
+    double2* chunks;       // [B][ntiles] draw masses (one chunk = one tile)
+    int32_t* out_tokens;
+    int32_t* out_acc;
+    double* diag;
+    PosDesc* pos;          // [K+2]: positions 0..K, then the final draw
+    int32_t* ulist;        // [K+1][2B] units to stream per position
+    int32_t* flist;        // [K+1][2B] nucleus units per position
+    int32_t* slist;        // [B] rows that draw over the full vocabulary at the end
+    FnUnit* fn_unit;       // [2B] nucleus cut of the current position
+    const double* ebk;     // [kNB] e^(-b/32)
+};
+
+template <int DT>
+__device__ __forceinline__ const void* unit_row(const StepArgs& a, int b, int side, int k) {
+    if (side == 0)
+        return static_cast<const char*>(a.target) +
+               ((int64_t)b * (a.K + 1) + k) * a.t_stride * Elt<DT>::kSize;
+    return static_cast<const char*>(a.draft) + ((int64_t)b * a.K + k) * a.d_stride * Elt<DT>::kSize;
+}
+
+// A row that continues to position k lists the units it needs there.
+__device__ inline void append_units(const StepArgs& a, int b, int k, RowInfo& ri) {
+    const int64_t base = (int64_t)k * 2 * a.B;
+    int li = atomicAdd(&a.pos[k].n_units, 1);
+    a.ulist[base + li] = b * 2;
+    ri.li_t = li;
+    const bool draft = ri.cls != CLS_GREEDY && k < ri.L;
+    if (draft) {
+        li = atomicAdd(&a.pos[k].n_units, 1);
+        a.ulist[base + li] = b * 2 + 1;
+        ri.li_d = li;
+    }
+    if (ri.cls == CLS_NUCLEUS) {
+        int f = atomicAdd(&a.pos[k].n_fn, 1);
+        a.flist[base + f] = b * 2;
+        if (draft) {
+            f = atomicAdd(&a.pos[k].n_fn, 1);
+            a.flist[base + f] = b * 2 + 1;
+        }
+    }
 }
 
 }  // namespace sv

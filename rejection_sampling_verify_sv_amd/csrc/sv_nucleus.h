@@ -23,6 +23,8 @@
 //           tokens while the preceding mass is below top_p * Z.  The cut key
 //           tau (last kept token) and the kept mass Z_S define the
 //           distribution: p(i) = [key_i >= tau] w_i / Z_S.
+// The streaming passes walk position k's list of nucleus units in segments,
+// like the row pass; the per-unit steps run one workgroup per unit.
 #pragma once
 
 #include "sv_decide.h"
@@ -30,259 +32,249 @@
 namespace sv {
 
 struct FnWork {
-    FnUnit* unit;        // [B*2]
-    uint64_t* hi;        // [B*2][kNB]
-    uint64_t* lo;        // [B*2][kNB]
-    uint32_t* cnt;       // [B*2][kNB]
-    uint64_t* coll;      // [B*2][kCollectCap]
-    const double* ebk;   // [kNB] e^(-b/32)
+    uint64_t* hi;    // [2B][kNB]
+    uint64_t* lo;    // [2B][kNB]
+    uint32_t* cnt;   // [2B][kNB]
+    uint64_t* coll;  // [2B][kCollectCap]
 };
 
-__device__ inline float unit_max(const StepArgs& a, int b, int side) {
-    const PartSlot* slots = a.parts + ((int64_t)b * 2 + side) * a.nseg;
+// Row max of unit (b, side) at position k from its row-pass records.
+__device__ inline float unit_max(const StepArgs& a, int b, int side, int k) {
+    int nseg, tps;
+    seg_plan(a.pos[k].n_units, a.ntiles, &nseg, &tps);
+    const int li = side == 0 ? a.rows[b].li_t : a.rows[b].li_d;
+    const PartSlot* slots = a.parts + (int64_t)li * nseg;
     float m = -INFINITY;
-    for (int s = 0; s < a.nseg; s++) m = fmaxf(m, reinterpret_cast<const FullStat*>(slots + s)->m);
+    for (int s = 0; s < nseg; s++) m = fmaxf(m, reinterpret_cast<const FullStat*>(slots + s)->m);
     return m;
 }
 
-// A nucleus unit (row b, side) is live at position k.
-__device__ __forceinline__ bool fn_live(const RowInfo& ri, int side, int k) {
-    if (ri.cls != CLS_NUCLEUS || ri.status != ST_LIVE || k > ri.L) return false;
-    return side == 0 || k < ri.L;
-}
-
-__device__ __forceinline__ const void* unit_row(const StepArgs& a, int b, int side, int k,
-                                                int esize) {
-    if (side == 0)
-        return static_cast<const char*>(a.target) + ((int64_t)b * (a.K + 1) + k) * a.t_stride * esize;
-    return static_cast<const char*>(a.draft) + ((int64_t)b * a.K + k) * a.d_stride * esize;
-}
-
-// e^(-b/32) table, written once per call.
-__global__ __launch_bounds__(kThreads) void fn_table_kernel(double* ebk) {
-    const int b = blockIdx.x * kThreads + threadIdx.x;
-    if (b < kNB) ebk[b] = exp(-(double)b / 32.0);
-}
-
-// Zero the histograms of every nucleus unit (once per call).
+// Zero the histograms of the nucleus units of position 0 (every nucleus row).
 __global__ __launch_bounds__(kThreads) void fn_zero_kernel(StepArgs a, FnWork w) {
-    const int u = blockIdx.x;  // b*2 + side
-    const RowInfo& ri = a.rows[u / 2];
-    if (ri.cls != CLS_NUCLEUS || ri.status != ST_LIVE) return;
-    for (int i = threadIdx.x; i < kNB; i += kThreads) {
-        w.hi[(int64_t)u * kNB + i] = 0ull;
-        w.lo[(int64_t)u * kNB + i] = 0ull;
-        w.cnt[(int64_t)u * kNB + i] = 0u;
+    const int n = a.pos[0].n_fn;
+    for (int i = blockIdx.x; i < n; i += gridDim.x) {
+        const int u = a.flist[i];
+        for (int j = threadIdx.x; j < kNB; j += kThreads) {
+            w.hi[(int64_t)u * kNB + j] = 0ull;
+            w.lo[(int64_t)u * kNB + j] = 0ull;
+            w.cnt[(int64_t)u * kNB + j] = 0u;
+        }
     }
 }
 
 template <int DT, bool kAligned>
-__global__ __launch_bounds__(kThreads) void fn_hist_kernel(StepArgs a, FnWork w, int k,
-                                                           int tiles_per_seg) {
+__global__ __launch_bounds__(kThreads) void fn_hist_kernel(StepArgs a, FnWork w, int k) {
     using TS = TileShape<DT>;
-    const int bid = blockIdx.x;
-    const int seg = bid % a.nseg;
-    const int side = (bid / a.nseg) & 1;
-    const int b = bid / (2 * a.nseg);
-    const RowInfo ri = a.rows[b];
-    if (!fn_live(ri, side, k)) return;
     __shared__ uint64_t s_hi[kNB];
     __shared__ uint64_t s_lo[kNB];
     __shared__ uint32_t s_cnt[kNB];
-    for (int i = threadIdx.x; i < kNB; i += kThreads) {
-        s_hi[i] = 0ull;
-        s_lo[i] = 0ull;
-        s_cnt[i] = 0u;
-    }
-    __syncthreads();
-    const float m = unit_max(a, b, side);
-    const double invT = 1.0 / (double)ri.T;
-    const void* row = unit_row(a, b, side, k, Elt<DT>::kSize);
-    const int64_t start = (int64_t)seg * tiles_per_seg * TS::kTile;
-    int64_t end = start + (int64_t)tiles_per_seg * TS::kTile;
-    if (end > a.V) end = a.V;
-    float v[TS::kE];
-    for (int64_t t0 = start; t0 < end; t0 += TS::kTile) {
-        const bool full = (t0 + TS::kTile <= end);
-        load_tile<DT, kAligned>(row, t0, end, full, v);
-#pragma unroll
-        for (int i = 0; i < TS::kE; i++) {
-            if (elem_id<DT>(t0, i) >= end) continue;
-            double d;
-            const int bk = fn_bucket(v[i], m, invT, &d);
-            if (bk >= kNB) continue;
-            uint64_t h, l;
-            fixed80(exp_neg_small(d), &h, &l);
-            atomicAdd((unsigned long long*)&s_hi[bk], (unsigned long long)h);
-            atomicAdd((unsigned long long*)&s_lo[bk], (unsigned long long)l);
-            atomicAdd(&s_cnt[bk], 1u);
+    const int n = a.pos[k].n_fn;
+    int nseg, tps;
+    seg_plan(n, a.ntiles, &nseg, &tps);
+    const int items = n * nseg;
+    const int32_t* list = a.flist + (int64_t)k * 2 * a.B;
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const int li = it / nseg, seg = it - li * nseg;
+        const int u = list[li];
+        const int b = u >> 1, side = u & 1;
+        for (int i = threadIdx.x; i < kNB; i += kThreads) {
+            s_hi[i] = 0ull;
+            s_lo[i] = 0ull;
+            s_cnt[i] = 0u;
         }
-    }
-    __syncthreads();
-    const int u = b * 2 + side;
-    for (int i = threadIdx.x; i < kNB; i += kThreads) {
-        if (s_cnt[i] == 0u) continue;
-        atomicAdd((unsigned long long*)&w.hi[(int64_t)u * kNB + i], (unsigned long long)s_hi[i]);
-        atomicAdd((unsigned long long*)&w.lo[(int64_t)u * kNB + i], (unsigned long long)s_lo[i]);
-        atomicAdd(&w.cnt[(int64_t)u * kNB + i], s_cnt[i]);
+        __syncthreads();
+        const float m = unit_max(a, b, side, k);
+        const double invT = 1.0 / (double)a.rows[b].T;
+        const int64_t start = (int64_t)seg * tps * TS::kTile;
+        int64_t end = start + (int64_t)tps * TS::kTile;
+        if (end > a.V) end = a.V;
+        stream_range<DT, kAligned>(unit_row<DT>(a, b, side, k), start, end,
+                                   [&](float (&v)[TS::kE], int64_t t0, bool full) {
+#pragma unroll
+            for (int i = 0; i < TS::kE; i++) {
+                if (!full && elem_id<DT>(t0, i) >= end) continue;
+                double d;
+                const int bk = fn_bucket(v[i], m, invT, &d);
+                if (bk >= kNB) continue;
+                uint64_t h, l;
+                fixed80(exp_neg_small(d), &h, &l);
+                atomicAdd((unsigned long long*)&s_hi[bk], (unsigned long long)h);
+                atomicAdd((unsigned long long*)&s_lo[bk], (unsigned long long)l);
+                atomicAdd(&s_cnt[bk], 1u);
+            }
+        });
+        __syncthreads();
+        for (int i = threadIdx.x; i < kNB; i += kThreads) {
+            if (s_cnt[i] == 0u) continue;
+            atomicAdd((unsigned long long*)&w.hi[(int64_t)u * kNB + i],
+                      (unsigned long long)s_hi[i]);
+            atomicAdd((unsigned long long*)&w.lo[(int64_t)u * kNB + i],
+                      (unsigned long long)s_lo[i]);
+            atomicAdd(&w.cnt[(int64_t)u * kNB + i], s_cnt[i]);
+        }
+        __syncthreads();
     }
 }
 
 // One workgroup per unit: total mass and the boundary bucket.
 __global__ __launch_bounds__(kThreads) void fn_select_kernel(StepArgs a, FnWork w, int k) {
-    const int u = blockIdx.x;
-    const int b = u / 2, side = u % 2;
-    const RowInfo ri = a.rows[b];
-    if (!fn_live(ri, side, k)) return;
     constexpr int kPer = kNB / kThreads;  // contiguous buckets per thread
     __shared__ double s_tmp[kWaves];
     __shared__ int s_beta;
-    double mass[kPer];
-    double mine = 0.0;
-    const int b0 = threadIdx.x * kPer;
+    const int n = a.pos[k].n_fn;
+    const int32_t* list = a.flist + (int64_t)k * 2 * a.B;
+    for (int li = blockIdx.x; li < n; li += gridDim.x) {
+        const int u = list[li];
+        const int b = u >> 1, side = u & 1;
+        double mass[kPer];
+        double mine = 0.0;
+        const int b0 = threadIdx.x * kPer;
 #pragma unroll
-    for (int j = 0; j < kPer; j++) {
-        const int bk = b0 + j;
-        mass[j] = unfixed80(w.hi[(int64_t)u * kNB + bk], w.lo[(int64_t)u * kNB + bk]) * w.ebk[bk];
-        mine += mass[j];
-    }
-    double Z;
-    const double excl0 = block_exclusive_scan(mine, s_tmp, &Z);
-    const double target = (double)ri.top_p * Z;
-    if (threadIdx.x == 0) s_beta = -1;
-    __syncthreads();
-    double run = excl0;
-    int best = -1;
+        for (int j = 0; j < kPer; j++) {
+            const int bk = b0 + j;
+            mass[j] = unfixed80(w.hi[(int64_t)u * kNB + bk], w.lo[(int64_t)u * kNB + bk]) * a.ebk[bk];
+            mine += mass[j];
+        }
+        double Z;
+        const double excl0 = block_exclusive_scan(mine, s_tmp, &Z);
+        const double target = (double)a.rows[b].top_p * Z;
+        if (threadIdx.x == 0) s_beta = -1;
+        __syncthreads();
+        double run = excl0;
+        int best = -1;
 #pragma unroll
-    for (int j = 0; j < kPer; j++) {
-        const int bk = b0 + j;
-        if (w.cnt[(int64_t)u * kNB + bk] > 0u && run < target) best = bk;
-        run += mass[j];
-    }
-    if (best >= 0) atomicMax(&s_beta, best);
-    __syncthreads();
-    const int beta = s_beta;
-    // the thread owning beta records the mass before it
-    if (beta >= b0 && beta < b0 + kPer) {
-        double before = excl0;
+        for (int j = 0; j < kPer; j++) {
+            const int bk = b0 + j;
+            if (w.cnt[(int64_t)u * kNB + bk] > 0u && run < target) best = bk;
+            run += mass[j];
+        }
+        if (best >= 0) atomicMax(&s_beta, best);
+        __syncthreads();
+        const int beta = s_beta;
+        FnUnit& fu = a.fn_unit[u];
+        if (beta >= b0 && beta < b0 + kPer) {
+            double before = excl0;
 #pragma unroll
-        for (int j = 0; j < kPer; j++)
-            if (j < beta - b0) before += mass[j];
-        FnUnit& fu = w.unit[u];
-        fu.Z = Z;
-        fu.Mabove = before;
-        fu.beta = beta;
-        fu.count = (int)w.cnt[(int64_t)u * kNB + beta];
-        fu.ncoll = 0;
-        fu.status = 0;
-        fu.m = unit_max(a, b, side);
-    }
-    if (beta < 0 && threadIdx.x == 0) {  // no finite logit: row error
-        w.unit[u].status = 2;
-        w.unit[u].ncoll = 0;
+            for (int j = 0; j < kPer; j++)
+                if (j < beta - b0) before += mass[j];
+            fu.Z = Z;
+            fu.Mabove = before;
+            fu.beta = beta;
+            fu.count = (int)w.cnt[(int64_t)u * kNB + beta];
+            fu.ncoll = 0;
+            fu.status = 0;
+            fu.m = unit_max(a, b, side, k);
+        }
+        if (beta < 0 && threadIdx.x == 0) {  // no finite logit: invalid row
+            fu.status = 2;
+            fu.ncoll = 0;
+        }
+        __syncthreads();
     }
 }
 
 template <int DT, bool kAligned>
-__global__ __launch_bounds__(kThreads) void fn_collect_kernel(StepArgs a, FnWork w, int k,
-                                                              int tiles_per_seg) {
+__global__ __launch_bounds__(kThreads) void fn_collect_kernel(StepArgs a, FnWork w, int k) {
     using TS = TileShape<DT>;
-    const int bid = blockIdx.x;
-    const int seg = bid % a.nseg;
-    const int side = (bid / a.nseg) & 1;
-    const int b = bid / (2 * a.nseg);
-    const RowInfo ri = a.rows[b];
-    if (!fn_live(ri, side, k)) return;
-    const int u = b * 2 + side;
-    FnUnit* fu = w.unit + u;
-    if (fu->status != 0) return;
-    const int beta = fu->beta;
-    const float m = fu->m;
-    const double invT = 1.0 / (double)ri.T;
-    const void* row = unit_row(a, b, side, k, Elt<DT>::kSize);
-    const int64_t start = (int64_t)seg * tiles_per_seg * TS::kTile;
-    int64_t end = start + (int64_t)tiles_per_seg * TS::kTile;
-    if (end > a.V) end = a.V;
-    uint64_t* coll = w.coll + (int64_t)u * kCollectCap;
-    float v[TS::kE];
-    for (int64_t t0 = start; t0 < end; t0 += TS::kTile) {
-        const bool full = (t0 + TS::kTile <= end);
-        load_tile<DT, kAligned>(row, t0, end, full, v);
+    const int n = a.pos[k].n_fn;
+    int nseg, tps;
+    seg_plan(n, a.ntiles, &nseg, &tps);
+    const int items = n * nseg;
+    const int32_t* list = a.flist + (int64_t)k * 2 * a.B;
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const int li = it / nseg, seg = it - li * nseg;
+        const int u = list[li];
+        const int b = u >> 1, side = u & 1;
+        FnUnit* fu = a.fn_unit + u;
+        if (fu->status != 0) continue;
+        const int beta = fu->beta;
+        const float m = fu->m;
+        const double invT = 1.0 / (double)a.rows[b].T;
+        const int64_t start = (int64_t)seg * tps * TS::kTile;
+        int64_t end = start + (int64_t)tps * TS::kTile;
+        if (end > a.V) end = a.V;
+        uint64_t* coll = w.coll + (int64_t)u * kCollectCap;
+        stream_range<DT, kAligned>(unit_row<DT>(a, b, side, k), start, end,
+                                   [&](float (&v)[TS::kE], int64_t t0, bool full) {
 #pragma unroll
-        for (int i = 0; i < TS::kE; i++) {
-            const int64_t id = elem_id<DT>(t0, i);
-            if (id >= end) continue;
-            double d;
-            if (fn_bucket(v[i], m, invT, &d) != beta) continue;
-            const int slot = atomicAdd(&fu->ncoll, 1);
-            if (slot < kCollectCap) coll[slot] = make_key(v[i], (uint32_t)id);
-        }
+            for (int i = 0; i < TS::kE; i++) {
+                const int64_t id = elem_id<DT>(t0, i);
+                if (!full && id >= end) continue;
+                double d;
+                if (fn_bucket(v[i], m, invT, &d) != beta) continue;
+                const int slot = atomicAdd(&fu->ncoll, 1);
+                if (slot < kCollectCap) coll[slot] = make_key(v[i], (uint32_t)id);
+            }
+        });
     }
 }
 
 // One workgroup per unit: exact cut inside the boundary bucket.  Always
 // clears the unit's histogram for the next position.
 __global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, FnWork w, int k) {
-    const int u = blockIdx.x;
-    const int b = u / 2, side = u % 2;
-    const RowInfo ri = a.rows[b];
-    if (!fn_live(ri, side, k)) return;
     __shared__ uint64_t s_key[kCollectCap];
     __shared__ double s_tmp[kWaves];
     __shared__ int s_keep;
-    FnUnit* fu = w.unit + u;
-    const int status = fu->status;
-    const int n = fu->ncoll;
-    const bool ok = status == 0 && n <= kCollectCap && n >= 1;
-    if (ok) {
-        const int P = pow2_ceil(n < 2 ? 2 : n);
-        const uint64_t* coll = w.coll + (int64_t)u * kCollectCap;
-        for (int i = threadIdx.x; i < P; i += kThreads) s_key[i] = (i < n) ? coll[i] : 0ull;
-        __syncthreads();
-        block_sort_desc(s_key, P);
-        const double invT = 1.0 / (double)ri.T;
-        const float m = fu->m;
-        const double target = (double)ri.top_p * fu->Z;
-        const double Mabove = fu->Mabove;
-        // thread t owns sorted positions [t*per, (t+1)*per)
-        const int per = (n + kThreads - 1) / kThreads;
-        const int j0 = threadIdx.x * per;
-        double mine = 0.0;
-        for (int j = j0; j < j0 + per && j < n; j++)
-            mine += fn_weight(key_logit(s_key[j]), m, invT, w.ebk);
-        double tot;
-        const double excl = block_exclusive_scan(mine, s_tmp, &tot);
-        if (threadIdx.x == 0) s_keep = 0;
-        __syncthreads();
-        double cum = Mabove + excl;
-        int keep_here = 0;
-        for (int j = j0; j < j0 + per && j < n; j++) {
-            if (cum < target) keep_here = j + 1;
-            cum += fn_weight(key_logit(s_key[j]), m, invT, w.ebk);
-        }
-        if (keep_here > 0) atomicMax(&s_keep, keep_here);
-        __syncthreads();
-        const int nk = s_keep;  // >= 1: the first token's preceding mass is below target
-        double kept = 0.0;
-        for (int j = j0; j < j0 + per && j < nk; j++)
-            kept += fn_weight(key_logit(s_key[j]), m, invT, w.ebk);
-        double ktot;
-        (void)block_exclusive_scan(kept, s_tmp, &ktot);
-        if (threadIdx.x == 0) {
-            if (nk < 1) {
-                fu->status = 1;
-            } else {
-                fu->tau = s_key[nk - 1];
-                fu->Zs = Mabove + ktot;
+    const int n_units = a.pos[k].n_fn;
+    const int32_t* list = a.flist + (int64_t)k * 2 * a.B;
+    for (int li = blockIdx.x; li < n_units; li += gridDim.x) {
+        const int u = list[li];
+        const int b = u >> 1;
+        FnUnit* fu = a.fn_unit + u;
+        const int status = fu->status;
+        const int n = fu->ncoll;
+        const bool ok = status == 0 && n <= kCollectCap && n >= 1;
+        if (ok) {
+            const int P = pow2_ceil(n < 2 ? 2 : n);
+            const uint64_t* coll = w.coll + (int64_t)u * kCollectCap;
+            for (int i = threadIdx.x; i < P; i += kThreads) s_key[i] = (i < n) ? coll[i] : 0ull;
+            __syncthreads();
+            block_sort_desc(s_key, P);
+            const double invT = 1.0 / (double)a.rows[b].T;
+            const float m = fu->m;
+            const double target = (double)a.rows[b].top_p * fu->Z;
+            const double Mabove = fu->Mabove;
+            // thread t owns sorted positions [t*per, (t+1)*per)
+            const int per = (n + kThreads - 1) / kThreads;
+            const int j0 = threadIdx.x * per;
+            double mine = 0.0;
+            for (int j = j0; j < j0 + per && j < n; j++)
+                mine += fn_weight(key_logit(s_key[j]), m, invT, a.ebk);
+            double tot;
+            const double excl = block_exclusive_scan(mine, s_tmp, &tot);
+            if (threadIdx.x == 0) s_keep = 0;
+            __syncthreads();
+            double cum = Mabove + excl;
+            int keep_here = 0;
+            for (int j = j0; j < j0 + per && j < n; j++) {
+                if (cum < target) keep_here = j + 1;
+                cum += fn_weight(key_logit(s_key[j]), m, invT, a.ebk);
             }
+            if (keep_here > 0) atomicMax(&s_keep, keep_here);
+            __syncthreads();
+            const int nk = s_keep;  // >= 1: the first token's preceding mass is below target
+            double kept = 0.0;
+            for (int j = j0; j < j0 + per && j < nk; j++)
+                kept += fn_weight(key_logit(s_key[j]), m, invT, a.ebk);
+            double ktot;
+            (void)block_exclusive_scan(kept, s_tmp, &ktot);
+            if (threadIdx.x == 0) {
+                if (nk < 1) {
+                    fu->status = 1;
+                } else {
+                    fu->tau = s_key[nk - 1];
+                    fu->Zs = Mabove + ktot;
+                }
+            }
+        } else if (threadIdx.x == 0 && status == 0) {
+            fu->status = 1;  // boundary bucket larger than kCollectCap
         }
-    } else if (threadIdx.x == 0 && status == 0) {
-        fu->status = 1;  // boundary bucket larger than kCollectCap
-    }
-    for (int i = threadIdx.x; i < kNB; i += kThreads) {
-        w.hi[(int64_t)u * kNB + i] = 0ull;
-        w.lo[(int64_t)u * kNB + i] = 0ull;
-        w.cnt[(int64_t)u * kNB + i] = 0u;
+        for (int i = threadIdx.x; i < kNB; i += kThreads) {
+            w.hi[(int64_t)u * kNB + i] = 0ull;
+            w.lo[(int64_t)u * kNB + i] = 0ull;
+            w.cnt[(int64_t)u * kNB + i] = 0u;
+        }
+        __syncthreads();
     }
 }
 

@@ -1,12 +1,20 @@
 // sv_rowpass.h — the streaming pass over logits rows (the HBM-bound step).
 //
-// One workgroup reads one segment of one logits row exactly once, in 16-byte
-// coalesced vectors, and leaves a small record:
+// A grid-stride loop walks the segments of the units live at position k.
+// One workgroup reads one segment exactly once, in 16-byte coalesced,
+// double-buffered vectors, and leaves a small record:
 //   * greedy rows:   the best (logit, lowest id) key of the segment;
-//   * top-k rows:    the segment's top-k keys, descending (k <= 64);
+//   * top-k rows:    the segment's best 64 keys, descending (k <= 64);
 //   * full-vocab:    {segment max m, sum of exp((l - m) / T)} (online).
 // Selection uses raw logits (the ranking does not depend on T > 0), so the
 // candidate sets are exact; probabilities are formed later in fp64.
+//
+// Top-k selection is per wave and free of workgroup barriers while streaming:
+// each wave keeps its running top-64 list in registers (one key per lane),
+// skips a tile with one max and one ballot when no lane holds a value above
+// the list's k-th key, and otherwise compacts candidates into a small
+// wave-private LDS buffer with ballot prefix counts, merging 64 at a time with
+// a wave bitonic sort and a bitonic merge.
 //
 // Coalesced single reads follow the read-coalescing technique described on
 // "Apple Silikon İçin Cihaz Üstü Çıkarımı Optimize Etme", section "Dikkat
@@ -19,165 +27,127 @@
 
 namespace sv {
 
-struct TopkSmem {
-    uint64_t list[kMaxTopK];
-    uint64_t buf[kMergeBuf];
+struct RowpassSmem {
+    uint64_t cbuf[kWaves][kCandBuf];
+    uint64_t lists[kWaves][kWave];
     uint64_t red[kWaves];
-    uint64_t thr;    // k-th key of the merged list (0 until it holds k keys)
-    uint64_t floor;  // lower bound from the segment's first tile
-    int ncand;
-    int nlist;
+    float redm[kWaves];
+    double reds[kWaves];
 };
 
-// Merge the candidate buffer into the running list (all threads call).
-__device__ inline void topk_merge(TopkSmem& sm, int k_eff) {
-    const int nc = sm.ncand < kCandCap ? sm.ncand : kCandCap;
-    const int nl = sm.nlist;
-    const int total = nc + nl;
-    const int P = pow2_ceil(total < 2 ? 2 : total);
-    for (int i = threadIdx.x; i < P; i += kThreads) {
-        if (i >= nc) sm.buf[i] = (i < total) ? sm.list[i - nc] : 0ull;
-    }
-    __syncthreads();
-    block_sort_desc(sm.buf, P);
-    const int newn = total < k_eff ? total : k_eff;
-    for (int i = threadIdx.x; i < newn; i += kThreads) sm.list[i] = sm.buf[i];
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        sm.nlist = newn;
-        sm.thr = (newn == k_eff) ? sm.list[k_eff - 1] : 0ull;
-        sm.ncand = 0;
-    }
-    __syncthreads();
-}
+// Running top-64 of one wave.
+struct WaveTopk {
+    uint64_t lst;  // this lane's entry of the list (descending over lanes)
+    uint64_t thr;  // candidates need key > thr (same in every lane)
+    int cnt;       // keys waiting in the wave's buffer (same in every lane)
+};
 
-// Logit below which no key can exceed `thr` (the id decides on equality).
-__device__ __forceinline__ float thr_floor(uint64_t thr) {
-    return ((uint32_t)(thr >> 32) < 0x007FFFFFu) ? -INFINITY : key_logit(thr);
+// Merge up to 64 buffered candidates into the list.
+__device__ __forceinline__ void wt_flush(WaveTopk& st, uint64_t* cbuf, int k_eff) {
+    const int lane = lane_id();
+    wave_lds_sync();
+    const int take = st.cnt < kWave ? st.cnt : kWave;
+    const int left = st.cnt - take;
+    uint64_t c = lane < take ? cbuf[lane] : 0ull;
+    const uint64_t rest = lane < left ? cbuf[kWave + lane] : 0ull;
+    wave_lds_sync();
+    if (lane < left) cbuf[lane] = rest;
+    st.cnt = left;
+    c = wave_sort_desc(c);
+    st.lst = wave_merge_top(st.lst, c);
+    const uint64_t kth = __shfl(st.lst, k_eff - 1, kWave);
+    if (kth > st.thr) st.thr = kth;
 }
 
 template <int DT, bool kAligned>
-__device__ void rowpass_topk(const void* row, int64_t start, int64_t end, int k_eff,
-                             PartSlot* out) {
+__device__ void seg_topk(const void* row, int64_t start, int64_t end, int k_eff, RowpassSmem& sm,
+                         PartSlot* out) {
     using TS = TileShape<DT>;
-    __shared__ TopkSmem sm;
-    if (threadIdx.x == 0) {
-        sm.ncand = 0;
-        sm.nlist = 0;
-        sm.thr = 0ull;
-        sm.floor = 0ull;
-    }
-    __syncthreads();
-    float v[TS::kE];
-    for (int64_t t0 = start; t0 < end; t0 += TS::kTile) {
-        const bool full = (t0 + TS::kTile <= end);
-        const bool last = (t0 + TS::kTile >= end);
-        load_tile<DT, kAligned>(row, t0, end, full, v);
+    const int w = wave_id(), lane = lane_id();
+    uint64_t* cbuf = sm.cbuf[w];
+    WaveTopk st;
+    st.lst = 0ull;
+    st.thr = 0ull;
+    st.cnt = 0;
+    bool first = true;
+    stream_range<DT, kAligned>(row, start, end, [&](float (&v)[TS::kE], int64_t t0, bool full) {
         float vmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < TS::kE; i++) vmax = fmaxf(vmax, v[i]);
-        uint64_t own_thr;
-        if (t0 == start) {
-            // Lower bound for the segment's k-th key: in each wave, the k-th
-            // largest of the lanes' best keys is reached by k distinct
-            // elements, so the segment's k-th key is at least the largest of
-            // these per-wave values.  Keys below it are never candidates.
+        if (first) {
+            // The k-th largest of the lanes' best keys is reached by k
+            // distinct elements of this wave, so every key of the wave's
+            // top-k is at least that large.
+            first = false;
             uint64_t best = 0ull;
 #pragma unroll
             for (int i = 0; i < TS::kE; i++) {
-                const int64_t id = elem_id<DT>(t0, i);
-                if (id < end && v[i] == vmax && best == 0ull) best = make_key(v[i], (uint32_t)id);
+                const bool valid = full || elem_id<DT>(t0, i) < end;
+                if (best == 0ull && valid && v[i] == vmax)
+                    best = make_key(v[i], (uint32_t)elem_id<DT>(t0, i));
             }
-            const uint64_t sorted = wave_sort_desc(best);
-            const uint64_t theta = __shfl(sorted, k_eff - 1, kWave);
-            if (threadIdx.x % kWave == 0) sm.red[threadIdx.x / kWave] = theta;
-            __syncthreads();
-            uint64_t th = sm.red[0];
-#pragma unroll
-            for (int w = 1; w < kWaves; w++) th = sm.red[w] > th ? sm.red[w] : th;
-            own_thr = th > 0ull ? th - 1ull : 0ull;
-            __syncthreads();
-            if (threadIdx.x == 0) sm.floor = own_thr;
-        } else {
-            own_thr = sm.thr > sm.floor ? sm.thr : sm.floor;
+            const uint64_t th = __shfl(wave_sort_desc(best), k_eff - 1, kWave);
+            if (th > 0ull && th - 1ull > st.thr) st.thr = th - 1ull;
         }
-        uint32_t pend = 0u;
-        {
-            const float tf = thr_floor(own_thr);
-            if (vmax >= tf) {
+        if (__ballot(vmax >= thr_floor(st.thr)) == 0ull) return;
 #pragma unroll
-                for (int i = 0; i < TS::kE; i++) {
-                    const int64_t id = elem_id<DT>(t0, i);
-                    if (id < end && v[i] >= tf && make_key(v[i], (uint32_t)id) > own_thr)
-                        pend |= (1u << i);
-                }
+        for (int i = 0; i < TS::kE; i++) {
+            const int64_t id = elem_id<DT>(t0, i);
+            const bool valid = full || id < end;
+            const uint64_t key = make_key(v[i], (uint32_t)id);
+            const bool c = valid && v[i] >= thr_floor(st.thr) && key > st.thr;
+            const uint64_t mask = __ballot(c);
+            if (mask) {
+                const int off = st.cnt + __popcll(mask & lanemask_lt());
+                if (c) cbuf[off] = key;
+                st.cnt += __popcll(mask);
+                if (st.cnt >= kWave) wt_flush(st, cbuf, k_eff);
             }
         }
-        for (;;) {
-            const uint64_t thr = own_thr > sm.thr ? own_thr : sm.thr;
-            uint32_t keep = 0u;
-            if (pend) {
-                // static indices keep v[] in registers
+    });
+    if (st.cnt > 0) wt_flush(st, cbuf, k_eff);
+    sm.lists[w][lane] = st.lst;
+    __syncthreads();
+    if (w == 0) {
+        uint64_t acc = sm.lists[0][lane];
 #pragma unroll
-                for (int i = 0; i < TS::kE; i++) {
-                    if (!(pend & (1u << i))) continue;
-                    const uint64_t key = make_key(v[i], (uint32_t)elem_id<DT>(t0, i));
-                    if (key <= thr) continue;
-                    const int slot = atomicAdd(&sm.ncand, 1);
-                    if (slot < kCandCap)
-                        sm.buf[slot] = key;
-                    else
-                        keep |= (1u << i);
-                }
-            }
-            pend = keep;
-            __syncthreads();
-            const int nc = sm.ncand;
-            const bool over = nc > kCandCap;
-            if (nc > 0 && (over || last || nc >= kCandCap / 2)) topk_merge(sm, k_eff);
-            __syncthreads();
-            if (!over) break;
-        }
+        for (int j = 1; j < kWaves; j++) acc = wave_merge_top(acc, sm.lists[j][lane]);
+        out->keys[lane] = acc;
     }
-    if (sm.ncand > 0) topk_merge(sm, k_eff);
-    for (int i = threadIdx.x; i < kMaxTopK; i += kThreads)
-        out->keys[i] = (i < sm.nlist) ? sm.list[i] : 0ull;
 }
 
 template <int DT, bool kAligned>
-__device__ void rowpass_greedy(const void* row, int64_t start, int64_t end, PartSlot* out) {
+__device__ void seg_greedy(const void* row, int64_t start, int64_t end, RowpassSmem& sm,
+                           PartSlot* out) {
     using TS = TileShape<DT>;
-    __shared__ uint64_t red[kWaves];
-    float v[TS::kE];
     uint64_t best = 0ull;  // 0 = nothing seen yet
     float best_v = -INFINITY;
-    for (int64_t t0 = start; t0 < end; t0 += TS::kTile) {
-        const bool full = (t0 + TS::kTile <= end);
-        load_tile<DT, kAligned>(row, t0, end, full, v);
+    stream_range<DT, kAligned>(row, start, end, [&](float (&v)[TS::kE], int64_t t0, bool full) {
         float vmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < TS::kE; i++) vmax = fmaxf(vmax, v[i]);
         if (vmax > best_v || best == 0ull) {
-            // earliest valid element holding the tile maximum (ids ascend with i);
-            // on a tie with best_v the earlier tile's element already wins
+            // earliest valid element holding the tile maximum (ids ascend with
+            // i); on a tie with best_v the earlier tile's element already wins
             uint64_t cand = 0ull;
 #pragma unroll
             for (int i = 0; i < TS::kE; i++) {
-                const int64_t id = elem_id<DT>(t0, i);
-                if (cand == 0ull && id < end && v[i] == vmax) cand = make_key(v[i], (uint32_t)id);
+                const bool valid = full || elem_id<DT>(t0, i) < end;
+                if (cand == 0ull && valid && v[i] == vmax)
+                    cand = make_key(v[i], (uint32_t)elem_id<DT>(t0, i));
             }
             if (cand > best) {
                 best = cand;
                 best_v = vmax;
             }
         }
-    }
-    const uint64_t r = block_max_u64(best, red);
+    });
+    const uint64_t r = block_max_u64(best, sm.red);
     if (threadIdx.x == 0) out->keys[0] = r;
 }
 
 // (m, s) pairs: s = sum of exp((l - m) / T).  Combining is exact up to one
-// fp64 rounding per term; the fixed xor-tree keeps it deterministic.
+// fp64 rounding per term; fixed combination trees keep it deterministic.
 __device__ __forceinline__ void ms_combine(float& m, double& s, float m2, double s2, double invT) {
     const float mm = fmaxf(m, m2);
     if (mm == -INFINITY) {
@@ -191,20 +161,26 @@ __device__ __forceinline__ void ms_combine(float& m, double& s, float m2, double
     s = a + b;
 }
 
+__device__ __forceinline__ void wave_ms_combine(float& m, double& s, double invT) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        const float m2 = __shfl_xor(m, o, kWave);
+        const double s2 = __shfl_xor(s, o, kWave);
+        ms_combine(m, s, m2, s2, invT);
+    }
+}
+
 template <int DT, bool kAligned>
-__device__ void rowpass_full(const void* row, int64_t start, int64_t end, float T, PartSlot* out) {
+__device__ void seg_full(const void* row, int64_t start, int64_t end, float T, RowpassSmem& sm,
+                         PartSlot* out) {
     using TS = TileShape<DT>;
-    __shared__ float red_m[kWaves];
-    __shared__ double red_s[kWaves];
     const double invT = 1.0 / (double)T;
     float c = (float)(1.4426950408889634 / (double)T);
     c = fminf(c, 3.0e38f);
-    float v[TS::kE];
     float m = -INFINITY;
     double s = 0.0;
-    for (int64_t t0 = start; t0 < end; t0 += TS::kTile) {
-        const bool full = (t0 + TS::kTile <= end);
-        load_tile<DT, kAligned>(row, t0, end, full, v);
+    stream_range<DT, kAligned>(row, start, end, [&](float (&v)[TS::kE], int64_t, bool) {
+        // out-of-range elements read as -inf and add nothing
         float vmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < TS::kE; i++) vmax = fmaxf(vmax, v[i]);
@@ -218,23 +194,17 @@ __device__ void rowpass_full(const void* row, int64_t start, int64_t end, float 
             for (int i = 0; i < TS::kE; i++) acc[i & 3] += exp2f((v[i] - m) * c);
             s += (double)((acc[0] + acc[1]) + (acc[2] + acc[3]));
         }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float m2 = __shfl_xor(m, o, kWave);
-        const double s2 = __shfl_xor(s, o, kWave);
-        ms_combine(m, s, m2, s2, invT);
-    }
-    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-    if (lane == 0) {
-        red_m[w] = m;
-        red_s[w] = s;
+    });
+    wave_ms_combine(m, s, invT);
+    if (lane_id() == 0) {
+        sm.redm[wave_id()] = m;
+        sm.reds[wave_id()] = s;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        float mm = red_m[0];
-        double ss = red_s[0];
-        for (int i = 1; i < kWaves; i++) ms_combine(mm, ss, red_m[i], red_s[i], invT);
+        float mm = sm.redm[0];
+        double ss = sm.reds[0];
+        for (int i = 1; i < kWaves; i++) ms_combine(mm, ss, sm.redm[i], sm.reds[i], invT);
         FullStat* fs = reinterpret_cast<FullStat*>(out);
         fs->m = mm;
         fs->pad = 0.f;
@@ -242,38 +212,35 @@ __device__ void rowpass_full(const void* row, int64_t start, int64_t end, float 
     }
 }
 
-// grid.x = B * 2 * nseg; block -> (row b, side, segment).  side 0 = target
-// row k, side 1 = draft row k.  Rows not live at position k exit at once.
+// Grid-stride over the segments of position k's unit list; the record of
+// item it = (list index li, segment s) goes to parts[it] = parts[li*nseg + s].
 template <int DT, bool kAligned>
-__global__ __launch_bounds__(kThreads) void rowpass_kernel(
-    const void* __restrict__ target, const void* __restrict__ draft, int64_t t_stride,
-    int64_t d_stride, int K, int V, int k, int nseg, int tiles_per_seg,
-    const RowInfo* __restrict__ rows, PartSlot* __restrict__ parts) {
+__global__ __launch_bounds__(kThreads) void rowpass_kernel(StepArgs a, int k) {
     using TS = TileShape<DT>;
-    const int bid = blockIdx.x;
-    const int seg = bid % nseg;
-    const int side = (bid / nseg) & 1;
-    const int b = bid / (2 * nseg);
-    const RowInfo& ri = rows[b];
-    const int status = ri.status, L = ri.L, cls = ri.cls;
-    if (status != ST_LIVE || k > L) return;
-    if (side == 1 && (cls == CLS_GREEDY || k >= L)) return;
-    const char* base;
-    if (side == 0)
-        base = static_cast<const char*>(target) +
-               ((int64_t)b * (K + 1) + k) * t_stride * Elt<DT>::kSize;
-    else
-        base = static_cast<const char*>(draft) + ((int64_t)b * K + k) * d_stride * Elt<DT>::kSize;
-    const int64_t start = (int64_t)seg * tiles_per_seg * TS::kTile;
-    int64_t end = start + (int64_t)tiles_per_seg * TS::kTile;
-    if (end > V) end = V;
-    PartSlot* out = parts + ((int64_t)b * 2 + side) * nseg + seg;
-    if (cls == CLS_GREEDY)
-        rowpass_greedy<DT, kAligned>(base, start, end, out);
-    else if (cls == CLS_TOPK)
-        rowpass_topk<DT, kAligned>(base, start, end, ri.k_eff, out);
-    else
-        rowpass_full<DT, kAligned>(base, start, end, ri.T, out);
+    __shared__ RowpassSmem sm;
+    const int n = a.pos[k].n_units;
+    int nseg, tps;
+    seg_plan(n, a.ntiles, &nseg, &tps);
+    const int items = n * nseg;
+    const int32_t* list = a.ulist + (int64_t)k * 2 * a.B;
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const int li = it / nseg, seg = it - li * nseg;
+        const int u = list[li];
+        const int b = u >> 1, side = u & 1;
+        const int cls = a.rows[b].cls;
+        const void* row = unit_row<DT>(a, b, side, k);
+        const int64_t start = (int64_t)seg * tps * TS::kTile;
+        int64_t end = start + (int64_t)tps * TS::kTile;
+        if (end > a.V) end = a.V;
+        PartSlot* out = a.parts + it;
+        if (cls == CLS_GREEDY)
+            seg_greedy<DT, kAligned>(row, start, end, sm, out);
+        else if (cls == CLS_TOPK)
+            seg_topk<DT, kAligned>(row, start, end, a.rows[b].k_eff, sm, out);
+        else
+            seg_full<DT, kAligned>(row, start, end, a.rows[b].T, sm, out);
+        __syncthreads();  // LDS is reused by the next item
+    }
 }
 
 }  // namespace sv

@@ -6,14 +6,14 @@
 // all accepted draw the bonus token from p at position L.  The walk is in
 // ascending token id (the reading used throughout this library).
 //
-// Two steps:
-//   sample_sums_kernel  one workgroup per (row, chunk of one tile): the chunk's
+// Two steps over the list of rows that need such a draw:
+//   sample_sums_kernel  grid-stride over (row, chunk of one tile): the chunk's
 //                       residual mass and p mass, fp64, fixed reduction tree;
 //   sample_pick_kernel  one workgroup per row: running sum over the chunk
 //                       masses, then a block-wide fp64 prefix scan inside the
 //                       chosen chunk to find the token.
-// Terms use the same exp2 formulation as the row pass that produced the
-// normalisers, so (p - q)+ is formed from consistent p and q.
+// Untruncated rows use the same exp2 terms as the row pass that produced
+// their normalisers; nucleus rows use the exact cut masses.
 #pragma once
 
 #include "sv_decide.h"
@@ -25,9 +25,6 @@ __device__ __forceinline__ float exp2_coef(float T) {
     return fminf(c, 3.0e38f);
 }
 
-// Draw weights of token `id` for a row that ended at kpos: the residual
-// (p - q)+ and the target weight (unnormalised exp2 terms on untruncated rows,
-// exact cut masses over Z_S on nucleus rows).
 struct DrawCtx {
     bool nucleus, resid;
     float mt, md, c;
@@ -50,10 +47,14 @@ __device__ __forceinline__ DrawCtx draw_ctx(const RowInfo& ri) {
     return x;
 }
 
+// Draw weights of token `id`: the residual (p - q)+ and the target weight
+// (unnormalised exp2 terms on untruncated rows, exact cut masses over Z_S on
+// nucleus rows).
 __device__ __forceinline__ void draw_weights(const DrawCtx& x, float lt, float ld, uint32_t id,
                                              const double* ebk, double* wr, double* wp) {
     if (x.nucleus) {
-        const double p = (make_key(lt, id) >= x.tau_t) ? fn_weight(lt, x.mt, x.invT, ebk) / x.zt : 0.0;
+        const double p =
+            (make_key(lt, id) >= x.tau_t) ? fn_weight(lt, x.mt, x.invT, ebk) / x.zt : 0.0;
         *wp = p;
         if (x.resid) {
             const double q =
@@ -79,53 +80,65 @@ __device__ __forceinline__ void draw_weights(const DrawCtx& x, float lt, float l
 template <int DT, bool kAligned>
 __global__ __launch_bounds__(kThreads) void sample_sums_kernel(StepArgs a) {
     using TS = TileShape<DT>;
-    const int b = blockIdx.x / a.nch, ch = blockIdx.x % a.nch;
-    const RowInfo& ri = a.rows[b];
-    if (ri.status != ST_SAMPLE) return;
-    const int kpos = ri.kpos;
-    const DrawCtx x = draw_ctx(ri);
-    const char* trow = static_cast<const char*>(a.target) +
-                       ((int64_t)b * (a.K + 1) + kpos) * a.t_stride * Elt<DT>::kSize;
-    const char* drow = static_cast<const char*>(a.draft) +
-                       ((int64_t)b * a.K + kpos) * a.d_stride * Elt<DT>::kSize;
-    const int64_t start = (int64_t)ch * TS::kTile;
-    const int64_t end = (start + TS::kTile < a.V) ? start + TS::kTile : a.V;
-    const bool full = start + TS::kTile <= a.V;
-    float vt[TS::kE], vd[TS::kE];
-    load_tile<DT, kAligned>(trow, start, end, full, vt);
-    if (x.resid) load_tile<DT, kAligned>(drow, start, end, full, vd);
-    double sr = 0.0, sp = 0.0;
-#pragma unroll
-    for (int i = 0; i < TS::kE; i++) {
-        const int64_t id = elem_id<DT>(start, i);
-        if (id >= end) continue;
-        double wr, wp;
-        draw_weights(x, vt[i], x.resid ? vd[i] : 0.f, (uint32_t)id, a.ebk, &wr, &wp);
-        sr += wr;
-        sp += wp;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        sr += __shfl_xor(sr, o, kWave);
-        sp += __shfl_xor(sp, o, kWave);
-    }
     __shared__ double red[2][kWaves];
-    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-    if (lane == 0) {
-        red[0][w] = sr;
-        red[1][w] = sp;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        double r0 = 0.0, r1 = 0.0;
-        for (int i = 0; i < kWaves; i++) {
-            r0 += red[0][i];
-            r1 += red[1][i];
+    const int n = a.pos[a.K + 1].n_sample;
+    const int items = n * a.ntiles;
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const int si = it / a.ntiles, ch = it - si * a.ntiles;
+        const int b = a.slist[si];
+        const RowInfo& ri = a.rows[b];
+        const int kpos = ri.kpos;
+        const DrawCtx x = draw_ctx(ri);
+        const void* trow = unit_row<DT>(a, b, 0, kpos);
+        const void* drow = x.resid ? unit_row<DT>(a, b, 1, kpos) : nullptr;
+        const int64_t start = (int64_t)ch * TS::kTile;
+        const int64_t end = (start + TS::kTile < a.V) ? start + TS::kTile : a.V;
+        const bool full = start + TS::kTile <= a.V;
+        float vt[TS::kE], vd[TS::kE];
+        if (kAligned && full) {
+            RawTile r;
+            issue_tile<DT>(trow, start, r);
+            unpack_tile<DT>(r, vt);
+            if (x.resid) {
+                issue_tile<DT>(drow, start, r);
+                unpack_tile<DT>(r, vd);
+            }
+        } else {
+            load_tile_partial<DT>(trow, start, end, vt);
+            if (x.resid) load_tile_partial<DT>(drow, start, end, vd);
         }
-        double2 out;
-        out.x = r0;
-        out.y = r1;
-        a.chunks[(int64_t)b * a.nch + ch] = out;
+        double sr = 0.0, sp = 0.0;
+#pragma unroll
+        for (int i = 0; i < TS::kE; i++) {
+            const int64_t id = elem_id<DT>(start, i);
+            if (id >= end) continue;
+            double wr, wp;
+            draw_weights(x, vt[i], x.resid ? vd[i] : 0.f, (uint32_t)id, a.ebk, &wr, &wp);
+            sr += wr;
+            sp += wp;
+        }
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1) {
+            sr += __shfl_down(sr, o, kWave);
+            sp += __shfl_down(sp, o, kWave);
+        }
+        if (lane_id() == 0) {
+            red[0][wave_id()] = sr;
+            red[1][wave_id()] = sp;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double r0 = 0.0, r1 = 0.0;
+            for (int i = 0; i < kWaves; i++) {
+                r0 += red[0][i];
+                r1 += red[1][i];
+            }
+            double2 out;
+            out.x = r0;
+            out.y = r1;
+            a.chunks[(int64_t)b * a.ntiles + ch] = out;
+        }
+        __syncthreads();
     }
 }
 
@@ -133,143 +146,153 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void sample_pick_kernel(StepArgs a) {
     using TS = TileShape<DT>;
     constexpr int kE = TS::kE;
-    const int b = blockIdx.x;
-    const RowInfo ri = a.rows[b];
-    if (ri.status != ST_SAMPLE) return;
     __shared__ int s_chunk, s_use_r, s_best, s_last;
     __shared__ double s_base, s_W, s_target;
     __shared__ double s_tmp[kWaves];
     __shared__ double s_lo, s_hi, s_wy;
-    const bool resid = ri.need == NEED_RESID;
-    const double u = (double)a.uniforms[(int64_t)b * (a.K + 1) + a.K];
-    if (threadIdx.x == 0) {
-        const double2* cs = a.chunks + (int64_t)b * a.nch;
-        double Wr = 0.0, Wp = 0.0;
-        for (int c = 0; c < a.nch; c++) {
-            Wr += cs[c].x;
-            Wp += cs[c].y;
+    const int n = a.pos[a.K + 1].n_sample;
+    for (int si = blockIdx.x; si < n; si += gridDim.x) {
+        const int b = a.slist[si];
+        const RowInfo ri = a.rows[b];
+        const bool resid = ri.need == NEED_RESID;
+        const double u = (double)a.uniforms[(int64_t)b * (a.K + 1) + a.K];
+        if (threadIdx.x == 0) {
+            const double2* cs = a.chunks + (int64_t)b * a.ntiles;
+            double Wr = 0.0, Wp = 0.0;
+            for (int c = 0; c < a.ntiles; c++) {
+                Wr += cs[c].x;
+                Wp += cs[c].y;
+            }
+            const int use_r = resid && Wr > 0.0;
+            const double W = use_r ? Wr : Wp;
+            const double target = u * W;
+            double S = 0.0, base = 0.0;
+            int chosen = -1, last = -1;
+            double last_base = 0.0;
+            for (int c = 0; c < a.ntiles; c++) {
+                const double wc = use_r ? cs[c].x : cs[c].y;
+                if (!(wc > 0.0)) continue;
+                const double before = S;
+                S += wc;
+                last = c;
+                last_base = before;
+                if (target < S) {
+                    chosen = c;
+                    base = before;
+                    break;
+                }
+            }
+            if (chosen < 0) {
+                chosen = last;
+                base = last_base;
+            }
+            s_chunk = chosen;
+            s_use_r = use_r;
+            s_base = base;
+            s_W = W;
+            s_target = target;
+            s_best = 0x7FFFFFFF;
+            s_last = -1;
+            s_lo = s_hi = s_wy = 0.0;
         }
-        const int use_r = resid && Wr > 0.0;
-        const double W = use_r ? Wr : Wp;
-        const double target = u * W;
-        double S = 0.0, base = 0.0;
-        int chosen = -1, last = -1;
-        double last_base = 0.0;
-        for (int c = 0; c < a.nch; c++) {
-            const double wc = use_r ? cs[c].x : cs[c].y;
-            if (!(wc > 0.0)) continue;
+        __syncthreads();
+        if (s_chunk < 0) {  // no positive mass anywhere: only reachable on corrupt stats
+            if (threadIdx.x == 0) {
+                a.out_acc[b] = -1;
+                a.rows[b].status = ST_ERROR;
+            }
+            __syncthreads();
+            continue;
+        }
+        const int kpos = ri.kpos;
+        const DrawCtx x = draw_ctx(ri);
+        const bool use_r = s_use_r;
+        const void* trow = unit_row<DT>(a, b, 0, kpos);
+        const void* drow = x.resid ? unit_row<DT>(a, b, 1, kpos) : nullptr;
+        // thread t owns the contiguous run [start + t*kE, start + (t+1)*kE)
+        const int64_t cstart = (int64_t)s_chunk * TS::kTile;
+        const int64_t r0 = cstart + (int64_t)threadIdx.x * kE;
+        double w[kE];
+        double mine = 0.0;
+#pragma unroll
+        for (int i = 0; i < kE; i++) {
+            const int64_t id = r0 + i;
+            double wi = 0.0;
+            if (id < a.V && id < cstart + TS::kTile) {
+                double wr, wp;
+                draw_weights(x, load_one<DT>(trow, id), x.resid ? load_one<DT>(drow, id) : 0.f,
+                             (uint32_t)id, a.ebk, &wr, &wp);
+                wi = use_r ? wr : wp;
+            }
+            w[i] = wi;
+            mine += wi;
+        }
+        double total;
+        const double off = block_exclusive_scan(mine, s_tmp, &total);
+        const double target = s_target;
+        double S = s_base + off;
+        int found = -1;
+        double f_before = 0.0, f_after = 0.0, f_w = 0.0;
+        int lastpos = -1;
+        double l_before = 0.0, l_after = 0.0, l_w = 0.0;
+#pragma unroll
+        for (int i = 0; i < kE; i++) {
+            if (!(w[i] > 0.0)) continue;
             const double before = S;
-            S += wc;
-            last = c;
-            last_base = before;
-            if (target < S) {
-                chosen = c;
-                base = before;
-                break;
+            S += w[i];
+            lastpos = i;
+            l_before = before;
+            l_after = S;
+            l_w = w[i];
+            if (found < 0 && target < S) {
+                found = i;
+                f_before = before;
+                f_after = S;
+                f_w = w[i];
             }
         }
-        if (chosen < 0) {
-            chosen = last;
-            base = last_base;
+        if (found >= 0) atomicMin(&s_best, (int)(r0 + found));
+        // rounding can push the target past this chunk's own running sums;
+        // then the chunk's last positive-weight token is taken (margin 0)
+        if (lastpos >= 0) atomicMax(&s_last, (int)(r0 + lastpos));
+        __syncthreads();
+        const bool fallback = s_best == 0x7FFFFFFF;
+        const int y = fallback ? s_last : s_best;
+        if (!fallback && found >= 0 && (int)(r0 + found) == y) {
+            s_lo = f_before;
+            s_hi = f_after;
+            s_wy = f_w;
+        } else if (fallback && lastpos >= 0 && (int)(r0 + lastpos) == y) {
+            s_lo = l_before;
+            s_hi = l_after;
+            s_wy = l_w;
         }
-        s_chunk = chosen;
-        s_use_r = use_r;
-        s_base = base;
-        s_W = W;
-        s_target = target;
-        s_best = 0x7FFFFFFF;
-        s_last = -1;
-        s_lo = s_hi = s_wy = 0.0;
-    }
-    __syncthreads();
-    if (s_chunk < 0) {  // no positive mass anywhere: only reachable on corrupt stats
+        __syncthreads();
         if (threadIdx.x == 0) {
-            a.out_acc[b] = -1;
-            a.rows[b].status = ST_ERROR;
+            const double W = s_W;
+            if (a.diag) {
+                double* dg = a.diag + (int64_t)b * 4 * (a.K + 1) + 4 * a.K;
+                const double lo = s_lo / W, hi = s_hi / W;
+                const double d1 = u - lo, d2 = hi - u;
+                dg[0] = s_wy / W;
+                dg[1] = lo;
+                dg[2] = hi;
+                dg[3] = fallback ? 0.0 : (d1 < d2 ? d1 : d2);
+            }
+            if (y < 0) {
+                a.out_acc[b] = -1;
+                a.rows[b].status = ST_ERROR;
+            } else {
+                int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
+                const int32_t* t = a.tokens + (int64_t)b * a.K;
+                for (int j = 0; j < kpos; j++) o[j] = t[j];
+                o[kpos] = y;
+                a.out_acc[b] = kpos;
+                a.rows[b].acc = kpos;
+                a.rows[b].status = ST_DONE;
+            }
         }
-        return;
-    }
-    const int kpos = ri.kpos;
-    const DrawCtx x = draw_ctx(ri);
-    const bool use_r = s_use_r;
-    const char* trow = static_cast<const char*>(a.target) +
-                       ((int64_t)b * (a.K + 1) + kpos) * a.t_stride * Elt<DT>::kSize;
-    const char* drow = static_cast<const char*>(a.draft) +
-                       ((int64_t)b * a.K + kpos) * a.d_stride * Elt<DT>::kSize;
-    // thread t owns the contiguous run [start + t*kE, start + (t+1)*kE)
-    const int64_t cstart = (int64_t)s_chunk * TS::kTile;
-    const int64_t r0 = cstart + (int64_t)threadIdx.x * kE;
-    double w[kE];
-    double mine = 0.0;
-#pragma unroll
-    for (int i = 0; i < kE; i++) {
-        const int64_t id = r0 + i;
-        double wi = 0.0;
-        if (id < a.V && id < cstart + TS::kTile) {
-            double wr, wp;
-            draw_weights(x, load_one<DT>(trow, id), x.resid ? load_one<DT>(drow, id) : 0.f,
-                         (uint32_t)id, a.ebk, &wr, &wp);
-            wi = use_r ? wr : wp;
-        }
-        w[i] = wi;
-        mine += wi;
-    }
-    double total;
-    const double off = block_exclusive_scan(mine, s_tmp, &total);
-    const double target = s_target;
-    double S = s_base + off;
-    int found = -1;
-    double f_before = 0.0, f_after = 0.0, f_w = 0.0;
-    int lastpos = -1;
-    double l_before = 0.0, l_after = 0.0, l_w = 0.0;
-#pragma unroll
-    for (int i = 0; i < kE; i++) {
-        if (!(w[i] > 0.0)) continue;
-        const double before = S;
-        S += w[i];
-        lastpos = i;
-        l_before = before;
-        l_after = S;
-        l_w = w[i];
-        if (found < 0 && target < S) {
-            found = i;
-            f_before = before;
-            f_after = S;
-            f_w = w[i];
-        }
-    }
-    if (found >= 0) atomicMin(&s_best, (int)(r0 + found));
-    // rounding can push the target past this chunk's own running sums; then
-    // the chunk's last positive-weight token is taken (margin reported as 0)
-    if (lastpos >= 0) atomicMax(&s_last, (int)(r0 + lastpos));
-    __syncthreads();
-    const bool fallback = s_best == 0x7FFFFFFF;
-    const int y = fallback ? s_last : s_best;
-    if (!fallback && found >= 0 && (int)(r0 + found) == y) {
-        s_lo = f_before;
-        s_hi = f_after;
-        s_wy = f_w;
-    } else if (fallback && lastpos >= 0 && (int)(r0 + lastpos) == y) {
-        s_lo = l_before;
-        s_hi = l_after;
-        s_wy = l_w;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const double W = s_W;
-        if (a.diag) {
-            double* dg = a.diag + (int64_t)b * 4 * (a.K + 1) + 4 * a.K;
-            const double lo = s_lo / W, hi = s_hi / W;
-            const double d1 = u - lo, d2 = hi - u;
-            dg[0] = s_wy / W;
-            dg[1] = lo;
-            dg[2] = hi;
-            dg[3] = fallback ? 0.0 : (d1 < d2 ? d1 : d2);
-        }
-        if (y < 0)
-            a.rows[b].status = ST_ERROR;  // no positive weight: cannot happen for a chosen chunk
-        else
-            emit_row(a, b, kpos, y);
+        __syncthreads();
     }
 }
 
