@@ -82,11 +82,11 @@ __device__ __forceinline__ int first_lane(bool pred) {
     return m ? __ffsll((unsigned long long)m) - 1 : -1;
 }
 
-// Top-64 keys (descending, lane j = j-th) of one unit from its segments.
-__device__ __forceinline__ uint64_t unit_top(const PartSlot* parts, int li, int nseg) {
-    const PartSlot* s = parts + (int64_t)li * nseg;
+// Top-64 keys (descending, lane j = j-th) of one unit from its records.
+__device__ __forceinline__ uint64_t unit_top(const PartSlot* parts, RecRange r) {
+    const PartSlot* s = parts + r.first;
     uint64_t acc = s[0].keys[lane_id()];
-    for (int i = 1; i < nseg; i++) acc = wave_merge_top(acc, s[i].keys[lane_id()]);
+    for (int i = 1; i < r.count; i++) acc = wave_merge_top(acc, s[i].keys[lane_id()]);
     return acc;
 }
 
@@ -157,7 +157,7 @@ __device__ inline void queue_draw(const StepArgs& a, int b) {
     a.rows[b].status = ST_SAMPLE;
 }
 
-__device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, int nseg) {
+__device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, int n) {
     __shared__ double s_w[kWave];
     __shared__ double s_p[kWave];
     __shared__ int s_id[kWave];
@@ -165,7 +165,7 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
     const int k_eff = ri.k_eff;
     const double T = (double)ri.T, top_p = (double)ri.top_p;
     const bool has_draft = k < ri.L;
-    const uint64_t kt = unit_top(a.parts, ri.li_t, nseg);
+    const uint64_t kt = unit_top(a.parts, unit_records(ri.li_t, n, a.ntiles));
     double p;
     bool keep_p;
     if (!topk_dist_wave(kt, k_eff, T, top_p, &p, &keep_p)) {
@@ -178,7 +178,7 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
     bool keep_q = false;
     int id_q = -1;
     if (has_draft) {
-        const uint64_t kd = unit_top(a.parts, ri.li_d, nseg);
+        const uint64_t kd = unit_top(a.parts, unit_records(ri.li_d, n, a.ntiles));
         if (!topk_dist_wave(kd, k_eff, T, top_p, &q, &keep_q)) {
             close_row_invalid(a, b, -1);
             return;
@@ -255,11 +255,12 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
     }
 }
 
-__device__ void decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri, int nseg) {
+__device__ void decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri, int n) {
     const int lane = lane_id();
-    const PartSlot* s = a.parts + (int64_t)ri.li_t * nseg;
+    const RecRange r = unit_records(ri.li_t, n, a.ntiles);
+    const PartSlot* s = a.parts + r.first;
     uint64_t best = 0ull;
-    for (int i = lane; i < nseg; i += kWave) best = s[i].keys[0] > best ? s[i].keys[0] : best;
+    for (int i = lane; i < r.count; i += kWave) best = s[i].keys[0] > best ? s[i].keys[0] : best;
     best = wave_max_u64(best);
     const int g = (int)key_id(best);
     if (k < ri.L && a.tokens[(int64_t)b * a.K + k] == g) {
@@ -269,15 +270,15 @@ __device__ void decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri
     if (lane == 0) emit_row(a, b, k, g);
 }
 
-// {max, sum-exp} of one full-vocab unit from its segment records (lanes
-// combine in a fixed tree; lane 0's result is broadcast).
-__device__ inline void full_stats(const PartSlot* parts, int li, int nseg, double invT, double* m,
+// {max, sum-exp} of one full-vocab unit from its records (lanes combine in a
+// fixed tree; lane 0's result is broadcast).
+__device__ inline void full_stats(const PartSlot* parts, RecRange r, double invT, double* m,
                                   double* z) {
     const int lane = lane_id();
     float mm = -INFINITY;
     double ss = 0.0;
-    const PartSlot* s = parts + (int64_t)li * nseg;
-    for (int i = lane; i < nseg; i += kWave) {
+    const PartSlot* s = parts + r.first;
+    for (int i = lane; i < r.count; i += kWave) {
         const FullStat* fs = reinterpret_cast<const FullStat*>(s + i);
         ms_combine(mm, ss, fs->m, fs->s, invT);
     }
@@ -292,10 +293,10 @@ __device__ inline void full_stats(const PartSlot* parts, int li, int nseg, doubl
 }
 
 template <int DT>
-__device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri, int nseg) {
+__device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri, int n) {
     const double T = (double)ri.T, invT = 1.0 / T;
     double mt, zt, md = 0.0, zd = 0.0;
-    full_stats(a.parts, ri.li_t, nseg, invT, &mt, &zt);
+    full_stats(a.parts, unit_records(ri.li_t, n, a.ntiles), invT, &mt, &zt);
     if (!(mt > -INFINITY)) {
         close_row_invalid(a, b, -1);
         return;
@@ -311,7 +312,7 @@ __device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri, 
         }
         return;
     }
-    full_stats(a.parts, ri.li_d, nseg, invT, &md, &zd);
+    full_stats(a.parts, unit_records(ri.li_d, n, a.ntiles), invT, &md, &zd);
     if (!(md > -INFINITY)) {
         close_row_invalid(a, b, -1);
         return;
@@ -398,16 +399,15 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepArgs a, int 
     const int b = blockIdx.x;
     const RowInfo ri = a.rows[b];
     if (ri.status != ST_LIVE || k > ri.L) return;
-    int nseg, tps;
-    seg_plan(a.pos[k].n_units, a.ntiles, &nseg, &tps);
+    const int n = a.pos[k].n_units;
     if (ri.cls == CLS_GREEDY)
-        decide_greedy(a, b, k, ri, nseg);
+        decide_greedy(a, b, k, ri, n);
     else if (ri.cls == CLS_TOPK)
-        decide_topk(a, b, k, ri, nseg);
+        decide_topk(a, b, k, ri, n);
     else if (ri.cls == CLS_NUCLEUS)
         decide_nucleus<DT>(a, b, k, ri);
     else
-        decide_full<DT>(a, b, k, ri, nseg);
+        decide_full<DT>(a, b, k, ri, n);
 }
 
 // Zero the work counters and write the e^(-b/32) table (once per call).

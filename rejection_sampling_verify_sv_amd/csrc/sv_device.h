@@ -8,10 +8,9 @@
 //     tiles are double-buffered, so two tiles per workgroup are in flight;
 //   * a "unit" is one logits row to stream: (batch row b, side), side 0 = the
 //     target row, side 1 = the draft row of the current position;
-//   * a "segment" is a run of whole tiles of one unit handled by one workgroup.
-//     Units live at a position are listed on the device; the number of
-//     segments per unit is chosen from that count so every position keeps the
-//     256 compute units busy even after most rows have stopped.
+//   * units live at a position are listed on the device, and their tiles are
+//     split evenly over a fixed grid of workgroups, so every position keeps the
+//     256 compute units equally busy even after most rows have stopped.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -26,9 +25,7 @@ constexpr int kWave = 64;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxTopK = SV_MAX_TOP_K;
 constexpr int kLoads = 4;          // 16-byte loads per thread per tile
-constexpr int kGrid = 2048;        // workgroups of a streaming launch (grid-stride)
-constexpr int kTargetItems = 4096; // segments wanted per streaming launch
-constexpr int kMaxSeg = 64;        // segments per unit (decide merges <= 64 lists)
+constexpr int kGrid = 1024;        // workgroups of a streaming launch (4 per CU)
 constexpr int kCandBuf = 128;      // per-wave candidate buffer (top-k select)
 
 enum RowClass : int32_t {
@@ -235,7 +232,9 @@ __device__ __forceinline__ void unpack_tile(const RawTile& r, float (&v)[TileSha
     }
 }
 
-// Element-wise load of a tile; elements at or past `end` read as -inf.
+// Element-wise load of a tile; elements at or past `end` read as -inf.  The
+// index is clamped instead of branched on, so every load is issued before the
+// first wait.  Requires start < end.
 template <int DT>
 __device__ __forceinline__ void load_tile_partial(const void* row, int64_t start, int64_t end,
                                                   float (&v)[TileShape<DT>::kE]) {
@@ -245,7 +244,50 @@ __device__ __forceinline__ void load_tile_partial(const void* row, int64_t start
 #pragma unroll
         for (int e = 0; e < kVec; e++) {
             const int64_t i = start + (int64_t)(j * kThreads + (int)threadIdx.x) * kVec + e;
-            v[j * kVec + e] = (i < end) ? load_one<DT>(row, i) : -INFINITY;
+            const float x = load_one<DT>(row, i < end ? i : end - 1);
+            v[j * kVec + e] = i < end ? x : -INFINITY;
+        }
+    }
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw, stride 0): loads past
+// the end return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Last, partial tile of a 16-byte aligned row: whole vectors below `end` come
+// in with 16-byte buffer loads (range-checked, so nothing past the last whole
+// vector is read), the few elements of a vector that straddles `end` one by
+// one; elements at or past `end` read as -inf.  Requires start < end <=
+// start + tile.
+template <int DT>
+__device__ __forceinline__ void load_tile_tail(const void* row, int64_t start, int64_t end,
+                                               float (&v)[TileShape<DT>::kE]) {
+    constexpr int kVec = Elt<DT>::kVec;
+    const int n = (int)(end - start);
+    const int nvec = n / kVec;
+    const char* base = static_cast<const char*>(row) + start * Elt<DT>::kSize;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (uint32_t)nvec * 16u);
+    RawTile r;
+#pragma unroll
+    for (int j = 0; j < kLoads; j++)
+        r.q[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (j * kThreads + (int)threadIdx.x) * 16,
+                                                      0, 2 /* nt */);
+    unpack_tile<DT>(r, v);
+#pragma unroll
+    for (int j = 0; j < kLoads; j++) {
+        const int vi = j * kThreads + (int)threadIdx.x;
+#pragma unroll
+        for (int e = 0; e < kVec; e++) {
+            const int i = vi * kVec + e;
+            if (i >= n) v[j * kVec + e] = -INFINITY;
+        }
+        if (vi == nvec && nvec * kVec < n) {  // the straddling vector
+#pragma unroll
+            for (int e = 0; e < kVec; e++)
+                if (vi * kVec + e < n) v[j * kVec + e] = load_one<DT>(row, start + vi * kVec + e);
         }
     }
 }
@@ -261,9 +303,11 @@ __device__ __forceinline__ int64_t elem_id(int64_t start, int idx) {
 
 // Stream the elements [start, end) of a row (start tile-aligned) through
 // body(v, t0, full).  Full tiles are double-buffered: the loads of tile t+1
-// are in flight while tile t is processed.  The ragged tail, and every tile
-// of a row that is not 16-byte aligned, is loaded element by element.
-// `body` must not contain workgroup barriers (they would drain the loads).
+// are in flight while tile t is processed, and the compiler's wait before a
+// tile is used only drains the older of the two buffers.  The ragged tail of
+// an aligned row comes in through range-checked buffer loads; every tile of a
+// row that is not 16-byte aligned is loaded element by element.  `body` must not contain workgroup barriers (they would
+// drain the loads).
 template <int DT, bool kAligned, class Body>
 __device__ __forceinline__ void stream_range(const void* row, int64_t start, int64_t end,
                                              Body&& body) {
@@ -273,43 +317,132 @@ __device__ __forceinline__ void stream_range(const void* row, int64_t start, int
     if constexpr (kAligned) {
         const int64_t full_end = start + ((end - start) / TS::kTile) * TS::kTile;
         if (t0 < full_end) {
+            // Counted pairs with a single exit keep the loop free of dead
+            // back edges, which would otherwise force a full drain of the
+            // outstanding loads at the loop head.  After an even count the
+            // last prefetch re-reads the final tile and is dropped.
+            const int64_t nt = (full_end - t0) / TS::kTile;
+            const int64_t last = full_end - TS::kTile;
             RawTile A, B;
             issue_tile<DT>(row, t0, A);
-            while (true) {
-                const bool moreB = t0 + TS::kTile < full_end;
-                if (moreB) issue_tile<DT>(row, t0 + TS::kTile, B);
+            for (int64_t p = nt >> 1; p > 0; --p) {
+                issue_tile<DT>(row, t0 + TS::kTile, B);
+                __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the wait
+                unpack_tile<DT>(A, v);
+                body(v, t0, true);
+                const int64_t tn = t0 + 2 * TS::kTile;
+                issue_tile<DT>(row, tn <= last ? tn : last, A);
+                __builtin_amdgcn_sched_barrier(0);
+                unpack_tile<DT>(B, v);
+                body(v, t0 + TS::kTile, true);
+                t0 += 2 * TS::kTile;
+            }
+            if (nt & 1) {
                 unpack_tile<DT>(A, v);
                 body(v, t0, true);
                 t0 += TS::kTile;
-                if (!moreB) break;
-                const bool moreA = t0 + TS::kTile < full_end;
-                if (moreA) issue_tile<DT>(row, t0 + TS::kTile, A);
-                unpack_tile<DT>(B, v);
-                body(v, t0, true);
-                t0 += TS::kTile;
-                if (!moreA) break;
             }
         }
     }
     while (t0 < end) {
-        load_tile_partial<DT>(row, t0, end, v);
+        if constexpr (kAligned)
+            load_tile_tail<DT>(row, t0, end, v);
+        else
+            load_tile_partial<DT>(row, t0, end, v);
         body(v, t0, t0 + TS::kTile <= end);
         t0 += TS::kTile;
     }
 }
 
-// ---- segmentation of a position's units ----------------------------------
-// nseg segments of tps tiles per unit, chosen from the number of units so a
-// launch has about kTargetItems segments.  Every kernel that touches the
-// segments of a list derives them from the same count with this function.
-__host__ __device__ __forceinline__ void seg_plan(int n_units, int ntiles, int* nseg, int* tps) {
-    int s = n_units > 0 ? kTargetItems / n_units : 1;
-    const int cap = ntiles < kMaxSeg ? ntiles : kMaxSeg;
-    if (s > cap) s = cap;
-    if (s < 1) s = 1;
-    const int t = (ntiles + s - 1) / s;
-    *tps = t;
-    *nseg = (ntiles + t - 1) / t;
+// Same as stream_range over two rows in lockstep (the second may be null):
+// body(va, vb, t0, full); vb is all -inf when rb is null.
+template <int DT, bool kAligned, class Body>
+__device__ __forceinline__ void stream_range2(const void* ra, const void* rb, int64_t start,
+                                              int64_t end, Body&& body) {
+    using TS = TileShape<DT>;
+    float va[TS::kE], vb[TS::kE];
+#pragma unroll
+    for (int i = 0; i < TS::kE; i++) vb[i] = -INFINITY;
+    int64_t t0 = start;
+    const void* rb2 = rb ? rb : ra;  // loads stay unconditional; vb is ignored then
+    if constexpr (kAligned) {
+        const int64_t full_end = start + ((end - start) / TS::kTile) * TS::kTile;
+        if (t0 < full_end) {
+            const int64_t nt = (full_end - t0) / TS::kTile;
+            const int64_t last = full_end - TS::kTile;
+            RawTile A, A2, B, B2;
+            issue_tile<DT>(ra, t0, A);
+            issue_tile<DT>(rb2, t0, A2);
+            for (int64_t p = nt >> 1; p > 0; --p) {
+                issue_tile<DT>(ra, t0 + TS::kTile, B);
+                issue_tile<DT>(rb2, t0 + TS::kTile, B2);
+                __builtin_amdgcn_sched_barrier(0);
+                unpack_tile<DT>(A, va);
+                if (rb) unpack_tile<DT>(A2, vb);
+                body(va, vb, t0, true);
+                const int64_t tn = t0 + 2 * TS::kTile;
+                issue_tile<DT>(ra, tn <= last ? tn : last, A);
+                issue_tile<DT>(rb2, tn <= last ? tn : last, A2);
+                __builtin_amdgcn_sched_barrier(0);
+                unpack_tile<DT>(B, va);
+                if (rb) unpack_tile<DT>(B2, vb);
+                body(va, vb, t0 + TS::kTile, true);
+                t0 += 2 * TS::kTile;
+            }
+            if (nt & 1) {
+                unpack_tile<DT>(A, va);
+                if (rb) unpack_tile<DT>(A2, vb);
+                body(va, vb, t0, true);
+                t0 += TS::kTile;
+            }
+        }
+    }
+    while (t0 < end) {
+        if constexpr (kAligned) {
+            load_tile_tail<DT>(ra, t0, end, va);
+            if (rb) load_tile_tail<DT>(rb, t0, end, vb);
+        } else {
+            load_tile_partial<DT>(ra, t0, end, va);
+            if (rb) load_tile_partial<DT>(rb, t0, end, vb);
+        }
+        body(va, vb, t0, t0 + TS::kTile <= end);
+        t0 += TS::kTile;
+    }
+}
+
+// ---- even split of a list's tiles over the workgroups ----------------------
+// The n units of a list are laid end to end, ntiles tiles each, and
+// workgroup w of G streams tiles [w*T/G, (w+1)*T/G) of that concatenation
+// (T = n*ntiles), so every workgroup reads the same amount.  A workgroup can
+// cover the end of one unit and the start of the next; it leaves one record
+// per (unit u, workgroup w) piece, at slot u + w (unique because both grow
+// along the concatenation), so n + G slots suffice.
+// Only min(G, T) workgroups take part, so every taking part owns a tile.
+__host__ __device__ __forceinline__ int flat_active(int64_t T, int G) {
+    return (int)(T < (int64_t)G ? T : (int64_t)G);
+}
+__host__ __device__ __forceinline__ int64_t flat_begin(int64_t T, int G, int w) {
+    const int Ga = flat_active(T, G);
+    return w < Ga ? ((int64_t)w * T) / Ga : T;
+}
+// Workgroup that streams tile t (0 <= t < T).
+__host__ __device__ __forceinline__ int flat_owner(int64_t t, int64_t T, int G) {
+    const int Ga = flat_active(T, G);
+    return (int)(((t + 1) * (int64_t)Ga - 1) / T);
+}
+
+// Record slots [first, first + count) of unit li of a list of n units.
+struct RecRange {
+    int first, count;
+};
+__device__ __forceinline__ RecRange unit_records(int li, int n, int ntiles) {
+    const int64_t T = (int64_t)n * ntiles;
+    const int w0 = flat_owner((int64_t)li * ntiles, T, kGrid);
+    const int w1 = flat_owner((int64_t)(li + 1) * ntiles - 1, T, kGrid);
+    RecRange r;
+    r.first = li + w0;
+    r.count = w1 - w0 + 1;
+    return r;
 }
 
 // ---- wave / block helpers -------------------------------------------------
@@ -435,8 +568,8 @@ struct StepArgs {
     const int32_t* tokens;
     const float* uniforms;
     RowInfo* rows;
-    PartSlot* parts;       // segment records of the current position
-    double2* chunks;       // [B][ntiles] draw masses (one chunk = one tile)
+    PartSlot* parts;       // piece records of the current position (slot u + w)
+    double2* chunks;       // [B][ntiles][kWaves] draw masses (one chunk = one tile)
     int32_t* out_tokens;
     int32_t* out_acc;
     double* diag;

@@ -23,8 +23,9 @@
 //           tokens while the preceding mass is below top_p * Z.  The cut key
 //           tau (last kept token) and the kept mass Z_S define the
 //           distribution: p(i) = [key_i >= tau] w_i / Z_S.
-// The streaming passes walk position k's list of nucleus units in segments,
-// like the row pass; the per-unit steps run one workgroup per unit.
+// The streaming passes split the tiles of position k's nucleus units evenly
+// over the workgroups, like the row pass; the per-unit steps run one
+// workgroup per unit.
 #pragma once
 
 #include "sv_decide.h"
@@ -40,12 +41,11 @@ struct FnWork {
 
 // Row max of unit (b, side) at position k from its row-pass records.
 __device__ inline float unit_max(const StepArgs& a, int b, int side, int k) {
-    int nseg, tps;
-    seg_plan(a.pos[k].n_units, a.ntiles, &nseg, &tps);
     const int li = side == 0 ? a.rows[b].li_t : a.rows[b].li_d;
-    const PartSlot* slots = a.parts + (int64_t)li * nseg;
+    const RecRange r = unit_records(li, a.pos[k].n_units, a.ntiles);
     float m = -INFINITY;
-    for (int s = 0; s < nseg; s++) m = fmaxf(m, reinterpret_cast<const FullStat*>(slots + s)->m);
+    for (int s = 0; s < r.count; s++)
+        m = fmaxf(m, reinterpret_cast<const FullStat*>(a.parts + r.first + s)->m);
     return m;
 }
 
@@ -68,13 +68,15 @@ __global__ __launch_bounds__(kThreads) void fn_hist_kernel(StepArgs a, FnWork w,
     __shared__ uint64_t s_hi[kNB];
     __shared__ uint64_t s_lo[kNB];
     __shared__ uint32_t s_cnt[kNB];
-    const int n = a.pos[k].n_fn;
-    int nseg, tps;
-    seg_plan(n, a.ntiles, &nseg, &tps);
-    const int items = n * nseg;
+    const int64_t T = (int64_t)a.pos[k].n_fn * a.ntiles;
+    int64_t t = flat_begin(T, gridDim.x, blockIdx.x);
+    const int64_t t_end = flat_begin(T, gridDim.x, blockIdx.x + 1);
     const int32_t* list = a.flist + (int64_t)k * 2 * a.B;
-    for (int it = blockIdx.x; it < items; it += gridDim.x) {
-        const int li = it / nseg, seg = it - li * nseg;
+    while (t < t_end) {
+        const int li = (int)(t / a.ntiles);
+        const int64_t tu0 = t - (int64_t)li * a.ntiles;
+        int64_t tu1 = tu0 + (t_end - t);
+        if (tu1 > a.ntiles) tu1 = a.ntiles;
         const int u = list[li];
         const int b = u >> 1, side = u & 1;
         for (int i = threadIdx.x; i < kNB; i += kThreads) {
@@ -85,8 +87,8 @@ __global__ __launch_bounds__(kThreads) void fn_hist_kernel(StepArgs a, FnWork w,
         __syncthreads();
         const float m = unit_max(a, b, side, k);
         const double invT = 1.0 / (double)a.rows[b].T;
-        const int64_t start = (int64_t)seg * tps * TS::kTile;
-        int64_t end = start + (int64_t)tps * TS::kTile;
+        const int64_t start = tu0 * TS::kTile;
+        int64_t end = tu1 * TS::kTile;
         if (end > a.V) end = a.V;
         stream_range<DT, kAligned>(unit_row<DT>(a, b, side, k), start, end,
                                    [&](float (&v)[TS::kE], int64_t t0, bool full) {
@@ -112,6 +114,7 @@ __global__ __launch_bounds__(kThreads) void fn_hist_kernel(StepArgs a, FnWork w,
                       (unsigned long long)s_lo[i]);
             atomicAdd(&w.cnt[(int64_t)u * kNB + i], s_cnt[i]);
         }
+        t += tu1 - tu0;
         __syncthreads();
     }
 }
@@ -176,13 +179,16 @@ __global__ __launch_bounds__(kThreads) void fn_select_kernel(StepArgs a, FnWork 
 template <int DT, bool kAligned>
 __global__ __launch_bounds__(kThreads) void fn_collect_kernel(StepArgs a, FnWork w, int k) {
     using TS = TileShape<DT>;
-    const int n = a.pos[k].n_fn;
-    int nseg, tps;
-    seg_plan(n, a.ntiles, &nseg, &tps);
-    const int items = n * nseg;
+    const int64_t T = (int64_t)a.pos[k].n_fn * a.ntiles;
+    int64_t t = flat_begin(T, gridDim.x, blockIdx.x);
+    const int64_t t_end = flat_begin(T, gridDim.x, blockIdx.x + 1);
     const int32_t* list = a.flist + (int64_t)k * 2 * a.B;
-    for (int it = blockIdx.x; it < items; it += gridDim.x) {
-        const int li = it / nseg, seg = it - li * nseg;
+    while (t < t_end) {
+        const int li = (int)(t / a.ntiles);
+        const int64_t tu0 = t - (int64_t)li * a.ntiles;
+        int64_t tu1 = tu0 + (t_end - t);
+        if (tu1 > a.ntiles) tu1 = a.ntiles;
+        t += tu1 - tu0;
         const int u = list[li];
         const int b = u >> 1, side = u & 1;
         FnUnit* fu = a.fn_unit + u;
@@ -190,8 +196,8 @@ __global__ __launch_bounds__(kThreads) void fn_collect_kernel(StepArgs a, FnWork
         const int beta = fu->beta;
         const float m = fu->m;
         const double invT = 1.0 / (double)a.rows[b].T;
-        const int64_t start = (int64_t)seg * tps * TS::kTile;
-        int64_t end = start + (int64_t)tps * TS::kTile;
+        const int64_t start = tu0 * TS::kTile;
+        int64_t end = tu1 * TS::kTile;
         if (end > a.V) end = a.V;
         uint64_t* coll = w.coll + (int64_t)u * kCollectCap;
         stream_range<DT, kAligned>(unit_row<DT>(a, b, side, k), start, end,
@@ -234,28 +240,42 @@ __global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, FnWork
             const float m = fu->m;
             const double target = (double)a.rows[b].top_p * fu->Z;
             const double Mabove = fu->Mabove;
-            // thread t owns sorted positions [t*per, (t+1)*per)
-            const int per = (n + kThreads - 1) / kThreads;
-            const int j0 = threadIdx.x * per;
+            // every collected token sits in the boundary bucket: w = e^(-beta/32) e^(-d)
+            const double eb = a.ebk[fu->beta];
+            // thread t owns sorted positions [t*kPer, (t+1)*kPer)
+            constexpr int kPer = kCollectCap / kThreads;
+            const int j0 = threadIdx.x * kPer;
+            double wv[kPer];
             double mine = 0.0;
-            for (int j = j0; j < j0 + per && j < n; j++)
-                mine += fn_weight(key_logit(s_key[j]), m, invT, a.ebk);
+#pragma unroll
+            for (int q = 0; q < kPer; q++) {
+                double d;
+                const int j = j0 + q;
+                wv[q] = 0.0;
+                if (j < n) {
+                    (void)fn_bucket(key_logit(s_key[j]), m, invT, &d);
+                    wv[q] = eb * exp_neg_small(d);
+                }
+                mine += wv[q];
+            }
             double tot;
             const double excl = block_exclusive_scan(mine, s_tmp, &tot);
             if (threadIdx.x == 0) s_keep = 0;
             __syncthreads();
             double cum = Mabove + excl;
             int keep_here = 0;
-            for (int j = j0; j < j0 + per && j < n; j++) {
-                if (cum < target) keep_here = j + 1;
-                cum += fn_weight(key_logit(s_key[j]), m, invT, a.ebk);
+#pragma unroll
+            for (int q = 0; q < kPer; q++) {
+                if (j0 + q < n && cum < target) keep_here = j0 + q + 1;
+                cum += wv[q];
             }
             if (keep_here > 0) atomicMax(&s_keep, keep_here);
             __syncthreads();
             const int nk = s_keep;  // >= 1: the first token's preceding mass is below target
             double kept = 0.0;
-            for (int j = j0; j < j0 + per && j < nk; j++)
-                kept += fn_weight(key_logit(s_key[j]), m, invT, a.ebk);
+#pragma unroll
+            for (int q = 0; q < kPer; q++)
+                if (j0 + q < nk) kept += wv[q];
             double ktot;
             (void)block_exclusive_scan(kept, s_tmp, &ktot);
             if (threadIdx.x == 0) {

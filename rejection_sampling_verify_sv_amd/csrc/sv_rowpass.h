@@ -1,8 +1,8 @@
 // sv_rowpass.h — the streaming pass over logits rows (the HBM-bound step).
 //
-// A grid-stride loop walks the segments of the units live at position k.
-// One workgroup reads one segment exactly once, in 16-byte coalesced,
-// double-buffered vectors, and leaves a small record:
+// The workgroups split the tiles of the units live at position k evenly.
+// A workgroup reads its tiles exactly once, in 16-byte coalesced,
+// double-buffered vectors, and leaves one small record per unit it touches:
 //   * greedy rows:   the best (logit, lowest id) key of the segment;
 //   * top-k rows:    the segment's best 64 keys, descending (k <= 64);
 //   * full-vocab:    {segment max m, sum of exp((l - m) / T)} (online).
@@ -60,7 +60,7 @@ __device__ __forceinline__ void wt_flush(WaveTopk& st, uint64_t* cbuf, int k_eff
 }
 
 template <int DT, bool kAligned>
-__device__ void seg_topk(const void* row, int64_t start, int64_t end, int k_eff, RowpassSmem& sm,
+__device__ __forceinline__ void seg_topk(const void* row, int64_t start, int64_t end, int k_eff, RowpassSmem& sm,
                          PartSlot* out) {
     using TS = TileShape<DT>;
     const int w = wave_id(), lane = lane_id();
@@ -70,7 +70,7 @@ __device__ void seg_topk(const void* row, int64_t start, int64_t end, int k_eff,
     st.thr = 0ull;
     st.cnt = 0;
     bool first = true;
-    stream_range<DT, kAligned>(row, start, end, [&](float (&v)[TS::kE], int64_t t0, bool full) {
+    stream_range<DT, kAligned>(row, start, end, [&](float (&v)[TS::kE], int64_t t0, bool full) __attribute__((always_inline)) {
         float vmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < TS::kE; i++) vmax = fmaxf(vmax, v[i]);
@@ -117,12 +117,12 @@ __device__ void seg_topk(const void* row, int64_t start, int64_t end, int k_eff,
 }
 
 template <int DT, bool kAligned>
-__device__ void seg_greedy(const void* row, int64_t start, int64_t end, RowpassSmem& sm,
+__device__ __forceinline__ void seg_greedy(const void* row, int64_t start, int64_t end, RowpassSmem& sm,
                            PartSlot* out) {
     using TS = TileShape<DT>;
     uint64_t best = 0ull;  // 0 = nothing seen yet
     float best_v = -INFINITY;
-    stream_range<DT, kAligned>(row, start, end, [&](float (&v)[TS::kE], int64_t t0, bool full) {
+    stream_range<DT, kAligned>(row, start, end, [&](float (&v)[TS::kE], int64_t t0, bool full) __attribute__((always_inline)) {
         float vmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < TS::kE; i++) vmax = fmaxf(vmax, v[i]);
@@ -171,7 +171,7 @@ __device__ __forceinline__ void wave_ms_combine(float& m, double& s, double invT
 }
 
 template <int DT, bool kAligned>
-__device__ void seg_full(const void* row, int64_t start, int64_t end, float T, RowpassSmem& sm,
+__device__ __forceinline__ void seg_full(const void* row, int64_t start, int64_t end, float T, RowpassSmem& sm,
                          PartSlot* out) {
     using TS = TileShape<DT>;
     const double invT = 1.0 / (double)T;
@@ -179,7 +179,7 @@ __device__ void seg_full(const void* row, int64_t start, int64_t end, float T, R
     c = fminf(c, 3.0e38f);
     float m = -INFINITY;
     double s = 0.0;
-    stream_range<DT, kAligned>(row, start, end, [&](float (&v)[TS::kE], int64_t, bool) {
+    stream_range<DT, kAligned>(row, start, end, [&](float (&v)[TS::kE], int64_t, bool) __attribute__((always_inline)) {
         // out-of-range elements read as -inf and add nothing
         float vmax = -INFINITY;
 #pragma unroll
@@ -212,34 +212,40 @@ __device__ void seg_full(const void* row, int64_t start, int64_t end, float T, R
     }
 }
 
-// Grid-stride over the segments of position k's unit list; the record of
-// item it = (list index li, segment s) goes to parts[it] = parts[li*nseg + s].
+// The workgroups split the tiles of position k's units evenly (see
+// flat_begin); each (unit, workgroup) piece leaves its record at slot
+// li + blockIdx.x.
 template <int DT, bool kAligned>
 __global__ __launch_bounds__(kThreads) void rowpass_kernel(StepArgs a, int k) {
     using TS = TileShape<DT>;
     __shared__ RowpassSmem sm;
     const int n = a.pos[k].n_units;
-    int nseg, tps;
-    seg_plan(n, a.ntiles, &nseg, &tps);
-    const int items = n * nseg;
+    const int64_t T = (int64_t)n * a.ntiles;
+    const int w = blockIdx.x;
+    int64_t t = flat_begin(T, gridDim.x, w);
+    const int64_t t_end = flat_begin(T, gridDim.x, w + 1);
     const int32_t* list = a.ulist + (int64_t)k * 2 * a.B;
-    for (int it = blockIdx.x; it < items; it += gridDim.x) {
-        const int li = it / nseg, seg = it - li * nseg;
+    while (t < t_end) {
+        const int li = (int)(t / a.ntiles);
+        const int64_t tu0 = t - (int64_t)li * a.ntiles;
+        int64_t tu1 = tu0 + (t_end - t);
+        if (tu1 > a.ntiles) tu1 = a.ntiles;
         const int u = list[li];
         const int b = u >> 1, side = u & 1;
         const int cls = a.rows[b].cls;
         const void* row = unit_row<DT>(a, b, side, k);
-        const int64_t start = (int64_t)seg * tps * TS::kTile;
-        int64_t end = start + (int64_t)tps * TS::kTile;
+        const int64_t start = tu0 * TS::kTile;
+        int64_t end = tu1 * TS::kTile;
         if (end > a.V) end = a.V;
-        PartSlot* out = a.parts + it;
+        PartSlot* out = a.parts + li + w;
         if (cls == CLS_GREEDY)
             seg_greedy<DT, kAligned>(row, start, end, sm, out);
         else if (cls == CLS_TOPK)
             seg_topk<DT, kAligned>(row, start, end, a.rows[b].k_eff, sm, out);
         else
             seg_full<DT, kAligned>(row, start, end, a.rows[b].T, sm, out);
-        __syncthreads();  // LDS is reused by the next item
+        t += tu1 - tu0;
+        __syncthreads();  // LDS is reused by the next piece
     }
 }
 

@@ -7,8 +7,9 @@
 // ascending token id (the reading used throughout this library).
 //
 // Two steps over the list of rows that need such a draw:
-//   sample_sums_kernel  grid-stride over (row, chunk of one tile): the chunk's
-//                       residual mass and p mass, fp64, fixed reduction tree;
+//   sample_sums_kernel  the tiles of those rows split evenly over the grid:
+//                       each tile's residual mass and p mass, fp64, fixed
+//                       reduction trees (one partial per wave);
 //   sample_pick_kernel  one workgroup per row: running sum over the chunk
 //                       masses, then a block-wide fp64 prefix scan inside the
 //                       chosen chunk to find the token.
@@ -53,16 +54,18 @@ __device__ __forceinline__ DrawCtx draw_ctx(const RowInfo& ri) {
 __device__ __forceinline__ void draw_weights(const DrawCtx& x, float lt, float ld, uint32_t id,
                                              const double* ebk, double* wr, double* wp) {
     if (x.nucleus) {
-        const double p =
-            (make_key(lt, id) >= x.tau_t) ? fn_weight(lt, x.mt, x.invT, ebk) / x.zt : 0.0;
-        *wp = p;
-        if (x.resid) {
-            const double q =
-                (make_key(ld, id) >= x.tau_d) ? fn_weight(ld, x.md, x.invT, ebk) / x.zd : 0.0;
-            const double d = p - q;
-            *wr = d > 0.0 ? d : 0.0;
-        } else {
-            *wr = 0.0;
+        // only tokens kept on the target side carry mass in either sum
+        *wp = 0.0;
+        *wr = 0.0;
+        if (make_key(lt, id) >= x.tau_t) {
+            const double p = fn_weight(lt, x.mt, x.invT, ebk) / x.zt;
+            *wp = p;
+            if (x.resid) {
+                const double q =
+                    (make_key(ld, id) >= x.tau_d) ? fn_weight(ld, x.md, x.invT, ebk) / x.zd : 0.0;
+                const double d = p - q;
+                *wr = d > 0.0 ? d : 0.0;
+            }
         }
     } else {
         const float ep = exp2f((lt - x.mt) * x.c);
@@ -77,68 +80,61 @@ __device__ __forceinline__ void draw_weights(const DrawCtx& x, float lt, float l
     }
 }
 
+// The workgroups split the tiles of the draw rows evenly; every wave leaves
+// its partial masses of each tile at chunks[(b*ntiles + tile)*kWaves + wave].
 template <int DT, bool kAligned>
 __global__ __launch_bounds__(kThreads) void sample_sums_kernel(StepArgs a) {
     using TS = TileShape<DT>;
-    __shared__ double red[2][kWaves];
+    // the bucket scales live in LDS: a global load inside the streaming loop
+    // would make every wait drain the prefetched tile as well
+    __shared__ double s_ebk[kNB];
+    for (int i = threadIdx.x; i < kNB; i += kThreads) s_ebk[i] = a.ebk[i];
+    __syncthreads();
     const int n = a.pos[a.K + 1].n_sample;
-    const int items = n * a.ntiles;
-    for (int it = blockIdx.x; it < items; it += gridDim.x) {
-        const int si = it / a.ntiles, ch = it - si * a.ntiles;
+    const int64_t T = (int64_t)n * a.ntiles;
+    int64_t t = flat_begin(T, gridDim.x, blockIdx.x);
+    const int64_t t_end = flat_begin(T, gridDim.x, blockIdx.x + 1);
+    while (t < t_end) {
+        const int si = (int)(t / a.ntiles);
+        const int64_t tu0 = t - (int64_t)si * a.ntiles;
+        int64_t tu1 = tu0 + (t_end - t);
+        if (tu1 > a.ntiles) tu1 = a.ntiles;
+        t += tu1 - tu0;
         const int b = a.slist[si];
         const RowInfo& ri = a.rows[b];
         const int kpos = ri.kpos;
         const DrawCtx x = draw_ctx(ri);
         const void* trow = unit_row<DT>(a, b, 0, kpos);
         const void* drow = x.resid ? unit_row<DT>(a, b, 1, kpos) : nullptr;
-        const int64_t start = (int64_t)ch * TS::kTile;
-        const int64_t end = (start + TS::kTile < a.V) ? start + TS::kTile : a.V;
-        const bool full = start + TS::kTile <= a.V;
-        float vt[TS::kE], vd[TS::kE];
-        if (kAligned && full) {
-            RawTile r;
-            issue_tile<DT>(trow, start, r);
-            unpack_tile<DT>(r, vt);
-            if (x.resid) {
-                issue_tile<DT>(drow, start, r);
-                unpack_tile<DT>(r, vd);
-            }
-        } else {
-            load_tile_partial<DT>(trow, start, end, vt);
-            if (x.resid) load_tile_partial<DT>(drow, start, end, vd);
-        }
-        double sr = 0.0, sp = 0.0;
+        const int64_t start = tu0 * TS::kTile;
+        int64_t end = tu1 * TS::kTile;
+        if (end > a.V) end = a.V;
+        double2* out = a.chunks + (int64_t)b * a.ntiles * kWaves;
+        stream_range2<DT, kAligned>(trow, drow, start, end,
+                                    [&](float (&vt)[TS::kE], float (&vd)[TS::kE], int64_t t0,
+                                        bool full) __attribute__((always_inline)) {
+            double sr = 0.0, sp = 0.0;
 #pragma unroll
-        for (int i = 0; i < TS::kE; i++) {
-            const int64_t id = elem_id<DT>(start, i);
-            if (id >= end) continue;
-            double wr, wp;
-            draw_weights(x, vt[i], x.resid ? vd[i] : 0.f, (uint32_t)id, a.ebk, &wr, &wp);
-            sr += wr;
-            sp += wp;
-        }
-#pragma unroll
-        for (int o = kWave / 2; o > 0; o >>= 1) {
-            sr += __shfl_down(sr, o, kWave);
-            sp += __shfl_down(sp, o, kWave);
-        }
-        if (lane_id() == 0) {
-            red[0][wave_id()] = sr;
-            red[1][wave_id()] = sp;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            double r0 = 0.0, r1 = 0.0;
-            for (int i = 0; i < kWaves; i++) {
-                r0 += red[0][i];
-                r1 += red[1][i];
+            for (int i = 0; i < TS::kE; i++) {
+                const int64_t id = elem_id<DT>(t0, i);
+                if (!full && id >= end) continue;
+                double wr, wp;
+                draw_weights(x, vt[i], vd[i], (uint32_t)id, s_ebk, &wr, &wp);
+                sr += wr;
+                sp += wp;
             }
-            double2 out;
-            out.x = r0;
-            out.y = r1;
-            a.chunks[(int64_t)b * a.ntiles + ch] = out;
-        }
-        __syncthreads();
+#pragma unroll
+            for (int o = kWave / 2; o > 0; o >>= 1) {
+                sr += __shfl_down(sr, o, kWave);
+                sp += __shfl_down(sp, o, kWave);
+            }
+            if (lane_id() == 0) {
+                double2 r;
+                r.x = sr;
+                r.y = sp;
+                out[(t0 / TS::kTile) * kWaves + wave_id()] = r;
+            }
+        });
     }
 }
 
@@ -157,11 +153,13 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(StepArgs a) {
         const bool resid = ri.need == NEED_RESID;
         const double u = (double)a.uniforms[(int64_t)b * (a.K + 1) + a.K];
         if (threadIdx.x == 0) {
-            const double2* cs = a.chunks + (int64_t)b * a.ntiles;
+            const double2* cs = a.chunks + (int64_t)b * a.ntiles * kWaves;
             double Wr = 0.0, Wp = 0.0;
             for (int c = 0; c < a.ntiles; c++) {
-                Wr += cs[c].x;
-                Wp += cs[c].y;
+                for (int q = 0; q < kWaves; q++) {
+                    Wr += cs[c * kWaves + q].x;
+                    Wp += cs[c * kWaves + q].y;
+                }
             }
             const int use_r = resid && Wr > 0.0;
             const double W = use_r ? Wr : Wp;
@@ -170,7 +168,8 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(StepArgs a) {
             int chosen = -1, last = -1;
             double last_base = 0.0;
             for (int c = 0; c < a.ntiles; c++) {
-                const double wc = use_r ? cs[c].x : cs[c].y;
+                double wc = 0.0;
+                for (int q = 0; q < kWaves; q++) wc += use_r ? cs[c * kWaves + q].x : cs[c * kWaves + q].y;
                 if (!(wc > 0.0)) continue;
                 const double before = S;
                 S += wc;

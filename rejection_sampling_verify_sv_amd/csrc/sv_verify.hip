@@ -48,7 +48,7 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
     p->tile = (dtype == SV_F32) ? TileShape<SV_F32>::kTile : TileShape<SV_BF16>::kTile;
     p->ntiles = (V + p->tile - 1) / p->tile;
     const size_t units = (size_t)B * 2;
-    const size_t slots = units > (size_t)kTargetItems ? units : (size_t)kTargetItems;
+    const size_t slots = units + kGrid;  // record slot u + w of a (unit, workgroup) piece
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -61,7 +61,7 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
     p->off_flist = take(sizeof(int32_t) * units * (size_t)(K + 1));
     p->off_slist = take(sizeof(int32_t) * (size_t)B);
     p->off_parts = take(sizeof(PartSlot) * slots);
-    p->off_chunks = take(sizeof(double2) * (size_t)B * p->ntiles);
+    p->off_chunks = take(sizeof(double2) * (size_t)B * p->ntiles * kWaves);
     p->off_fnu = take(sizeof(FnUnit) * units);
     p->off_hi = take(sizeof(uint64_t) * units * kNB);
     p->off_lo = take(sizeof(uint64_t) * units * kNB);
