@@ -95,6 +95,21 @@ def algorithmic_rows(acc, draft_len, params):
     return int(tgt.sum()), int(drf.sum())
 
 
+def rows_at_position(acc, draft_len, params, K):
+    """Logits rows (target + draft) the method reads at each position k."""
+    acc = np.asarray(acc)
+    L = np.asarray(draft_len)
+    greedy = np.asarray(params["temperature"]) == 0
+    ok = acc >= 0
+    f = np.where(ok, acc, -1)
+    out = []
+    for k in range(K + 1):
+        tgt = ok & (k <= f)
+        drf = ok & ~greedy & (k <= np.minimum(f, L - 1))
+        out.append(int(tgt.sum() + drf.sum()))
+    return out
+
+
 def cpu_baseline(wl):
     import oracle
 
@@ -179,10 +194,12 @@ def main():
         hip.destroy(evsets[s])
     rowpass_launches = names.count("rowpass")
     rowpass_mean_ms = float(np.mean(rowpass_ms))
+    by_pos_ms = np.mean(np.asarray(rowpass_ms).reshape(args.steps, rowpass_launches), axis=0)
 
     acc = out_acc.cpu().numpy()
     n_tgt, n_drf = algorithmic_rows(acc, wl.draft_len, wl.params)
     row_bytes = V * esz
+    pos_bytes = [r * row_bytes for r in rows_at_position(acc, wl.draft_len, wl.params, K)]
     alg_bytes_step = (n_tgt + n_drf) * row_bytes
     alg_bytes_launch = alg_bytes_step / rowpass_launches
     achieved = alg_bytes_launch / (rowpass_mean_ms * 1e-3) / 1e9
@@ -226,6 +243,8 @@ def main():
             "launch_ms": round(rowpass_mean_ms, 4),
         },
         "kernels_ms_per_step": {k: round(v, 4) for k, v in per_kernel.items()},
+        "rowpass_by_position": [{"ms": round(float(m), 4), "GBps": round(b / (m * 1e-3) / 1e9, 1)}
+                                for m, b in zip(by_pos_ms, pos_bytes)],
         "useful_GBps_whole_step": round(alg_bytes_step / (ms_per_step * 1e-3) / 1e9, 1),
         "acceptance_rate": round(acc_rate, 4),
     }

@@ -165,7 +165,7 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
     const int k_eff = ri.k_eff;
     const double T = (double)ri.T, top_p = (double)ri.top_p;
     const bool has_draft = k < ri.L;
-    const uint64_t kt = unit_top(a.parts, unit_records(ri.li_t, n, a.ntiles));
+    const uint64_t kt = unit_top(a.parts, unit_records(ri.li_t, n, a.ntiles, a.g_row));
     double p;
     bool keep_p;
     if (!topk_dist_wave(kt, k_eff, T, top_p, &p, &keep_p)) {
@@ -178,7 +178,7 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
     bool keep_q = false;
     int id_q = -1;
     if (has_draft) {
-        const uint64_t kd = unit_top(a.parts, unit_records(ri.li_d, n, a.ntiles));
+        const uint64_t kd = unit_top(a.parts, unit_records(ri.li_d, n, a.ntiles, a.g_row));
         if (!topk_dist_wave(kd, k_eff, T, top_p, &q, &keep_q)) {
             close_row_invalid(a, b, -1);
             return;
@@ -257,7 +257,7 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
 
 __device__ void decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri, int n) {
     const int lane = lane_id();
-    const RecRange r = unit_records(ri.li_t, n, a.ntiles);
+    const RecRange r = unit_records(ri.li_t, n, a.ntiles, a.g_row);
     const PartSlot* s = a.parts + r.first;
     uint64_t best = 0ull;
     for (int i = lane; i < r.count; i += kWave) best = s[i].keys[0] > best ? s[i].keys[0] : best;
@@ -270,18 +270,28 @@ __device__ void decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri
     if (lane == 0) emit_row(a, b, k, g);
 }
 
-// {max, sum-exp} of one full-vocab unit from its records (lanes combine in a
-// fixed tree; lane 0's result is broadcast).
-__device__ inline void full_stats(const PartSlot* parts, RecRange r, double invT, double* m,
-                                  double* z) {
+// (m, s) pairs: s = sum of exp((l - m) / T).  Combining is exact up to one
+// fp64 rounding per term.
+__device__ __forceinline__ void ms_combine(float& m, double& s, float m2, double s2, double invT) {
+    const float mm = fmaxf(m, m2);
+    if (mm == -INFINITY) {
+        m = mm;
+        s = 0.0;
+        return;
+    }
+    const double a = (m == mm) ? s : s * exp(((double)m - (double)mm) * invT);
+    const double b = (m2 == mm) ? s2 : s2 * exp(((double)m2 - (double)mm) * invT);
+    m = mm;
+    s = a + b;
+}
+
+// {max, sum-exp} of one full-vocab unit from its n per-(tile, wave) records;
+// lanes combine in a fixed tree and lane 0's result is broadcast.
+__device__ inline void full_stats(const FullStat* rec, int n, double invT, double* m, double* z) {
     const int lane = lane_id();
     float mm = -INFINITY;
     double ss = 0.0;
-    const PartSlot* s = parts + r.first;
-    for (int i = lane; i < r.count; i += kWave) {
-        const FullStat* fs = reinterpret_cast<const FullStat*>(s + i);
-        ms_combine(mm, ss, fs->m, fs->s, invT);
-    }
+    for (int i = lane; i < n; i += kWave) ms_combine(mm, ss, rec[i].m, rec[i].s, invT);
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) {
         const float m2 = __shfl_down(mm, o, kWave);
@@ -293,10 +303,11 @@ __device__ inline void full_stats(const PartSlot* parts, RecRange r, double invT
 }
 
 template <int DT>
-__device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri, int n) {
+__device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri) {
     const double T = (double)ri.T, invT = 1.0 / T;
     double mt, zt, md = 0.0, zd = 0.0;
-    full_stats(a.parts, unit_records(ri.li_t, n, a.ntiles), invT, &mt, &zt);
+    const int nrec = a.ntiles * kWaves;
+    full_stats(a.tstat + (int64_t)(2 * b) * nrec, nrec, invT, &mt, &zt);
     if (!(mt > -INFINITY)) {
         close_row_invalid(a, b, -1);
         return;
@@ -312,7 +323,7 @@ __device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri, 
         }
         return;
     }
-    full_stats(a.parts, unit_records(ri.li_d, n, a.ntiles), invT, &md, &zd);
+    full_stats(a.tstat + (int64_t)(2 * b + 1) * nrec, nrec, invT, &md, &zd);
     if (!(md > -INFINITY)) {
         close_row_invalid(a, b, -1);
         return;
@@ -341,8 +352,8 @@ __device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri, 
     }
 }
 
-// Nucleus rows: p(x) = [key(x) >= tau] w(x) / Z_S with the exact masses of
-// the cut computed by the nucleus kernels for this position.
+// Nucleus rows: p(x) = [key(x) >= tau] w(x) / S with the fixed-point masses
+// of the cut computed by the nucleus kernels for this position.
 template <int DT>
 __device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& ri) {
     const FnUnit ut = a.fn_unit[b * 2];
@@ -361,19 +372,21 @@ __device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& r
         w.need = NEED_BONUS;
         w.kpos = k;
         w.mt = (double)ut.m;
-        w.zt = ut.Zs;
+        w.zt = (double)ut.Sfix;
         w.tau_t = ut.tau;
         queue_draw(a, b);
         return;
     }
-    const double invT = 1.0 / (double)ri.T;
+    const float c = exp2_coef(ri.T);
     const int x = a.tokens[(int64_t)b * a.K + k];
     const float lx = load_one<DT>(unit_row<DT>(a, b, 0, k), x);
     const float ld = load_one<DT>(unit_row<DT>(a, b, 1, k), x);
-    const double px =
-        (make_key(lx, (uint32_t)x) >= ut.tau) ? fn_weight(lx, ut.m, invT, a.ebk) / ut.Zs : 0.0;
-    const double qx =
-        (make_key(ld, (uint32_t)x) >= ud.tau) ? fn_weight(ld, ud.m, invT, a.ebk) / ud.Zs : 0.0;
+    const double px = (make_key(lx, (uint32_t)x) >= ut.tau)
+                          ? (double)nuc_wfix(lx, ut.m, c) / (double)ut.Sfix
+                          : 0.0;
+    const double qx = (make_key(ld, (uint32_t)x) >= ud.tau)
+                          ? (double)nuc_wfix(ld, ud.m, c) / (double)ud.Sfix
+                          : 0.0;
     const double acc = accept_prob(px, qx);
     const double uk = (double)a.uniforms[(int64_t)b * (a.K + 1) + k];
     write_accept_diag(a, b, k, px, qx, acc, uk);
@@ -384,10 +397,10 @@ __device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& r
         w.need = NEED_RESID;
         w.kpos = k;
         w.mt = (double)ut.m;
-        w.zt = ut.Zs;
+        w.zt = (double)ut.Sfix;
         w.tau_t = ut.tau;
         w.md = (double)ud.m;
-        w.zd = ud.Zs;
+        w.zd = (double)ud.Sfix;
         w.tau_d = ud.tau;
         queue_draw(a, b);
     }
@@ -407,11 +420,11 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepArgs a, int 
     else if (ri.cls == CLS_NUCLEUS)
         decide_nucleus<DT>(a, b, k, ri);
     else
-        decide_full<DT>(a, b, k, ri, n);
+        decide_full<DT>(a, b, k, ri);
 }
 
-// Zero the work counters and write the e^(-b/32) table (once per call).
-__global__ __launch_bounds__(kThreads) void init_kernel(StepArgs a, double* ebk) {
+// Zero the work counters (once per call).
+__global__ __launch_bounds__(kThreads) void init_kernel(StepArgs a) {
     const int i = blockIdx.x * kThreads + threadIdx.x;
     if (i < a.K + 2) {
         a.pos[i].n_units = 0;
@@ -419,7 +432,6 @@ __global__ __launch_bounds__(kThreads) void init_kernel(StepArgs a, double* ebk)
         a.pos[i].n_sample = 0;
         a.pos[i].pad = 0;
     }
-    if (i < kNB) ebk[i] = exp(-(double)i / 32.0);
 }
 
 // Row classification, output initialisation and the position-0 unit lists

@@ -25,7 +25,7 @@ constexpr int kWave = 64;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxTopK = SV_MAX_TOP_K;
 constexpr int kLoads = 4;          // 16-byte loads per thread per tile
-constexpr int kGrid = 1024;        // workgroups of a streaming launch (4 per CU)
+constexpr int kGrid = 1024;        // most workgroups of a streaming launch (record slots)
 constexpr int kCandBuf = 128;      // per-wave candidate buffer (top-k select)
 
 enum RowClass : int32_t {
@@ -60,79 +60,69 @@ struct PosDesc {
     int32_t pad;
 };
 
-// One segment's result: either a descending top-k key list (zero-padded)
-// or, for full-vocab rows, {max, sum-exp relative to max}.
+// One segment's result: a descending top-k key list (zero-padded), or the
+// best key of a greedy segment in keys[0].
 struct PartSlot {
     uint64_t keys[kMaxTopK];
 };
+
+// Full-vocab rows: {max, sum of exp((l - max) / T)} of the part of one tile
+// that one wave reads.  Records are laid out per (row, side, tile, wave), so
+// the order in which they are combined never depends on how the tiles were
+// split over workgroups.
 struct FullStat {
     float m;
     float pad;
     double s;
 };
 
-// ---- exact masses for the full-vocab nucleus cut ---------------------------
-constexpr int kNB = 2048;           // buckets of width 1/32 in z, z < 64
+// exp(x / T) = exp2(x * c) with c = log2(e) / T (clamped so that c is finite).
+__host__ __device__ __forceinline__ float exp2_coef(float T) {
+    const float c = (float)(1.4426950408889634 / (double)T);
+    return c < 3.0e38f ? c : 3.0e38f;
+}
+
+// ---- masses for the full-vocab nucleus cut ---------------------------------
+// Weights w = exp((l - m) / T) <= 1 are taken in 40-bit fixed point, so every
+// sum of them is an exact integer whatever the order of the additions.
+// Buckets cut z = (m - l) / T into slices of width 1/64; a higher logit never
+// lands in a later bucket.  Tokens with z >= 32 have a fixed-point weight of
+// zero and fall into the dropped bucket kNB.
+constexpr int kNB = 2048;
+constexpr float kBucketScale = 64.0f;
 constexpr int kCollectCap = 4096;   // boundary-bucket tokens resolved per unit
+constexpr double kFix = 1099511627776.0;            // 2^40
+constexpr double kUnfix = 1.0 / 1099511627776.0;    // 2^-40
+
+__device__ __forceinline__ uint64_t nuc_wfix(float l, float m, float c) {
+    const float w = exp2f((l - m) * c);
+    return (uint64_t)((double)w * kFix);
+}
+
+// Bucket scale 64 / T, clamped finite like exp2_coef.
+__host__ __device__ __forceinline__ float bucket_coef(float T) {
+    const float c = kBucketScale / T;
+    return c < 3.0e38f ? c : 3.0e38f;
+}
+
+__device__ __forceinline__ int nuc_bucket(float l, float m, float cb) {
+    const float d = m - l;
+    if (!(d > 0.f)) return d == 0.f ? 0 : kNB;  // the max itself; NaN dropped
+    const float z = d * cb;
+    return z < (float)kNB ? (int)z : kNB;
+}
 
 // Per (row, side) state of the nucleus cut at the current position.
 struct FnUnit {
-    double Z;        // total mass (relative to the row max)
-    double Mabove;   // mass of the buckets before the boundary bucket
-    double Zs;       // kept mass
-    uint64_t tau;    // key of the last kept token
-    float m;         // row max
-    int32_t beta;    // boundary bucket
-    int32_t count;   // tokens in the boundary bucket (histogram)
-    int32_t ncoll;   // tokens appended by the collect pass
-    int32_t status;  // 0 ok, 1 boundary bucket too large to resolve, 2 no finite logit
-    int32_t pad;
+    uint64_t Zfix;    // total mass
+    uint64_t Afix;    // mass of the buckets before the boundary bucket
+    uint64_t Sfix;    // kept mass
+    uint64_t tau;     // key of the last kept token
+    float m;          // row max
+    int32_t beta;     // boundary bucket
+    int32_t ncoll;    // tokens appended by the collect pass
+    int32_t status;   // 0 ok, 1 boundary bucket too large to resolve, 2 no finite logit
 };
-
-// e^(-d) for d in [0, 1/32): Taylor series to degree 8.
-__device__ __forceinline__ double exp_neg_small(double d) {
-    double p = 1.0 / 40320.0;
-    p = fma(p, -d, 1.0 / 5040.0);
-    p = fma(p, -d, 1.0 / 720.0);
-    p = fma(p, -d, 1.0 / 120.0);
-    p = fma(p, -d, 1.0 / 24.0);
-    p = fma(p, -d, 1.0 / 6.0);
-    p = fma(p, -d, 0.5);
-    p = fma(p, -d, 1.0);
-    p = fma(p, -d, 1.0);
-    return p;
-}
-
-// Bucket of a logit (kNB = tail) and its in-bucket offset; identical in every
-// pass so that the histogram, the collect pass and the resolve agree.
-__device__ __forceinline__ int fn_bucket(float l, float m, double invT, double* d) {
-    const double z = ((double)m - (double)l) * invT;
-    if (!(z < 64.0)) {
-        *d = 0.0;
-        return kNB;
-    }
-    const int b = (int)(z * 32.0);
-    *d = z - (double)b * (1.0 / 32.0);
-    return b;
-}
-
-// Exact-mass weight of a logit (0 for the dropped tail).
-__device__ __forceinline__ double fn_weight(float l, float m, double invT, const double* ebk) {
-    double d;
-    const int b = fn_bucket(l, m, invT, &d);
-    return b < kNB ? ebk[b] * exp_neg_small(d) : 0.0;
-}
-
-__device__ __forceinline__ void fixed80(double e, uint64_t* hi, uint64_t* lo) {
-    const double t = e * 1099511627776.0;  // 2^40
-    const double h = floor(t);
-    *hi = (uint64_t)h;
-    *lo = (uint64_t)((t - h) * 1099511627776.0);
-}
-
-__device__ __forceinline__ double unfixed80(uint64_t hi, uint64_t lo) {
-    return (double)hi * 9.094947017729282e-13 + (double)lo * 8.271806125530277e-25;
-}
 
 // ---- element types and tiles ----------------------------------------------
 template <int DT>
@@ -435,10 +425,10 @@ __host__ __device__ __forceinline__ int flat_owner(int64_t t, int64_t T, int G) 
 struct RecRange {
     int first, count;
 };
-__device__ __forceinline__ RecRange unit_records(int li, int n, int ntiles) {
+__device__ __forceinline__ RecRange unit_records(int li, int n, int ntiles, int G) {
     const int64_t T = (int64_t)n * ntiles;
-    const int w0 = flat_owner((int64_t)li * ntiles, T, kGrid);
-    const int w1 = flat_owner((int64_t)(li + 1) * ntiles - 1, T, kGrid);
+    const int w0 = flat_owner((int64_t)li * ntiles, T, G);
+    const int w1 = flat_owner((int64_t)(li + 1) * ntiles - 1, T, G);
     RecRange r;
     r.first = li + w0;
     r.count = w1 - w0 + 1;
@@ -513,19 +503,19 @@ __device__ __forceinline__ uint64_t wave_merge_top(uint64_t a, uint64_t b) {
 }
 
 // Block-wide exclusive prefix sum of one double per thread (fixed order).
-__device__ inline double block_exclusive_scan(double v, double* tmp /* kWaves */,
-                                              double* total) {
+template <class T>
+__device__ inline T block_exclusive_scan(T v, T* tmp /* kWaves */, T* total) {
     const int lane = lane_id(), w = wave_id();
-    double incl = v;
+    T incl = v;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
-        const double t = __shfl_up(incl, o, kWave);
+        const T t = __shfl_up(incl, o, kWave);
         if (lane >= o) incl += t;
     }
     __syncthreads();
     if (lane == kWave - 1) tmp[w] = incl;
     __syncthreads();
-    double off = 0.0, tot = 0.0;
+    T off = 0, tot = 0;
     for (int i = 0; i < kWaves; i++) {
         if (i < w) off += tmp[i];
         tot += tmp[i];
@@ -565,10 +555,12 @@ struct StepArgs {
     const void* draft;
     int64_t t_stride, d_stride;
     int B, K, V, ntiles;
+    int g_row;             // grid of the row pass (its records are laid out by it)
     const int32_t* tokens;
     const float* uniforms;
     RowInfo* rows;
     PartSlot* parts;       // piece records of the current position (slot u + w)
+    FullStat* tstat;       // [2B][ntiles][kWaves] full-vocab row stats of the current position
     double2* chunks;       // [B][ntiles][kWaves] draw masses (one chunk = one tile)
     int32_t* out_tokens;
     int32_t* out_acc;
@@ -578,7 +570,9 @@ struct StepArgs {
     int32_t* flist;        // [K+1][2B] nucleus units per position
     int32_t* slist;        // [B] rows that draw over the full vocabulary at the end
     FnUnit* fn_unit;       // [2B] nucleus cut of the current position
-    const double* ebk;     // [kNB] e^(-b/32)
+    uint64_t* hist;        // [2B + kGrid][kNB] nucleus mass histograms, slot u + w
+    uint64_t* coll;        // [2B][kCollectCap] boundary-bucket keys
+    int g_hist;            // grid of the histogram pass
 };
 
 template <int DT>

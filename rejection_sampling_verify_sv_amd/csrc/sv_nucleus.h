@@ -1,73 +1,54 @@
-// sv_nucleus.h — the exact top_p cut over the whole vocabulary (top_k off).
+// sv_nucleus.h — the top_p cut over the whole vocabulary (top_k off).
 //
 // deniz.in "Üç düzeltmeden sonra Qwen3.5 ve Qwen3.6 MTP head…", section
 // "Kesme her iki tarafta eşleşmek zorunda": both distributions are cut to the
 // smallest head of the ranking whose preceding mass stays below top_p.  With
 // top_k disabled that head can hold tens of thousands of tokens, so the cut is
-// located by mass instead of by sorting:
+// located by mass instead of by sorting the row:
 //
-//   masses  w = exp((l - m) / T), m = the row max, z = (m - l) / T >= 0.
-//           Bucket b = floor(32 z) (z < 64; larger z is a tail whose total
-//           mass, below V * e^-64, is dropped).  Inside a bucket
-//           w = e^(-b/32) * e^(-d) with d = z - b/32 in [0, 1/32), so every
-//           bucket's mass is e^(-b/32) times a sum of e^(-d) terms, each in
-//           (0.969, 1], evaluated by a degree-8 Taylor polynomial (truncation
-//           below 1e-19).  The sums are kept in 80-bit fixed point (two 64-bit
-//           integer words at 2^-40 and 2^-80 per unit), so the histogram is
-//           exact up to the term rounding and independent of the order in
-//           which workgroups add into it.
-//   select  Z = total mass; the boundary bucket is the last non-empty bucket
-//           whose preceding mass is still below top_p * Z.
-//   collect the keys of the boundary bucket's tokens.
-//   resolve sort them by (logit desc, id asc), walk the running mass and keep
-//           tokens while the preceding mass is below top_p * Z.  The cut key
-//           tau (last kept token) and the kept mass Z_S define the
-//           distribution: p(i) = [key_i >= tau] w_i / Z_S.
-// The streaming passes split the tiles of position k's nucleus units evenly
-// over the workgroups, like the row pass; the per-unit steps run one
-// workgroup per unit.
+//   hist     every token's weight w = exp((l - m) / T) (m = row max) in 40-bit
+//            fixed point, added into bucket floor(64 (m - l) / T); one
+//            histogram per (unit, workgroup) piece, written without atomics;
+//   select   per unit: sum the pieces, Z = total mass; the boundary bucket is
+//            the last non-empty bucket whose preceding mass is below top_p Z;
+//   collect  the keys of the boundary bucket's tokens;
+//   resolve  per unit: a token of the boundary bucket is kept when the mass
+//            before the bucket plus the mass of the bucket's tokens ranked
+//            ahead of it (logit desc, id asc) is below top_p Z.  The cut key
+//            tau (last kept token) and the kept mass S define the
+//            distribution p(i) = [key_i >= tau] w_i / S.
+// Fixed-point sums are exact, so the cut does not depend on the order of any
+// addition.  The streaming passes split the tiles of position k's nucleus
+// units evenly over the workgroups, like the row pass; the per-unit steps run
+// one workgroup per unit.
 #pragma once
 
 #include "sv_decide.h"
 
 namespace sv {
 
-struct FnWork {
-    uint64_t* hi;    // [2B][kNB]
-    uint64_t* lo;    // [2B][kNB]
-    uint32_t* cnt;   // [2B][kNB]
-    uint64_t* coll;  // [2B][kCollectCap]
-};
-
-// Row max of unit (b, side) at position k from its row-pass records.
-__device__ inline float unit_max(const StepArgs& a, int b, int side, int k) {
-    const int li = side == 0 ? a.rows[b].li_t : a.rows[b].li_d;
-    const RecRange r = unit_records(li, a.pos[k].n_units, a.ntiles);
+// Row max of one unit from its per-(tile, wave) row-pass records; every
+// thread of the block gets it.  Contains barriers.
+__device__ inline float block_unit_max(const FullStat* rec, int n, float* tmp /* kWaves */) {
     float m = -INFINITY;
-    for (int s = 0; s < r.count; s++)
-        m = fmaxf(m, reinterpret_cast<const FullStat*>(a.parts + r.first + s)->m);
-    return m;
-}
-
-// Zero the histograms of the nucleus units of position 0 (every nucleus row).
-__global__ __launch_bounds__(kThreads) void fn_zero_kernel(StepArgs a, FnWork w) {
-    const int n = a.pos[0].n_fn;
-    for (int i = blockIdx.x; i < n; i += gridDim.x) {
-        const int u = a.flist[i];
-        for (int j = threadIdx.x; j < kNB; j += kThreads) {
-            w.hi[(int64_t)u * kNB + j] = 0ull;
-            w.lo[(int64_t)u * kNB + j] = 0ull;
-            w.cnt[(int64_t)u * kNB + j] = 0u;
-        }
-    }
+    for (int i = threadIdx.x; i < n; i += kThreads) m = fmaxf(m, rec[i].m);
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    __syncthreads();
+    if (lane_id() == 0) tmp[wave_id()] = m;
+    __syncthreads();
+    float r = tmp[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; i++) r = fmaxf(r, tmp[i]);
+    return r;
 }
 
 template <int DT, bool kAligned>
-__global__ __launch_bounds__(kThreads) void fn_hist_kernel(StepArgs a, FnWork w, int k) {
+__global__ __launch_bounds__(kThreads) void fn_hist_kernel(StepArgs a, int k) {
     using TS = TileShape<DT>;
-    __shared__ uint64_t s_hi[kNB];
-    __shared__ uint64_t s_lo[kNB];
-    __shared__ uint32_t s_cnt[kNB];
+    __shared__ uint64_t s_h[kNB];
+    __shared__ float s_red[kWaves];
+    const int nrec = a.ntiles * kWaves;
     const int64_t T = (int64_t)a.pos[k].n_fn * a.ntiles;
     int64_t t = flat_begin(T, gridDim.x, blockIdx.x);
     const int64_t t_end = flat_begin(T, gridDim.x, blockIdx.x + 1);
@@ -79,105 +60,97 @@ __global__ __launch_bounds__(kThreads) void fn_hist_kernel(StepArgs a, FnWork w,
         if (tu1 > a.ntiles) tu1 = a.ntiles;
         const int u = list[li];
         const int b = u >> 1, side = u & 1;
-        for (int i = threadIdx.x; i < kNB; i += kThreads) {
-            s_hi[i] = 0ull;
-            s_lo[i] = 0ull;
-            s_cnt[i] = 0u;
-        }
-        __syncthreads();
-        const float m = unit_max(a, b, side, k);
-        const double invT = 1.0 / (double)a.rows[b].T;
+        for (int i = threadIdx.x; i < kNB; i += kThreads) s_h[i] = 0ull;
+        const float m = block_unit_max(a.tstat + (int64_t)u * nrec, nrec, s_red);
+        const float T_ = a.rows[b].T;
+        const float c = exp2_coef(T_), cb = bucket_coef(T_);
         const int64_t start = tu0 * TS::kTile;
         int64_t end = tu1 * TS::kTile;
         if (end > a.V) end = a.V;
         stream_range<DT, kAligned>(unit_row<DT>(a, b, side, k), start, end,
-                                   [&](float (&v)[TS::kE], int64_t t0, bool full) {
+                                   [&](float (&v)[TS::kE], int64_t, bool)
+                                       __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < TS::kE; i++) {
-                if (!full && elem_id<DT>(t0, i) >= end) continue;
-                double d;
-                const int bk = fn_bucket(v[i], m, invT, &d);
-                if (bk >= kNB) continue;
-                uint64_t h, l;
-                fixed80(exp_neg_small(d), &h, &l);
-                atomicAdd((unsigned long long*)&s_hi[bk], (unsigned long long)h);
-                atomicAdd((unsigned long long*)&s_lo[bk], (unsigned long long)l);
-                atomicAdd(&s_cnt[bk], 1u);
+                const int bk = nuc_bucket(v[i], m, cb);
+                // elements past `end` read as -inf and land in the dropped bucket
+                if (bk < kNB) {
+                    const uint64_t wf = nuc_wfix(v[i], m, c);
+                    if (wf != 0ull) atomicAdd((unsigned long long*)&s_h[bk], (unsigned long long)wf);
+                }
             }
         });
         __syncthreads();
-        for (int i = threadIdx.x; i < kNB; i += kThreads) {
-            if (s_cnt[i] == 0u) continue;
-            atomicAdd((unsigned long long*)&w.hi[(int64_t)u * kNB + i],
-                      (unsigned long long)s_hi[i]);
-            atomicAdd((unsigned long long*)&w.lo[(int64_t)u * kNB + i],
-                      (unsigned long long)s_lo[i]);
-            atomicAdd(&w.cnt[(int64_t)u * kNB + i], s_cnt[i]);
-        }
+        uint64_t* out = a.hist + (int64_t)(li + blockIdx.x) * kNB;
+        for (int i = threadIdx.x; i < kNB; i += kThreads) out[i] = s_h[i];
         t += tu1 - tu0;
-        __syncthreads();
+        __syncthreads();  // s_h is cleared for the next piece
     }
 }
 
-// One workgroup per unit: total mass and the boundary bucket.
-__global__ __launch_bounds__(kThreads) void fn_select_kernel(StepArgs a, FnWork w, int k) {
+// One workgroup per unit: total mass, boundary bucket and row max.
+__global__ __launch_bounds__(kThreads) void fn_select_kernel(StepArgs a, int k) {
     constexpr int kPer = kNB / kThreads;  // contiguous buckets per thread
-    __shared__ double s_tmp[kWaves];
+    __shared__ uint64_t s_tmp[kWaves];
+    __shared__ float s_red[kWaves];
     __shared__ int s_beta;
     const int n = a.pos[k].n_fn;
+    const int nrec = a.ntiles * kWaves;
     const int32_t* list = a.flist + (int64_t)k * 2 * a.B;
     for (int li = blockIdx.x; li < n; li += gridDim.x) {
         const int u = list[li];
-        const int b = u >> 1, side = u & 1;
-        double mass[kPer];
-        double mine = 0.0;
+        const int b = u >> 1;
+        const RecRange r = unit_records(li, n, a.ntiles, a.g_hist);
         const int b0 = threadIdx.x * kPer;
+        uint64_t mass[kPer];
 #pragma unroll
-        for (int j = 0; j < kPer; j++) {
-            const int bk = b0 + j;
-            mass[j] = unfixed80(w.hi[(int64_t)u * kNB + bk], w.lo[(int64_t)u * kNB + bk]) * a.ebk[bk];
-            mine += mass[j];
+        for (int j = 0; j < kPer; j++) mass[j] = 0ull;
+        for (int p = 0; p < r.count; p++) {
+            const uint64_t* h = a.hist + (int64_t)(r.first + p) * kNB + b0;
+#pragma unroll
+            for (int j = 0; j < kPer; j++) mass[j] += h[j];
         }
-        double Z;
-        const double excl0 = block_exclusive_scan(mine, s_tmp, &Z);
-        const double target = (double)a.rows[b].top_p * Z;
+        uint64_t mine = 0ull;
+#pragma unroll
+        for (int j = 0; j < kPer; j++) mine += mass[j];
+        uint64_t Z;
+        const uint64_t excl0 = block_exclusive_scan(mine, s_tmp, &Z);
+        const double target = (double)a.rows[b].top_p * (double)Z;
         if (threadIdx.x == 0) s_beta = -1;
         __syncthreads();
-        double run = excl0;
+        uint64_t run = excl0;
         int best = -1;
+        uint64_t best_before = 0ull;
 #pragma unroll
         for (int j = 0; j < kPer; j++) {
-            const int bk = b0 + j;
-            if (w.cnt[(int64_t)u * kNB + bk] > 0u && run < target) best = bk;
+            if (mass[j] != 0ull && (double)run < target) {
+                best = b0 + j;
+                best_before = run;
+            }
             run += mass[j];
         }
         if (best >= 0) atomicMax(&s_beta, best);
-        __syncthreads();
+        const float m = block_unit_max(a.tstat + (int64_t)u * nrec, nrec, s_red);  // barriers
         const int beta = s_beta;
-        FnUnit& fu = a.fn_unit[u];
-        if (beta >= b0 && beta < b0 + kPer) {
-            double before = excl0;
-#pragma unroll
-            for (int j = 0; j < kPer; j++)
-                if (j < beta - b0) before += mass[j];
-            fu.Z = Z;
-            fu.Mabove = before;
-            fu.beta = beta;
-            fu.count = (int)w.cnt[(int64_t)u * kNB + beta];
-            fu.ncoll = 0;
-            fu.status = 0;
-            fu.m = unit_max(a, b, side, k);
+        FnUnit* fu = a.fn_unit + u;
+        if (beta >= 0 && best == beta) {
+            fu->Zfix = Z;
+            fu->Afix = best_before;
+            fu->beta = beta;
+            fu->m = m;
+            fu->ncoll = 0;
+            fu->status = 0;
         }
         if (beta < 0 && threadIdx.x == 0) {  // no finite logit: invalid row
-            fu.status = 2;
-            fu.ncoll = 0;
+            fu->status = 2;
+            fu->ncoll = 0;
         }
         __syncthreads();
     }
 }
 
 template <int DT, bool kAligned>
-__global__ __launch_bounds__(kThreads) void fn_collect_kernel(StepArgs a, FnWork w, int k) {
+__global__ __launch_bounds__(kThreads) void fn_collect_kernel(StepArgs a, int k) {
     using TS = TileShape<DT>;
     const int64_t T = (int64_t)a.pos[k].n_fn * a.ntiles;
     int64_t t = flat_begin(T, gridDim.x, blockIdx.x);
@@ -195,32 +168,68 @@ __global__ __launch_bounds__(kThreads) void fn_collect_kernel(StepArgs a, FnWork
         if (fu->status != 0) continue;
         const int beta = fu->beta;
         const float m = fu->m;
-        const double invT = 1.0 / (double)a.rows[b].T;
+        const float cb = bucket_coef(a.rows[b].T);
         const int64_t start = tu0 * TS::kTile;
         int64_t end = tu1 * TS::kTile;
         if (end > a.V) end = a.V;
-        uint64_t* coll = w.coll + (int64_t)u * kCollectCap;
+        uint64_t* coll = a.coll + (int64_t)u * kCollectCap;
         stream_range<DT, kAligned>(unit_row<DT>(a, b, side, k), start, end,
-                                   [&](float (&v)[TS::kE], int64_t t0, bool full) {
+                                   [&](float (&v)[TS::kE], int64_t t0, bool)
+                                       __attribute__((always_inline)) {
+            // past `end` elements read as -inf and land in the dropped bucket
+            uint32_t hit = 0u;
+#pragma unroll
+            for (int i = 0; i < TS::kE; i++)
+                hit |= (nuc_bucket(v[i], m, cb) == beta ? 1u : 0u) << i;
+            if (__ballot(hit != 0u) == 0ull) return;
+            // one counter update per wave and tile
+            const int mine = __popc(hit);
+            int incl = mine;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const int t = __shfl_up(incl, o, kWave);
+                if (lane_id() >= o) incl += t;
+            }
+            const int total = __shfl(incl, kWave - 1, kWave);
+            int base = 0;
+            if (lane_id() == kWave - 1) base = atomicAdd(&fu->ncoll, total);
+            int slot = __shfl(base, kWave - 1, kWave) + incl - mine;
 #pragma unroll
             for (int i = 0; i < TS::kE; i++) {
-                const int64_t id = elem_id<DT>(t0, i);
-                if (!full && id >= end) continue;
-                double d;
-                if (fn_bucket(v[i], m, invT, &d) != beta) continue;
-                const int slot = atomicAdd(&fu->ncoll, 1);
-                if (slot < kCollectCap) coll[slot] = make_key(v[i], (uint32_t)id);
+                if (hit & (1u << i)) {
+                    if (slot < kCollectCap) coll[slot] = make_key(v[i], (uint32_t)elem_id<DT>(t0, i));
+                    slot++;
+                }
             }
         });
     }
 }
 
-// One workgroup per unit: exact cut inside the boundary bucket.  Always
-// clears the unit's histogram for the next position.
-__global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, FnWork w, int k) {
+// One workgroup per unit: the exact cut inside the boundary bucket.
+//   1. the bucket's n tokens are split into 256 sub-buckets by the fraction
+//      of their bucket coordinate (a finer cut of the same monotone map), and
+//      the sub-bucket masses give the boundary sub-bucket the same way the
+//      buckets gave the boundary bucket;
+//   2. every token of the boundary sub-bucket is ranked implicitly: its
+//      preceding mass is the bucket mass before the sub-bucket plus the
+//      masses of the sub-bucket's tokens with a larger key.
+// The first token of the boundary sub-bucket is always kept (its preceding
+// mass is below top_p Z by the choice of the sub-bucket), so the cut key tau
+// lies in that sub-bucket.
+constexpr int kSub = 256;
+static_assert(kSub == kThreads, "one sub-bucket per thread");
+
+__global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, int k) {
+    constexpr int kOwn = 4;  // boundary tokens a thread ranks per pass
     __shared__ uint64_t s_key[kCollectCap];
-    __shared__ double s_tmp[kWaves];
-    __shared__ int s_keep;
+    __shared__ uint64_t s_w[kCollectCap];
+    __shared__ uint16_t s_sel[kCollectCap];
+    __shared__ uint8_t s_sb[kCollectCap];
+    __shared__ uint64_t s_sub[kSub];
+    __shared__ uint64_t s_tmp[kWaves];
+    __shared__ unsigned long long s_tau, s_kept;
+    __shared__ int s_star, s_nsel;
+    __shared__ uint64_t s_before;
     const int n_units = a.pos[k].n_fn;
     const int32_t* list = a.flist + (int64_t)k * 2 * a.B;
     for (int li = blockIdx.x; li < n_units; li += gridDim.x) {
@@ -229,70 +238,90 @@ __global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, FnWork
         FnUnit* fu = a.fn_unit + u;
         const int status = fu->status;
         const int n = fu->ncoll;
-        const bool ok = status == 0 && n <= kCollectCap && n >= 1;
-        if (ok) {
-            const int P = pow2_ceil(n < 2 ? 2 : n);
-            const uint64_t* coll = w.coll + (int64_t)u * kCollectCap;
-            for (int i = threadIdx.x; i < P; i += kThreads) s_key[i] = (i < n) ? coll[i] : 0ull;
-            __syncthreads();
-            block_sort_desc(s_key, P);
-            const double invT = 1.0 / (double)a.rows[b].T;
-            const float m = fu->m;
-            const double target = (double)a.rows[b].top_p * fu->Z;
-            const double Mabove = fu->Mabove;
-            // every collected token sits in the boundary bucket: w = e^(-beta/32) e^(-d)
-            const double eb = a.ebk[fu->beta];
-            // thread t owns sorted positions [t*kPer, (t+1)*kPer)
-            constexpr int kPer = kCollectCap / kThreads;
-            const int j0 = threadIdx.x * kPer;
-            double wv[kPer];
-            double mine = 0.0;
-#pragma unroll
-            for (int q = 0; q < kPer; q++) {
-                double d;
-                const int j = j0 + q;
-                wv[q] = 0.0;
-                if (j < n) {
-                    (void)fn_bucket(key_logit(s_key[j]), m, invT, &d);
-                    wv[q] = eb * exp_neg_small(d);
-                }
-                mine += wv[q];
-            }
-            double tot;
-            const double excl = block_exclusive_scan(mine, s_tmp, &tot);
-            if (threadIdx.x == 0) s_keep = 0;
-            __syncthreads();
-            double cum = Mabove + excl;
-            int keep_here = 0;
-#pragma unroll
-            for (int q = 0; q < kPer; q++) {
-                if (j0 + q < n && cum < target) keep_here = j0 + q + 1;
-                cum += wv[q];
-            }
-            if (keep_here > 0) atomicMax(&s_keep, keep_here);
-            __syncthreads();
-            const int nk = s_keep;  // >= 1: the first token's preceding mass is below target
-            double kept = 0.0;
-#pragma unroll
-            for (int q = 0; q < kPer; q++)
-                if (j0 + q < nk) kept += wv[q];
-            double ktot;
-            (void)block_exclusive_scan(kept, s_tmp, &ktot);
-            if (threadIdx.x == 0) {
-                if (nk < 1) {
-                    fu->status = 1;
-                } else {
-                    fu->tau = s_key[nk - 1];
-                    fu->Zs = Mabove + ktot;
-                }
-            }
-        } else if (threadIdx.x == 0 && status == 0) {
-            fu->status = 1;  // boundary bucket larger than kCollectCap
+        __syncthreads();  // every thread has read fu before thread 0 may write it
+        if (status != 0) continue;  // uniform over the block
+        if (n < 1 || n > kCollectCap) {
+            if (threadIdx.x == 0) fu->status = 1;  // boundary bucket too large
+            continue;
         }
-        for (int i = threadIdx.x; i < kNB; i += kThreads) {
-            w.hi[(int64_t)u * kNB + i] = 0ull;
-            w.lo[(int64_t)u * kNB + i] = 0ull;
-            w.cnt[(int64_t)u * kNB + i] = 0u;
+        const float m = fu->m;
+        const float T = a.rows[b].T;
+        const float c = exp2_coef(T), cb = bucket_coef(T);
+        const float beta = (float)fu->beta;
+        const uint64_t* coll = a.coll + (int64_t)u * kCollectCap;
+        s_sub[threadIdx.x] = 0ull;
+        if (threadIdx.x == 0) {
+            s_tau = ~0ull;
+            s_kept = 0ull;
+            s_star = -1;
+            s_nsel = 0;
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < n; i += kThreads) {
+            const uint64_t key = coll[i];
+            const float l = key_logit(key);
+            const uint64_t w = nuc_wfix(l, m, c);
+            // same coordinate as nuc_bucket; its fraction in the bucket, in [0, 1)
+            const float d = m - l;
+            const float f = (d > 0.f ? d * cb : 0.f) - beta;
+            int sb = (int)(f * (float)kSub);
+            sb = sb < 0 ? 0 : (sb >= kSub ? kSub - 1 : sb);
+            s_key[i] = key;
+            s_w[i] = w;
+            s_sb[i] = (uint8_t)sb;
+            atomicAdd((unsigned long long*)&s_sub[sb], (unsigned long long)w);
+        }
+        __syncthreads();
+        const double target = (double)a.rows[b].top_p * (double)fu->Zfix;
+        const uint64_t A = fu->Afix;
+        {
+            const uint64_t mine = s_sub[threadIdx.x];
+            uint64_t tot;
+            const uint64_t before = block_exclusive_scan(mine, s_tmp, &tot);
+            const bool cand = mine != 0ull && (double)(A + before) < target;
+            if (cand) atomicMax(&s_star, (int)threadIdx.x);
+            __syncthreads();
+            if ((int)threadIdx.x == s_star) s_before = before;
+        }
+        __syncthreads();
+        const int star = s_star;
+        if (star < 0) {  // cannot happen: the bucket's first token qualifies
+            if (threadIdx.x == 0) fu->status = 1;
+            __syncthreads();
+            continue;
+        }
+        for (int i = threadIdx.x; i < n; i += kThreads)
+            if (s_sb[i] == star) s_sel[atomicAdd(&s_nsel, 1)] = (uint16_t)i;
+        __syncthreads();
+        const int nsel = s_nsel;
+        const uint64_t A2 = A + s_before;
+        for (int base = 0; base < nsel; base += kThreads * kOwn) {
+            uint64_t key[kOwn], pre[kOwn];
+#pragma unroll
+            for (int q = 0; q < kOwn; q++) {
+                const int i = base + q * kThreads + (int)threadIdx.x;
+                key[q] = i < nsel ? s_key[s_sel[i]] : ~0ull;  // placeholder, never kept
+                pre[q] = 0ull;
+            }
+            for (int j = 0; j < nsel; j++) {
+                const int sj = s_sel[j];
+                const uint64_t kj = s_key[sj], wj = s_w[sj];
+#pragma unroll
+                for (int q = 0; q < kOwn; q++) pre[q] += kj > key[q] ? wj : 0ull;
+            }
+#pragma unroll
+            for (int q = 0; q < kOwn; q++) {
+                const int i = base + q * kThreads + (int)threadIdx.x;
+                if (i < nsel && (double)(A2 + pre[q]) < target) {
+                    atomicMin(&s_tau, (unsigned long long)key[q]);
+                    atomicAdd(&s_kept, (unsigned long long)s_w[s_sel[i]]);
+                }
+            }
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            fu->tau = s_tau;
+            fu->Sfix = A2 + s_kept;
         }
         __syncthreads();
     }

@@ -5,7 +5,7 @@
 // double-buffered vectors, and leaves one small record per unit it touches:
 //   * greedy rows:   the best (logit, lowest id) key of the segment;
 //   * top-k rows:    the segment's best 64 keys, descending (k <= 64);
-//   * full-vocab:    {segment max m, sum of exp((l - m) / T)} (online).
+//   * full-vocab:    per (tile, wave): {max m, sum of exp((l - m) / T)}.
 // Selection uses raw logits (the ranking does not depend on T > 0), so the
 // candidate sets are exact; probabilities are formed later in fp64.
 //
@@ -31,8 +31,6 @@ struct RowpassSmem {
     uint64_t cbuf[kWaves][kCandBuf];
     uint64_t lists[kWaves][kWave];
     uint64_t red[kWaves];
-    float redm[kWaves];
-    double reds[kWaves];
 };
 
 // Running top-64 of one wave.
@@ -146,70 +144,40 @@ __device__ __forceinline__ void seg_greedy(const void* row, int64_t start, int64
     if (threadIdx.x == 0) out->keys[0] = r;
 }
 
-// (m, s) pairs: s = sum of exp((l - m) / T).  Combining is exact up to one
-// fp64 rounding per term; fixed combination trees keep it deterministic.
-__device__ __forceinline__ void ms_combine(float& m, double& s, float m2, double s2, double invT) {
-    const float mm = fmaxf(m, m2);
-    if (mm == -INFINITY) {
-        m = mm;
-        s = 0.0;
-        return;
-    }
-    const double a = (m == mm) ? s : s * exp(((double)m - (double)mm) * invT);
-    const double b = (m2 == mm) ? s2 : s2 * exp(((double)m2 - (double)mm) * invT);
-    m = mm;
-    s = a + b;
-}
-
-__device__ __forceinline__ void wave_ms_combine(float& m, double& s, double invT) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-        const float m2 = __shfl_xor(m, o, kWave);
-        const double s2 = __shfl_xor(s, o, kWave);
-        ms_combine(m, s, m2, s2, invT);
-    }
-}
-
+// Full-vocab rows: per tile, every wave leaves {max, sum of exp((l - max)/T)}
+// of the part it read (exp2 terms in fp32, the wave sum in fp64 over a fixed
+// lane tree).  The records are indexed by tile, so how the tiles were split
+// over workgroups never changes the result.
 template <int DT, bool kAligned>
-__device__ __forceinline__ void seg_full(const void* row, int64_t start, int64_t end, float T, RowpassSmem& sm,
-                         PartSlot* out) {
+__device__ __forceinline__ void seg_full(const void* row, int64_t start, int64_t end, float T,
+                                         FullStat* rec) {
     using TS = TileShape<DT>;
-    const double invT = 1.0 / (double)T;
-    float c = (float)(1.4426950408889634 / (double)T);
-    c = fminf(c, 3.0e38f);
-    float m = -INFINITY;
-    double s = 0.0;
-    stream_range<DT, kAligned>(row, start, end, [&](float (&v)[TS::kE], int64_t, bool) __attribute__((always_inline)) {
+    const float c = exp2_coef(T);
+    const int w = wave_id();
+    stream_range<DT, kAligned>(row, start, end, [&](float (&v)[TS::kE], int64_t t0, bool)
+                                                    __attribute__((always_inline)) {
         // out-of-range elements read as -inf and add nothing
-        float vmax = -INFINITY;
+        float m = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < TS::kE; i++) vmax = fmaxf(vmax, v[i]);
-        if (vmax > m) {
-            s = (m == -INFINITY) ? 0.0 : s * exp(((double)m - (double)vmax) * invT);
-            m = vmax;
-        }
+        for (int i = 0; i < TS::kE; i++) m = fmaxf(m, v[i]);
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
         if (m > -INFINITY) {
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < TS::kE; i++) acc[i & 3] += exp2f((v[i] - m) * c);
-            s += (double)((acc[0] + acc[1]) + (acc[2] + acc[3]));
+        }
+        double s = (double)((acc[0] + acc[1]) + (acc[2] + acc[3]));
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1) s += __shfl_down(s, o, kWave);
+        if (lane_id() == 0) {
+            FullStat r;
+            r.m = m;
+            r.pad = 0.f;
+            r.s = s;
+            rec[(t0 / TS::kTile) * kWaves + w] = r;
         }
     });
-    wave_ms_combine(m, s, invT);
-    if (lane_id() == 0) {
-        sm.redm[wave_id()] = m;
-        sm.reds[wave_id()] = s;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float mm = sm.redm[0];
-        double ss = sm.reds[0];
-        for (int i = 1; i < kWaves; i++) ms_combine(mm, ss, sm.redm[i], sm.reds[i], invT);
-        FullStat* fs = reinterpret_cast<FullStat*>(out);
-        fs->m = mm;
-        fs->pad = 0.f;
-        fs->s = ss;
-    }
 }
 
 // The workgroups split the tiles of position k's units evenly (see
@@ -243,7 +211,8 @@ __global__ __launch_bounds__(kThreads) void rowpass_kernel(StepArgs a, int k) {
         else if (cls == CLS_TOPK)
             seg_topk<DT, kAligned>(row, start, end, a.rows[b].k_eff, sm, out);
         else
-            seg_full<DT, kAligned>(row, start, end, a.rows[b].T, sm, out);
+            seg_full<DT, kAligned>(row, start, end, a.rows[b].T,
+                                   a.tstat + (int64_t)u * a.ntiles * kWaves);
         t += tu1 - tu0;
         __syncthreads();  // LDS is reused by the next piece
     }

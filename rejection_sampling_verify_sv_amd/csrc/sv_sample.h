@@ -21,15 +21,10 @@
 
 namespace sv {
 
-__device__ __forceinline__ float exp2_coef(float T) {
-    float c = (float)(1.4426950408889634 / (double)T);
-    return fminf(c, 3.0e38f);
-}
-
 struct DrawCtx {
     bool nucleus, resid;
     float mt, md, c;
-    double zt, zd, invT;
+    double zt, zd;
     uint64_t tau_t, tau_d;
 };
 
@@ -42,27 +37,27 @@ __device__ __forceinline__ DrawCtx draw_ctx(const RowInfo& ri) {
     x.c = exp2_coef(ri.T);
     x.zt = ri.zt;
     x.zd = ri.zd;
-    x.invT = 1.0 / (double)ri.T;
     x.tau_t = ri.tau_t;
     x.tau_d = ri.tau_d;
     return x;
 }
 
 // Draw weights of token `id`: the residual (p - q)+ and the target weight
-// (unnormalised exp2 terms on untruncated rows, exact cut masses over Z_S on
-// nucleus rows).
+// (unnormalised exp2 terms on untruncated rows, fixed-point cut masses over
+// the kept mass on nucleus rows).
 __device__ __forceinline__ void draw_weights(const DrawCtx& x, float lt, float ld, uint32_t id,
-                                             const double* ebk, double* wr, double* wp) {
+                                             double* wr, double* wp) {
     if (x.nucleus) {
         // only tokens kept on the target side carry mass in either sum
         *wp = 0.0;
         *wr = 0.0;
         if (make_key(lt, id) >= x.tau_t) {
-            const double p = fn_weight(lt, x.mt, x.invT, ebk) / x.zt;
+            const double p = (double)nuc_wfix(lt, x.mt, x.c) / x.zt;
             *wp = p;
             if (x.resid) {
-                const double q =
-                    (make_key(ld, id) >= x.tau_d) ? fn_weight(ld, x.md, x.invT, ebk) / x.zd : 0.0;
+                const double q = (make_key(ld, id) >= x.tau_d)
+                                     ? (double)nuc_wfix(ld, x.md, x.c) / x.zd
+                                     : 0.0;
                 const double d = p - q;
                 *wr = d > 0.0 ? d : 0.0;
             }
@@ -85,11 +80,6 @@ __device__ __forceinline__ void draw_weights(const DrawCtx& x, float lt, float l
 template <int DT, bool kAligned>
 __global__ __launch_bounds__(kThreads) void sample_sums_kernel(StepArgs a) {
     using TS = TileShape<DT>;
-    // the bucket scales live in LDS: a global load inside the streaming loop
-    // would make every wait drain the prefetched tile as well
-    __shared__ double s_ebk[kNB];
-    for (int i = threadIdx.x; i < kNB; i += kThreads) s_ebk[i] = a.ebk[i];
-    __syncthreads();
     const int n = a.pos[a.K + 1].n_sample;
     const int64_t T = (int64_t)n * a.ntiles;
     int64_t t = flat_begin(T, gridDim.x, blockIdx.x);
@@ -119,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void sample_sums_kernel(StepArgs a) {
                 const int64_t id = elem_id<DT>(t0, i);
                 if (!full && id >= end) continue;
                 double wr, wp;
-                draw_weights(x, vt[i], vd[i], (uint32_t)id, s_ebk, &wr, &wp);
+                draw_weights(x, vt[i], vd[i], (uint32_t)id, &wr, &wp);
                 sr += wr;
                 sp += wp;
             }
@@ -220,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(StepArgs a) {
             if (id < a.V && id < cstart + TS::kTile) {
                 double wr, wp;
                 draw_weights(x, load_one<DT>(trow, id), x.resid ? load_one<DT>(drow, id) : 0.f,
-                             (uint32_t)id, a.ebk, &wr, &wp);
+                             (uint32_t)id, &wr, &wp);
                 wi = use_r ? wr : wp;
             }
             w[i] = wi;

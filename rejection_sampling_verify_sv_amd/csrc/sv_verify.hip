@@ -2,10 +2,9 @@
 //
 // Launch sequence for one verify step (all on the caller's stream, no host
 // synchronisation, no device reads on the host):
-//   init_kernel                   zero the work counters, e^(-b/32) table
+//   init_kernel                   zero the work counters
 //   plan_kernel                   classify rows, initialise outputs, list the
 //                                 units of position 0
-//   fn_zero_kernel                clear the nucleus histograms
 //   for k = 0 .. K:
 //     rowpass_kernel<k>           stream the units live at position k
 //     fn_hist / fn_select /
@@ -19,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdio.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "sv.h"
 #include "sv_decide.h"
@@ -35,8 +36,8 @@ constexpr int kMaxDraft = 1024;  // init_kernel clears K+2 <= kNB counters
 
 struct Plan {
     int tile, ntiles;
-    size_t off_rows, off_pos, off_ulist, off_flist, off_slist, off_parts, off_chunks, off_fnu,
-        off_hi, off_lo, off_cnt, off_coll, off_ebk, bytes;
+    size_t off_rows, off_pos, off_ulist, off_flist, off_slist, off_parts, off_tstat, off_chunks,
+        off_fnu, off_hist, off_coll, bytes;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -61,13 +62,11 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
     p->off_flist = take(sizeof(int32_t) * units * (size_t)(K + 1));
     p->off_slist = take(sizeof(int32_t) * (size_t)B);
     p->off_parts = take(sizeof(PartSlot) * slots);
+    p->off_tstat = take(sizeof(FullStat) * units * p->ntiles * kWaves);
     p->off_chunks = take(sizeof(double2) * (size_t)B * p->ntiles * kWaves);
     p->off_fnu = take(sizeof(FnUnit) * units);
-    p->off_hi = take(sizeof(uint64_t) * units * kNB);
-    p->off_lo = take(sizeof(uint64_t) * units * kNB);
-    p->off_cnt = take(sizeof(uint32_t) * units * kNB);
+    p->off_hist = take(sizeof(uint64_t) * slots * kNB);
     p->off_coll = take(sizeof(uint64_t) * units * kCollectCap);
-    p->off_ebk = take(sizeof(double) * kNB);
     p->bytes = off;
     return true;
 }
@@ -80,9 +79,9 @@ int hip_fail(hipError_t e) {
 }
 
 // Launch order of one step; sv_launch_count / sv_launch_name describe it.
-constexpr int kPre = 3;
+constexpr int kPre = 2;
 constexpr int kPerPos = 6;
-const char* const kPreNames[kPre] = {"init", "plan", "fn_zero"};
+const char* const kPreNames[kPre] = {"init", "plan"};
 const char* const kPosNames[kPerPos] = {"rowpass", "fn_hist", "fn_select",
                                         "fn_collect", "fn_resolve", "decide"};
 int launch_count(int K) { return kPre + kPerPos * (K + 1) + 2; }
@@ -94,11 +93,68 @@ const char* launch_name(int K, int i) {
     return (i == kPre + kPerPos * (K + 1)) ? "sample_sums" : "sample_pick";
 }
 
+// The streaming kernels split their tiles evenly over the grid, so the grid
+// is one resident wave of workgroups: compute units x workgroups each unit
+// holds at the kernel's register and LDS use (at most kGrid, the record
+// slots reserved per position).  A second, partial wave would double the
+// time of the workgroups in it.
+struct Grids {
+    unsigned rowpass, hist, collect, sums;
+};
+
+template <class Kern>
+unsigned resident_grid(Kern kernel, int cus) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    const long g = (long)cus * per_cu;
+    return (unsigned)(g < kGrid ? g : kGrid);
+}
+
+constexpr int kMaxDevices = 64;
+
+template <int DT, bool kAligned>
+int grids_for_device(Grids* out) {
+    static std::mutex mu;
+    static Grids cache[kMaxDevices];
+    static bool have[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev >= 0 && dev < kMaxDevices && have[dev]) {
+        *out = cache[dev];
+        return SV_OK;
+    }
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (cus < 1) cus = 1;
+    Grids g;
+    g.rowpass = resident_grid(rowpass_kernel<DT, kAligned>, cus);
+    g.hist = resident_grid(fn_hist_kernel<DT, kAligned>, cus);
+    g.collect = resident_grid(fn_collect_kernel<DT, kAligned>, cus);
+    g.sums = resident_grid(sample_sums_kernel<DT, kAligned>, cus);
+    (void)hipGetLastError();
+    if (dev >= 0 && dev < kMaxDevices) {
+        cache[dev] = g;
+        have[dev] = true;
+    }
+    *out = g;
+    return SV_OK;
+}
+
 // ev (optional, launch_count+1 events): ev[i] is recorded just before launch
 // i and ev[launch_count] after the last launch.
 template <int DT, bool kAligned>
-int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepArgs a, FnWork fw,
-               double* ebk, hipStream_t st, hipEvent_t const* ev) {
+int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepArgs a,
+               hipStream_t st, hipEvent_t const* ev) {
+    Grids g;
+    const int rc = grids_for_device<DT, kAligned>(&g);
+    if (rc != SV_OK) return rc;
+    a.g_row = (int)g.rowpass;
+    a.g_hist = (int)g.hist;
     int n = 0;
     auto mark = [&]() {
         if (ev) (void)hipEventRecord(ev[n], st);
@@ -108,27 +164,25 @@ int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepAr
     const unsigned unit_grid = (unsigned)(2 * B < kGrid ? 2 * B : kGrid);
     const unsigned row_grid = (unsigned)(B < kGrid ? B : kGrid);
     mark();
-    init_kernel<<<(kNB + kThreads - 1) / kThreads, kThreads, 0, st>>>(a, ebk);
+    init_kernel<<<(a.K + 2 + kThreads - 1) / kThreads, kThreads, 0, st>>>(a);
     mark();
     plan_kernel<<<(B + kThreads - 1) / kThreads, kThreads, 0, st>>>(a, draft_len, params);
-    mark();
-    fn_zero_kernel<<<unit_grid, kThreads, 0, st>>>(a, fw);
     for (int k = 0; k <= a.K; k++) {
         mark();
-        rowpass_kernel<DT, kAligned><<<kGrid, kThreads, 0, st>>>(a, k);
+        rowpass_kernel<DT, kAligned><<<g.rowpass, kThreads, 0, st>>>(a, k);
         mark();
-        fn_hist_kernel<DT, kAligned><<<kGrid, kThreads, 0, st>>>(a, fw, k);
+        fn_hist_kernel<DT, kAligned><<<g.hist, kThreads, 0, st>>>(a, k);
         mark();
-        fn_select_kernel<<<unit_grid, kThreads, 0, st>>>(a, fw, k);
+        fn_select_kernel<<<unit_grid, kThreads, 0, st>>>(a, k);
         mark();
-        fn_collect_kernel<DT, kAligned><<<kGrid, kThreads, 0, st>>>(a, fw, k);
+        fn_collect_kernel<DT, kAligned><<<g.collect, kThreads, 0, st>>>(a, k);
         mark();
-        fn_resolve_kernel<<<unit_grid, kThreads, 0, st>>>(a, fw, k);
+        fn_resolve_kernel<<<unit_grid, kThreads, 0, st>>>(a, k);
         mark();
         decide_kernel<DT><<<(unsigned)B, kDecideThreads, 0, st>>>(a, k);
     }
     mark();
-    sample_sums_kernel<DT, kAligned><<<kGrid, kThreads, 0, st>>>(a);
+    sample_sums_kernel<DT, kAligned><<<g.sums, kThreads, 0, st>>>(a);
     mark();
     sample_pick_kernel<DT><<<row_grid, kThreads, 0, st>>>(a);
     mark();
@@ -184,13 +238,10 @@ static int verify_impl(const void* target_logits, const void* draft_logits,
     a.flist = reinterpret_cast<int32_t*>(ws + pl.off_flist);
     a.slist = reinterpret_cast<int32_t*>(ws + pl.off_slist);
     a.fn_unit = reinterpret_cast<FnUnit*>(ws + pl.off_fnu);
-    double* ebk = reinterpret_cast<double*>(ws + pl.off_ebk);
-    a.ebk = ebk;
-    FnWork fw;
-    fw.hi = reinterpret_cast<uint64_t*>(ws + pl.off_hi);
-    fw.lo = reinterpret_cast<uint64_t*>(ws + pl.off_lo);
-    fw.cnt = reinterpret_cast<uint32_t*>(ws + pl.off_cnt);
-    fw.coll = reinterpret_cast<uint64_t*>(ws + pl.off_coll);
+    a.tstat = reinterpret_cast<FullStat*>(ws + pl.off_tstat);
+    a.hist = reinterpret_cast<uint64_t*>(ws + pl.off_hist);
+    a.coll = reinterpret_cast<uint64_t*>(ws + pl.off_coll);
+    a.g_row = a.g_hist = 0;
 
     const size_t esz = (dt == SV_F32) ? 4 : 2;
     const bool aligned = reinterpret_cast<uintptr_t>(target_logits) % 16 == 0 &&
@@ -198,10 +249,10 @@ static int verify_impl(const void* target_logits, const void* draft_logits,
                          ((size_t)ts * esz) % 16 == 0 && ((size_t)ds * esz) % 16 == 0;
     hipStream_t st = static_cast<hipStream_t>(cfg->stream);
     if (dt == SV_F32)
-        return aligned ? launch_all<SV_F32, true>(draft_len, sampler_params, a, fw, ebk, st, ev)
-                       : launch_all<SV_F32, false>(draft_len, sampler_params, a, fw, ebk, st, ev);
-    return aligned ? launch_all<SV_BF16, true>(draft_len, sampler_params, a, fw, ebk, st, ev)
-                   : launch_all<SV_BF16, false>(draft_len, sampler_params, a, fw, ebk, st, ev);
+        return aligned ? launch_all<SV_F32, true>(draft_len, sampler_params, a, st, ev)
+                       : launch_all<SV_F32, false>(draft_len, sampler_params, a, st, ev);
+    return aligned ? launch_all<SV_BF16, true>(draft_len, sampler_params, a, st, ev)
+                   : launch_all<SV_BF16, false>(draft_len, sampler_params, a, st, ev);
 }
 
 extern "C" int sv_verify(const void* target_logits, const void* draft_logits,
