@@ -130,6 +130,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixed_samplers_b1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after the measurement, run 5 device-to-device copies of MIB MiB "
+                         "(the reference kernel for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the verify step "
@@ -248,6 +251,17 @@ def main():
         "useful_GBps_whole_step": round(alg_bytes_step / (ms_per_step * 1e-3) / 1e9, 1),
         "acceptance_rate": round(acc_rate, 4),
     }
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["calibration_copy_bytes"] = n
+        del src, dst
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on host cores)")
         cb, ref = cpu_baseline(wl)
