@@ -60,12 +60,6 @@ __device__ inline void close_row_invalid(const StepArgs& a, int b, int code) {
 // ---- wave arithmetic in a fixed order -------------------------------------
 // Sum over the wave, computed in one fixed tree and broadcast from lane 0,
 // so every lane holds the same bits.
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_down(v, o, kWave);
-    return __shfl(v, 0, kWave);
-}
-
 __device__ __forceinline__ double wave_incl_scan(double v) {
     const int lane = lane_id();
 #pragma unroll

@@ -76,6 +76,10 @@ struct FullStat {
     double s;
 };
 
+// 2^x by the hardware exp2 (about 1 ulp; results below 2^-126 may flush to
+// zero, far below anything these sums can resolve).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // exp(x / T) = exp2(x * c) with c = log2(e) / T (clamped so that c is finite).
 __host__ __device__ __forceinline__ float exp2_coef(float T) {
     const float c = (float)(1.4426950408889634 / (double)T);
@@ -94,9 +98,14 @@ constexpr int kCollectCap = 4096;   // boundary-bucket tokens resolved per unit
 constexpr double kFix = 1099511627776.0;            // 2^40
 constexpr double kUnfix = 1.0 / 1099511627776.0;    // 2^-40
 
+// floor(w * 2^40) for w = exp2((l - m) c) in [0, 1], from the float's fields
+// (the same value as converting through fp64, without fp64 instructions).
 __device__ __forceinline__ uint64_t nuc_wfix(float l, float m, float c) {
-    const float w = exp2f((l - m) * c);
-    return (uint64_t)((double)w * kFix);
+    const uint32_t b = __float_as_uint(fast_exp2((l - m) * c));
+    const uint64_t mant = (uint64_t)((b & 0x7FFFFFu) | 0x800000u);
+    const int sh = (int)(b >> 23) - 110;  // w = mant * 2^(e - 150), times 2^40
+    if (b == 0u || sh <= -24) return 0ull;
+    return sh >= 0 ? mant << (sh < 24 ? sh : 24) : mant >> -sh;  // w <= 1 keeps sh <= 17
 }
 
 // Bucket scale 64 / T, clamped finite like exp2_coef.
@@ -222,6 +231,15 @@ __device__ __forceinline__ void unpack_tile(const RawTile& r, float (&v)[TileSha
     }
 }
 
+// threadIdx.x behind an empty asm: values derived from it are recomputed
+// where used instead of being hoisted into registers that stay live across
+// the whole streaming loop.
+__device__ __forceinline__ int tid_opaque() {
+    int t = (int)threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
 // Element-wise load of a tile; elements at or past `end` read as -inf.  The
 // index is clamped instead of branched on, so every load is issued before the
 // first wait.  Requires start < end.
@@ -261,19 +279,17 @@ __device__ __forceinline__ void load_tile_tail(const void* row, int64_t start, i
     const char* base = static_cast<const char*>(row) + start * Elt<DT>::kSize;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (uint32_t)nvec * 16u);
     RawTile r;
+    const int tid = tid_opaque();
 #pragma unroll
     for (int j = 0; j < kLoads; j++)
-        r.q[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (j * kThreads + (int)threadIdx.x) * 16,
-                                                      0, 2 /* nt */);
+        r.q[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (j * kThreads + tid) * 16, 0, 2 /* nt */);
     unpack_tile<DT>(r, v);
 #pragma unroll
     for (int j = 0; j < kLoads; j++) {
-        const int vi = j * kThreads + (int)threadIdx.x;
+        const int vi = j * kThreads + tid;
 #pragma unroll
-        for (int e = 0; e < kVec; e++) {
-            const int i = vi * kVec + e;
-            if (i >= n) v[j * kVec + e] = -INFINITY;
-        }
+        for (int e = 0; e < kVec; e++)
+            if (vi * kVec + e >= n) v[j * kVec + e] = -INFINITY;
         if (vi == nvec && nvec * kVec < n) {  // the straddling vector
 #pragma unroll
             for (int e = 0; e < kVec; e++)
@@ -288,7 +304,7 @@ template <int DT>
 __device__ __forceinline__ int64_t elem_id(int64_t start, int idx) {
     constexpr int kVec = Elt<DT>::kVec;
     const int j = idx / kVec, e = idx % kVec;
-    return start + (int64_t)(j * kThreads + (int)threadIdx.x) * kVec + e;
+    return start + (int64_t)(j * kThreads + tid_opaque()) * kVec + e;
 }
 
 // Stream the elements [start, end) of a row (start tile-aligned) through
@@ -441,6 +457,33 @@ __device__ __forceinline__ int wave_id() { return (int)(threadIdx.x / kWave); }
 
 __device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
 
+// Exclusive prefix over the wave of a per-lane count c < 64 (bit planes
+// through ballots, no LDS); *total gets the wave sum.
+__device__ __forceinline__ int wave_excl_count(uint32_t c, int* total) {
+    int excl = 0, tot = 0;
+#pragma unroll
+    for (int bit = 0; bit < 6; bit++) {
+        const uint64_t m = __ballot((c >> bit) & 1u);
+        const uint32_t below =
+            __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        excl += (int)below << bit;
+        tot += __popcll(m) << bit;
+    }
+    *total = tot;
+    return excl;
+}
+
+// Relaxed atomic LDS accesses for values other waves update concurrently:
+// always re-read (never cached in registers), and kept in the LDS address
+// space so they wait on the LDS counter only, not on outstanding HBM loads.
+typedef __attribute__((address_space(3))) uint64_t lds_u64;
+__device__ __forceinline__ uint64_t lds_load_relaxed(const uint64_t* p) {
+    return __atomic_load_n((const lds_u64*)p, __ATOMIC_RELAXED);
+}
+__device__ __forceinline__ void lds_store_relaxed(uint64_t* p, uint64_t v) {
+    __atomic_store_n((lds_u64*)p, v, __ATOMIC_RELAXED);
+}
+
 // Order this wave's LDS accesses (writes by some lanes, reads by others).
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -455,6 +498,56 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
         v = w > v ? w : v;
     }
     return v;
+}
+
+// ---- wave reductions on the DPP network (no LDS round trips) --------------
+// The steps combine lanes pairwise inside quads, then rows of 16 (rotations),
+// then broadcast row results up the wave; lane 63 ends with the full result,
+// which readlane hands to every lane.  Lanes whose DPP source does not exist
+// see the identity.  The order of the combination is fixed, so results are
+// deterministic.  Every lane of the wave must be active.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float identity, float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(v),
+                                                      kCtrl, 0xf, 0xf, false));
+}
+template <int kCtrl>
+__device__ __forceinline__ double dpp_move(double identity, double v) {
+    const int64_t iv = __double_as_longlong(v), io = __double_as_longlong(identity);
+    const int lo = __builtin_amdgcn_update_dpp((int)io, (int)iv, kCtrl, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp((int)(io >> 32), (int)(iv >> 32), kCtrl, 0xf, 0xf,
+                                               false);
+    return __longlong_as_double((int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+__device__ __forceinline__ float readlane63(float v) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ double readlane63(double v) {
+    const int64_t iv = __double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)iv, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(iv >> 32), 63);
+    return __longlong_as_double((int64_t)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+    const float id = -INFINITY;
+    v = fmaxf(v, dpp_move<0xb1>(id, v));   // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_move<0x4e>(id, v));   // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_move<0x124>(id, v));  // row_ror:4
+    v = fmaxf(v, dpp_move<0x128>(id, v));  // row_ror:8
+    v = fmaxf(v, dpp_move<0x142>(id, v));  // row_bcast:15
+    v = fmaxf(v, dpp_move<0x143>(id, v));  // row_bcast:31
+    return readlane63(v);
+}
+template <class F>
+__device__ __forceinline__ F wave_sum(F v) {
+    const F id = (F)0;
+    v += dpp_move<0xb1>(id, v);
+    v += dpp_move<0x4e>(id, v);
+    v += dpp_move<0x124>(id, v);
+    v += dpp_move<0x128>(id, v);
+    v += dpp_move<0x142>(id, v);
+    v += dpp_move<0x143>(id, v);
+    return readlane63(v);
 }
 
 // Block-wide max of a u64; every thread gets the result.  `tmp` holds kWaves.

@@ -149,9 +149,17 @@ __global__ __launch_bounds__(kThreads) void fn_select_kernel(StepArgs a, int k) 
     }
 }
 
+// Keys of the boundary bucket.  Each workgroup gathers its piece's keys in
+// LDS (one LDS counter update per wave and tile) and reserves space in the
+// unit's list with one global atomic per piece.  A piece with more than
+// kCollectCap keys means the bucket is too large to resolve anyway; the count
+// still records that.
 template <int DT, bool kAligned>
 __global__ __launch_bounds__(kThreads) void fn_collect_kernel(StepArgs a, int k) {
     using TS = TileShape<DT>;
+    static_assert(TS::kE <= 32, "hit mask is 32 bits");
+    __shared__ uint64_t s_keys[kCollectCap];
+    __shared__ int s_n, s_base;
     const int64_t T = (int64_t)a.pos[k].n_fn * a.ntiles;
     int64_t t = flat_begin(T, gridDim.x, blockIdx.x);
     const int64_t t_end = flat_begin(T, gridDim.x, blockIdx.x + 1);
@@ -165,43 +173,46 @@ __global__ __launch_bounds__(kThreads) void fn_collect_kernel(StepArgs a, int k)
         const int u = list[li];
         const int b = u >> 1, side = u & 1;
         FnUnit* fu = a.fn_unit + u;
-        if (fu->status != 0) continue;
+        if (fu->status != 0) continue;  // uniform over the block
+        if (threadIdx.x == 0) s_n = 0;
+        __syncthreads();
         const int beta = fu->beta;
         const float m = fu->m;
         const float cb = bucket_coef(a.rows[b].T);
         const int64_t start = tu0 * TS::kTile;
         int64_t end = tu1 * TS::kTile;
         if (end > a.V) end = a.V;
-        uint64_t* coll = a.coll + (int64_t)u * kCollectCap;
         stream_range<DT, kAligned>(unit_row<DT>(a, b, side, k), start, end,
                                    [&](float (&v)[TS::kE], int64_t t0, bool)
                                        __attribute__((always_inline)) {
             // past `end` elements read as -inf and land in the dropped bucket
             uint32_t hit = 0u;
 #pragma unroll
-            for (int i = 0; i < TS::kE; i++)
-                hit |= (nuc_bucket(v[i], m, cb) == beta ? 1u : 0u) << i;
+            for (int i = TS::kE - 1; i >= 0; i--)
+                hit = (hit << 1) | (nuc_bucket(v[i], m, cb) == beta ? 1u : 0u);
             if (__ballot(hit != 0u) == 0ull) return;
-            // one counter update per wave and tile
-            const int mine = __popc(hit);
-            int incl = mine;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const int t = __shfl_up(incl, o, kWave);
-                if (lane_id() >= o) incl += t;
-            }
-            const int total = __shfl(incl, kWave - 1, kWave);
+            int total;
+            const int excl = wave_excl_count((uint32_t)__popc(hit), &total);
             int base = 0;
-            if (lane_id() == kWave - 1) base = atomicAdd(&fu->ncoll, total);
-            int slot = __shfl(base, kWave - 1, kWave) + incl - mine;
+            if (lane_id() == 0) base = atomicAdd(&s_n, total);
+            int slot = __builtin_amdgcn_readfirstlane(base) + excl;
 #pragma unroll
             for (int i = 0; i < TS::kE; i++) {
-                if (hit & (1u << i)) {
-                    if (slot < kCollectCap) coll[slot] = make_key(v[i], (uint32_t)elem_id<DT>(t0, i));
+                if ((hit >> i) & 1u) {
+                    if (slot < kCollectCap) s_keys[slot] = make_key(v[i], (uint32_t)elem_id<DT>(t0, i));
                     slot++;
                 }
             }
         });
+        __syncthreads();
+        const int n = s_n;
+        if (threadIdx.x == 0) s_base = n > 0 ? atomicAdd(&fu->ncoll, n) : 0;
+        __syncthreads();
+        const int nb = s_base;
+        uint64_t* coll = a.coll + (int64_t)u * kCollectCap;
+        for (int i = threadIdx.x; i < n && i < kCollectCap && nb + i < kCollectCap; i += kThreads)
+            coll[nb + i] = s_keys[i];
+        __syncthreads();  // s_keys and s_n are reused by the next piece
     }
 }
 

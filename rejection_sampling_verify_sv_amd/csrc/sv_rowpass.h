@@ -31,22 +31,47 @@ struct RowpassSmem {
     uint64_t cbuf[kWaves][kCandBuf];
     uint64_t lists[kWaves][kWave];
     uint64_t red[kWaves];
+    uint64_t wthr[kWaves];  // each wave's current k-th key in this piece
 };
 
 // Running top-64 of one wave.
 struct WaveTopk {
     uint64_t lst;  // this lane's entry of the list (descending over lanes)
-    uint64_t thr;  // candidates need key > thr (same in every lane)
+    uint64_t thr;  // keys <= thr cannot be in the piece's top-k (same in every lane)
     int cnt;       // keys waiting in the wave's buffer (same in every lane)
 };
 
-// Merge up to 64 buffered candidates into the list.
-__device__ __forceinline__ void wt_flush(WaveTopk& st, uint64_t* cbuf, int k_eff) {
+// The largest k-th key any wave of the workgroup has published for this
+// piece.  A wave's k-th key bounds the piece's k-th key from below, so the
+// largest of them is a valid threshold for every wave; values only grow,
+// so a stale read is merely a weaker bound.
+__device__ __forceinline__ uint64_t shared_thr(const RowpassSmem& sm) {
+    uint64_t t = lds_load_relaxed(&sm.wthr[0]);
+#pragma unroll
+    for (int i = 1; i < kWaves; i++) {
+        const uint64_t x = lds_load_relaxed(&sm.wthr[i]);
+        t = x > t ? x : t;
+    }
+    return t;
+}
+
+// Buffered candidates hold the raw float bits and the id; the ranking key is
+// formed when they are merged, so nothing per element has to stay in
+// registers while candidates are appended.
+__device__ __forceinline__ uint64_t make_raw(float f, uint32_t id) {
+    return ((uint64_t)__float_as_uint(f) << 32) | (uint64_t)(0xFFFFFFFFu - id);
+}
+__device__ __forceinline__ uint64_t raw_to_key(uint64_t r) {
+    return ((uint64_t)ord32(__uint_as_float((uint32_t)(r >> 32))) << 32) | (r & 0xFFFFFFFFull);
+}
+
+// Merge up to 64 buffered candidates into the list; publish the new k-th key.
+__device__ __forceinline__ void wt_flush(WaveTopk& st, uint64_t* cbuf, int k_eff, RowpassSmem& sm) {
     const int lane = lane_id();
     wave_lds_sync();
     const int take = st.cnt < kWave ? st.cnt : kWave;
     const int left = st.cnt - take;
-    uint64_t c = lane < take ? cbuf[lane] : 0ull;
+    uint64_t c = lane < take ? raw_to_key(cbuf[lane]) : 0ull;
     const uint64_t rest = lane < left ? cbuf[kWave + lane] : 0ull;
     wave_lds_sync();
     if (lane < left) cbuf[lane] = rest;
@@ -54,21 +79,33 @@ __device__ __forceinline__ void wt_flush(WaveTopk& st, uint64_t* cbuf, int k_eff
     c = wave_sort_desc(c);
     st.lst = wave_merge_top(st.lst, c);
     const uint64_t kth = __shfl(st.lst, k_eff - 1, kWave);
-    if (kth > st.thr) st.thr = kth;
+    if (kth > st.thr) {
+        st.thr = kth;
+        if (lane == 0) lds_store_relaxed(&sm.wthr[wave_id()], kth);
+    }
 }
 
+// Top-k of one piece.  A tile is skipped after one max and one ballot when
+// no lane holds a value at or above the floor of the threshold; otherwise
+// every lane marks its candidates in a bit mask and the wave appends them to
+// its LDS buffer in rounds (one prefix count per round, no per-element
+// ballots), merging 64 at a time.
 template <int DT, bool kAligned>
-__device__ __forceinline__ void seg_topk(const void* row, int64_t start, int64_t end, int k_eff, RowpassSmem& sm,
-                         PartSlot* out) {
+__device__ __forceinline__ void seg_topk(const void* row, int64_t start, int64_t end, int k_eff,
+                                         RowpassSmem& sm, PartSlot* out) {
     using TS = TileShape<DT>;
+    static_assert(TS::kE <= 32, "candidate mask is 32 bits");
     const int w = wave_id(), lane = lane_id();
     uint64_t* cbuf = sm.cbuf[w];
+    if (lane == 0) sm.wthr[w] = 0ull;
+    __syncthreads();  // no wave reads a threshold left by the previous piece
     WaveTopk st;
     st.lst = 0ull;
     st.thr = 0ull;
     st.cnt = 0;
     bool first = true;
-    stream_range<DT, kAligned>(row, start, end, [&](float (&v)[TS::kE], int64_t t0, bool full) __attribute__((always_inline)) {
+    stream_range<DT, kAligned>(row, start, end, [&](float (&v)[TS::kE], int64_t t0, bool full)
+                                                    __attribute__((always_inline)) {
         float vmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < TS::kE; i++) vmax = fmaxf(vmax, v[i]);
@@ -88,22 +125,57 @@ __device__ __forceinline__ void seg_topk(const void* row, int64_t start, int64_t
             if (th > 0ull && th - 1ull > st.thr) st.thr = th - 1ull;
         }
         if (__ballot(vmax >= thr_floor(st.thr)) == 0ull) return;
+        const uint64_t tsh = shared_thr(sm);
+        if (tsh > st.thr) st.thr = tsh;
+        float fl = thr_floor(st.thr);
+        // masks are built by shifting in one bit per element (highest index
+        // first) so that no per-element constant has to live in a register
+        uint32_t bits = 0u;
 #pragma unroll
-        for (int i = 0; i < TS::kE; i++) {
-            const int64_t id = elem_id<DT>(t0, i);
-            const bool valid = full || id < end;
-            const uint64_t key = make_key(v[i], (uint32_t)id);
-            const bool c = valid && v[i] >= thr_floor(st.thr) && key > st.thr;
-            const uint64_t mask = __ballot(c);
-            if (mask) {
-                const int off = st.cnt + __popcll(mask & lanemask_lt());
-                if (c) cbuf[off] = key;
-                st.cnt += __popcll(mask);
-                if (st.cnt >= kWave) wt_flush(st, cbuf, k_eff);
+        for (int i = TS::kE - 1; i >= 0; i--) {
+            const bool valid = full || elem_id<DT>(t0, i) < end;
+            bits = (bits << 1) | (valid && v[i] >= fl ? 1u : 0u);
+        }
+        while (__ballot(bits != 0u) != 0ull) {
+            int total;
+            const uint32_t c = (uint32_t)__popc(bits);
+            const int excl = wave_excl_count(c, &total);
+            // this lane's candidates that still fit in the buffer
+            int room = kCandBuf - (st.cnt + excl);
+            room = room < 0 ? 0 : room;
+            const int nw = (int)c < room ? (int)c : room;
+            // the ids are formed inside the loop: hoisting 16-32 keys out of
+            // it would cost registers for the whole streaming loop
+            uint32_t id0 = (uint32_t)elem_id<DT>(t0, 0);
+            asm volatile("" : "+v"(id0));
+            int pos = st.cnt + excl, k = 0;
+#pragma unroll
+            for (int i = 0; i < TS::kE; i++) {
+                constexpr int kVec = Elt<DT>::kVec;
+                const bool bit = (bits >> i) & 1u;
+                if (bit && k < nw) {
+                    const uint32_t id = id0 + (uint32_t)((i / kVec) * kThreads * kVec + i % kVec);
+                    cbuf[pos + k] = make_raw(v[i], id);
+                }
+                k += bit ? 1 : 0;
+            }
+            if (nw == (int)c) {
+                bits = 0u;
+            } else {
+                for (int j = 0; j < nw; j++) bits &= bits - 1u;  // drop the written ones
+            }
+            st.cnt = st.cnt + total < kCandBuf ? st.cnt + total : kCandBuf;
+            if (st.cnt >= kWave) {
+                wt_flush(st, cbuf, k_eff, sm);
+                fl = thr_floor(st.thr);
+                uint32_t keep = 0u;
+#pragma unroll
+                for (int i = TS::kE - 1; i >= 0; i--) keep = (keep << 1) | (v[i] >= fl ? 1u : 0u);
+                bits &= keep;
             }
         }
     });
-    if (st.cnt > 0) wt_flush(st, cbuf, k_eff);
+    if (st.cnt > 0) wt_flush(st, cbuf, k_eff, sm);
     sm.lists[w][lane] = st.lst;
     __syncthreads();
     if (w == 0) {
@@ -145,8 +217,8 @@ __device__ __forceinline__ void seg_greedy(const void* row, int64_t start, int64
 }
 
 // Full-vocab rows: per tile, every wave leaves {max, sum of exp((l - max)/T)}
-// of the part it read (exp2 terms in fp32, the wave sum in fp64 over a fixed
-// lane tree).  The records are indexed by tile, so how the tiles were split
+// of the part it read (exp2 terms in fp32, the wave sum in fp64 over the
+// fixed DPP tree).  The records are indexed by tile, so how the tiles were split
 // over workgroups never changes the result.
 template <int DT, bool kAligned>
 __device__ __forceinline__ void seg_full(const void* row, int64_t start, int64_t end, float T,
@@ -157,19 +229,16 @@ __device__ __forceinline__ void seg_full(const void* row, int64_t start, int64_t
     stream_range<DT, kAligned>(row, start, end, [&](float (&v)[TS::kE], int64_t t0, bool)
                                                     __attribute__((always_inline)) {
         // out-of-range elements read as -inf and add nothing
-        float m = -INFINITY;
+        float lm = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < TS::kE; i++) m = fmaxf(m, v[i]);
-#pragma unroll
-        for (int o = kWave / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+        for (int i = 0; i < TS::kE; i++) lm = fmaxf(lm, v[i]);
+        const float m = wave_max_f32(lm);
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         if (m > -INFINITY) {
 #pragma unroll
-            for (int i = 0; i < TS::kE; i++) acc[i & 3] += exp2f((v[i] - m) * c);
+            for (int i = 0; i < TS::kE; i++) acc[i & 3] += fast_exp2((v[i] - m) * c);
         }
-        double s = (double)((acc[0] + acc[1]) + (acc[2] + acc[3]));
-#pragma unroll
-        for (int o = kWave / 2; o > 0; o >>= 1) s += __shfl_down(s, o, kWave);
+        const double s = wave_sum((double)((acc[0] + acc[1]) + (acc[2] + acc[3])));
         if (lane_id() == 0) {
             FullStat r;
             r.m = m;

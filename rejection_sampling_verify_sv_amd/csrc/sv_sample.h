@@ -24,7 +24,7 @@ namespace sv {
 struct DrawCtx {
     bool nucleus, resid;
     float mt, md, c;
-    double zt, zd;
+    double izt, izd;  // reciprocals of the normalisers (no division per token)
     uint64_t tau_t, tau_d;
 };
 
@@ -35,8 +35,8 @@ __device__ __forceinline__ DrawCtx draw_ctx(const RowInfo& ri) {
     x.mt = (float)ri.mt;
     x.md = (float)ri.md;
     x.c = exp2_coef(ri.T);
-    x.zt = ri.zt;
-    x.zd = ri.zd;
+    x.izt = 1.0 / ri.zt;
+    x.izd = ri.zd != 0.0 ? 1.0 / ri.zd : 0.0;
     x.tau_t = ri.tau_t;
     x.tau_d = ri.tau_d;
     return x;
@@ -52,22 +52,22 @@ __device__ __forceinline__ void draw_weights(const DrawCtx& x, float lt, float l
         *wp = 0.0;
         *wr = 0.0;
         if (make_key(lt, id) >= x.tau_t) {
-            const double p = (double)nuc_wfix(lt, x.mt, x.c) / x.zt;
+            const double p = (double)nuc_wfix(lt, x.mt, x.c) * x.izt;
             *wp = p;
             if (x.resid) {
                 const double q = (make_key(ld, id) >= x.tau_d)
-                                     ? (double)nuc_wfix(ld, x.md, x.c) / x.zd
+                                     ? (double)nuc_wfix(ld, x.md, x.c) * x.izd
                                      : 0.0;
                 const double d = p - q;
                 *wr = d > 0.0 ? d : 0.0;
             }
         }
     } else {
-        const float ep = exp2f((lt - x.mt) * x.c);
+        const float ep = fast_exp2((lt - x.mt) * x.c);
         *wp = (double)ep;
         if (x.resid) {
-            const float eq = exp2f((ld - x.md) * x.c);
-            const double d = (double)ep / x.zt - (double)eq / x.zd;
+            const float eq = fast_exp2((ld - x.md) * x.c);
+            const double d = fma((double)ep, x.izt, -((double)eq * x.izd));
             *wr = d > 0.0 ? d : 0.0;
         } else {
             *wr = 0.0;
@@ -113,11 +113,8 @@ __global__ __launch_bounds__(kThreads) void sample_sums_kernel(StepArgs a) {
                 sr += wr;
                 sp += wp;
             }
-#pragma unroll
-            for (int o = kWave / 2; o > 0; o >>= 1) {
-                sr += __shfl_down(sr, o, kWave);
-                sp += __shfl_down(sp, o, kWave);
-            }
+            sr = wave_sum(sr);
+            sp = wave_sum(sp);
             if (lane_id() == 0) {
                 double2 r;
                 r.x = sr;
