@@ -417,67 +417,89 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepArgs a, int 
         decide_full<DT>(a, b, k, ri);
 }
 
-// Zero the work counters (once per call).
-__global__ __launch_bounds__(kThreads) void init_kernel(StepArgs a) {
-    const int i = blockIdx.x * kThreads + threadIdx.x;
-    if (i < a.K + 2) {
+// One workgroup: zero the work counters, then classify every row, initialise
+// its outputs and list its position-0 units.  A row is invalid when T is
+// negative, NaN or infinite, top_p is not > 0, draft_len is outside [0, K] or
+// a read draft token is outside [0, V).
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const int32_t* draft_len,
+                                                            const sv_sampler_params* params) {
+    __shared__ int s_nu, s_nf;  // position-0 list lengths (LDS counters)
+    for (int i = threadIdx.x; i < a.K + 2; i += kPlanThreads) {
         a.pos[i].n_units = 0;
         a.pos[i].n_fn = 0;
         a.pos[i].n_sample = 0;
         a.pos[i].pad = 0;
     }
-}
-
-// Row classification, output initialisation and the position-0 unit lists
-// (one thread per row).  A row is invalid when T is negative, NaN or
-// infinite, top_p is not > 0, draft_len is outside [0, K] or a read draft
-// token is outside [0, V).
-__global__ __launch_bounds__(kThreads) void plan_kernel(StepArgs a, const int32_t* draft_len,
-                                                        const sv_sampler_params* params) {
-    const int b = blockIdx.x * kThreads + threadIdx.x;
-    if (b >= a.B) return;
-    const sv_sampler_params prm = params[b];
-    const int L = draft_len ? draft_len[b] : a.K;
-    const float T = prm.temperature, tp = prm.top_p;
-    const int tk = prm.top_k;
-    bool bad = !(T >= 0.f) || !(T < INFINITY) || !(tp > 0.f) || L < 0 || L > a.K;
-    if (!bad) {
-        for (int j = 0; j < L; j++) {
-            const int t = a.tokens[(int64_t)b * a.K + j];
-            if (t < 0 || t >= a.V) bad = true;
+    if (threadIdx.x == 0) s_nu = s_nf = 0;
+    __syncthreads();
+    for (int b = threadIdx.x; b < a.B; b += kPlanThreads) {
+        const sv_sampler_params prm = params[b];
+        const int L = draft_len ? draft_len[b] : a.K;
+        const float T = prm.temperature, tp = prm.top_p;
+        const int tk = prm.top_k;
+        bool bad = !(T >= 0.f) || !(T < INFINITY) || !(tp > 0.f) || L < 0 || L > a.K;
+        if (!bad) {
+            for (int j = 0; j < L; j++) {
+                const int t = a.tokens[(int64_t)b * a.K + j];
+                if (t < 0 || t >= a.V) bad = true;
+            }
+        }
+        int cls;
+        if (bad)
+            cls = CLS_ERROR;
+        else if (T == 0.f)
+            cls = CLS_GREEDY;
+        else if (tk > 0 && tk < a.V)
+            cls = (tk <= kMaxTopK) ? CLS_TOPK : CLS_UNSUP;
+        else
+            cls = (tp < 1.f) ? CLS_NUCLEUS : CLS_FULL;
+        RowInfo ri;
+        ri.cls = cls;
+        ri.L = L;
+        ri.status = (cls >= 0) ? ST_LIVE : ST_ERROR;
+        ri.acc = 0;
+        ri.kpos = 0;
+        ri.need = NEED_NONE;
+        ri.k_eff = (cls == CLS_TOPK) ? tk : 0;
+        ri.flags = 0;
+        ri.T = T;
+        ri.top_p = tp;
+        ri.li_t = ri.li_d = -1;
+        ri.mt = ri.zt = ri.md = ri.zd = 0.0;
+        ri.tau_t = ri.tau_d = 0ull;
+        if (cls >= 0) {
+            // position-0 units (same layout as append_units, LDS counters)
+            const bool draft = cls != CLS_GREEDY && 0 < L;
+            const int nu = draft ? 2 : 1;
+            int li = atomicAdd(&s_nu, nu);
+            a.ulist[li] = b * 2;
+            ri.li_t = li;
+            if (draft) {
+                a.ulist[li + 1] = b * 2 + 1;
+                ri.li_d = li + 1;
+            }
+            if (cls == CLS_NUCLEUS) {
+                const int f = atomicAdd(&s_nf, nu);
+                a.flist[f] = b * 2;
+                if (draft) a.flist[f + 1] = b * 2 + 1;
+            }
+        }
+        a.rows[b] = ri;
+        int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
+        for (int j = 0; j <= a.K; j++) o[j] = -1;
+        a.out_acc[b] = (cls == CLS_ERROR) ? -1 : (cls == CLS_UNSUP ? -2 : 0);
+        if (a.diag) {
+            double* d = a.diag + (int64_t)b * 4 * (a.K + 1);
+            for (int j = 0; j < 4 * (a.K + 1); j++)
+                d[j] = __longlong_as_double(0x7FF8000000000000ll);
         }
     }
-    int cls;
-    if (bad)
-        cls = CLS_ERROR;
-    else if (T == 0.f)
-        cls = CLS_GREEDY;
-    else if (tk > 0 && tk < a.V)
-        cls = (tk <= kMaxTopK) ? CLS_TOPK : CLS_UNSUP;
-    else
-        cls = (tp < 1.f) ? CLS_NUCLEUS : CLS_FULL;
-    RowInfo ri;
-    ri.cls = cls;
-    ri.L = L;
-    ri.status = (cls >= 0) ? ST_LIVE : ST_ERROR;
-    ri.acc = 0;
-    ri.kpos = 0;
-    ri.need = NEED_NONE;
-    ri.k_eff = (cls == CLS_TOPK) ? tk : 0;
-    ri.flags = 0;
-    ri.T = T;
-    ri.top_p = tp;
-    ri.li_t = ri.li_d = -1;
-    ri.mt = ri.zt = ri.md = ri.zd = 0.0;
-    ri.tau_t = ri.tau_d = 0ull;
-    if (cls >= 0) append_units(a, b, 0, ri);
-    a.rows[b] = ri;
-    int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
-    for (int j = 0; j <= a.K; j++) o[j] = -1;
-    a.out_acc[b] = (cls == CLS_ERROR) ? -1 : (cls == CLS_UNSUP ? -2 : 0);
-    if (a.diag) {
-        double* d = a.diag + (int64_t)b * 4 * (a.K + 1);
-        for (int j = 0; j < 4 * (a.K + 1); j++) d[j] = __longlong_as_double(0x7FF8000000000000ll);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        a.pos[0].n_units = s_nu;
+        a.pos[0].n_fn = s_nf;
     }
 }
 

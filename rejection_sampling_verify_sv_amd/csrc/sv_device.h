@@ -679,22 +679,19 @@ __device__ __forceinline__ const void* unit_row(const StepArgs& a, int b, int si
 // A row that continues to position k lists the units it needs there.
 __device__ inline void append_units(const StepArgs& a, int b, int k, RowInfo& ri) {
     const int64_t base = (int64_t)k * 2 * a.B;
-    int li = atomicAdd(&a.pos[k].n_units, 1);
+    const bool draft = ri.cls != CLS_GREEDY && k < ri.L;
+    const int nu = draft ? 2 : 1;
+    const int li = atomicAdd(&a.pos[k].n_units, nu);
     a.ulist[base + li] = b * 2;
     ri.li_t = li;
-    const bool draft = ri.cls != CLS_GREEDY && k < ri.L;
     if (draft) {
-        li = atomicAdd(&a.pos[k].n_units, 1);
-        a.ulist[base + li] = b * 2 + 1;
-        ri.li_d = li;
+        a.ulist[base + li + 1] = b * 2 + 1;
+        ri.li_d = li + 1;
     }
     if (ri.cls == CLS_NUCLEUS) {
-        int f = atomicAdd(&a.pos[k].n_fn, 1);
+        const int f = atomicAdd(&a.pos[k].n_fn, nu);
         a.flist[base + f] = b * 2;
-        if (draft) {
-            f = atomicAdd(&a.pos[k].n_fn, 1);
-            a.flist[base + f] = b * 2 + 1;
-        }
+        if (draft) a.flist[base + f + 1] = b * 2 + 1;
     }
 }
 

@@ -125,159 +125,181 @@ __global__ __launch_bounds__(kThreads) void sample_sums_kernel(StepArgs a) {
     }
 }
 
+// One workgroup: the drawn token of row b from its chunk masses.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void sample_pick_kernel(StepArgs a) {
+__device__ __forceinline__ void pick_row(const StepArgs& a, int b) {
     using TS = TileShape<DT>;
     constexpr int kE = TS::kE;
-    __shared__ int s_chunk, s_use_r, s_best, s_last;
-    __shared__ double s_base, s_W, s_target;
+    __shared__ int s_chunk, s_lastc, s_best, s_last;
+    __shared__ double s_base, s_lbase;
     __shared__ double s_tmp[kWaves];
     __shared__ double s_lo, s_hi, s_wy;
+    const RowInfo ri = a.rows[b];
+    const bool resid = ri.need == NEED_RESID;
+    const double u = (double)a.uniforms[(int64_t)b * (a.K + 1) + a.K];
+    // chunk masses: thread t sums the tiles [c0, c1), one chunk = one tile
+    // (its kWaves partials in wave order); block scans give the running sums
+    const double2* cs = a.chunks + (int64_t)b * a.ntiles * kWaves;
+    const int per = (a.ntiles + kThreads - 1) / kThreads;
+    const int c0 = min(a.ntiles, (int)threadIdx.x * per), c1 = min(a.ntiles, c0 + per);
+    double my_r = 0.0, my_p = 0.0;
+    for (int c = c0; c < c1; c++) {
+        double wr = 0.0, wp = 0.0;
+        for (int q = 0; q < kWaves; q++) {
+            wr += cs[c * kWaves + q].x;
+            wp += cs[c * kWaves + q].y;
+        }
+        my_r += wr;
+        my_p += wp;
+    }
+    double Wr, Wp;
+    (void)block_exclusive_scan(my_r, s_tmp, &Wr);
+    (void)block_exclusive_scan(my_p, s_tmp, &Wp);
+    const bool use_r = resid && Wr > 0.0;
+    const double W = use_r ? Wr : Wp;
+    const double target = u * W;
+    double tot;
+    const double excl = block_exclusive_scan(use_r ? my_r : my_p, s_tmp, &tot);
+    if (threadIdx.x == 0) {
+        s_chunk = 0x7FFFFFFF;
+        s_lastc = -1;
+        s_best = 0x7FFFFFFF;
+        s_last = -1;
+        s_lo = s_hi = s_wy = 0.0;
+    }
+    __syncthreads();
+    double S = excl, my_base = 0.0, my_lbase = 0.0;
+    int my_chunk = -1, my_last = -1;
+    for (int c = c0; c < c1; c++) {
+        double wc = 0.0;
+        for (int q = 0; q < kWaves; q++)
+            wc += use_r ? cs[c * kWaves + q].x : cs[c * kWaves + q].y;
+        if (!(wc > 0.0)) continue;
+        const double before = S;
+        S += wc;
+        my_last = c;
+        my_lbase = before;
+        if (my_chunk < 0 && target < S) {
+            my_chunk = c;
+            my_base = before;
+        }
+    }
+    if (my_chunk >= 0) atomicMin(&s_chunk, my_chunk);
+    if (my_last >= 0) atomicMax(&s_lastc, my_last);
+    __syncthreads();
+    // rounding can leave the target past every running sum: then the last
+    // chunk with positive mass is used
+    if (s_chunk != 0x7FFFFFFF && my_chunk == s_chunk) s_base = my_base;
+    if (s_chunk == 0x7FFFFFFF && my_last >= 0 && my_last == s_lastc) s_lbase = my_lbase;
+    __syncthreads();
+    if (s_chunk == 0x7FFFFFFF) {
+        if (threadIdx.x == 0) {
+            s_chunk = s_lastc;
+            s_base = s_lbase;
+        }
+        __syncthreads();
+    }
+    if (s_chunk < 0) {  // no positive mass anywhere: only reachable on corrupt stats
+        if (threadIdx.x == 0) {
+            a.out_acc[b] = -1;
+            a.rows[b].status = ST_ERROR;
+        }
+        __syncthreads();
+        return;
+    }
+    const int kpos = ri.kpos;
+    const DrawCtx x = draw_ctx(ri);
+    const void* trow = unit_row<DT>(a, b, 0, kpos);
+    const void* drow = x.resid ? unit_row<DT>(a, b, 1, kpos) : nullptr;
+    // thread t owns the contiguous run [start + t*kE, start + (t+1)*kE)
+    const int64_t cstart = (int64_t)s_chunk * TS::kTile;
+    const int64_t r0 = cstart + (int64_t)threadIdx.x * kE;
+    double w[kE];
+    double mine = 0.0;
+#pragma unroll
+    for (int i = 0; i < kE; i++) {
+        const int64_t id = r0 + i;
+        double wi = 0.0;
+        if (id < a.V && id < cstart + TS::kTile) {
+            double wr, wp;
+            draw_weights(x, load_one<DT>(trow, id), x.resid ? load_one<DT>(drow, id) : 0.f,
+                         (uint32_t)id, &wr, &wp);
+            wi = use_r ? wr : wp;
+        }
+        w[i] = wi;
+        mine += wi;
+    }
+    double total;
+    const double off = block_exclusive_scan(mine, s_tmp, &total);
+    S = s_base + off;
+    int found = -1;
+    double f_before = 0.0, f_after = 0.0, f_w = 0.0;
+    int lastpos = -1;
+    double l_before = 0.0, l_after = 0.0, l_w = 0.0;
+#pragma unroll
+    for (int i = 0; i < kE; i++) {
+        if (!(w[i] > 0.0)) continue;
+        const double before = S;
+        S += w[i];
+        lastpos = i;
+        l_before = before;
+        l_after = S;
+        l_w = w[i];
+        if (found < 0 && target < S) {
+            found = i;
+            f_before = before;
+            f_after = S;
+            f_w = w[i];
+        }
+    }
+    if (found >= 0) atomicMin(&s_best, (int)(r0 + found));
+    // rounding can push the target past this chunk's own running sums;
+    // then the chunk's last positive-weight token is taken (margin 0)
+    if (lastpos >= 0) atomicMax(&s_last, (int)(r0 + lastpos));
+    __syncthreads();
+    const bool fallback = s_best == 0x7FFFFFFF;
+    const int y = fallback ? s_last : s_best;
+    if (!fallback && found >= 0 && (int)(r0 + found) == y) {
+        s_lo = f_before;
+        s_hi = f_after;
+        s_wy = f_w;
+    } else if (fallback && lastpos >= 0 && (int)(r0 + lastpos) == y) {
+        s_lo = l_before;
+        s_hi = l_after;
+        s_wy = l_w;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        if (a.diag) {
+            double* dg = a.diag + (int64_t)b * 4 * (a.K + 1) + 4 * a.K;
+            const double lo = s_lo / W, hi = s_hi / W;
+            const double d1 = u - lo, d2 = hi - u;
+            dg[0] = s_wy / W;
+            dg[1] = lo;
+            dg[2] = hi;
+            dg[3] = fallback ? 0.0 : (d1 < d2 ? d1 : d2);
+        }
+        if (y < 0) {
+            a.out_acc[b] = -1;
+            a.rows[b].status = ST_ERROR;
+        } else {
+            int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
+            const int32_t* t = a.tokens + (int64_t)b * a.K;
+            for (int j = 0; j < kpos; j++) o[j] = t[j];
+            o[kpos] = y;
+            a.out_acc[b] = kpos;
+            a.rows[b].acc = kpos;
+            a.rows[b].status = ST_DONE;
+        }
+    }
+    __syncthreads();
+}
+// One workgroup per row that draws over the full vocabulary.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void sample_pick_kernel(StepArgs a) {
     const int n = a.pos[a.K + 1].n_sample;
     for (int si = blockIdx.x; si < n; si += gridDim.x) {
-        const int b = a.slist[si];
-        const RowInfo ri = a.rows[b];
-        const bool resid = ri.need == NEED_RESID;
-        const double u = (double)a.uniforms[(int64_t)b * (a.K + 1) + a.K];
-        if (threadIdx.x == 0) {
-            const double2* cs = a.chunks + (int64_t)b * a.ntiles * kWaves;
-            double Wr = 0.0, Wp = 0.0;
-            for (int c = 0; c < a.ntiles; c++) {
-                for (int q = 0; q < kWaves; q++) {
-                    Wr += cs[c * kWaves + q].x;
-                    Wp += cs[c * kWaves + q].y;
-                }
-            }
-            const int use_r = resid && Wr > 0.0;
-            const double W = use_r ? Wr : Wp;
-            const double target = u * W;
-            double S = 0.0, base = 0.0;
-            int chosen = -1, last = -1;
-            double last_base = 0.0;
-            for (int c = 0; c < a.ntiles; c++) {
-                double wc = 0.0;
-                for (int q = 0; q < kWaves; q++) wc += use_r ? cs[c * kWaves + q].x : cs[c * kWaves + q].y;
-                if (!(wc > 0.0)) continue;
-                const double before = S;
-                S += wc;
-                last = c;
-                last_base = before;
-                if (target < S) {
-                    chosen = c;
-                    base = before;
-                    break;
-                }
-            }
-            if (chosen < 0) {
-                chosen = last;
-                base = last_base;
-            }
-            s_chunk = chosen;
-            s_use_r = use_r;
-            s_base = base;
-            s_W = W;
-            s_target = target;
-            s_best = 0x7FFFFFFF;
-            s_last = -1;
-            s_lo = s_hi = s_wy = 0.0;
-        }
-        __syncthreads();
-        if (s_chunk < 0) {  // no positive mass anywhere: only reachable on corrupt stats
-            if (threadIdx.x == 0) {
-                a.out_acc[b] = -1;
-                a.rows[b].status = ST_ERROR;
-            }
-            __syncthreads();
-            continue;
-        }
-        const int kpos = ri.kpos;
-        const DrawCtx x = draw_ctx(ri);
-        const bool use_r = s_use_r;
-        const void* trow = unit_row<DT>(a, b, 0, kpos);
-        const void* drow = x.resid ? unit_row<DT>(a, b, 1, kpos) : nullptr;
-        // thread t owns the contiguous run [start + t*kE, start + (t+1)*kE)
-        const int64_t cstart = (int64_t)s_chunk * TS::kTile;
-        const int64_t r0 = cstart + (int64_t)threadIdx.x * kE;
-        double w[kE];
-        double mine = 0.0;
-#pragma unroll
-        for (int i = 0; i < kE; i++) {
-            const int64_t id = r0 + i;
-            double wi = 0.0;
-            if (id < a.V && id < cstart + TS::kTile) {
-                double wr, wp;
-                draw_weights(x, load_one<DT>(trow, id), x.resid ? load_one<DT>(drow, id) : 0.f,
-                             (uint32_t)id, &wr, &wp);
-                wi = use_r ? wr : wp;
-            }
-            w[i] = wi;
-            mine += wi;
-        }
-        double total;
-        const double off = block_exclusive_scan(mine, s_tmp, &total);
-        const double target = s_target;
-        double S = s_base + off;
-        int found = -1;
-        double f_before = 0.0, f_after = 0.0, f_w = 0.0;
-        int lastpos = -1;
-        double l_before = 0.0, l_after = 0.0, l_w = 0.0;
-#pragma unroll
-        for (int i = 0; i < kE; i++) {
-            if (!(w[i] > 0.0)) continue;
-            const double before = S;
-            S += w[i];
-            lastpos = i;
-            l_before = before;
-            l_after = S;
-            l_w = w[i];
-            if (found < 0 && target < S) {
-                found = i;
-                f_before = before;
-                f_after = S;
-                f_w = w[i];
-            }
-        }
-        if (found >= 0) atomicMin(&s_best, (int)(r0 + found));
-        // rounding can push the target past this chunk's own running sums;
-        // then the chunk's last positive-weight token is taken (margin 0)
-        if (lastpos >= 0) atomicMax(&s_last, (int)(r0 + lastpos));
-        __syncthreads();
-        const bool fallback = s_best == 0x7FFFFFFF;
-        const int y = fallback ? s_last : s_best;
-        if (!fallback && found >= 0 && (int)(r0 + found) == y) {
-            s_lo = f_before;
-            s_hi = f_after;
-            s_wy = f_w;
-        } else if (fallback && lastpos >= 0 && (int)(r0 + lastpos) == y) {
-            s_lo = l_before;
-            s_hi = l_after;
-            s_wy = l_w;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const double W = s_W;
-            if (a.diag) {
-                double* dg = a.diag + (int64_t)b * 4 * (a.K + 1) + 4 * a.K;
-                const double lo = s_lo / W, hi = s_hi / W;
-                const double d1 = u - lo, d2 = hi - u;
-                dg[0] = s_wy / W;
-                dg[1] = lo;
-                dg[2] = hi;
-                dg[3] = fallback ? 0.0 : (d1 < d2 ? d1 : d2);
-            }
-            if (y < 0) {
-                a.out_acc[b] = -1;
-                a.rows[b].status = ST_ERROR;
-            } else {
-                int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
-                const int32_t* t = a.tokens + (int64_t)b * a.K;
-                for (int j = 0; j < kpos; j++) o[j] = t[j];
-                o[kpos] = y;
-                a.out_acc[b] = kpos;
-                a.rows[b].acc = kpos;
-                a.rows[b].status = ST_DONE;
-            }
-        }
+        pick_row<DT>(a, a.slist[si]);
         __syncthreads();
     }
 }

@@ -2,8 +2,8 @@
 //
 // Launch sequence for one verify step (all on the caller's stream, no host
 // synchronisation, no device reads on the host):
-//   init_kernel                   zero the work counters
-//   plan_kernel                   classify rows, initialise outputs, list the
+//   plan_kernel                   one workgroup: zero the work counters,
+//                                 classify rows, initialise outputs, list the
 //                                 units of position 0
 //   for k = 0 .. K:
 //     rowpass_kernel<k>           stream the units live at position k
@@ -32,7 +32,7 @@ namespace {
 
 using namespace sv;
 
-constexpr int kMaxDraft = 1024;  // init_kernel clears K+2 <= kNB counters
+constexpr int kMaxDraft = 1024;
 
 struct Plan {
     int tile, ntiles;
@@ -79,9 +79,9 @@ int hip_fail(hipError_t e) {
 }
 
 // Launch order of one step; sv_launch_count / sv_launch_name describe it.
-constexpr int kPre = 2;
+constexpr int kPre = 1;
 constexpr int kPerPos = 6;
-const char* const kPreNames[kPre] = {"init", "plan"};
+const char* const kPreNames[kPre] = {"plan"};
 const char* const kPosNames[kPerPos] = {"rowpass", "fn_hist", "fn_select",
                                         "fn_collect", "fn_resolve", "decide"};
 int launch_count(int K) { return kPre + kPerPos * (K + 1) + 2; }
@@ -164,9 +164,7 @@ int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepAr
     const unsigned unit_grid = (unsigned)(2 * B < kGrid ? 2 * B : kGrid);
     const unsigned row_grid = (unsigned)(B < kGrid ? B : kGrid);
     mark();
-    init_kernel<<<(a.K + 2 + kThreads - 1) / kThreads, kThreads, 0, st>>>(a);
-    mark();
-    plan_kernel<<<(B + kThreads - 1) / kThreads, kThreads, 0, st>>>(a, draft_len, params);
+    plan_kernel<<<1, kPlanThreads, 0, st>>>(a, draft_len, params);
     for (int k = 0; k <= a.K; k++) {
         mark();
         rowpass_kernel<DT, kAligned><<<g.rowpass, kThreads, 0, st>>>(a, k);
