@@ -32,6 +32,7 @@ struct RowpassSmem {
     uint64_t lists[kWaves][kWave];
     uint64_t red[kWaves];
     uint64_t wthr[kWaves];  // each wave's current k-th key in this piece
+    uint64_t wq[kWaves];    // a key that at least ceil(k/4) of the wave's elements reach
 };
 
 // Running top-64 of one wave.
@@ -41,18 +42,26 @@ struct WaveTopk {
     int cnt;       // keys waiting in the wave's buffer (same in every lane)
 };
 
-// The largest k-th key any wave of the workgroup has published for this
-// piece.  A wave's k-th key bounds the piece's k-th key from below, so the
-// largest of them is a valid threshold for every wave; values only grow,
-// so a stale read is merely a weaker bound.
+// A threshold every wave of the workgroup may use for this piece, from what
+// the waves published:
+//   * a wave's k-th key: the wave holds k elements at or above it, so the
+//     piece's k-th key is at least that large;
+//   * the smallest of the four wq keys: each wave holds ceil(k/4) elements at
+//     or above its wq key and the waves' elements are distinct, so together
+//     they hold k elements at or above the smallest one.
+// Published values only grow, so a stale read is merely a weaker bound.
 __device__ __forceinline__ uint64_t shared_thr(const RowpassSmem& sm) {
     uint64_t t = lds_load_relaxed(&sm.wthr[0]);
+    uint64_t q = lds_load_relaxed(&sm.wq[0]);
 #pragma unroll
     for (int i = 1; i < kWaves; i++) {
         const uint64_t x = lds_load_relaxed(&sm.wthr[i]);
+        const uint64_t y = lds_load_relaxed(&sm.wq[i]);
         t = x > t ? x : t;
+        q = y < q ? y : q;
     }
-    return t;
+    // keys equal to the smallest wq key may still belong to the top k
+    return (q > 0ull && q - 1ull > t) ? q - 1ull : t;
 }
 
 // Buffered candidates hold the raw float bits and the id; the ranking key is
@@ -79,6 +88,8 @@ __device__ __forceinline__ void wt_flush(WaveTopk& st, uint64_t* cbuf, int k_eff
     c = wave_sort_desc(c);
     st.lst = wave_merge_top(st.lst, c);
     const uint64_t kth = __shfl(st.lst, k_eff - 1, kWave);
+    const uint64_t qth = __shfl(st.lst, (k_eff + kWaves - 1) / kWaves - 1, kWave);
+    if (lane == 0 && qth != 0ull) lds_store_relaxed(&sm.wq[wave_id()], qth);
     if (kth > st.thr) {
         st.thr = kth;
         if (lane == 0) lds_store_relaxed(&sm.wthr[wave_id()], kth);
@@ -97,7 +108,10 @@ __device__ __forceinline__ void seg_topk(const void* row, int64_t start, int64_t
     static_assert(TS::kE <= 32, "candidate mask is 32 bits");
     const int w = wave_id(), lane = lane_id();
     uint64_t* cbuf = sm.cbuf[w];
-    if (lane == 0) sm.wthr[w] = 0ull;
+    if (lane == 0) {
+        sm.wthr[w] = 0ull;
+        sm.wq[w] = 0ull;
+    }
     __syncthreads();  // no wave reads a threshold left by the previous piece
     WaveTopk st;
     st.lst = 0ull;
@@ -121,8 +135,11 @@ __device__ __forceinline__ void seg_topk(const void* row, int64_t start, int64_t
                 if (best == 0ull && valid && v[i] == vmax)
                     best = make_key(v[i], (uint32_t)elem_id<DT>(t0, i));
             }
-            const uint64_t th = __shfl(wave_sort_desc(best), k_eff - 1, kWave);
+            const uint64_t sl = wave_sort_desc(best);
+            const uint64_t th = __shfl(sl, k_eff - 1, kWave);
+            const uint64_t thq = __shfl(sl, (k_eff + kWaves - 1) / kWaves - 1, kWave);
             if (th > 0ull && th - 1ull > st.thr) st.thr = th - 1ull;
+            if (lane == 0 && thq != 0ull) lds_store_relaxed(&sm.wq[w], thq);
         }
         if (__ballot(vmax >= thr_floor(st.thr)) == 0ull) return;
         const uint64_t tsh = shared_thr(sm);
