@@ -97,9 +97,10 @@ def test_recipe_small_vocab_every_row(oracle_mod, dev, name):
     check(oracle_mod, wl, dev, label=f"{name}@V=20011")
 
 
-def _random_case(rng, B, K, V, dtype, T, top_k, top_p, scale=2.0, quant=None, draft_len=None):
+def _random_case(rng, B, K, V, dtype, T, top_k, top_p, scale=2.0, quant=None, draft_len=None,
+                 noise=0.6):
     t = rng.normal(0, scale, (B, K + 1, V))
-    d = t[:, :K] * 0.8 + rng.normal(0, scale * 0.6, (B, K, V))
+    d = t[:, :K] * 0.8 + rng.normal(0, scale * noise, (B, K, V))
     if quant:
         t, d = np.round(t * quant) / quant, np.round(d * quant) / quant
     prm = np.zeros(B, PARAMS_DTYPE)
@@ -170,3 +171,126 @@ def test_deterministic(dev):
     b = run_gpu(wl, dev)
     for x, y in zip(a, b):
         assert np.array_equal(x, y, equal_nan=True)
+
+
+def _to_padded(x, pad, offset, fill):
+    """Copy device tensor x [B, R, V] into the columns offset..offset+V of a
+    wider [B, R, V + pad] tensor whose other columns hold `fill`; returns the
+    strided view (row stride V + pad, base shifted by `offset` elements)."""
+    import torch
+
+    B, R, V = x.shape
+    base = torch.full((B, R, V + pad), fill, dtype=x.dtype, device=x.device)
+    view = base[:, :, offset:offset + V]
+    view.copy_(x)
+    return view
+
+
+@pytest.mark.parametrize("dtype,V,pad,offset", [
+    ("f32", 30008, 8, 0),     # aligned rows wider than V: the tail reads stop at V
+    ("f32", 30011, 13, 1),    # base and stride off the 16-byte grid
+    ("bf16", 50000, 16, 0),
+    ("bf16", 20011, 5, 3),
+], ids=["f32_aligned", "f32_unaligned", "bf16_aligned", "bf16_unaligned"])
+def test_strided_rows(oracle_mod, dev, dtype, V, pad, offset):
+    import torch
+
+    import rejection_sampling_verify_sv_amd as sv
+
+    rng = np.random.default_rng(V + pad + offset)
+    B = 48
+    wl = _random_case(rng, B, 3, V, dtype, 1.0, 20, 0.9)
+    prm = wl.params
+    prm["top_k"][::3] = 0            # nucleus rows
+    prm["top_p"][1::6] = 1.0         # and untruncated full-vocab rows
+    prm["temperature"][2::5] = 0.0   # and greedy rows
+    t, d, tok, dl, pt, uni = workloads.to_torch(wl, dev)
+    # +inf in the padding wins every comparison if a kernel ever reads it
+    tp = _to_padded(t, pad, offset, float("inf"))
+    dp = _to_padded(d, pad, offset, float("inf"))
+    assert tp.stride(1) == V + pad and tp.data_ptr() % 16 == (offset * tp.element_size()) % 16
+    _say(f"[gpu] strided rows {dtype} V={V} stride={V + pad} offset={offset}")
+    g_tok, g_acc, g_dg = sv.verify(tp, dp, tok, dl, pt, uni, diag=True)
+    torch.cuda.synchronize()
+    rep = compare(g_tok.cpu().numpy(), g_acc.cpu().numpy(), g_dg.cpu().numpy(),
+                  run_oracle(oracle_mod, wl))
+    _say(f"[gpu] strided rows: {rep.describe()}")
+    assert rep.ok, rep.describe()
+    assert rep.unsupported == 0 and rep.error_rows == 0
+    # the same inputs packed densely give the same bits
+    c_tok, c_acc, c_dg = run_gpu(wl, dev)
+    assert np.array_equal(c_tok, g_tok.cpu().numpy())
+    assert np.array_equal(c_acc, g_acc.cpu().numpy())
+    assert np.array_equal(c_dg, g_dg.cpu().numpy(), equal_nan=True)
+
+
+def test_side_stream(dev):
+    import torch
+
+    import rejection_sampling_verify_sv_amd as sv
+
+    wl = workloads.make("mixed_samplers_b1024", batch=96, vocab=20011)
+    ref = run_gpu(wl, dev)
+    ins = workloads.to_torch(wl, dev)
+    s = torch.cuda.Stream(device=dev)  # default priority
+    s.wait_stream(torch.cuda.current_stream(dev))
+    _say("[gpu] verify on a side stream")
+    tok, acc, dg = sv.verify(*ins, diag=True, stream=s)
+    s.synchronize()
+    for x, y in zip(ref, (tok.cpu().numpy(), acc.cpu().numpy(), dg.cpu().numpy())):
+        assert np.array_equal(x, y, equal_nan=True)
+
+
+def test_top_k_above_limit_unsupported(oracle_mod, dev):
+    import rejection_sampling_verify_sv_amd as sv
+
+    rng = np.random.default_rng(11)
+    V = 3000
+    wl = _random_case(rng, 24, 2, V, "f32", 1.0, 20, 0.9)
+    bad = [1, 4, 9, 17]
+    wl.params["top_k"][bad] = [sv.SV_MAX_TOP_K + 1, 100, V - 1, 2 * sv.SV_MAX_TOP_K]
+    wl.params["top_k"][[2, 3]] = [sv.SV_MAX_TOP_K, V]   # served: the limit itself, and top_k = V
+    rep, g_tok, g_acc = check(oracle_mod, wl, dev, label="top_k_above_limit")
+    assert g_acc[bad].tolist() == [-2] * len(bad)
+    assert (g_tok[bad] == -1).all()
+    assert rep.unsupported == len(bad)
+    assert rep.compared == wl.B - len(bad)
+
+
+@pytest.mark.parametrize("dtype,K,top_k,top_p", [
+    ("bf16", 8, 20, 0.9),
+    ("f32", 7, 0, 0.8),
+    ("bf16", 8, 0, 1.0),
+], ids=["topk_K8", "nucleus_K7", "untruncated_K8"])
+def test_long_drafts(oracle_mod, dev, dtype, K, top_k, top_p):
+    rng = np.random.default_rng(K * 100 + top_k)
+    B, V = 40, 20011
+    L = rng.integers(K - 2, K + 1, B).astype(np.int32)
+    wl = _random_case(rng, B, K, V, dtype, 1.0, top_k, top_p, draft_len=L)
+    # drafts close to the target so that acceptance runs deep into the draft
+    wl_close = _random_case(rng, B, K, V, dtype, 1.0, top_k, top_p, draft_len=L, noise=0.1)
+    for case, lab in ((wl, "random"), (wl_close, "close")):
+        rep, _, g_acc = check(oracle_mod, case, dev, label=f"long_drafts_{lab}_{dtype}_K{K}")
+        assert rep.unsupported == 0
+
+
+EXTREME_T = [
+    # label, V, dtype, T, top_k, top_p, scale
+    ("topk_T50", 20000, "f32", 50.0, 50, 0.95, 2.0),
+    ("topk_T1e-3", 20000, "bf16", 1e-3, 20, 0.9, 2.0),
+    ("greedy_equiv_top_k_1_T4", 20000, "f32", 4.0, 1, 1.0, 2.0),
+    ("untruncated_T8", 30011, "f32", 8.0, 0, 1.0, 2.0),
+    ("untruncated_T1e-3", 30011, "bf16", 1e-3, 0, 1.0, 2.0),
+    ("nucleus_T4", 30011, "f32", 4.0, 0, 0.9, 2.0),
+    ("nucleus_T1e-3", 30011, "bf16", 1e-3, 0, 0.9, 2.0),
+    ("nucleus_T1e-2_f32", 30011, "f32", 1e-2, 0, 0.95, 2.0),
+]
+
+
+@pytest.mark.parametrize("label,V,dtype,T,top_k,top_p,scale", EXTREME_T,
+                         ids=[e[0] for e in EXTREME_T])
+def test_extreme_temperature(oracle_mod, dev, label, V, dtype, T, top_k, top_p, scale):
+    rng = np.random.default_rng(zlib.crc32(label.encode()))
+    wl = _random_case(rng, 32, 2, V, dtype, T, top_k, top_p, scale=scale)
+    rep, _, _ = check(oracle_mod, wl, dev, label=label)
+    assert rep.unsupported == 0 and rep.error_rows == 0
