@@ -11,7 +11,9 @@
 //            histogram per (unit, workgroup) piece, written without atomics;
 //   select   per unit: sum the pieces, Z = total mass; the boundary bucket is
 //            the last non-empty bucket whose preceding mass is below top_p Z;
-//   collect  the keys of the boundary bucket's tokens;
+//   collect  the keys of the boundary bucket's tokens (a bucket too large for
+//            the workgroup's LDS is instead narrowed by a radix select
+//            over its keys that re-reads the row, see resolve_wide);
 //   resolve  per unit: a token of the boundary bucket is kept when the mass
 //            before the bucket plus the mass of the bucket's tokens ranked
 //            ahead of it (logit desc, id asc) is below top_p Z.  The cut key
@@ -151,9 +153,8 @@ __global__ __launch_bounds__(kThreads) void fn_select_kernel(StepArgs a, int k) 
 
 // Keys of the boundary bucket.  Each workgroup gathers its piece's keys in
 // LDS (one LDS counter update per wave and tile) and reserves space in the
-// unit's list with one global atomic per piece.  A piece with more than
-// kCollectCap keys means the bucket is too large to resolve anyway; the count
-// still records that.
+// unit's list with one global atomic per piece.  Keys beyond kCollectCap are
+// dropped but still counted: such a bucket is resolved from the row itself.
 template <int DT, bool kAligned>
 __global__ __launch_bounds__(kThreads) void fn_collect_kernel(StepArgs a, int k) {
     using TS = TileShape<DT>;
@@ -230,6 +231,168 @@ __global__ __launch_bounds__(kThreads) void fn_collect_kernel(StepArgs a, int k)
 constexpr int kSub = 256;
 static_assert(kSub == kThreads, "one sub-bucket per thread");
 
+// Boundary buckets of more than kCollectCap tokens (nearly flat rows, high
+// temperatures) are resolved by the unit's workgroup alone, re-reading the
+// row once per step of a radix select over the bucket's keys:
+//   range  the bucket's keys form one interval [lo, hi] of the key order
+//          (the bucket index never decreases as the logit falls, and equal
+//          logits share a bucket); one pass finds it;
+//   level  the interval is cut into at most kNB bins of 2^s consecutive
+//          keys; one pass adds every token's fixed-point weight and a count
+//          into its bin; the boundary bin is chosen as the boundary bucket
+//          was (last bin with mass whose preceding mass is below top_p Z),
+//          the mass of the bins ahead of it joins the mass before the
+//          interval, and the interval shrinks to that bin;
+//   rank   once the interval holds at most kThreads tokens (with 2^s = 1 it
+//          holds one, as keys are distinct), they are ranked one per thread
+//          like the boundary sub-bucket of the narrow path.
+// The first token of every chosen bin is kept, so tau stays in the interval.
+// Returns the cut key and the kept mass through fu.  Contains barriers; every
+// thread of the block calls it.
+template <int DT, bool kAligned>
+__device__ void resolve_wide(const void* row, int64_t V, FnUnit* fu, float m, float c, float cb,
+                             int beta, double target, uint64_t* s_mass /* kNB */,
+                             uint32_t* s_cnt /* kNB */, uint64_t* s_key /* kThreads */,
+                             uint64_t* s_w /* kThreads */, uint64_t* s_tmp /* kWaves */) {
+    using TS = TileShape<DT>;
+    constexpr int kPer = kNB / kThreads;  // bins per thread, in descending key order
+    __shared__ unsigned long long s_lo, s_hi, s_tau, s_kept;
+    __shared__ uint64_t s_A;
+    __shared__ int s_star, s_n;
+    __shared__ uint32_t s_bincnt;
+    static_assert(kNB == 2048, "11-bit bins");
+    if (threadIdx.x == 0) {
+        s_lo = ~0ull;
+        s_hi = 0ull;
+    }
+    __syncthreads();
+    {
+        uint64_t lo = ~0ull, hi = 0ull;
+        stream_range<DT, kAligned>(row, 0, V, [&](float (&v)[TS::kE], int64_t t0, bool)
+                                                  __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < TS::kE; i++) {
+                if (nuc_bucket(v[i], m, cb) == beta) {
+                    const uint64_t key = make_key(v[i], (uint32_t)elem_id<DT>(t0, i));
+                    lo = key < lo ? key : lo;
+                    hi = key > hi ? key : hi;
+                }
+            }
+        });
+        if (lo <= hi) {
+            atomicMin(&s_lo, (unsigned long long)lo);
+            atomicMax(&s_hi, (unsigned long long)hi);
+        }
+    }
+    __syncthreads();
+    uint64_t rlo = s_lo, rhi = s_hi;
+    uint64_t A = fu->Afix;
+    for (;;) {
+        // bin width 2^s with (rhi - rlo) >> s < kNB
+        const uint64_t span = rhi - rlo;
+        const int bits = span == 0ull ? 0 : 64 - __clzll((long long)span);
+        const int s = bits > 11 ? bits - 11 : 0;
+        for (int i = threadIdx.x; i < kNB; i += kThreads) {
+            s_mass[i] = 0ull;
+            s_cnt[i] = 0u;
+        }
+        if (threadIdx.x == 0) s_star = -1;
+        __syncthreads();
+        stream_range<DT, kAligned>(row, 0, V, [&](float (&v)[TS::kE], int64_t t0, bool)
+                                                  __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < TS::kE; i++) {
+                const uint64_t key = make_key(v[i], (uint32_t)elem_id<DT>(t0, i));
+                if (key >= rlo && key <= rhi) {
+                    const int bin = (int)((key - rlo) >> s);
+                    const uint64_t w = nuc_wfix(v[i], m, c);
+                    if (w != 0ull) atomicAdd((unsigned long long*)&s_mass[bin], (unsigned long long)w);
+                    atomicAdd(&s_cnt[bin], 1u);
+                }
+            }
+        });
+        __syncthreads();
+        uint64_t mass[kPer];
+        uint64_t mine = 0ull;
+#pragma unroll
+        for (int q = 0; q < kPer; q++) {
+            mass[q] = s_mass[kNB - 1 - (threadIdx.x * kPer + q)];
+            mine += mass[q];
+        }
+        uint64_t tot;
+        uint64_t run = A + block_exclusive_scan(mine, s_tmp, &tot);
+        int cand = -1;
+        uint64_t cand_before = 0ull;
+#pragma unroll
+        for (int q = 0; q < kPer; q++) {
+            if (mass[q] != 0ull && (double)run < target) {
+                cand = threadIdx.x * kPer + q;
+                cand_before = run;
+            }
+            run += mass[q];
+        }
+        if (cand >= 0) atomicMax(&s_star, cand);
+        __syncthreads();
+        const int star = s_star;
+        if (star < 0) {  // cannot happen: the interval's first token qualifies
+            if (threadIdx.x == 0) fu->status = 1;
+            __syncthreads();
+            return;
+        }
+        if (cand == star) {
+            s_A = cand_before;
+            s_bincnt = s_cnt[kNB - 1 - star];
+        }
+        __syncthreads();
+        A = s_A;
+        const uint32_t nbin = s_bincnt;
+        const uint64_t j = (uint64_t)(kNB - 1 - star);
+        rlo = rlo + (j << s);
+        const uint64_t top = rlo + ((1ull << s) - 1ull);
+        rhi = top < rhi ? top : rhi;
+        __syncthreads();  // s_tmp, s_mass and s_cnt are reused
+        if (nbin <= (uint32_t)kThreads || s == 0) break;
+    }
+    if (threadIdx.x == 0) {
+        s_n = 0;
+        s_tau = ~0ull;
+        s_kept = 0ull;
+    }
+    __syncthreads();
+    stream_range<DT, kAligned>(row, 0, V, [&](float (&v)[TS::kE], int64_t t0, bool)
+                                              __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < TS::kE; i++) {
+            const uint64_t key = make_key(v[i], (uint32_t)elem_id<DT>(t0, i));
+            if (key >= rlo && key <= rhi) {
+                const int slot = atomicAdd(&s_n, 1);
+                if (slot < kThreads) {
+                    s_key[slot] = key;
+                    s_w[slot] = nuc_wfix(v[i], m, c);
+                }
+            }
+        }
+    });
+    __syncthreads();
+    const int n = s_n < kThreads ? s_n : kThreads;
+    if ((int)threadIdx.x < n) {
+        const uint64_t key = s_key[threadIdx.x];
+        uint64_t pre = 0ull;
+        for (int j = 0; j < n; j++) pre += s_key[j] > key ? s_w[j] : 0ull;
+        if ((double)(A + pre) < target) {
+            atomicMin(&s_tau, (unsigned long long)key);
+            atomicAdd(&s_kept, (unsigned long long)s_w[threadIdx.x]);
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        fu->tau = s_tau;
+        fu->Sfix = A + s_kept;
+    }
+    __syncthreads();
+}
+
+template <int DT, bool kAligned>
 __global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, int k) {
     constexpr int kOwn = 4;  // boundary tokens a thread ranks per pass
     __shared__ uint64_t s_key[kCollectCap];
@@ -251,13 +414,20 @@ __global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, int k)
         const int n = fu->ncoll;
         __syncthreads();  // every thread has read fu before thread 0 may write it
         if (status != 0) continue;  // uniform over the block
-        if (n < 1 || n > kCollectCap) {
-            if (threadIdx.x == 0) fu->status = 1;  // boundary bucket too large
+        if (n < 1) {  // cannot happen: the boundary bucket has mass
+            if (threadIdx.x == 0) fu->status = 1;
             continue;
         }
         const float m = fu->m;
         const float T = a.rows[b].T;
         const float c = exp2_coef(T), cb = bucket_coef(T);
+        if (n > kCollectCap) {
+            resolve_wide<DT, kAligned>(unit_row<DT>(a, b, u & 1, k), a.V, fu, m, c, cb, fu->beta,
+                                       (double)a.rows[b].top_p * (double)fu->Zfix, s_key,
+                                       reinterpret_cast<uint32_t*>(s_w), s_key + kNB,
+                                       s_w + kNB, s_tmp);
+            continue;
+        }
         const float beta = (float)fu->beta;
         const uint64_t* coll = a.coll + (int64_t)u * kCollectCap;
         s_sub[threadIdx.x] = 0ull;

@@ -175,7 +175,7 @@ int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepAr
         mark();
         fn_collect_kernel<DT, kAligned><<<g.collect, kThreads, 0, st>>>(a, k);
         mark();
-        fn_resolve_kernel<<<unit_grid, kThreads, 0, st>>>(a, k);
+        fn_resolve_kernel<DT, kAligned><<<unit_grid, kThreads, 0, st>>>(a, k);
         mark();
         decide_kernel<DT><<<(unsigned)B, kDecideThreads, 0, st>>>(a, k);
     }

@@ -132,6 +132,11 @@ EDGE = [
     ("nucleus_tiny_top_p", 32, 2, 10000, "f32", 1.0, 0, 1e-3, {}),
     ("nucleus_all_equal", 16, 2, 3000, "f32", 1.0, 0, 0.5, {"scale": 0.0}),
     ("nucleus_top_k_ge_V", 32, 2, 4000, "bf16", 1.2, 5000, 0.7, {}),
+    # boundary buckets beyond the LDS collect capacity: the radix-select path
+    ("nucleus_wide_all_equal", 16, 2, 20011, "f32", 1.0, 0, 0.6, {"scale": 0.0}),
+    ("nucleus_wide_flat_f32", 24, 2, 151936, "f32", 2.0, 0, 0.8, {"scale": 0.1}),
+    ("nucleus_wide_ties_bf16", 24, 2, 90000, "bf16", 8.0, 0, 0.8, {"scale": 0.5, "quant": 64}),
+    ("nucleus_wide_T50", 24, 3, 90001, "f32", 50.0, 0, 0.9, {}),
 ]
 
 
@@ -139,7 +144,8 @@ EDGE = [
 def test_edge_cases(oracle_mod, dev, label, B, K, V, dtype, T, top_k, top_p, extra):
     rng = np.random.default_rng(zlib.crc32(label.encode()))
     wl = _random_case(rng, B, K, V, dtype, T, top_k, top_p, **extra)
-    check(oracle_mod, wl, dev, label=label)
+    rep, _, _ = check(oracle_mod, wl, dev, label=label)
+    assert rep.unsupported == 0 and rep.compared == B
 
 
 def test_ragged_draft_len_and_zero(oracle_mod, dev):
