@@ -68,7 +68,8 @@ typedef struct {
 /* Host-side descriptor of shapes, layout, stream and scratch. */
 typedef struct {
     int32_t batch;     /* B >= 1                                              */
-    int32_t max_draft; /* 1 <= K <= 1024 (drafted positions per row)         */
+    int32_t max_draft; /* 0 <= K <= 1024 (drafted positions per row); with
+                          K = 0 a step only draws one token per row       */
     int32_t vocab;     /* V >= 2, shared by target and draft                  */
     int32_t dtype;     /* SV_F32 or SV_BF16, same for both logits tensors     */
     int64_t target_row_stride; /* elements between consecutive (b, k) rows; 0 => V */
@@ -97,8 +98,10 @@ size_t sv_workspace_bytes(int32_t batch, int32_t max_draft, int32_t vocab, int32
  * one stream.
  *
  *   target_logits  [B][K+1] rows of V logits (row r at r*target_row_stride)
- *   draft_logits   [B][K]   rows of V logits (row r at r*draft_row_stride)
- *   draft_tokens   [B][K] int32; only the first draft_len[b] are read
+ *   draft_logits   [B][K]   rows of V logits (row r at r*draft_row_stride);
+ *                  may be NULL when K = 0
+ *   draft_tokens   [B][K] int32; only the first draft_len[b] are read; may be
+ *                  NULL when K = 0
  *   draft_len      [B] int32 in [0, K], or NULL (= K for every row)
  *   sampler_params [B] sv_sampler_params
  *   uniforms       [B][K+1] fp32 in [0, 1): column k is the accept test of
@@ -133,7 +136,33 @@ int sv_verify_profiled(const void* target_logits, const void* draft_logits,
                        int32_t* out_tokens, int32_t* out_accept_len, const sv_config* cfg,
                        void* const* events, int32_t n_events);
 
-/* Number of kernel launches in one step for max_draft K (0 if K < 1), and
+/*
+ * Draw one token per row from one row of logits, with the temperature,
+ * top_k / top_p truncation and inverse-CDF draw of the final draw of
+ * sv_verify (it is sv_verify with K = 0: the bonus draw at position 0).
+ * Uses: the draft model's own sampling step before a verify, which must
+ * apply the same truncation as the target (deniz.in page, section "Kesme her
+ * iki tarafta eşleşmek zorunda"), and plain decoding; the drawn ids stay in
+ * device memory for the next step ("Apple Silikon İçin Cihaz Üstü Çıkarımı
+ * Optimize Etme", section "Kelime parçacığı devrini GPU üzerinde tutun").
+ *
+ *   logits         [B] rows of V logits (row b at b*cfg->target_row_stride)
+ *   sampler_params [B] sv_sampler_params
+ *   uniforms       [B] fp32 in [0, 1)
+ *   out_tokens     [B] int32: the drawn token (the argmax on greedy rows), -1
+ *                  on a row whose status is not 0
+ *   out_status     [B] int32 or NULL: 0, -1 invalid row, -2 unsupported top_k
+ *   cfg            as for sv_verify; max_draft and draft_row_stride are
+ *                  ignored; the workspace must hold
+ *                  sv_workspace_bytes(B, 0, V, dtype) bytes; diag, if set, is
+ *                  [B][1][4] (slot K = 0 of sv_verify's layout).
+ * Same ownership, ordering, error and determinism rules as sv_verify.
+ */
+int sv_sample(const void* logits, const sv_sampler_params* sampler_params, const float* uniforms,
+              int32_t* out_tokens, int32_t* out_status, const sv_config* cfg);
+
+/* Number of kernel launches in one step for max_draft K (0 if K is outside
+ * [0, 1024]), and
  * the name of launch i ("plan", "rowpass", "decide", ...; NULL if out of
  * range).  Static strings, host only. */
 int32_t sv_launch_count(int32_t max_draft);

@@ -129,3 +129,19 @@ def dist(logits, temperature: float, top_k: int, top_p: float):
     if rc != 0:
         raise ValueError("distribution undefined (T <= 0 or no finite logit)")
     return prob, cm.value
+
+
+def sample(logits, params, uniforms, *, dtype="f32", nthreads: int = 0):
+    """One draw per row from the truncated distribution of each row of
+    logits [B, V] (float32, or uint16 bf16 bit patterns for dtype="bf16"):
+    the final draw of ``verify`` with no drafts (K = 0), that is
+    invcdf(dist(row, T, top_k, top_p), u) in ascending token-id order, or the
+    argmax (lowest id on ties) when T = 0.  uniforms [B] float32.
+    Returns (tokens [B], status [B] (0, or -1 for an invalid row),
+    diag [B, 1, 4])."""
+    logits = np.ascontiguousarray(logits)
+    B, V = logits.shape
+    out, acc, diag, _, _ = verify(logits.reshape(B, 1, V), None, np.zeros((B, 0), np.int32),
+                                  None, params, np.asarray(uniforms, np.float32).reshape(B, 1),
+                                  dtype=dtype, nthreads=nthreads)
+    return out[:, 0].copy(), acc, diag

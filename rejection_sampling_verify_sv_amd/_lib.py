@@ -19,8 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libsv.so")
 SV_F32, SV_BF16 = 0, 1
 SV_MAX_TOP_K = 64
 ERRORS = {0: "SV_OK", -1: "SV_EINVAL", -2: "SV_EWORKSPACE", -3: "SV_EHIP"}
-EXPORTED = ("sv_verify", "sv_verify_profiled", "sv_workspace_bytes", "sv_strerror",
-            "sv_launch_count", "sv_launch_name")
+EXPORTED = ("sv_verify", "sv_verify_profiled", "sv_sample", "sv_workspace_bytes",
+            "sv_strerror", "sv_launch_count", "sv_launch_name")
 
 
 class SvConfig(ctypes.Structure):
@@ -56,6 +56,8 @@ def load() -> ctypes.CDLL:
         lib.sv_verify_profiled.restype = ctypes.c_int
         lib.sv_verify_profiled.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.POINTER(SvConfig)]
                                            + [ctypes.c_void_p, ctypes.c_int32])
+        lib.sv_sample.restype = ctypes.c_int
+        lib.sv_sample.argtypes = [ctypes.c_void_p] * 5 + [ctypes.POINTER(SvConfig)]
         lib.sv_strerror.restype = ctypes.c_char_p
         lib.sv_strerror.argtypes = [ctypes.c_int]
         lib.sv_launch_count.restype = ctypes.c_int32
@@ -107,7 +109,8 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
 
     target [B, K+1, V], draft [B, K, V]: float32 or bfloat16 CUDA tensors.
     draft_tokens [B, K] int32; draft_len [B] int32 or None; params as in
-    params_tensor(); uniforms [B, K+1] float32.  Nothing is synchronised.
+    params_tensor(); uniforms [B, K+1] float32.  With K = 0, draft and
+    draft_tokens may be None.  Nothing is synchronised.
     """
     lib = load()
     if not target.is_cuda:
@@ -119,17 +122,24 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
         code = SV_BF16
     else:
         raise TypeError("logits must be float32 or bfloat16")
-    if draft.dtype != target.dtype or draft.device != dev:
-        raise TypeError("draft must match target's dtype and device")
     B, K1, V = target.shape
     K = K1 - 1
-    if tuple(draft.shape) != (B, K, V):
-        raise ValueError(f"draft shape {tuple(draft.shape)} != {(B, K, V)}")
     target, ts = _rows_layout(target, B * K1)
-    draft, ds = _rows_layout(draft, B * K)
-    tok = draft_tokens.to(dev, torch.int32).contiguous()
-    if tuple(tok.shape) != (B, K):
-        raise ValueError("draft_tokens must be [B, K]")
+    if K == 0 and draft is None:
+        ds = 0
+    else:
+        if draft.dtype != target.dtype or draft.device != dev:
+            raise TypeError("draft must match target's dtype and device")
+        if tuple(draft.shape) != (B, K, V):
+            raise ValueError(f"draft shape {tuple(draft.shape)} != {(B, K, V)}")
+        draft, ds = _rows_layout(draft, B * K) if K > 0 else (None, 0)
+    tok = None
+    if K > 0 or draft_tokens is not None:
+        tok = draft_tokens.to(dev, torch.int32).contiguous()
+        if tuple(tok.shape) != (B, K):
+            raise ValueError("draft_tokens must be [B, K]")
+        if K == 0:
+            tok = None
     dl = None
     if draft_len is not None:
         dl = draft_len.to(dev, torch.int32).contiguous()
@@ -161,7 +171,8 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
     cfg.workspace = wptr + pad
     cfg.workspace_bytes = workspace.numel() * workspace.element_size() - pad
     cfg.diag = dg.data_ptr() if dg is not None else None
-    args = (target.data_ptr(), draft.data_ptr(), tok.data_ptr(),
+    args = (target.data_ptr(), draft.data_ptr() if draft is not None else None,
+            tok.data_ptr() if tok is not None else None,
             dl.data_ptr() if dl is not None else None, prm.data_ptr(), uni.data_ptr(),
             out_tokens.data_ptr(), out_accept_len.data_ptr(), ctypes.byref(cfg))
     if events is None:
@@ -178,3 +189,64 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
             if t is not None:
                 t.record_stream(st)
     return out_tokens, out_accept_len, dg
+
+
+def sample(logits: torch.Tensor, params, uniforms: torch.Tensor, *, diag: bool = False,
+           workspace: torch.Tensor | None = None, out_tokens: torch.Tensor | None = None,
+           out_status: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+    """Enqueue one draw per row from the truncated distribution of each row of
+    logits [B, V] (float32 or bfloat16 CUDA tensor; rows may be strided).
+    params as in params_tensor(); uniforms [B] float32.  Returns
+    (out_tokens [B] int32, out_status [B] int32, diag [B, 1, 4] | None).
+    Nothing is synchronised."""
+    lib = load()
+    if not logits.is_cuda:
+        raise RuntimeError("sample needs GPU tensors (no CPU path exists)")
+    dev = logits.device
+    if logits.dtype == torch.float32:
+        code = SV_F32
+    elif logits.dtype == torch.bfloat16:
+        code = SV_BF16
+    else:
+        raise TypeError("logits must be float32 or bfloat16")
+    if logits.dim() != 2:
+        raise ValueError("logits must be [B, V]")
+    B, V = logits.shape
+    if logits.stride(1) != 1:
+        logits = logits.contiguous()
+    prm = params_tensor(params, dev)
+    if prm.shape[0] != B:
+        raise ValueError("params must have B rows")
+    uni = uniforms.to(dev, torch.float32).contiguous().reshape(-1)
+    if uni.shape[0] != B:
+        raise ValueError("uniforms must be [B]")
+    if out_tokens is None:
+        out_tokens = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_status is None:
+        out_status = torch.empty((B,), dtype=torch.int32, device=dev)
+    dg = torch.empty((B, 1, 4), dtype=torch.float64, device=dev) if diag else None
+    need = workspace_bytes(B, 0, V, code)
+    if need == 0:
+        raise ValueError("invalid shape for sv_sample")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    wptr = workspace.data_ptr()
+    pad = (-wptr) % 256
+    cfg = SvConfig()
+    cfg.batch, cfg.max_draft, cfg.vocab, cfg.dtype = B, 0, V, code
+    cfg.target_row_stride = logits.stride(0)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    cfg.stream = st.cuda_stream
+    cfg.workspace = wptr + pad
+    cfg.workspace_bytes = workspace.numel() * workspace.element_size() - pad
+    cfg.diag = dg.data_ptr() if dg is not None else None
+    rc = lib.sv_sample(logits.data_ptr(), prm.data_ptr(), uni.data_ptr(), out_tokens.data_ptr(),
+                       out_status.data_ptr(), ctypes.byref(cfg))
+    if rc != 0:
+        raise RuntimeError(f"sv_sample failed: {ERRORS.get(rc, rc)}: "
+                           f"{lib.sv_strerror(rc).decode()}")
+    if stream is not None:
+        for t in (logits, prm, uni, workspace, out_tokens, out_status, dg):
+            if t is not None:
+                t.record_stream(st)
+    return out_tokens, out_status, dg

@@ -37,13 +37,13 @@ constexpr int kMaxDraft = 1024;
 struct Plan {
     int tile, ntiles;
     size_t off_rows, off_pos, off_ulist, off_flist, off_slist, off_parts, off_tstat, off_chunks,
-        off_fnu, off_hist, off_coll, bytes;
+        off_fnu, off_hist, off_coll, off_status, bytes;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
-    if (B <= 0 || K < 1 || V < 2 || (dtype != SV_F32 && dtype != SV_BF16)) return false;
+    if (B <= 0 || K < 0 || V < 2 || (dtype != SV_F32 && dtype != SV_BF16)) return false;
     if (K > kMaxDraft || (int64_t)B * (K + 1) > 0x3FFFFFFFll || V > 0x7FFFFFFF - (1 << 16))
         return false;
     p->tile = (dtype == SV_F32) ? TileShape<SV_F32>::kTile : TileShape<SV_BF16>::kTile;
@@ -67,6 +67,7 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
     p->off_fnu = take(sizeof(FnUnit) * units);
     p->off_hist = take(sizeof(uint64_t) * slots * kNB);
     p->off_coll = take(sizeof(uint64_t) * units * kCollectCap);
+    p->off_status = take(sizeof(int32_t) * (size_t)B);  // sv_sample without out_status
     p->bytes = off;
     return true;
 }
@@ -201,14 +202,14 @@ static int verify_impl(const void* target_logits, const void* draft_logits,
                        const sv_sampler_params* sampler_params, const float* uniforms,
                        int32_t* out_tokens, int32_t* out_accept_len, const sv_config* cfg,
                        hipEvent_t const* ev) {
-    if (!cfg || !target_logits || !draft_logits || !draft_tokens || !sampler_params ||
-        !uniforms || !out_tokens || !out_accept_len)
+    if (!cfg || !target_logits || !sampler_params || !uniforms || !out_tokens || !out_accept_len)
         return SV_EINVAL;
     const int32_t B = cfg->batch, K = cfg->max_draft, V = cfg->vocab, dt = cfg->dtype;
+    if (K > 0 && (!draft_logits || !draft_tokens)) return SV_EINVAL;
     Plan pl;
     if (!make_plan(B, K, V, dt, &pl)) return SV_EINVAL;
     const int64_t ts = cfg->target_row_stride ? cfg->target_row_stride : V;
-    const int64_t ds = cfg->draft_row_stride ? cfg->draft_row_stride : V;
+    const int64_t ds = (K > 0 && cfg->draft_row_stride) ? cfg->draft_row_stride : V;
     if (ts < V || ds < V) return SV_EINVAL;
     if (!cfg->workspace || cfg->workspace_bytes < pl.bytes) return SV_EWORKSPACE;
     if (reinterpret_cast<uintptr_t>(cfg->workspace) % 256 != 0) return SV_EWORKSPACE;
@@ -243,8 +244,9 @@ static int verify_impl(const void* target_logits, const void* draft_logits,
 
     const size_t esz = (dt == SV_F32) ? 4 : 2;
     const bool aligned = reinterpret_cast<uintptr_t>(target_logits) % 16 == 0 &&
-                         reinterpret_cast<uintptr_t>(draft_logits) % 16 == 0 &&
-                         ((size_t)ts * esz) % 16 == 0 && ((size_t)ds * esz) % 16 == 0;
+                         ((size_t)ts * esz) % 16 == 0 &&
+                         (K == 0 || (reinterpret_cast<uintptr_t>(draft_logits) % 16 == 0 &&
+                                     ((size_t)ds * esz) % 16 == 0));
     hipStream_t st = static_cast<hipStream_t>(cfg->stream);
     if (dt == SV_F32)
         return aligned ? launch_all<SV_F32, true>(draft_len, sampler_params, a, st, ev)
@@ -266,7 +268,8 @@ extern "C" int sv_verify_profiled(const void* target_logits, const void* draft_l
                                   const sv_sampler_params* sampler_params, const float* uniforms,
                                   int32_t* out_tokens, int32_t* out_accept_len,
                                   const sv_config* cfg, void* const* events, int32_t n_events) {
-    if (!cfg || !events || cfg->max_draft < 1 || n_events < launch_count(cfg->max_draft) + 1)
+    if (!cfg || !events || cfg->max_draft < 0 || cfg->max_draft > kMaxDraft ||
+        n_events < launch_count(cfg->max_draft) + 1)
         return SV_EINVAL;
     for (int i = 0; i <= launch_count(cfg->max_draft); i++)
         if (!events[i]) return SV_EINVAL;
@@ -275,12 +278,31 @@ extern "C" int sv_verify_profiled(const void* target_logits, const void* draft_l
                        reinterpret_cast<hipEvent_t const*>(events));
 }
 
+extern "C" int sv_sample(const void* logits, const sv_sampler_params* sampler_params,
+                         const float* uniforms, int32_t* out_tokens, int32_t* out_status,
+                         const sv_config* cfg) {
+    if (!cfg) return SV_EINVAL;
+    sv_config c = *cfg;
+    c.max_draft = 0;
+    c.draft_row_stride = 0;
+    if (!out_status) {
+        Plan pl;
+        if (!make_plan(c.batch, 0, c.vocab, c.dtype, &pl)) return SV_EINVAL;
+        if (!c.workspace || c.workspace_bytes < pl.bytes ||
+            reinterpret_cast<uintptr_t>(c.workspace) % 256 != 0)
+            return SV_EWORKSPACE;
+        out_status = reinterpret_cast<int32_t*>(static_cast<char*>(c.workspace) + pl.off_status);
+    }
+    return verify_impl(logits, nullptr, nullptr, nullptr, sampler_params, uniforms, out_tokens,
+                       out_status, &c, nullptr);
+}
+
 extern "C" int32_t sv_launch_count(int32_t max_draft) {
-    return max_draft >= 1 ? launch_count(max_draft) : 0;
+    return (max_draft >= 0 && max_draft <= kMaxDraft) ? launch_count(max_draft) : 0;
 }
 
 extern "C" const char* sv_launch_name(int32_t max_draft, int32_t i) {
-    return max_draft >= 1 ? launch_name(max_draft, i) : nullptr;
+    return (max_draft >= 0 && max_draft <= kMaxDraft) ? launch_name(max_draft, i) : nullptr;
 }
 
 extern "C" const char* sv_strerror(int code) {

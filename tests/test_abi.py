@@ -36,7 +36,8 @@ def test_workspace_bytes_is_pure_and_validates(lib):
     f = _lib.workspace_bytes
     assert f(1024, 3, 151936, 0) > 0
     assert f(1024, 3, 151936, 0) == f(1024, 3, 151936, 0)
-    for bad in [(0, 3, 100, 0), (4, 0, 100, 0), (4, 3, 1, 0), (4, 3, 100, 7)]:
+    assert f(4, 0, 100, 0) > 0  # K = 0: a plain draw per row
+    for bad in [(0, 3, 100, 0), (4, -1, 100, 0), (4, 1025, 100, 0), (4, 3, 1, 0), (4, 3, 100, 7)]:
         assert f(*bad) == 0
 
 
@@ -60,3 +61,31 @@ def test_verify_rejects_bad_arguments_on_host(lib):
     assert lib.sv_verify(*args, ctypes.byref(cfg)) == -2
     assert b"workspace" in lib.sv_strerror(-2)
     assert lib.sv_strerror(0) == b"ok"
+
+
+def test_sample_and_k0_reject_bad_arguments_on_host(lib):
+    from rejection_sampling_verify_sv_amd import _lib
+    cfg = _lib.SvConfig()
+    cfg.batch, cfg.max_draft, cfg.vocab, cfg.dtype = 2, 1, 100, 0
+    dummy = ctypes.c_void_p(0x1000)
+    args = [dummy] * 8
+    bad = list(args)
+    bad[1] = None                                        # no draft with K = 1
+    assert lib.sv_verify(*bad, ctypes.byref(cfg)) == -1
+    cfg.max_draft = 0                                    # K = 0: draft may be NULL
+    bad[2] = None
+    assert lib.sv_verify(*bad, ctypes.byref(cfg)) == -2  # passes to the workspace check
+    s_args = [dummy] * 5
+    assert lib.sv_sample(*s_args, None) == -1            # no config
+    s_bad = list(s_args)
+    s_bad[0] = None                                      # no logits
+    assert lib.sv_sample(*s_bad, ctypes.byref(cfg)) == -1
+    cfg.max_draft = 7                                    # ignored by sv_sample
+    assert lib.sv_sample(*s_args, ctypes.byref(cfg)) == -2
+    s_bad = list(s_args)
+    s_bad[4] = None                                      # status kept in the workspace
+    assert lib.sv_sample(*s_bad, ctypes.byref(cfg)) == -2
+    cfg.batch = 0
+    assert lib.sv_sample(*s_args, ctypes.byref(cfg)) == -1
+    assert lib.sv_launch_count(0) == lib.sv_launch_count(1) - 6
+    assert lib.sv_launch_count(-1) == 0 and lib.sv_launch_count(1025) == 0
