@@ -98,14 +98,15 @@ constexpr int kCollectCap = 4096;   // boundary-bucket tokens resolved per unit
 constexpr double kFix = 1099511627776.0;            // 2^40
 constexpr double kUnfix = 1.0 / 1099511627776.0;    // 2^-40
 
-// floor(w * 2^40) for w = exp2((l - m) c) in [0, 1], from the float's fields
-// (the same value as converting through fp64, without fp64 instructions).
+// floor(w * 2^40) for w = exp2((l - m) c) in [0, 1], without branches or
+// 64-bit shifts: hi = floor(w 2^8) and the remainder w 2^40 - hi 2^32, which
+// one fma gives exactly (it is a multiple of w 2^40's unit in the last place
+// and below 2^32, so it fits a float's 24 bits), truncated to 32 bits.
 __device__ __forceinline__ uint64_t nuc_wfix(float l, float m, float c) {
-    const uint32_t b = __float_as_uint(fast_exp2((l - m) * c));
-    const uint64_t mant = (uint64_t)((b & 0x7FFFFFu) | 0x800000u);
-    const int sh = (int)(b >> 23) - 110;  // w = mant * 2^(e - 150), times 2^40
-    if (b == 0u || sh <= -24) return 0ull;
-    return sh >= 0 ? mant << (sh < 24 ? sh : 24) : mant >> -sh;  // w <= 1 keeps sh <= 17
+    const float w = fast_exp2((m - l) * -c);  // the same value as (l - m) c
+    const uint32_t hi = (uint32_t)(w * 256.0f);  // <= 256
+    const float rest = fmaf(-(float)hi, 4294967296.0f, w * 1099511627776.0f);
+    return ((uint64_t)hi << 32) | (uint64_t)(uint32_t)rest;
 }
 
 // Bucket scale 64 / T, clamped finite like exp2_coef.
@@ -115,10 +116,9 @@ __host__ __device__ __forceinline__ float bucket_coef(float T) {
 }
 
 __device__ __forceinline__ int nuc_bucket(float l, float m, float cb) {
-    const float d = m - l;
-    if (!(d > 0.f)) return d == 0.f ? 0 : kNB;  // the max itself; NaN dropped
-    const float z = d * cb;
-    return z < (float)kNB ? (int)z : kNB;
+    const float d = m - l;  // >= 0 for every token; NaN fails the compare below
+    const int z = (int)fminf(d * cb, (float)kNB);
+    return d >= 0.f ? z : kNB;
 }
 
 // Per (row, side) state of the nucleus cut at the current position.
@@ -130,7 +130,7 @@ struct FnUnit {
     float m;          // row max
     int32_t beta;     // boundary bucket
     int32_t ncoll;    // tokens appended by the collect pass
-    int32_t status;   // 0 ok, 1 boundary bucket too large to resolve, 2 no finite logit
+    int32_t status;   // 0 ok, 1 no boundary found (not reached), 2 no finite logit
 };
 
 // ---- element types and tiles ----------------------------------------------

@@ -75,11 +75,10 @@ __global__ __launch_bounds__(kThreads) void fn_hist_kernel(StepArgs a, int k) {
 #pragma unroll
             for (int i = 0; i < TS::kE; i++) {
                 const int bk = nuc_bucket(v[i], m, cb);
+                const uint64_t wf = nuc_wfix(v[i], m, c);
                 // elements past `end` read as -inf and land in the dropped bucket
-                if (bk < kNB) {
-                    const uint64_t wf = nuc_wfix(v[i], m, c);
-                    if (wf != 0ull) atomicAdd((unsigned long long*)&s_h[bk], (unsigned long long)wf);
-                }
+                if (bk < kNB && wf != 0ull)
+                    atomicAdd((unsigned long long*)&s_h[bk], (unsigned long long)wf);
             }
         });
         __syncthreads();
