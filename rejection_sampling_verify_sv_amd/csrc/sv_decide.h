@@ -346,8 +346,9 @@ __device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri) 
     }
 }
 
-// Nucleus rows: p(x) = [key(x) >= tau] w(x) / S with the fixed-point masses
-// of the cut computed by the nucleus kernels for this position.
+// Nucleus rows: p(x) = [key(x) >= tau] exp(t(x) / 64) / S with the anchor
+// coordinate t and the kept mass S of the cut computed by the nucleus kernels
+// for this position.
 template <int DT>
 __device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& ri) {
     const FnUnit ut = a.fn_unit[b * 2];
@@ -365,21 +366,21 @@ __device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& r
     if (!has_draft) {
         w.need = NEED_BONUS;
         w.kpos = k;
-        w.mt = (double)ut.m;
-        w.zt = (double)ut.Sfix;
+        w.mt = (double)ut.la;
+        w.zt = ut.S;
         w.tau_t = ut.tau;
         queue_draw(a, b);
         return;
     }
-    const float c = exp2_coef(ri.T);
+    const float cb = bucket_coef(ri.T);
     const int x = a.tokens[(int64_t)b * a.K + k];
     const float lx = load_one<DT>(unit_row<DT>(a, b, 0, k), x);
     const float ld = load_one<DT>(unit_row<DT>(a, b, 1, k), x);
     const double px = (make_key(lx, (uint32_t)x) >= ut.tau)
-                          ? (double)nuc_wfix(lx, ut.m, c) / (double)ut.Sfix
+                          ? exp((double)nuc_t(lx, ut.la, cb) * (1.0 / 64.0)) / ut.S
                           : 0.0;
     const double qx = (make_key(ld, (uint32_t)x) >= ud.tau)
-                          ? (double)nuc_wfix(ld, ud.m, c) / (double)ud.Sfix
+                          ? exp((double)nuc_t(ld, ud.la, cb) * (1.0 / 64.0)) / ud.S
                           : 0.0;
     const double acc = accept_prob(px, qx);
     const double uk = (double)a.uniforms[(int64_t)b * (a.K + 1) + k];
@@ -390,11 +391,11 @@ __device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& r
     } else {
         w.need = NEED_RESID;
         w.kpos = k;
-        w.mt = (double)ut.m;
-        w.zt = (double)ut.Sfix;
+        w.mt = (double)ut.la;
+        w.zt = ut.S;
         w.tau_t = ut.tau;
-        w.md = (double)ud.m;
-        w.zd = (double)ud.Sfix;
+        w.md = (double)ud.la;
+        w.zd = ud.S;
         w.tau_d = ud.tau;
         queue_draw(a, b);
     }
@@ -483,7 +484,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
             if (cls == CLS_NUCLEUS) {
                 const int f = atomicAdd(&s_nf, nu);
                 a.flist[f] = b * 2;
-                if (draft) a.flist[f + 1] = b * 2 + 1;
+                a.fn_unit[b * 2].rehist = 0;
+                if (draft) {
+                    a.flist[f + 1] = b * 2 + 1;
+                    a.fn_unit[b * 2 + 1].rehist = 0;
+                }
             }
         }
         a.rows[b] = ri;

@@ -87,27 +87,26 @@ __host__ __device__ __forceinline__ float exp2_coef(float T) {
 }
 
 // ---- masses for the full-vocab nucleus cut ---------------------------------
-// Weights w = exp((l - m) / T) <= 1 are taken in 40-bit fixed point, so every
-// sum of them is an exact integer whatever the order of the additions.
-// Buckets cut z = (m - l) / T into slices of width 1/64; a higher logit never
-// lands in a later bucket.  Tokens with z >= 32 have a fixed-point weight of
-// zero and fall into the dropped bucket kNB.
-constexpr int kNB = 2048;
+// A nucleus unit is measured against an anchor logit la: the largest of the
+// row's first 64 vectors (every piece of the row pass reads them and gets the
+// same value), or the row max on a second pass (below).  Token l sits at
+// t = (l - la) 64 / T, its weight relative to the anchor is exp(t / 64), and
+// it falls into bucket floor(t) + kHalf of a window of kNW buckets (slices of
+// 1/64 in (l - la) / T; a higher logit never lands in a lower bucket).
+// Within bucket b a weight is scale_b w_rel with
+// scale_b = exp((b - kHalf + 1) / 64) and w_rel = exp((frac(t) - 1) / 64) in
+// (0.984, 1], the latter in 31-bit fixed point, so a bucket's mass is scale_b
+// times an exact integer whatever the order of the additions.
+//   * t < -kHalf: at least 32 T below the anchor, hence below the row max;
+//     the weight is under e^-32 of the max's and the token is dropped;
+//   * t >= kHalf: the row max lies far above the anchor; the unit is then
+//     histogrammed again, anchored at its row max (where t <= 0).
+constexpr int kNW = 4096;
+constexpr int kHalf = kNW / 2;
 constexpr float kBucketScale = 64.0f;
-constexpr int kCollectCap = 4096;   // boundary-bucket tokens resolved per unit
-constexpr double kFix = 1099511627776.0;            // 2^40
-constexpr double kUnfix = 1.0 / 1099511627776.0;    // 2^-40
-
-// floor(w * 2^40) for w = exp2((l - m) c) in [0, 1], without branches or
-// 64-bit shifts: hi = floor(w 2^8) and the remainder w 2^40 - hi 2^32, which
-// one fma gives exactly (it is a multiple of w 2^40's unit in the last place
-// and below 2^32, so it fits a float's 24 bits), truncated to 32 bits.
-__device__ __forceinline__ uint64_t nuc_wfix(float l, float m, float c) {
-    const float w = fast_exp2((m - l) * -c);  // the same value as (l - m) c
-    const uint32_t hi = (uint32_t)(w * 256.0f);  // <= 256
-    const float rest = fmaf(-(float)hi, 4294967296.0f, w * 1099511627776.0f);
-    return ((uint64_t)hi << 32) | (uint64_t)(uint32_t)rest;
-}
+constexpr float kLog2e64 = 0.022542110013490055f;  // log2(e) / 64
+constexpr int kCollectCap = 4096;   // boundary-bucket tokens resolved in LDS per unit
+constexpr double kUnfix = 1.0 / 2147483648.0;    // 2^-31, the weights' fixed-point unit
 
 // Bucket scale 64 / T, clamped finite like exp2_coef.
 __host__ __device__ __forceinline__ float bucket_coef(float T) {
@@ -115,22 +114,46 @@ __host__ __device__ __forceinline__ float bucket_coef(float T) {
     return c < 3.0e38f ? c : 3.0e38f;
 }
 
-__device__ __forceinline__ int nuc_bucket(float l, float m, float cb) {
-    const float d = m - l;  // >= 0 for every token; NaN fails the compare below
-    const int z = (int)fminf(d * cb, (float)kNB);
-    return d >= 0.f ? z : kNB;
+// Window coordinate of logit l (NaN when l or la is NaN, or both are -inf).
+__device__ __forceinline__ float nuc_t(float l, float la, float cb) { return (l - la) * cb; }
+// t lies in the window (false for NaN).
+__device__ __forceinline__ bool nuc_in(float t) {
+    return t >= -(float)kHalf && t < (float)kHalf;
+}
+// Bucket of an in-window coordinate.
+__device__ __forceinline__ int nuc_bin(float t) { return (int)floorf(t) + kHalf; }
+
+// floor(w_rel 2^31) for w_rel = exp2((fr - 1) log2(e) / 64), fr = frac(t) in
+// [0, 1): below 2^31, so one 32-bit conversion gives it exactly; sums of up
+// to 2^33 of them fit 64 bits.
+__device__ __forceinline__ uint64_t nuc_wrel(float fr) {
+    const float w = fast_exp2(fmaf(fr, kLog2e64, -kLog2e64));
+    return (uint64_t)(uint32_t)(w * 2147483648.0f);
+}
+// Fixed-point weight of an in-window coordinate t, and its bucket.
+__device__ __forceinline__ uint64_t nuc_wfix_t(float t, int* bin) {
+    const float f = floorf(t);
+    *bin = (int)f + kHalf;
+    return nuc_wrel(t - f);
+}
+// scale_b: the weight of bucket b's upper edge relative to the anchor.
+__device__ __forceinline__ double nuc_scale(int b) {
+    return exp((double)(b - kHalf + 1) * (1.0 / 64.0));
 }
 
-// Per (row, side) state of the nucleus cut at the current position.
+// Per (row, side) state of the nucleus cut at the current position; masses
+// are relative to the anchor (a token weighs exp(t / 64)).
 struct FnUnit {
-    uint64_t Zfix;    // total mass
-    uint64_t Afix;    // mass of the buckets before the boundary bucket
-    uint64_t Sfix;    // kept mass
+    double Z;         // total mass
+    double A;         // mass of the buckets above the boundary bucket
+    double S;         // kept mass
     uint64_t tau;     // key of the last kept token
-    float m;          // row max
+    float la;         // anchor logit
     int32_t beta;     // boundary bucket
     int32_t ncoll;    // tokens appended by the collect pass
     int32_t status;   // 0 ok, 1 no boundary found (not reached), 2 no finite logit
+    int32_t rehist;   // set by the row pass: a token lies above the window
+    int32_t pad;
 };
 
 // ---- element types and tiles ----------------------------------------------
@@ -562,6 +585,18 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* tmp) {
     return r;
 }
 
+// Block-wide max of a float; every thread gets the result.  `tmp` holds kWaves.
+__device__ __forceinline__ float block_max_f32(float v, uint64_t* tmp) {
+    v = wave_max_f32(v);
+    __syncthreads();
+    if (lane_id() == 0) tmp[wave_id()] = (uint64_t)__float_as_uint(v);
+    __syncthreads();
+    float r = __uint_as_float((uint32_t)tmp[0]);
+#pragma unroll
+    for (int i = 1; i < kWaves; i++) r = fmaxf(r, __uint_as_float((uint32_t)tmp[i]));
+    return r;
+}
+
 // Bitonic sort (descending) of one u64 per lane across a wave.
 __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
     const int lane = lane_id();
@@ -663,7 +698,8 @@ struct StepArgs {
     int32_t* flist;        // [K+1][2B] nucleus units per position
     int32_t* slist;        // [B] rows that draw over the full vocabulary at the end
     FnUnit* fn_unit;       // [2B] nucleus cut of the current position
-    uint64_t* hist;        // [2B + kGrid][kNB] nucleus mass histograms, slot u + w
+    uint64_t* hist;        // [2B + kGrid][kNW] nucleus histograms of the row pass, slot u + w
+    uint64_t* hist2;       // [2B + kGrid][kNW] nucleus histograms anchored at the row max
     uint64_t* coll;        // [2B][kCollectCap] boundary-bucket keys
     int g_hist;            // grid of the histogram pass
 };
@@ -691,7 +727,11 @@ __device__ inline void append_units(const StepArgs& a, int b, int k, RowInfo& ri
     if (ri.cls == CLS_NUCLEUS) {
         const int f = atomicAdd(&a.pos[k].n_fn, nu);
         a.flist[base + f] = b * 2;
-        if (draft) a.flist[base + f + 1] = b * 2 + 1;
+        a.fn_unit[b * 2].rehist = 0;
+        if (draft) {
+            a.flist[base + f + 1] = b * 2 + 1;
+            a.fn_unit[b * 2 + 1].rehist = 0;
+        }
     }
 }
 

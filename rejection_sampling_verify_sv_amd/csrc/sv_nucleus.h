@@ -4,11 +4,14 @@
 // "Kesme her iki tarafta eşleşmek zorunda": both distributions are cut to the
 // smallest head of the ranking whose preceding mass stays below top_p.  With
 // top_k disabled that head can hold tens of thousands of tokens, so the cut is
-// located by mass instead of by sorting the row:
+// located by mass instead of by sorting the row.  Weights and buckets are
+// those of the anchor window (sv_device.h):
 //
-//   hist     every token's weight w = exp((l - m) / T) (m = row max) in 40-bit
-//            fixed point, added into bucket floor(64 (m - l) / T); one
-//            histogram per (unit, workgroup) piece, written without atomics;
+//   row pass every piece of a nucleus unit adds its tokens' fixed-point
+//            weights into its own LDS histogram over the window, written out
+//            whole (no atomics between workgroups);
+//   hist     only units with a token above the window: the same histogram
+//            again, anchored at the row max;
 //   select   per unit: sum the pieces, Z = total mass; the boundary bucket is
 //            the last non-empty bucket whose preceding mass is below top_p Z;
 //   collect  the keys of the boundary bucket's tokens (a bucket too large for
@@ -18,40 +21,38 @@
 //            before the bucket plus the mass of the bucket's tokens ranked
 //            ahead of it (logit desc, id asc) is below top_p Z.  The cut key
 //            tau (last kept token) and the kept mass S define the
-//            distribution p(i) = [key_i >= tau] w_i / S.
-// Fixed-point sums are exact, so the cut does not depend on the order of any
-// addition.  The streaming passes split the tiles of position k's nucleus
-// units evenly over the workgroups, like the row pass; the per-unit steps run
-// one workgroup per unit.
+//            distribution p(i) = [key_i >= tau] exp(t_i / 64) / S.
+// Within a bucket the masses are exact fixed-point integers; across buckets
+// they are combined in fp64 in one fixed order, so the cut is deterministic.
+// The streaming passes split the tiles of position k's nucleus units evenly
+// over the workgroups, like the row pass; the per-unit steps run one
+// workgroup per unit.
 #pragma once
 
 #include "sv_decide.h"
 
 namespace sv {
 
-// Row max of one unit from its per-(tile, wave) row-pass records; every
-// thread of the block gets it.  Contains barriers.
-__device__ inline float block_unit_max(const FullStat* rec, int n, float* tmp /* kWaves */) {
+// Max over the row-pass pieces of one unit (keys[0] holds each piece's max as
+// float bits); every thread of the block gets it.  Contains barriers.
+__device__ inline float unit_piece_max(const PartSlot* parts, RecRange r, uint64_t* tmp) {
     float m = -INFINITY;
-    for (int i = threadIdx.x; i < n; i += kThreads) m = fmaxf(m, rec[i].m);
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-    __syncthreads();
-    if (lane_id() == 0) tmp[wave_id()] = m;
-    __syncthreads();
-    float r = tmp[0];
-#pragma unroll
-    for (int i = 1; i < kWaves; i++) r = fmaxf(r, tmp[i]);
-    return r;
+    for (int i = threadIdx.x; i < r.count; i += kThreads)
+        m = fmaxf(m, __uint_as_float((uint32_t)parts[r.first + i].keys[0]));
+    return block_max_f32(m, tmp);
 }
 
+// Units marked by the row pass (a token above the anchor window): the
+// histogram again, anchored at the row max, so every token has t <= 0.
+// Pieces of other units are skipped without reading the row.
 template <int DT, bool kAligned>
 __global__ __launch_bounds__(kThreads) void fn_hist_kernel(StepArgs a, int k) {
     using TS = TileShape<DT>;
-    __shared__ uint64_t s_h[kNB];
-    __shared__ float s_red[kWaves];
-    const int nrec = a.ntiles * kWaves;
-    const int64_t T = (int64_t)a.pos[k].n_fn * a.ntiles;
+    __shared__ uint64_t s_h[kNW];
+    __shared__ uint64_t s_red[kWaves];
+    const int n = a.pos[k].n_fn;
+    const int n_units = a.pos[k].n_units;
+    const int64_t T = (int64_t)n * a.ntiles;
     int64_t t = flat_begin(T, gridDim.x, blockIdx.x);
     const int64_t t_end = flat_begin(T, gridDim.x, blockIdx.x + 1);
     const int32_t* list = a.flist + (int64_t)k * 2 * a.B;
@@ -60,12 +61,16 @@ __global__ __launch_bounds__(kThreads) void fn_hist_kernel(StepArgs a, int k) {
         const int64_t tu0 = t - (int64_t)li * a.ntiles;
         int64_t tu1 = tu0 + (t_end - t);
         if (tu1 > a.ntiles) tu1 = a.ntiles;
+        t += tu1 - tu0;
         const int u = list[li];
+        if (a.fn_unit[u].rehist == 0) continue;  // uniform over the block
         const int b = u >> 1, side = u & 1;
-        for (int i = threadIdx.x; i < kNB; i += kThreads) s_h[i] = 0ull;
-        const float m = block_unit_max(a.tstat + (int64_t)u * nrec, nrec, s_red);
-        const float T_ = a.rows[b].T;
-        const float c = exp2_coef(T_), cb = bucket_coef(T_);
+        const RowInfo& ri = a.rows[b];
+        const float m = unit_piece_max(
+            a.parts, unit_records(side ? ri.li_d : ri.li_t, n_units, a.ntiles, a.g_row), s_red);
+        const float cb = bucket_coef(ri.T);
+        for (int i = threadIdx.x; i < kNW; i += kThreads) s_h[i] = 0ull;
+        __syncthreads();
         const int64_t start = tu0 * TS::kTile;
         int64_t end = tu1 * TS::kTile;
         if (end > a.V) end = a.V;
@@ -74,75 +79,102 @@ __global__ __launch_bounds__(kThreads) void fn_hist_kernel(StepArgs a, int k) {
                                        __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < TS::kE; i++) {
-                const int bk = nuc_bucket(v[i], m, cb);
-                const uint64_t wf = nuc_wfix(v[i], m, c);
-                // elements past `end` read as -inf and land in the dropped bucket
-                if (bk < kNB && wf != 0ull)
-                    atomicAdd((unsigned long long*)&s_h[bk], (unsigned long long)wf);
+                const float tt = nuc_t(v[i], m, cb);
+                int bin;
+                const uint64_t w = nuc_wfix_t(tt, &bin);
+                if (nuc_in(tt)) atomicAdd((unsigned long long*)&s_h[bin], (unsigned long long)w);
             }
         });
         __syncthreads();
-        uint64_t* out = a.hist + (int64_t)(li + blockIdx.x) * kNB;
-        for (int i = threadIdx.x; i < kNB; i += kThreads) out[i] = s_h[i];
-        t += tu1 - tu0;
+        uint64_t* out = a.hist2 + (int64_t)(li + blockIdx.x) * kNW;
+        for (int i = threadIdx.x; i < kNW; i += kThreads) out[i] = s_h[i];
         __syncthreads();  // s_h is cleared for the next piece
     }
 }
 
-// One workgroup per unit: total mass, boundary bucket and row max.
+// One workgroup per unit: total mass, boundary bucket, anchor.
 __global__ __launch_bounds__(kThreads) void fn_select_kernel(StepArgs a, int k) {
-    constexpr int kPer = kNB / kThreads;  // contiguous buckets per thread
-    __shared__ uint64_t s_tmp[kWaves];
-    __shared__ float s_red[kWaves];
+    constexpr int kPer = kNW / kThreads;  // buckets per thread, taken in descending order
+    __shared__ double s_tmp[kWaves];
+    __shared__ uint64_t s_red[kWaves];
     __shared__ int s_beta;
     const int n = a.pos[k].n_fn;
-    const int nrec = a.ntiles * kWaves;
+    const int n_units = a.pos[k].n_units;
     const int32_t* list = a.flist + (int64_t)k * 2 * a.B;
     for (int li = blockIdx.x; li < n; li += gridDim.x) {
         const int u = list[li];
-        const int b = u >> 1;
-        const RecRange r = unit_records(li, n, a.ntiles, a.g_hist);
-        const int b0 = threadIdx.x * kPer;
-        uint64_t mass[kPer];
-#pragma unroll
-        for (int j = 0; j < kPer; j++) mass[j] = 0ull;
-        for (int p = 0; p < r.count; p++) {
-            const uint64_t* h = a.hist + (int64_t)(r.first + p) * kNB + b0;
-#pragma unroll
-            for (int j = 0; j < kPer; j++) mass[j] += h[j];
+        const int b = u >> 1, side = u & 1;
+        const RowInfo& ri = a.rows[b];
+        FnUnit* fu = a.fn_unit + u;
+        const RecRange rr = unit_records(side ? ri.li_d : ri.li_t, n_units, a.ntiles, a.g_row);
+        const bool re = fu->rehist != 0;
+        float la;
+        RecRange r;
+        const uint64_t* hbase;
+        if (re) {
+            la = unit_piece_max(a.parts, rr, s_red);  // barriers
+            r = unit_records(li, n, a.ntiles, a.g_hist);
+            hbase = a.hist2;
+        } else {
+            la = fu->la;
+            r = rr;
+            hbase = a.hist;
         }
-        uint64_t mine = 0ull;
+        const int j0 = kNW - kPer * ((int)threadIdx.x + 1);  // this thread's lowest bucket
+        uint64_t rel[kPer];
 #pragma unroll
-        for (int j = 0; j < kPer; j++) mine += mass[j];
-        uint64_t Z;
-        const uint64_t excl0 = block_exclusive_scan(mine, s_tmp, &Z);
-        const double target = (double)a.rows[b].top_p * (double)Z;
+        for (int q = 0; q < kPer; q++) rel[q] = 0ull;
+        for (int p = 0; p < r.count; p++) {
+            // row-pass pieces hold the buckets [lo, hi] of their slot's range
+            int lo = 0, hi = kNW - 1;
+            if (!re) {
+                const uint64_t rg = a.parts[r.first + p].keys[1];
+                lo = (int)(uint32_t)(rg >> 32);
+                hi = (int)(uint32_t)rg;
+            }
+            if (hi < j0 || lo > j0 + kPer - 1) continue;
+            const uint64_t* h = hbase + (int64_t)(r.first + p) * kNW + j0;
+#pragma unroll
+            for (int q = 0; q < kPer; q++) {
+                const int j = j0 + kPer - 1 - q;
+                rel[q] += (j >= lo && j <= hi) ? h[kPer - 1 - q] : 0ull;
+            }
+        }
+        double mass[kPer];
+        double mine = 0.0;
+#pragma unroll
+        for (int q = 0; q < kPer; q++) {
+            mass[q] = rel[q] != 0ull ? nuc_scale(j0 + kPer - 1 - q) * ((double)rel[q] * kUnfix) : 0.0;
+            mine += mass[q];
+        }
+        double Z;
+        const double excl0 = block_exclusive_scan(mine, s_tmp, &Z);
+        const double target = (double)ri.top_p * Z;
         if (threadIdx.x == 0) s_beta = -1;
         __syncthreads();
-        uint64_t run = excl0;
+        double run = excl0;
         int best = -1;
-        uint64_t best_before = 0ull;
+        double best_before = 0.0;
 #pragma unroll
-        for (int j = 0; j < kPer; j++) {
-            if (mass[j] != 0ull && (double)run < target) {
-                best = b0 + j;
+        for (int q = 0; q < kPer; q++) {
+            if (rel[q] != 0ull && run < target) {
+                best = (int)threadIdx.x * kPer + q;
                 best_before = run;
             }
-            run += mass[j];
+            run += mass[q];
         }
         if (best >= 0) atomicMax(&s_beta, best);
-        const float m = block_unit_max(a.tstat + (int64_t)u * nrec, nrec, s_red);  // barriers
-        const int beta = s_beta;
-        FnUnit* fu = a.fn_unit + u;
-        if (beta >= 0 && best == beta) {
-            fu->Zfix = Z;
-            fu->Afix = best_before;
-            fu->beta = beta;
-            fu->m = m;
+        __syncthreads();
+        const int star = s_beta;
+        if (star >= 0 && best == star) {
+            fu->Z = Z;
+            fu->A = best_before;
+            fu->beta = kNW - 1 - star;
+            fu->la = la;
             fu->ncoll = 0;
             fu->status = 0;
         }
-        if (beta < 0 && threadIdx.x == 0) {  // no finite logit: invalid row
+        if (star < 0 && threadIdx.x == 0) {  // no finite logit: invalid row
             fu->status = 2;
             fu->ncoll = 0;
         }
@@ -177,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void fn_collect_kernel(StepArgs a, int k)
         if (threadIdx.x == 0) s_n = 0;
         __syncthreads();
         const int beta = fu->beta;
-        const float m = fu->m;
+        const float la = fu->la;
         const float cb = bucket_coef(a.rows[b].T);
         const int64_t start = tu0 * TS::kTile;
         int64_t end = tu1 * TS::kTile;
@@ -185,11 +217,13 @@ __global__ __launch_bounds__(kThreads) void fn_collect_kernel(StepArgs a, int k)
         stream_range<DT, kAligned>(unit_row<DT>(a, b, side, k), start, end,
                                    [&](float (&v)[TS::kE], int64_t t0, bool)
                                        __attribute__((always_inline)) {
-            // past `end` elements read as -inf and land in the dropped bucket
+            // past `end` elements read as -inf, outside the window
             uint32_t hit = 0u;
 #pragma unroll
-            for (int i = TS::kE - 1; i >= 0; i--)
-                hit = (hit << 1) | (nuc_bucket(v[i], m, cb) == beta ? 1u : 0u);
+            for (int i = TS::kE - 1; i >= 0; i--) {
+                const float tt = nuc_t(v[i], la, cb);
+                hit = (hit << 1) | (nuc_in(tt) && nuc_bin(tt) == beta ? 1u : 0u);
+            }
             if (__ballot(hit != 0u) == 0ull) return;
             int total;
             const int excl = wave_excl_count((uint32_t)__popc(hit), &total);
@@ -218,12 +252,14 @@ __global__ __launch_bounds__(kThreads) void fn_collect_kernel(StepArgs a, int k)
 
 // One workgroup per unit: the exact cut inside the boundary bucket.
 //   1. the bucket's n tokens are split into 256 sub-buckets by the fraction
-//      of their bucket coordinate (a finer cut of the same monotone map), and
-//      the sub-bucket masses give the boundary sub-bucket the same way the
-//      buckets gave the boundary bucket;
+//      of their window coordinate (a finer cut of the same monotone map),
+//      and the sub-bucket masses give the boundary sub-bucket the same way
+//      the buckets gave the boundary bucket;
 //   2. every token of the boundary sub-bucket is ranked implicitly: its
 //      preceding mass is the bucket mass before the sub-bucket plus the
 //      masses of the sub-bucket's tokens with a larger key.
+// Inside the bucket every mass is an exact fixed-point integer scaled by the
+// bucket's one factor, so these comparisons are exact up to that one product.
 // The first token of the boundary sub-bucket is always kept (its preceding
 // mass is below top_p Z by the choice of the sub-bucket), so the cut key tau
 // lies in that sub-bucket.
@@ -234,9 +270,9 @@ static_assert(kSub == kThreads, "one sub-bucket per thread");
 // temperatures) are resolved by the unit's workgroup alone, re-reading the
 // row once per step of a radix select over the bucket's keys:
 //   range  the bucket's keys form one interval [lo, hi] of the key order
-//          (the bucket index never decreases as the logit falls, and equal
+//          (the bucket index never rises as the logit falls, and equal
 //          logits share a bucket); one pass finds it;
-//   level  the interval is cut into at most kNB bins of 2^s consecutive
+//   level  the interval is cut into at most kBins bins of 2^s consecutive
 //          keys; one pass adds every token's fixed-point weight and a count
 //          into its bin; the boundary bin is chosen as the boundary bucket
 //          was (last bin with mass whose preceding mass is below top_p Z),
@@ -246,20 +282,24 @@ static_assert(kSub == kThreads, "one sub-bucket per thread");
 //          holds one, as keys are distinct), they are ranked one per thread
 //          like the boundary sub-bucket of the narrow path.
 // The first token of every chosen bin is kept, so tau stays in the interval.
-// Returns the cut key and the kept mass through fu.  Contains barriers; every
-// thread of the block calls it.
+// `pre` counts the bucket's mass ranked ahead of the interval (exact), the
+// preceding mass of a token is A + sc * (pre + ...).  Returns the cut key and
+// the kept mass through fu.  Contains barriers; every thread of the block
+// calls it.
+constexpr int kBins = 2048;
+
 template <int DT, bool kAligned>
-__device__ void resolve_wide(const void* row, int64_t V, FnUnit* fu, float m, float c, float cb,
-                             int beta, double target, uint64_t* s_mass /* kNB */,
-                             uint32_t* s_cnt /* kNB */, uint64_t* s_key /* kThreads */,
+__device__ void resolve_wide(const void* row, int64_t V, FnUnit* fu, float la, float cb, int beta,
+                             double A, double sc, double target, uint64_t* s_mass /* kBins */,
+                             uint32_t* s_cnt /* kBins */, uint64_t* s_key /* kThreads */,
                              uint64_t* s_w /* kThreads */, uint64_t* s_tmp /* kWaves */) {
     using TS = TileShape<DT>;
-    constexpr int kPer = kNB / kThreads;  // bins per thread, in descending key order
+    constexpr int kPer = kBins / kThreads;  // bins per thread, in descending key order
     __shared__ unsigned long long s_lo, s_hi, s_tau, s_kept;
-    __shared__ uint64_t s_A;
+    __shared__ uint64_t s_pre;
     __shared__ int s_star, s_n;
     __shared__ uint32_t s_bincnt;
-    static_assert(kNB == 2048, "11-bit bins");
+    static_assert(kBins == 2048, "11-bit bins");
     if (threadIdx.x == 0) {
         s_lo = ~0ull;
         s_hi = 0ull;
@@ -271,7 +311,8 @@ __device__ void resolve_wide(const void* row, int64_t V, FnUnit* fu, float m, fl
                                                   __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < TS::kE; i++) {
-                if (nuc_bucket(v[i], m, cb) == beta) {
+                const float t = nuc_t(v[i], la, cb);
+                if (nuc_in(t) && nuc_bin(t) == beta) {
                     const uint64_t key = make_key(v[i], (uint32_t)elem_id<DT>(t0, i));
                     lo = key < lo ? key : lo;
                     hi = key > hi ? key : hi;
@@ -285,13 +326,13 @@ __device__ void resolve_wide(const void* row, int64_t V, FnUnit* fu, float m, fl
     }
     __syncthreads();
     uint64_t rlo = s_lo, rhi = s_hi;
-    uint64_t A = fu->Afix;
+    uint64_t pre = 0ull;
     for (;;) {
-        // bin width 2^s with (rhi - rlo) >> s < kNB
+        // bin width 2^s with (rhi - rlo) >> s < kBins
         const uint64_t span = rhi - rlo;
         const int bits = span == 0ull ? 0 : 64 - __clzll((long long)span);
         const int s = bits > 11 ? bits - 11 : 0;
-        for (int i = threadIdx.x; i < kNB; i += kThreads) {
+        for (int i = threadIdx.x; i < kBins; i += kThreads) {
             s_mass[i] = 0ull;
             s_cnt[i] = 0u;
         }
@@ -302,10 +343,11 @@ __device__ void resolve_wide(const void* row, int64_t V, FnUnit* fu, float m, fl
 #pragma unroll
             for (int i = 0; i < TS::kE; i++) {
                 const uint64_t key = make_key(v[i], (uint32_t)elem_id<DT>(t0, i));
-                if (key >= rlo && key <= rhi) {
+                if (key >= rlo && key <= rhi) {  // in the bucket (its keys form [lo, hi])
                     const int bin = (int)((key - rlo) >> s);
-                    const uint64_t w = nuc_wfix(v[i], m, c);
-                    if (w != 0ull) atomicAdd((unsigned long long*)&s_mass[bin], (unsigned long long)w);
+                    int bk;
+                    const uint64_t w = nuc_wfix_t(nuc_t(v[i], la, cb), &bk);
+                    atomicAdd((unsigned long long*)&s_mass[bin], (unsigned long long)w);
                     atomicAdd(&s_cnt[bin], 1u);
                 }
             }
@@ -315,16 +357,16 @@ __device__ void resolve_wide(const void* row, int64_t V, FnUnit* fu, float m, fl
         uint64_t mine = 0ull;
 #pragma unroll
         for (int q = 0; q < kPer; q++) {
-            mass[q] = s_mass[kNB - 1 - (threadIdx.x * kPer + q)];
+            mass[q] = s_mass[kBins - 1 - (threadIdx.x * kPer + q)];
             mine += mass[q];
         }
         uint64_t tot;
-        uint64_t run = A + block_exclusive_scan(mine, s_tmp, &tot);
+        uint64_t run = pre + block_exclusive_scan(mine, s_tmp, &tot);
         int cand = -1;
         uint64_t cand_before = 0ull;
 #pragma unroll
         for (int q = 0; q < kPer; q++) {
-            if (mass[q] != 0ull && (double)run < target) {
+            if (mass[q] != 0ull && A + sc * (double)run < target) {
                 cand = threadIdx.x * kPer + q;
                 cand_before = run;
             }
@@ -339,13 +381,13 @@ __device__ void resolve_wide(const void* row, int64_t V, FnUnit* fu, float m, fl
             return;
         }
         if (cand == star) {
-            s_A = cand_before;
-            s_bincnt = s_cnt[kNB - 1 - star];
+            s_pre = cand_before;
+            s_bincnt = s_cnt[kBins - 1 - star];
         }
         __syncthreads();
-        A = s_A;
+        pre = s_pre;
         const uint32_t nbin = s_bincnt;
-        const uint64_t j = (uint64_t)(kNB - 1 - star);
+        const uint64_t j = (uint64_t)(kBins - 1 - star);
         rlo = rlo + (j << s);
         const uint64_t top = rlo + ((1ull << s) - 1ull);
         rhi = top < rhi ? top : rhi;
@@ -366,8 +408,9 @@ __device__ void resolve_wide(const void* row, int64_t V, FnUnit* fu, float m, fl
             if (key >= rlo && key <= rhi) {
                 const int slot = atomicAdd(&s_n, 1);
                 if (slot < kThreads) {
+                    int bk;
                     s_key[slot] = key;
-                    s_w[slot] = nuc_wfix(v[i], m, c);
+                    s_w[slot] = nuc_wfix_t(nuc_t(v[i], la, cb), &bk);
                 }
             }
         }
@@ -376,9 +419,9 @@ __device__ void resolve_wide(const void* row, int64_t V, FnUnit* fu, float m, fl
     const int n = s_n < kThreads ? s_n : kThreads;
     if ((int)threadIdx.x < n) {
         const uint64_t key = s_key[threadIdx.x];
-        uint64_t pre = 0ull;
-        for (int j = 0; j < n; j++) pre += s_key[j] > key ? s_w[j] : 0ull;
-        if ((double)(A + pre) < target) {
+        uint64_t p = pre;
+        for (int j = 0; j < n; j++) p += s_key[j] > key ? s_w[j] : 0ull;
+        if (A + sc * (double)p < target) {
             atomicMin(&s_tau, (unsigned long long)key);
             atomicAdd(&s_kept, (unsigned long long)s_w[threadIdx.x]);
         }
@@ -386,7 +429,7 @@ __device__ void resolve_wide(const void* row, int64_t V, FnUnit* fu, float m, fl
     __syncthreads();
     if (threadIdx.x == 0) {
         fu->tau = s_tau;
-        fu->Sfix = A + s_kept;
+        fu->S = A + sc * (double)(pre + s_kept);
     }
     __syncthreads();
 }
@@ -403,6 +446,9 @@ __global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, int k)
     __shared__ unsigned long long s_tau, s_kept;
     __shared__ int s_star, s_nsel;
     __shared__ uint64_t s_before;
+    static_assert(kBins <= kCollectCap && 2 * kBins * sizeof(uint32_t) <= sizeof(s_w) &&
+                      kBins + kThreads <= kCollectCap,
+                  "the wide path reuses s_key and s_w");
     const int n_units = a.pos[k].n_fn;
     const int32_t* list = a.flist + (int64_t)k * 2 * a.B;
     for (int li = blockIdx.x; li < n_units; li += gridDim.x) {
@@ -411,23 +457,24 @@ __global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, int k)
         FnUnit* fu = a.fn_unit + u;
         const int status = fu->status;
         const int n = fu->ncoll;
+        const float la = fu->la;
+        const int beta = fu->beta;
+        const double A = fu->A;
+        const double target = (double)a.rows[b].top_p * fu->Z;
         __syncthreads();  // every thread has read fu before thread 0 may write it
         if (status != 0) continue;  // uniform over the block
         if (n < 1) {  // cannot happen: the boundary bucket has mass
             if (threadIdx.x == 0) fu->status = 1;
             continue;
         }
-        const float m = fu->m;
-        const float T = a.rows[b].T;
-        const float c = exp2_coef(T), cb = bucket_coef(T);
+        const float cb = bucket_coef(a.rows[b].T);
+        const double sc = nuc_scale(beta) * kUnfix;
         if (n > kCollectCap) {
-            resolve_wide<DT, kAligned>(unit_row<DT>(a, b, u & 1, k), a.V, fu, m, c, cb, fu->beta,
-                                       (double)a.rows[b].top_p * (double)fu->Zfix, s_key,
-                                       reinterpret_cast<uint32_t*>(s_w), s_key + kNB,
-                                       s_w + kNB, s_tmp);
+            resolve_wide<DT, kAligned>(unit_row<DT>(a, b, u & 1, k), a.V, fu, la, cb, beta, A, sc,
+                                       target, s_key, reinterpret_cast<uint32_t*>(s_w),
+                                       s_key + kBins, s_w + kBins, s_tmp);
             continue;
         }
-        const float beta = (float)fu->beta;
         const uint64_t* coll = a.coll + (int64_t)u * kCollectCap;
         s_sub[threadIdx.x] = 0ull;
         if (threadIdx.x == 0) {
@@ -439,26 +486,23 @@ __global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, int k)
         __syncthreads();
         for (int i = threadIdx.x; i < n; i += kThreads) {
             const uint64_t key = coll[i];
-            const float l = key_logit(key);
-            const uint64_t w = nuc_wfix(l, m, c);
-            // same coordinate as nuc_bucket; its fraction in the bucket, in [0, 1)
-            const float d = m - l;
-            const float f = (d > 0.f ? d * cb : 0.f) - beta;
-            int sb = (int)(f * (float)kSub);
+            const float t = nuc_t(key_logit(key), la, cb);
+            const float fr = t - floorf(t);
+            // sub-buckets in ranking order: a larger fraction is a larger logit
+            int sb = kSub - 1 - (int)(fr * (float)kSub);
             sb = sb < 0 ? 0 : (sb >= kSub ? kSub - 1 : sb);
+            const uint64_t w = nuc_wrel(fr);
             s_key[i] = key;
             s_w[i] = w;
             s_sb[i] = (uint8_t)sb;
             atomicAdd((unsigned long long*)&s_sub[sb], (unsigned long long)w);
         }
         __syncthreads();
-        const double target = (double)a.rows[b].top_p * (double)fu->Zfix;
-        const uint64_t A = fu->Afix;
         {
             const uint64_t mine = s_sub[threadIdx.x];
             uint64_t tot;
             const uint64_t before = block_exclusive_scan(mine, s_tmp, &tot);
-            const bool cand = mine != 0ull && (double)(A + before) < target;
+            const bool cand = mine != 0ull && A + sc * (double)before < target;
             if (cand) atomicMax(&s_star, (int)threadIdx.x);
             __syncthreads();
             if ((int)threadIdx.x == s_star) s_before = before;
@@ -474,14 +518,14 @@ __global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, int k)
             if (s_sb[i] == star) s_sel[atomicAdd(&s_nsel, 1)] = (uint16_t)i;
         __syncthreads();
         const int nsel = s_nsel;
-        const uint64_t A2 = A + s_before;
+        const uint64_t before = s_before;
         for (int base = 0; base < nsel; base += kThreads * kOwn) {
             uint64_t key[kOwn], pre[kOwn];
 #pragma unroll
             for (int q = 0; q < kOwn; q++) {
                 const int i = base + q * kThreads + (int)threadIdx.x;
                 key[q] = i < nsel ? s_key[s_sel[i]] : ~0ull;  // placeholder, never kept
-                pre[q] = 0ull;
+                pre[q] = before;
             }
             for (int j = 0; j < nsel; j++) {
                 const int sj = s_sel[j];
@@ -492,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, int k)
 #pragma unroll
             for (int q = 0; q < kOwn; q++) {
                 const int i = base + q * kThreads + (int)threadIdx.x;
-                if (i < nsel && (double)(A2 + pre[q]) < target) {
+                if (i < nsel && A + sc * (double)pre[q] < target) {
                     atomicMin(&s_tau, (unsigned long long)key[q]);
                     atomicAdd(&s_kept, (unsigned long long)s_w[s_sel[i]]);
                 }
@@ -501,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, int k)
         __syncthreads();
         if (threadIdx.x == 0) {
             fu->tau = s_tau;
-            fu->Sfix = A2 + s_kept;
+            fu->S = A + sc * (double)(before + s_kept);
         }
         __syncthreads();
     }

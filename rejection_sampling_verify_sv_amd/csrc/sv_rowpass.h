@@ -5,7 +5,9 @@
 // double-buffered vectors, and leaves one small record per unit it touches:
 //   * greedy rows:   the best (logit, lowest id) key of the segment;
 //   * top-k rows:    the segment's best 64 keys, descending (k <= 64);
-//   * full-vocab:    per (tile, wave): {max m, sum of exp((l - m) / T)}.
+//   * full-vocab:    per (tile, wave): {max m, sum of exp((l - m) / T)};
+//   * nucleus rows:  the segment's fixed-point mass histogram over the
+//                    unit's anchor window (see sv_device.h) and its max.
 // Selection uses raw logits (the ranking does not depend on T > 0), so the
 // candidate sets are exact; probabilities are formed later in fp64.
 //
@@ -266,6 +268,69 @@ __device__ __forceinline__ void seg_full(const void* row, int64_t start, int64_t
     });
 }
 
+// Nucleus rows: the piece's mass histogram over the unit's anchor window,
+// added in LDS one token at a time (fixed-point, so exact in any order).
+// The anchor is the largest of the row's first 64 vectors (64 kVec elements,
+// fewer when V is smaller): every wave of every piece reads the same ones and
+// gets the same value; the loads go out before the first tile's and are
+// reduced once that tile has arrived.  Written out: the buckets from the
+// piece max's bucket down to 2048 below it (lower ones weigh under e^-32 of
+// the piece max), their range in keys[1] of the slot and the piece max in
+// keys[0] (float bits).  A piece max above the window marks the unit for the
+// second histogram pass.
+template <int DT, bool kAligned>
+__device__ __forceinline__ void seg_nuc(const void* row, int64_t start, int64_t end, int64_t V,
+                                        float T, uint64_t* s_h, RowpassSmem& sm, PartSlot* out,
+                                        FnUnit* fu, uint64_t* hout) {
+    using TS = TileShape<DT>;
+    constexpr int kVec = Elt<DT>::kVec;
+    float av[kVec];
+#pragma unroll
+    for (int e = 0; e < kVec; e++) {
+        const int64_t i = (int64_t)lane_id() * kVec + e;
+        av[e] = i < V ? load_one<DT>(row, i) : -INFINITY;
+    }
+    const float cb = bucket_coef(T);
+    u32x4* h4 = reinterpret_cast<u32x4*>(s_h);
+    for (int i = threadIdx.x; i < kNW / 2; i += kThreads) h4[i] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    float lmax = -INFINITY, la = 0.f;
+    bool first = true;
+    stream_range<DT, kAligned>(row, start, end, [&](float (&v)[TS::kE], int64_t, bool)
+                                                    __attribute__((always_inline)) {
+        if (first) {
+            first = false;
+            float m = av[0];
+#pragma unroll
+            for (int e = 1; e < kVec; e++) m = fmaxf(m, av[e]);
+            la = wave_max_f32(m);
+        }
+        // elements past `end` read as -inf: t = -inf, outside the window
+#pragma unroll
+        for (int i = 0; i < TS::kE; i++) {
+            lmax = fmaxf(lmax, v[i]);
+            const float t = nuc_t(v[i], la, cb);
+            int bin;
+            const uint64_t w = nuc_wfix_t(t, &bin);
+            if (nuc_in(t)) atomicAdd((unsigned long long*)&s_h[bin], (unsigned long long)w);
+        }
+    });
+    const float pm = block_max_f32(lmax, sm.red);  // barriers
+    const float tm = nuc_t(pm, la, cb);
+    const int hi = nuc_in(tm) ? nuc_bin(tm) : (tm >= (float)kHalf ? kNW - 1 : -1);
+    const int lo = hi - 2048 > 0 ? hi - 2048 : 0;
+    u32x4* o4 = reinterpret_cast<u32x4*>(hout);
+    for (int i = (lo >> 1) + (int)threadIdx.x; i <= (hi >> 1); i += kThreads) o4[i] = h4[i];
+    if (threadIdx.x == 0) {
+        out->keys[0] = (uint64_t)__float_as_uint(pm);
+        out->keys[1] = ((uint64_t)(uint32_t)lo << 32) | (uint64_t)(uint32_t)hi;
+        fu->la = la;  // the same value from every piece
+        // t is monotone in l: the piece max is the token that would lie
+        // highest above the window
+        if (tm >= (float)kHalf) fu->rehist = 1;
+    }
+}
+
 // The workgroups split the tiles of position k's units evenly (see
 // flat_begin); each (unit, workgroup) piece leaves its record at slot
 // li + blockIdx.x.
@@ -273,6 +338,7 @@ template <int DT, bool kAligned>
 __global__ __launch_bounds__(kThreads) void rowpass_kernel(StepArgs a, int k) {
     using TS = TileShape<DT>;
     __shared__ RowpassSmem sm;
+    __shared__ uint64_t s_h[kNW];  // nucleus pieces
     const int n = a.pos[k].n_units;
     const int64_t T = (int64_t)n * a.ntiles;
     const int w = blockIdx.x;
@@ -296,6 +362,9 @@ __global__ __launch_bounds__(kThreads) void rowpass_kernel(StepArgs a, int k) {
             seg_greedy<DT, kAligned>(row, start, end, sm, out);
         else if (cls == CLS_TOPK)
             seg_topk<DT, kAligned>(row, start, end, a.rows[b].k_eff, sm, out);
+        else if (cls == CLS_NUCLEUS)
+            seg_nuc<DT, kAligned>(row, start, end, a.V, a.rows[b].T, s_h, sm, out, a.fn_unit + u,
+                                  a.hist + (int64_t)(li + w) * kNW);
         else
             seg_full<DT, kAligned>(row, start, end, a.rows[b].T,
                                    a.tstat + (int64_t)u * a.ntiles * kWaves);

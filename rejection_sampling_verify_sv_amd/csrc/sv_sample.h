@@ -14,7 +14,7 @@
 //                       masses, then a block-wide fp64 prefix scan inside the
 //                       chosen chunk to find the token.
 // Untruncated rows use the same exp2 terms as the row pass that produced
-// their normalisers; nucleus rows use the exact cut masses.
+// their normalisers; nucleus rows the anchor-relative weights of their cut.
 #pragma once
 
 #include "sv_decide.h"
@@ -23,7 +23,7 @@ namespace sv {
 
 struct DrawCtx {
     bool nucleus, resid;
-    float mt, md, c;
+    float mt, md, c, cb;
     double izt, izd;  // reciprocals of the normalisers (no division per token)
     uint64_t tau_t, tau_d;
 };
@@ -35,6 +35,7 @@ __device__ __forceinline__ DrawCtx draw_ctx(const RowInfo& ri) {
     x.mt = (float)ri.mt;
     x.md = (float)ri.md;
     x.c = exp2_coef(ri.T);
+    x.cb = bucket_coef(ri.T);
     x.izt = 1.0 / ri.zt;
     x.izd = ri.zd != 0.0 ? 1.0 / ri.zd : 0.0;
     x.tau_t = ri.tau_t;
@@ -43,8 +44,9 @@ __device__ __forceinline__ DrawCtx draw_ctx(const RowInfo& ri) {
 }
 
 // Draw weights of token `id`: the residual (p - q)+ and the target weight
-// (unnormalised exp2 terms on untruncated rows, fixed-point cut masses over
-// the kept mass on nucleus rows).
+// (unnormalised exp2 terms on untruncated rows; on nucleus rows the kept
+// token's weight exp(t / 64) over the kept mass, with mt / md holding the
+// anchors).
 __device__ __forceinline__ void draw_weights(const DrawCtx& x, float lt, float ld, uint32_t id,
                                              double* wr, double* wp) {
     if (x.nucleus) {
@@ -52,11 +54,11 @@ __device__ __forceinline__ void draw_weights(const DrawCtx& x, float lt, float l
         *wp = 0.0;
         *wr = 0.0;
         if (make_key(lt, id) >= x.tau_t) {
-            const double p = (double)nuc_wfix(lt, x.mt, x.c) * x.izt;
+            const double p = (double)fast_exp2(nuc_t(lt, x.mt, x.cb) * kLog2e64) * x.izt;
             *wp = p;
             if (x.resid) {
                 const double q = (make_key(ld, id) >= x.tau_d)
-                                     ? (double)nuc_wfix(ld, x.md, x.c) * x.izd
+                                     ? (double)fast_exp2(nuc_t(ld, x.md, x.cb) * kLog2e64) * x.izd
                                      : 0.0;
                 const double d = p - q;
                 *wr = d > 0.0 ? d : 0.0;

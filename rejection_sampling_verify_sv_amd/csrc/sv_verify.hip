@@ -9,6 +9,9 @@
 //     rowpass_kernel<k>           stream the units live at position k
 //     fn_hist / fn_select /
 //     fn_collect / fn_resolve<k>  exact top_p cut of full-vocab nucleus rows
+//                                 (their histograms come from the row pass;
+//                                 fn_hist only redoes rows whose max lies
+//                                 far above the anchor)
 //     decide_kernel<k>            accept / reject / draw; list the units of k+1
 //   sample_sums_kernel            full-vocab rows: per-chunk draw masses
 //   sample_pick_kernel            full-vocab rows: the drawn token
@@ -37,7 +40,7 @@ constexpr int kMaxDraft = 1024;
 struct Plan {
     int tile, ntiles;
     size_t off_rows, off_pos, off_ulist, off_flist, off_slist, off_parts, off_tstat, off_chunks,
-        off_fnu, off_hist, off_coll, off_status, bytes;
+        off_fnu, off_hist, off_hist2, off_coll, off_status, bytes;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -65,7 +68,8 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
     p->off_tstat = take(sizeof(FullStat) * units * p->ntiles * kWaves);
     p->off_chunks = take(sizeof(double2) * (size_t)B * p->ntiles * kWaves);
     p->off_fnu = take(sizeof(FnUnit) * units);
-    p->off_hist = take(sizeof(uint64_t) * slots * kNB);
+    p->off_hist = take(sizeof(uint64_t) * slots * kNW);
+    p->off_hist2 = take(sizeof(uint64_t) * slots * kNW);
     p->off_coll = take(sizeof(uint64_t) * units * kCollectCap);
     p->off_status = take(sizeof(int32_t) * (size_t)B);  // sv_sample without out_status
     p->bytes = off;
@@ -239,6 +243,7 @@ static int verify_impl(const void* target_logits, const void* draft_logits,
     a.fn_unit = reinterpret_cast<FnUnit*>(ws + pl.off_fnu);
     a.tstat = reinterpret_cast<FullStat*>(ws + pl.off_tstat);
     a.hist = reinterpret_cast<uint64_t*>(ws + pl.off_hist);
+    a.hist2 = reinterpret_cast<uint64_t*>(ws + pl.off_hist2);
     a.coll = reinterpret_cast<uint64_t*>(ws + pl.off_coll);
     a.g_row = a.g_hist = 0;
 
