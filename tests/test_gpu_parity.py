@@ -300,3 +300,25 @@ def test_extreme_temperature(oracle_mod, dev, label, V, dtype, T, top_k, top_p, 
     wl = _random_case(rng, 32, 2, V, dtype, T, top_k, top_p, scale=scale)
     rep, _, _ = check(oracle_mod, wl, dev, label=label)
     assert rep.unsupported == 0 and rep.error_rows == 0
+
+
+def test_nucleus_anchor_cases(oracle_mod, dev):
+    """Nucleus rows measured against the anchor window: rows whose max lies
+    far above the largest of the first 64 vectors (second histogram pass),
+    rows whose first vectors are all -inf, and ordinary rows, in one batch."""
+    rng = np.random.default_rng(zlib.crc32(b"nucleus_anchor"))
+    B, K, V = 36, 2, 30011
+    wl = _random_case(rng, B, K, V, "f32", 0.5, 0, 0.9)
+    T = 0.5
+    for b in range(0, B, 3):       # a spike 40 T above everything else, late in the row
+        for k in range(K + 1):
+            row = wl.target[b, k]
+            row[V - 7 - b] = row.max() + 40 * T
+        for k in range(K):
+            row = wl.draft[b, k]
+            row[V - 11 - b] = row.max() + 40 * T
+    for b in range(1, B, 3):       # the anchor's vectors hold no finite logit
+        wl.target[b, :, :512] = -np.inf
+        wl.draft[b, :, :512] = -np.inf
+    rep, _, g_acc = check(oracle_mod, wl, dev, label="nucleus_anchor_cases")
+    assert rep.unsupported == 0 and rep.error_rows == 0 and rep.compared == B
