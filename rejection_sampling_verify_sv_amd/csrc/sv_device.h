@@ -136,10 +136,37 @@ __device__ __forceinline__ uint64_t nuc_wfix_t(float t, int* bin) {
     *bin = (int)f + kHalf;
     return nuc_wrel(t - f);
 }
-// scale_b: the weight of bucket b's upper edge relative to the anchor.
-__device__ __forceinline__ double nuc_scale(int b) {
-    return exp((double)(b - kHalf + 1) * (1.0 / 64.0));
+// Bucket of any non-NaN logit: -1 below the window, kNW above it.  Never
+// decreases as l grows.
+__device__ __forceinline__ int nuc_gbin(float l, float la, float cb) {
+    const float t = nuc_t(l, la, cb);
+    return nuc_in(t) ? nuc_bin(t) : (t < 0.f ? -1 : kNW);
 }
+// The float with ranking image o (the inverse of ord32 on non-NaN values).
+__device__ __forceinline__ float ord_float(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+// scale_b = exp((b - kHalf + 1) / 64), the weight of bucket b's upper edge
+// relative to the anchor, as a table built at compile time: e^(1/64) from its
+// Taylor series (20 terms, far past double precision), then repeated
+// products outward from scale_{kHalf-1} = 1 (at most 2048 roundings: the
+// relative error stays below 1e-12).
+struct NucScaleTable {
+    double v[kNW];
+    constexpr NucScaleTable() : v() {
+        double e = 1.0, term = 1.0;
+        for (int i = 1; i < 20; i++) {
+            term = term / (64.0 * i);
+            e += term;
+        }
+        const double ie = 1.0 / e;
+        v[kHalf - 1] = 1.0;
+        for (int b = kHalf; b < kNW; b++) v[b] = v[b - 1] * e;
+        for (int b = kHalf - 2; b >= 0; b--) v[b] = v[b + 1] * ie;
+    }
+};
+__device__ constexpr NucScaleTable kNucScale{};
+__device__ __forceinline__ double nuc_scale(int b) { return kNucScale.v[b]; }
 
 // Per (row, side) state of the nucleus cut at the current position; masses
 // are relative to the anchor (a token weighs exp(t / 64)).
@@ -153,6 +180,7 @@ struct FnUnit {
     int32_t ncoll;    // tokens appended by the collect pass
     int32_t status;   // 0 ok, 1 no boundary found (not reached), 2 no finite logit
     int32_t rehist;   // set by the row pass: a token lies above the window
+    float l_lo, l_hi; // the boundary bucket's logits are exactly those in [l_lo, l_hi]
     int32_t pad;
 };
 

@@ -13,7 +13,8 @@
 //   hist     only units with a token above the window: the same histogram
 //            again, anchored at the row max;
 //   select   per unit: sum the pieces, Z = total mass; the boundary bucket is
-//            the last non-empty bucket whose preceding mass is below top_p Z;
+//            the last non-empty bucket whose preceding mass is below top_p Z,
+//            and its exact logit range [l_lo, l_hi];
 //   collect  the keys of the boundary bucket's tokens (a bucket too large for
 //            the workgroup's LDS is instead narrowed by a radix select
 //            over its keys that re-reads the row, see resolve_wide);
@@ -33,6 +34,26 @@
 
 namespace sv {
 
+// Smallest ranking image o in [-inf, +inf] with nuc_gbin(o) >= beta (that of
+// +inf is kNW, so one exists); the logits of bucket beta are exactly those
+// from ord_float(first(beta)) to ord_float(first(beta + 1) - 1).  Wave-wide: every lane calls it and gets the
+// result; each round probes 64 evenly spaced images and keeps the gap where
+// the predicate turns true, so six rounds cover the 32-bit range.
+__device__ inline uint32_t nuc_first_image(int beta, float la, float cb) {
+    uint32_t lo = 0x007FFFFFu, hi = 0xFF800000u;
+    const int lane = lane_id();
+    while (lo < hi) {
+        const uint64_t span = hi - lo;
+        const uint32_t p = lo + (uint32_t)((span * (uint64_t)(lane + 1)) / (kWave + 1));
+        const uint64_t m = __ballot(nuc_gbin(ord_float(p), la, cb) >= beta);
+        const int f = m ? __ffsll((unsigned long long)m) - 1 : kWave;
+        const uint32_t nlo = f == 0 ? lo : (uint32_t)__shfl((int)p, f - 1, kWave) + 1u;
+        const uint32_t nhi = f == kWave ? hi : (uint32_t)__shfl((int)p, f, kWave);
+        lo = nlo;
+        hi = nhi;
+    }
+    return lo;
+}
 // Max over the row-pass pieces of one unit (keys[0] holds each piece's max as
 // float bits); every thread of the block gets it.  Contains barriers.
 __device__ inline float unit_piece_max(const PartSlot* parts, RecRange r, uint64_t* tmp) {
@@ -92,100 +113,137 @@ __global__ __launch_bounds__(kThreads) void fn_hist_kernel(StepArgs a, int k) {
     }
 }
 
-// One workgroup per unit: total mass, boundary bucket, anchor.
-__global__ __launch_bounds__(kThreads) void fn_select_kernel(StepArgs a, int k) {
+// The cut's boundary for unit u (position k, nucleus list index li): sums
+// the unit's piece histograms, then Z and the boundary bucket (the last
+// non-empty bucket whose preceding mass is below top_p Z).  Every thread of
+// the block calls it (barriers inside); the result lands in *o, with
+// o->beta = -1 when the unit has no mass (no finite logit).
+struct SelOut {
+    double Z, A;
+    float la, l_lo, l_hi;
+    int beta;
+};
+
+__device__ inline void unit_select(const StepArgs& a, int k, int li, int u,
+                                   double* s_tmp /* kWaves */, uint64_t* s_red /* kWaves */,
+                                   int* s_star, SelOut* o) {
     constexpr int kPer = kNW / kThreads;  // buckets per thread, taken in descending order
+    const int b = u >> 1, side = u & 1;
+    const RowInfo& ri = a.rows[b];
+    const FnUnit* fu = a.fn_unit + u;
+    const RecRange rr =
+        unit_records(side ? ri.li_d : ri.li_t, a.pos[k].n_units, a.ntiles, a.g_row);
+    const bool re = fu->rehist != 0;
+    float la;
+    RecRange r;
+    const uint64_t* hbase;
+    if (re) {
+        la = unit_piece_max(a.parts, rr, s_red);  // barriers
+        r = unit_records(li, a.pos[k].n_fn, a.ntiles, a.g_hist);
+        hbase = a.hist2;
+    } else {
+        la = fu->la;
+        r = rr;
+        hbase = a.hist;
+    }
+    const int j0 = kNW - kPer * ((int)threadIdx.x + 1);  // this thread's lowest bucket
+    uint64_t rel[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; q++) rel[q] = 0ull;
+    for (int p = 0; p < r.count; p++) {
+        // row-pass pieces hold the buckets [lo, hi] of their slot's range
+        int lo = 0, hi = kNW - 1;
+        if (!re) {
+            const uint64_t rg = a.parts[r.first + p].keys[1];
+            lo = (int)(uint32_t)(rg >> 32);
+            hi = (int)(uint32_t)rg;
+        }
+        if (hi < j0 || lo > j0 + kPer - 1) continue;
+        const uint64_t* h = hbase + (int64_t)(r.first + p) * kNW + j0;
+#pragma unroll
+        for (int q = 0; q < kPer; q++) {
+            const int j = j0 + kPer - 1 - q;
+            rel[q] += (j >= lo && j <= hi) ? h[kPer - 1 - q] : 0ull;
+        }
+    }
+    double mine = 0.0;
+#pragma unroll
+    for (int q = 0; q < kPer; q++)
+        mine += nuc_scale(j0 + kPer - 1 - q) * ((double)rel[q] * kUnfix);
+    double Z;
+    const double excl0 = block_exclusive_scan(mine, s_tmp, &Z);
+    const double target = (double)ri.top_p * Z;
+    if (threadIdx.x == 0) *s_star = -1;
+    __syncthreads();
+    double run = excl0;
+    int best = -1;
+    double best_before = 0.0;
+#pragma unroll
+    for (int q = 0; q < kPer; q++) {
+        const double m = nuc_scale(j0 + kPer - 1 - q) * ((double)rel[q] * kUnfix);
+        if (rel[q] != 0ull && run < target) {
+            best = (int)threadIdx.x * kPer + q;
+            best_before = run;
+        }
+        run += m;
+    }
+    if (best >= 0) atomicMax(s_star, best);
+    __syncthreads();
+    const int star = *s_star;
+    if (star >= 0 && best == star) {
+        o->Z = Z;
+        o->A = best_before;
+        o->beta = kNW - 1 - star;
+        o->la = la;
+    }
+    if (star < 0 && threadIdx.x == 0) o->beta = -1;
+    if (star >= 0 && wave_id() < 2) {  // wave 0: the range's low end, wave 1: its high end
+        const uint32_t im = nuc_first_image(kNW - 1 - star + wave_id(), la, bucket_coef(ri.T));
+        if (lane_id() == 0) {
+            if (wave_id() == 0)
+                o->l_lo = ord_float(im);
+            else
+                o->l_hi = ord_float(im - 1u);
+        }
+    }
+    __syncthreads();
+}
+
+// One workgroup per unit: the boundary bucket and its logit range.
+__global__ __launch_bounds__(kThreads) void fn_select_kernel(StepArgs a, int k) {
     __shared__ double s_tmp[kWaves];
     __shared__ uint64_t s_red[kWaves];
-    __shared__ int s_beta;
+    __shared__ SelOut s_sel;
+    __shared__ int s_star;
     const int n = a.pos[k].n_fn;
-    const int n_units = a.pos[k].n_units;
     const int32_t* list = a.flist + (int64_t)k * 2 * a.B;
     for (int li = blockIdx.x; li < n; li += gridDim.x) {
         const int u = list[li];
-        const int b = u >> 1, side = u & 1;
-        const RowInfo& ri = a.rows[b];
-        FnUnit* fu = a.fn_unit + u;
-        const RecRange rr = unit_records(side ? ri.li_d : ri.li_t, n_units, a.ntiles, a.g_row);
-        const bool re = fu->rehist != 0;
-        float la;
-        RecRange r;
-        const uint64_t* hbase;
-        if (re) {
-            la = unit_piece_max(a.parts, rr, s_red);  // barriers
-            r = unit_records(li, n, a.ntiles, a.g_hist);
-            hbase = a.hist2;
-        } else {
-            la = fu->la;
-            r = rr;
-            hbase = a.hist;
-        }
-        const int j0 = kNW - kPer * ((int)threadIdx.x + 1);  // this thread's lowest bucket
-        uint64_t rel[kPer];
-#pragma unroll
-        for (int q = 0; q < kPer; q++) rel[q] = 0ull;
-        for (int p = 0; p < r.count; p++) {
-            // row-pass pieces hold the buckets [lo, hi] of their slot's range
-            int lo = 0, hi = kNW - 1;
-            if (!re) {
-                const uint64_t rg = a.parts[r.first + p].keys[1];
-                lo = (int)(uint32_t)(rg >> 32);
-                hi = (int)(uint32_t)rg;
-            }
-            if (hi < j0 || lo > j0 + kPer - 1) continue;
-            const uint64_t* h = hbase + (int64_t)(r.first + p) * kNW + j0;
-#pragma unroll
-            for (int q = 0; q < kPer; q++) {
-                const int j = j0 + kPer - 1 - q;
-                rel[q] += (j >= lo && j <= hi) ? h[kPer - 1 - q] : 0ull;
+        unit_select(a, k, li, u, s_tmp, s_red, &s_star, &s_sel);  // barriers
+        if (threadIdx.x == 0) {
+            FnUnit* fu = a.fn_unit + u;
+            const SelOut so = s_sel;
+            if (so.beta >= 0) {
+                fu->Z = so.Z;
+                fu->A = so.A;
+                fu->beta = so.beta;
+                fu->la = so.la;
+                fu->l_lo = so.l_lo;
+                fu->l_hi = so.l_hi;
+                fu->status = 0;
+            } else {
+                fu->status = 2;  // no finite logit: invalid row
             }
         }
-        double mass[kPer];
-        double mine = 0.0;
-#pragma unroll
-        for (int q = 0; q < kPer; q++) {
-            mass[q] = rel[q] != 0ull ? nuc_scale(j0 + kPer - 1 - q) * ((double)rel[q] * kUnfix) : 0.0;
-            mine += mass[q];
-        }
-        double Z;
-        const double excl0 = block_exclusive_scan(mine, s_tmp, &Z);
-        const double target = (double)ri.top_p * Z;
-        if (threadIdx.x == 0) s_beta = -1;
-        __syncthreads();
-        double run = excl0;
-        int best = -1;
-        double best_before = 0.0;
-#pragma unroll
-        for (int q = 0; q < kPer; q++) {
-            if (rel[q] != 0ull && run < target) {
-                best = (int)threadIdx.x * kPer + q;
-                best_before = run;
-            }
-            run += mass[q];
-        }
-        if (best >= 0) atomicMax(&s_beta, best);
-        __syncthreads();
-        const int star = s_beta;
-        if (star >= 0 && best == star) {
-            fu->Z = Z;
-            fu->A = best_before;
-            fu->beta = kNW - 1 - star;
-            fu->la = la;
-            fu->ncoll = 0;
-            fu->status = 0;
-        }
-        if (star < 0 && threadIdx.x == 0) {  // no finite logit: invalid row
-            fu->status = 2;
-            fu->ncoll = 0;
-        }
-        __syncthreads();
+        __syncthreads();  // s_sel is reused
     }
 }
 
-// Keys of the boundary bucket.  Each workgroup gathers its piece's keys in
-// LDS (one LDS counter update per wave and tile) and reserves space in the
-// unit's list with one global atomic per piece.  Keys beyond kCollectCap are
-// dropped but still counted: such a bucket is resolved from the row itself.
+// Keys of the boundary bucket: the logits in [l_lo, l_hi].  Each workgroup
+// gathers its piece's keys in LDS (one LDS counter update per wave and tile)
+// and reserves space in the unit's list with one global atomic per piece.
+// Keys beyond kCollectCap are dropped but still counted: such a bucket is
+// resolved from the row itself.
 template <int DT, bool kAligned>
 __global__ __launch_bounds__(kThreads) void fn_collect_kernel(StepArgs a, int k) {
     using TS = TileShape<DT>;
@@ -206,24 +264,20 @@ __global__ __launch_bounds__(kThreads) void fn_collect_kernel(StepArgs a, int k)
         const int b = u >> 1, side = u & 1;
         FnUnit* fu = a.fn_unit + u;
         if (fu->status != 0) continue;  // uniform over the block
+        const float l_lo = fu->l_lo, l_hi = fu->l_hi;
         if (threadIdx.x == 0) s_n = 0;
         __syncthreads();
-        const int beta = fu->beta;
-        const float la = fu->la;
-        const float cb = bucket_coef(a.rows[b].T);
         const int64_t start = tu0 * TS::kTile;
         int64_t end = tu1 * TS::kTile;
         if (end > a.V) end = a.V;
         stream_range<DT, kAligned>(unit_row<DT>(a, b, side, k), start, end,
                                    [&](float (&v)[TS::kE], int64_t t0, bool)
                                        __attribute__((always_inline)) {
-            // past `end` elements read as -inf, outside the window
+            // past `end` elements read as -inf, below every boundary bucket
             uint32_t hit = 0u;
 #pragma unroll
-            for (int i = TS::kE - 1; i >= 0; i--) {
-                const float tt = nuc_t(v[i], la, cb);
-                hit = (hit << 1) | (nuc_in(tt) && nuc_bin(tt) == beta ? 1u : 0u);
-            }
+            for (int i = TS::kE - 1; i >= 0; i--)
+                hit = (hit << 1) | (v[i] >= l_lo && v[i] <= l_hi ? 1u : 0u);
             if (__ballot(hit != 0u) == 0ull) return;
             int total;
             const int excl = wave_excl_count((uint32_t)__popc(hit), &total);
@@ -289,8 +343,9 @@ static_assert(kSub == kThreads, "one sub-bucket per thread");
 constexpr int kBins = 2048;
 
 template <int DT, bool kAligned>
-__device__ void resolve_wide(const void* row, int64_t V, FnUnit* fu, float la, float cb, int beta,
-                             double A, double sc, double target, uint64_t* s_mass /* kBins */,
+__device__ void resolve_wide(const void* row, int64_t V, FnUnit* fu, float la, float cb,
+                             float l_lo, float l_hi, double A, double sc, double target,
+                             uint64_t* s_mass /* kBins */,
                              uint32_t* s_cnt /* kBins */, uint64_t* s_key /* kThreads */,
                              uint64_t* s_w /* kThreads */, uint64_t* s_tmp /* kWaves */) {
     using TS = TileShape<DT>;
@@ -311,8 +366,7 @@ __device__ void resolve_wide(const void* row, int64_t V, FnUnit* fu, float la, f
                                                   __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < TS::kE; i++) {
-                const float t = nuc_t(v[i], la, cb);
-                if (nuc_in(t) && nuc_bin(t) == beta) {
+                if (v[i] >= l_lo && v[i] <= l_hi) {
                     const uint64_t key = make_key(v[i], (uint32_t)elem_id<DT>(t0, i));
                     lo = key < lo ? key : lo;
                     hi = key > hi ? key : hi;
@@ -470,8 +524,8 @@ __global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, int k)
         const float cb = bucket_coef(a.rows[b].T);
         const double sc = nuc_scale(beta) * kUnfix;
         if (n > kCollectCap) {
-            resolve_wide<DT, kAligned>(unit_row<DT>(a, b, u & 1, k), a.V, fu, la, cb, beta, A, sc,
-                                       target, s_key, reinterpret_cast<uint32_t*>(s_w),
+            resolve_wide<DT, kAligned>(unit_row<DT>(a, b, u & 1, k), a.V, fu, la, cb, fu->l_lo,
+                                       fu->l_hi, A, sc, target, s_key, reinterpret_cast<uint32_t*>(s_w),
                                        s_key + kBins, s_w + kBins, s_tmp);
             continue;
         }

@@ -87,5 +87,6 @@ def test_sample_and_k0_reject_bad_arguments_on_host(lib):
     assert lib.sv_sample(*s_bad, ctypes.byref(cfg)) == -2
     cfg.batch = 0
     assert lib.sv_sample(*s_args, ctypes.byref(cfg)) == -1
-    assert lib.sv_launch_count(0) == lib.sv_launch_count(1) - 6
+    per_position = lib.sv_launch_count(2) - lib.sv_launch_count(1)
+    assert per_position > 0 and lib.sv_launch_count(0) == lib.sv_launch_count(1) - per_position
     assert lib.sv_launch_count(-1) == 0 and lib.sv_launch_count(1025) == 0
