@@ -159,7 +159,9 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
     const int k_eff = ri.k_eff;
     const double T = (double)ri.T, top_p = (double)ri.top_p;
     const bool has_draft = k < ri.L;
-    const uint64_t kt = unit_top(a.parts, unit_records(ri.li_t, n, a.ntiles, a.g_row));
+    const PosDesc P = a.pos[k];
+    const uint64_t kt =
+        unit_top(a.parts, unit_records(unit_index(P, CLS_TOPK, ri.li_t), n, a.ntiles, a.g_row));
     double p;
     bool keep_p;
     if (!topk_dist_wave(kt, k_eff, T, top_p, &p, &keep_p)) {
@@ -172,7 +174,8 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
     bool keep_q = false;
     int id_q = -1;
     if (has_draft) {
-        const uint64_t kd = unit_top(a.parts, unit_records(ri.li_d, n, a.ntiles, a.g_row));
+        const uint64_t kd = unit_top(
+            a.parts, unit_records(unit_index(P, CLS_TOPK, ri.li_d), n, a.ntiles, a.g_row));
         if (!topk_dist_wave(kd, k_eff, T, top_p, &q, &keep_q)) {
             close_row_invalid(a, b, -1);
             return;
@@ -251,7 +254,8 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
 
 __device__ void decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri, int n) {
     const int lane = lane_id();
-    const RecRange r = unit_records(ri.li_t, n, a.ntiles, a.g_row);
+    const RecRange r =
+        unit_records(unit_index(a.pos[k], CLS_GREEDY, ri.li_t), n, a.ntiles, a.g_row);
     const PartSlot* s = a.parts + r.first;
     uint64_t best = 0ull;
     for (int i = lane; i < r.count; i += kWave) best = s[i].keys[0] > best ? s[i].keys[0] : best;
@@ -407,7 +411,7 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepArgs a, int 
     const int b = blockIdx.x;
     const RowInfo ri = a.rows[b];
     if (ri.status != ST_LIVE || k > ri.L) return;
-    const int n = a.pos[k].n_units;
+    const int n = pos_units(a.pos[k]);
     if (ri.cls == CLS_GREEDY)
         decide_greedy(a, b, k, ri, n);
     else if (ri.cls == CLS_TOPK)
@@ -426,14 +430,12 @@ constexpr int kPlanThreads = 1024;
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const int32_t* draft_len,
                                                             const sv_sampler_params* params) {
-    __shared__ int s_nu, s_nf;  // position-0 list lengths (LDS counters)
+    __shared__ int s_nc[kNumCls];  // position-0 region lengths (LDS counters)
     for (int i = threadIdx.x; i < a.K + 2; i += kPlanThreads) {
-        a.pos[i].n_units = 0;
-        a.pos[i].n_fn = 0;
+        for (int c = 0; c < kNumCls; c++) a.pos[i].n_cls[c] = 0;
         a.pos[i].n_sample = 0;
-        a.pos[i].pad = 0;
     }
-    if (threadIdx.x == 0) s_nu = s_nf = 0;
+    if (threadIdx.x < kNumCls) s_nc[threadIdx.x] = 0;
     __syncthreads();
     for (int b = threadIdx.x; b < a.B; b += kPlanThreads) {
         const sv_sampler_params prm = params[b];
@@ -474,21 +476,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
             // position-0 units (same layout as append_units, LDS counters)
             const bool draft = cls != CLS_GREEDY && 0 < L;
             const int nu = draft ? 2 : 1;
-            int li = atomicAdd(&s_nu, nu);
-            a.ulist[li] = b * 2;
+            const int li = atomicAdd(&s_nc[cls], nu);
+            int32_t* ul = a.ulist + (int64_t)cls * 2 * a.B;
+            ul[li] = b * 2;
             ri.li_t = li;
             if (draft) {
-                a.ulist[li + 1] = b * 2 + 1;
+                ul[li + 1] = b * 2 + 1;
                 ri.li_d = li + 1;
             }
             if (cls == CLS_NUCLEUS) {
-                const int f = atomicAdd(&s_nf, nu);
-                a.flist[f] = b * 2;
                 a.fn_unit[b * 2].rehist = 0;
-                if (draft) {
-                    a.flist[f + 1] = b * 2 + 1;
-                    a.fn_unit[b * 2 + 1].rehist = 0;
-                }
+                if (draft) a.fn_unit[b * 2 + 1].rehist = 0;
             }
         }
         a.rows[b] = ri;
@@ -502,10 +500,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
         }
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        a.pos[0].n_units = s_nu;
-        a.pos[0].n_fn = s_nf;
-    }
+    if (threadIdx.x < kNumCls) a.pos[0].n_cls[threadIdx.x] = s_nc[threadIdx.x];
 }
 
 }  // namespace sv

@@ -45,20 +45,33 @@ struct RowInfo {
     int32_t cls, L, status, acc;
     int32_t kpos, need, k_eff, flags;
     float T, top_p;
-    int32_t li_t, li_d;      // list index of the target / draft unit at the current position
+    int32_t li_t, li_d;      // index of the target / draft unit in its class region at the current position
     double mt, zt, md, zd;   // full-vocab stats (max, normaliser) at position kpos
     uint64_t tau_t, tau_d;   // nucleus rows: key of the last kept token
 };
 static_assert(sizeof(RowInfo) == 96, "RowInfo layout");
 
-// Work counters of one position (units to stream, nucleus units, rows to
-// draw from at the end).
+// Work counters of one position.  The units to stream are listed in one
+// region per row class (greedy, top-k, untruncated, nucleus), laid end to end
+// in that order, so that neighbouring workgroups of the row pass mostly run
+// the same code (mixed classes on one compute unit measurably slow it).
+constexpr int kNumCls = 4;
+static_assert(CLS_GREEDY == 0 && CLS_TOPK == 1 && CLS_FULL == 2 && CLS_NUCLEUS == 3,
+              "row classes index the unit regions");
 struct PosDesc {
-    int32_t n_units;
-    int32_t n_fn;
-    int32_t n_sample;
-    int32_t pad;
+    int32_t n_cls[kNumCls];  // units listed per class region
+    int32_t n_sample;        // rows to draw from at the end (final slot only)
+    int32_t pad[3];
 };
+__device__ __forceinline__ int pos_units(const PosDesc& p) {
+    return p.n_cls[0] + p.n_cls[1] + p.n_cls[2] + p.n_cls[3];
+}
+// Index in the concatenated list of entry j of class c's region.
+__device__ __forceinline__ int unit_index(const PosDesc& p, int c, int j) {
+    int s = 0;
+    for (int i = 0; i < c; i++) s += p.n_cls[i];
+    return s + j;
+}
 
 // One segment's result: a descending top-k key list (zero-padded), or the
 // best key of a greedy segment in keys[0].
@@ -722,8 +735,7 @@ struct StepArgs {
     int32_t* out_acc;
     double* diag;
     PosDesc* pos;          // [K+2]: positions 0..K, then the final draw
-    int32_t* ulist;        // [K+1][2B] units to stream per position
-    int32_t* flist;        // [K+1][2B] nucleus units per position
+    int32_t* ulist;        // [K+1][kNumCls][2B] units to stream per position and class
     int32_t* slist;        // [B] rows that draw over the full vocabulary at the end
     FnUnit* fn_unit;       // [2B] nucleus cut of the current position
     uint64_t* hist;        // [2B + kGrid][kNW] nucleus histograms of the row pass, slot u + w
@@ -742,25 +754,32 @@ __device__ __forceinline__ const void* unit_row(const StepArgs& a, int b, int si
 
 // A row that continues to position k lists the units it needs there.
 __device__ inline void append_units(const StepArgs& a, int b, int k, RowInfo& ri) {
-    const int64_t base = (int64_t)k * 2 * a.B;
     const bool draft = ri.cls != CLS_GREEDY && k < ri.L;
     const int nu = draft ? 2 : 1;
-    const int li = atomicAdd(&a.pos[k].n_units, nu);
-    a.ulist[base + li] = b * 2;
+    const int li = atomicAdd(&a.pos[k].n_cls[ri.cls], nu);
+    int32_t* ul = a.ulist + ((int64_t)k * kNumCls + ri.cls) * 2 * a.B;
+    ul[li] = b * 2;
     ri.li_t = li;
     if (draft) {
-        a.ulist[base + li + 1] = b * 2 + 1;
+        ul[li + 1] = b * 2 + 1;
         ri.li_d = li + 1;
     }
     if (ri.cls == CLS_NUCLEUS) {
-        const int f = atomicAdd(&a.pos[k].n_fn, nu);
-        a.flist[base + f] = b * 2;
         a.fn_unit[b * 2].rehist = 0;
-        if (draft) {
-            a.flist[base + f + 1] = b * 2 + 1;
-            a.fn_unit[b * 2 + 1].rehist = 0;
-        }
+        if (draft) a.fn_unit[b * 2 + 1].rehist = 0;
     }
+}
+
+// The nucleus units of position k (their class region) and their number.
+__device__ __forceinline__ const int32_t* nuc_list(const StepArgs& a, int k) {
+    return a.ulist + ((int64_t)k * kNumCls + CLS_NUCLEUS) * 2 * a.B;
+}
+
+// Unit at index li of position k's concatenated list.
+__device__ __forceinline__ int32_t unit_at(const StepArgs& a, int k, const PosDesc& p, int li) {
+    int c = 0;
+    while (c < kNumCls - 1 && li >= p.n_cls[c]) li -= p.n_cls[c++];
+    return a.ulist[((int64_t)k * kNumCls + c) * 2 * a.B + li];
 }
 
 }  // namespace sv

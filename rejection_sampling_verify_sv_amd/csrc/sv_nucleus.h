@@ -71,12 +71,13 @@ __global__ __launch_bounds__(kThreads) void fn_hist_kernel(StepArgs a, int k) {
     using TS = TileShape<DT>;
     __shared__ uint64_t s_h[kNW];
     __shared__ uint64_t s_red[kWaves];
-    const int n = a.pos[k].n_fn;
-    const int n_units = a.pos[k].n_units;
+    const int n = a.pos[k].n_cls[CLS_NUCLEUS];
+    const PosDesc P = a.pos[k];
+    const int n_units = pos_units(P);
     const int64_t T = (int64_t)n * a.ntiles;
     int64_t t = flat_begin(T, gridDim.x, blockIdx.x);
     const int64_t t_end = flat_begin(T, gridDim.x, blockIdx.x + 1);
-    const int32_t* list = a.flist + (int64_t)k * 2 * a.B;
+    const int32_t* list = nuc_list(a, k);
     while (t < t_end) {
         const int li = (int)(t / a.ntiles);
         const int64_t tu0 = t - (int64_t)li * a.ntiles;
@@ -88,7 +89,10 @@ __global__ __launch_bounds__(kThreads) void fn_hist_kernel(StepArgs a, int k) {
         const int b = u >> 1, side = u & 1;
         const RowInfo& ri = a.rows[b];
         const float m = unit_piece_max(
-            a.parts, unit_records(side ? ri.li_d : ri.li_t, n_units, a.ntiles, a.g_row), s_red);
+            a.parts,
+            unit_records(unit_index(P, CLS_NUCLEUS, side ? ri.li_d : ri.li_t), n_units, a.ntiles,
+                         a.g_row),
+            s_red);
         const float cb = bucket_coef(ri.T);
         for (int i = threadIdx.x; i < kNW; i += kThreads) s_h[i] = 0ull;
         __syncthreads();
@@ -131,15 +135,16 @@ __device__ inline void unit_select(const StepArgs& a, int k, int li, int u,
     const int b = u >> 1, side = u & 1;
     const RowInfo& ri = a.rows[b];
     const FnUnit* fu = a.fn_unit + u;
-    const RecRange rr =
-        unit_records(side ? ri.li_d : ri.li_t, a.pos[k].n_units, a.ntiles, a.g_row);
+    const PosDesc P = a.pos[k];
+    const RecRange rr = unit_records(unit_index(P, CLS_NUCLEUS, side ? ri.li_d : ri.li_t),
+                                     pos_units(P), a.ntiles, a.g_row);
     const bool re = fu->rehist != 0;
     float la;
     RecRange r;
     const uint64_t* hbase;
     if (re) {
         la = unit_piece_max(a.parts, rr, s_red);  // barriers
-        r = unit_records(li, a.pos[k].n_fn, a.ntiles, a.g_hist);
+        r = unit_records(li, a.pos[k].n_cls[CLS_NUCLEUS], a.ntiles, a.g_hist);
         hbase = a.hist2;
     } else {
         la = fu->la;
@@ -215,8 +220,8 @@ __global__ __launch_bounds__(kThreads) void fn_select_kernel(StepArgs a, int k) 
     __shared__ uint64_t s_red[kWaves];
     __shared__ SelOut s_sel;
     __shared__ int s_star;
-    const int n = a.pos[k].n_fn;
-    const int32_t* list = a.flist + (int64_t)k * 2 * a.B;
+    const int n = a.pos[k].n_cls[CLS_NUCLEUS];
+    const int32_t* list = nuc_list(a, k);
     for (int li = blockIdx.x; li < n; li += gridDim.x) {
         const int u = list[li];
         unit_select(a, k, li, u, s_tmp, s_red, &s_star, &s_sel);  // barriers
@@ -250,10 +255,10 @@ __global__ __launch_bounds__(kThreads) void fn_collect_kernel(StepArgs a, int k)
     static_assert(TS::kE <= 32, "hit mask is 32 bits");
     __shared__ uint64_t s_keys[kCollectCap];
     __shared__ int s_n, s_base;
-    const int64_t T = (int64_t)a.pos[k].n_fn * a.ntiles;
+    const int64_t T = (int64_t)a.pos[k].n_cls[CLS_NUCLEUS] * a.ntiles;
     int64_t t = flat_begin(T, gridDim.x, blockIdx.x);
     const int64_t t_end = flat_begin(T, gridDim.x, blockIdx.x + 1);
-    const int32_t* list = a.flist + (int64_t)k * 2 * a.B;
+    const int32_t* list = nuc_list(a, k);
     while (t < t_end) {
         const int li = (int)(t / a.ntiles);
         const int64_t tu0 = t - (int64_t)li * a.ntiles;
@@ -503,8 +508,8 @@ __global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, int k)
     static_assert(kBins <= kCollectCap && 2 * kBins * sizeof(uint32_t) <= sizeof(s_w) &&
                       kBins + kThreads <= kCollectCap,
                   "the wide path reuses s_key and s_w");
-    const int n_units = a.pos[k].n_fn;
-    const int32_t* list = a.flist + (int64_t)k * 2 * a.B;
+    const int n_units = a.pos[k].n_cls[CLS_NUCLEUS];
+    const int32_t* list = nuc_list(a, k);
     for (int li = blockIdx.x; li < n_units; li += gridDim.x) {
         const int u = list[li];
         const int b = u >> 1;

@@ -340,18 +340,18 @@ __global__ __launch_bounds__(kThreads) void rowpass_kernel(StepArgs a, int k) {
     using TS = TileShape<DT>;
     __shared__ RowpassSmem sm;
     __shared__ uint64_t s_h[kNW];  // nucleus pieces
-    const int n = a.pos[k].n_units;
+    const PosDesc P = a.pos[k];
+    const int n = pos_units(P);
     const int64_t T = (int64_t)n * a.ntiles;
     const int w = blockIdx.x;
     int64_t t = flat_begin(T, gridDim.x, w);
     const int64_t t_end = flat_begin(T, gridDim.x, w + 1);
-    const int32_t* list = a.ulist + (int64_t)k * 2 * a.B;
     while (t < t_end) {
         const int li = (int)(t / a.ntiles);
         const int64_t tu0 = t - (int64_t)li * a.ntiles;
         int64_t tu1 = tu0 + (t_end - t);
         if (tu1 > a.ntiles) tu1 = a.ntiles;
-        const int u = list[li];
+        const int u = unit_at(a, k, P, li);
         const int b = u >> 1, side = u & 1;
         const int cls = a.rows[b].cls;
         const void* row = unit_row<DT>(a, b, side, k);

@@ -39,7 +39,7 @@ constexpr int kMaxDraft = 1024;
 
 struct Plan {
     int tile, ntiles;
-    size_t off_rows, off_pos, off_ulist, off_flist, off_slist, off_parts, off_tstat, off_chunks,
+    size_t off_rows, off_pos, off_ulist, off_slist, off_parts, off_tstat, off_chunks,
         off_fnu, off_hist, off_hist2, off_coll, off_status, bytes;
 };
 
@@ -61,8 +61,7 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
     };
     p->off_rows = take(sizeof(RowInfo) * (size_t)B);
     p->off_pos = take(sizeof(PosDesc) * (size_t)(K + 2));
-    p->off_ulist = take(sizeof(int32_t) * units * (size_t)(K + 1));
-    p->off_flist = take(sizeof(int32_t) * units * (size_t)(K + 1));
+    p->off_ulist = take(sizeof(int32_t) * units * kNumCls * (size_t)(K + 1));
     p->off_slist = take(sizeof(int32_t) * (size_t)B);
     p->off_parts = take(sizeof(PartSlot) * slots);
     p->off_tstat = take(sizeof(FullStat) * units * p->ntiles * kWaves);
@@ -238,7 +237,6 @@ static int verify_impl(const void* target_logits, const void* draft_logits,
     a.diag = cfg->diag;
     a.pos = reinterpret_cast<PosDesc*>(ws + pl.off_pos);
     a.ulist = reinterpret_cast<int32_t*>(ws + pl.off_ulist);
-    a.flist = reinterpret_cast<int32_t*>(ws + pl.off_flist);
     a.slist = reinterpret_cast<int32_t*>(ws + pl.off_slist);
     a.fn_unit = reinterpret_cast<FnUnit*>(ws + pl.off_fnu);
     a.tstat = reinterpret_cast<FullStat*>(ws + pl.off_tstat);
