@@ -26,7 +26,18 @@
 
 namespace sv {
 
-constexpr int kDecideThreads = kWave;  // one wave per row
+// One wave per row, kDecideRows rows per workgroup.  A row's wave only
+// records what it adds to the next position's unit lists or to the draw list
+// (DecideIntent, in LDS); the workgroup then reserves space for all its rows
+// with one global atomic per list, instead of one per row.
+constexpr int kDecideRows = 4;
+constexpr int kDecideThreads = kDecideRows * kWave;
+
+struct DecideIntent {
+    int32_t nu;    // units to list at position k+1 (0: none)
+    int32_t cls;   // their class region
+    int32_t draw;  // 1: the row draws over the full vocabulary at the end
+};
 
 __device__ inline void diag_nan_row(double* diag, int b, int K) {
     if (!diag) return;
@@ -135,33 +146,49 @@ __device__ __forceinline__ void write_accept_diag(const StepArgs& a, int b, int 
     }
 }
 
-// Row b accepted the draft at position k: continue at k+1.
-__device__ inline void continue_row(const StepArgs& a, int b, int k) {
-    if (lane_id() == 0) {
-        RowInfo& w = a.rows[b];
-        w.acc = k + 1;
-        append_units(a, b, k + 1, w);
-    }
+// Row b accepted the draft at position k: its units go to position k+1's
+// lists (one lane calls this).
+__device__ inline void note_continue(const StepArgs& a, int b, int k, const RowInfo& ri,
+                                     DecideIntent& it) {
+    a.rows[b].acc = k + 1;
+    it.nu = (ri.cls != CLS_GREEDY && k + 1 < ri.L) ? 2 : 1;
+    it.cls = ri.cls;
+}
+__device__ inline void continue_row(const StepArgs& a, int b, int k, const RowInfo& ri,
+                                    DecideIntent& it) {
+    if (lane_id() == 0) note_continue(a, b, k, ri, it);
 }
 
-// Row b ends at position k with a draw over the full vocabulary.
-__device__ inline void queue_draw(const StepArgs& a, int b) {
-    const int i = atomicAdd(&a.pos[a.K + 1].n_sample, 1);
-    a.slist[i] = b;
-    a.rows[b].status = ST_SAMPLE;
-}
+// Row b ends at position k with a draw over the full vocabulary (one lane).
+__device__ inline void queue_draw(DecideIntent& it) { it.draw = 1; }
 
-__device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, int n) {
-    __shared__ double s_w[kWave];
-    __shared__ double s_p[kWave];
-    __shared__ int s_id[kWave];
+__device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, int n,
+                            DecideIntent& it) {
+    __shared__ double s_wr[kDecideRows][kWave];
+    __shared__ double s_pr[kDecideRows][kWave];
+    __shared__ int s_idr[kDecideRows][kWave];
+    double* s_w = s_wr[wave_id()];
+    double* s_p = s_pr[wave_id()];
+    int* s_id = s_idr[wave_id()];
     const int lane = lane_id();
     const int k_eff = ri.k_eff;
     const double T = (double)ri.T, top_p = (double)ri.top_p;
     const bool has_draft = k < ri.L;
     const PosDesc P = a.pos[k];
+    const float* u = a.uniforms + (int64_t)b * (a.K + 1);
+    // every load first, so that their latencies overlap
     const uint64_t kt =
         unit_top(a.parts, unit_records(unit_index(P, CLS_TOPK, ri.li_t), n, a.ntiles, a.g_row));
+    uint64_t kd = 0ull;
+    int x = 0;
+    double uk = 0.0;
+    if (has_draft) {
+        kd = unit_top(a.parts,
+                      unit_records(unit_index(P, CLS_TOPK, ri.li_d), n, a.ntiles, a.g_row));
+        x = a.tokens[(int64_t)b * a.K + k];
+        uk = (double)u[k];
+    }
+    const double uf = (double)u[a.K];
     double p;
     bool keep_p;
     if (!topk_dist_wave(kt, k_eff, T, top_p, &p, &keep_p)) {
@@ -169,26 +196,21 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
         return;
     }
     const int id_p = (int)key_id(kt);
-    const float* u = a.uniforms + (int64_t)b * (a.K + 1);
     double q = 0.0;
     bool keep_q = false;
     int id_q = -1;
     if (has_draft) {
-        const uint64_t kd = unit_top(
-            a.parts, unit_records(unit_index(P, CLS_TOPK, ri.li_d), n, a.ntiles, a.g_row));
         if (!topk_dist_wave(kd, k_eff, T, top_p, &q, &keep_q)) {
             close_row_invalid(a, b, -1);
             return;
         }
         id_q = (int)key_id(kd);
-        const int x = a.tokens[(int64_t)b * a.K + k];
         const double px = lookup_lane(keep_p, id_p, p, x);
         const double qx = lookup_lane(keep_q, id_q, q, x);
         const double acc = accept_prob(px, qx);
-        const double uk = (double)u[k];
         write_accept_diag(a, b, k, px, qx, acc, uk);
         if (uk < acc) {
-            continue_row(a, b, k);
+            continue_row(a, b, k, ri, it);
             return;
         }
     }
@@ -222,7 +244,6 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
         wr = pr;
         W = wave_sum(wr);
     }
-    const double uf = (double)u[a.K];
     const double target = uf * W;
     const double incl = wave_incl_scan(wr);
     const double excl_raw = __shfl_up(incl, 1, kWave);
@@ -252,7 +273,8 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
     }
 }
 
-__device__ void decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri, int n) {
+__device__ void decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri, int n,
+                              DecideIntent& it) {
     const int lane = lane_id();
     const RecRange r =
         unit_records(unit_index(a.pos[k], CLS_GREEDY, ri.li_t), n, a.ntiles, a.g_row);
@@ -262,49 +284,48 @@ __device__ void decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri
     best = wave_max_u64(best);
     const int g = (int)key_id(best);
     if (k < ri.L && a.tokens[(int64_t)b * a.K + k] == g) {
-        continue_row(a, b, k);
+        continue_row(a, b, k, ri, it);
         return;
     }
     if (lane == 0) emit_row(a, b, k, g);
 }
 
-// (m, s) pairs: s = sum of exp((l - m) / T).  Combining is exact up to one
-// fp64 rounding per term.
-__device__ __forceinline__ void ms_combine(float& m, double& s, float m2, double s2, double invT) {
-    const float mm = fmaxf(m, m2);
-    if (mm == -INFINITY) {
-        m = mm;
-        s = 0.0;
-        return;
-    }
-    const double a = (m == mm) ? s : s * exp(((double)m - (double)mm) * invT);
-    const double b = (m2 == mm) ? s2 : s2 * exp(((double)m2 - (double)mm) * invT);
-    m = mm;
-    s = a + b;
-}
-
-// {max, sum-exp} of one full-vocab unit from its n per-(tile, wave) records;
-// lanes combine in a fixed tree and lane 0's result is broadcast.
+// {max, sum-exp} of one full-vocab unit from its n per-(tile, wave) records
+// {m_i, s_i}: M = max m_i, Z = sum s_i exp((m_i - M) / T), each lane summing
+// its records in index order and the lanes in the fixed DPP tree, so every
+// lane gets the same bits.  One exp per record, none along the tree.
 __device__ inline void full_stats(const FullStat* rec, int n, double invT, double* m, double* z) {
     const int lane = lane_id();
     float mm = -INFINITY;
+    for (int i = lane; i < n; i += kWave) mm = fmaxf(mm, rec[i].m);
+    const float M = wave_max_f32(mm);
     double ss = 0.0;
-    for (int i = lane; i < n; i += kWave) ms_combine(mm, ss, rec[i].m, rec[i].s, invT);
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-        const float m2 = __shfl_down(mm, o, kWave);
-        const double s2 = __shfl_down(ss, o, kWave);
-        if (lane + o < kWave) ms_combine(mm, ss, m2, s2, invT);
+    if (M > -INFINITY) {
+        for (int i = lane; i < n; i += kWave) {
+            const FullStat r = rec[i];
+            if (r.m > -INFINITY) ss += r.s * exp(((double)r.m - (double)M) * invT);
+        }
     }
-    *m = (double)__shfl(mm, 0, kWave);
-    *z = __shfl(ss, 0, kWave);
+    *m = (double)M;
+    *z = wave_sum(ss);
 }
 
 template <int DT>
-__device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri) {
+__device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri, DecideIntent& it) {
     const double T = (double)ri.T, invT = 1.0 / T;
     double mt, zt, md = 0.0, zd = 0.0;
     const int nrec = a.ntiles * kWaves;
+    // the drafted token's logits and the uniform, loaded while the records are
+    float lx = 0.f, ld = 0.f, ukf = 0.f;
+    int x = 0;
+    if (k < ri.L) {
+        x = a.tokens[(int64_t)b * a.K + k];
+        if (x >= 0 && x < a.V) {  // validated by the plan; kept in range here regardless
+            lx = load_one<DT>(unit_row<DT>(a, b, 0, k), x);
+            ld = load_one<DT>(unit_row<DT>(a, b, 1, k), x);
+        }
+        ukf = a.uniforms[(int64_t)b * (a.K + 1) + k];
+    }
     full_stats(a.tstat + (int64_t)(2 * b) * nrec, nrec, invT, &mt, &zt);
     if (!(mt > -INFINITY)) {
         close_row_invalid(a, b, -1);
@@ -317,7 +338,7 @@ __device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri) 
             w.kpos = k;
             w.mt = mt;
             w.zt = zt;
-            queue_draw(a, b);
+            queue_draw(it);
         }
         return;
     }
@@ -327,18 +348,14 @@ __device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri) 
         return;
     }
     if (lane_id() != 0) return;
-    const int x = a.tokens[(int64_t)b * a.K + k];
-    const double lx = (double)load_one<DT>(unit_row<DT>(a, b, 0, k), x);
-    const double ld = (double)load_one<DT>(unit_row<DT>(a, b, 1, k), x);
-    const double px = exp((lx - mt) / T) / zt;
-    const double qx = exp((ld - md) / T) / zd;
+    const double px = exp(((double)lx - mt) / T) / zt;
+    const double qx = exp(((double)ld - md) / T) / zd;
     const double acc = accept_prob(px, qx);
-    const double uk = (double)a.uniforms[(int64_t)b * (a.K + 1) + k];
+    const double uk = (double)ukf;
     write_accept_diag(a, b, k, px, qx, acc, uk);
     RowInfo& w = a.rows[b];
     if (uk < acc) {
-        w.acc = k + 1;
-        append_units(a, b, k + 1, w);
+        note_continue(a, b, k, ri, it);
     } else {
         w.need = NEED_RESID;
         w.kpos = k;
@@ -346,7 +363,7 @@ __device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri) 
         w.zt = zt;
         w.md = md;
         w.zd = zd;
-        queue_draw(a, b);
+        queue_draw(it);
     }
 }
 
@@ -354,12 +371,23 @@ __device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri) 
 // coordinate t and the kept mass S of the cut computed by the nucleus kernels
 // for this position.
 template <int DT>
-__device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& ri) {
+__device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& ri,
+                               DecideIntent& it) {
     const FnUnit ut = a.fn_unit[b * 2];
     const bool has_draft = k < ri.L;
     FnUnit ud;
     ud.status = 0;
-    if (has_draft) ud = a.fn_unit[b * 2 + 1];
+    float lx = 0.f, ld = 0.f, ukf = 0.f;
+    int x = 0;
+    if (has_draft) {  // loaded together with the cut states
+        ud = a.fn_unit[b * 2 + 1];
+        x = a.tokens[(int64_t)b * a.K + k];
+        if (x >= 0 && x < a.V) {  // validated by the plan; kept in range here regardless
+            lx = load_one<DT>(unit_row<DT>(a, b, 0, k), x);
+            ld = load_one<DT>(unit_row<DT>(a, b, 1, k), x);
+        }
+        ukf = a.uniforms[(int64_t)b * (a.K + 1) + k];
+    }
     const int st = ut.status != 0 ? ut.status : (has_draft ? ud.status : 0);
     if (st != 0) {
         close_row_invalid(a, b, st == 1 ? -2 : -1);
@@ -373,13 +401,10 @@ __device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& r
         w.mt = (double)ut.la;
         w.zt = ut.S;
         w.tau_t = ut.tau;
-        queue_draw(a, b);
+        queue_draw(it);
         return;
     }
     const float cb = bucket_coef(ri.T);
-    const int x = a.tokens[(int64_t)b * a.K + k];
-    const float lx = load_one<DT>(unit_row<DT>(a, b, 0, k), x);
-    const float ld = load_one<DT>(unit_row<DT>(a, b, 1, k), x);
     const double px = (make_key(lx, (uint32_t)x) >= ut.tau)
                           ? exp((double)nuc_t(lx, ut.la, cb) * (1.0 / 64.0)) / ut.S
                           : 0.0;
@@ -387,11 +412,10 @@ __device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& r
                           ? exp((double)nuc_t(ld, ud.la, cb) * (1.0 / 64.0)) / ud.S
                           : 0.0;
     const double acc = accept_prob(px, qx);
-    const double uk = (double)a.uniforms[(int64_t)b * (a.K + 1) + k];
+    const double uk = (double)ukf;
     write_accept_diag(a, b, k, px, qx, acc, uk);
     if (uk < acc) {
-        w.acc = k + 1;
-        append_units(a, b, k + 1, w);
+        note_continue(a, b, k, ri, it);
     } else {
         w.need = NEED_RESID;
         w.kpos = k;
@@ -401,25 +425,74 @@ __device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& r
         w.md = (double)ud.la;
         w.zd = ud.S;
         w.tau_d = ud.tau;
-        queue_draw(a, b);
+        queue_draw(it);
     }
 }
 
-// One wave per row; rows not live at position k return at once.
+// One wave per row (rows not live at position k do nothing), then the
+// workgroup's list updates: per class region and for the draw list, one
+// global atomic reserves the space of all its rows, and each row writes its
+// entries in wave order.
 template <int DT>
 __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepArgs a, int k) {
-    const int b = blockIdx.x;
-    const RowInfo ri = a.rows[b];
-    if (ri.status != ST_LIVE || k > ri.L) return;
-    const int n = pos_units(a.pos[k]);
-    if (ri.cls == CLS_GREEDY)
-        decide_greedy(a, b, k, ri, n);
-    else if (ri.cls == CLS_TOPK)
-        decide_topk(a, b, k, ri, n);
-    else if (ri.cls == CLS_NUCLEUS)
-        decide_nucleus<DT>(a, b, k, ri);
-    else
-        decide_full<DT>(a, b, k, ri);
+    __shared__ DecideIntent s_it[kDecideRows];
+    __shared__ int s_base[kNumCls + 1];
+    const int w = wave_id(), lane = lane_id();
+    const int b = blockIdx.x * kDecideRows + w;
+    if (lane == 0) {
+        s_it[w].nu = 0;
+        s_it[w].cls = 0;
+        s_it[w].draw = 0;
+    }
+    RowInfo ri;
+    if (b < a.B) ri = a.rows[b];
+    if (b < a.B && ri.status == ST_LIVE && k <= ri.L) {
+        const int n = pos_units(a.pos[k]);
+        DecideIntent& it = s_it[w];
+        if (ri.cls == CLS_GREEDY)
+            decide_greedy(a, b, k, ri, n, it);
+        else if (ri.cls == CLS_TOPK)
+            decide_topk(a, b, k, ri, n, it);
+        else if (ri.cls == CLS_NUCLEUS)
+            decide_nucleus<DT>(a, b, k, ri, it);
+        else
+            decide_full<DT>(a, b, k, ri, it);
+    }
+    __syncthreads();
+    if (threadIdx.x <= kNumCls) {  // thread c < kNumCls: class region c; kNumCls: draws
+        const int c = threadIdx.x;
+        int cnt = 0;
+        for (int j = 0; j < kDecideRows; j++)
+            cnt += (c < kNumCls) ? (s_it[j].cls == c ? s_it[j].nu : 0) : s_it[j].draw;
+        int base = 0;
+        if (cnt > 0)
+            base = atomicAdd(c < kNumCls ? &a.pos[k + 1].n_cls[c] : &a.pos[a.K + 1].n_sample, cnt);
+        s_base[c] = base;
+    }
+    __syncthreads();
+    const DecideIntent it = s_it[w];
+    if (lane == 0 && it.nu > 0) {
+        int li = s_base[it.cls];
+        for (int j = 0; j < w; j++) li += s_it[j].cls == it.cls ? s_it[j].nu : 0;
+        int32_t* ul = a.ulist + ((int64_t)(k + 1) * kNumCls + it.cls) * 2 * a.B;
+        ul[li] = b * 2;
+        RowInfo& r = a.rows[b];
+        r.li_t = li;
+        if (it.nu == 2) {
+            ul[li + 1] = b * 2 + 1;
+            r.li_d = li + 1;
+        }
+        if (it.cls == CLS_NUCLEUS) {
+            a.fn_unit[b * 2].rehist = 0;
+            if (it.nu == 2) a.fn_unit[b * 2 + 1].rehist = 0;
+        }
+    }
+    if (lane == 0 && it.draw) {
+        int i = s_base[kNumCls];
+        for (int j = 0; j < w; j++) i += s_it[j].draw;
+        a.slist[i] = b;
+        a.rows[b].status = ST_SAMPLE;
+    }
 }
 
 // One workgroup: zero the work counters, then classify every row, initialise
@@ -473,7 +546,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
         ri.mt = ri.zt = ri.md = ri.zd = 0.0;
         ri.tau_t = ri.tau_d = 0ull;
         if (cls >= 0) {
-            // position-0 units (same layout as append_units, LDS counters)
+            // position-0 units (the layout decide_kernel uses, LDS counters)
             const bool draft = cls != CLS_GREEDY && 0 < L;
             const int nu = draft ? 2 : 1;
             const int li = atomicAdd(&s_nc[cls], nu);

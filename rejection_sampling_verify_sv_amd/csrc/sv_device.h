@@ -752,24 +752,6 @@ __device__ __forceinline__ const void* unit_row(const StepArgs& a, int b, int si
     return static_cast<const char*>(a.draft) + ((int64_t)b * a.K + k) * a.d_stride * Elt<DT>::kSize;
 }
 
-// A row that continues to position k lists the units it needs there.
-__device__ inline void append_units(const StepArgs& a, int b, int k, RowInfo& ri) {
-    const bool draft = ri.cls != CLS_GREEDY && k < ri.L;
-    const int nu = draft ? 2 : 1;
-    const int li = atomicAdd(&a.pos[k].n_cls[ri.cls], nu);
-    int32_t* ul = a.ulist + ((int64_t)k * kNumCls + ri.cls) * 2 * a.B;
-    ul[li] = b * 2;
-    ri.li_t = li;
-    if (draft) {
-        ul[li + 1] = b * 2 + 1;
-        ri.li_d = li + 1;
-    }
-    if (ri.cls == CLS_NUCLEUS) {
-        a.fn_unit[b * 2].rehist = 0;
-        if (draft) a.fn_unit[b * 2 + 1].rehist = 0;
-    }
-}
-
 // The nucleus units of position k (their class region) and their number.
 __device__ __forceinline__ const int32_t* nuc_list(const StepArgs& a, int k) {
     return a.ulist + ((int64_t)k * kNumCls + CLS_NUCLEUS) * 2 * a.B;

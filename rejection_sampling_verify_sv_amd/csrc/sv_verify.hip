@@ -181,7 +181,8 @@ int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepAr
         mark();
         fn_resolve_kernel<DT, kAligned><<<unit_grid, kThreads, 0, st>>>(a, k);
         mark();
-        decide_kernel<DT><<<(unsigned)B, kDecideThreads, 0, st>>>(a, k);
+        decide_kernel<DT><<<(unsigned)((B + kDecideRows - 1) / kDecideRows), kDecideThreads, 0, st>>>(a,
+                                                                                           k);
     }
     mark();
     sample_sums_kernel<DT, kAligned><<<g.sums, kThreads, 0, st>>>(a);
