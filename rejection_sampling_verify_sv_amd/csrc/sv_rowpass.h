@@ -66,6 +66,21 @@ __device__ __forceinline__ uint64_t shared_thr(const RowpassSmem& sm) {
     return (q > 0ull && q - 1ull > t) ? q - 1ull : t;
 }
 
+// v[i] for a per-lane index i: a tree of selects on the bits of i.
+template <int N>
+__device__ __forceinline__ float pick_elem(const float (&v)[N], int i) {
+    static_assert((N & (N - 1)) == 0, "power of two");
+    float t[N];
+#pragma unroll
+    for (int j = 0; j < N; j++) t[j] = v[j];
+#pragma unroll
+    for (int w = N / 2, b = 0; w >= 1; w /= 2, b++) {
+#pragma unroll
+        for (int j = 0; j < w; j++) t[j] = ((i >> b) & 1) ? t[2 * j + 1] : t[2 * j];
+    }
+    return t[0];
+}
+
 // Buffered candidates hold the raw float bits and the id; the ranking key is
 // formed when they are merged, so nothing per element has to stay in
 // registers while candidates are appended.
@@ -167,21 +182,15 @@ __device__ __forceinline__ void seg_topk(const void* row, int64_t start, int64_t
             // it would cost registers for the whole streaming loop
             uint32_t id0 = (uint32_t)elem_id<DT>(t0, 0);
             asm volatile("" : "+v"(id0));
-            int pos = st.cnt + excl, k = 0;
-#pragma unroll
-            for (int i = 0; i < TS::kE; i++) {
+            const int pos = st.cnt + excl;
+            // one iteration per candidate this lane writes (lanes hold few of
+            // them once the threshold has risen), element picked by its index
+            for (int j = 0; j < nw; j++) {
                 constexpr int kVec = Elt<DT>::kVec;
-                const bool bit = (bits >> i) & 1u;
-                if (bit && k < nw) {
-                    const uint32_t id = id0 + (uint32_t)((i / kVec) * kThreads * kVec + i % kVec);
-                    cbuf[pos + k] = make_raw(v[i], id);
-                }
-                k += bit ? 1 : 0;
-            }
-            if (nw == (int)c) {
-                bits = 0u;
-            } else {
-                for (int j = 0; j < nw; j++) bits &= bits - 1u;  // drop the written ones
+                const int i = __builtin_ctz(bits);
+                bits &= bits - 1u;
+                const uint32_t id = id0 + (uint32_t)((i / kVec) * kThreads * kVec + i % kVec);
+                cbuf[pos + j] = make_raw(pick_elem(v, i), id);
             }
             st.cnt = st.cnt + total < kCandBuf ? st.cnt + total : kCandBuf;
             if (st.cnt >= kWave) {
