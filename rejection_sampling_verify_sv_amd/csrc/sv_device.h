@@ -184,17 +184,11 @@ __device__ __forceinline__ double nuc_scale(int b) { return kNucScale.v[b]; }
 // Per (row, side) state of the nucleus cut at the current position; masses
 // are relative to the anchor (a token weighs exp(t / 64)).
 struct FnUnit {
-    double Z;         // total mass
-    double A;         // mass of the buckets above the boundary bucket
     double S;         // kept mass
     uint64_t tau;     // key of the last kept token
     float la;         // anchor logit
-    int32_t beta;     // boundary bucket
-    int32_t ncoll;    // tokens appended by the collect pass
     int32_t status;   // 0 ok, 1 no boundary found (not reached), 2 no finite logit
     int32_t rehist;   // set by the row pass: a token lies above the window
-    float l_lo, l_hi; // the boundary bucket's logits are exactly those in [l_lo, l_hi]
-    int32_t pad;
 };
 
 // ---- element types and tiles ----------------------------------------------
@@ -739,9 +733,6 @@ struct StepArgs {
     int32_t* slist;        // [B] rows that draw over the full vocabulary at the end
     FnUnit* fn_unit;       // [2B] nucleus cut of the current position
     uint64_t* hist;        // [2B + kGrid][kNW] nucleus histograms of the row pass, slot u + w
-    uint64_t* hist2;       // [2B + kGrid][kNW] nucleus histograms anchored at the row max
-    uint64_t* coll;        // [2B][kCollectCap] boundary-bucket keys
-    int g_hist;            // grid of the histogram pass
 };
 
 template <int DT>

@@ -5,29 +5,29 @@
 // smallest head of the ranking whose preceding mass stays below top_p.  With
 // top_k disabled that head can hold tens of thousands of tokens, so the cut is
 // located by mass instead of by sorting the row.  Weights and buckets are
-// those of the anchor window (sv_device.h):
+// those of the anchor window (sv_device.h).
 //
-//   row pass every piece of a nucleus unit adds its tokens' fixed-point
-//            weights into its own LDS histogram over the window, written out
-//            whole (no atomics between workgroups);
-//   hist     only units with a token above the window: the same histogram
-//            again, anchored at the row max;
-//   select   per unit: sum the pieces, Z = total mass; the boundary bucket is
-//            the last non-empty bucket whose preceding mass is below top_p Z,
-//            and its exact logit range [l_lo, l_hi];
-//   collect  the keys of the boundary bucket's tokens (a bucket too large for
-//            the workgroup's LDS is instead narrowed by a radix select
-//            over its keys that re-reads the row, see resolve_wide);
-//   resolve  per unit: a token of the boundary bucket is kept when the mass
-//            before the bucket plus the mass of the bucket's tokens ranked
-//            ahead of it (logit desc, id asc) is below top_p Z.  The cut key
-//            tau (last kept token) and the kept mass S define the
-//            distribution p(i) = [key_i >= tau] exp(t_i / 64) / S.
+// The row pass leaves each nucleus unit's mass histogram, one per piece.
+// Then one workgroup per unit (fn_cut) finishes the cut:
+//   hist     the unit's histogram in LDS: the sum of its pieces, or, when a
+//            piece saw a token above the window, the row again, anchored at
+//            the row max;
+//   select   Z = total mass; the boundary bucket is the last non-empty bucket
+//            whose preceding mass is below top_p Z, with its exact logit
+//            range [l_lo, l_hi];
+//   collect  the row once more, keeping the keys of the boundary bucket's
+//            tokens in LDS (a bucket too large for LDS is instead narrowed by
+//            a radix select over its keys, see resolve_wide);
+//   resolve  a token of the boundary bucket is kept when the mass before the
+//            bucket plus the mass of the bucket's tokens ranked ahead of it
+//            (logit desc, id asc) is below top_p Z.  The cut key tau (last
+//            kept token) and the kept mass S define the distribution
+//            p(i) = [key_i >= tau] exp(t_i / 64) / S.
 // Within a bucket the masses are exact fixed-point integers; across buckets
 // they are combined in fp64 in one fixed order, so the cut is deterministic.
-// The streaming passes split the tiles of position k's nucleus units evenly
-// over the workgroups, like the row pass; the per-unit steps run one
-// workgroup per unit.
+// A workgroup streams its row at about 100 GB/s alone, and a few hundred of
+// them together saturate HBM, so one launch per position replaces the
+// grid-wide passes and the launches between them.
 #pragma once
 
 #include "sv_decide.h"
@@ -63,265 +63,6 @@ __device__ inline float unit_piece_max(const PartSlot* parts, RecRange r, uint64
     return block_max_f32(m, tmp);
 }
 
-// Units marked by the row pass (a token above the anchor window): the
-// histogram again, anchored at the row max, so every token has t <= 0.
-// Pieces of other units are skipped without reading the row.
-template <int DT, bool kAligned>
-__global__ __launch_bounds__(kThreads) void fn_hist_kernel(StepArgs a, int k) {
-    using TS = TileShape<DT>;
-    __shared__ uint64_t s_h[kNW];
-    __shared__ uint64_t s_red[kWaves];
-    const int n = a.pos[k].n_cls[CLS_NUCLEUS];
-    const PosDesc P = a.pos[k];
-    const int n_units = pos_units(P);
-    const int64_t T = (int64_t)n * a.ntiles;
-    int64_t t = flat_begin(T, gridDim.x, blockIdx.x);
-    const int64_t t_end = flat_begin(T, gridDim.x, blockIdx.x + 1);
-    const int32_t* list = nuc_list(a, k);
-    while (t < t_end) {
-        const int li = (int)(t / a.ntiles);
-        const int64_t tu0 = t - (int64_t)li * a.ntiles;
-        int64_t tu1 = tu0 + (t_end - t);
-        if (tu1 > a.ntiles) tu1 = a.ntiles;
-        t += tu1 - tu0;
-        const int u = list[li];
-        if (a.fn_unit[u].rehist == 0) continue;  // uniform over the block
-        const int b = u >> 1, side = u & 1;
-        const RowInfo& ri = a.rows[b];
-        const float m = unit_piece_max(
-            a.parts,
-            unit_records(unit_index(P, CLS_NUCLEUS, side ? ri.li_d : ri.li_t), n_units, a.ntiles,
-                         a.g_row),
-            s_red);
-        const float cb = bucket_coef(ri.T);
-        for (int i = threadIdx.x; i < kNW; i += kThreads) s_h[i] = 0ull;
-        __syncthreads();
-        const int64_t start = tu0 * TS::kTile;
-        int64_t end = tu1 * TS::kTile;
-        if (end > a.V) end = a.V;
-        stream_range<DT, kAligned>(unit_row<DT>(a, b, side, k), start, end,
-                                   [&](float (&v)[TS::kE], int64_t, bool)
-                                       __attribute__((always_inline)) {
-#pragma unroll
-            for (int i = 0; i < TS::kE; i++) {
-                const float tt = nuc_t(v[i], m, cb);
-                int bin;
-                const uint64_t w = nuc_wfix_t(tt, &bin);
-                if (nuc_in(tt)) atomicAdd((unsigned long long*)&s_h[bin], (unsigned long long)w);
-            }
-        });
-        __syncthreads();
-        uint64_t* out = a.hist2 + (int64_t)(li + blockIdx.x) * kNW;
-        for (int i = threadIdx.x; i < kNW; i += kThreads) out[i] = s_h[i];
-        __syncthreads();  // s_h is cleared for the next piece
-    }
-}
-
-// The cut's boundary for unit u (position k, nucleus list index li): sums
-// the unit's piece histograms, then Z and the boundary bucket (the last
-// non-empty bucket whose preceding mass is below top_p Z).  Every thread of
-// the block calls it (barriers inside); the result lands in *o, with
-// o->beta = -1 when the unit has no mass (no finite logit).
-struct SelOut {
-    double Z, A;
-    float la, l_lo, l_hi;
-    int beta;
-};
-
-__device__ inline void unit_select(const StepArgs& a, int k, int li, int u,
-                                   double* s_tmp /* kWaves */, uint64_t* s_red /* kWaves */,
-                                   int* s_star, SelOut* o) {
-    constexpr int kPer = kNW / kThreads;  // buckets per thread, taken in descending order
-    const int b = u >> 1, side = u & 1;
-    const RowInfo& ri = a.rows[b];
-    const FnUnit* fu = a.fn_unit + u;
-    const PosDesc P = a.pos[k];
-    const RecRange rr = unit_records(unit_index(P, CLS_NUCLEUS, side ? ri.li_d : ri.li_t),
-                                     pos_units(P), a.ntiles, a.g_row);
-    const bool re = fu->rehist != 0;
-    float la;
-    RecRange r;
-    const uint64_t* hbase;
-    if (re) {
-        la = unit_piece_max(a.parts, rr, s_red);  // barriers
-        r = unit_records(li, a.pos[k].n_cls[CLS_NUCLEUS], a.ntiles, a.g_hist);
-        hbase = a.hist2;
-    } else {
-        la = fu->la;
-        r = rr;
-        hbase = a.hist;
-    }
-    const int j0 = kNW - kPer * ((int)threadIdx.x + 1);  // this thread's lowest bucket
-    uint64_t rel[kPer];
-#pragma unroll
-    for (int q = 0; q < kPer; q++) rel[q] = 0ull;
-    for (int p = 0; p < r.count; p++) {
-        // row-pass pieces hold the buckets [lo, hi] of their slot's range
-        int lo = 0, hi = kNW - 1;
-        if (!re) {
-            const uint64_t rg = a.parts[r.first + p].keys[1];
-            lo = (int)(uint32_t)(rg >> 32);
-            hi = (int)(uint32_t)rg;
-        }
-        if (hi < j0 || lo > j0 + kPer - 1) continue;
-        const uint64_t* h = hbase + (int64_t)(r.first + p) * kNW + j0;
-#pragma unroll
-        for (int q = 0; q < kPer; q++) {
-            const int j = j0 + kPer - 1 - q;
-            rel[q] += (j >= lo && j <= hi) ? h[kPer - 1 - q] : 0ull;
-        }
-    }
-    double mine = 0.0;
-#pragma unroll
-    for (int q = 0; q < kPer; q++)
-        mine += nuc_scale(j0 + kPer - 1 - q) * ((double)rel[q] * kUnfix);
-    double Z;
-    const double excl0 = block_exclusive_scan(mine, s_tmp, &Z);
-    const double target = (double)ri.top_p * Z;
-    if (threadIdx.x == 0) *s_star = -1;
-    __syncthreads();
-    double run = excl0;
-    int best = -1;
-    double best_before = 0.0;
-#pragma unroll
-    for (int q = 0; q < kPer; q++) {
-        const double m = nuc_scale(j0 + kPer - 1 - q) * ((double)rel[q] * kUnfix);
-        if (rel[q] != 0ull && run < target) {
-            best = (int)threadIdx.x * kPer + q;
-            best_before = run;
-        }
-        run += m;
-    }
-    if (best >= 0) atomicMax(s_star, best);
-    __syncthreads();
-    const int star = *s_star;
-    if (star >= 0 && best == star) {
-        o->Z = Z;
-        o->A = best_before;
-        o->beta = kNW - 1 - star;
-        o->la = la;
-    }
-    if (star < 0 && threadIdx.x == 0) o->beta = -1;
-    if (star >= 0 && wave_id() < 2) {  // wave 0: the range's low end, wave 1: its high end
-        const uint32_t im = nuc_first_image(kNW - 1 - star + wave_id(), la, bucket_coef(ri.T));
-        if (lane_id() == 0) {
-            if (wave_id() == 0)
-                o->l_lo = ord_float(im);
-            else
-                o->l_hi = ord_float(im - 1u);
-        }
-    }
-    __syncthreads();
-}
-
-// One workgroup per unit: the boundary bucket and its logit range.
-__global__ __launch_bounds__(kThreads) void fn_select_kernel(StepArgs a, int k) {
-    __shared__ double s_tmp[kWaves];
-    __shared__ uint64_t s_red[kWaves];
-    __shared__ SelOut s_sel;
-    __shared__ int s_star;
-    const int n = a.pos[k].n_cls[CLS_NUCLEUS];
-    const int32_t* list = nuc_list(a, k);
-    for (int li = blockIdx.x; li < n; li += gridDim.x) {
-        const int u = list[li];
-        unit_select(a, k, li, u, s_tmp, s_red, &s_star, &s_sel);  // barriers
-        if (threadIdx.x == 0) {
-            FnUnit* fu = a.fn_unit + u;
-            const SelOut so = s_sel;
-            if (so.beta >= 0) {
-                fu->Z = so.Z;
-                fu->A = so.A;
-                fu->beta = so.beta;
-                fu->la = so.la;
-                fu->l_lo = so.l_lo;
-                fu->l_hi = so.l_hi;
-                fu->status = 0;
-            } else {
-                fu->status = 2;  // no finite logit: invalid row
-            }
-        }
-        __syncthreads();  // s_sel is reused
-    }
-}
-
-// Keys of the boundary bucket: the logits in [l_lo, l_hi].  Each workgroup
-// gathers its piece's keys in LDS (one LDS counter update per wave and tile)
-// and reserves space in the unit's list with one global atomic per piece.
-// Keys beyond kCollectCap are dropped but still counted: such a bucket is
-// resolved from the row itself.
-template <int DT, bool kAligned>
-__global__ __launch_bounds__(kThreads) void fn_collect_kernel(StepArgs a, int k) {
-    using TS = TileShape<DT>;
-    static_assert(TS::kE <= 32, "hit mask is 32 bits");
-    __shared__ uint64_t s_keys[kCollectCap];
-    __shared__ int s_n, s_base;
-    const int64_t T = (int64_t)a.pos[k].n_cls[CLS_NUCLEUS] * a.ntiles;
-    int64_t t = flat_begin(T, gridDim.x, blockIdx.x);
-    const int64_t t_end = flat_begin(T, gridDim.x, blockIdx.x + 1);
-    const int32_t* list = nuc_list(a, k);
-    while (t < t_end) {
-        const int li = (int)(t / a.ntiles);
-        const int64_t tu0 = t - (int64_t)li * a.ntiles;
-        int64_t tu1 = tu0 + (t_end - t);
-        if (tu1 > a.ntiles) tu1 = a.ntiles;
-        t += tu1 - tu0;
-        const int u = list[li];
-        const int b = u >> 1, side = u & 1;
-        FnUnit* fu = a.fn_unit + u;
-        if (fu->status != 0) continue;  // uniform over the block
-        const float l_lo = fu->l_lo, l_hi = fu->l_hi;
-        if (threadIdx.x == 0) s_n = 0;
-        __syncthreads();
-        const int64_t start = tu0 * TS::kTile;
-        int64_t end = tu1 * TS::kTile;
-        if (end > a.V) end = a.V;
-        stream_range<DT, kAligned>(unit_row<DT>(a, b, side, k), start, end,
-                                   [&](float (&v)[TS::kE], int64_t t0, bool)
-                                       __attribute__((always_inline)) {
-            // past `end` elements read as -inf, below every boundary bucket
-            uint32_t hit = 0u;
-#pragma unroll
-            for (int i = TS::kE - 1; i >= 0; i--)
-                hit = (hit << 1) | (v[i] >= l_lo && v[i] <= l_hi ? 1u : 0u);
-            if (__ballot(hit != 0u) == 0ull) return;
-            int total;
-            const int excl = wave_excl_count((uint32_t)__popc(hit), &total);
-            int base = 0;
-            if (lane_id() == 0) base = atomicAdd(&s_n, total);
-            int slot = __builtin_amdgcn_readfirstlane(base) + excl;
-#pragma unroll
-            for (int i = 0; i < TS::kE; i++) {
-                if ((hit >> i) & 1u) {
-                    if (slot < kCollectCap) s_keys[slot] = make_key(v[i], (uint32_t)elem_id<DT>(t0, i));
-                    slot++;
-                }
-            }
-        });
-        __syncthreads();
-        const int n = s_n;
-        if (threadIdx.x == 0) s_base = n > 0 ? atomicAdd(&fu->ncoll, n) : 0;
-        __syncthreads();
-        const int nb = s_base;
-        uint64_t* coll = a.coll + (int64_t)u * kCollectCap;
-        for (int i = threadIdx.x; i < n && i < kCollectCap && nb + i < kCollectCap; i += kThreads)
-            coll[nb + i] = s_keys[i];
-        __syncthreads();  // s_keys and s_n are reused by the next piece
-    }
-}
-
-// One workgroup per unit: the exact cut inside the boundary bucket.
-//   1. the bucket's n tokens are split into 256 sub-buckets by the fraction
-//      of their window coordinate (a finer cut of the same monotone map),
-//      and the sub-bucket masses give the boundary sub-bucket the same way
-//      the buckets gave the boundary bucket;
-//   2. every token of the boundary sub-bucket is ranked implicitly: its
-//      preceding mass is the bucket mass before the sub-bucket plus the
-//      masses of the sub-bucket's tokens with a larger key.
-// Inside the bucket every mass is an exact fixed-point integer scaled by the
-// bucket's one factor, so these comparisons are exact up to that one product.
-// The first token of the boundary sub-bucket is always kept (its preceding
-// mass is below top_p Z by the choice of the sub-bucket), so the cut key tau
-// lies in that sub-bucket.
 constexpr int kSub = 256;
 static_assert(kSub == kThreads, "one sub-bucket per thread");
 
@@ -493,48 +234,194 @@ __device__ void resolve_wide(const void* row, int64_t V, FnUnit* fu, float la, f
     __syncthreads();
 }
 
+// The boundary of the cut from the unit's histogram in s_h (kNW buckets,
+// fixed point): Z, the boundary bucket (the last non-empty bucket whose
+// preceding mass is below top_p Z), the mass A before it and its logit range.
+// Every thread calls it (barriers inside); o->beta = -1 when there is no mass.
+struct SelOut {
+    double Z, A;
+    float l_lo, l_hi;
+    int beta;
+};
+
+__device__ inline void select_boundary(const uint64_t* s_h, float top_p, float la, float cb,
+                                       double* s_tmp /* kWaves */, int* s_star, SelOut* o) {
+    constexpr int kPer = kNW / kThreads;  // buckets per thread, taken in descending order
+    const int j0 = kNW - kPer * ((int)threadIdx.x + 1);  // this thread's lowest bucket
+    double mine = 0.0;
+#pragma unroll
+    for (int q = 0; q < kPer; q++) {
+        const int j = j0 + kPer - 1 - q;
+        mine += nuc_scale(j) * ((double)s_h[j] * kUnfix);
+    }
+    double Z;
+    const double excl0 = block_exclusive_scan(mine, s_tmp, &Z);
+    const double target = (double)top_p * Z;
+    if (threadIdx.x == 0) *s_star = -1;
+    __syncthreads();
+    double run = excl0;
+    int best = -1;
+    double best_before = 0.0;
+#pragma unroll
+    for (int q = 0; q < kPer; q++) {
+        const int j = j0 + kPer - 1 - q;
+        const uint64_t rel = s_h[j];
+        if (rel != 0ull && run < target) {
+            best = (int)threadIdx.x * kPer + q;
+            best_before = run;
+        }
+        run += nuc_scale(j) * ((double)rel * kUnfix);
+    }
+    if (best >= 0) atomicMax(s_star, best);
+    __syncthreads();
+    const int star = *s_star;
+    if (star >= 0 && best == star) {
+        o->Z = Z;
+        o->A = best_before;
+        o->beta = kNW - 1 - star;
+    }
+    if (star < 0 && threadIdx.x == 0) o->beta = -1;
+    if (star >= 0 && wave_id() < 2) {  // wave 0: the range's low end, wave 1: its high end
+        const uint32_t im = nuc_first_image(kNW - 1 - star + wave_id(), la, cb);
+        if (lane_id() == 0) {
+            if (wave_id() == 0)
+                o->l_lo = ord_float(im);
+            else
+                o->l_hi = ord_float(im - 1u);
+        }
+    }
+    __syncthreads();
+}
+
+// One workgroup per nucleus unit of position k: histogram, boundary bucket,
+// its keys, and the exact cut (see the top of this file).
 template <int DT, bool kAligned>
-__global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, int k) {
+__global__ __launch_bounds__(kThreads) void fn_cut_kernel(StepArgs a, int k) {
+    using TS = TileShape<DT>;
+    static_assert(TS::kE <= 32, "hit mask is 32 bits");
     constexpr int kOwn = 4;  // boundary tokens a thread ranks per pass
-    __shared__ uint64_t s_key[kCollectCap];
-    __shared__ uint64_t s_w[kCollectCap];
+    static_assert(kNW <= kCollectCap && kBins <= kCollectCap && kBins + kThreads <= kCollectCap,
+                  "LDS arrays are shared between the steps");
+    __shared__ uint64_t s_h[kCollectCap];    // histogram, then the boundary tokens' weights
+    __shared__ uint64_t s_key[kCollectCap];  // boundary-bucket keys
     __shared__ uint16_t s_sel[kCollectCap];
     __shared__ uint8_t s_sb[kCollectCap];
     __shared__ uint64_t s_sub[kSub];
-    __shared__ uint64_t s_tmp[kWaves];
+    __shared__ uint64_t s_tmp[kWaves], s_red[kWaves];
+    __shared__ double s_tmpd[kWaves];
+    __shared__ SelOut s_so;
     __shared__ unsigned long long s_tau, s_kept;
-    __shared__ int s_star, s_nsel;
+    __shared__ int s_star, s_nsel, s_n;
     __shared__ uint64_t s_before;
-    static_assert(kBins <= kCollectCap && 2 * kBins * sizeof(uint32_t) <= sizeof(s_w) &&
-                      kBins + kThreads <= kCollectCap,
-                  "the wide path reuses s_key and s_w");
-    const int n_units = a.pos[k].n_cls[CLS_NUCLEUS];
+    const PosDesc P = a.pos[k];
+    const int n_units = P.n_cls[CLS_NUCLEUS];
     const int32_t* list = nuc_list(a, k);
     for (int li = blockIdx.x; li < n_units; li += gridDim.x) {
         const int u = list[li];
-        const int b = u >> 1;
+        const int b = u >> 1, side = u & 1;
+        const RowInfo& ri = a.rows[b];
         FnUnit* fu = a.fn_unit + u;
-        const int status = fu->status;
-        const int n = fu->ncoll;
-        const float la = fu->la;
-        const int beta = fu->beta;
-        const double A = fu->A;
-        const double target = (double)a.rows[b].top_p * fu->Z;
-        __syncthreads();  // every thread has read fu before thread 0 may write it
-        if (status != 0) continue;  // uniform over the block
-        if (n < 1) {  // cannot happen: the boundary bucket has mass
-            if (threadIdx.x == 0) fu->status = 1;
+        const void* row = unit_row<DT>(a, b, side, k);
+        const float cb = bucket_coef(ri.T);
+        const RecRange rr =
+            unit_records(unit_index(P, CLS_NUCLEUS, li), pos_units(P), a.ntiles, a.g_row);
+        const bool re = fu->rehist != 0;
+        // 1. the unit's histogram in LDS
+        float la;
+        if (re) {
+            for (int j = threadIdx.x; j < kNW; j += kThreads) s_h[j] = 0ull;
+            la = unit_piece_max(a.parts, rr, s_red);  // barriers
+            stream_range<DT, kAligned>(row, 0, a.V, [&](float (&v)[TS::kE], int64_t, bool)
+                                                        __attribute__((always_inline)) {
+#pragma unroll
+                for (int i = 0; i < TS::kE; i++) {
+                    const float t = nuc_t(v[i], la, cb);
+                    int bin;
+                    const uint64_t w = nuc_wfix_t(t, &bin);
+                    if (nuc_in(t)) atomicAdd((unsigned long long*)&s_h[bin], (unsigned long long)w);
+                }
+            });
+        } else {
+            // thread t sums buckets t + q kThreads over the pieces in
+            // registers; a piece holds the buckets [lo, hi] of its slot's
+            // range, and all 16 loads of a piece go out together
+            constexpr int kPer = kNW / kThreads;
+            la = fu->la;
+            uint64_t acc[kPer];
+#pragma unroll
+            for (int q = 0; q < kPer; q++) acc[q] = 0ull;
+            for (int p = 0; p < rr.count; p++) {
+                const uint64_t rg = a.parts[rr.first + p].keys[1];
+                const int lo = (int)(uint32_t)(rg >> 32), hi = (int)(uint32_t)rg;
+                const uint64_t* h = a.hist + (int64_t)(rr.first + p) * kNW + threadIdx.x;
+#pragma unroll
+                for (int q = 0; q < kPer; q++) {
+                    const int j = q * kThreads + (int)threadIdx.x;
+                    acc[q] += (j >= lo && j <= hi) ? h[q * kThreads] : 0ull;
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < kPer; q++) s_h[q * kThreads + threadIdx.x] = acc[q];
+        }
+        __syncthreads();
+        // 2. the boundary bucket
+        select_boundary(s_h, ri.top_p, la, cb, s_tmpd, &s_star, &s_so);  // barriers
+        const SelOut so = s_so;
+        if (threadIdx.x == 0) fu->status = so.beta < 0 ? 2 : 0;  // 2: no finite logit
+        if (so.beta < 0) {
+            __syncthreads();
             continue;
         }
-        const float cb = bucket_coef(a.rows[b].T);
-        const double sc = nuc_scale(beta) * kUnfix;
-        if (n > kCollectCap) {
-            resolve_wide<DT, kAligned>(unit_row<DT>(a, b, u & 1, k), a.V, fu, la, cb, fu->l_lo,
-                                       fu->l_hi, A, sc, target, s_key, reinterpret_cast<uint32_t*>(s_w),
-                                       s_key + kBins, s_w + kBins, s_tmp);
+        // 3. the boundary bucket's keys
+        if (threadIdx.x == 0) s_n = 0;
+        __syncthreads();
+        stream_range<DT, kAligned>(row, 0, a.V, [&](float (&v)[TS::kE], int64_t t0, bool)
+                                                    __attribute__((always_inline)) {
+            // v lies in [l_lo, l_hi] iff (v - l_lo) (l_hi - v) >= 0, read off the
+            // product's sign bit (no compare-and-select chain); past `end`
+            // elements read as -inf and give a negative product
+            uint32_t hit = 0u;
+#pragma unroll
+            for (int i = 0; i < TS::kE; i++) {
+                const float pr = (v[i] - so.l_lo) * (so.l_hi - v[i]);
+                hit |= ((~__float_as_uint(pr)) >> 31) << i;
+            }
+            if (__ballot(hit != 0u) == 0ull) return;
+            int total;
+            const int nh = __popc(hit);
+            const int excl = wave_excl_count((uint32_t)nh, &total);
+            int base = 0;
+            if (lane_id() == 0) base = atomicAdd(&s_n, total);
+            const int slot = __builtin_amdgcn_readfirstlane(base) + excl;
+            uint32_t id0 = (uint32_t)elem_id<DT>(t0, 0);
+            asm volatile("" : "+v"(id0));
+            // one iteration per hit of this lane (few per tile)
+            for (int j = 0; j < nh; j++) {
+                constexpr int kVec = Elt<DT>::kVec;
+                const int i = __builtin_ctz(hit);
+                hit &= hit - 1u;
+                const uint32_t id = id0 + (uint32_t)((i / kVec) * kThreads * kVec + i % kVec);
+                if (slot + j < kCollectCap) s_key[slot + j] = make_key(pick_elem(v, i), id);
+            }
+        });
+        __syncthreads();
+        const int n = s_n;
+        const double target = (double)ri.top_p * so.Z;
+        const double sc = nuc_scale(so.beta) * kUnfix;
+        const double A = so.A;
+        if (n < 1 || n > kCollectCap) {
+            if (n < 1) {  // cannot happen: the boundary bucket has mass
+                if (threadIdx.x == 0) fu->status = 1;
+                __syncthreads();
+                continue;
+            }
+            if (threadIdx.x == 0) fu->la = la;
+            resolve_wide<DT, kAligned>(row, a.V, fu, la, cb, so.l_lo, so.l_hi, A, sc, target, s_h,
+                                       reinterpret_cast<uint32_t*>(s_key), s_h + kBins,
+                                       s_key + kBins, s_tmp);  // tau and S (barriers)
             continue;
         }
-        const uint64_t* coll = a.coll + (int64_t)u * kCollectCap;
+        // 4. the cut inside the boundary bucket
         s_sub[threadIdx.x] = 0ull;
         if (threadIdx.x == 0) {
             s_tau = ~0ull;
@@ -544,15 +431,14 @@ __global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, int k)
         }
         __syncthreads();
         for (int i = threadIdx.x; i < n; i += kThreads) {
-            const uint64_t key = coll[i];
+            const uint64_t key = s_key[i];
             const float t = nuc_t(key_logit(key), la, cb);
             const float fr = t - floorf(t);
             // sub-buckets in ranking order: a larger fraction is a larger logit
             int sb = kSub - 1 - (int)(fr * (float)kSub);
             sb = sb < 0 ? 0 : (sb >= kSub ? kSub - 1 : sb);
             const uint64_t w = nuc_wrel(fr);
-            s_key[i] = key;
-            s_w[i] = w;
+            s_h[i] = w;
             s_sb[i] = (uint8_t)sb;
             atomicAdd((unsigned long long*)&s_sub[sb], (unsigned long long)w);
         }
@@ -588,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, int k)
             }
             for (int j = 0; j < nsel; j++) {
                 const int sj = s_sel[j];
-                const uint64_t kj = s_key[sj], wj = s_w[sj];
+                const uint64_t kj = s_key[sj], wj = s_h[sj];
 #pragma unroll
                 for (int q = 0; q < kOwn; q++) pre[q] += kj > key[q] ? wj : 0ull;
             }
@@ -597,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, int k)
                 const int i = base + q * kThreads + (int)threadIdx.x;
                 if (i < nsel && A + sc * (double)pre[q] < target) {
                     atomicMin(&s_tau, (unsigned long long)key[q]);
-                    atomicAdd(&s_kept, (unsigned long long)s_w[s_sel[i]]);
+                    atomicAdd(&s_kept, (unsigned long long)s_h[s_sel[i]]);
                 }
             }
         }
@@ -605,6 +491,7 @@ __global__ __launch_bounds__(kThreads) void fn_resolve_kernel(StepArgs a, int k)
         if (threadIdx.x == 0) {
             fu->tau = s_tau;
             fu->S = A + sc * (double)(before + s_kept);
+            fu->la = la;
         }
         __syncthreads();
     }

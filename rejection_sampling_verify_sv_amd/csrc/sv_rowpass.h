@@ -334,7 +334,6 @@ __device__ __forceinline__ void seg_nuc(const void* row, int64_t start, int64_t 
         out->keys[0] = (uint64_t)__float_as_uint(pm);
         out->keys[1] = ((uint64_t)(uint32_t)lo << 32) | (uint64_t)(uint32_t)hi;
         fu->la = la;  // the same value from every piece
-        if (start == 0) fu->ncoll = 0;  // the collect pass counts from here
         // t is monotone in l: the piece max is the token that would lie
         // highest above the window
         if (tm >= (float)kHalf) fu->rehist = 1;

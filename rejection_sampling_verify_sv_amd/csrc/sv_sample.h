@@ -104,16 +104,22 @@ __global__ __launch_bounds__(kThreads) void sample_sums_kernel(StepArgs a) {
         double2* out = a.chunks + (int64_t)b * a.ntiles * kWaves;
         stream_range2<DT, kAligned>(trow, drow, start, end,
                                     [&](float (&vt)[TS::kE], float (&vd)[TS::kE], int64_t t0,
-                                        bool full) __attribute__((always_inline)) {
+                                        bool) __attribute__((always_inline)) {
+            // elements past `end` read as -inf on both rows and weigh 0
             double sr = 0.0, sp = 0.0;
+            uint32_t id0 = (uint32_t)elem_id<DT>(t0, 0);
+            asm volatile("" : "+v"(id0));  // keeps 16-32 ids from being hoisted
 #pragma unroll
             for (int i = 0; i < TS::kE; i++) {
-                const int64_t id = elem_id<DT>(t0, i);
-                if (!full && id >= end) continue;
+                constexpr int kVec = Elt<DT>::kVec;
+                const uint32_t id = id0 + (uint32_t)((i / kVec) * kThreads * kVec + i % kVec);
                 double wr, wp;
-                draw_weights(x, vt[i], vd[i], (uint32_t)id, &wr, &wp);
+                draw_weights(x, vt[i], vd[i], id, &wr, &wp);
                 sr += wr;
                 sp += wp;
+                // four elements at a time: the fp64 terms of all of them would
+                // otherwise be live at once
+                if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
             }
             sr = wave_sum(sr);
             sp = wave_sum(sp);

@@ -7,11 +7,9 @@
 //                                 units of position 0
 //   for k = 0 .. K:
 //     rowpass_kernel<k>           stream the units live at position k
-//     fn_hist / fn_select /
-//     fn_collect / fn_resolve<k>  exact top_p cut of full-vocab nucleus rows
-//                                 (their histograms come from the row pass;
-//                                 fn_hist only redoes rows whose max lies
-//                                 far above the anchor)
+//     fn_cut_kernel<k>            exact top_p cut of full-vocab nucleus rows,
+//                                 one workgroup per unit, from the
+//                                 histograms the row pass left
 //     decide_kernel<k>            accept / reject / draw; list the units of k+1
 //   sample_sums_kernel            full-vocab rows: per-chunk draw masses
 //   sample_pick_kernel            full-vocab rows: the drawn token
@@ -40,7 +38,7 @@ constexpr int kMaxDraft = 1024;
 struct Plan {
     int tile, ntiles;
     size_t off_rows, off_pos, off_ulist, off_slist, off_parts, off_tstat, off_chunks,
-        off_fnu, off_hist, off_hist2, off_coll, off_status, bytes;
+        off_fnu, off_hist, off_status, bytes;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -68,8 +66,6 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
     p->off_chunks = take(sizeof(double2) * (size_t)B * p->ntiles * kWaves);
     p->off_fnu = take(sizeof(FnUnit) * units);
     p->off_hist = take(sizeof(uint64_t) * slots * kNW);
-    p->off_hist2 = take(sizeof(uint64_t) * slots * kNW);
-    p->off_coll = take(sizeof(uint64_t) * units * kCollectCap);
     p->off_status = take(sizeof(int32_t) * (size_t)B);  // sv_sample without out_status
     p->bytes = off;
     return true;
@@ -84,10 +80,9 @@ int hip_fail(hipError_t e) {
 
 // Launch order of one step; sv_launch_count / sv_launch_name describe it.
 constexpr int kPre = 1;
-constexpr int kPerPos = 6;
+constexpr int kPerPos = 3;
 const char* const kPreNames[kPre] = {"plan"};
-const char* const kPosNames[kPerPos] = {"rowpass", "fn_hist", "fn_select",
-                                        "fn_collect", "fn_resolve", "decide"};
+const char* const kPosNames[kPerPos] = {"rowpass", "fn_cut", "decide"};
 int launch_count(int K) { return kPre + kPerPos * (K + 1) + 2; }
 
 const char* launch_name(int K, int i) {
@@ -103,7 +98,7 @@ const char* launch_name(int K, int i) {
 // slots reserved per position).  A second, partial wave would double the
 // time of the workgroups in it.
 struct Grids {
-    unsigned rowpass, hist, collect, sums;
+    unsigned rowpass, cut, sums;
 };
 
 template <class Kern>
@@ -137,8 +132,7 @@ int grids_for_device(Grids* out) {
     if (cus < 1) cus = 1;
     Grids g;
     g.rowpass = resident_grid(rowpass_kernel<DT, kAligned>, cus);
-    g.hist = resident_grid(fn_hist_kernel<DT, kAligned>, cus);
-    g.collect = resident_grid(fn_collect_kernel<DT, kAligned>, cus);
+    g.cut = resident_grid(fn_cut_kernel<DT, kAligned>, cus);
     g.sums = resident_grid(sample_sums_kernel<DT, kAligned>, cus);
     (void)hipGetLastError();
     if (dev >= 0 && dev < kMaxDevices) {
@@ -158,7 +152,6 @@ int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepAr
     const int rc = grids_for_device<DT, kAligned>(&g);
     if (rc != SV_OK) return rc;
     a.g_row = (int)g.rowpass;
-    a.g_hist = (int)g.hist;
     int n = 0;
     auto mark = [&]() {
         if (ev) (void)hipEventRecord(ev[n], st);
@@ -173,13 +166,7 @@ int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepAr
         mark();
         rowpass_kernel<DT, kAligned><<<g.rowpass, kThreads, 0, st>>>(a, k);
         mark();
-        fn_hist_kernel<DT, kAligned><<<g.hist, kThreads, 0, st>>>(a, k);
-        mark();
-        fn_select_kernel<<<unit_grid, kThreads, 0, st>>>(a, k);
-        mark();
-        fn_collect_kernel<DT, kAligned><<<g.collect, kThreads, 0, st>>>(a, k);
-        mark();
-        fn_resolve_kernel<DT, kAligned><<<unit_grid, kThreads, 0, st>>>(a, k);
+        fn_cut_kernel<DT, kAligned><<<g.cut < unit_grid ? g.cut : unit_grid, kThreads, 0, st>>>(a, k);
         mark();
         decide_kernel<DT><<<(unsigned)((B + kDecideRows - 1) / kDecideRows), kDecideThreads, 0, st>>>(a,
                                                                                            k);
@@ -242,9 +229,7 @@ static int verify_impl(const void* target_logits, const void* draft_logits,
     a.fn_unit = reinterpret_cast<FnUnit*>(ws + pl.off_fnu);
     a.tstat = reinterpret_cast<FullStat*>(ws + pl.off_tstat);
     a.hist = reinterpret_cast<uint64_t*>(ws + pl.off_hist);
-    a.hist2 = reinterpret_cast<uint64_t*>(ws + pl.off_hist2);
-    a.coll = reinterpret_cast<uint64_t*>(ws + pl.off_coll);
-    a.g_row = a.g_hist = 0;
+    a.g_row = 0;
 
     const size_t esz = (dt == SV_F32) ? 4 : 2;
     const bool aligned = reinterpret_cast<uintptr_t>(target_logits) % 16 == 0 &&
