@@ -509,6 +509,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
         a.pos[i].n_sample = 0;
     }
     if (threadIdx.x < kNumCls) s_nc[threadIdx.x] = 0;
+    {  // counters of split nucleus units (each launch leaves them at zero)
+        const int rows = 2 * a.B < kGrid / 2 ? 2 * a.B : kGrid / 2;
+        for (int i = threadIdx.x; i < 2 * rows; i += kPlanThreads) a.fn_sync[i] = 0;
+    }
     __syncthreads();
     for (int b = threadIdx.x; b < a.B; b += kPlanThreads) {
         const sv_sampler_params prm = params[b];

@@ -5,7 +5,8 @@
 //   * a "tile" is what one workgroup reads in one step: every thread issues
 //     kLoads 16-byte loads, consecutive lanes read consecutive 16-byte vectors
 //     (fully coalesced), so a tile is 16 KiB of logits (4096 fp32 or 8192 bf16);
-//     tiles are double-buffered, so two tiles per workgroup are in flight;
+//     tiles are double-buffered, so two tiles per workgroup are in flight
+//     (a workgroup streaming a whole row alone keeps more, see TileRing);
 //   * a "unit" is one logits row to stream: (batch row b, side), side 0 = the
 //     target row, side 1 = the draft row of the current position;
 //   * units live at a position are listed on the device, and their tiles are
@@ -418,6 +419,77 @@ __device__ __forceinline__ void stream_range(const void* row, int64_t start, int
     }
 }
 
+// Elements [start, end) of a row (start tile-aligned) streamed by one
+// workgroup, kDepth full tiles in flight.  A workgroup working alone is bound
+// by the latency of its loads, not by HBM, so it keeps more of them
+// outstanding than the double buffer of stream_range.  start() issues the
+// first tiles and may run well before run(): the loads then overlap whatever
+// the workgroup does in between.  run() covers the same ground as
+// stream_range (full tiles, then the ragged tail); `body` must not contain
+// barriers.
+template <int DT, bool kAligned, int kDepth>
+struct TileRing {
+    using TS = TileShape<DT>;
+    RawTile r[kDepth];
+    int64_t nt;  // full tiles streamed through the ring
+
+    __device__ __forceinline__ void start(const void* row, int64_t start, int64_t end) {
+        nt = kAligned ? (end - start) / TS::kTile : 0;
+        if (nt > 0) {
+#pragma unroll
+            for (int j = 0; j < kDepth; j++)
+                issue_tile<DT>(row, start + (j < nt ? j : nt - 1) * TS::kTile, r[j]);
+        } else {
+            // defined on every path: buffers left undefined here were seen
+            // to be kept live (as copies of an earlier use) across a
+            // caller's surrounding loop
+#pragma unroll
+            for (int j = 0; j < kDepth; j++)
+#pragma unroll
+                for (int q = 0; q < kLoads; q++) r[j].q[q] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+
+    // Counted rounds with one exit, as in stream_range; prefetches past the
+    // last full tile re-read it and are dropped.
+    template <class Body>
+    __device__ __forceinline__ void run(const void* row, int64_t start, int64_t end, Body&& body) {
+        float v[TS::kE];
+        int64_t t0 = start;
+        if (nt > 0) {
+            const int64_t last = start + (nt - 1) * TS::kTile;
+            for (int64_t p = nt / kDepth; p > 0; --p) {
+#pragma unroll
+                for (int j = 0; j < kDepth; j++) {
+                    unpack_tile<DT>(r[j], v);
+                    body(v, t0 + j * TS::kTile, true);
+                    const int64_t tn = t0 + (kDepth + j) * TS::kTile;
+                    issue_tile<DT>(row, tn <= last ? tn : last, r[j]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                t0 += kDepth * TS::kTile;
+            }
+            const int rem = (int)(nt % kDepth);
+#pragma unroll
+            for (int j = 0; j < kDepth - 1; j++) {
+                if (j < rem) {
+                    unpack_tile<DT>(r[j], v);
+                    body(v, t0, true);
+                    t0 += TS::kTile;
+                }
+            }
+        }
+        while (t0 < end) {
+            if constexpr (kAligned)
+                load_tile_tail<DT>(row, t0, end, v);
+            else
+                load_tile_partial<DT>(row, t0, end, v);
+            body(v, t0, t0 + TS::kTile <= end);
+            t0 += TS::kTile;
+        }
+    }
+};
+
 // Same as stream_range over two rows in lockstep (the second may be null):
 // body(va, vb, t0, full); vb is all -inf when rb is null.
 template <int DT, bool kAligned, class Body>
@@ -733,6 +805,8 @@ struct StepArgs {
     int32_t* slist;        // [B] rows that draw over the full vocabulary at the end
     FnUnit* fn_unit;       // [2B] nucleus cut of the current position
     uint64_t* hist;        // [2B + kGrid][kNW] nucleus histograms of the row pass, slot u + w
+    uint64_t* fn_keys;     // [kGrid / 2][kCollectCap] boundary keys of a unit whose cut is split
+    int32_t* fn_sync;      // [kGrid / 2][2] per split unit: workgroups arrived, keys reserved
 };
 
 template <int DT>

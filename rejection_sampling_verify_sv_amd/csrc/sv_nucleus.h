@@ -8,26 +8,32 @@
 // those of the anchor window (sv_device.h).
 //
 // The row pass leaves each nucleus unit's mass histogram, one per piece.
-// Then one workgroup per unit (fn_cut) finishes the cut:
+// Then fn_cut finishes the cut, one workgroup per unit, or several when the
+// units are few:
 //   hist     the unit's histogram in LDS: the sum of its pieces, or, when a
 //            piece saw a token above the window, the row again, anchored at
 //            the row max;
 //   select   Z = total mass; the boundary bucket is the last non-empty bucket
 //            whose preceding mass is below top_p Z, with its exact logit
 //            range [l_lo, l_hi];
-//   collect  the row once more, keeping the keys of the boundary bucket's
-//            tokens in LDS (a bucket too large for LDS is instead narrowed by
-//            a radix select over its keys, see resolve_wide);
+//   collect  the row once more (a slice of it per workgroup of a split
+//            unit), keeping the keys of the boundary bucket's tokens; a split
+//            unit's workgroups publish theirs to global memory and the last
+//            to arrive goes on with all of them (a bucket too large for LDS
+//            is instead narrowed by a radix select over its keys, see
+//            resolve_wide);
 //   resolve  a token of the boundary bucket is kept when the mass before the
 //            bucket plus the mass of the bucket's tokens ranked ahead of it
 //            (logit desc, id asc) is below top_p Z.  The cut key tau (last
 //            kept token) and the kept mass S define the distribution
 //            p(i) = [key_i >= tau] exp(t_i / 64) / S.
 // Within a bucket the masses are exact fixed-point integers; across buckets
-// they are combined in fp64 in one fixed order, so the cut is deterministic.
-// A workgroup streams its row at about 100 GB/s alone, and a few hundred of
-// them together saturate HBM, so one launch per position replaces the
-// grid-wide passes and the launches between them.
+// they are combined in fp64 in one fixed order, so the cut is deterministic
+// (the workgroups of a split unit find the same boundary).  One launch per
+// position replaces grid-wide passes and the launches between them: a few
+// hundred workgroups reading rows on their own saturate HBM, and a few
+// dozen units are split so that their rows are still read by many compute
+// units.
 #pragma once
 
 #include "sv_decide.h"
@@ -247,7 +253,9 @@ struct SelOut {
 __device__ inline void select_boundary(const uint64_t* s_h, float top_p, float la, float cb,
                                        double* s_tmp /* kWaves */, int* s_star, SelOut* o) {
     constexpr int kPer = kNW / kThreads;  // buckets per thread, taken in descending order
-    const int j0 = kNW - kPer * ((int)threadIdx.x + 1);  // this thread's lowest bucket
+    // this thread's lowest bucket; opaque, so that the scales below are
+    // loaded here rather than hoisted and held across the caller's loop
+    const int j0 = kNW - kPer * (tid_opaque() + 1);
     double mine = 0.0;
 #pragma unroll
     for (int q = 0; q < kPer; q++) {
@@ -293,13 +301,32 @@ __device__ inline void select_boundary(const uint64_t* s_h, float top_p, float l
     __syncthreads();
 }
 
-// One workgroup per nucleus unit of position k: histogram, boundary bucket,
-// its keys, and the exact cut (see the top of this file).
+// Workgroups per unit in fn_cut.  One workgroup alone reads a row far below
+// its share of HBM (its collect step is bound by instruction issue), so when
+// the units are few each gets several, up to one per compute unit in all
+// (the grid holds two per compute unit; two on one compute unit only halve
+// each other's issue rate), at most kMaxSplit and one per tile of the row.
+// A split unit's index in the nucleus list is below gridDim.x / 4 < kGrid / 2,
+// the rows of fn_sync and fn_keys.
+constexpr int kMaxSplit = 8;
+__host__ __device__ inline int fn_split(int n_units, int grid, int ntiles) {
+    if (n_units <= 0) return 1;
+    int s = (grid / 2) / n_units;
+    s = s < kMaxSplit ? s : kMaxSplit;
+    s = s < ntiles ? s : ntiles;
+    return s > 1 ? s : 1;
+}
+
+// The nucleus units of position k, one or (few units) several workgroups
+// each: histogram, boundary bucket, its keys, and the exact cut (see the top
+// of this file).
 template <int DT, bool kAligned>
 __global__ __launch_bounds__(kThreads) void fn_cut_kernel(StepArgs a, int k) {
     using TS = TileShape<DT>;
     static_assert(TS::kE <= 32, "hit mask is 32 bits");
     constexpr int kOwn = 4;  // boundary tokens a thread ranks per pass
+    constexpr int kRing = 4;  // tiles in flight while collecting
+    constexpr int kWaveCap = kCollectCap / kWaves;  // boundary keys a wave can hold
     static_assert(kNW <= kCollectCap && kBins <= kCollectCap && kBins + kThreads <= kCollectCap,
                   "LDS arrays are shared between the steps");
     __shared__ uint64_t s_h[kCollectCap];    // histogram, then the boundary tokens' weights
@@ -311,12 +338,19 @@ __global__ __launch_bounds__(kThreads) void fn_cut_kernel(StepArgs a, int k) {
     __shared__ double s_tmpd[kWaves];
     __shared__ SelOut s_so;
     __shared__ unsigned long long s_tau, s_kept;
-    __shared__ int s_star, s_nsel, s_n;
+    __shared__ int s_star, s_nsel, s_wcnt[kWaves], s_base, s_last;
     __shared__ uint64_t s_before;
     const PosDesc P = a.pos[k];
     const int n_units = P.n_cls[CLS_NUCLEUS];
     const int32_t* list = nuc_list(a, k);
-    for (int li = blockIdx.x; li < n_units; li += gridDim.x) {
+    // Few units: each is split over S workgroups, which all find the same
+    // boundary from the same histogram and collect the keys of one slice of
+    // the row each; the last of them to finish ranks the keys.  Many units:
+    // one workgroup per unit.
+    const int S = fn_split(n_units, (int)gridDim.x, a.ntiles);
+    const int n_work = n_units * S;
+    for (int wi = blockIdx.x; wi < n_work; wi += gridDim.x) {
+        const int li = wi / S, sl = wi - li * S;
         const int u = list[li];
         const int b = u >> 1, side = u & 1;
         const RowInfo& ri = a.rows[b];
@@ -344,7 +378,8 @@ __global__ __launch_bounds__(kThreads) void fn_cut_kernel(StepArgs a, int k) {
         } else {
             // thread t sums buckets t + q kThreads over the pieces in
             // registers; a piece holds the buckets [lo, hi] of its slot's
-            // range, and all 16 loads of a piece go out together
+            // range (the rest are stale and masked off), so its loads go out
+            // together with that of its range
             constexpr int kPer = kNW / kThreads;
             la = fu->la;
             uint64_t acc[kPer];
@@ -352,12 +387,15 @@ __global__ __launch_bounds__(kThreads) void fn_cut_kernel(StepArgs a, int k) {
             for (int q = 0; q < kPer; q++) acc[q] = 0ull;
             for (int p = 0; p < rr.count; p++) {
                 const uint64_t rg = a.parts[rr.first + p].keys[1];
-                const int lo = (int)(uint32_t)(rg >> 32), hi = (int)(uint32_t)rg;
                 const uint64_t* h = a.hist + (int64_t)(rr.first + p) * kNW + threadIdx.x;
+                uint64_t x[kPer];
+#pragma unroll
+                for (int q = 0; q < kPer; q++) x[q] = h[q * kThreads];
+                const int lo = (int)(uint32_t)(rg >> 32), hi = (int)(uint32_t)rg;
 #pragma unroll
                 for (int q = 0; q < kPer; q++) {
                     const int j = q * kThreads + (int)threadIdx.x;
-                    acc[q] += (j >= lo && j <= hi) ? h[q * kThreads] : 0ull;
+                    acc[q] += (j >= lo && j <= hi) ? x[q] : 0ull;
                 }
             }
 #pragma unroll
@@ -372,40 +410,122 @@ __global__ __launch_bounds__(kThreads) void fn_cut_kernel(StepArgs a, int k) {
             __syncthreads();
             continue;
         }
-        // 3. the boundary bucket's keys
-        if (threadIdx.x == 0) s_n = 0;
-        __syncthreads();
-        stream_range<DT, kAligned>(row, 0, a.V, [&](float (&v)[TS::kE], int64_t t0, bool)
-                                                    __attribute__((always_inline)) {
-            // v lies in [l_lo, l_hi] iff (v - l_lo) (l_hi - v) >= 0, read off the
-            // product's sign bit (no compare-and-select chain); past `end`
-            // elements read as -inf and give a negative product
+        // 3. the boundary bucket's keys in this workgroup's slice of the row,
+        //    appended by each wave to its own quarter of s_h (free once the
+        //    boundary is known) with a wave-uniform count: no atomics and no
+        //    scans on the way
+        const float l_lo = so.l_lo, l_hi = so.l_hi;
+        const int64_t e_lo = ((int64_t)sl * a.ntiles / S) * TS::kTile;
+        const int64_t e_hi = min(((int64_t)(sl + 1) * a.ntiles / S) * TS::kTile, (int64_t)a.V);
+        uint64_t* const s_mine = s_h + wave_id() * kWaveCap;
+        int filled = 0;  // wave-uniform
+        auto cbody = [&](float (&v)[TS::kE], int64_t t0, bool)
+                                      __attribute__((always_inline)) {
+            // v lies in [l_lo, l_hi] iff clamping it to that range leaves it
+            // unchanged (never for -inf past `end`); the wave-wide test costs
+            // two vector instructions per element, the per-lane bits are only
+            // formed for tiles with a hit
+            bool any = false;
+#pragma unroll
+            for (int i = 0; i < TS::kE; i++) any |= __builtin_amdgcn_fmed3f(v[i], l_lo, l_hi) == v[i];
+            if (__ballot(any) == 0ull) return;
+            // per-lane bits from the sign of (v - l_lo) (l_hi - v), the same
+            // test in another form (not merged with the one above, whose
+            // per-element masks would otherwise stay live in scalar registers)
             uint32_t hit = 0u;
 #pragma unroll
             for (int i = 0; i < TS::kE; i++) {
-                const float pr = (v[i] - so.l_lo) * (so.l_hi - v[i]);
+                const float pr = (v[i] - l_lo) * (l_hi - v[i]);
                 hit |= ((~__float_as_uint(pr)) >> 31) << i;
             }
-            if (__ballot(hit != 0u) == 0ull) return;
-            int total;
-            const int nh = __popc(hit);
-            const int excl = wave_excl_count((uint32_t)nh, &total);
-            int base = 0;
-            if (lane_id() == 0) base = atomicAdd(&s_n, total);
-            const int slot = __builtin_amdgcn_readfirstlane(base) + excl;
             uint32_t id0 = (uint32_t)elem_id<DT>(t0, 0);
             asm volatile("" : "+v"(id0));
-            // one iteration per hit of this lane (few per tile)
-            for (int j = 0; j < nh; j++) {
-                constexpr int kVec = Elt<DT>::kVec;
-                const int i = __builtin_ctz(hit);
-                hit &= hit - 1u;
-                const uint32_t id = id0 + (uint32_t)((i / kVec) * kThreads * kVec + i % kVec);
-                if (slot + j < kCollectCap) s_key[slot + j] = make_key(pick_elem(v, i), id);
+            // round r stores the r-th hit of every lane that has one; the
+            // lane's slot is its rank among those lanes
+            for (;;) {
+                const uint64_t m = __ballot(hit != 0u);
+                if (m == 0ull) break;
+                if (hit != 0u) {
+                    constexpr int kVec = Elt<DT>::kVec;
+                    const int i = __builtin_ctz(hit);
+                    hit &= hit - 1u;
+                    const int slot = filled + (int)__builtin_amdgcn_mbcnt_hi(
+                                                  (uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    const uint32_t id = id0 + (uint32_t)((i / kVec) * kThreads * kVec + i % kVec);
+                    if (slot < kWaveCap) s_mine[slot] = make_key(pick_elem(v, i), id);
+                }
+                filled += __popcll(m);
             }
-        });
+        };
+        // a split unit's workgroup streams a short slice alone: keep more
+        // tiles in flight; one workgroup per unit means many units, which
+        // share HBM evenly with the plain double buffer
+        if (S > 1) {
+            TileRing<DT, kAligned, kRing> ring;
+            ring.start(row, e_lo, e_hi);
+            ring.run(row, e_lo, e_hi, cbody);
+        } else {
+            stream_range<DT, kAligned>(row, e_lo, e_hi, cbody);
+        }
+        if (lane_id() == 0) s_wcnt[wave_id()] = filled;
         __syncthreads();
-        const int n = s_n;
+        int n = 0;
+        bool over = false;
+#pragma unroll
+        for (int w = 0; w < kWaves; w++) {
+            n += s_wcnt[w];
+            over |= s_wcnt[w] > kWaveCap;
+        }
+        if (!over) {  // the waves' lists, end to end, into s_key
+            for (int i = threadIdx.x; i < n; i += kThreads) {
+                int w = 0, off = 0;
+#pragma unroll
+                for (int q = 0; q < kWaves - 1; q++) {
+                    const bool past = i >= off + s_wcnt[w];
+                    off += past ? s_wcnt[w] : 0;
+                    w += past ? 1 : 0;
+                }
+                s_key[i] = s_h[w * kWaveCap + (i - off)];
+            }
+        }
+        if (S > 1) {
+            // Publish the slice's keys; only the unit's last workgroup goes
+            // on.  The keys are stored and loaded at device scope (through
+            // to, and from, the point where all of the chip's caches agree),
+            // and the arrival is a release: it follows those stores.  No
+            // acquire fence is needed on the reading side, whose device-scope
+            // loads cannot be served from a stale line, and an acquire would
+            // invalidate the whole L2 under every workgroup sharing it.
+            int32_t* const sync = a.fn_sync + 2 * li;  // [0] arrived, [1] keys reserved
+            uint64_t* const gk = a.fn_keys + (int64_t)li * kCollectCap;
+            __syncthreads();
+            if (threadIdx.x == 0) s_base = atomicAdd(&sync[1], over ? kCollectCap + 1 : n);
+            __syncthreads();
+            const int base = s_base;
+            if (!over)
+                for (int i = threadIdx.x; i < n && base + i < kCollectCap; i += kThreads)
+                    __hip_atomic_store(gk + base + i, s_key[i], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            if (threadIdx.x == 0)
+                s_last = __hip_atomic_fetch_add(&sync[0], 1, __ATOMIC_RELEASE,
+                                                __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+            __syncthreads();
+            if (!s_last) continue;
+            n = __hip_atomic_load(&sync[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            over = n > kCollectCap;
+            if (!over)
+                for (int i = threadIdx.x; i < n; i += kThreads)
+                    s_key[i] = __hip_atomic_load(gk + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            if (threadIdx.x == 0) {  // ready for the next position's launch
+                sync[0] = 0;
+                sync[1] = 0;
+            }
+        }
+        __syncthreads();
+        if (over) n = kCollectCap + 1;
         const double target = (double)ri.top_p * so.Z;
         const double sc = nuc_scale(so.beta) * kUnfix;
         const double A = so.A;

@@ -7,9 +7,10 @@
 //                                 units of position 0
 //   for k = 0 .. K:
 //     rowpass_kernel<k>           stream the units live at position k
-//     fn_cut_kernel<k>            exact top_p cut of full-vocab nucleus rows,
-//                                 one workgroup per unit, from the
-//                                 histograms the row pass left
+//     fn_cut_kernel<k>            exact top_p cut of full-vocab nucleus rows
+//                                 from the histograms the row pass left,
+//                                 one or (few units) several workgroups
+//                                 per unit
 //     decide_kernel<k>            accept / reject / draw; list the units of k+1
 //   sample_sums_kernel            full-vocab rows: per-chunk draw masses
 //   sample_pick_kernel            full-vocab rows: the drawn token
@@ -38,7 +39,7 @@ constexpr int kMaxDraft = 1024;
 struct Plan {
     int tile, ntiles;
     size_t off_rows, off_pos, off_ulist, off_slist, off_parts, off_tstat, off_chunks,
-        off_fnu, off_hist, off_status, bytes;
+        off_fnu, off_hist, off_fnkeys, off_fnsync, off_status, bytes;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -66,6 +67,11 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
     p->off_chunks = take(sizeof(double2) * (size_t)B * p->ntiles * kWaves);
     p->off_fnu = take(sizeof(FnUnit) * units);
     p->off_hist = take(sizeof(uint64_t) * slots * kNW);
+    // split nucleus units: their index in the position's list is below
+    // min(2B, kGrid / 2)
+    const size_t split_rows = units < (size_t)kGrid / 2 ? units : (size_t)kGrid / 2;
+    p->off_fnkeys = take(sizeof(uint64_t) * split_rows * kCollectCap);
+    p->off_fnsync = take(sizeof(int32_t) * 2 * split_rows);
     p->off_status = take(sizeof(int32_t) * (size_t)B);  // sv_sample without out_status
     p->bytes = off;
     return true;
@@ -158,7 +164,9 @@ int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepAr
         n++;
     };
     const int B = a.B;
-    const unsigned unit_grid = (unsigned)(2 * B < kGrid ? 2 * B : kGrid);
+    // fn_cut: up to kMaxSplit workgroups per nucleus unit
+    const unsigned cut_cap = (unsigned)(2 * B * kMaxSplit < kGrid ? 2 * B * kMaxSplit : kGrid);
+    const unsigned cut_grid = g.cut < cut_cap ? g.cut : cut_cap;
     const unsigned row_grid = (unsigned)(B < kGrid ? B : kGrid);
     mark();
     plan_kernel<<<1, kPlanThreads, 0, st>>>(a, draft_len, params);
@@ -166,7 +174,7 @@ int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepAr
         mark();
         rowpass_kernel<DT, kAligned><<<g.rowpass, kThreads, 0, st>>>(a, k);
         mark();
-        fn_cut_kernel<DT, kAligned><<<g.cut < unit_grid ? g.cut : unit_grid, kThreads, 0, st>>>(a, k);
+        fn_cut_kernel<DT, kAligned><<<cut_grid, kThreads, 0, st>>>(a, k);
         mark();
         decide_kernel<DT><<<(unsigned)((B + kDecideRows - 1) / kDecideRows), kDecideThreads, 0, st>>>(a,
                                                                                            k);
@@ -229,6 +237,8 @@ static int verify_impl(const void* target_logits, const void* draft_logits,
     a.fn_unit = reinterpret_cast<FnUnit*>(ws + pl.off_fnu);
     a.tstat = reinterpret_cast<FullStat*>(ws + pl.off_tstat);
     a.hist = reinterpret_cast<uint64_t*>(ws + pl.off_hist);
+    a.fn_keys = reinterpret_cast<uint64_t*>(ws + pl.off_fnkeys);
+    a.fn_sync = reinterpret_cast<int32_t*>(ws + pl.off_fnsync);
     a.g_row = 0;
 
     const size_t esz = (dt == SV_F32) ? 4 : 2;

@@ -322,3 +322,33 @@ def test_nucleus_anchor_cases(oracle_mod, dev):
         wl.draft[b, :, :512] = -np.inf
     rep, _, g_acc = check(oracle_mod, wl, dev, label="nucleus_anchor_cases")
     assert rep.unsupported == 0 and rep.error_rows == 0 and rep.compared == B
+
+
+@pytest.mark.parametrize("B", [8, 80], ids=["split_units", "one_workgroup_per_unit"])
+def test_nucleus_boundary_in_one_wave(oracle_mod, dev, B):
+    """A boundary bucket of 2000 equal logits, all at offsets that one wave
+    of a 4096-element tile reads: with one workgroup per unit (80 rows, 160
+    nucleus units) that wave's share of the collect buffer overflows and the
+    cut takes the wide path; with few rows the unit is split into slices and
+    each slice's keys fit."""
+    rng = np.random.default_rng(zlib.crc32(b"boundary_one_wave") + B)
+    K, V = 2, 20480
+    pos = np.flatnonzero(np.arange(V) % 1024 < 256)
+
+    def row():
+        r = rng.normal(-5.0, 0.3, V)
+        r[rng.choice(pos, size=2000, replace=False)] = 0.0
+        return r
+
+    t = np.stack([np.stack([row() for _ in range(K + 1)]) for _ in range(B)])
+    d = np.stack([np.stack([row() for _ in range(K)]) for _ in range(B)])
+    prm = np.zeros(B, PARAMS_DTYPE)
+    prm["temperature"], prm["top_k"], prm["top_p"] = 1.0, 0, 0.5
+    tok = np.zeros((B, K), np.int32)
+    for b in range(B):
+        for k in range(K):
+            tok[b, k] = int(np.argmax(d[b, k] + rng.gumbel(size=V)))
+    u = rng.random((B, K + 1), dtype=np.float32)
+    wl = workloads.custom(t, d, tok, np.full(B, K, np.int32), prm, u, dtype="f32")
+    rep, _, _ = check(oracle_mod, wl, dev, label=f"nucleus_boundary_in_one_wave_B{B}")
+    assert rep.unsupported == 0 and rep.error_rows == 0 and rep.compared == B
