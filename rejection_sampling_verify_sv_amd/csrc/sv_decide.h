@@ -30,14 +30,34 @@ namespace sv {
 // records what it adds to the next position's unit lists or to the draw list
 // (DecideIntent, in LDS); the workgroup then reserves space for all its rows
 // with one global atomic per list, instead of one per row.
-constexpr int kDecideRows = 4;
-constexpr int kDecideThreads = kDecideRows * kWave;
+constexpr int kDecideRows = kWaves;
 
 struct DecideIntent {
     int32_t nu;    // units to list at position k+1 (0: none)
     int32_t cls;   // their class region
     int32_t draw;  // 1: the row draws over the full vocabulary at the end
 };
+
+// Per-wave LDS of the top-k draw, passed in by the kernel (which lays it over
+// memory that its other steps use).
+struct TopkScratch {
+    double w[kWave];
+    double p[kWave];
+    int32_t id[kWave];
+};
+
+// A nucleus unit's cut, as another workgroup of the same launch may have
+// left it (device-scope loads, see dev_store).
+__device__ inline FnUnit fn_unit_load(const FnUnit* f) {
+    FnUnit* m = const_cast<FnUnit*>(f);
+    FnUnit r;
+    r.S = __longlong_as_double((long long)dev_load(reinterpret_cast<uint64_t*>(&m->S)));
+    r.tau = dev_load(&m->tau);
+    r.la = __int_as_float(dev_load(reinterpret_cast<int32_t*>(&m->la)));
+    r.status = dev_load(&m->status);
+    r.rehist = 0;
+    return r;
+}
 
 __device__ inline void diag_nan_row(double* diag, int b, int K) {
     if (!diag) return;
@@ -163,13 +183,10 @@ __device__ inline void continue_row(const StepArgs& a, int b, int k, const RowIn
 __device__ inline void queue_draw(DecideIntent& it) { it.draw = 1; }
 
 __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, int n,
-                            DecideIntent& it) {
-    __shared__ double s_wr[kDecideRows][kWave];
-    __shared__ double s_pr[kDecideRows][kWave];
-    __shared__ int s_idr[kDecideRows][kWave];
-    double* s_w = s_wr[wave_id()];
-    double* s_p = s_pr[wave_id()];
-    int* s_id = s_idr[wave_id()];
+                            TopkScratch& ts, DecideIntent& it) {
+    double* s_w = ts.w;
+    double* s_p = ts.p;
+    int* s_id = ts.id;
     const int lane = lane_id();
     const int k_eff = ri.k_eff;
     const double T = (double)ri.T, top_p = (double)ri.top_p;
@@ -373,14 +390,14 @@ __device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri, 
 template <int DT>
 __device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& ri,
                                DecideIntent& it) {
-    const FnUnit ut = a.fn_unit[b * 2];
+    const FnUnit ut = fn_unit_load(a.fn_unit + b * 2);
     const bool has_draft = k < ri.L;
     FnUnit ud;
     ud.status = 0;
     float lx = 0.f, ld = 0.f, ukf = 0.f;
     int x = 0;
     if (has_draft) {  // loaded together with the cut states
-        ud = a.fn_unit[b * 2 + 1];
+        ud = fn_unit_load(a.fn_unit + b * 2 + 1);
         x = a.tokens[(int64_t)b * a.K + k];
         if (x >= 0 && x < a.V) {  // validated by the plan; kept in range here regardless
             lx = load_one<DT>(unit_row<DT>(a, b, 0, k), x);
@@ -429,40 +446,46 @@ __device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& r
     }
 }
 
-// One wave per row (rows not live at position k do nothing), then the
-// workgroup's list updates: per class region and for the draw list, one
-// global atomic reserves the space of all its rows, and each row writes its
-// entries in wave order.
+// One row per wave (b_w < 0: none; rows not live at position k, and
+// nucleus rows when skip_nucleus is set, do nothing), then the workgroup's
+// list updates: per class region and for the draw list, one global atomic
+// reserves the space of all its rows, and each row writes its entries in
+// wave order.  Every thread of the workgroup calls it (barriers inside).
+// Not inlined, so that its registers are not added to those of the cut
+// around it; the arguments come from their copy in device memory (a kernel
+// argument passed by reference would be copied to private memory first).
 template <int DT>
-__global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepArgs a, int k) {
-    __shared__ DecideIntent s_it[kDecideRows];
-    __shared__ int s_base[kNumCls + 1];
+__device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, int k, int b_w,
+                                                      bool skip_nucleus, DecideIntent* s_it,
+                                                      int* s_base, TopkScratch* s_ts) {
+    const StepArgs& a = *ga;
     const int w = wave_id(), lane = lane_id();
-    const int b = blockIdx.x * kDecideRows + w;
     if (lane == 0) {
         s_it[w].nu = 0;
         s_it[w].cls = 0;
         s_it[w].draw = 0;
     }
-    RowInfo ri;
-    if (b < a.B) ri = a.rows[b];
-    if (b < a.B && ri.status == ST_LIVE && k <= ri.L) {
-        const int n = pos_units(a.pos[k]);
-        DecideIntent& it = s_it[w];
-        if (ri.cls == CLS_GREEDY)
-            decide_greedy(a, b, k, ri, n, it);
-        else if (ri.cls == CLS_TOPK)
-            decide_topk(a, b, k, ri, n, it);
-        else if (ri.cls == CLS_NUCLEUS)
-            decide_nucleus<DT>(a, b, k, ri, it);
-        else
-            decide_full<DT>(a, b, k, ri, it);
+    if (b_w >= 0) {
+        const int b = b_w;
+        const RowInfo ri = a.rows[b];
+        if (ri.status == ST_LIVE && k <= ri.L && !(skip_nucleus && ri.cls == CLS_NUCLEUS)) {
+            const int n = pos_units(a.pos[k]);
+            DecideIntent& it = s_it[w];
+            if (ri.cls == CLS_GREEDY)
+                decide_greedy(a, b, k, ri, n, it);
+            else if (ri.cls == CLS_TOPK)
+                decide_topk(a, b, k, ri, n, s_ts[w], it);
+            else if (ri.cls == CLS_NUCLEUS)
+                decide_nucleus<DT>(a, b, k, ri, it);
+            else
+                decide_full<DT>(a, b, k, ri, it);
+        }
     }
     __syncthreads();
     if (threadIdx.x <= kNumCls) {  // thread c < kNumCls: class region c; kNumCls: draws
         const int c = threadIdx.x;
         int cnt = 0;
-        for (int j = 0; j < kDecideRows; j++)
+        for (int j = 0; j < kWaves; j++)
             cnt += (c < kNumCls) ? (s_it[j].cls == c ? s_it[j].nu : 0) : s_it[j].draw;
         int base = 0;
         if (cnt > 0)
@@ -471,6 +494,7 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(StepArgs a, int 
     }
     __syncthreads();
     const DecideIntent it = s_it[w];
+    const int b = b_w;
     if (lane == 0 && it.nu > 0) {
         int li = s_base[it.cls];
         for (int j = 0; j < w; j++) li += s_it[j].cls == it.cls ? s_it[j].nu : 0;
@@ -509,9 +533,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
         a.pos[i].n_sample = 0;
     }
     if (threadIdx.x < kNumCls) s_nc[threadIdx.x] = 0;
+    if (threadIdx.x == 0) *const_cast<StepArgs*>(a.self) = a;
     {  // counters of split nucleus units (each launch leaves them at zero)
         const int rows = 2 * a.B < kGrid / 2 ? 2 * a.B : kGrid / 2;
         for (int i = threadIdx.x; i < 2 * rows; i += kPlanThreads) a.fn_sync[i] = 0;
+        for (int i = threadIdx.x; i < a.B; i += kPlanThreads) a.fn_row[i] = 0;
     }
     __syncthreads();
     for (int b = threadIdx.x; b < a.B; b += kPlanThreads) {

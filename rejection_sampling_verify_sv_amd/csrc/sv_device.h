@@ -192,6 +192,33 @@ struct FnUnit {
     int32_t rehist;   // set by the row pass: a token lies above the window
 };
 
+// Cross-workgroup hand-offs inside one launch.  The data another workgroup
+// will read is stored at device scope, which writes it through to the point
+// where the caches of all compute units agree; the writer then waits for its
+// stores to complete (dev_stores_done) before it signals with a device-scope
+// atomic, and the reader, having seen the signal, loads at device scope.  The
+// stores being written through, no cache-wide write-back (what a release
+// fence would add) is needed.
+template <class T>
+__device__ __forceinline__ void dev_store(T* p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T dev_load(T* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Every memory operation this wave issued has completed.
+__device__ __forceinline__ void dev_stores_done() { __builtin_amdgcn_s_waitcnt(0); }
+
+__device__ __forceinline__ void fn_put_status(FnUnit* f, int32_t st) { dev_store(&f->status, st); }
+__device__ __forceinline__ void fn_put_la(FnUnit* f, float la) {
+    dev_store(reinterpret_cast<int32_t*>(&f->la), __float_as_int(la));
+}
+__device__ __forceinline__ void fn_put_cut(FnUnit* f, uint64_t tau, double S) {
+    dev_store(&f->tau, tau);
+    dev_store(reinterpret_cast<uint64_t*>(&f->S), (uint64_t)__double_as_longlong(S));
+}
+
 // ---- element types and tiles ----------------------------------------------
 template <int DT>
 struct Elt;
@@ -807,6 +834,8 @@ struct StepArgs {
     uint64_t* hist;        // [2B + kGrid][kNW] nucleus histograms of the row pass, slot u + w
     uint64_t* fn_keys;     // [kGrid / 2][kCollectCap] boundary keys of a unit whose cut is split
     int32_t* fn_sync;      // [kGrid / 2][2] per split unit: workgroups arrived, keys reserved
+    int32_t* fn_row;       // [B] nucleus units of the row whose cut is complete
+    const StepArgs* self;  // a copy of these arguments in device memory (written by the plan)
 };
 
 template <int DT>

@@ -182,7 +182,7 @@ __device__ void resolve_wide(const void* row, int64_t V, FnUnit* fu, float la, f
         __syncthreads();
         const int star = s_star;
         if (star < 0) {  // cannot happen: the interval's first token qualifies
-            if (threadIdx.x == 0) fu->status = 1;
+            if (threadIdx.x == 0) fn_put_status(fu, 1);
             __syncthreads();
             return;
         }
@@ -234,8 +234,7 @@ __device__ void resolve_wide(const void* row, int64_t V, FnUnit* fu, float la, f
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        fu->tau = s_tau;
-        fu->S = A + sc * (double)(pre + s_kept);
+        fn_put_cut(fu, s_tau, A + sc * (double)(pre + s_kept));
     }
     __syncthreads();
 }
@@ -317,11 +316,12 @@ __host__ __device__ inline int fn_split(int n_units, int grid, int ntiles) {
     return s > 1 ? s : 1;
 }
 
-// The nucleus units of position k, one or (few units) several workgroups
-// each: histogram, boundary bucket, its keys, and the exact cut (see the top
-// of this file).
+// Position k after its row pass: the cut of every nucleus unit, one or (few
+// units) several workgroups each (histogram, boundary bucket, its keys and
+// the exact cut, see the top of this file), and the decision of every live
+// row (sv_decide.h).
 template <int DT, bool kAligned>
-__global__ __launch_bounds__(kThreads) void fn_cut_kernel(StepArgs a, int k) {
+__global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k) {
     using TS = TileShape<DT>;
     static_assert(TS::kE <= 32, "hit mask is 32 bits");
     constexpr int kOwn = 4;  // boundary tokens a thread ranks per pass
@@ -340,6 +340,12 @@ __global__ __launch_bounds__(kThreads) void fn_cut_kernel(StepArgs a, int k) {
     __shared__ unsigned long long s_tau, s_kept;
     __shared__ int s_star, s_nsel, s_wcnt[kWaves], s_base, s_last;
     __shared__ uint64_t s_before;
+    __shared__ DecideIntent s_it[kWaves];
+    __shared__ int s_dbase[kNumCls + 1];
+    constexpr int kPend = 32;  // completed nucleus rows awaiting their decision
+    __shared__ int s_pend[kPend], s_npend;
+    static_assert(sizeof(TopkScratch) * kWaves <= sizeof(uint64_t) * kCollectCap,
+                  "the decisions' scratch lies over s_key");
     const PosDesc P = a.pos[k];
     const int n_units = P.n_cls[CLS_NUCLEUS];
     const int32_t* list = nuc_list(a, k);
@@ -349,8 +355,9 @@ __global__ __launch_bounds__(kThreads) void fn_cut_kernel(StepArgs a, int k) {
     // one workgroup per unit.
     const int S = fn_split(n_units, (int)gridDim.x, a.ntiles);
     const int n_work = n_units * S;
-    for (int wi = blockIdx.x; wi < n_work; wi += gridDim.x) {
-        const int li = wi / S, sl = wi - li * S;
+    // one unit, or one slice of a split unit; true for the workgroup that
+    // completes the unit's cut
+    auto cut_unit = [&](int li, int sl) -> bool {
         const int u = list[li];
         const int b = u >> 1, side = u & 1;
         const RowInfo& ri = a.rows[b];
@@ -405,10 +412,10 @@ __global__ __launch_bounds__(kThreads) void fn_cut_kernel(StepArgs a, int k) {
         // 2. the boundary bucket
         select_boundary(s_h, ri.top_p, la, cb, s_tmpd, &s_star, &s_so);  // barriers
         const SelOut so = s_so;
-        if (threadIdx.x == 0) fu->status = so.beta < 0 ? 2 : 0;  // 2: no finite logit
+        if (threadIdx.x == 0) fn_put_status(fu, so.beta < 0 ? 2 : 0);  // 2: no finite logit
         if (so.beta < 0) {
             __syncthreads();
-            continue;
+            return sl == 0;
         }
         // 3. the boundary bucket's keys in this workgroup's slice of the row,
         //    appended by each wave to its own quarter of s_h (free once the
@@ -490,13 +497,8 @@ __global__ __launch_bounds__(kThreads) void fn_cut_kernel(StepArgs a, int k) {
             }
         }
         if (S > 1) {
-            // Publish the slice's keys; only the unit's last workgroup goes
-            // on.  The keys are stored and loaded at device scope (through
-            // to, and from, the point where all of the chip's caches agree),
-            // and the arrival is a release: it follows those stores.  No
-            // acquire fence is needed on the reading side, whose device-scope
-            // loads cannot be served from a stale line, and an acquire would
-            // invalidate the whole L2 under every workgroup sharing it.
+            // Publish the slice's keys (device-scope stores, see dev_store);
+            // only the unit's last workgroup goes on, and reads them all.
             int32_t* const sync = a.fn_sync + 2 * li;  // [0] arrived, [1] keys reserved
             uint64_t* const gk = a.fn_keys + (int64_t)li * kCollectCap;
             __syncthreads();
@@ -505,19 +507,19 @@ __global__ __launch_bounds__(kThreads) void fn_cut_kernel(StepArgs a, int k) {
             const int base = s_base;
             if (!over)
                 for (int i = threadIdx.x; i < n && base + i < kCollectCap; i += kThreads)
-                    __hip_atomic_store(gk + base + i, s_key[i], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+                    dev_store(gk + base + i, s_key[i]);
+            dev_stores_done();  // every wave's keys, before the arrival below
             __syncthreads();
             if (threadIdx.x == 0)
-                s_last = __hip_atomic_fetch_add(&sync[0], 1, __ATOMIC_RELEASE,
+                s_last = __hip_atomic_fetch_add(&sync[0], 1, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT) == S - 1;
             __syncthreads();
-            if (!s_last) continue;
-            n = __hip_atomic_load(&sync[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (!s_last) return false;
+            n = dev_load(&sync[1]);
             over = n > kCollectCap;
             if (!over)
                 for (int i = threadIdx.x; i < n; i += kThreads)
-                    s_key[i] = __hip_atomic_load(gk + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    s_key[i] = dev_load(gk + i);
             __syncthreads();
             if (threadIdx.x == 0) {  // ready for the next position's launch
                 sync[0] = 0;
@@ -531,15 +533,15 @@ __global__ __launch_bounds__(kThreads) void fn_cut_kernel(StepArgs a, int k) {
         const double A = so.A;
         if (n < 1 || n > kCollectCap) {
             if (n < 1) {  // cannot happen: the boundary bucket has mass
-                if (threadIdx.x == 0) fu->status = 1;
+                if (threadIdx.x == 0) fn_put_status(fu, 1);
                 __syncthreads();
-                continue;
+                return true;
             }
-            if (threadIdx.x == 0) fu->la = la;
+            if (threadIdx.x == 0) fn_put_la(fu, la);
             resolve_wide<DT, kAligned>(row, a.V, fu, la, cb, so.l_lo, so.l_hi, A, sc, target, s_h,
                                        reinterpret_cast<uint32_t*>(s_key), s_h + kBins,
                                        s_key + kBins, s_tmp);  // tau and S (barriers)
-            continue;
+            return true;
         }
         // 4. the cut inside the boundary bucket
         s_sub[threadIdx.x] = 0ull;
@@ -575,9 +577,9 @@ __global__ __launch_bounds__(kThreads) void fn_cut_kernel(StepArgs a, int k) {
         __syncthreads();
         const int star = s_star;
         if (star < 0) {  // cannot happen: the bucket's first token qualifies
-            if (threadIdx.x == 0) fu->status = 1;
+            if (threadIdx.x == 0) fn_put_status(fu, 1);
             __syncthreads();
-            continue;
+            return true;
         }
         for (int i = threadIdx.x; i < n; i += kThreads)
             if (s_sb[i] == star) s_sel[atomicAdd(&s_nsel, 1)] = (uint16_t)i;
@@ -609,12 +611,59 @@ __global__ __launch_bounds__(kThreads) void fn_cut_kernel(StepArgs a, int k) {
         }
         __syncthreads();
         if (threadIdx.x == 0) {
-            fu->tau = s_tau;
-            fu->S = A + sc * (double)(before + s_kept);
-            fu->la = la;
+            fn_put_cut(fu, s_tau, A + sc * (double)(before + s_kept));
+            fn_put_la(fu, la);
         }
         __syncthreads();
+        return true;
+    };
+
+    // Work items: the units' cuts first (the long ones), then the rows of the
+    // other classes, kDecideRows per item.  A nucleus row is decided by the
+    // workgroup that completes the last of its units (its FnUnit is written
+    // at device scope and the completion counted with a device-scope atomic,
+    // see dev_store); such rows wait in s_pend and are decided kWaves at a
+    // time when the workgroup runs out of work or the list is full, so that
+    // the decisions add one step to a workgroup's chain of units, not one
+    // per row.
+    const int n_groups = (a.B + kDecideRows - 1) / kDecideRows;
+    TopkScratch* const s_ts = reinterpret_cast<TopkScratch*>(s_key);  // free between units
+    auto decide_pending = [&]() {
+        const int np = s_npend;
+        for (int i = 0; i < np; i += kWaves) {
+            const int j = i + wave_id();
+            decide_rows<DT>(a.self, k, j < np ? s_pend[j] : -1, false, s_it, s_dbase, s_ts);
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) s_npend = 0;
+        __syncthreads();
+    };
+    if (threadIdx.x == 0) s_npend = 0;
+    __syncthreads();
+    for (int wi = blockIdx.x; wi < n_work + n_groups; wi += gridDim.x) {
+        if (wi >= n_work) {
+            const int bw = (wi - n_work) * kDecideRows + wave_id();
+            decide_rows<DT>(a.self, k, bw < a.B ? bw : -1, true, s_it, s_dbase, s_ts);
+            __syncthreads();  // LDS is reused by the next item
+            continue;
+        }
+        const int li = wi / S, sl = wi - li * S;
+        if (!cut_unit(li, sl)) continue;
+        if (threadIdx.x == 0) {
+            const int b = list[li] >> 1;
+            bool last = true;
+            if (k < a.rows[b].L) {  // a target and a draft unit: the second to finish decides
+                dev_stores_done();  // this unit's FnUnit stores, before the count
+                last = __hip_atomic_fetch_add(&a.fn_row[b], 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT) == 1;
+                if (last) a.fn_row[b] = 0;  // ready for the next position's launch
+            }
+            if (last) s_pend[s_npend++] = b;
+        }
+        __syncthreads();
+        if (s_npend == kPend) decide_pending();
     }
+    decide_pending();
 }
 
 }  // namespace sv

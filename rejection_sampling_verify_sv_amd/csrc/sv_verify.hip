@@ -7,11 +7,11 @@
 //                                 units of position 0
 //   for k = 0 .. K:
 //     rowpass_kernel<k>           stream the units live at position k
-//     fn_cut_kernel<k>            exact top_p cut of full-vocab nucleus rows
-//                                 from the histograms the row pass left,
-//                                 one or (few units) several workgroups
-//                                 per unit
-//     decide_kernel<k>            accept / reject / draw; list the units of k+1
+//     cut_decide_kernel<k>        exact top_p cut of full-vocab nucleus rows
+//                                 from the histograms the row pass left (one
+//                                 or, few units, several workgroups per
+//                                 unit); accept / reject / draw for every
+//                                 live row; list the units of k+1
 //   sample_sums_kernel            full-vocab rows: per-chunk draw masses
 //   sample_pick_kernel            full-vocab rows: the drawn token
 // Positions after a row's first rejection are never read (the first
@@ -39,7 +39,7 @@ constexpr int kMaxDraft = 1024;
 struct Plan {
     int tile, ntiles;
     size_t off_rows, off_pos, off_ulist, off_slist, off_parts, off_tstat, off_chunks,
-        off_fnu, off_hist, off_fnkeys, off_fnsync, off_status, bytes;
+        off_fnu, off_hist, off_fnkeys, off_fnsync, off_fnrow, off_self, off_status, bytes;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -72,6 +72,8 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
     const size_t split_rows = units < (size_t)kGrid / 2 ? units : (size_t)kGrid / 2;
     p->off_fnkeys = take(sizeof(uint64_t) * split_rows * kCollectCap);
     p->off_fnsync = take(sizeof(int32_t) * 2 * split_rows);
+    p->off_fnrow = take(sizeof(int32_t) * (size_t)B);
+    p->off_self = take(sizeof(StepArgs));
     p->off_status = take(sizeof(int32_t) * (size_t)B);  // sv_sample without out_status
     p->bytes = off;
     return true;
@@ -86,9 +88,9 @@ int hip_fail(hipError_t e) {
 
 // Launch order of one step; sv_launch_count / sv_launch_name describe it.
 constexpr int kPre = 1;
-constexpr int kPerPos = 3;
+constexpr int kPerPos = 2;
 const char* const kPreNames[kPre] = {"plan"};
-const char* const kPosNames[kPerPos] = {"rowpass", "fn_cut", "decide"};
+const char* const kPosNames[kPerPos] = {"rowpass", "cut_decide"};
 int launch_count(int K) { return kPre + kPerPos * (K + 1) + 2; }
 
 const char* launch_name(int K, int i) {
@@ -138,7 +140,7 @@ int grids_for_device(Grids* out) {
     if (cus < 1) cus = 1;
     Grids g;
     g.rowpass = resident_grid(rowpass_kernel<DT, kAligned>, cus);
-    g.cut = resident_grid(fn_cut_kernel<DT, kAligned>, cus);
+    g.cut = resident_grid(cut_decide_kernel<DT, kAligned>, cus);
     g.sums = resident_grid(sample_sums_kernel<DT, kAligned>, cus);
     (void)hipGetLastError();
     if (dev >= 0 && dev < kMaxDevices) {
@@ -174,10 +176,7 @@ int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepAr
         mark();
         rowpass_kernel<DT, kAligned><<<g.rowpass, kThreads, 0, st>>>(a, k);
         mark();
-        fn_cut_kernel<DT, kAligned><<<cut_grid, kThreads, 0, st>>>(a, k);
-        mark();
-        decide_kernel<DT><<<(unsigned)((B + kDecideRows - 1) / kDecideRows), kDecideThreads, 0, st>>>(a,
-                                                                                           k);
+        cut_decide_kernel<DT, kAligned><<<cut_grid, kThreads, 0, st>>>(a, k);
     }
     mark();
     sample_sums_kernel<DT, kAligned><<<g.sums, kThreads, 0, st>>>(a);
@@ -239,6 +238,8 @@ static int verify_impl(const void* target_logits, const void* draft_logits,
     a.hist = reinterpret_cast<uint64_t*>(ws + pl.off_hist);
     a.fn_keys = reinterpret_cast<uint64_t*>(ws + pl.off_fnkeys);
     a.fn_sync = reinterpret_cast<int32_t*>(ws + pl.off_fnsync);
+    a.fn_row = reinterpret_cast<int32_t*>(ws + pl.off_fnrow);
+    a.self = reinterpret_cast<const StepArgs*>(ws + pl.off_self);
     a.g_row = 0;
 
     const size_t esz = (dt == SV_F32) ? 4 : 2;
