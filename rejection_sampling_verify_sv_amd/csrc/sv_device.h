@@ -64,7 +64,7 @@ struct PosDesc {
     int32_t n_sample;        // rows to draw from at the end (final slot only)
     int32_t pad[3];
 };
-__device__ __forceinline__ int pos_units(const PosDesc& p) {
+__host__ __device__ __forceinline__ int pos_units(const PosDesc& p) {
     return p.n_cls[0] + p.n_cls[1] + p.n_cls[2] + p.n_cls[3];
 }
 // Index in the concatenated list of entry j of class c's region.
@@ -598,7 +598,7 @@ __host__ __device__ __forceinline__ int flat_owner(int64_t t, int64_t T, int G) 
 struct RecRange {
     int first, count;
 };
-__device__ __forceinline__ RecRange unit_records(int li, int n, int ntiles, int G) {
+__host__ __device__ __forceinline__ RecRange unit_records(int li, int n, int ntiles, int G) {
     const int64_t T = (int64_t)n * ntiles;
     const int w0 = flat_owner((int64_t)li * ntiles, T, G);
     const int w1 = flat_owner((int64_t)(li + 1) * ntiles - 1, T, G);

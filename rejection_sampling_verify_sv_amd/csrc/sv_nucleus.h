@@ -325,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
     using TS = TileShape<DT>;
     static_assert(TS::kE <= 32, "hit mask is 32 bits");
     constexpr int kOwn = 4;  // boundary tokens a thread ranks per pass
-    constexpr int kRing = 4;  // tiles in flight while collecting
+    constexpr int kRing = DT == SV_BF16 ? 3 : 4;  // tiles in flight while collecting a slice
     constexpr int kWaveCap = kCollectCap / kWaves;  // boundary keys a wave can hold
     static_assert(kNW <= kCollectCap && kBins <= kCollectCap && kBins + kThreads <= kCollectCap,
                   "LDS arrays are shared between the steps");
