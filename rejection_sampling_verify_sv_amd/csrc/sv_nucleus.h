@@ -619,14 +619,19 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
     };
 
     // Work items: the units' cuts first (the long ones), then the rows of the
-    // other classes, kDecideRows per item.  A nucleus row is decided by the
+    // other classes, R per item.  A nucleus row is decided by the
     // workgroup that completes the last of its units (its FnUnit is written
     // at device scope and the completion counted with a device-scope atomic,
     // see dev_store); such rows wait in s_pend and are decided kWaves at a
     // time when the workgroup runs out of work or the list is full, so that
     // the decisions add one step to a workgroup's chain of units, not one
     // per row.
-    const int n_groups = (a.B + kDecideRows - 1) / kDecideRows;
+    // rows per decision item: enough that the items fit in the workgroups the
+    // cuts leave free, so that no workgroup runs a cut and a group in turn
+    const int n_free = (int)gridDim.x - n_work;
+    int R = n_free > 0 ? (a.B + n_free - 1) / n_free : kDecideRows;
+    R = (R + kDecideRows - 1) / kDecideRows * kDecideRows;
+    const int n_groups = (a.B + R - 1) / R;
     TopkScratch* const s_ts = reinterpret_cast<TopkScratch*>(s_key);  // free between units
     auto decide_pending = [&]() {
         const int np = s_npend;
@@ -642,9 +647,12 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
     __syncthreads();
     for (int wi = blockIdx.x; wi < n_work + n_groups; wi += gridDim.x) {
         if (wi >= n_work) {
-            const int bw = (wi - n_work) * kDecideRows + wave_id();
-            decide_rows<DT>(a.self, k, bw < a.B ? bw : -1, true, s_it, s_dbase, s_ts);
-            __syncthreads();  // LDS is reused by the next item
+            const int r0 = (wi - n_work) * R;
+            for (int r = r0; r < r0 + R && r < a.B; r += kDecideRows) {
+                const int bw = r + wave_id();
+                decide_rows<DT>(a.self, k, bw < a.B ? bw : -1, true, s_it, s_dbase, s_ts);
+                __syncthreads();  // LDS is reused by the next rows
+            }
             continue;
         }
         const int li = wi / S, sl = wi - li * S;
