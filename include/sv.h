@@ -163,7 +163,7 @@ int sv_sample(const void* logits, const sv_sampler_params* sampler_params, const
 
 /* Number of kernel launches in one step for max_draft K (0 if K is outside
  * [0, 1024]), and
- * the name of launch i ("plan", "rowpass", "decide", ...; NULL if out of
+ * the name of launch i ("plan", "rowpass", "cut_decide", ...; NULL if out of
  * range).  Static strings, host only. */
 int32_t sv_launch_count(int32_t max_draft);
 const char* sv_launch_name(int32_t max_draft, int32_t i);

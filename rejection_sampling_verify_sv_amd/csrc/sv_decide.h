@@ -576,7 +576,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
         ri.mt = ri.zt = ri.md = ri.zd = 0.0;
         ri.tau_t = ri.tau_d = 0ull;
         if (cls >= 0) {
-            // position-0 units (the layout decide_kernel uses, LDS counters)
+            // position-0 units (the layout the decisions use, LDS counters)
             const bool draft = cls != CLS_GREEDY && 0 < L;
             const int nu = draft ? 2 : 1;
             const int li = atomicAdd(&s_nc[cls], nu);

@@ -8,7 +8,7 @@
 // those of the anchor window (sv_device.h).
 //
 // The row pass leaves each nucleus unit's mass histogram, one per piece.
-// Then fn_cut finishes the cut, one workgroup per unit, or several when the
+// Then cut_decide_kernel finishes the cut, one workgroup per unit, or several when the
 // units are few:
 //   hist     the unit's histogram in LDS: the sum of its pieces, or, when a
 //            piece saw a token above the window, the row again, anchored at
@@ -300,7 +300,7 @@ __device__ inline void select_boundary(const uint64_t* s_h, float top_p, float l
     __syncthreads();
 }
 
-// Workgroups per unit in fn_cut.  One workgroup alone reads a row far below
+// Workgroups per unit in the cut.  One workgroup alone reads a row far below
 // its share of HBM (its collect step is bound by instruction issue), so when
 // the units are few each gets several, up to one per compute unit in all
 // (the grid holds two per compute unit; two on one compute unit only halve

@@ -166,7 +166,7 @@ int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepAr
         n++;
     };
     const int B = a.B;
-    // fn_cut: up to kMaxSplit workgroups per nucleus unit
+    // cut_decide: up to kMaxSplit workgroups per nucleus unit
     const unsigned cut_cap = (unsigned)(2 * B * kMaxSplit < kGrid ? 2 * B * kMaxSplit : kGrid);
     const unsigned cut_grid = g.cut < cut_cap ? g.cut : cut_cap;
     const unsigned row_grid = (unsigned)(B < kGrid ? B : kGrid);
