@@ -161,6 +161,38 @@ int sv_verify_profiled(const void* target_logits, const void* draft_logits,
 int sv_sample(const void* logits, const sv_sampler_params* sampler_params, const float* uniforms,
               int32_t* out_tokens, int32_t* out_status, const sv_config* cfg);
 
+/*
+ * Acceptance statistics of one draft position, per row: how often drafts
+ * would be kept under the rejection test with matched truncation, under a
+ * check that compares two independent draws, and under the rejection test
+ * with the draft alone truncated or nothing truncated (deniz.in "Üç
+ * düzeltmeden sonra Qwen3.5 ve Qwen3.6 MTP head…", sections "Örnekleme
+ * altında doğrulama yanlıştı" and "Kesme her iki tarafta eşleşmek zorunda":
+ * the rejection test's acceptance is the overlap of the two distributions).
+ * With p, q the target and draft distributions of row b after temperature and
+ * the row's top_k / top_p (as sv_verify forms them) and p~, q~ after
+ * temperature only:
+ *   out[b][0] = sum_i min(p_i, q_i)
+ *   out[b][1] = sum_i p_i q_i
+ *   out[b][2] = sum_i min(p~_i, q_i)
+ *   out[b][3] = sum_i min(p~_i, q~_i)
+ * On a greedy row (temperature 0) all four are 1 when the two argmaxes agree
+ * and 0 otherwise; on a row with invalid parameters, an unsupported top_k or
+ * no finite logit on either side they are NaN.  Sums are fp64 over fp32
+ * exp2 terms (relative error about 1e-7).
+ *
+ *   target_logits  [B] rows of V logits (row b at b*cfg->target_row_stride)
+ *   draft_logits   [B] rows of V logits (row b at b*cfg->draft_row_stride)
+ *   sampler_params [B] sv_sampler_params
+ *   out            [B][4] fp64, device
+ *   cfg            batch, vocab, dtype, strides, stream, workspace (at least
+ *                  sv_workspace_bytes(B, 1, V, dtype) bytes); max_draft and
+ *                  diag are ignored.
+ * Same ownership, ordering, error and determinism rules as sv_verify.
+ */
+int sv_accept_stats(const void* target_logits, const void* draft_logits,
+                    const sv_sampler_params* sampler_params, double* out, const sv_config* cfg);
+
 /* Number of kernel launches in one step for max_draft K (0 if K is outside
  * [0, 1024]), and
  * the name of launch i ("plan", "rowpass", "cut_decide", ...; NULL if out of

@@ -145,3 +145,64 @@ def sample(logits, params, uniforms, *, dtype="f32", nthreads: int = 0):
                                   None, params, np.asarray(uniforms, np.float32).reshape(B, 1),
                                   dtype=dtype, nthreads=nthreads)
     return out[:, 0].copy(), acc, diag
+
+
+def _row_f64(row, dtype):
+    if dtype == "f32":
+        return np.asarray(row, dtype=np.float32).astype(np.float64)
+    bits = np.asarray(row, dtype=np.uint16).astype(np.uint32) << 16
+    return bits.view(np.float32).astype(np.float64)
+
+
+def accept_stats(target, draft, params, *, dtype="f32"):
+    """Acceptance statistics of one draft position, per row (the quantities
+    sv_accept_stats computes).
+
+    deniz.in "Üç düzeltmeden sonra Qwen3.5 ve Qwen3.6 MTP head…": the check
+    that compares two independent draws agrees with probability sum p q
+    (section "Örnekleme altında doğrulama yanlıştı"); the rejection test keeps
+    a draft token x ~ q with min(1, p(x)/q(x)), so its acceptance is
+    sum min(p, q), the overlap of the two distributions (section "Kesme her
+    iki tarafta eşleşmek zorunda"), which is why truncating only one side
+    lowers it.
+
+    target, draft: [B, V] float32 (or uint16 bf16 patterns with
+    dtype="bf16"); params: [B] PARAMS_DTYPE.  p, q are the distributions of
+    dist() with the row's parameters, p~, q~ those with temperature only.
+    Returns (stats [B, 4] float64 = sum min(p, q), sum p q, sum min(p~, q),
+    sum min(p~, q~); cut_margin [B], the smaller of the two sides' cut
+    margins from dist()).  Greedy rows (T = 0): 1 in every slot when the
+    argmaxes (lowest id among equal logits) agree, else 0.  Rows with T < 0
+    or not finite, top_p <= 0, or no finite logit on a side: NaN."""
+    target = np.asarray(target)
+    draft = np.asarray(draft)
+    B = target.shape[0]
+    params = np.ascontiguousarray(params)
+    out = np.full((B, 4), np.nan)
+    margin = np.full(B, np.inf)
+    for b in range(B):
+        T = float(params["temperature"][b])
+        k = int(params["top_k"][b])
+        tp = float(params["top_p"][b])
+        if not (T >= 0.0 and np.isfinite(T) and tp > 0.0):
+            continue
+        t = _row_f64(target[b], dtype)
+        d = _row_f64(draft[b], dtype)
+        if T == 0.0:
+            if not (np.isfinite(t).any() and np.isfinite(d).any()):
+                continue
+            out[b] = 1.0 if int(np.argmax(t)) == int(np.argmax(d)) else 0.0
+            continue
+        try:
+            p, mp = dist(t, T, k, tp)
+            q, mq = dist(d, T, k, tp)
+            pu, _ = dist(t, T, 0, 1.0)
+            qu, _ = dist(d, T, 0, 1.0)
+        except ValueError:
+            continue
+        out[b, 0] = np.minimum(p, q).sum()
+        out[b, 1] = (p * q).sum()
+        out[b, 2] = np.minimum(pu, q).sum()
+        out[b, 3] = np.minimum(pu, qu).sum()
+        margin[b] = min(mp, mq)
+    return out, margin

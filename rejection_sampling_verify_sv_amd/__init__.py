@@ -2,11 +2,12 @@
 
 ``verify`` enqueues the HIP kernels of libsv.so (C ABI in include/sv.h) on the
 current torch stream; ``sample`` draws one token per row with the same
-truncation (the draft side's sampling step, or plain decoding).  ``workloads``
-builds the seeded synthetic inputs.
+truncation (the draft side's sampling step, or plain decoding);
+``accept_stats`` gives per-row acceptance statistics of one draft position.
+``workloads`` builds the seeded synthetic inputs.
 """
-from ._lib import (SV_BF16, SV_F32, SV_MAX_TOP_K, load, params_tensor, sample, verify,
-                   workspace_bytes)
+from ._lib import (SV_BF16, SV_F32, SV_MAX_TOP_K, accept_stats, load, params_tensor, sample,
+                   verify, workspace_bytes)
 
-__all__ = ["verify", "sample", "params_tensor", "workspace_bytes", "load", "SV_F32", "SV_BF16",
-           "SV_MAX_TOP_K"]
+__all__ = ["verify", "sample", "accept_stats", "params_tensor", "workspace_bytes", "load",
+           "SV_F32", "SV_BF16", "SV_MAX_TOP_K"]

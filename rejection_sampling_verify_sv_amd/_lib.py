@@ -19,8 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libsv.so")
 SV_F32, SV_BF16 = 0, 1
 SV_MAX_TOP_K = 64
 ERRORS = {0: "SV_OK", -1: "SV_EINVAL", -2: "SV_EWORKSPACE", -3: "SV_EHIP"}
-EXPORTED = ("sv_verify", "sv_verify_profiled", "sv_sample", "sv_workspace_bytes",
-            "sv_strerror", "sv_launch_count", "sv_launch_name")
+EXPORTED = ("sv_verify", "sv_verify_profiled", "sv_sample", "sv_accept_stats",
+            "sv_workspace_bytes", "sv_strerror", "sv_launch_count", "sv_launch_name")
 
 
 class SvConfig(ctypes.Structure):
@@ -58,6 +58,8 @@ def load() -> ctypes.CDLL:
                                            + [ctypes.c_void_p, ctypes.c_int32])
         lib.sv_sample.restype = ctypes.c_int
         lib.sv_sample.argtypes = [ctypes.c_void_p] * 5 + [ctypes.POINTER(SvConfig)]
+        lib.sv_accept_stats.restype = ctypes.c_int
+        lib.sv_accept_stats.argtypes = [ctypes.c_void_p] * 4 + [ctypes.POINTER(SvConfig)]
         lib.sv_strerror.restype = ctypes.c_char_p
         lib.sv_strerror.argtypes = [ctypes.c_int]
         lib.sv_launch_count.restype = ctypes.c_int32
@@ -250,3 +252,61 @@ def sample(logits: torch.Tensor, params, uniforms: torch.Tensor, *, diag: bool =
             if t is not None:
                 t.record_stream(st)
     return out_tokens, out_status, dg
+
+
+def accept_stats(target: torch.Tensor, draft: torch.Tensor, params, *,
+                 workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                 stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Enqueue the acceptance statistics of one draft position (sv_accept_stats):
+    target and draft logits [B, V] (float32 or bfloat16 CUDA tensors of one
+    dtype; rows may be strided), params as in params_tensor().  Returns out
+    [B, 4] float64: sum min(p, q), sum p q, sum min(p~, q), sum min(p~, q~).
+    Nothing is synchronised."""
+    lib = load()
+    if not (target.is_cuda and draft.is_cuda):
+        raise RuntimeError("accept_stats needs GPU tensors (no CPU path exists)")
+    dev = target.device
+    if target.dtype != draft.dtype:
+        raise TypeError("target and draft must share a dtype")
+    if target.dtype == torch.float32:
+        code = SV_F32
+    elif target.dtype == torch.bfloat16:
+        code = SV_BF16
+    else:
+        raise TypeError("logits must be float32 or bfloat16")
+    if target.dim() != 2 or draft.dim() != 2 or target.shape != draft.shape:
+        raise ValueError("target and draft must both be [B, V]")
+    B, V = target.shape
+    if target.stride(1) != 1:
+        target = target.contiguous()
+    if draft.stride(1) != 1:
+        draft = draft.contiguous()
+    prm = params_tensor(params, dev)
+    if prm.shape[0] != B:
+        raise ValueError("params must have B rows")
+    if out is None:
+        out = torch.empty((B, 4), dtype=torch.float64, device=dev)
+    need = workspace_bytes(B, 1, V, code)
+    if need == 0:
+        raise ValueError("invalid shape for sv_accept_stats")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    wptr = workspace.data_ptr()
+    pad = (-wptr) % 256
+    cfg = SvConfig()
+    cfg.batch, cfg.max_draft, cfg.vocab, cfg.dtype = B, 1, V, code
+    cfg.target_row_stride, cfg.draft_row_stride = target.stride(0), draft.stride(0)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    cfg.stream = st.cuda_stream
+    cfg.workspace = wptr + pad
+    cfg.workspace_bytes = workspace.numel() * workspace.element_size() - pad
+    cfg.diag = None
+    rc = lib.sv_accept_stats(target.data_ptr(), draft.data_ptr(), prm.data_ptr(), out.data_ptr(),
+                             ctypes.byref(cfg))
+    if rc != 0:
+        raise RuntimeError(f"sv_accept_stats failed: {ERRORS.get(rc, rc)}: "
+                           f"{lib.sv_strerror(rc).decode()}")
+    if stream is not None:
+        for t in (target, draft, prm, workspace, out):
+            t.record_stream(st)
+    return out

@@ -546,7 +546,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
         const float T = prm.temperature, tp = prm.top_p;
         const int tk = prm.top_k;
         bool bad = !(T >= 0.f) || !(T < INFINITY) || !(tp > 0.f) || L < 0 || L > a.K;
-        if (!bad) {
+        if (!bad && !a.stats) {  // the statistics read no draft tokens
             for (int j = 0; j < L; j++) {
                 const int t = a.tokens[(int64_t)b * a.K + j];
                 if (t < 0 || t >= a.V) bad = true;
@@ -577,7 +577,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
         ri.tau_t = ri.tau_d = 0ull;
         if (cls >= 0) {
             // position-0 units (the layout the decisions use, LDS counters)
-            const bool draft = cls != CLS_GREEDY && 0 < L;
+            const bool draft = (cls != CLS_GREEDY || a.stats) && 0 < L;
             const int nu = draft ? 2 : 1;
             const int li = atomicAdd(&s_nc[cls], nu);
             int32_t* ul = a.ulist + (int64_t)cls * 2 * a.B;
@@ -593,6 +593,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
             }
         }
         a.rows[b] = ri;
+        if (a.stats) continue;  // no verify outputs
         int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
         for (int j = 0; j <= a.K; j++) o[j] = -1;
         a.out_acc[b] = (cls == CLS_ERROR) ? -1 : (cls == CLS_UNSUP ? -2 : 0);

@@ -812,11 +812,24 @@ __device__ __forceinline__ int pow2_ceil(int n) {
 }
 
 // ---- arguments shared by the step kernels ---------------------------------
+// Per-row description of the four distributions of the acceptance
+// statistics (sv_stats.h): with e = exp((l - m) / T) on each side, the
+// untruncated probability is e * iz and the truncated one [key >= tau] e * kap.
+struct StatDesc {
+    uint64_t tau_t, tau_d;
+    double kap_t, kap_d, iz_t, iz_d;
+    float m_t, m_d, c;
+    int32_t pad;
+};
+
 struct StepArgs {
     const void* target;
     const void* draft;
     int64_t t_stride, d_stride;
     int B, K, V, ntiles;
+    int t_rows, d_rows;    // rows per batch entry in each tensor (K + 1 and K for a verify step)
+    int stats;             // 1: acceptance statistics instead of a verify step (sv_stats.h)
+    int force_full;        // row pass: every unit as an untruncated one
     int g_row;             // grid of the row pass (its records are laid out by it)
     const int32_t* tokens;
     const float* uniforms;
@@ -836,14 +849,18 @@ struct StepArgs {
     int32_t* fn_sync;      // [kGrid / 2][2] per split unit: workgroups arrived, keys reserved
     int32_t* fn_row;       // [B] nucleus units of the row whose cut is complete
     const StepArgs* self;  // a copy of these arguments in device memory (written by the plan)
+    StatDesc* sdesc;       // [B] acceptance statistics: the rows' distributions
+    double* srec;          // [B][ntiles][kWaves][4] acceptance statistics: partial sums
+    double* sout;          // [B][4] acceptance statistics: the result
 };
 
 template <int DT>
 __device__ __forceinline__ const void* unit_row(const StepArgs& a, int b, int side, int k) {
     if (side == 0)
         return static_cast<const char*>(a.target) +
-               ((int64_t)b * (a.K + 1) + k) * a.t_stride * Elt<DT>::kSize;
-    return static_cast<const char*>(a.draft) + ((int64_t)b * a.K + k) * a.d_stride * Elt<DT>::kSize;
+               ((int64_t)b * a.t_rows + k) * a.t_stride * Elt<DT>::kSize;
+    return static_cast<const char*>(a.draft) +
+           ((int64_t)b * a.d_rows + k) * a.d_stride * Elt<DT>::kSize;
 }
 
 // The nucleus units of position k (their class region) and their number.

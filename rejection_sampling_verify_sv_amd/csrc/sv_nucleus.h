@@ -631,7 +631,7 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
     const int n_free = (int)gridDim.x - n_work;
     int R = n_free > 0 ? (a.B + n_free - 1) / n_free : kDecideRows;
     R = (R + kDecideRows - 1) / kDecideRows * kDecideRows;
-    const int n_groups = (a.B + R - 1) / R;
+    const int n_groups = a.stats ? 0 : (a.B + R - 1) / R;  // the statistics decide nothing
     TopkScratch* const s_ts = reinterpret_cast<TopkScratch*>(s_key);  // free between units
     auto decide_pending = [&]() {
         const int np = s_npend;
@@ -656,7 +656,7 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
             continue;
         }
         const int li = wi / S, sl = wi - li * S;
-        if (!cut_unit(li, sl)) continue;
+        if (!cut_unit(li, sl) || a.stats) continue;
         if (threadIdx.x == 0) {
             const int b = list[li] >> 1;
             bool last = true;

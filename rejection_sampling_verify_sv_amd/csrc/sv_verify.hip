@@ -29,6 +29,7 @@
 #include "sv_nucleus.h"
 #include "sv_rowpass.h"
 #include "sv_sample.h"
+#include "sv_stats.h"
 
 namespace {
 
@@ -39,7 +40,7 @@ constexpr int kMaxDraft = 1024;
 struct Plan {
     int tile, ntiles;
     size_t off_rows, off_pos, off_ulist, off_slist, off_parts, off_tstat, off_chunks,
-        off_fnu, off_hist, off_fnkeys, off_fnsync, off_fnrow, off_self, off_status, bytes;
+        off_fnu, off_hist, off_fnkeys, off_fnsync, off_fnrow, off_self, off_sdesc, off_srec, off_status, bytes;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -74,6 +75,8 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
     p->off_fnsync = take(sizeof(int32_t) * 2 * split_rows);
     p->off_fnrow = take(sizeof(int32_t) * (size_t)B);
     p->off_self = take(sizeof(StepArgs));
+    p->off_sdesc = take(sizeof(StatDesc) * (size_t)B);  // sv_accept_stats
+    p->off_srec = take(sizeof(double) * 4 * (size_t)B * p->ntiles * kWaves);
     p->off_status = take(sizeof(int32_t) * (size_t)B);  // sv_sample without out_status
     p->bytes = off;
     return true;
@@ -106,7 +109,7 @@ const char* launch_name(int K, int i) {
 // slots reserved per position).  A second, partial wave would double the
 // time of the workgroups in it.
 struct Grids {
-    unsigned rowpass, cut, sums;
+    unsigned rowpass, cut, sums, stats;
 };
 
 template <class Kern>
@@ -142,6 +145,7 @@ int grids_for_device(Grids* out) {
     g.rowpass = resident_grid(rowpass_kernel<DT, kAligned>, cus);
     g.cut = resident_grid(cut_decide_kernel<DT, kAligned>, cus);
     g.sums = resident_grid(sample_sums_kernel<DT, kAligned>, cus);
+    g.stats = resident_grid(stats_stream_kernel<DT, kAligned>, cus);
     (void)hipGetLastError();
     if (dev >= 0 && dev < kMaxDevices) {
         cache[dev] = g;
@@ -187,6 +191,32 @@ int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepAr
     return e == hipSuccess ? SV_OK : hip_fail(e);
 }
 
+// Acceptance statistics of one position (sv_stats.h): the row pass, the
+// nucleus cut (no decisions), the row pass again with every unit
+// untruncated, then the statistics.
+template <int DT, bool kAligned>
+int launch_stats(const sv_sampler_params* params, StepArgs a, hipStream_t st) {
+    Grids g;
+    const int rc = grids_for_device<DT, kAligned>(&g);
+    if (rc != SV_OK) return rc;
+    a.g_row = (int)g.rowpass;
+    const int B = a.B;
+    const unsigned cut_cap = (unsigned)(2 * B * kMaxSplit < kGrid ? 2 * B * kMaxSplit : kGrid);
+    const unsigned cut_grid = g.cut < cut_cap ? g.cut : cut_cap;
+    const unsigned row_groups = (unsigned)((B + kWaves - 1) / kWaves);
+    plan_kernel<<<1, kPlanThreads, 0, st>>>(a, nullptr, params);
+    rowpass_kernel<DT, kAligned><<<g.rowpass, kThreads, 0, st>>>(a, 0);
+    cut_decide_kernel<DT, kAligned><<<cut_grid, kThreads, 0, st>>>(a, 0);
+    StepArgs full = a;
+    full.force_full = 1;
+    rowpass_kernel<DT, kAligned><<<g.rowpass, kThreads, 0, st>>>(full, 0);
+    stats_prep_kernel<DT><<<row_groups, kThreads, 0, st>>>(a);
+    stats_stream_kernel<DT, kAligned><<<g.stats, kThreads, 0, st>>>(a);
+    stats_reduce_kernel<<<row_groups, kThreads, 0, st>>>(a);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SV_OK : hip_fail(e);
+}
+
 }  // namespace
 
 extern "C" size_t sv_workspace_bytes(int32_t batch, int32_t max_draft, int32_t vocab,
@@ -222,6 +252,10 @@ static int verify_impl(const void* target_logits, const void* draft_logits,
     a.K = K;
     a.V = V;
     a.ntiles = pl.ntiles;
+    a.t_rows = K + 1;
+    a.d_rows = K;
+    a.stats = 0;
+    a.force_full = 0;
     a.tokens = draft_tokens;
     a.uniforms = uniforms;
     a.rows = reinterpret_cast<RowInfo*>(ws + pl.off_rows);
@@ -240,6 +274,9 @@ static int verify_impl(const void* target_logits, const void* draft_logits,
     a.fn_sync = reinterpret_cast<int32_t*>(ws + pl.off_fnsync);
     a.fn_row = reinterpret_cast<int32_t*>(ws + pl.off_fnrow);
     a.self = reinterpret_cast<const StepArgs*>(ws + pl.off_self);
+    a.sdesc = reinterpret_cast<StatDesc*>(ws + pl.off_sdesc);
+    a.srec = reinterpret_cast<double*>(ws + pl.off_srec);
+    a.sout = nullptr;
     a.g_row = 0;
 
     const size_t esz = (dt == SV_F32) ? 4 : 2;
@@ -295,6 +332,66 @@ extern "C" int sv_sample(const void* logits, const sv_sampler_params* sampler_pa
     }
     return verify_impl(logits, nullptr, nullptr, nullptr, sampler_params, uniforms, out_tokens,
                        out_status, &c, nullptr);
+}
+
+extern "C" int sv_accept_stats(const void* target_logits, const void* draft_logits,
+                               const sv_sampler_params* sampler_params, double* out,
+                               const sv_config* cfg) {
+    if (!cfg || !target_logits || !draft_logits || !sampler_params || !out) return SV_EINVAL;
+    const int32_t B = cfg->batch, V = cfg->vocab, dt = cfg->dtype;
+    Plan pl;
+    if (!make_plan(B, 1, V, dt, &pl)) return SV_EINVAL;
+    const int64_t ts = cfg->target_row_stride ? cfg->target_row_stride : V;
+    const int64_t ds = cfg->draft_row_stride ? cfg->draft_row_stride : V;
+    if (ts < V || ds < V) return SV_EINVAL;
+    if (!cfg->workspace || cfg->workspace_bytes < pl.bytes) return SV_EWORKSPACE;
+    if (reinterpret_cast<uintptr_t>(cfg->workspace) % 256 != 0) return SV_EWORKSPACE;
+    char* ws = static_cast<char*>(cfg->workspace);
+    StepArgs a;
+    a.target = target_logits;
+    a.draft = draft_logits;
+    a.t_stride = ts;
+    a.d_stride = ds;
+    a.B = B;
+    a.K = 1;  // one draft position: target and draft row b are rows b of their tensors
+    a.V = V;
+    a.ntiles = pl.ntiles;
+    a.t_rows = 1;
+    a.d_rows = 1;
+    a.stats = 1;
+    a.force_full = 0;
+    a.tokens = nullptr;
+    a.uniforms = nullptr;
+    a.rows = reinterpret_cast<RowInfo*>(ws + pl.off_rows);
+    a.parts = reinterpret_cast<PartSlot*>(ws + pl.off_parts);
+    a.chunks = reinterpret_cast<double2*>(ws + pl.off_chunks);
+    a.out_tokens = nullptr;
+    a.out_acc = nullptr;
+    a.diag = nullptr;
+    a.pos = reinterpret_cast<PosDesc*>(ws + pl.off_pos);
+    a.ulist = reinterpret_cast<int32_t*>(ws + pl.off_ulist);
+    a.slist = reinterpret_cast<int32_t*>(ws + pl.off_slist);
+    a.fn_unit = reinterpret_cast<FnUnit*>(ws + pl.off_fnu);
+    a.tstat = reinterpret_cast<FullStat*>(ws + pl.off_tstat);
+    a.hist = reinterpret_cast<uint64_t*>(ws + pl.off_hist);
+    a.fn_keys = reinterpret_cast<uint64_t*>(ws + pl.off_fnkeys);
+    a.fn_sync = reinterpret_cast<int32_t*>(ws + pl.off_fnsync);
+    a.fn_row = reinterpret_cast<int32_t*>(ws + pl.off_fnrow);
+    a.self = reinterpret_cast<const StepArgs*>(ws + pl.off_self);
+    a.sdesc = reinterpret_cast<StatDesc*>(ws + pl.off_sdesc);
+    a.srec = reinterpret_cast<double*>(ws + pl.off_srec);
+    a.sout = out;
+    a.g_row = 0;
+    const size_t esz = (dt == SV_F32) ? 4 : 2;
+    const bool aligned = reinterpret_cast<uintptr_t>(target_logits) % 16 == 0 &&
+                         reinterpret_cast<uintptr_t>(draft_logits) % 16 == 0 &&
+                         ((size_t)ts * esz) % 16 == 0 && ((size_t)ds * esz) % 16 == 0;
+    hipStream_t st = static_cast<hipStream_t>(cfg->stream);
+    if (dt == SV_F32)
+        return aligned ? launch_stats<SV_F32, true>(sampler_params, a, st)
+                       : launch_stats<SV_F32, false>(sampler_params, a, st);
+    return aligned ? launch_stats<SV_BF16, true>(sampler_params, a, st)
+                   : launch_stats<SV_BF16, false>(sampler_params, a, st);
 }
 
 extern "C" int32_t sv_launch_count(int32_t max_draft) {

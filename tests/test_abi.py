@@ -90,3 +90,26 @@ def test_sample_and_k0_reject_bad_arguments_on_host(lib):
     per_position = lib.sv_launch_count(2) - lib.sv_launch_count(1)
     assert per_position > 0 and lib.sv_launch_count(0) == lib.sv_launch_count(1) - per_position
     assert lib.sv_launch_count(-1) == 0 and lib.sv_launch_count(1025) == 0
+
+
+def test_accept_stats_rejects_bad_arguments_on_host(lib):
+    from rejection_sampling_verify_sv_amd import _lib
+    cfg = _lib.SvConfig()
+    cfg.batch, cfg.max_draft, cfg.vocab, cfg.dtype = 3, 0, 100, 0
+    dummy = ctypes.c_void_p(0x1000)
+    args = [dummy] * 4
+    assert lib.sv_accept_stats(*args, None) == -1             # no config
+    for i in range(4):                                        # every pointer is required
+        bad = list(args)
+        bad[i] = None
+        assert lib.sv_accept_stats(*bad, ctypes.byref(cfg)) == -1
+    assert lib.sv_accept_stats(*args, ctypes.byref(cfg)) == -2  # no workspace
+    cfg.workspace = 0x100000
+    cfg.workspace_bytes = lib.sv_workspace_bytes(3, 1, 100, 0)
+    cfg.target_row_stride = 50                                # shorter than a row
+    assert lib.sv_accept_stats(*args, ctypes.byref(cfg)) == -1
+    cfg.target_row_stride = 0
+    cfg.workspace_bytes -= 1
+    assert lib.sv_accept_stats(*args, ctypes.byref(cfg)) == -2
+    cfg.dtype = 7
+    assert lib.sv_accept_stats(*args, ctypes.byref(cfg)) == -1
