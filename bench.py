@@ -11,6 +11,11 @@ top_p), inputs already resident in HBM.  Prints one JSON line:
   cpu_baseline  the fp64 oracle on the host cores over one full batch
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+With --op accept_stats it measures sv_accept_stats instead (the acceptance
+statistics of position 0 of the same workload) and adds the study: the mean
+of each statistic per sampler class and the expected tokens per step for
+K = 1..4 that each implies.
 """
 from __future__ import annotations
 
@@ -123,6 +128,99 @@ def cpu_baseline(wl):
                       f"{dt:.2f} s, OpenMP over rows"}, out
 
 
+STAT_NAMES = ["sum_min_p_q", "sum_p_q", "sum_min_p~_q", "sum_min_p~_q~"]
+
+
+def expected_tokens(alpha, K):
+    """Tokens per verify step (accepted drafts + the one drawn token) when
+    every draft is accepted with probability alpha independently: the sum of
+    alpha^j for j = 0..K."""
+    alpha = np.asarray(alpha, np.float64)
+    return np.sum([alpha ** j for j in range(K + 1)], axis=0)
+
+
+def bench_accept_stats(args, wl, dev):
+    import torch
+
+    import rejection_sampling_verify_sv_amd as sv
+    from rejection_sampling_verify_sv_amd import workloads
+
+    B, V = wl.B, wl.V
+    t, d, _, _, prm, _ = workloads.to_torch(wl, dev)
+    t0, d0 = t[:, 0, :], d[:, 0, :]
+    code = sv.SV_F32 if wl.dtype == "f32" else sv.SV_BF16
+    ws = torch.empty(sv.workspace_bytes(B, 1, V, code) + 256, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, 4), dtype=torch.float64, device=dev)
+    for _ in range(args.warmup):
+        sv.accept_stats(t0, d0, prm, workspace=ws, out=out)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        sv.accept_stats(t0, d0, prm, workspace=ws, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    st = out.cpu().numpy()
+    # two reads of both rows are what the method needs: the normalisers and
+    # cuts, then the sums
+    alg_bytes = 2 * 2 * B * V * wl.elem_size
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    P = wl.params
+    cls = np.where(P["temperature"] == 0, "greedy",
+                   np.where(P["top_k"] > 0, "top_k", np.where(P["top_p"] < 1, "nucleus", "full")))
+    study = {}
+    for c in ["greedy", "top_k", "full", "nucleus", "all"]:
+        m = (cls == c) if c != "all" else np.ones(B, bool)
+        m &= np.isfinite(st).all(axis=1)
+        if not m.any():
+            continue
+        study[c] = {"rows": int(m.sum()),
+                    "mean": {n: round(float(st[m, j].mean()), 4) for j, n in enumerate(STAT_NAMES)},
+                    "tokens_per_step": {f"K={K}": {n: round(float(expected_tokens(st[m, j], K).mean()), 3)
+                                                   for j, n in enumerate(STAT_NAMES)}
+                                        for K in range(1, 5)}}
+    line = {
+        "metric": "acceptance-statistics rows/s, V=%d" % V,
+        "value": round(B / (ms * 1e-3), 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wl.dtype == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload + " position 0", "vocab": V, "batch": B,
+                   "logits": wl.dtype},
+        "roofline": {"bound": "hbm", "kernel": "whole call (7 launches)",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "alg_bytes_per_call": int(alg_bytes)},
+        "study": study,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        oracle.build(force=False)
+        rows = np.arange(0, B, 16)
+        tc = time.perf_counter()
+        ref, _ = oracle.accept_stats(wl.target[rows, 0], wl.draft[rows, 0], P[rows],
+                                     dtype=wl.dtype)
+        dt = time.perf_counter() - tc
+        line["cpu_baseline"] = {"value": len(rows) / dt, "unit": "rows/s", "cores": 1,
+                                "kind": "oracle",
+                                "sample": f"{len(rows)} rows (every 16th), one thread, {dt:.2f} s"}
+        ok = np.isfinite(ref).all(axis=1)
+        line["oracle_max_abs_diff"] = float(np.abs(ref[ok] - st[rows][ok]).max())
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +228,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixed_samplers_b1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", default="verify", choices=["verify", "accept_stats"])
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the measurement, run 5 device-to-device copies of MIB MiB "
                          "(the reference kernel for scaling HBM counters)")
@@ -149,6 +248,9 @@ def main():
     lib = sv.load()
     log(f"[bench] generating {args.workload}")
     wl = workloads.make(args.workload)
+    if args.op == "accept_stats":
+        bench_accept_stats(args, wl, dev)
+        return
     esz = wl.elem_size
     t, d, tok, dl, prm, uni = workloads.to_torch(wl, dev)
     B, K, V = wl.B, wl.K, wl.V
