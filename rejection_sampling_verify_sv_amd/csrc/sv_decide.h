@@ -182,8 +182,8 @@ __device__ inline void continue_row(const StepArgs& a, int b, int k, const RowIn
 // Row b ends at position k with a draw over the full vocabulary (one lane).
 __device__ inline void queue_draw(DecideIntent& it) { it.draw = 1; }
 
-__device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, int n,
-                            TopkScratch& ts, DecideIntent& it) {
+__device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, TopkScratch& ts,
+                            DecideIntent& it) {
     double* s_w = ts.w;
     double* s_p = ts.p;
     int* s_id = ts.id;
@@ -195,13 +195,13 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
     const float* u = a.uniforms + (int64_t)b * (a.K + 1);
     // every load first, so that their latencies overlap
     const uint64_t kt =
-        unit_top(a.parts, unit_records(unit_index(P, CLS_TOPK, ri.li_t), n, a.ntiles, a.g_row));
+        unit_top(a.parts, unit_records(P, unit_index(P, CLS_TOPK, ri.li_t), a.ntiles, a.g_row));
     uint64_t kd = 0ull;
     int x = 0;
     double uk = 0.0;
     if (has_draft) {
         kd = unit_top(a.parts,
-                      unit_records(unit_index(P, CLS_TOPK, ri.li_d), n, a.ntiles, a.g_row));
+                      unit_records(P, unit_index(P, CLS_TOPK, ri.li_d), a.ntiles, a.g_row));
         x = a.tokens[(int64_t)b * a.K + k];
         uk = (double)u[k];
     }
@@ -290,11 +290,11 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
     }
 }
 
-__device__ void decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri, int n,
+__device__ void decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri,
                               DecideIntent& it) {
     const int lane = lane_id();
     const RecRange r =
-        unit_records(unit_index(a.pos[k], CLS_GREEDY, ri.li_t), n, a.ntiles, a.g_row);
+        unit_records(a.pos[k], unit_index(a.pos[k], CLS_GREEDY, ri.li_t), a.ntiles, a.g_row);
     const PartSlot* s = a.parts + r.first;
     uint64_t best = 0ull;
     for (int i = lane; i < r.count; i += kWave) best = s[i].keys[0] > best ? s[i].keys[0] : best;
@@ -469,12 +469,11 @@ __device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, int k,
         const int b = b_w;
         const RowInfo ri = a.rows[b];
         if (ri.status == ST_LIVE && k <= ri.L && !(skip_nucleus && ri.cls == CLS_NUCLEUS)) {
-            const int n = pos_units(a.pos[k]);
             DecideIntent& it = s_it[w];
             if (ri.cls == CLS_GREEDY)
-                decide_greedy(a, b, k, ri, n, it);
+                decide_greedy(a, b, k, ri, it);
             else if (ri.cls == CLS_TOPK)
-                decide_topk(a, b, k, ri, n, s_ts[w], it);
+                decide_topk(a, b, k, ri, s_ts[w], it);
             else if (ri.cls == CLS_NUCLEUS)
                 decide_nucleus<DT>(a, b, k, ri, it);
             else

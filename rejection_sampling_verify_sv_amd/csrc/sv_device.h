@@ -594,14 +594,31 @@ __host__ __device__ __forceinline__ int flat_owner(int64_t t, int64_t T, int G) 
     return (int)(((t + 1) * (int64_t)Ga - 1) / T);
 }
 
-// Record slots [first, first + count) of unit li of a list of n units.
+// The row pass gives every workgroup taking part at least kRowMinTiles tiles
+// (when the position has that many) unless all its units are untruncated:
+// with few units, a unit split over one workgroup per tile leaves dozens of
+// records that the decision merges one after another (a top-k list, a best
+// key or a histogram per piece), and every piece pays its own start (the
+// first tiles of a top-k piece are the costly ones).  Untruncated units keep
+// per-tile records whatever the split, so they keep one tile per workgroup.
+constexpr int kRowMinTiles = 4;
+__host__ __device__ __forceinline__ int row_grid(const PosDesc& P, int64_t T, int G) {
+    if (P.n_cls[CLS_FULL] == pos_units(P)) return flat_active(T, G);
+    const int64_t g = (T + kRowMinTiles - 1) / kRowMinTiles;
+    return (int)(g < (int64_t)G ? (g > 0 ? g : 1) : (int64_t)G);
+}
+
+// Record slots [first, first + count) of unit li (index in position P's
+// list), from the row pass of G workgroups.
 struct RecRange {
     int first, count;
 };
-__host__ __device__ __forceinline__ RecRange unit_records(int li, int n, int ntiles, int G) {
-    const int64_t T = (int64_t)n * ntiles;
-    const int w0 = flat_owner((int64_t)li * ntiles, T, G);
-    const int w1 = flat_owner((int64_t)(li + 1) * ntiles - 1, T, G);
+__host__ __device__ __forceinline__ RecRange unit_records(const PosDesc& P, int li, int ntiles,
+                                                           int G) {
+    const int64_t T = (int64_t)pos_units(P) * ntiles;
+    const int Gr = row_grid(P, T, G);
+    const int w0 = flat_owner((int64_t)li * ntiles, T, Gr);
+    const int w1 = flat_owner((int64_t)(li + 1) * ntiles - 1, T, Gr);
     RecRange r;
     r.first = li + w0;
     r.count = w1 - w0 + 1;

@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
         const void* row = unit_row<DT>(a, b, side, k);
         const float cb = bucket_coef(ri.T);
         const RecRange rr =
-            unit_records(unit_index(P, CLS_NUCLEUS, li), pos_units(P), a.ntiles, a.g_row);
+            unit_records(P, unit_index(P, CLS_NUCLEUS, li), a.ntiles, a.g_row);
         const bool re = fu->rehist != 0;
         // 1. the unit's histogram in LDS
         float la;

@@ -352,8 +352,9 @@ __global__ __launch_bounds__(kThreads) void rowpass_kernel(StepArgs a, int k) {
     const int n = pos_units(P);
     const int64_t T = (int64_t)n * a.ntiles;
     const int w = blockIdx.x;
-    int64_t t = flat_begin(T, gridDim.x, w);
-    const int64_t t_end = flat_begin(T, gridDim.x, w + 1);
+    const int Gr = row_grid(P, T, (int)gridDim.x);  // the workgroups taking part
+    int64_t t = flat_begin(T, Gr, w);
+    const int64_t t_end = flat_begin(T, Gr, w + 1);
     while (t < t_end) {
         const int li = (int)(t / a.ntiles);
         const int64_t tu0 = t - (int64_t)li * a.ntiles;

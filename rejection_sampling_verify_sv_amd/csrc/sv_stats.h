@@ -52,12 +52,11 @@ __global__ __launch_bounds__(kThreads) void stats_prep_kernel(StepArgs a) {
         return;
     }
     const PosDesc P = a.pos[0];
-    const int n = pos_units(P);
     if (ri.cls == CLS_GREEDY) {
         uint64_t best[2];
         for (int s = 0; s < 2; s++) {
-            const RecRange r = unit_records(unit_index(P, CLS_GREEDY, s == 0 ? ri.li_t : ri.li_d),
-                                            n, a.ntiles, a.g_row);
+            const RecRange r = unit_records(
+                P, unit_index(P, CLS_GREEDY, s == 0 ? ri.li_t : ri.li_d), a.ntiles, a.g_row);
             uint64_t m = 0ull;
             for (int i = lane; i < r.count; i += kWave) {
                 const uint64_t k = a.parts[r.first + i].keys[0];
@@ -93,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void stats_prep_kernel(StepArgs a) {
         // its last one, the scale exp((m - l0) / T) over the kept mass
         for (int s = 0; s < 2; s++) {
             const uint64_t key = unit_top(
-                a.parts, unit_records(unit_index(P, CLS_TOPK, s == 0 ? ri.li_t : ri.li_d), n,
+                a.parts, unit_records(P, unit_index(P, CLS_TOPK, s == 0 ? ri.li_t : ri.li_d),
                                       a.ntiles, a.g_row));
             double pr;
             bool keep;

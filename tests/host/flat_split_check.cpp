@@ -1,10 +1,12 @@
 // Host-side check of the row pass's split of a position's tiles over its
-// workgroups (flat_begin / flat_owner / unit_records in sv_device.h): for
-// many unit counts, tile counts and grids, every workgroup taking part owns a
-// contiguous, non-empty range, the ranges tile the concatenation in order,
-// the owner of every tile is the workgroup whose range holds it, every unit's
-// records are exactly the pieces that cover it, and the record slots u + w
-// are unique and below n + G.
+// workgroups (row_grid / flat_begin / flat_owner / unit_records in
+// sv_device.h): for many class mixes, tile counts and grids, the number of
+// workgroups taking part (at least kRowMinTiles tiles each unless every unit
+// is untruncated), every one of them owning a contiguous, non-empty range,
+// the ranges tiling the concatenation in order, the owner of every tile
+// being the workgroup whose range holds it, every unit's records being
+// exactly the pieces that cover it, and the record slots u + w unique and
+// below n + G.
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -20,8 +22,13 @@ static unsigned next_u32() {
     return (unsigned)(rng_state >> 33);
 }
 
-static int check(int n, int ntiles, int G) {
+static int check(const PosDesc& P, int ntiles, int G0) {
+    const int n = pos_units(P);
     const int64_t T = (int64_t)n * ntiles;
+    const int G = row_grid(P, T, G0);  // the workgroups the row pass lets take part
+    const bool all_full = P.n_cls[CLS_FULL] == n;
+    const int64_t want = all_full ? T : (T + kRowMinTiles - 1) / kRowMinTiles;
+    if (G != (want < G0 ? want : G0)) return 1;
     const int Ga = flat_active(T, G);
     if (flat_begin(T, G, 0) != 0 || flat_begin(T, G, G) != T) return 2;
     std::vector<int> owner(T, -1);
@@ -36,7 +43,7 @@ static int check(int n, int ntiles, int G) {
         if (owner[t] < 0 || flat_owner(t, T, G) != owner[t]) return 6;
     std::vector<char> used(n + G, 0);
     for (int li = 0; li < n; li++) {
-        const RecRange r = unit_records(li, n, ntiles, G);
+        const RecRange r = unit_records(P, li, ntiles, G0);
         const int w0 = owner[(int64_t)li * ntiles], w1 = owner[(int64_t)(li + 1) * ntiles - 1];
         if (r.first != li + w0 || r.count != w1 - w0 + 1) return 7;
         for (int w = w0; w <= w1; w++) {  // each of them streams part of unit li
@@ -55,12 +62,19 @@ int main() {
     const int grids[] = {1, 3, 256, 768, 1024};
     const int tiles[] = {1, 2, 5, 37, 61};
     for (int iter = 0; iter < 3000; iter++) {
-        const int scale = (iter % 3 == 0) ? 4 : (iter % 3 == 1 ? 64 : 2800);
-        const int n = 1 + (int)(next_u32() % (unsigned)scale);
+        PosDesc P = {};
+        const int scale = (iter % 3 == 0) ? 4 : (iter % 3 == 1 ? 64 : 700);
+        for (int c = 0; c < kNumCls; c++)
+            P.n_cls[c] = (next_u32() % 4 == 0) ? 0 : (int)(next_u32() % (unsigned)scale);
+        if (iter % 5 == 0)  // untruncated units only
+            for (int c = 0; c < kNumCls; c++)
+                if (c != CLS_FULL) P.n_cls[c] = 0;
+        if (pos_units(P) == 0) P.n_cls[next_u32() % kNumCls] = 1;
         const int G = grids[next_u32() % 5], nt = tiles[next_u32() % 5];
-        const int rc = check(n, nt, G);
+        const int rc = check(P, nt, G);
         if (rc) {
-            printf("FAIL rc=%d n=%d ntiles=%d G=%d\n", rc, n, nt, G);
+            printf("FAIL rc=%d n_cls=%d,%d,%d,%d ntiles=%d G=%d\n", rc, P.n_cls[0], P.n_cls[1],
+                   P.n_cls[2], P.n_cls[3], nt, G);
             return 1;
         }
         cases++;
