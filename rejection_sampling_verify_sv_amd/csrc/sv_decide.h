@@ -233,17 +233,21 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
     }
     // Final draw over p's kept tokens in ascending id order: the residual
     // (p - q)+ after a rejection, p itself for the bonus token.
+    // The kept tokens of each side are a prefix of its lanes: broadcast them
+    // one at a time (scalar reads of a lane, no LDS traffic) and only as many
+    // as are kept.  qj: q of this lane's token; rank: kept p tokens of lower id.
+    const int nq = __popcll(__ballot(keep_q));
+    const int np = __popcll(__ballot(keep_p));
     double qj = 0.0;
     int rank = 0;
-    for (int s = 0; s < kWave; s++) {
-        const int ids = __shfl(id_q, s, kWave);
-        const double qs = __shfl(q, s, kWave);
-        const bool ks = __shfl((int)keep_q, s, kWave) != 0;
-        if (ks && ids == id_p) qj = qs;
-        const int idp = __shfl(id_p, s, kWave);
-        const bool kp = __shfl((int)keep_p, s, kWave) != 0;
-        rank += (kp && idp < id_p) ? 1 : 0;
+    const int q_lo = __double2loint(q), q_hi = __double2hiint(q);
+    for (int s = 0; s < nq; s++) {
+        const int ids = __builtin_amdgcn_readlane(id_q, s);
+        const double qs = __hiloint2double(__builtin_amdgcn_readlane(q_hi, s),
+                                           __builtin_amdgcn_readlane(q_lo, s));
+        if (ids == id_p) qj = qs;
     }
+    for (int s = 0; s < np; s++) rank += __builtin_amdgcn_readlane(id_p, s) < id_p ? 1 : 0;
     if (keep_p) {
         const double d = p - qj;
         s_w[rank] = has_draft ? (d > 0.0 ? d : 0.0) : p;
