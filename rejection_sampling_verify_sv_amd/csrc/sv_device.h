@@ -665,13 +665,113 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        uint64_t w = __shfl_xor(v, o, kWave);
-        v = w > v ? w : v;
+// ---- lane exchanges without LDS ------------------------------------------
+// xor_lane<S>(v) is v of lane (lane ^ S), S a power of two below 64.  Inside
+// a row of 16 lanes DPP does it: S = 1, 2 are quad permutations, S = 8 is a
+// rotation by 8, and S = 4 takes two rotations (by 4 and by 12), each written
+// only to the quads (DPP banks) whose partner it reaches.  Across rows the
+// gfx950 permlane swaps exchange the odd rows (S = 16) or the upper half
+// (S = 32) of one register with the even rows / lower half of another; given
+// v twice, every lane ends holding the values of both lanes of its pair, the
+// lower lane's in the first result and the higher lane's in the second.
+template <int S>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+    static_assert(S == 1 || S == 2 || S == 4 || S == 8 || S == 16 || S == 32, "stride");
+    const int iv = (int)v;
+    if constexpr (S == 1) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(iv, iv, 0xb1, 0xf, 0xf, false);  // [1,0,3,2]
+    } else if constexpr (S == 2) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(iv, iv, 0x4e, 0xf, 0xf, false);  // [2,3,0,1]
+    } else if constexpr (S == 4) {
+        // row_ror:4 reads lane i - 4 (quads 1, 3), row_ror:12 lane i + 4 (quads 0, 2)
+        const int t = __builtin_amdgcn_update_dpp(iv, iv, 0x124, 0xf, 0xa, false);
+        return (uint32_t)__builtin_amdgcn_update_dpp(t, iv, 0x12c, 0xf, 0x5, false);
+    } else if constexpr (S == 8) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(iv, iv, 0x128, 0xf, 0xf, false);  // row_ror:8
+    } else if constexpr (S == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane_id() & 16) ? (uint32_t)r[0] : (uint32_t)r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane_id() & 32) ? (uint32_t)r[0] : (uint32_t)r[1];
     }
+}
+template <int S>
+__device__ __forceinline__ uint64_t xor_lane(uint64_t v) {
+    const uint32_t lo = xor_lane<S>((uint32_t)v), hi = xor_lane<S>((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+// v of lane 63 - lane: mirror inside rows (row_mirror), then swap rows and halves.
+__device__ __forceinline__ uint64_t wave_reverse(uint64_t v) {
+    const int lo = __builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp((int)(v >> 32), (int)(v >> 32), 0x140, 0xf, 0xf,
+                                               false);
+    const uint64_t m = ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+    return xor_lane<32>(xor_lane<16>(m));
+}
+// v of lane i for a wave-uniform i (scalar reads, no LDS).
+__device__ __forceinline__ uint64_t lane_value(uint64_t v, int i) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)v, i);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), i);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    uint64_t w;
+    w = xor_lane<1>(v);  v = w > v ? w : v;
+    w = xor_lane<2>(v);  v = w > v ? w : v;
+    w = xor_lane<4>(v);  v = w > v ? w : v;
+    w = xor_lane<8>(v);  v = w > v ? w : v;
+    w = xor_lane<16>(v); v = w > v ? w : v;
+    w = xor_lane<32>(v); v = w > v ? w : v;
     return v;
+}
+
+// One compare-exchange stage of a bitonic network: lanes (i, i ^ kStride)
+// order their pair descending inside blocks of kSize lanes whose bit kSize
+// is clear and ascending in the others (flipped when kDesc is false; at
+// kSize = 64 every block is the first one).
+template <bool kDesc, int kSize, int kStride>
+__device__ __forceinline__ uint64_t bitonic_stage(uint64_t v, int lane) {
+    const uint64_t o = xor_lane<kStride>(v);
+    const bool first_block = (lane & kSize) == 0;
+    const bool lower = (lane & kStride) == 0;
+    const bool keep_max = (lower == first_block) == kDesc;
+    return keep_max ? (o > v ? o : v) : (o < v ? o : v);
+}
+template <bool kDesc, int kSize, int kStride>
+__device__ __forceinline__ uint64_t bitonic_from(uint64_t v, int lane) {
+    v = bitonic_stage<kDesc, kSize, kStride>(v, lane);
+    if constexpr (kStride > 1) return bitonic_from<kDesc, kSize, kStride / 2>(v, lane);
+    else if constexpr (kSize < kWave) return bitonic_from<kDesc, kSize * 2, kSize>(v, lane);
+    else return v;
+}
+// Bitonic sort of one u64 per lane across a wave: descending (lane 0 the
+// largest) or ascending.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
+    return bitonic_from<true, 2, 1>(v, lane_id());
+}
+__device__ __forceinline__ uint64_t wave_sort_asc(uint64_t v) {
+    return bitonic_from<false, 2, 1>(v, lane_id());
+}
+
+// Top 64 of a descending and an ascending 64-list (one entry per lane),
+// descending: max(a_j, b_j) holds the 64 largest of the union as a bitonic
+// sequence, which six half-cleaner stages sort.
+template <int kStride>
+__device__ __forceinline__ uint64_t half_clean_desc(uint64_t v, int lane) {
+    const uint64_t o = xor_lane<kStride>(v);
+    const bool lower = (lane & kStride) == 0;
+    v = lower ? (o > v ? o : v) : (o < v ? o : v);
+    if constexpr (kStride > 1) return half_clean_desc<kStride / 2>(v, lane);
+    else return v;
+}
+__device__ __forceinline__ uint64_t wave_merge_top_asc(uint64_t a, uint64_t b_asc) {
+    return half_clean_desc<kWave / 2>(a > b_asc ? a : b_asc, lane_id());
+}
+// The same for two descending lists.
+__device__ __forceinline__ uint64_t wave_merge_top(uint64_t a, uint64_t b) {
+    return wave_merge_top_asc(a, wave_reverse(b));
 }
 
 // ---- wave reductions on the DPP network (no LDS round trips) --------------
@@ -746,39 +846,6 @@ __device__ __forceinline__ float block_max_f32(float v, uint64_t* tmp) {
 #pragma unroll
     for (int i = 1; i < kWaves; i++) r = fmaxf(r, __uint_as_float((uint32_t)tmp[i]));
     return r;
-}
-
-// Bitonic sort (descending) of one u64 per lane across a wave.
-__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int size = 2; size <= kWave; size <<= 1) {
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const uint64_t o = __shfl_xor(v, stride, kWave);
-            const bool dir = (lane & size) == 0;       // descending block
-            const bool lower = (lane & stride) == 0;   // lower index of the pair
-            const bool keep_max = (lower == dir);
-            v = keep_max ? (o > v ? o : v) : (o < v ? o : v);
-        }
-    }
-    return v;
-}
-
-// Top 64 of two descending 64-lists (one entry per lane), descending.
-// max(a_j, b_{63-j}) holds the 64 largest of the union as a bitonic
-// sequence; six half-cleaner stages sort it.
-__device__ __forceinline__ uint64_t wave_merge_top(uint64_t a, uint64_t b) {
-    const int lane = lane_id();
-    const uint64_t br = __shfl(b, kWave - 1 - lane, kWave);
-    uint64_t v = a > br ? a : br;
-#pragma unroll
-    for (int stride = kWave / 2; stride > 0; stride >>= 1) {
-        const uint64_t o = __shfl_xor(v, stride, kWave);
-        const bool lower = (lane & stride) == 0;
-        v = lower ? (o > v ? o : v) : (o < v ? o : v);
-    }
-    return v;
 }
 
 // Block-wide exclusive prefix sum of one double per thread (fixed order).

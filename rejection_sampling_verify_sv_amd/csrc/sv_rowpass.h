@@ -102,10 +102,9 @@ __device__ __forceinline__ void wt_flush(WaveTopk& st, uint64_t* cbuf, int k_eff
     wave_lds_sync();
     if (lane < left) cbuf[lane] = rest;
     st.cnt = left;
-    c = wave_sort_desc(c);
-    st.lst = wave_merge_top(st.lst, c);
-    const uint64_t kth = __shfl(st.lst, k_eff - 1, kWave);
-    const uint64_t qth = __shfl(st.lst, (k_eff + kWaves - 1) / kWaves - 1, kWave);
+    st.lst = wave_merge_top_asc(st.lst, wave_sort_asc(c));
+    const uint64_t kth = lane_value(st.lst, k_eff - 1);
+    const uint64_t qth = lane_value(st.lst, (k_eff + kWaves - 1) / kWaves - 1);
     if (lane == 0 && qth != 0ull) lds_store_relaxed(&sm.wq[wave_id()], qth);
     if (kth > st.thr) {
         st.thr = kth;
@@ -153,8 +152,8 @@ __device__ __forceinline__ void seg_topk(const void* row, int64_t start, int64_t
                     best = make_key(v[i], (uint32_t)elem_id<DT>(t0, i));
             }
             const uint64_t sl = wave_sort_desc(best);
-            const uint64_t th = __shfl(sl, k_eff - 1, kWave);
-            const uint64_t thq = __shfl(sl, (k_eff + kWaves - 1) / kWaves - 1, kWave);
+            const uint64_t th = lane_value(sl, k_eff - 1);
+            const uint64_t thq = lane_value(sl, (k_eff + kWaves - 1) / kWaves - 1);
             if (th > 0ull && th - 1ull > st.thr) st.thr = th - 1ull;
             if (lane == 0 && thq != 0ull) lds_store_relaxed(&sm.wq[w], thq);
         }
