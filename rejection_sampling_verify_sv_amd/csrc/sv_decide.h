@@ -88,19 +88,6 @@ __device__ inline void close_row_invalid(const StepArgs& a, int b, int code) {
     }
 }
 
-// ---- wave arithmetic in a fixed order -------------------------------------
-// Sum over the wave, computed in one fixed tree and broadcast from lane 0,
-// so every lane holds the same bits.
-__device__ __forceinline__ double wave_incl_scan(double v) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const double t = __shfl_up(v, o, kWave);
-        if (lane >= o) v += t;
-    }
-    return v;
-}
-
 // Index of the first lane where pred holds, or -1.
 __device__ __forceinline__ int first_lane(bool pred) {
     const uint64_t m = __ballot(pred);
@@ -124,15 +111,14 @@ __device__ bool topk_dist_wave(uint64_t key, int k_eff, double T, double top_p, 
     const int lane = lane_id();
     const bool valid = lane < k_eff;
     const double l = (double)key_logit(key);
-    const double l0 = __shfl(l, 0, kWave);
+    const double l0 = lane_value(l, 0);
     if (!(l0 > -INFINITY)) return false;
     const double w = valid ? exp((l - l0) / T) : 0.0;
     int nkeep = k_eff;
     if (top_p < 1.0) {
         const double zk = wave_sum(w);
         const double P = w / zk;
-        const double up = __shfl_up(wave_incl_scan(P), 1, kWave);
-        const double mass_before = lane == 0 ? 0.0 : up;
+        const double mass_before = wave_shift_up1(wave_incl_scan(P));  // 0 in lane 0
         const int f = first_lane(valid && !(mass_before < top_p));
         nkeep = f < 0 ? k_eff : f;
     }
@@ -144,7 +130,7 @@ __device__ bool topk_dist_wave(uint64_t key, int k_eff, double T, double top_p, 
 
 __device__ __forceinline__ double lookup_lane(bool keep, int id, double p, int token) {
     const int j = first_lane(keep && id == token);
-    return j < 0 ? 0.0 : __shfl(p, j, kWave);
+    return j < 0 ? 0.0 : lane_value(p, j);
 }
 
 __device__ __forceinline__ double accept_prob(double px, double qx) {
@@ -267,8 +253,7 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
     }
     const double target = uf * W;
     const double incl = wave_incl_scan(wr);
-    const double excl_raw = __shfl_up(incl, 1, kWave);
-    const double excl = lane == 0 ? 0.0 : excl_raw;
+    const double excl = wave_shift_up1(incl);  // 0 in lane 0
     int j = first_lane(wr > 0.0 && target < incl);
     double margin_scale = 1.0;
     if (j < 0) {  // not reachable for u < 1; keeps the function total
@@ -276,11 +261,12 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
         j = 63 - __clzll((unsigned long long)pos);
         margin_scale = 0.0;
     }
-    const int y = __shfl(idr, j, kWave);
-    const double lo = __shfl(excl, j, kWave) / W;
-    const double hi = (margin_scale == 0.0) ? 1.0 : __shfl(incl, j, kWave) / W;
-    const double wy = __shfl(wr, j, kWave);
-    const double py = __shfl(pr, j, kWave);
+    // j is the same in every lane: scalar reads of lane j
+    const int y = __builtin_amdgcn_readlane(idr, j);
+    const double lo = lane_value(excl, j) / W;
+    const double hi = (margin_scale == 0.0) ? 1.0 : lane_value(incl, j) / W;
+    const double wy = lane_value(wr, j);
+    const double py = lane_value(pr, j);
     if (lane == 0) {
         if (a.diag) {
             double* dg = a.diag + (int64_t)b * 4 * (a.K + 1) + 4 * a.K;

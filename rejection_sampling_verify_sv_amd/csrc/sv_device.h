@@ -716,6 +716,44 @@ __device__ __forceinline__ uint64_t lane_value(uint64_t v, int i) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+__device__ __forceinline__ double lane_value(double v, int i) {
+    return __longlong_as_double((long long)lane_value((uint64_t)__double_as_longlong(v), i));
+}
+
+// 64-bit DPP move (two 32-bit moves); lanes whose source lies outside the
+// pattern, or outside the rows of kRowMask, read 0.
+template <int kCtrl, int kRowMask, class T>
+__device__ __forceinline__ T dpp_zero(T v) {
+    static_assert(sizeof(T) == 8, "64-bit values");
+    uint64_t u;
+    __builtin_memcpy(&u, &v, 8);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)u, kCtrl, kRowMask, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(u >> 32), kCtrl, kRowMask, 0xf, false);
+    const uint64_t r = ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+    T o;
+    __builtin_memcpy(&o, &r, 8);
+    return o;
+}
+// Inclusive prefix sum over the wave (lane i gets lanes 0..i) in one fixed
+// order: inside each row of 16 by shifts of 1, 2, 4 and 8 lanes
+// (row_shr), then the totals of rows 0 and 2 added into rows 1 and 3
+// (row_bcast:15) and the total of rows 0-1 into rows 2 and 3 (row_bcast:31).
+template <class T>
+__device__ __forceinline__ T wave_incl_scan(T v) {
+    v += dpp_zero<0x111, 0xf>(v);
+    v += dpp_zero<0x112, 0xf>(v);
+    v += dpp_zero<0x114, 0xf>(v);
+    v += dpp_zero<0x118, 0xf>(v);
+    v += dpp_zero<0x142, 0xa>(v);
+    v += dpp_zero<0x143, 0xc>(v);
+    return v;
+}
+// v of lane i - 1, 0 in lane 0 (wave_shr:1).
+template <class T>
+__device__ __forceinline__ T wave_shift_up1(T v) {
+    return dpp_zero<0x138, 0xf>(v);
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     uint64_t w;
     w = xor_lane<1>(v);  v = w > v ? w : v;
@@ -852,12 +890,7 @@ __device__ __forceinline__ float block_max_f32(float v, uint64_t* tmp) {
 template <class T>
 __device__ inline T block_exclusive_scan(T v, T* tmp /* kWaves */, T* total) {
     const int lane = lane_id(), w = wave_id();
-    T incl = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const T t = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += t;
-    }
+    const T incl = wave_incl_scan(v);
     __syncthreads();
     if (lane == kWave - 1) tmp[w] = incl;
     __syncthreads();

@@ -53,8 +53,10 @@ __device__ inline uint32_t nuc_first_image(int beta, float la, float cb) {
         const uint32_t p = lo + (uint32_t)((span * (uint64_t)(lane + 1)) / (kWave + 1));
         const uint64_t m = __ballot(nuc_gbin(ord_float(p), la, cb) >= beta);
         const int f = m ? __ffsll((unsigned long long)m) - 1 : kWave;
-        const uint32_t nlo = f == 0 ? lo : (uint32_t)__shfl((int)p, f - 1, kWave) + 1u;
-        const uint32_t nhi = f == kWave ? hi : (uint32_t)__shfl((int)p, f, kWave);
+        // f is the same in every lane: scalar reads of lanes f - 1 and f
+        const uint32_t nlo =
+            f == 0 ? lo : (uint32_t)__builtin_amdgcn_readlane((int)p, f - 1) + 1u;
+        const uint32_t nhi = f == kWave ? hi : (uint32_t)__builtin_amdgcn_readlane((int)p, f);
         lo = nlo;
         hi = nhi;
     }
@@ -255,11 +257,13 @@ __device__ inline void select_boundary(const uint64_t* s_h, float top_p, float l
     // this thread's lowest bucket; opaque, so that the scales below are
     // loaded here rather than hoisted and held across the caller's loop
     const int j0 = kNW - kPer * (tid_opaque() + 1);
+    double m[kPer];  // bucket masses, highest bucket first
     double mine = 0.0;
 #pragma unroll
     for (int q = 0; q < kPer; q++) {
         const int j = j0 + kPer - 1 - q;
-        mine += nuc_scale(j) * ((double)s_h[j] * kUnfix);
+        m[q] = nuc_scale(j) * ((double)s_h[j] * kUnfix);
+        mine += m[q];
     }
     double Z;
     const double excl0 = block_exclusive_scan(mine, s_tmp, &Z);
@@ -271,13 +275,11 @@ __device__ inline void select_boundary(const uint64_t* s_h, float top_p, float l
     double best_before = 0.0;
 #pragma unroll
     for (int q = 0; q < kPer; q++) {
-        const int j = j0 + kPer - 1 - q;
-        const uint64_t rel = s_h[j];
-        if (rel != 0ull && run < target) {
+        if (m[q] != 0.0 && run < target) {  // a bucket's mass is 0 iff it holds no weight
             best = (int)threadIdx.x * kPer + q;
             best_before = run;
         }
-        run += nuc_scale(j) * ((double)rel * kUnfix);
+        run += m[q];
     }
     if (best >= 0) atomicMax(s_star, best);
     __syncthreads();
