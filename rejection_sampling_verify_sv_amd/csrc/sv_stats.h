@@ -101,9 +101,9 @@ __global__ __launch_bounds__(kThreads) void stats_prep_kernel(StepArgs a) {
                 return;
             }
             const int nk = __popcll(__ballot(keep));
-            const uint64_t tau = __shfl(key, nk - 1, kWave);
+            const uint64_t tau = lane_value(key, nk - 1);  // nk >= 1: the best token is kept
             const double l = (double)key_logit(key);
-            const double l0 = __shfl(l, 0, kWave);
+            const double l0 = lane_value(l, 0);
             const double zs = wave_sum(keep ? exp((l - l0) * invT) : 0.0);
             const double kap = exp(((s == 0 ? mt : md) - l0) * invT) / zs;
             if (s == 0) {
