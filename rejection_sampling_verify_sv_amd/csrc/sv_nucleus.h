@@ -438,15 +438,15 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
 #pragma unroll
             for (int i = 0; i < TS::kE; i++) any |= __builtin_amdgcn_fmed3f(v[i], l_lo, l_hi) == v[i];
             if (__ballot(any) == 0ull) return;
-            // per-lane bits from the sign of (v - l_lo) (l_hi - v), the same
-            // test in another form (not merged with the one above, whose
-            // per-element masks would otherwise stay live in scalar registers)
+            // per-lane bits: the same clamp test again, on copies of the range
+            // the compiler cannot see through (merged with the one above, its
+            // per-element masks would stay live in scalar registers)
+            float lo2 = l_lo, hi2 = l_hi;
+            asm volatile("" : "+v"(lo2), "+v"(hi2));
             uint32_t hit = 0u;
 #pragma unroll
-            for (int i = 0; i < TS::kE; i++) {
-                const float pr = (v[i] - l_lo) * (l_hi - v[i]);
-                hit |= ((~__float_as_uint(pr)) >> 31) << i;
-            }
+            for (int i = 0; i < TS::kE; i++)
+                hit |= (__builtin_amdgcn_fmed3f(v[i], lo2, hi2) == v[i] ? 1u : 0u) << i;
             uint32_t id0 = (uint32_t)elem_id<DT>(t0, 0);
             asm volatile("" : "+v"(id0));
             // round r stores the r-th hit of every lane that has one; the
