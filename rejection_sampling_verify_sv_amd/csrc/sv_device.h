@@ -601,11 +601,25 @@ __host__ __device__ __forceinline__ int flat_owner(int64_t t, int64_t T, int G) 
 // key or a histogram per piece), and every piece pays its own start (the
 // first tiles of a top-k piece are the costly ones).  Untruncated units keep
 // per-tile records whatever the split, so they keep one tile per workgroup.
+// With at most one unit per workgroup and pieces of at least 2 kRowMinTiles
+// tiles, the workgroups taking part are a multiple of the unit count when
+// that keeps at least 7/8 of them: every unit then gets the same number of
+// workgroups, each streaming a part of one unit only (the even split's
+// boundaries fall on unit boundaries), so no workgroup pays for the start and
+// end of a second piece.  (Measured: the last position of the 1024-row mix,
+// 330 units, 4.5 us faster; at 4-tile pieces, as in small batches, no gain.)
 constexpr int kRowMinTiles = 4;
 __host__ __device__ __forceinline__ int row_grid(const PosDesc& P, int64_t T, int G) {
-    if (P.n_cls[CLS_FULL] == pos_units(P)) return flat_active(T, G);
+    const int n = pos_units(P);
+    if (P.n_cls[CLS_FULL] == n) return flat_active(T, G);
     const int64_t g = (T + kRowMinTiles - 1) / kRowMinTiles;
-    return (int)(g < (int64_t)G ? (g > 0 ? g : 1) : (int64_t)G);
+    const int Gm = (int)(g < (int64_t)G ? (g > 0 ? g : 1) : (int64_t)G);
+    if (n > 0 && n <= G && T >= (int64_t)Gm * 2 * kRowMinTiles) {
+        const int64_t cap = (T / n) / kRowMinTiles;  // pieces of at least kRowMinTiles tiles
+        const int64_t per = (int64_t)(G / n) < cap ? (int64_t)(G / n) : cap;
+        if (per >= 1 && (int64_t)n * per * 8 >= (int64_t)Gm * 7) return (int)(n * per);
+    }
+    return Gm;
 }
 
 // Record slots [first, first + count) of unit li (index in position P's

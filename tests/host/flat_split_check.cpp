@@ -2,7 +2,8 @@
 // workgroups (row_grid / flat_begin / flat_owner / unit_records in
 // sv_device.h): for many class mixes, tile counts and grids, the number of
 // workgroups taking part (at least kRowMinTiles tiles each unless every unit
-// is untruncated), every one of them owning a contiguous, non-empty range,
+// is untruncated; with long pieces a multiple of the unit count, each
+// workgroup inside one unit, when that keeps 7/8 of them), every one of them owning a contiguous, non-empty range,
 // the ranges tiling the concatenation in order, the owner of every tile
 // being the workgroup whose range holds it, every unit's records being
 // exactly the pieces that cover it, and the record slots u + w unique and
@@ -22,13 +23,28 @@ static unsigned next_u32() {
     return (unsigned)(rng_state >> 33);
 }
 
+static int n_aligned = 0;  // cases that took the unit-aligned split
+
 static int check(const PosDesc& P, int ntiles, int G0) {
     const int n = pos_units(P);
     const int64_t T = (int64_t)n * ntiles;
     const int G = row_grid(P, T, G0);  // the workgroups the row pass lets take part
     const bool all_full = P.n_cls[CLS_FULL] == n;
     const int64_t want = all_full ? T : (T + kRowMinTiles - 1) / kRowMinTiles;
-    if (G != (want < G0 ? want : G0)) return 1;
+    const int Gm = (int)(want < G0 ? want : G0);
+    // a multiple of the unit count (same pieces per unit) when that keeps 7/8
+    // of the workgroups and pieces of kRowMinTiles tiles, else Gm
+    int Gw = Gm;
+    if (!all_full && n <= G0 && T >= (int64_t)Gm * 2 * kRowMinTiles) {
+        for (int per = G0 / n; per >= 1; per--) {
+            if (per * kRowMinTiles > ntiles) continue;
+            if ((int64_t)n * per * 8 >= (int64_t)Gm * 7) Gw = n * per;
+            break;
+        }
+    }
+    if (G != Gw) return 1;
+    const bool aligned = G % n == 0 && !all_full && G != Gm;
+    if (aligned) n_aligned++;
     const int Ga = flat_active(T, G);
     if (flat_begin(T, G, 0) != 0 || flat_begin(T, G, G) != T) return 2;
     std::vector<int> owner(T, -1);
@@ -37,6 +53,8 @@ static int check(const PosDesc& P, int ntiles, int G0) {
         if (b < a) return 3;
         if (w < Ga && b == a) return 4;  // a workgroup taking part without a tile
         if (w >= Ga && b != a) return 5;
+        // an aligned split never puts two units into one workgroup
+        if (aligned && b > a && a / ntiles != (b - 1) / ntiles) return 10;
         for (int64_t t = a; t < b; t++) owner[t] = w;
     }
     for (int64_t t = 0; t < T; t++)
@@ -79,6 +97,10 @@ int main() {
         }
         cases++;
     }
-    printf("ok %d cases\n", cases);
+    if (n_aligned == 0) {
+        printf("FAIL no case took the unit-aligned split\n");
+        return 1;
+    }
+    printf("ok %d cases (%d unit-aligned)\n", cases, n_aligned);
     return 0;
 }
