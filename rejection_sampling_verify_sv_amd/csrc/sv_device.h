@@ -603,11 +603,13 @@ __host__ __device__ __forceinline__ int flat_owner(int64_t t, int64_t T, int G) 
 // per-tile records whatever the split, so they keep one tile per workgroup.
 // With at most one unit per workgroup and pieces of at least 2 kRowMinTiles
 // tiles, the workgroups taking part are a multiple of the unit count when
-// that keeps at least 7/8 of them: every unit then gets the same number of
+// that keeps at least 5/8 of them: every unit then gets the same number of
 // workgroups, each streaming a part of one unit only (the even split's
 // boundaries fall on unit boundaries), so no workgroup pays for the start and
-// end of a second piece.  (Measured: the last position of the 1024-row mix,
-// 330 units, 4.5 us faster; at 4-tile pieces, as in small batches, no gain.)
+// end of a second piece.  Measured on the 1024-row mix: 330 units on 990
+// workgroups took 46 us against 50.5, 715 units on 715 workgroups (one unit
+// each) 82 against 87 on all 1024; at 4-tile pieces, as in small batches,
+// there was no gain.
 constexpr int kRowMinTiles = 4;
 __host__ __device__ __forceinline__ int row_grid(const PosDesc& P, int64_t T, int G) {
     const int n = pos_units(P);
@@ -617,7 +619,7 @@ __host__ __device__ __forceinline__ int row_grid(const PosDesc& P, int64_t T, in
     if (n > 0 && n <= G && T >= (int64_t)Gm * 2 * kRowMinTiles) {
         const int64_t cap = (T / n) / kRowMinTiles;  // pieces of at least kRowMinTiles tiles
         const int64_t per = (int64_t)(G / n) < cap ? (int64_t)(G / n) : cap;
-        if (per >= 1 && (int64_t)n * per * 8 >= (int64_t)Gm * 7) return (int)(n * per);
+        if (per >= 1 && (int64_t)n * per * 8 >= (int64_t)Gm * 5) return (int)(n * per);
     }
     return Gm;
 }

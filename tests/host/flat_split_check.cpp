@@ -3,7 +3,7 @@
 // sv_device.h): for many class mixes, tile counts and grids, the number of
 // workgroups taking part (at least kRowMinTiles tiles each unless every unit
 // is untruncated; with long pieces a multiple of the unit count, each
-// workgroup inside one unit, when that keeps 7/8 of them), every one of them owning a contiguous, non-empty range,
+// workgroup inside one unit, when that keeps 5/8 of them), every one of them owning a contiguous, non-empty range,
 // the ranges tiling the concatenation in order, the owner of every tile
 // being the workgroup whose range holds it, every unit's records being
 // exactly the pieces that cover it, and the record slots u + w unique and
@@ -32,13 +32,13 @@ static int check(const PosDesc& P, int ntiles, int G0) {
     const bool all_full = P.n_cls[CLS_FULL] == n;
     const int64_t want = all_full ? T : (T + kRowMinTiles - 1) / kRowMinTiles;
     const int Gm = (int)(want < G0 ? want : G0);
-    // a multiple of the unit count (same pieces per unit) when that keeps 7/8
+    // a multiple of the unit count (same pieces per unit) when that keeps 5/8
     // of the workgroups and pieces of kRowMinTiles tiles, else Gm
     int Gw = Gm;
     if (!all_full && n <= G0 && T >= (int64_t)Gm * 2 * kRowMinTiles) {
         for (int per = G0 / n; per >= 1; per--) {
             if (per * kRowMinTiles > ntiles) continue;
-            if ((int64_t)n * per * 8 >= (int64_t)Gm * 7) Gw = n * per;
+            if ((int64_t)n * per * 8 >= (int64_t)Gm * 5) Gw = n * per;
             break;
         }
     }
