@@ -97,6 +97,16 @@ def test_recipe_small_vocab_every_row(oracle_mod, dev, name):
     check(oracle_mod, wl, dev, label=f"{name}@V=20011")
 
 
+def test_unit_aligned_grid_every_row(oracle_mod, dev):
+    # 160 rows of the mix at V = 151936: position 0 holds about 290 units of
+    # 38 tiles, so the row pass (1024 resident workgroups) takes the
+    # unit-aligned grid (three workgroups per unit, one piece each); every
+    # row is compared, of every sampler class
+    wl = workloads.make("mixed_samplers_b1024", batch=160)
+    rep, _, _ = check(oracle_mod, wl, dev, label="unit_aligned_b160")
+    assert rep.compared > 100
+
+
 def _random_case(rng, B, K, V, dtype, T, top_k, top_p, scale=2.0, quant=None, draft_len=None,
                  noise=0.6):
     t = rng.normal(0, scale, (B, K + 1, V))
