@@ -193,6 +193,23 @@ int sv_sample(const void* logits, const sv_sampler_params* sampler_params, const
 int sv_accept_stats(const void* target_logits, const void* draft_logits,
                     const sv_sampler_params* sampler_params, double* out, const sv_config* cfg);
 
+/*
+ * Measurement aid, not part of the verify step: stream `bytes` bytes of
+ * device memory once with the tiling of the verify step's row pass (16-byte
+ * coalesced non-temporal loads, double-buffered tiles split evenly over one
+ * resident wave of workgroups) and no work per element beyond a max, which
+ * each workgroup folds into *out (device uint32; the caller zeroes it, the
+ * value itself means nothing).  Its rate is the sustainable read rate the
+ * row pass is measured against, the second denominator next to the HBM
+ * peak, after "Apple Silikon İçin Cihaz Üstü Çıkarımı Optimize Etme",
+ * section "Daha fazla optimizasyonun sınırları" (judge a kernel against what
+ * a trivial read of the same bytes reaches on the part).
+ *   data   device pointer, 16-byte aligned; bytes > 0, a multiple of 16
+ *   stream hipStream_t, NULL => default stream
+ * Returns SV_OK once enqueued, SV_EINVAL on bad arguments, SV_EHIP.
+ */
+int sv_stream_read(const void* data, size_t bytes, uint32_t* out, void* stream);
+
 /* Number of kernel launches in one step for max_draft K (0 if K is outside
  * [0, 1024]), and
  * the name of launch i ("plan", "rowpass", "cut_decide", ...; NULL if out of

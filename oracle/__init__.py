@@ -56,6 +56,14 @@ def _load():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
+        lib.sv_oracle_explain.restype = ctypes.c_int
+        lib.sv_oracle_explain.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ]
         lib.sv_oracle_dist.restype = ctypes.c_int
         lib.sv_oracle_dist.argtypes = [
             ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_double,
@@ -114,6 +122,48 @@ def verify(target, draft, tokens, draft_len, params, uniforms, *, dtype="f32",
     if used < 0:
         raise ValueError("sv_oracle_verify rejected its arguments")
     return out_tok, acc, diag, cut, used
+
+
+def explain(target, draft, tokens, draft_len, params, acc, y, *, dtype="f32",
+            nthreads: int = 0):
+    """The rule's decisions along given outcomes (accept length ``acc[b]``,
+    final token ``y[b]``) of rows laid out as for ``verify`` (K = 0: the one
+    draw per row of ``sample``).
+
+    Returns a dict of arrays: ``a``, ``px``, ``qx`` [B, K] (accept
+    probability and p(x), q(x) of each draft the outcome reaches: positions
+    0..min(acc, L-1), NaN past them); ``lo``, ``hi`` [B] (edges of y's bin in
+    the inverse CDF of the final distribution: the residual at acc when
+    acc < L, p at L otherwise); ``py`` [B] (probability of y under it);
+    ``status`` [B] (0, 1 for a greedy row, -1 invalid row or outcome).  An
+    outcome is what the rule gives for uniforms u' iff u'_j < a_j for j < acc,
+    u'_acc >= a_acc when acc < L, lo <= u'_K < hi and py > 0."""
+    lib = _load()
+    code = {"f32": 0, "bf16": 1}[dtype]
+    target = np.ascontiguousarray(target)
+    B, K1, V = target.shape
+    K = K1 - 1
+    draft = np.ascontiguousarray(draft) if K > 0 else None
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32).reshape(B, K)
+    if K == 0:
+        tokens = np.zeros((B, 1), np.int32)
+    if draft_len is not None:
+        draft_len = np.ascontiguousarray(draft_len, dtype=np.int32).reshape(B)
+    params = np.ascontiguousarray(params)
+    acc = np.ascontiguousarray(acc, dtype=np.int32).reshape(B)
+    y = np.ascontiguousarray(y, dtype=np.int32).reshape(B)
+    out = {n: np.empty((B, max(K, 1)), np.float64) for n in ("a", "px", "qx")}
+    out.update({n: np.empty(B, np.float64) for n in ("lo", "hi", "py")})
+    out["status"] = np.empty(B, np.int32)
+    used = lib.sv_oracle_explain(
+        _ptr(target), _ptr(draft), code, B, K, V, V, V, _ptr(tokens), _ptr(draft_len),
+        _ptr(params), _ptr(acc), _ptr(y), _ptr(out["a"]), _ptr(out["px"]), _ptr(out["qx"]),
+        _ptr(out["lo"]), _ptr(out["hi"]), _ptr(out["py"]), _ptr(out["status"]), int(nthreads))
+    if used < 0:
+        raise ValueError("sv_oracle_explain rejected its arguments")
+    for n in ("a", "px", "qx"):
+        out[n] = out[n][:, :K]
+    return out
 
 
 def dist(logits, temperature: float, top_k: int, top_p: float):

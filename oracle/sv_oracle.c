@@ -387,3 +387,143 @@ int sv_oracle_dist(const double* logit, int V, double T, int top_k, double top_p
     free(w);
     return rc;
 }
+
+/*
+ * The decisions the verify rule takes along one given outcome of a row, for
+ * judging an outcome that differs from the oracle's own: does some uniform
+ * vector within a small distance of the given one lead the rule to it?
+ * The outcome is an accept length acc in [0, L] and a final token y.  Along
+ * it, for j = 0 .. min(acc, L - 1): a_out[j], px_out[j], qx_out[j] are the
+ * accept probability min(1, p_j(x_j) / q_j(x_j)) (R6 for q = 0) and its two
+ * probabilities (the outcome accepts draft j for j < acc and rejects draft
+ * acc when acc < L).  The final distribution is the residual (p - q)+ at acc
+ * (R10: p itself when its mass is 0) when acc < L, p at position L (R11)
+ * otherwise; *lo and *hi are the edges of y's bin of its inverse CDF in
+ * ascending id order (R9), as fractions of its total, and *py the probability
+ * of y under it (0 when y carries no weight).  Slots past the path are NaN.
+ * Returns 0, 1 for a greedy row (T = 0: no uniform takes part, nothing to
+ * explain), -1 for an invalid row or an outcome outside [0, L] x [0, V).
+ * [OPTIQ] "Örnekleme altında doğrulama yanlıştı", [MTPLX] 3.3: the same
+ * accept test and residual as or_verify_row, evaluated on a forced path.
+ */
+static int or_explain_row(const void* target, const void* draft, int dtype, int K, int V,
+                          int64_t t_stride, int64_t d_stride, int b, const int32_t* tokens,
+                          int L, const or_params* prm, int acc, int y, double* a_out,
+                          double* px_out, double* qx_out, double* lo, double* hi, double* py,
+                          or_scratch* s) {
+    or_fill_nan(a_out, K);
+    or_fill_nan(px_out, K);
+    or_fill_nan(qx_out, K);
+    *lo = *hi = *py = NAN;
+    const double T = (double)prm->temperature;
+    const double top_p = (double)prm->top_p;
+    if (!(T >= 0.0) || !(T < INFINITY) || !(top_p > 0.0) || L < 0 || L > K) return -1;
+    for (int k = 0; k < L; k++)
+        if (tokens[k] < 0 || tokens[k] >= V) return -1;
+    if (T == 0.0) return 1;
+    if (acc < 0 || acc > L || y < 0 || y >= V) return -1;
+    const size_t trow0 = (size_t)b * (size_t)(K + 1);
+    const size_t drow0 = (size_t)b * (size_t)K;
+    const int last = acc < L ? acc : L - 1;
+    double cm;
+    for (int k = 0; k <= last; k++) {
+        or_load_row(target, dtype, (trow0 + (size_t)k) * (size_t)t_stride, V, s->logit);
+        if (or_dist(s->logit, V, T, prm->top_k, top_p, s->items, s->w, s->p, &cm) != 0)
+            return -1;
+        or_load_row(draft, dtype, (drow0 + (size_t)k) * (size_t)d_stride, V, s->logit);
+        if (or_dist(s->logit, V, T, prm->top_k, top_p, s->items, s->w, s->q, &cm) != 0)
+            return -1;
+        const int x = tokens[k];
+        const double px = s->p[x], qx = s->q[x];
+        double a;
+        if (qx > 0.0) {
+            a = px / qx;
+            if (a > 1.0) a = 1.0;
+        } else {
+            a = (px > 0.0) ? 1.0 : 0.0;
+        }
+        a_out[k] = a;
+        px_out[k] = px;
+        qx_out[k] = qx;
+    }
+    const double* wgt;
+    if (acc < L) {
+        /* s->p and s->q hold position acc (the last one evaluated above) */
+        double W = 0.0;
+        for (int i = 0; i < V; i++) {
+            double d = s->p[i] - s->q[i];
+            s->r[i] = d > 0.0 ? d : 0.0;
+            W += s->r[i];
+        }
+        wgt = (W > 0.0) ? s->r : s->p;
+    } else {
+        or_load_row(target, dtype, (trow0 + (size_t)L) * (size_t)t_stride, V, s->logit);
+        if (or_dist(s->logit, V, T, prm->top_k, top_p, s->items, s->w, s->p, &cm) != 0)
+            return -1;
+        wgt = s->p;
+    }
+    double W = 0.0, before = 0.0;
+    for (int i = 0; i < V; i++) {
+        if (i == y) before = W;
+        W += wgt[i];
+    }
+    *lo = before / W;
+    *hi = (before + wgt[y]) / W;
+    *py = wgt[y] / W;
+    return 0;
+}
+
+/*
+ * Batch form of or_explain_row over rows laid out as for sv_oracle_verify
+ * (K = 0 allowed: draft may then be NULL and the outcome is the one draw).
+ * acc [B], y [B]: the outcomes to explain; a_out, px_out, qx_out [B][K];
+ * lo, hi, py [B]; status [B] (the row's return code).  Returns the number of
+ * threads used, or -1 on a null required pointer.
+ */
+int sv_oracle_explain(const void* target, const void* draft, int dtype, int B, int K, int V,
+                      int64_t t_stride, int64_t d_stride, const int32_t* tokens,
+                      const int32_t* draft_len, const void* params, const int32_t* acc,
+                      const int32_t* y, double* a_out, double* px_out, double* qx_out,
+                      double* lo, double* hi, double* py, int32_t* status, int nthreads) {
+    if (!target || !tokens || !params || !acc || !y || !a_out || !px_out || !qx_out || !lo ||
+        !hi || !py || !status)
+        return -1;
+    if (K > 0 && !draft) return -1;
+    if (B <= 0 || K < 0 || V < 1 || t_stride < V || (K > 0 && d_stride < V)) return -1;
+    const or_params* prm = (const or_params*)params;
+    int used = 1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+#pragma omp parallel
+    {
+#ifdef _OPENMP
+#pragma omp single
+        used = omp_get_num_threads();
+#endif
+        or_scratch s;
+        s.logit = (double*)malloc(sizeof(double) * (size_t)V);
+        s.items = (or_item*)malloc(sizeof(or_item) * (size_t)V);
+        s.w = (double*)malloc(sizeof(double) * (size_t)V);
+        s.p = (double*)malloc(sizeof(double) * (size_t)V);
+        s.q = (double*)malloc(sizeof(double) * (size_t)V);
+        s.r = (double*)malloc(sizeof(double) * (size_t)V);
+#pragma omp for schedule(dynamic, 1)
+        for (int b = 0; b < B; b++) {
+            const int L = draft_len ? draft_len[b] : K;
+            status[b] = or_explain_row(target, draft, dtype, K, V, t_stride, d_stride, b,
+                                       tokens + (size_t)b * (size_t)K, L, prm + b, acc[b], y[b],
+                                       a_out + (size_t)b * (size_t)K,
+                                       px_out + (size_t)b * (size_t)K,
+                                       qx_out + (size_t)b * (size_t)K, lo + b, hi + b, py + b,
+                                       &s);
+        }
+        free(s.logit);
+        free(s.items);
+        free(s.w);
+        free(s.p);
+        free(s.q);
+        free(s.r);
+    }
+    return used;
+}

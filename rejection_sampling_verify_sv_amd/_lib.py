@@ -20,7 +20,8 @@ SV_F32, SV_BF16 = 0, 1
 SV_MAX_TOP_K = 64
 ERRORS = {0: "SV_OK", -1: "SV_EINVAL", -2: "SV_EWORKSPACE", -3: "SV_EHIP"}
 EXPORTED = ("sv_verify", "sv_verify_profiled", "sv_sample", "sv_accept_stats",
-            "sv_workspace_bytes", "sv_strerror", "sv_launch_count", "sv_launch_name")
+            "sv_workspace_bytes", "sv_strerror", "sv_launch_count", "sv_launch_name",
+            "sv_stream_read")
 
 
 class SvConfig(ctypes.Structure):
@@ -64,6 +65,9 @@ def load() -> ctypes.CDLL:
         lib.sv_strerror.argtypes = [ctypes.c_int]
         lib.sv_launch_count.restype = ctypes.c_int32
         lib.sv_launch_count.argtypes = [ctypes.c_int32]
+        lib.sv_stream_read.restype = ctypes.c_int
+        lib.sv_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                       ctypes.c_void_p]
         lib.sv_launch_name.restype = ctypes.c_char_p
         lib.sv_launch_name.argtypes = [ctypes.c_int32, ctypes.c_int32]
         _lib = lib
@@ -78,6 +82,22 @@ def launch_names(max_draft: int) -> list:
     lib = load()
     return [lib.sv_launch_name(max_draft, i).decode()
             for i in range(lib.sv_launch_count(max_draft))]
+
+
+def stream_read(data: torch.Tensor, out: torch.Tensor, stream: torch.cuda.Stream | None = None):
+    """Enqueue sv_stream_read over the bytes of ``data`` (a contiguous CUDA
+    tensor, 16-byte aligned, size a multiple of 16); ``out`` is a zeroed
+    one-element int32 CUDA tensor.  A measurement aid: the sustainable
+    streaming-read rate with the row pass's tiling."""
+    lib = load()
+    if not (data.is_cuda and out.is_cuda and data.is_contiguous()):
+        raise RuntimeError("stream_read needs contiguous GPU tensors")
+    st = stream if stream is not None else torch.cuda.current_stream(data.device)
+    rc = lib.sv_stream_read(data.data_ptr(), data.numel() * data.element_size(), out.data_ptr(),
+                            st.cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"sv_stream_read failed: {ERRORS.get(rc, rc)}: "
+                           f"{lib.sv_strerror(rc).decode()}")
 
 
 def params_tensor(params, device) -> torch.Tensor:

@@ -217,7 +217,49 @@ int launch_stats(const sv_sampler_params* params, StepArgs a, hipStream_t st) {
     return e == hipSuccess ? SV_OK : hip_fail(e);
 }
 
+// Sustainable streaming-read rate: the row pass's tiling (16-byte coalesced
+// non-temporal loads, double-buffered tiles, the tiles split evenly over one
+// resident wave of workgroups) with nothing per element but a max, so that
+// the loads stay live.  Each workgroup folds its maximum (as raw bits, any
+// data will do) into *out.
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const void* data, int64_t n,
+                                                               uint32_t* out) {
+    using TS = TileShape<SV_F32>;
+    const int64_t T = (n + TS::kTile - 1) / TS::kTile;
+    const int64_t t0 = flat_begin(T, (int)gridDim.x, (int)blockIdx.x);
+    const int64_t t1 = flat_begin(T, (int)gridDim.x, (int)blockIdx.x + 1);
+    if (t0 >= t1) return;
+    const int64_t end = t1 * TS::kTile < n ? t1 * TS::kTile : n;
+    float m = -INFINITY;
+    stream_range<SV_F32, true>(data, t0 * TS::kTile, end,
+                               [&](float (&v)[TS::kE], int64_t, bool) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < TS::kE; i++) m = fmaxf(m, v[i]);
+    });
+    __shared__ uint64_t s_red[kWaves];
+    const float r = block_max_f32(m, s_red);
+    if (threadIdx.x == 0) atomicMax(out, __float_as_uint(r));
+}
+
 }  // namespace
+
+extern "C" int sv_stream_read(const void* data, size_t bytes, uint32_t* out, void* stream) {
+    if (!data || !out || bytes == 0 || bytes % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(data) % 16 != 0 || bytes / 4 > (size_t)INT64_MAX)
+        return SV_EINVAL;
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stream_read_kernel, kThreads, 0);
+    if (e != hipSuccess) return hip_fail(e);
+    const long g = (long)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    stream_read_kernel<<<(unsigned)(g < kGrid ? g : kGrid), kThreads, 0, st>>>(
+        data, (int64_t)(bytes / 4), out);
+    e = hipGetLastError();
+    return e == hipSuccess ? SV_OK : hip_fail(e);
+}
 
 extern "C" size_t sv_workspace_bytes(int32_t batch, int32_t max_draft, int32_t vocab,
                                      int32_t dtype) {

@@ -1,32 +1,47 @@
 """Summaries of rocprofv3 output for the verify kernels.
 
-Two offline commands turn the CSV files rocprofv3 writes into the short text
-summaries kept next to the code:
+Offline commands that turn the CSV files rocprofv3 writes into the short text
+summaries kept under profiles/ (the library never imports this module):
 
   python -m rejection_sampling_verify_sv_amd.prof trace DIR --command CMD
       per-kernel table (calls, mean and total duration) from a
       ``--kernel-trace --stats`` run, as markdown on stdout;
 
   python -m rejection_sampling_verify_sv_amd.prof counters \\
-      --fetch DIR --write DIR --kernel rowpass_kernel --bench-log LOG \\
+      --fetch DIR --write DIR --bench-log LOG \\
       --command-fetch CMD --command-write CMD
-      HBM bytes per launch of one kernel from a ``--pmc FETCH_SIZE`` run and a
-      ``--pmc WRITE_SIZE`` run, each scaled by what the same counter reads for
-      the 1 GiB device-to-device copies ``bench.py --calibrate-copy 1024``
-      runs at the end (known bytes / counted bytes), as JSON on stdout.
-
-Nothing here is imported by the library itself.
+      HBM bytes per dispatch of every kernel of the verify step from a
+      ``--pmc FETCH_SIZE`` run and a ``--pmc WRITE_SIZE`` run of
+      ``bench.py --no-extras --calibrate-copy 1024``, each counter scaled by
+      what it reads for the 1 GiB device-to-device copies that run ends with
+      (known bytes / counted bytes); plus the bytes of one whole step
+      (per-dispatch bytes x dispatches per verify call), as JSON on stdout.
+      The JSON carries the workload and a hash of the kernel sources: bench.py
+      uses it only for that workload and only while the sources are unchanged.
 """
 from __future__ import annotations
 
 import argparse
 import csv
 import glob
+import hashlib
 import json
 import os
+import re
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+
+
+def kernel_source_hash() -> str:
+    """Hash of every kernel source file: counters taken on other sources are
+    not reported."""
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
 
 
 def _one(pattern: str) -> str:
@@ -67,33 +82,48 @@ def _bench_line(log: str) -> dict:
     raise SystemExit(f"no bench JSON line in {log}")
 
 
-def counters(fetch_dir, write_dir, kernel, bench_log, cmd_fetch, cmd_write) -> dict:
-    sys.path.insert(0, ROOT)
-    import bench  # noqa: E402
+def _short(name: str) -> str:
+    """sv::rowpass_kernel<0, true>(...) -> rowpass_kernel."""
+    m = re.search(r"sv::(\w+)", name)
+    return m.group(1) if m else name
 
+
+def counters(fetch_dir, write_dir, bench_log, cmd_fetch, cmd_write) -> dict:
     line = _bench_line(bench_log)
     copy_bytes = int(line["calibration_copy_bytes"])
-    out = {"kernel": kernel, "workload": line["config"]["workload"],
-           "kernel_source_hash": bench.kernel_source_hash(),
-           "alg_bytes_per_launch": line["roofline"]["alg_bytes_per_launch"]}
-    total = 0.0
-    for name, d, cmd in (("FETCH_SIZE", fetch_dir, cmd_fetch), ("WRITE_SIZE", write_dir, cmd_write)):
+    calls = int(line["verify_calls"])
+    out = {"workload": line["config"]["workload"], "kernel_source_hash": kernel_source_hash(),
+           "verify_calls": calls, "alg_bytes_per_step": line["whole_step"]["alg_bytes"],
+           "rowpass_alg_bytes_per_launch": line["roofline"]["alg_bytes_per_launch"],
+           "commands": {"FETCH_SIZE": cmd_fetch, "WRITE_SIZE": cmd_write}, "calibration": {},
+           "kernels": {}}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter_rows(d)
         cal_kib, ncal = _calibration(rows, copy_bytes)
         factor = copy_bytes / (cal_kib * 1024.0)
-        vals = [float(r["Counter_Value"]) for r in rows if kernel in r["Kernel_Name"]]
-        if not vals:
-            raise SystemExit(f"kernel {kernel} not found in {d}")
-        mean_kib = sum(vals) / len(vals)
-        scaled = mean_kib * 1024.0 * factor
-        total += scaled
-        out[name] = {"mean_kib_per_dispatch": round(mean_kib, 1), "dispatches": len(vals),
-                     "calibration_copy_bytes": copy_bytes,
-                     "calibration_counted_kib": round(cal_kib, 1), "calibration_copies": ncal,
-                     "scale": round(factor, 4), "bytes_per_launch": int(scaled),
-                     "command": cmd}
-    out["hbm_bytes_per_launch"] = int(total)
-    out["traffic_over_algorithmic"] = round(total / out["alg_bytes_per_launch"], 4)
+        out["calibration"][name] = {"copy_bytes": copy_bytes, "counted_kib": round(cal_kib, 1),
+                                    "copies": ncal, "scale": round(factor, 4)}
+        per = {}
+        for r in rows:
+            if "sv::" not in r["Kernel_Name"]:
+                continue
+            per.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        for k, vals in per.items():
+            e = out["kernels"].setdefault(k, {})
+            e[name.lower() + "_bytes_per_dispatch"] = int(sum(vals) / len(vals) * 1024.0 * factor)
+            e["dispatches"] = len(vals)
+    step = 0.0
+    for k, e in out["kernels"].items():
+        e["bytes_per_dispatch"] = e.get("fetch_size_bytes_per_dispatch", 0) + \
+            e.get("write_size_bytes_per_dispatch", 0)
+        e["dispatches_per_step"] = round(e["dispatches"] / calls, 3)
+        step += e["bytes_per_dispatch"] * e["dispatches"] / calls
+    out["step_bytes"] = int(step)
+    out["step_traffic_over_alg"] = round(step / out["alg_bytes_per_step"], 4)
+    rp = out["kernels"].get("rowpass_kernel")
+    if rp:
+        out["rowpass_traffic_over_alg"] = round(
+            rp["bytes_per_dispatch"] / out["rowpass_alg_bytes_per_launch"], 4)
     return out
 
 
@@ -106,7 +136,6 @@ def main():
     c = sub.add_parser("counters")
     c.add_argument("--fetch", required=True)
     c.add_argument("--write", required=True)
-    c.add_argument("--kernel", default="rowpass_kernel")
     c.add_argument("--bench-log", required=True)
     c.add_argument("--command-fetch", required=True)
     c.add_argument("--command-write", required=True)
@@ -114,8 +143,8 @@ def main():
     if a.what == "trace":
         sys.stdout.write(trace_table(a.dir, a.command))
     else:
-        json.dump(counters(a.fetch, a.write, a.kernel, a.bench_log, a.command_fetch,
-                           a.command_write), sys.stdout, indent=1)
+        json.dump(counters(a.fetch, a.write, a.bench_log, a.command_fetch, a.command_write),
+                  sys.stdout, indent=1)
         sys.stdout.write("\n")
 
 

@@ -28,11 +28,16 @@ permutation of the ranks for every (row, position); the draft of a Zipf
 workload mixes the target with an independent copy of the same recipe,
 d = rho t + (1 - rho) t'.
 
-Draft tokens: greedy rows take the argmax of the draft logits.  Sampling rows
-draw a Gumbel-max sample from the draft logits at temperature T restricted to
-the top_k largest draft logits (all of them when top_k is 0); the nucleus cut
-is not applied here, so a few percent of drafted tokens fall outside the
-truncated draft distribution and exercise the q(x) = 0 rule.
+Draft tokens: greedy rows take the argmax of the draft logits (lowest id among
+equal maxima).  Sampling rows draw x ~ q, the draft distribution the verify
+step itself forms: temperature T, the top_k largest draft logits (ranked by
+logit descending, id ascending; all of them when top_k is 0 or >= V), the
+nucleus walk over that set renormalised (a token is kept while the mass ranked
+ahead of it is below top_p; top_p >= 1 keeps all), then a Gumbel-max draw over
+the kept set at temperature T.  This is the draft model's own sampling step
+(the deniz.in page, section "Kesme her iki tarafta eşleşmek zorunda": the
+draft samples with the same truncation the target applies); it is written
+here independently of both the verify library and the oracle.
 
 Seeds: numpy PCG64 with SeedSequence(20261202 + recipe_id).spawn(4) giving
 separate streams for logits, draft tokens, uniforms and sampler parameters.
@@ -163,9 +168,35 @@ def _zipf_rows(seed: np.random.SeedSequence, base: np.ndarray, n: int,
     return out
 
 
+def _kept_set(row: np.ndarray, T: float, top_k: int, top_p: float) -> np.ndarray:
+    """Ids of the truncated draft distribution of one row (see the module
+    docstring), in ranking order."""
+    V = row.size
+    if top_p >= 1.0 and not 0 < top_k < V:
+        return np.arange(V)  # untruncated: every id (the draw does not need an order)
+    if 0 < top_k < V:
+        # the top_k best by (logit desc, id asc): partition, then an exact
+        # stable order of the candidates and of the ties at the k-th value
+        cut = np.partition(row, V - top_k)[V - top_k]
+        cand = np.flatnonzero(row >= cut)
+    else:
+        cand = np.arange(V)
+    order = cand[np.argsort(-row[cand], kind="stable")]
+    if 0 < top_k < V:
+        order = order[:top_k]
+    if top_p >= 1.0:
+        return order
+    lv = row[order].astype(np.float64)
+    w = np.exp((lv - lv[0]) / T)
+    P = w / w.sum()
+    before = np.concatenate(([0.0], np.cumsum(P)[:-1]))
+    n = int(np.count_nonzero(before < top_p))
+    return order[:max(n, 1)]
+
+
 def _draft_tokens(seed: np.random.SeedSequence, draft_f32: np.ndarray, params: np.ndarray,
                   draft_len: np.ndarray) -> np.ndarray:
-    """Gumbel-max draft tokens (see module docstring); -1 past draft_len.
+    """Draft tokens x ~ q (see the module docstring); -1 past draft_len.
     One child seed per batch row."""
     B, K, V = draft_f32.shape
     tok = np.full((B, K), -1, np.int32)
@@ -175,20 +206,16 @@ def _draft_tokens(seed: np.random.SeedSequence, draft_f32: np.ndarray, params: n
         rng = np.random.Generator(np.random.PCG64(seeds[b]))
         T = float(params["temperature"][b])
         kk = int(params["top_k"][b])
+        tp = float(params["top_p"][b])
         for k in range(int(draft_len[b])):
             row = draft_f32[b, k]
             if T == 0.0:
                 tok[b, k] = int(np.argmax(row))
                 continue
-            if 0 < kk < V:
-                cand = np.argpartition(-row, kk - 1)[:kk]
-                vals = row[cand].astype(np.float64)
-            else:
-                cand = None
-                vals = row.astype(np.float64)
+            kept = _kept_set(row, T, kk, tp)
+            vals = row[kept].astype(np.float64)
             g = -np.log(-np.log(rng.random(vals.size)))
-            j = int(np.argmax(vals / T + g))
-            tok[b, k] = j if cand is None else int(cand[j])
+            tok[b, k] = int(kept[int(np.argmax(vals / T + g))])
 
     with ThreadPoolExecutor(max_workers=8) as ex:
         list(ex.map(work, range(B)))

@@ -1,16 +1,24 @@
 """GPU-vs-oracle comparison with decision-band accounting.
 
 Rules (the bar the GPU path is held to):
-* token ids and accept lengths must equal the oracle's on every row, except
-  rows where a uniform lies within BAND of a decision threshold that fixed the
-  row's outcome (an evaluated accept test |u - a|, or the final draw's CDF bin
-  edges); those rows are counted as in band and may differ;
+* token ids and accept lengths equal the oracle's on every row, except where
+  the GPU's outcome is what the rule gives for uniforms within BAND of the
+  ones passed in: oracle.explain() evaluates the rule along the GPU's outcome
+  (its accepted drafts, its rejection, its final token), and the outcome is
+  accepted only if every accept test it passed has u_j < a_j + BAND, the test
+  it failed has u_j >= a_j - BAND, and the final uniform lies within BAND of
+  the final token's CDF bin [lo, hi) (a bin of positive width).  Such rows are
+  counted as mismatch_in_band, per sampler class; greedy rows use no uniform
+  and must always match;
 * invalid rows (-1) must match exactly; rows the GPU build does not serve
   (-2) are counted and skipped;
 * probabilities reported in the diagnostics (p(x), q(x), a, and the drawn
-  token's final-distribution probability and bin edges) must agree within
-  PROB_TOL absolute on rows whose outcome matches.
-Margins come from the oracle (the definition), never from the GPU.
+  token's final-distribution probability and bin edges) agree within
+  PROB_TOL absolute, on matching rows against the oracle's own diagnostics and
+  on in-band rows against explain()'s values along the GPU's outcome.
+Margins and probabilities come from the oracle (the definition), never from
+the GPU.  in_band_rows counts rows whose own outcome the oracle decided with a
+margin below BAND (the rows where a differing outcome can be expected).
 """
 from __future__ import annotations
 
@@ -20,6 +28,7 @@ import numpy as np
 
 BAND = 1e-5
 PROB_TOL = 1e-5
+CLASSES = ("greedy", "top_k", "full", "nucleus")
 
 
 @dataclasses.dataclass
@@ -35,36 +44,72 @@ class Report:
     diag_max_err: float = 0.0
     diag_bad_rows: list = dataclasses.field(default_factory=list)
     min_cut_margin: float = float("inf")
+    rows_by_class: dict = dataclasses.field(default_factory=dict)
+    in_band_by_class: dict = dataclasses.field(default_factory=dict)
+    mismatch_in_band_by_class: dict = dataclasses.field(default_factory=dict)
+    mismatch_in_band_rows: list = dataclasses.field(default_factory=list)
 
     @property
     def ok(self) -> bool:
-        return not self.mismatch_out_of_band and not self.diag_bad_rows
+        return (not self.mismatch_out_of_band and not self.diag_bad_rows
+                and self.mismatch_in_band_by_class.get("greedy", 0) == 0)
 
     def describe(self) -> str:
+        by = " ".join(f"{c}:{self.rows_by_class.get(c, 0)}/{self.in_band_by_class.get(c, 0)}"
+                      f"/{self.mismatch_in_band_by_class.get(c, 0)}" for c in CLASSES)
         return (f"rows={self.rows} compared={self.compared} exact={self.exact} "
                 f"in_band={self.in_band_rows} mismatch_in_band={self.mismatch_in_band} "
                 f"mismatch_out_of_band={len(self.mismatch_out_of_band)} "
                 f"unsupported={self.unsupported} error_rows={self.error_rows} "
                 f"diag_max_err={self.diag_max_err:.3g} diag_bad={len(self.diag_bad_rows)} "
-                f"min_topp_margin={self.min_cut_margin:.3g}")
+                f"min_topp_margin={self.min_cut_margin:.3g} "
+                f"[class rows/in_band/mismatch_in_band: {by}]")
 
 
-def row_in_band(o_diag_row: np.ndarray, K: int) -> bool:
+def row_class(prm, V: int) -> str:
+    T, k, p = float(prm["temperature"]), int(prm["top_k"]), float(prm["top_p"])
+    if T == 0.0:
+        return "greedy"
+    if 0 < k < V:
+        return "top_k"
+    return "nucleus" if p < 1.0 else "full"
+
+
+def row_in_band(o_diag_row: np.ndarray) -> bool:
     m = o_diag_row[:, 3]
     m = m[~np.isnan(m)]
     return bool((m < BAND).any())
 
 
-def compare(g_tok, g_acc, g_diag, ref, rows=None) -> Report:
+def _explained(ex, i, u, L, ga, K) -> bool:
+    """The GPU outcome (accept length ga) of oracle row i is what the rule
+    gives for uniforms within BAND of u (see the module docstring)."""
+    if ex["status"][i] != 0:
+        return False
+    a = ex["a"][i]
+    for j in range(ga):
+        if not u[j] < a[j] + BAND:
+            return False
+    if ga < L and not u[ga] >= a[ga] - BAND:
+        return False
+    lo, hi, py = ex["lo"][i], ex["hi"][i], ex["py"][i]
+    return bool(py > 0.0 and lo - BAND <= u[K] < hi + BAND)
+
+
+def compare(g_tok, g_acc, g_diag, ref, rows=None, *, inputs, oracle_mod) -> Report:
     """Compare GPU outputs (numpy) against oracle outputs ``ref`` (the tuple
-    returned by oracle.verify).  ``rows`` maps oracle rows to GPU rows when the
-    oracle ran on a sample."""
+    returned by oracle.verify).  ``inputs`` holds the arrays the oracle ran on
+    (row i = oracle row i): an object with fields target, draft, tokens,
+    draft_len, params, uniforms and dtype (a workloads.Workload).  ``rows``
+    maps oracle rows to GPU rows when the oracle ran on a subset."""
     o_tok, o_acc, o_diag, o_cut, _ = ref
     if rows is None:
         rows = np.arange(len(o_acc))
     rows = np.asarray(rows)
     K = o_tok.shape[1] - 1
+    V = inputs.target.shape[-1]
     rep = Report(rows=len(rows))
+    pending = []  # (oracle row, GPU row) pairs whose outcomes differ
     for i, b in enumerate(rows):
         ga = int(g_acc[b])
         oa = int(o_acc[i])
@@ -72,32 +117,101 @@ def compare(g_tok, g_acc, g_diag, ref, rows=None) -> Report:
             rep.unsupported += 1
             continue
         rep.compared += 1
+        cls = row_class(inputs.params[i], V)
+        rep.rows_by_class[cls] = rep.rows_by_class.get(cls, 0) + 1
         if np.isfinite(o_cut[i]):
             rep.min_cut_margin = min(rep.min_cut_margin, float(o_cut[i]))
         if oa == -1:
             rep.error_rows += 1
-        same = ga == oa and np.array_equal(g_tok[b], o_tok[i])
-        band = oa >= 0 and row_in_band(o_diag[i], K)
+        band = oa >= 0 and row_in_band(o_diag[i])
         rep.in_band_rows += band
-        if same:
+        if band:
+            rep.in_band_by_class[cls] = rep.in_band_by_class.get(cls, 0) + 1
+        if ga == oa and np.array_equal(g_tok[b], o_tok[i]):
             rep.exact += 1
-        elif band:
-            rep.mismatch_in_band += 1
+            if g_diag is None or oa < 0:
+                continue
+            od, gd = o_diag[i], g_diag[b]
+            ev = ~np.isnan(od[:, 0])
+            if not np.array_equal(ev, ~np.isnan(gd[:, 0])):
+                rep.diag_bad_rows.append(int(b))
+                continue
+            err = np.abs(od[ev][:, :3] - gd[ev][:, :3])
+            e = float(err.max()) if err.size else 0.0
+            rep.diag_max_err = max(rep.diag_max_err, e)
+            if e > PROB_TOL:
+                rep.diag_bad_rows.append(int(b))
             continue
-        else:
+        if oa < 0 or ga < 0 or cls == "greedy":
+            if cls == "greedy" and oa >= 0 and ga >= 0:
+                rep.mismatch_in_band_by_class["greedy"] = \
+                    rep.mismatch_in_band_by_class.get("greedy", 0) + 1
             rep.mismatch_out_of_band.append(int(b))
             continue
-        if g_diag is None or oa < 0:
+        L = int(inputs.draft_len[i]) if inputs.draft_len is not None else K
+        gt = np.asarray(g_tok[b])
+        if (ga > L or not np.array_equal(gt[:ga], inputs.tokens[i][:ga])
+                or not (gt[ga + 1:] == -1).all()):
+            rep.mismatch_out_of_band.append(int(b))
             continue
-        od, gd = o_diag[i], g_diag[b]
-        ev = ~np.isnan(od[:, 0])
-        if not np.array_equal(ev, ~np.isnan(gd[:, 0])):
-            rep.diag_bad_rows.append(int(b))
-            continue
-        cols = [0, 1, 2]
-        err = np.abs(od[ev][:, cols] - gd[ev][:, cols])
-        e = float(err.max()) if err.size else 0.0
-        rep.diag_max_err = max(rep.diag_max_err, e)
-        if e > PROB_TOL:
-            rep.diag_bad_rows.append(int(b))
+        pending.append((i, int(b)))
+    if pending:
+        idx = np.array([p[0] for p in pending])
+        gb = np.array([p[1] for p in pending])
+        ga = np.asarray(g_acc)[gb].astype(np.int32)
+        gy = np.asarray(g_tok)[gb, ga].astype(np.int32)
+        ex = oracle_mod.explain(inputs.target[idx], inputs.draft[idx] if K > 0 else None,
+                                inputs.tokens[idx],
+                                inputs.draft_len[idx] if inputs.draft_len is not None else None,
+                                inputs.params[idx], ga, gy, dtype=inputs.dtype)
+        for n, (i, b) in enumerate(pending):
+            L = int(inputs.draft_len[i]) if inputs.draft_len is not None else K
+            cls = row_class(inputs.params[i], V)
+            if not _explained(ex, n, np.asarray(inputs.uniforms[i], np.float64), L, int(ga[n]),
+                              K):
+                rep.mismatch_out_of_band.append(b)
+                continue
+            rep.mismatch_in_band += 1
+            rep.mismatch_in_band_rows.append(b)
+            rep.mismatch_in_band_by_class[cls] = rep.mismatch_in_band_by_class.get(cls, 0) + 1
+            if g_diag is None:
+                continue
+            gd = g_diag[b]
+            ev = min(int(ga[n]), L - 1) + 1
+            want = np.concatenate([np.stack([ex["px"][n, :ev], ex["qx"][n, :ev],
+                                             ex["a"][n, :ev]], axis=1).reshape(-1),
+                                   [ex["py"][n], ex["lo"][n], ex["hi"][n]]])
+            got = np.concatenate([gd[:ev, :3].reshape(-1), gd[K, :3]])
+            e = float(np.max(np.abs(want - got))) if want.size else 0.0
+            if not np.isfinite(e) or e > PROB_TOL:
+                rep.diag_bad_rows.append(b)
+            else:
+                rep.diag_max_err = max(rep.diag_max_err, e)
     return rep
+
+
+def draws(rows, params, uniforms, dtype):
+    """One draw per row (K = 0) from logits rows [B, V], as an object
+    compare() takes."""
+    import types
+
+    rows = np.asarray(rows)
+    B, V = rows.shape
+    return types.SimpleNamespace(target=rows.reshape(B, 1, V), draft=None,
+                                 tokens=np.zeros((B, 0), np.int32), draft_len=None,
+                                 params=np.asarray(params),
+                                 uniforms=np.asarray(uniforms, np.float32).reshape(B, 1),
+                                 dtype=dtype, B=B, K=0, V=V)
+
+
+def subset(wl, rows):
+    """The rows ``rows`` of a workload, as an object compare() takes."""
+    import copy
+
+    rows = np.asarray(rows)
+    s = copy.copy(wl)
+    s.target, s.draft = wl.target[rows], wl.draft[rows]
+    s.tokens, s.params, s.uniforms = wl.tokens[rows], wl.params[rows], wl.uniforms[rows]
+    s.draft_len = wl.draft_len[rows] if wl.draft_len is not None else None
+    s.B = len(rows)
+    return s

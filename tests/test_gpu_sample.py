@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 from rejection_sampling_verify_sv_amd import workloads
-from tests.parity import compare
+from tests.parity import compare, draws, subset
 
 pytestmark = pytest.mark.gpu
 
@@ -81,8 +81,10 @@ def test_sample_parity(oracle_mod, dev, name, vocab, k):
     _say(f"[gpu] sample {name} B={wl.B} V={wl.V} {wl.dtype} position {k}")
     g_tok, g_st, g_dg = _gpu_sample(rows, wl.params, u, wl.dtype, dev)
     ref = _oracle_draw(oracle_mod, rows, wl.params, u, wl.dtype)
-    rep = compare(g_tok[:, None], g_st, g_dg, ref)
+    rep = compare(g_tok[:, None], g_st, g_dg, ref, inputs=draws(rows, wl.params, u, wl.dtype),
+                  oracle_mod=oracle_mod)
     _say(f"[gpu] sample {name}: {rep.describe()}")
+    assert rep.mismatch_in_band_by_class.get("top_k", 0) == 0, rep.describe()
     assert rep.ok, rep.describe()
     assert rep.unsupported == 0 and rep.compared == wl.B
     # sv_verify with K = 0 is the same launch sequence: identical bits
@@ -115,7 +117,8 @@ def test_sample_edge_rows(oracle_mod, dev):
     u[10] = np.float32(1.0) - np.float32(2.0 ** -24)
     g_tok, g_st, g_dg = _gpu_sample(rows, prm, u, "f32", dev)
     ref = _oracle_draw(oracle_mod, rows, prm, u, "f32")
-    rep = compare(g_tok[:, None], g_st, g_dg, ref)
+    rep = compare(g_tok[:, None], g_st, g_dg, ref, inputs=draws(rows, prm, u, "f32"),
+                  oracle_mod=oracle_mod)
     _say(f"[gpu] sample edges: {rep.describe()}")
     assert rep.ok, rep.describe()
     assert g_st.tolist()[3:6] == [-2, -1, -1]
@@ -143,13 +146,16 @@ def test_draft_then_verify_chain(oracle_mod, dev, name, vocab):
     for k in range(K):
         rows = np.ascontiguousarray(wl.draft[:, k, :])
         gt, gs, _ = _gpu_sample(rows, wl.params, np.ascontiguousarray(v[:, k]), wl.dtype, dev)
-        ot, oa, od, _, _ = _oracle_draw(oracle_mod, rows, wl.params, np.ascontiguousarray(v[:, k]),
-                                        wl.dtype)
+        vk = np.ascontiguousarray(v[:, k])
+        ref_k = _oracle_draw(oracle_mod, rows, wl.params, vk, wl.dtype)
+        ot, oa = ref_k[0], ref_k[1]
         assert (gs == 0).all() and (oa == 0).all()
         g_x[:, k], o_x[:, k] = gt, ot[:, 0]
         diff = gt != ot[:, 0]
-        # a differing draw must have been decided within the band of a CDF edge
-        assert (od[diff, 0, 3] < 1e-5).all(), np.nonzero(diff)[0]
+        # a differing draw must be the rule's draw for a uniform within the band
+        rep_k = compare(gt[:, None], gs, None, ref_k, inputs=draws(rows, wl.params, vk, wl.dtype),
+                        oracle_mod=oracle_mod)
+        assert rep_k.ok, rep_k.describe()
         same &= ~diff
     _say(f"[gpu] chain {name}: {int(same.sum())}/{B} rows drew identical drafts")
     L = np.where(wl.draft_len >= 0, wl.draft_len, K).astype(np.int32)
@@ -162,7 +168,10 @@ def test_draft_then_verify_chain(oracle_mod, dev, name, vocab):
                             dtype=wl.dtype)
     rows = np.nonzero(same)[0]
     ref_same = tuple(r[rows] if isinstance(r, np.ndarray) else r for r in ref)
-    rep = compare(tok.cpu().numpy(), acc.cpu().numpy(), dg.cpu().numpy(), ref_same, rows)
+    wl_o = subset(wl, rows)
+    wl_o.tokens = o_x_used[rows]
+    rep = compare(tok.cpu().numpy(), acc.cpu().numpy(), dg.cpu().numpy(), ref_same, rows,
+                  inputs=wl_o, oracle_mod=oracle_mod)
     _say(f"[gpu] chain {name} verify: {rep.describe()}")
     assert rep.ok, rep.describe()
     assert rep.compared == len(rows) and len(rows) >= B - 2
