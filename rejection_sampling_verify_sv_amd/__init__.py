@@ -7,7 +7,7 @@ truncation (the draft side's sampling step, or plain decoding);
 ``workloads`` builds the seeded synthetic inputs.
 """
 from ._lib import (SV_BF16, SV_F32, SV_MAX_TOP_K, accept_stats, load, params_tensor, sample,
-                   verify, workspace_bytes)
+                   stream_read, verify, workspace_bytes)
 
 __all__ = ["verify", "sample", "accept_stats", "params_tensor", "workspace_bytes", "load",
-           "SV_F32", "SV_BF16", "SV_MAX_TOP_K"]
+           "stream_read", "SV_F32", "SV_BF16", "SV_MAX_TOP_K"]
