@@ -52,8 +52,13 @@ enum {
     SV_OK = 0,
     SV_EINVAL = -1,     /* null required pointer, bad size, dtype or stride   */
     SV_EWORKSPACE = -2, /* workspace missing or smaller than sv_workspace_bytes */
-    SV_EHIP = -3        /* a HIP launch failed; sv_strerror gives the reason   */
+    SV_EHIP = -3,       /* a HIP launch failed; sv_strerror gives the reason   */
+    SV_ESCRATCH = -4    /* sv_verify_noalloc: the shape needs more scratch than
+                           SV_NOALLOC_SCRATCH_BYTES                            */
 };
+
+/* Size of the static device scratch of sv_verify_noalloc (per GPU). */
+#define SV_NOALLOC_SCRATCH_BYTES (128ull << 20)
 
 /* Per-row sampler parameters, 16 bytes, one per batch row (device memory).
  * temperature: 0 = greedy, > 0 finite = sampling; anything else is a row
@@ -135,6 +140,30 @@ int sv_verify_profiled(const void* target_logits, const void* draft_logits,
                        const sv_sampler_params* sampler_params, const float* uniforms,
                        int32_t* out_tokens, int32_t* out_accept_len, const sv_config* cfg,
                        void* const* events, int32_t n_events);
+
+/*
+ * sv_verify for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, semantics and results as sv_verify, except that cfg->workspace
+ * and cfg->workspace_bytes are ignored: the step's scratch lives in a static
+ * device array of SV_NOALLOC_SCRATCH_BYTES (128 MiB) that the library holds on
+ * every GPU it runs on until the process ends.  The call itself allocates
+ * nothing (no hipMalloc, no hipFree; the array's device address is looked up
+ * once per device, on the first call there).  The caller still passes every
+ * input and output buffer.
+ *   Returns SV_ESCRATCH when sv_workspace_bytes(B, K, V, dtype) exceeds
+ *   SV_NOALLOC_SCRATCH_BYTES (nothing is enqueued), otherwise as sv_verify.
+ *   Every call on one GPU shares that GPU's array, which keeps the last
+ *   call's contents: calls that may overlap on one GPU (different streams,
+ *   or host threads without ordering) race and must not be made.
+ */
+int sv_verify_noalloc(const void* target_logits, const void* draft_logits,
+                      const int32_t* draft_tokens, const int32_t* draft_len,
+                      const sv_sampler_params* sampler_params, const float* uniforms,
+                      int32_t* out_tokens, int32_t* out_accept_len, const sv_config* cfg);
+
+/* SV_NOALLOC_SCRATCH_BYTES, as built into the library. */
+size_t sv_noalloc_scratch_bytes(void);
 
 /*
  * Draw one token per row from one row of logits, with the temperature,

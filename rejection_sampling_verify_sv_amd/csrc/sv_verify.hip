@@ -334,6 +334,34 @@ static int verify_impl(const void* target_logits, const void* draft_logits,
                    : launch_all<SV_BF16, false>(draft_len, sampler_params, a, st, ev);
 }
 
+// ---- sv_verify_noalloc: the workspace in a static device array -------------
+// One array per GPU, loaded with the code object and held until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it
+// is only a stand-in for the symbol): its device address is looked up once
+// per device with hipGetSymbolAddress and that pointer is what the kernels
+// get.  Every call on one GPU shares the array; the plan kernel of each call
+// clears the counters that must start at zero.
+static constexpr size_t kNoAllocBytes = SV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocBytes];
+
+static int scratch_for_device(void** out) {
+    static std::mutex mu;
+    static void* ptr[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return SV_EINVAL;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+        ptr[dev] = p;
+    }
+    *out = ptr[dev];
+    return SV_OK;
+}
+
 extern "C" int sv_verify(const void* target_logits, const void* draft_logits,
                          const int32_t* draft_tokens, const int32_t* draft_len,
                          const sv_sampler_params* sampler_params, const float* uniforms,
@@ -341,6 +369,27 @@ extern "C" int sv_verify(const void* target_logits, const void* draft_logits,
     return verify_impl(target_logits, draft_logits, draft_tokens, draft_len, sampler_params,
                        uniforms, out_tokens, out_accept_len, cfg, nullptr);
 }
+
+extern "C" int sv_verify_noalloc(const void* target_logits, const void* draft_logits,
+                                 const int32_t* draft_tokens, const int32_t* draft_len,
+                                 const sv_sampler_params* sampler_params, const float* uniforms,
+                                 int32_t* out_tokens, int32_t* out_accept_len,
+                                 const sv_config* cfg) {
+    if (!cfg) return SV_EINVAL;
+    Plan pl;
+    if (!make_plan(cfg->batch, cfg->max_draft, cfg->vocab, cfg->dtype, &pl)) return SV_EINVAL;
+    if (pl.bytes > kNoAllocBytes) return SV_ESCRATCH;
+    void* ws = nullptr;
+    const int rc = scratch_for_device(&ws);
+    if (rc != SV_OK) return rc;
+    sv_config c = *cfg;
+    c.workspace = ws;
+    c.workspace_bytes = kNoAllocBytes;
+    return verify_impl(target_logits, draft_logits, draft_tokens, draft_len, sampler_params,
+                       uniforms, out_tokens, out_accept_len, &c, nullptr);
+}
+
+extern "C" size_t sv_noalloc_scratch_bytes(void) { return kNoAllocBytes; }
 
 extern "C" int sv_verify_profiled(const void* target_logits, const void* draft_logits,
                                   const int32_t* draft_tokens, const int32_t* draft_len,
@@ -454,6 +503,10 @@ extern "C" const char* sv_strerror(int code) {
             return "workspace missing, misaligned or smaller than sv_workspace_bytes()";
         case SV_EHIP:
             return g_hip_msg[0] ? g_hip_msg : "HIP error";
+        case SV_ESCRATCH:
+            return "shape needs more scratch than sv_verify_noalloc holds "
+                   "(sv_workspace_bytes() > SV_NOALLOC_SCRATCH_BYTES); use sv_verify with a "
+                   "workspace";
         default:
             return "unknown error code";
     }
