@@ -64,6 +64,14 @@ def _load():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
+        lib.sv_oracle_verify_tree.restype = ctypes.c_int
+        lib.sv_oracle_verify_tree.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 9 + [ctypes.c_int]
+        lib.sv_oracle_explain_tree.restype = ctypes.c_int
+        lib.sv_oracle_explain_tree.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 13 + [ctypes.c_int]
         lib.sv_oracle_dist.restype = ctypes.c_int
         lib.sv_oracle_dist.argtypes = [
             ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_double,
@@ -163,6 +171,87 @@ def explain(target, draft, tokens, draft_len, params, acc, y, *, dtype="f32",
         raise ValueError("sv_oracle_explain rejected its arguments")
     for n in ("a", "px", "qx"):
         out[n] = out[n][:, :K]
+    return out
+
+
+def _tree_args(target, draft, tok, par, n_cand, params, dtype):
+    code = {"f32": 0, "bf16": 1}[dtype]
+    target = np.ascontiguousarray(target)
+    B, K1, V = target.shape
+    K = K1 - 1
+    want = np.float32 if code == 0 else np.uint16
+    if target.dtype != want:
+        raise TypeError(f"target must be {want.__name__} for dtype={dtype}")
+    draft = np.ascontiguousarray(draft) if K > 0 else None
+    if draft is not None and (draft.shape != (B, K, V) or draft.dtype != want):
+        raise TypeError("draft must be [B, K, V] of the same dtype as target")
+    tok = np.ascontiguousarray(tok, dtype=np.int32).reshape(B, K)
+    par = np.ascontiguousarray(par, dtype=np.int32).reshape(B, K)
+    if K == 0:
+        tok = np.zeros((B, 1), np.int32)
+        par = np.zeros((B, 1), np.int32)
+    if n_cand is not None:
+        n_cand = np.ascontiguousarray(n_cand, dtype=np.int32).reshape(B)
+    params = np.ascontiguousarray(params)
+    if params.dtype != PARAMS_DTYPE or params.shape != (B,):
+        raise TypeError("params must be [B] of PARAMS_DTYPE")
+    return code, target, draft, tok, par, n_cand, params, B, K, V
+
+
+def verify_tree(target, draft, tokens, parents, n_cand, params, uniforms, *, dtype="f32",
+                nthreads: int = 0):
+    """Tree / multi-candidate verify on host arrays (see sv_oracle_verify_tree
+    in sv_oracle.c for the rule, readings R17-R20).
+
+    target [B, K+1, V] (row v = node v), draft [B, K, V] (row v = node v < K),
+    tokens / parents [B, K] int32 (entry c-1 = candidate node c; parent in
+    [0, c)), n_cand [B] in [0, K] or None, params [B] PARAMS_DTYPE,
+    uniforms [B, K+1] float32 (column c-1 tests node c, column K the final
+    draw).  Returns (out_tokens [B, K+1], out_len [B] (accepted path length,
+    -1 invalid row), out_path [B, K+1] (accepted nodes, -1 padded),
+    diag [B, K+1, 4], threads_used)."""
+    lib = _load()
+    code, target, draft, tok, par, n_cand, params, B, K, V = _tree_args(
+        target, draft, tokens, parents, n_cand, params, dtype)
+    uniforms = np.ascontiguousarray(uniforms, dtype=np.float32).reshape(B, K + 1)
+    out_tok = np.empty((B, K + 1), np.int32)
+    out_len = np.empty(B, np.int32)
+    out_path = np.empty((B, K + 1), np.int32)
+    diag = np.empty((B, K + 1, 4), np.float64)
+    used = lib.sv_oracle_verify_tree(
+        _ptr(target), _ptr(draft), code, B, K, V, V, V, _ptr(tok), _ptr(par), _ptr(n_cand),
+        _ptr(params), _ptr(uniforms), _ptr(out_tok), _ptr(out_len), _ptr(out_path), _ptr(diag),
+        int(nthreads))
+    if used < 0:
+        raise ValueError("sv_oracle_verify_tree rejected its arguments")
+    return out_tok, out_len, out_path, diag, used
+
+
+def explain_tree(target, draft, tokens, parents, n_cand, params, path, length, y, *,
+                 dtype="f32", nthreads: int = 0):
+    """The tree rule's decisions along given outcomes: accepted nodes
+    ``path[b, :length[b]]`` and final token ``y[b]``.  Returns a dict:
+    ``a`` [B, K] (accept probability of node c's test at [c-1], NaN if the
+    outcome does not test c), ``need`` [B, K] (+1 accepted, -1 rejected, 0
+    untested), ``lo``, ``hi``, ``py`` [B] (y's bin and probability in the final
+    draw) and ``status`` [B] (0, 1 greedy row, -1 invalid row or outcome)."""
+    lib = _load()
+    code, target, draft, tok, par, n_cand, params, B, K, V = _tree_args(
+        target, draft, tokens, parents, n_cand, params, dtype)
+    path = np.ascontiguousarray(path, dtype=np.int32).reshape(B, K + 1)
+    length = np.ascontiguousarray(length, dtype=np.int32).reshape(B)
+    y = np.ascontiguousarray(y, dtype=np.int32).reshape(B)
+    Kc = max(K, 1)
+    out = {"a": np.empty((B, Kc), np.float64), "need": np.empty((B, Kc), np.int32)}
+    out.update({n: np.empty(B, np.float64) for n in ("lo", "hi", "py")})
+    out["status"] = np.empty(B, np.int32)
+    used = lib.sv_oracle_explain_tree(
+        _ptr(target), _ptr(draft), code, B, K, V, V, V, _ptr(tok), _ptr(par), _ptr(n_cand),
+        _ptr(params), _ptr(path), _ptr(length), _ptr(y), _ptr(out["a"]), _ptr(out["need"]),
+        _ptr(out["lo"]), _ptr(out["hi"]), _ptr(out["py"]), _ptr(out["status"]), int(nthreads))
+    if used < 0:
+        raise ValueError("sv_oracle_explain_tree rejected its arguments")
+    out["a"], out["need"] = out["a"][:, :K], out["need"][:, :K]
     return out
 
 

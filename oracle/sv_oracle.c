@@ -527,3 +527,347 @@ int sv_oracle_explain(const void* target, const void* draft, int dtype, int B, i
     }
     return used;
 }
+
+/* ---------------------------------------------------------------------------
+ * Tree / multi-candidate verify.
+ *
+ * [TINYCTO], question "Medusa / Eagle spekülatif taslak mekanizması nedir?":
+ * draft heads propose candidate tokens; the pages give no rule for checking
+ * several candidates at one position.  This oracle takes the reading that
+ * keeps the output law equal to the target's when the candidates at a node
+ * are drawn independently from q at that node: recursive rejection.
+ *   R17 nodes: node 0 is the committed context; node c >= 1 carries the
+ *       candidate token tok[c-1], drawn at its parent par[c-1] < c.  Target
+ *       row v is the target's logits after node v's path, draft row v
+ *       (v < K) the draft's logits there (its children were drawn from it).
+ *   R18 at node v the children c_1 < ... < c_m (ascending node index) are
+ *       tested in turn against r, which starts as p_v: candidate x is
+ *       accepted iff u[c-1] < min(1, r(x) / q_v(x)) (R6 for q_v(x) = 0);
+ *       after a rejection r becomes (r - q_v)+ normalised (unchanged when
+ *       that has no mass, R10).  An accepted child becomes v.
+ *   R19 when every child of v is rejected, or v has none, the final token
+ *       is drawn from r with uniform u[K] (R9): the residual after the
+ *       rejections, p_v itself at a leaf (the bonus token, R11).
+ *   R20 greedy rows accept the first child whose token is the argmax of
+ *       target row v and otherwise emit that argmax.
+ * With one child per node (par[c-1] = c-1) this is or_verify_row exactly.
+ * ------------------------------------------------------------------------- */
+
+/* Children of v among nodes 1..n-1, ascending; returns their number. */
+static int or_children(const int32_t* par, int n, int v, int* out) {
+    int m = 0;
+    for (int c = v + 1; c < n; c++)
+        if (par[c - 1] == v) out[m++] = c;
+    return m;
+}
+
+static int or_tree_row(const void* target, const void* draft, int dtype, int K, int V,
+                       int64_t t_stride, int64_t d_stride, int b, const int32_t* tok,
+                       const int32_t* par, int n_cand, const or_params* prm, const float* u,
+                       int32_t* out_tok, int32_t* out_path, double* diag, or_scratch* s,
+                       int* kids) {
+    for (int k = 0; k <= K; k++) out_tok[k] = -1;
+    if (out_path)
+        for (int k = 0; k <= K; k++) out_path[k] = -1;
+    if (diag) or_fill_nan(diag, 4 * (K + 1));
+    const double T = (double)prm->temperature;
+    const double top_p = (double)prm->top_p;
+    if (!(T >= 0.0) || !(T < INFINITY) || !(top_p > 0.0)) return -1;
+    if (n_cand < 0 || n_cand > K) return -1;
+    const int n = n_cand + 1;
+    for (int c = 1; c < n; c++)
+        if (par[c - 1] < 0 || par[c - 1] >= c || tok[c - 1] < 0 || tok[c - 1] >= V) return -1;
+    const size_t trow0 = (size_t)b * (size_t)(K + 1);
+    const size_t drow0 = (size_t)b * (size_t)K;
+    int v = 0, depth = 0;
+    for (;;) {
+        const int m = or_children(par, n, v, kids);
+        or_load_row(target, dtype, (trow0 + (size_t)v) * (size_t)t_stride, V, s->logit);
+        if (T == 0.0) { /* R20 */
+            const int g = or_argmax(s->logit, V);
+            int next = -1;
+            for (int i = 0; i < m && next < 0; i++)
+                if (tok[kids[i] - 1] == g) next = kids[i];
+            if (next < 0) {
+                out_tok[depth] = g;
+                return depth;
+            }
+            out_tok[depth] = g;
+            if (out_path) out_path[depth] = next;
+            depth++;
+            v = next;
+            continue;
+        }
+        double cm;
+        if (or_dist(s->logit, V, T, prm->top_k, top_p, s->items, s->w, s->p, &cm) != 0) return -1;
+        /* r = p_v, kept in s->r */
+        for (int i = 0; i < V; i++) s->r[i] = s->p[i];
+        int next = -1;
+        if (m > 0) {
+            or_load_row(draft, dtype, (drow0 + (size_t)v) * (size_t)d_stride, V, s->logit);
+            if (or_dist(s->logit, V, T, prm->top_k, top_p, s->items, s->w, s->q, &cm) != 0)
+                return -1;
+            for (int i = 0; i < m && next < 0; i++) { /* R18 */
+                const int c = kids[i];
+                const int x = tok[c - 1];
+                const double rx = s->r[x], qx = s->q[x];
+                double a;
+                if (qx > 0.0) {
+                    a = rx / qx;
+                    if (a > 1.0) a = 1.0;
+                } else {
+                    a = (rx > 0.0) ? 1.0 : 0.0;
+                }
+                const double uc = (double)u[c - 1];
+                if (diag) {
+                    diag[4 * (c - 1) + 0] = rx;
+                    diag[4 * (c - 1) + 1] = qx;
+                    diag[4 * (c - 1) + 2] = a;
+                    diag[4 * (c - 1) + 3] = fabs(uc - a);
+                }
+                if (uc < a) {
+                    next = c;
+                    break;
+                }
+                double W = 0.0;
+                for (int e = 0; e < V; e++) {
+                    const double d = s->r[e] - s->q[e];
+                    s->w[e] = d > 0.0 ? d : 0.0;
+                    W += s->w[e];
+                }
+                if (W > 0.0)
+                    for (int e = 0; e < V; e++) s->r[e] = s->w[e] / W;
+            }
+        }
+        if (next >= 0) {
+            out_tok[depth] = tok[next - 1];
+            if (out_path) out_path[depth] = next;
+            depth++;
+            v = next;
+            continue;
+        }
+        /* R19 */
+        double lo, hi, mg;
+        const int y = or_invcdf(s->r, V, (double)u[K], &lo, &hi, &mg);
+        out_tok[depth] = y;
+        if (diag) {
+            double Wn = 0.0;
+            for (int e = 0; e < V; e++) Wn += s->r[e];
+            diag[4 * K + 0] = s->r[y] / Wn;
+            diag[4 * K + 1] = lo;
+            diag[4 * K + 2] = hi;
+            diag[4 * K + 3] = mg;
+        }
+        return depth;
+    }
+}
+
+/*
+ * Batch entry point of the tree verify (host pointers), laid out like
+ * sv_oracle_verify with K candidate nodes per row:
+ *   target [B][K+1] rows (row v = node v), draft [B][K] rows (row v = node v,
+ *   v < K); tok, par [B][K] (entry c-1 = node c); n_cand [B] in [0, K] or
+ *   NULL (= K): nodes 1..n_cand are used; params [B]; uniforms [B][K+1]
+ *   (column c-1 = the test of node c, column K = the final draw).
+ *   out_tokens [B][K+1]: the accepted path's tokens, then the final token
+ *   (the greedy argmax on greedy rows), then -1; out_len [B]: the accepted
+ *   path's length (-1: invalid row); out_path [B][K+1] or NULL: the accepted
+ *   nodes, -1 padded; diag [B][K+1][4] or NULL: slot c-1 = (r(x), q(x), a,
+ *   |u - a|) of node c's test, slot K = the final draw as in
+ *   sv_oracle_verify.
+ * Returns the number of threads used, or -1 on a null required pointer.
+ */
+int sv_oracle_verify_tree(const void* target, const void* draft, int dtype, int B, int K, int V,
+                          int64_t t_stride, int64_t d_stride, const int32_t* tok,
+                          const int32_t* par, const int32_t* n_cand, const void* params,
+                          const float* uniforms, int32_t* out_tokens, int32_t* out_len,
+                          int32_t* out_path, double* diag, int nthreads) {
+    if (!target || !tok || !par || !params || !uniforms || !out_tokens || !out_len) return -1;
+    if (K > 0 && !draft) return -1;
+    if (B <= 0 || K < 0 || V < 1 || t_stride < V || (K > 0 && d_stride < V)) return -1;
+    const or_params* prm = (const or_params*)params;
+    int used = 1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+#pragma omp parallel
+    {
+#ifdef _OPENMP
+#pragma omp single
+        used = omp_get_num_threads();
+#endif
+        or_scratch s;
+        s.logit = (double*)malloc(sizeof(double) * (size_t)V);
+        s.items = (or_item*)malloc(sizeof(or_item) * (size_t)V);
+        s.w = (double*)malloc(sizeof(double) * (size_t)V);
+        s.p = (double*)malloc(sizeof(double) * (size_t)V);
+        s.q = (double*)malloc(sizeof(double) * (size_t)V);
+        s.r = (double*)malloc(sizeof(double) * (size_t)V);
+        int* kids = (int*)malloc(sizeof(int) * (size_t)(K + 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int b = 0; b < B; b++) {
+            const int nc = n_cand ? n_cand[b] : K;
+            int32_t* ot = out_tokens + (size_t)b * (size_t)(K + 1);
+            int32_t* op = out_path ? out_path + (size_t)b * (size_t)(K + 1) : NULL;
+            double* dg = diag ? diag + (size_t)b * 4 * (size_t)(K + 1) : NULL;
+            const int d = or_tree_row(target, draft, dtype, K, V, t_stride, d_stride, b,
+                                      tok + (size_t)b * (size_t)K, par + (size_t)b * (size_t)K,
+                                      nc, prm + b, uniforms + (size_t)b * (size_t)(K + 1), ot, op,
+                                      dg, &s, kids);
+            if (d < 0) {
+                for (int k = 0; k <= K; k++) ot[k] = -1;
+                if (op)
+                    for (int k = 0; k <= K; k++) op[k] = -1;
+                if (dg) or_fill_nan(dg, 4 * (K + 1));
+            }
+            out_len[b] = d;
+        }
+        free(s.logit);
+        free(s.items);
+        free(s.w);
+        free(s.p);
+        free(s.q);
+        free(s.r);
+        free(kids);
+    }
+    return used;
+}
+
+/*
+ * The tree rule's decisions along one given outcome (the tree counterpart of
+ * or_explain_row): the accepted path path[0..len-1] (node indices) and the
+ * final token y.  For every test the outcome implies, at node c: a_out[c-1]
+ * = min(1, r(x)/q(x)) and need[c-1] = +1 (the outcome accepts c) or -1 (it
+ * rejects c); need = 0 for nodes the outcome does not test.  *lo, *hi, *py:
+ * y's bin in the final draw (R19) and its probability.  Returns 0, 1 for a
+ * greedy row, -1 for an invalid row or an outcome that is not a path of
+ * children from node 0.
+ */
+static int or_explain_tree_row(const void* target, const void* draft, int dtype, int K, int V,
+                               int64_t t_stride, int64_t d_stride, int b, const int32_t* tok,
+                               const int32_t* par, int n_cand, const or_params* prm,
+                               const int32_t* path, int len, int y, double* a_out, int32_t* need,
+                               double* lo, double* hi, double* py, or_scratch* s, int* kids) {
+    or_fill_nan(a_out, K);
+    for (int k = 0; k < K; k++) need[k] = 0;
+    *lo = *hi = *py = NAN;
+    const double T = (double)prm->temperature;
+    const double top_p = (double)prm->top_p;
+    if (!(T >= 0.0) || !(T < INFINITY) || !(top_p > 0.0)) return -1;
+    if (n_cand < 0 || n_cand > K) return -1;
+    const int n = n_cand + 1;
+    for (int c = 1; c < n; c++)
+        if (par[c - 1] < 0 || par[c - 1] >= c || tok[c - 1] < 0 || tok[c - 1] >= V) return -1;
+    if (T == 0.0) return 1;
+    if (len < 0 || len > K || y < 0 || y >= V) return -1;
+    const size_t trow0 = (size_t)b * (size_t)(K + 1);
+    const size_t drow0 = (size_t)b * (size_t)K;
+    int v = 0;
+    double cm;
+    for (int d = 0; d <= len; d++) {
+        const int m = or_children(par, n, v, kids);
+        const int want = d < len ? path[d] : -1;
+        or_load_row(target, dtype, (trow0 + (size_t)v) * (size_t)t_stride, V, s->logit);
+        if (or_dist(s->logit, V, T, prm->top_k, top_p, s->items, s->w, s->p, &cm) != 0) return -1;
+        for (int i = 0; i < V; i++) s->r[i] = s->p[i];
+        int found = 0;
+        if (m > 0) {
+            or_load_row(draft, dtype, (drow0 + (size_t)v) * (size_t)d_stride, V, s->logit);
+            if (or_dist(s->logit, V, T, prm->top_k, top_p, s->items, s->w, s->q, &cm) != 0)
+                return -1;
+            for (int i = 0; i < m; i++) {
+                const int c = kids[i];
+                const int x = tok[c - 1];
+                const double rx = s->r[x], qx = s->q[x];
+                double a;
+                if (qx > 0.0) {
+                    a = rx / qx;
+                    if (a > 1.0) a = 1.0;
+                } else {
+                    a = (rx > 0.0) ? 1.0 : 0.0;
+                }
+                a_out[c - 1] = a;
+                if (c == want) {
+                    need[c - 1] = 1;
+                    found = 1;
+                    break;
+                }
+                need[c - 1] = -1;
+                double W = 0.0;
+                for (int e = 0; e < V; e++) {
+                    const double dd = s->r[e] - s->q[e];
+                    s->w[e] = dd > 0.0 ? dd : 0.0;
+                    W += s->w[e];
+                }
+                if (W > 0.0)
+                    for (int e = 0; e < V; e++) s->r[e] = s->w[e] / W;
+            }
+        }
+        if (d < len) {
+            if (!found) return -1;
+            v = want;
+            continue;
+        }
+        double W = 0.0, before = 0.0;
+        for (int e = 0; e < V; e++) {
+            if (e == y) before = W;
+            W += s->r[e];
+        }
+        *lo = before / W;
+        *hi = (before + s->r[y]) / W;
+        *py = s->r[y] / W;
+    }
+    return 0;
+}
+
+/* Batch form: path [B][K+1] (the outcome's nodes, -1 padded), len [B], y [B];
+ * a_out [B][K], need [B][K]; lo, hi, py [B]; status [B]. */
+int sv_oracle_explain_tree(const void* target, const void* draft, int dtype, int B, int K, int V,
+                           int64_t t_stride, int64_t d_stride, const int32_t* tok,
+                           const int32_t* par, const int32_t* n_cand, const void* params,
+                           const int32_t* path, const int32_t* len, const int32_t* y,
+                           double* a_out, int32_t* need, double* lo, double* hi, double* py,
+                           int32_t* status, int nthreads) {
+    if (!target || !tok || !par || !params || !path || !len || !y || !a_out || !need || !lo ||
+        !hi || !py || !status)
+        return -1;
+    if (K > 0 && !draft) return -1;
+    if (B <= 0 || K < 0 || V < 1 || t_stride < V || (K > 0 && d_stride < V)) return -1;
+    const or_params* prm = (const or_params*)params;
+    int used = 1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+#pragma omp parallel
+    {
+#ifdef _OPENMP
+#pragma omp single
+        used = omp_get_num_threads();
+#endif
+        or_scratch s;
+        s.logit = (double*)malloc(sizeof(double) * (size_t)V);
+        s.items = (or_item*)malloc(sizeof(or_item) * (size_t)V);
+        s.w = (double*)malloc(sizeof(double) * (size_t)V);
+        s.p = (double*)malloc(sizeof(double) * (size_t)V);
+        s.q = (double*)malloc(sizeof(double) * (size_t)V);
+        s.r = (double*)malloc(sizeof(double) * (size_t)V);
+        int* kids = (int*)malloc(sizeof(int) * (size_t)(K + 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int b = 0; b < B; b++) {
+            const int nc = n_cand ? n_cand[b] : K;
+            status[b] = or_explain_tree_row(
+                target, draft, dtype, K, V, t_stride, d_stride, b, tok + (size_t)b * (size_t)K,
+                par + (size_t)b * (size_t)K, nc, prm + b, path + (size_t)b * (size_t)(K + 1),
+                len[b], y[b], a_out + (size_t)b * (size_t)K, need + (size_t)b * (size_t)K, lo + b,
+                hi + b, py + b, &s, kids);
+        }
+        free(s.logit);
+        free(s.items);
+        free(s.w);
+        free(s.p);
+        free(s.q);
+        free(s.r);
+        free(kids);
+    }
+    return used;
+}

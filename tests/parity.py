@@ -215,3 +215,112 @@ def subset(wl, rows):
     s.draft_len = wl.draft_len[rows] if wl.draft_len is not None else None
     s.B = len(rows)
     return s
+
+
+def compare_tree(g_tok, g_len, g_path, g_diag, ref, *, inputs, oracle_mod) -> Report:
+    """Tree verify: compare GPU outputs with oracle.verify_tree's ``ref``
+    (out_tokens, out_len, out_path, diag, threads) under the same rules as
+    compare(): identical tokens, lengths and paths, except outcomes that
+    oracle.explain_tree shows the rule gives for uniforms within BAND of the
+    given ones (the accepted nodes' tests u < a + BAND, the rejected
+    siblings' u >= a - BAND, the final draw within BAND of its bin).
+    ``inputs``: target, draft, tokens, parents, n_cand, params, uniforms,
+    dtype."""
+    o_tok, o_len, o_path, o_diag, _ = ref
+    K = o_tok.shape[1] - 1
+    V = inputs.target.shape[-1]
+    B = len(o_len)
+    rep = Report(rows=B)
+    pending = []
+    for b in range(B):
+        gl, ol = int(g_len[b]), int(o_len[b])
+        if gl == -2:
+            rep.unsupported += 1
+            continue
+        rep.compared += 1
+        cls = row_class(inputs.params[b], V)
+        rep.rows_by_class[cls] = rep.rows_by_class.get(cls, 0) + 1
+        if ol == -1:
+            rep.error_rows += 1
+        band = ol >= 0 and row_in_band(o_diag[b])
+        rep.in_band_rows += band
+        if band:
+            rep.in_band_by_class[cls] = rep.in_band_by_class.get(cls, 0) + 1
+        if (gl == ol and np.array_equal(g_tok[b], o_tok[b])
+                and np.array_equal(g_path[b], o_path[b])):
+            rep.exact += 1
+            if g_diag is None or ol < 0:
+                continue
+            od, gd = o_diag[b], g_diag[b]
+            ev = ~np.isnan(od[:, 0])
+            if not np.array_equal(ev, ~np.isnan(gd[:, 0])):
+                rep.diag_bad_rows.append(b)
+                continue
+            err = np.abs(od[ev][:, :3] - gd[ev][:, :3])
+            e = float(err.max()) if err.size else 0.0
+            rep.diag_max_err = max(rep.diag_max_err, e)
+            if e > PROB_TOL:
+                rep.diag_bad_rows.append(b)
+            continue
+        if ol < 0 or gl < 0 or cls == "greedy":
+            if cls == "greedy" and ol >= 0 and gl >= 0:
+                rep.mismatch_in_band_by_class["greedy"] = \
+                    rep.mismatch_in_band_by_class.get("greedy", 0) + 1
+            rep.mismatch_out_of_band.append(b)
+            continue
+        gp = np.asarray(g_path[b])
+        gt = np.asarray(g_tok[b])
+        well_formed = (gl <= K and (gp[gl:] == -1).all() and (gt[gl + 1:] == -1).all()
+                       and all(0 < gp[i] <= K and gt[i] == inputs.tokens[b][gp[i] - 1]
+                               for i in range(gl)))
+        if not well_formed:
+            rep.mismatch_out_of_band.append(b)
+            continue
+        pending.append(b)
+    if pending:
+        idx = np.array(pending)
+        ex = oracle_mod.explain_tree(
+            inputs.target[idx], inputs.draft[idx] if K > 0 else None, inputs.tokens[idx],
+            inputs.parents[idx], inputs.n_cand[idx] if inputs.n_cand is not None else None,
+            inputs.params[idx], np.asarray(g_path)[idx], np.asarray(g_len)[idx],
+            np.asarray(g_tok)[idx, np.asarray(g_len)[idx]], dtype=inputs.dtype)
+        for n, b in enumerate(pending):
+            u = np.asarray(inputs.uniforms[b], np.float64)
+            a, need = ex["a"][n], ex["need"][n]
+            ok = ex["status"][n] == 0
+            for c in range(K):
+                if need[c] == 1 and not u[c] < a[c] + BAND:
+                    ok = False
+                if need[c] == -1 and not u[c] >= a[c] - BAND:
+                    ok = False
+            ok = ok and ex["py"][n] > 0 and ex["lo"][n] - BAND <= u[K] < ex["hi"][n] + BAND
+            cls = row_class(inputs.params[b], V)
+            if not ok:
+                rep.mismatch_out_of_band.append(b)
+                continue
+            rep.mismatch_in_band += 1
+            rep.mismatch_in_band_rows.append(b)
+            rep.mismatch_in_band_by_class[cls] = rep.mismatch_in_band_by_class.get(cls, 0) + 1
+            if g_diag is None:
+                continue
+            gd = g_diag[b]
+            tested = need != 0
+            want = np.concatenate([a[tested], [ex["py"][n], ex["lo"][n], ex["hi"][n]]])
+            got = np.concatenate([gd[:K][tested, 2], gd[K, :3]])
+            e = float(np.max(np.abs(want - got))) if want.size else 0.0
+            if not np.isfinite(e) or e > PROB_TOL:
+                rep.diag_bad_rows.append(b)
+            else:
+                rep.diag_max_err = max(rep.diag_max_err, e)
+    return rep
+
+
+def tree_inputs(target, draft, tokens, parents, n_cand, params, uniforms, dtype):
+    """The inputs of a tree verify, as an object compare_tree() takes."""
+    import types
+
+    return types.SimpleNamespace(target=target, draft=draft, tokens=np.asarray(tokens),
+                                 parents=np.asarray(parents),
+                                 n_cand=None if n_cand is None else np.asarray(n_cand),
+                                 params=np.asarray(params), uniforms=np.asarray(uniforms),
+                                 dtype=dtype)

@@ -143,3 +143,63 @@ def test_invalid_or_malformed_outcomes_fail(oracle_mod, field):
         tok[b, 0] = (wl.tokens[b, 0] + 1) % wl.V
     rep = compare(tok, acc, None, ref, inputs=wl, oracle_mod=oracle_mod)
     assert not rep.ok and b in rep.mismatch_out_of_band
+
+
+def _tree_case(oracle_mod, seed=0, B=40, K=5, V=200):
+    from tests.parity import tree_inputs
+
+    rng = np.random.default_rng(seed)
+    t = rng.normal(0, 2.0, (B, K + 1, V))
+    d = 0.8 * t[:, :K] + rng.normal(0, 0.8, (B, K, V))
+    prm = np.zeros(B, PARAMS_DTYPE)
+    prm["temperature"] = np.where(np.arange(B) % 5 == 4, 0.0, 1.0)
+    prm["top_k"] = np.where(np.arange(B) % 3 == 0, 20, 0)
+    prm["top_p"] = np.where(np.arange(B) % 3 == 1, 0.9, 1.0)
+    par = np.zeros((B, K), np.int32)
+    tok = np.zeros((B, K), np.int32)
+    for b in range(B):
+        for c in range(1, K + 1):
+            par[b, c - 1] = rng.integers(0, c)
+            tok[b, c - 1] = int(np.argsort(-d[b, par[b, c - 1]])[rng.integers(0, 3)])
+    u = rng.random((B, K + 1), dtype=np.float32)
+    wl = workloads.custom(t, d, tok, np.full(B, K, np.int32), prm, u)
+    inp = tree_inputs(wl.target, wl.draft, wl.tokens, par, wl.draft_len, wl.params,
+                      wl.uniforms, "f32")
+    ref = oracle_mod.verify_tree(wl.target, wl.draft, wl.tokens, par, wl.draft_len, wl.params,
+                                 wl.uniforms)
+    return inp, ref
+
+
+def test_tree_rule(oracle_mod):
+    from tests.parity import compare_tree
+
+    inp, ref = _tree_case(oracle_mod)
+    tok, ln, path, dg = (x.copy() for x in ref[:4])
+    rep = compare_tree(tok, ln, path, dg, ref, inputs=inp, oracle_mod=oracle_mod)
+    assert rep.ok and rep.exact == rep.compared
+    K = tok.shape[1] - 1
+    # a sampling row: move its final uniform just past the top of its drawn
+    # token's bin; the outcome before the move is then explained in band,
+    # 5 bands away it is not
+    b = next(b for b in range(len(ln)) if inp.params["temperature"][b] > 0
+             and ref[3][b, K, 2] < 0.99)
+    hi = ref[3][b, K, 2]
+    for move, explained in ((0.5 * BAND, True), (5 * BAND, False)):
+        inp.uniforms[b, K] = np.float32(hi + move)
+        ref2 = oracle_mod.verify_tree(inp.target, inp.draft, inp.tokens, inp.parents, inp.n_cand,
+                                      inp.params, inp.uniforms)
+        assert ref2[0][b, ref2[1][b]] != ref[0][b, ref[1][b]]
+        g = [x.copy() for x in ref2[:4]]
+        for x, y in zip(g, ref[:4]):
+            x[b] = y[b]
+        rep = compare_tree(*g, ref2, inputs=inp, oracle_mod=oracle_mod)
+        if explained:
+            assert rep.ok and rep.mismatch_in_band_rows == [b], rep.describe()
+        else:
+            assert rep.mismatch_out_of_band == [b]
+    # a path that is not made of children, or a greedy row that differs, fails
+    g = [x.copy() for x in ref[:4]]
+    gb = int(np.flatnonzero(inp.params["temperature"] == 0)[0])
+    g[0][gb, g[1][gb]] = (g[0][gb, g[1][gb]] + 1) % inp.target.shape[-1]
+    rep = compare_tree(*g, ref, inputs=inp, oracle_mod=oracle_mod)
+    assert gb in rep.mismatch_out_of_band and not rep.ok
