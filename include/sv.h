@@ -142,6 +142,57 @@ int sv_verify_profiled(const void* target_logits, const void* draft_logits,
                        void* const* events, int32_t n_events);
 
 /*
+ * Tree / multi-candidate verify: draft heads that propose several candidate
+ * tokens per position (tinycto.tv "Spekülatif Kod Çözme (Speculative
+ * Decoding)…", question "Medusa / Eagle spekülatif taslak mekanizması nedir?";
+ * the pages give no checking rule).  Reading: the candidates at a node are
+ * drawn independently from the draft distribution q there, and the node's
+ * children are tested in ascending node order by recursive rejection, child
+ * x against the residual r left by the children rejected before it
+ * (r = p at first, r <- (r - q)+ normalised after each rejection, unchanged
+ * when that has no mass), accepting with min(1, r(x)/q(x)) (q(x) = 0: accept
+ * iff r(x) > 0).  An accepted child becomes the current node; when every
+ * child is rejected, or the node has none, the final token is drawn from r
+ * by the inverse CDF in ascending token id.  Greedy rows take the first child
+ * whose token is the target argmax.  With one child per node this is
+ * sv_verify exactly (same arguments, parents[c-1] = c - 1).
+ *
+ * Node 0 is the committed context; nodes 1..K are candidates.
+ *   target_logits  [B][K+1] rows: row v = the target's logits after node v
+ *   draft_logits   [B][K] rows: row v = the draft's logits at node v (its
+ *                  children were drawn from them); may be NULL when K = 0
+ *   node_tokens    [B][K] int32: entry c-1 = candidate token of node c
+ *   node_parents   [B][K] int32: entry c-1 = parent of node c, in [0, c)
+ *   n_cand         [B] int32 in [0, K]: nodes 1..n_cand[b] are used; NULL = K
+ *   sampler_params [B]; the same temperature / top_k / top_p on both sides
+ *   uniforms       [B][K+1] fp32 in [0, 1): column c-1 is node c's test,
+ *                  column K the final draw
+ *   out_tokens     [B][K+1] int32: the accepted path's tokens, then the drawn
+ *                  token (the argmax on greedy rows), then -1
+ *   out_accept_len [B] int32: length of the accepted path; -1 invalid row
+ *                  (as sv_verify, and: a parent outside [0, c), a node deeper
+ *                  than max_depth, a node with more than max_children
+ *                  children), -2 unsupported top_k
+ *   out_path       [B][K+1] int32 or NULL: the accepted nodes, -1 padded
+ *   max_depth      0 <= max_depth <= K: levels the call walks
+ *   max_children   1 <= max_children <= 64 (K > 0): children per node; a
+ *                  full-vocabulary row (top_k off) needs one pass over the
+ *                  node's two rows per rejected child beyond the first
+ *   cfg            as for sv_verify; diag, if set, is [B][K+1][4] fp64 with
+ *                  slot c-1 = (r(x), q(x), a, |u - a|) of node c's test and
+ *                  slot K = the final draw, NaN elsewhere.
+ * Returns SV_OK once enqueued, SV_EINVAL (also for max_depth / max_children
+ * out of range), SV_EWORKSPACE, SV_EHIP.  Ownership, ordering and
+ * determinism as for sv_verify.
+ */
+int sv_verify_tree(const void* target_logits, const void* draft_logits,
+                   const int32_t* node_tokens, const int32_t* node_parents,
+                   const int32_t* n_cand, const sv_sampler_params* sampler_params,
+                   const float* uniforms, int32_t* out_tokens, int32_t* out_accept_len,
+                   int32_t* out_path, int32_t max_depth, int32_t max_children,
+                   const sv_config* cfg);
+
+/*
  * sv_verify for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
  * arguments, semantics and results as sv_verify, except that cfg->workspace

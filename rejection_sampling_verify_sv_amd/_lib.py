@@ -18,10 +18,10 @@ LIB_PATH = os.path.join(_HERE, "libsv.so")
 
 SV_F32, SV_BF16 = 0, 1
 SV_MAX_TOP_K = 64
-ERRORS = {0: "SV_OK", -1: "SV_EINVAL", -2: "SV_EWORKSPACE", -3: "SV_EHIP"}
+ERRORS = {0: "SV_OK", -1: "SV_EINVAL", -2: "SV_EWORKSPACE", -3: "SV_EHIP", -4: "SV_ESCRATCH"}
 EXPORTED = ("sv_verify", "sv_verify_profiled", "sv_sample", "sv_accept_stats",
             "sv_workspace_bytes", "sv_strerror", "sv_launch_count", "sv_launch_name",
-            "sv_stream_read")
+            "sv_stream_read", "sv_verify_tree", "sv_verify_noalloc", "sv_noalloc_scratch_bytes")
 
 
 class SvConfig(ctypes.Structure):
@@ -65,6 +65,12 @@ def load() -> ctypes.CDLL:
         lib.sv_strerror.argtypes = [ctypes.c_int]
         lib.sv_launch_count.restype = ctypes.c_int32
         lib.sv_launch_count.argtypes = [ctypes.c_int32]
+        lib.sv_verify_tree.restype = ctypes.c_int
+        lib.sv_verify_tree.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int32, ctypes.c_int32]
+                                       + [ctypes.POINTER(SvConfig)])
+        lib.sv_verify_noalloc.restype = ctypes.c_int
+        lib.sv_verify_noalloc.argtypes = [ctypes.c_void_p] * 8 + [ctypes.POINTER(SvConfig)]
+        lib.sv_noalloc_scratch_bytes.restype = ctypes.c_size_t
         lib.sv_stream_read.restype = ctypes.c_int
         lib.sv_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                        ctypes.c_void_p]
@@ -211,6 +217,95 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
             if t is not None:
                 t.record_stream(st)
     return out_tokens, out_accept_len, dg
+
+
+def verify_tree(target: torch.Tensor, draft: torch.Tensor | None, node_tokens: torch.Tensor | None,
+                node_parents: torch.Tensor | None, n_cand: torch.Tensor | None, params,
+                uniforms: torch.Tensor, *, max_depth: int, max_children: int, diag: bool = False,
+                workspace: torch.Tensor | None = None, out_tokens: torch.Tensor | None = None,
+                out_accept_len: torch.Tensor | None = None, out_path: torch.Tensor | None = None,
+                stream: torch.cuda.Stream | None = None):
+    """Enqueue one tree verify (sv_verify_tree); returns (out_tokens,
+    out_accept_len, out_path, diag|None).
+
+    target [B, K+1, V] (row v = node v), draft [B, K, V] (row v = node v):
+    float32 or bfloat16 CUDA tensors.  node_tokens, node_parents [B, K] int32
+    (entry c-1 = candidate node c); n_cand [B] int32 or None; params as in
+    params_tensor(); uniforms [B, K+1] float32 (column c-1 tests node c,
+    column K the final draw).  Nothing is synchronised."""
+    lib = load()
+    if not target.is_cuda:
+        raise RuntimeError("verify_tree needs GPU tensors (no CPU path exists)")
+    dev = target.device
+    if target.dtype == torch.float32:
+        code = SV_F32
+    elif target.dtype == torch.bfloat16:
+        code = SV_BF16
+    else:
+        raise TypeError("logits must be float32 or bfloat16")
+    B, K1, V = target.shape
+    K = K1 - 1
+    target, ts = _rows_layout(target, B * K1)
+    ds = 0
+    if K > 0:
+        if draft is None or draft.dtype != target.dtype or tuple(draft.shape) != (B, K, V):
+            raise ValueError("draft must be [B, K, V] of target's dtype")
+        draft, ds = _rows_layout(draft, B * K)
+    tok = par = None
+    if K > 0:
+        tok = node_tokens.to(dev, torch.int32).contiguous()
+        par = node_parents.to(dev, torch.int32).contiguous()
+        if tuple(tok.shape) != (B, K) or tuple(par.shape) != (B, K):
+            raise ValueError("node_tokens and node_parents must be [B, K]")
+    nc = None
+    if n_cand is not None:
+        nc = n_cand.to(dev, torch.int32).contiguous()
+        if tuple(nc.shape) != (B,):
+            raise ValueError("n_cand must be [B]")
+    prm = params_tensor(params, dev)
+    if prm.shape[0] != B:
+        raise ValueError("params must have B rows")
+    uni = uniforms.to(dev, torch.float32).contiguous()
+    if tuple(uni.shape) != (B, K1):
+        raise ValueError("uniforms must be [B, K+1]")
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K1), dtype=torch.int32, device=dev)
+    if out_accept_len is None:
+        out_accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_path is None:
+        out_path = torch.empty((B, K1), dtype=torch.int32, device=dev)
+    dg = torch.empty((B, K1, 4), dtype=torch.float64, device=dev) if diag else None
+    need = workspace_bytes(B, K, V, code)
+    if need == 0:
+        raise ValueError("invalid shape for sv_verify_tree")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    wptr = workspace.data_ptr()
+    pad = (-wptr) % 256
+    cfg = SvConfig()
+    cfg.batch, cfg.max_draft, cfg.vocab, cfg.dtype = B, K, V, code
+    cfg.target_row_stride, cfg.draft_row_stride = ts, ds
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    cfg.stream = st.cuda_stream
+    cfg.workspace = wptr + pad
+    cfg.workspace_bytes = workspace.numel() * workspace.element_size() - pad
+    cfg.diag = dg.data_ptr() if dg is not None else None
+    rc = lib.sv_verify_tree(target.data_ptr(), draft.data_ptr() if draft is not None else None,
+                            tok.data_ptr() if tok is not None else None,
+                            par.data_ptr() if par is not None else None,
+                            nc.data_ptr() if nc is not None else None, prm.data_ptr(),
+                            uni.data_ptr(), out_tokens.data_ptr(), out_accept_len.data_ptr(),
+                            out_path.data_ptr(), int(max_depth), int(max_children),
+                            ctypes.byref(cfg))
+    if rc != 0:
+        raise RuntimeError(f"sv_verify_tree failed: {ERRORS.get(rc, rc)}: "
+                           f"{lib.sv_strerror(rc).decode()}")
+    if stream is not None:
+        for t in (target, draft, tok, par, nc, prm, uni, workspace, out_tokens, out_accept_len,
+                  out_path, dg):
+            if t is not None:
+                t.record_stream(st)
+    return out_tokens, out_accept_len, out_path, dg
 
 
 def sample(logits: torch.Tensor, params, uniforms: torch.Tensor, *, diag: bool = False,

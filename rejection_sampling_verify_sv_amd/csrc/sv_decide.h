@@ -36,6 +36,7 @@ struct DecideIntent {
     int32_t nu;    // units to list at position k+1 (0: none)
     int32_t cls;   // their class region
     int32_t draw;  // 1: the row draws over the full vocabulary at the end
+    int32_t rnd;   // 1: tree verify, the row tests its node's next child after a pass
 };
 
 // Per-wave LDS of the top-k draw, passed in by the kernel (which lays it over
@@ -66,11 +67,14 @@ __device__ inline void diag_nan_row(double* diag, int b, int K) {
         d[i] = __longlong_as_double(0x7FF8000000000000ll);
 }
 
-// One lane: write accepted drafts + final token, close the row.
+// One lane: write accepted drafts + final token, close the row.  A tree
+// verify writes each accepted token as its walk takes it (tree_continue).
 __device__ inline void emit_row(const StepArgs& a, int b, int acc, int y) {
     int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
-    const int32_t* t = a.tokens + (int64_t)b * a.K;
-    for (int j = 0; j < acc; j++) o[j] = t[j];
+    if (!a.tree) {
+        const int32_t* t = a.tokens + (int64_t)b * a.K;
+        for (int j = 0; j < acc; j++) o[j] = t[j];
+    }
     o[acc] = y;
     a.out_acc[b] = acc;
     a.rows[b].acc = acc;
@@ -83,6 +87,8 @@ __device__ inline void close_row_invalid(const StepArgs& a, int b, int code) {
     if (lane_id() == 0) {
         int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
         for (int j = 0; j <= a.K; j++) o[j] = -1;
+        if (a.out_path)  // a tree verify writes its path as it walks
+            for (int j = 0; j <= a.K; j++) a.out_path[(int64_t)b * (a.K + 1) + j] = -1;
         a.out_acc[b] = code;  // -1 invalid data, -2 not served
         a.rows[b].status = ST_ERROR;
     }
@@ -141,15 +147,64 @@ __device__ __forceinline__ double accept_prob(double px, double qx) {
     return (px > 0.0) ? 1.0 : 0.0;
 }
 
-__device__ __forceinline__ void write_accept_diag(const StepArgs& a, int b, int k, double px,
+// Diagnostics of one accept test, slot `slot` (draft position k, or node c's
+// test at c - 1 in a tree verify).
+__device__ __forceinline__ void write_accept_diag(const StepArgs& a, int b, int slot, double px,
                                                   double qx, double acc, double uk) {
     if (a.diag && lane_id() == 0) {
         double* dg = a.diag + (int64_t)b * 4 * (a.K + 1);
-        dg[4 * k + 0] = px;
-        dg[4 * k + 1] = qx;
-        dg[4 * k + 2] = acc;
-        dg[4 * k + 3] = fabs(uk - acc);
+        dg[4 * slot + 0] = px;
+        dg[4 * slot + 1] = qx;
+        dg[4 * slot + 2] = acc;
+        dg[4 * slot + 3] = fabs(uk - acc);
     }
+}
+
+// ---- tree verify helpers -----------------------------------------------------
+// Node c >= 1 of row b has parent parents[b][c-1] < c, so the children of v
+// are nodes in (v, L].  Wave-wide scans (every lane gets the result).
+// The first child of v after node `after`, or -1.
+__device__ inline int next_child(const StepArgs& a, int b, int v, int after, int L) {
+    const int32_t* par = a.parents + (int64_t)b * a.K;
+    for (int c0 = (after > v ? after : v) + 1; c0 <= L; c0 += kWave) {
+        const int c = c0 + lane_id();
+        const uint64_t m = __ballot(c <= L && par[c - 1] == v);
+        if (m) return c0 + __ffsll((unsigned long long)m) - 1;
+    }
+    return -1;
+}
+// The first child of v whose token is `tok`, or -1.
+__device__ inline int child_with_token(const StepArgs& a, int b, int v, int L, int tok) {
+    const int32_t* par = a.parents + (int64_t)b * a.K;
+    const int32_t* tk = a.tokens + (int64_t)b * a.K;
+    for (int c0 = v + 1; c0 <= L; c0 += kWave) {
+        const int c = c0 + lane_id();
+        const uint64_t m = __ballot(c <= L && par[c - 1] == v && tk[c - 1] == tok);
+        if (m) return c0 + __ffsll((unsigned long long)m) - 1;
+    }
+    return -1;
+}
+// The first child of the row's current node, or -1 (a verify step: the next
+// drafted position, node k + 1, while k < L).
+__device__ inline int first_child(const StepArgs& a, int b, int k, const RowInfo& ri) {
+    if (!a.tree) return k < ri.L ? k + 1 : -1;
+    return next_child(a, b, ri.node, ri.node, ri.L);
+}
+// Row b accepts child c (token x) of its node at level k: the token and the
+// node are written out, c becomes the row's node, and its units are listed
+// for level k + 1 (c's draft row only when c has children).  One lane.
+__device__ inline void tree_continue(const StepArgs& a, int b, int k, int c, int x, bool kids,
+                                     const RowInfo& ri, DecideIntent& it) {
+    a.out_tokens[(int64_t)b * (a.K + 1) + k] = x;
+    if (a.out_path) a.out_path[(int64_t)b * (a.K + 1) + k] = c;
+    RowInfo& w = a.rows[b];
+    w.acc = k + 1;
+    w.node = c;
+    w.kids = kids ? 1 : 0;
+    w.rounds = 0;
+    w.nxt = -1;
+    it.nu = (ri.cls != CLS_GREEDY && kids) ? 2 : 1;
+    it.cls = ri.cls;
 }
 
 // Row b accepted the draft at position k: its units go to position k+1's
@@ -168,64 +223,11 @@ __device__ inline void continue_row(const StepArgs& a, int b, int k, const RowIn
 // Row b ends at position k with a draw over the full vocabulary (one lane).
 __device__ inline void queue_draw(DecideIntent& it) { it.draw = 1; }
 
-__device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, TopkScratch& ts,
-                            DecideIntent& it) {
-    double* s_w = ts.w;
-    double* s_p = ts.p;
-    int* s_id = ts.id;
-    const int lane = lane_id();
-    const int k_eff = ri.k_eff;
-    const double T = (double)ri.T, top_p = (double)ri.top_p;
-    const bool has_draft = k < ri.L;
-    const PosDesc P = a.pos[k];
-    const float* u = a.uniforms + (int64_t)b * (a.K + 1);
-    // every load first, so that their latencies overlap
-    const uint64_t kt =
-        unit_top(a.parts, unit_records(P, unit_index(P, CLS_TOPK, ri.li_t), a.ntiles, a.g_row));
-    uint64_t kd = 0ull;
-    int x = 0;
-    double uk = 0.0;
-    if (has_draft) {
-        kd = unit_top(a.parts,
-                      unit_records(P, unit_index(P, CLS_TOPK, ri.li_d), a.ntiles, a.g_row));
-        x = a.tokens[(int64_t)b * a.K + k];
-        uk = (double)u[k];
-    }
-    const double uf = (double)u[a.K];
-    double p;
-    bool keep_p;
-    if (!topk_dist_wave(kt, k_eff, T, top_p, &p, &keep_p)) {
-        close_row_invalid(a, b, -1);
-        return;
-    }
-    const int id_p = (int)key_id(kt);
-    double q = 0.0;
-    bool keep_q = false;
-    int id_q = -1;
-    if (has_draft) {
-        if (!topk_dist_wave(kd, k_eff, T, top_p, &q, &keep_q)) {
-            close_row_invalid(a, b, -1);
-            return;
-        }
-        id_q = (int)key_id(kd);
-        const double px = lookup_lane(keep_p, id_p, p, x);
-        const double qx = lookup_lane(keep_q, id_q, q, x);
-        const double acc = accept_prob(px, qx);
-        write_accept_diag(a, b, k, px, qx, acc, uk);
-        if (uk < acc) {
-            continue_row(a, b, k, ri, it);
-            return;
-        }
-    }
-    // Final draw over p's kept tokens in ascending id order: the residual
-    // (p - q)+ after a rejection, p itself for the bonus token.
-    // The kept tokens of each side are a prefix of its lanes: broadcast them
-    // one at a time (scalar reads of a lane, no LDS traffic) and only as many
-    // as are kept.  qj: q of this lane's token; rank: kept p tokens of lower id.
+// q of each lane's kept p token (0 when q drops it): the kept q tokens are a
+// prefix of the lanes, broadcast one at a time by scalar lane reads.
+__device__ __forceinline__ double q_of_lane(int id_p, int id_q, double q, bool keep_q) {
     const int nq = __popcll(__ballot(keep_q));
-    const int np = __popcll(__ballot(keep_p));
     double qj = 0.0;
-    int rank = 0;
     const int q_lo = __double2loint(q), q_hi = __double2hiint(q);
     for (int s = 0; s < nq; s++) {
         const int ids = __builtin_amdgcn_readlane(id_q, s);
@@ -233,20 +235,34 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
                                            __builtin_amdgcn_readlane(q_lo, s));
         if (ids == id_p) qj = qs;
     }
+    return qj;
+}
+
+// Final draw of a top-k row over p's kept tokens in ascending id order, with
+// weight fw in the lane of each kept token: the residual after a rejection
+// (resid; p itself when the residual has no mass), p for the bonus token.
+// Writes the final diagnostics and closes the row at accept length k.
+__device__ void topk_draw(const StepArgs& a, int b, int k, double p, bool keep_p, int id_p,
+                          double fw, bool resid, double uf, TopkScratch& ts) {
+    double* s_w = ts.w;
+    double* s_p = ts.p;
+    int* s_id = ts.id;
+    const int lane = lane_id();
+    const int np = __popcll(__ballot(keep_p));
+    int rank = 0;
     for (int s = 0; s < np; s++) rank += __builtin_amdgcn_readlane(id_p, s) < id_p ? 1 : 0;
     if (keep_p) {
-        const double d = p - qj;
-        s_w[rank] = has_draft ? (d > 0.0 ? d : 0.0) : p;
+        s_w[rank] = fw;
         s_p[rank] = p;
         s_id[rank] = id_p;
     }
     wave_lds_sync();
-    const int kp = __popcll(__ballot(keep_p));
+    const int kp = np;
     double wr = lane < kp ? s_w[lane] : 0.0;
     const double pr = lane < kp ? s_p[lane] : 0.0;
     const int idr = lane < kp ? s_id[lane] : -1;
     double W = wave_sum(wr);
-    const bool fallback = has_draft && !(W > 0.0);
+    const bool fallback = resid && !(W > 0.0);
     if (fallback) {  // p == q up to rounding: draw from p
         wr = pr;
         W = wave_sum(wr);
@@ -271,13 +287,99 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
         if (a.diag) {
             double* dg = a.diag + (int64_t)b * 4 * (a.K + 1) + 4 * a.K;
             const double d1 = uf - lo, d2 = hi - uf;
-            dg[0] = has_draft ? wy / W : py;
+            dg[0] = resid ? wy / W : py;
             dg[1] = lo;
             dg[2] = hi;
             dg[3] = margin_scale * (d1 < d2 ? d1 : d2);
         }
         emit_row(a, b, k, y);
     }
+}
+
+__device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, TopkScratch& ts,
+                            DecideIntent& it) {
+    const int k_eff = ri.k_eff;
+    const double T = (double)ri.T, top_p = (double)ri.top_p;
+    const int child = first_child(a, b, k, ri);
+    const bool has_draft = child >= 0;
+    const PosDesc P = a.pos[k];
+    const float* u = a.uniforms + (int64_t)b * (a.K + 1);
+    // every load first, so that their latencies overlap
+    const uint64_t kt =
+        unit_top(a.parts, unit_records(P, unit_index(P, CLS_TOPK, ri.li_t), a.ntiles, a.g_row));
+    uint64_t kd = 0ull;
+    int x = 0;
+    double uk = 0.0;
+    if (has_draft) {
+        kd = unit_top(a.parts,
+                      unit_records(P, unit_index(P, CLS_TOPK, ri.li_d), a.ntiles, a.g_row));
+        x = a.tokens[(int64_t)b * a.K + child - 1];
+        uk = (double)u[child - 1];
+    }
+    const double uf = (double)u[a.K];
+    double p;
+    bool keep_p;
+    if (!topk_dist_wave(kt, k_eff, T, top_p, &p, &keep_p)) {
+        close_row_invalid(a, b, -1);
+        return;
+    }
+    const int id_p = (int)key_id(kt);
+    if (!has_draft) {  // bonus token from p
+        topk_draw(a, b, k, p, keep_p, id_p, p, false, uf, ts);
+        return;
+    }
+    double q;
+    bool keep_q;
+    if (!topk_dist_wave(kd, k_eff, T, top_p, &q, &keep_q)) {
+        close_row_invalid(a, b, -1);
+        return;
+    }
+    const int id_q = (int)key_id(kd);
+    if (!a.tree) {
+        const double px = lookup_lane(keep_p, id_p, p, x);
+        const double qx = lookup_lane(keep_q, id_q, q, x);
+        const double acc = accept_prob(px, qx);
+        write_accept_diag(a, b, k, px, qx, acc, uk);
+        if (uk < acc) {
+            continue_row(a, b, k, ri, it);
+            return;
+        }
+        // the residual (p - q)+ over p's kept tokens
+        const double d = p - q_of_lane(id_p, id_q, q, keep_q);
+        topk_draw(a, b, k, p, keep_p, id_p, d > 0.0 ? d : 0.0, true, uf, ts);
+        return;
+    }
+    // Tree verify: the node's children in turn against r, which starts as p
+    // and becomes the normalised residual (r - q)+ after each rejection
+    // (unchanged when that has no mass); all rejected: draw from what is
+    // left of r.
+    const double qj = q_of_lane(id_p, id_q, q, keep_q);
+    double r = keep_p ? p : 0.0;
+    int c = child;
+    double fw;
+    for (;;) {
+        const double rx = lookup_lane(keep_p, id_p, r, x);
+        const double qx = lookup_lane(keep_q, id_q, q, x);
+        const double acc = accept_prob(rx, qx);
+        write_accept_diag(a, b, c - 1, rx, qx, acc, uk);
+        if (uk < acc) {
+            const bool kids = next_child(a, b, c, c, ri.L) >= 0;
+            if (lane_id() == 0) tree_continue(a, b, k, c, x, kids, ri, it);
+            return;
+        }
+        const double d = keep_p ? r - qj : 0.0;
+        const double w = d > 0.0 ? d : 0.0;
+        const double W = wave_sum(w);
+        c = next_child(a, b, ri.node, c, ri.L);
+        if (c < 0) {
+            fw = W > 0.0 ? w : r;
+            break;
+        }
+        if (W > 0.0) r = w / W;
+        x = a.tokens[(int64_t)b * a.K + c - 1];
+        uk = (double)u[c - 1];
+    }
+    topk_draw(a, b, k, p, keep_p, id_p, fw, true, uf, ts);
 }
 
 __device__ void decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri,
@@ -290,7 +392,14 @@ __device__ void decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri
     for (int i = lane; i < r.count; i += kWave) best = s[i].keys[0] > best ? s[i].keys[0] : best;
     best = wave_max_u64(best);
     const int g = (int)key_id(best);
-    if (k < ri.L && a.tokens[(int64_t)b * a.K + k] == g) {
+    if (a.tree) {  // the first child whose token is the argmax, if any
+        const int c = child_with_token(a, b, ri.node, ri.L, g);
+        if (c >= 0) {
+            const bool kids = next_child(a, b, c, c, ri.L) >= 0;
+            if (lane == 0) tree_continue(a, b, k, c, g, kids, ri, it);
+            return;
+        }
+    } else if (k < ri.L && a.tokens[(int64_t)b * a.K + k] == g) {
         continue_row(a, b, k, ri, it);
         return;
     }
@@ -317,32 +426,45 @@ __device__ inline void full_stats(const FullStat* rec, int n, double invT, doubl
     *z = wave_sum(ss);
 }
 
+// Tree verify, full-vocab rows: the row rejected child `c` of its node and the
+// node has another child, nxt: the next test needs the mass of the residual,
+// one more pass over the node's two rows (tree_sums / tree_round).  One lane.
+__device__ inline void tree_to_round(const StepArgs& a, int b, int v, int nxt, DecideIntent& it) {
+    RowInfo& w = a.rows[b];
+    w.kpos = v;
+    w.rounds = 0;
+    w.nxt = nxt;
+    it.rnd = 1;
+}
+
 template <int DT>
 __device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri, DecideIntent& it) {
     const double T = (double)ri.T, invT = 1.0 / T;
     double mt, zt, md = 0.0, zd = 0.0;
     const int nrec = a.ntiles * kWaves;
+    const int v = row_at(a, b, k);
+    const int child = first_child(a, b, k, ri);
     // the drafted token's logits and the uniform, loaded while the records are
     float lx = 0.f, ld = 0.f, ukf = 0.f;
     int x = 0;
-    if (k < ri.L) {
-        x = a.tokens[(int64_t)b * a.K + k];
+    if (child >= 0) {
+        x = a.tokens[(int64_t)b * a.K + child - 1];
         if (x >= 0 && x < a.V) {  // validated by the plan; kept in range here regardless
-            lx = load_one<DT>(unit_row<DT>(a, b, 0, k), x);
-            ld = load_one<DT>(unit_row<DT>(a, b, 1, k), x);
+            lx = load_one<DT>(unit_row<DT>(a, b, 0, v), x);
+            ld = load_one<DT>(unit_row<DT>(a, b, 1, v), x);
         }
-        ukf = a.uniforms[(int64_t)b * (a.K + 1) + k];
+        ukf = a.uniforms[(int64_t)b * (a.K + 1) + child - 1];
     }
     full_stats(a.tstat + (int64_t)(2 * b) * nrec, nrec, invT, &mt, &zt);
     if (!(mt > -INFINITY)) {
         close_row_invalid(a, b, -1);
         return;
     }
-    if (k == ri.L) {
+    if (child < 0) {
         if (lane_id() == 0) {
             RowInfo& w = a.rows[b];
             w.need = NEED_BONUS;
-            w.kpos = k;
+            w.kpos = v;
             w.mt = mt;
             w.zt = zt;
             queue_draw(it);
@@ -354,22 +476,32 @@ __device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri, 
         close_row_invalid(a, b, -1);
         return;
     }
+    // tree verify: whether the child has children, the node's next child
+    const bool kids = a.tree && next_child(a, b, child, child, ri.L) >= 0;
+    const int nxt = a.tree ? next_child(a, b, v, child, ri.L) : -1;
     if (lane_id() != 0) return;
     const double px = exp(((double)lx - mt) / T) / zt;
     const double qx = exp(((double)ld - md) / T) / zd;
     const double acc = accept_prob(px, qx);
     const double uk = (double)ukf;
-    write_accept_diag(a, b, k, px, qx, acc, uk);
+    write_accept_diag(a, b, child - 1, px, qx, acc, uk);
     RowInfo& w = a.rows[b];
     if (uk < acc) {
-        note_continue(a, b, k, ri, it);
+        if (a.tree)
+            tree_continue(a, b, k, child, x, kids, ri, it);
+        else
+            note_continue(a, b, k, ri, it);
     } else {
-        w.need = NEED_RESID;
-        w.kpos = k;
         w.mt = mt;
         w.zt = zt;
         w.md = md;
         w.zd = zd;
+        if (nxt >= 0) {
+            tree_to_round(a, b, v, nxt, it);
+            return;
+        }
+        w.need = NEED_RESID;
+        w.kpos = v;
         queue_draw(it);
     }
 }
@@ -381,30 +513,34 @@ template <int DT>
 __device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& ri,
                                DecideIntent& it) {
     const FnUnit ut = fn_unit_load(a.fn_unit + b * 2);
-    const bool has_draft = k < ri.L;
+    const int v = row_at(a, b, k);
+    const int child = first_child(a, b, k, ri);
+    const bool has_draft = child >= 0;
     FnUnit ud;
     ud.status = 0;
     float lx = 0.f, ld = 0.f, ukf = 0.f;
     int x = 0;
     if (has_draft) {  // loaded together with the cut states
         ud = fn_unit_load(a.fn_unit + b * 2 + 1);
-        x = a.tokens[(int64_t)b * a.K + k];
+        x = a.tokens[(int64_t)b * a.K + child - 1];
         if (x >= 0 && x < a.V) {  // validated by the plan; kept in range here regardless
-            lx = load_one<DT>(unit_row<DT>(a, b, 0, k), x);
-            ld = load_one<DT>(unit_row<DT>(a, b, 1, k), x);
+            lx = load_one<DT>(unit_row<DT>(a, b, 0, v), x);
+            ld = load_one<DT>(unit_row<DT>(a, b, 1, v), x);
         }
-        ukf = a.uniforms[(int64_t)b * (a.K + 1) + k];
+        ukf = a.uniforms[(int64_t)b * (a.K + 1) + child - 1];
     }
     const int st = ut.status != 0 ? ut.status : (has_draft ? ud.status : 0);
     if (st != 0) {
         close_row_invalid(a, b, st == 1 ? -2 : -1);
         return;
     }
+    const bool kids = a.tree && has_draft && next_child(a, b, child, child, ri.L) >= 0;
+    const int nxt = (a.tree && has_draft) ? next_child(a, b, v, child, ri.L) : -1;
     if (lane_id() != 0) return;
     RowInfo& w = a.rows[b];
     if (!has_draft) {
         w.need = NEED_BONUS;
-        w.kpos = k;
+        w.kpos = v;
         w.mt = (double)ut.la;
         w.zt = ut.S;
         w.tau_t = ut.tau;
@@ -420,25 +556,33 @@ __device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& r
                           : 0.0;
     const double acc = accept_prob(px, qx);
     const double uk = (double)ukf;
-    write_accept_diag(a, b, k, px, qx, acc, uk);
+    write_accept_diag(a, b, child - 1, px, qx, acc, uk);
     if (uk < acc) {
-        note_continue(a, b, k, ri, it);
+        if (a.tree)
+            tree_continue(a, b, k, child, x, kids, ri, it);
+        else
+            note_continue(a, b, k, ri, it);
     } else {
-        w.need = NEED_RESID;
-        w.kpos = k;
         w.mt = (double)ut.la;
         w.zt = ut.S;
         w.tau_t = ut.tau;
         w.md = (double)ud.la;
         w.zd = ud.S;
         w.tau_d = ud.tau;
+        if (nxt >= 0) {
+            tree_to_round(a, b, v, nxt, it);
+            return;
+        }
+        w.need = NEED_RESID;
+        w.kpos = v;
         queue_draw(it);
     }
 }
 
 // One row per wave (b_w < 0: none; rows not live at position k, and
 // nucleus rows when skip_nucleus is set, do nothing), then the workgroup's
-// list updates: per class region and for the draw list, one global atomic
+// list updates: per class region, for the draw list and for a tree verify's
+// first child round, one global atomic
 // reserves the space of all its rows, and each row writes its entries in
 // wave order.  Every thread of the workgroup calls it (barriers inside).
 // Not inlined, so that its registers are not added to those of the cut
@@ -454,6 +598,7 @@ __device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, int k,
         s_it[w].nu = 0;
         s_it[w].cls = 0;
         s_it[w].draw = 0;
+        s_it[w].rnd = 0;
     }
     if (b_w >= 0) {
         const int b = b_w;
@@ -471,14 +616,20 @@ __device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, int k,
         }
     }
     __syncthreads();
-    if (threadIdx.x <= kNumCls) {  // thread c < kNumCls: class region c; kNumCls: draws
+    // thread c < kNumCls: class region c; kNumCls: draws; kNumCls + 1: the
+    // first child round of a tree verify
+    if (threadIdx.x <= kNumCls + 1) {
         const int c = threadIdx.x;
         int cnt = 0;
         for (int j = 0; j < kWaves; j++)
-            cnt += (c < kNumCls) ? (s_it[j].cls == c ? s_it[j].nu : 0) : s_it[j].draw;
+            cnt += (c < kNumCls) ? (s_it[j].cls == c ? s_it[j].nu : 0)
+                                 : (c == kNumCls ? s_it[j].draw : s_it[j].rnd);
         int base = 0;
         if (cnt > 0)
-            base = atomicAdd(c < kNumCls ? &a.pos[k + 1].n_cls[c] : &a.pos[a.K + 1].n_sample, cnt);
+            base = atomicAdd(c < kNumCls    ? &a.pos[k + 1].n_cls[c]
+                             : c == kNumCls ? &a.pos[a.K + 1].n_sample
+                                            : &a.tcount[k * kMaxKids + 1],
+                             cnt);
         s_base[c] = base;
     }
     __syncthreads();
@@ -506,6 +657,11 @@ __device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, int k,
         a.slist[i] = b;
         a.rows[b].status = ST_SAMPLE;
     }
+    if (lane == 0 && it.rnd) {
+        int i = s_base[kNumCls + 1];
+        for (int j = 0; j < w; j++) i += s_it[j].rnd;
+        a.tlist[a.B + i] = b;  // round 1's list
+    }
 }
 
 // One workgroup: zero the work counters, then classify every row, initialise
@@ -528,6 +684,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
         for (int i = threadIdx.x; i < 2 * rows; i += kPlanThreads) a.fn_sync[i] = 0;
         for (int i = threadIdx.x; i < a.B; i += kPlanThreads) a.fn_row[i] = 0;
     }
+    if (a.tree)  // rows per (level, child round) of a tree verify
+        for (int i = threadIdx.x; i < (a.K + 1) * kMaxKids; i += kPlanThreads) a.tcount[i] = 0;
     __syncthreads();
     for (int b = threadIdx.x; b < a.B; b += kPlanThreads) {
         const sv_sampler_params prm = params[b];
@@ -539,6 +697,27 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
             for (int j = 0; j < L; j++) {
                 const int t = a.tokens[(int64_t)b * a.K + j];
                 if (t < 0 || t >= a.V) bad = true;
+            }
+        }
+        if (!bad && a.tree) {
+            // nodes 1..L: parent in [0, c), depth at most max_depth, at most
+            // max_kids children per node (the host loops over that many
+            // levels and child rounds)
+            const int32_t* par = a.parents + (int64_t)b * a.K;
+            int32_t* ns = a.nscr + (int64_t)b * (a.K + 1);
+            ns[0] = 0;
+            for (int c = 1; c <= L && !bad; c++) {
+                const int pc = par[c - 1];
+                if (pc < 0 || pc >= c) {
+                    bad = true;
+                } else {
+                    ns[c] = ns[pc] + 1;
+                    bad = ns[c] > a.max_depth;
+                }
+            }
+            if (!bad) {
+                for (int c = 0; c <= L; c++) ns[c] = 0;
+                for (int c = 1; c <= L; c++) bad |= ++ns[par[c - 1]] > a.max_kids;
             }
         }
         int cls;
@@ -558,7 +737,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
         ri.kpos = 0;
         ri.need = NEED_NONE;
         ri.k_eff = (cls == CLS_TOPK) ? tk : 0;
-        ri.flags = 0;
+        ri.node = 0;
+        ri.rounds = 0;
+        ri.nxt = -1;
+        ri.kids = (L > 0) ? 1 : 0;  // in a tree node 1's parent is node 0
+        ri.pad = 0;
         ri.T = T;
         ri.top_p = tp;
         ri.li_t = ri.li_d = -1;
@@ -585,6 +768,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
         if (a.stats) continue;  // no verify outputs
         int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
         for (int j = 0; j <= a.K; j++) o[j] = -1;
+        if (a.out_path)
+            for (int j = 0; j <= a.K; j++) a.out_path[(int64_t)b * (a.K + 1) + j] = -1;
         a.out_acc[b] = (cls == CLS_ERROR) ? -1 : (cls == CLS_UNSUP ? -2 : 0);
         if (a.diag) {
             double* d = a.diag + (int64_t)b * 4 * (a.K + 1);

@@ -41,16 +41,28 @@ enum RowClass : int32_t {
 enum RowStatus : int32_t { ST_LIVE = 0, ST_DONE = 1, ST_SAMPLE = 2, ST_ERROR = 3 };
 enum Need : int32_t { NEED_NONE = 0, NEED_RESID = 1, NEED_BONUS = 2 };
 
-// Per-row bookkeeping kept in the workspace (96 bytes).
+// Per-row bookkeeping kept in the workspace (112 bytes).  A verify step walks
+// positions 0..L of a chain of drafts; a tree verify walks from node 0 to an
+// accepted child at every level (then `node` names the node whose rows the
+// current level reads, and `acc` the level).
 struct RowInfo {
     int32_t cls, L, status, acc;
-    int32_t kpos, need, k_eff, flags;
+    int32_t kpos, need, k_eff, node;  // kpos: row index of the final draw (position or node)
     float T, top_p;
     int32_t li_t, li_d;      // index of the target / draft unit in its class region at the current position
     double mt, zt, md, zd;   // full-vocab stats (max, normaliser) at position kpos
     uint64_t tau_t, tau_d;   // nucleus rows: key of the last kept token
+    int32_t rounds;          // tree, full-vocab rows: children rejected at the current node
+    int32_t nxt;             // tree, full-vocab rows: the next child to test (-1: none)
+    int32_t kids;            // tree: the current node has children (its draft row is listed)
+    int32_t pad;
 };
-static_assert(sizeof(RowInfo) == 96, "RowInfo layout");
+static_assert(sizeof(RowInfo) == 112, "RowInfo layout");
+
+// Children per node a tree verify serves on full-vocab rows (each rejected
+// child there costs a pass over the node's two rows); top-k and greedy rows
+// take any number.
+constexpr int kMaxKids = 64;
 
 // Work counters of one position.  The units to stream are listed in one
 // region per row class (greedy, top-k, untruncated, nucleus), laid end to end
@@ -985,7 +997,23 @@ struct StepArgs {
     StatDesc* sdesc;       // [B] acceptance statistics: the rows' distributions
     double* srec;          // [B][ntiles][kWaves][4] acceptance statistics: partial sums
     double* sout;          // [B][4] acceptance statistics: the result
+    // tree verify (tree = 1): node c >= 1 has token tokens[b][c-1] and parent
+    // parents[b][c-1] < c; rows are indexed by node
+    int tree;
+    const int32_t* parents;
+    int32_t* out_path;     // [B][K+1] accepted nodes, or null
+    double* wchain;        // [B][kMaxKids] masses of the residuals after each rejected child
+    int32_t* tlist;        // [kMaxKids][B] full-vocab rows in each child round of a level
+    int32_t* tcount;       // [K+1][kMaxKids] their numbers, per level and round
+    int32_t* nscr;         // [B][K+1] per-node scratch of the plan (depths, child counts)
+    int max_depth, max_kids;  // the tree's bounds: levels after 0, children per node
 };
+
+// Row index (within batch entry b's rows) read at position / level k: the
+// position itself in a verify step, the row's current node in a tree verify.
+__device__ __forceinline__ int row_at(const StepArgs& a, int b, int k) {
+    return a.tree ? a.rows[b].node : k;
+}
 
 template <int DT>
 __device__ __forceinline__ const void* unit_row(const StepArgs& a, int b, int side, int k) {

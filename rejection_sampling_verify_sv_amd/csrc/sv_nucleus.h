@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
     __shared__ int s_star, s_nsel, s_wcnt[kWaves], s_base, s_last;
     __shared__ uint64_t s_before;
     __shared__ DecideIntent s_it[kWaves];
-    __shared__ int s_dbase[kNumCls + 1];
+    __shared__ int s_dbase[kNumCls + 2];
     constexpr int kPend = 32;  // completed nucleus rows awaiting their decision
     __shared__ int s_pend[kPend], s_npend;
     static_assert(sizeof(TopkScratch) * kWaves <= sizeof(uint64_t) * kCollectCap,
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
         const int b = u >> 1, side = u & 1;
         const RowInfo& ri = a.rows[b];
         FnUnit* fu = a.fn_unit + u;
-        const void* row = unit_row<DT>(a, b, side, k);
+        const void* row = unit_row<DT>(a, b, side, row_at(a, b, k));
         const float cb = bucket_coef(ri.T);
         const RecRange rr =
             unit_records(P, unit_index(P, CLS_NUCLEUS, li), a.ntiles, a.g_row);
@@ -662,7 +662,8 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
         if (threadIdx.x == 0) {
             const int b = list[li] >> 1;
             bool last = true;
-            if (k < a.rows[b].L) {  // a target and a draft unit: the second to finish decides
+            // a target and a draft unit: the second to finish decides
+            if (a.tree ? a.rows[b].kids != 0 : k < a.rows[b].L) {
                 dev_stores_done();  // this unit's FnUnit stores, before the count
                 last = __hip_atomic_fetch_add(&a.fn_row[b], 1, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT) == 1;

@@ -26,12 +26,31 @@ struct DrawCtx {
     float mt, md, c, cb;
     double izt, izd;  // reciprocals of the normalisers (no division per token)
     uint64_t tau_t, tau_d;
+    int rounds;             // tree verify: residual masses known before this draw
+    const double* wchain;   // their values
 };
 
-__device__ __forceinline__ DrawCtx draw_ctx(const RowInfo& ri) {
+// A tree verify's row whose node had `rounds` children rejected before the
+// current one: r_0 = p and r_i = (r_{i-1} - q)+ / W_i (r_{i-1} when W_i <= 0)
+// at one token, from its normalised probabilities.
+__device__ __forceinline__ double resid_chain(double pe, double qe, int rounds,
+                                              const double* wchain) {
+    double r = pe;
+    for (int i = 0; i < rounds; i++) {
+        const double W = wchain[i];
+        const double d = r - qe;
+        r = W > 0.0 ? (d > 0.0 ? d : 0.0) / W : r;
+    }
+    return r;
+}
+
+__device__ __forceinline__ DrawCtx draw_ctx(const StepArgs& a, int b, const RowInfo& ri,
+                                            bool resid) {
     DrawCtx x;
     x.nucleus = ri.cls == CLS_NUCLEUS;
-    x.resid = ri.need == NEED_RESID;
+    x.resid = resid;
+    x.rounds = ri.rounds;
+    x.wchain = a.wchain + (int64_t)b * kMaxKids;
     x.mt = (float)ri.mt;
     x.md = (float)ri.md;
     x.c = exp2_coef(ri.T);
@@ -49,6 +68,27 @@ __device__ __forceinline__ DrawCtx draw_ctx(const RowInfo& ri) {
 // anchors).
 __device__ __forceinline__ void draw_weights(const DrawCtx& x, float lt, float ld, uint32_t id,
                                              double* wr, double* wp) {
+    if (x.rounds > 0) {
+        // tree verify after earlier rejections at this node: the residual of
+        // the residual chain (r_R - q)+ and, for its fallback, r_R itself
+        double pe, qe;
+        if (x.nucleus) {
+            pe = (make_key(lt, id) >= x.tau_t)
+                     ? (double)fast_exp2(nuc_t(lt, x.mt, x.cb) * kLog2e64) * x.izt
+                     : 0.0;
+            qe = (make_key(ld, id) >= x.tau_d)
+                     ? (double)fast_exp2(nuc_t(ld, x.md, x.cb) * kLog2e64) * x.izd
+                     : 0.0;
+        } else {
+            pe = (double)fast_exp2((lt - x.mt) * x.c) * x.izt;
+            qe = (double)fast_exp2((ld - x.md) * x.c) * x.izd;
+        }
+        const double r = resid_chain(pe, qe, x.rounds, x.wchain);
+        const double d = r - qe;
+        *wr = d > 0.0 ? d : 0.0;
+        *wp = r;
+        return;
+    }
     if (x.nucleus) {
         // only tokens kept on the target side carry mass in either sum
         *wp = 0.0;
@@ -77,12 +117,16 @@ __device__ __forceinline__ void draw_weights(const DrawCtx& x, float lt, float l
     }
 }
 
-// The workgroups split the tiles of the draw rows evenly; every wave leaves
+// The workgroups split the tiles of the listed rows evenly; every wave leaves
 // its partial masses of each tile at chunks[(b*ntiles + tile)*kWaves + wave].
+// The rows: those that draw over the full vocabulary at the end (list slist,
+// count pos[K+1].n_sample), or, in a tree verify, those that need the mass of
+// a residual before testing their node's next child (round lists).
 template <int DT, bool kAligned>
-__global__ __launch_bounds__(kThreads) void sample_sums_kernel(StepArgs a) {
+__global__ __launch_bounds__(kThreads) void sample_sums_kernel(StepArgs a, const int32_t* list,
+                                                               const int32_t* count) {
     using TS = TileShape<DT>;
-    const int n = a.pos[a.K + 1].n_sample;
+    const int n = *count;
     const int64_t T = (int64_t)n * a.ntiles;
     int64_t t = flat_begin(T, gridDim.x, blockIdx.x);
     const int64_t t_end = flat_begin(T, gridDim.x, blockIdx.x + 1);
@@ -92,10 +136,10 @@ __global__ __launch_bounds__(kThreads) void sample_sums_kernel(StepArgs a) {
         int64_t tu1 = tu0 + (t_end - t);
         if (tu1 > a.ntiles) tu1 = a.ntiles;
         t += tu1 - tu0;
-        const int b = a.slist[si];
+        const int b = list[si];
         const RowInfo& ri = a.rows[b];
         const int kpos = ri.kpos;
-        const DrawCtx x = draw_ctx(ri);
+        const DrawCtx x = draw_ctx(a, b, ri, ri.need != NEED_BONUS);
         const void* trow = unit_row<DT>(a, b, 0, kpos);
         const void* drow = x.resid ? unit_row<DT>(a, b, 1, kpos) : nullptr;
         const int64_t start = tu0 * TS::kTile;
@@ -216,7 +260,7 @@ __device__ __forceinline__ void pick_row(const StepArgs& a, int b) {
         return;
     }
     const int kpos = ri.kpos;
-    const DrawCtx x = draw_ctx(ri);
+    const DrawCtx x = draw_ctx(a, b, ri, resid);
     const void* trow = unit_row<DT>(a, b, 0, kpos);
     const void* drow = x.resid ? unit_row<DT>(a, b, 1, kpos) : nullptr;
     // thread t owns the contiguous run [start + t*kE, start + (t+1)*kE)
@@ -287,11 +331,21 @@ __device__ __forceinline__ void pick_row(const StepArgs& a, int b) {
             dg[2] = hi;
             dg[3] = fallback ? 0.0 : (d1 < d2 ? d1 : d2);
         }
+        int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
         if (y < 0) {
             a.out_acc[b] = -1;
             a.rows[b].status = ST_ERROR;
+            if (a.tree) {  // the walk wrote its accepted tokens and nodes already
+                for (int j = 0; j <= a.K; j++) o[j] = -1;
+                if (a.out_path)
+                    for (int j = 0; j <= a.K; j++) a.out_path[(int64_t)b * (a.K + 1) + j] = -1;
+            }
+        } else if (a.tree) {
+            // tree verify: kpos is the node, the accepted path's length is acc
+            o[ri.acc] = y;
+            a.out_acc[b] = ri.acc;
+            a.rows[b].status = ST_DONE;
         } else {
-            int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
             const int32_t* t = a.tokens + (int64_t)b * a.K;
             for (int j = 0; j < kpos; j++) o[j] = t[j];
             o[kpos] = y;

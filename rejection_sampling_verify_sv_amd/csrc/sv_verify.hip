@@ -30,6 +30,7 @@
 #include "sv_rowpass.h"
 #include "sv_sample.h"
 #include "sv_stats.h"
+#include "sv_tree.h"
 
 namespace {
 
@@ -40,7 +41,8 @@ constexpr int kMaxDraft = 1024;
 struct Plan {
     int tile, ntiles;
     size_t off_rows, off_pos, off_ulist, off_slist, off_parts, off_tstat, off_chunks,
-        off_fnu, off_hist, off_fnkeys, off_fnsync, off_fnrow, off_self, off_sdesc, off_srec, off_status, bytes;
+        off_fnu, off_hist, off_fnkeys, off_fnsync, off_fnrow, off_self, off_sdesc, off_srec, off_status,
+        off_wchain, off_tlist, off_tcount, off_nscr, bytes;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -78,6 +80,12 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
     p->off_sdesc = take(sizeof(StatDesc) * (size_t)B);  // sv_accept_stats
     p->off_srec = take(sizeof(double) * 4 * (size_t)B * p->ntiles * kWaves);
     p->off_status = take(sizeof(int32_t) * (size_t)B);  // sv_sample without out_status
+    // sv_verify_tree: residual masses and child-round lists of full-vocab
+    // rows, per-node scratch of the plan
+    p->off_wchain = take(sizeof(double) * (size_t)B * kMaxKids);
+    p->off_tlist = take(sizeof(int32_t) * (size_t)kMaxKids * B);
+    p->off_tcount = take(sizeof(int32_t) * (size_t)(K + 1) * kMaxKids);
+    p->off_nscr = take(sizeof(int32_t) * (size_t)B * (K + 1));
     p->bytes = off;
     return true;
 }
@@ -183,10 +191,42 @@ int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepAr
         cut_decide_kernel<DT, kAligned><<<cut_grid, kThreads, 0, st>>>(a, k);
     }
     mark();
-    sample_sums_kernel<DT, kAligned><<<g.sums, kThreads, 0, st>>>(a);
+    sample_sums_kernel<DT, kAligned><<<g.sums, kThreads, 0, st>>>(a, a.slist,
+                                                                 &a.pos[a.K + 1].n_sample);
     mark();
     sample_pick_kernel<DT><<<row_grid, kThreads, 0, st>>>(a);
     mark();
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SV_OK : hip_fail(e);
+}
+
+// Tree verify: per level the row pass and the cut / decisions, then the
+// child rounds of full-vocab rows (sv_tree.h); the final draws at the end.
+template <int DT, bool kAligned>
+int launch_tree(const int32_t* n_cand, const sv_sampler_params* params, StepArgs a,
+                hipStream_t st) {
+    Grids g;
+    const int rc = grids_for_device<DT, kAligned>(&g);
+    if (rc != SV_OK) return rc;
+    a.g_row = (int)g.rowpass;
+    const int B = a.B;
+    const unsigned cut_cap = (unsigned)(2 * B * kMaxSplit < kGrid ? 2 * B * kMaxSplit : kGrid);
+    const unsigned cut_grid = g.cut < cut_cap ? g.cut : cut_cap;
+    const unsigned row_grid = (unsigned)(B < kGrid ? B : kGrid);
+    const unsigned wave_grid = (unsigned)((B + kWaves - 1) / kWaves);
+    plan_kernel<<<1, kPlanThreads, 0, st>>>(a, n_cand, params);
+    for (int k = 0; k <= a.max_depth; k++) {
+        rowpass_kernel<DT, kAligned><<<g.rowpass, kThreads, 0, st>>>(a, k);
+        cut_decide_kernel<DT, kAligned><<<cut_grid, kThreads, 0, st>>>(a, k);
+        for (int j = 1; j < a.max_kids; j++) {
+            sample_sums_kernel<DT, kAligned><<<g.sums, kThreads, 0, st>>>(
+                a, a.tlist + (int64_t)j * B, a.tcount + k * kMaxKids + j);
+            tree_round_kernel<DT><<<wave_grid, kThreads, 0, st>>>(a, k, j);
+        }
+    }
+    sample_sums_kernel<DT, kAligned><<<g.sums, kThreads, 0, st>>>(a, a.slist,
+                                                                 &a.pos[a.K + 1].n_sample);
+    sample_pick_kernel<DT><<<row_grid, kThreads, 0, st>>>(a);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? SV_OK : hip_fail(e);
 }
@@ -267,11 +307,18 @@ extern "C" size_t sv_workspace_bytes(int32_t batch, int32_t max_draft, int32_t v
     return make_plan(batch, max_draft, vocab, dtype, &p) ? p.bytes : 0;
 }
 
+// The tree of a tree verify (null for a verify step).
+struct TreeIn {
+    const int32_t* parents;
+    int32_t* out_path;
+    int max_depth, max_kids;
+};
+
 static int verify_impl(const void* target_logits, const void* draft_logits,
                        const int32_t* draft_tokens, const int32_t* draft_len,
                        const sv_sampler_params* sampler_params, const float* uniforms,
                        int32_t* out_tokens, int32_t* out_accept_len, const sv_config* cfg,
-                       hipEvent_t const* ev) {
+                       hipEvent_t const* ev, const TreeIn* tree = nullptr) {
     if (!cfg || !target_logits || !sampler_params || !uniforms || !out_tokens || !out_accept_len)
         return SV_EINVAL;
     const int32_t B = cfg->batch, K = cfg->max_draft, V = cfg->vocab, dt = cfg->dtype;
@@ -320,6 +367,15 @@ static int verify_impl(const void* target_logits, const void* draft_logits,
     a.srec = reinterpret_cast<double*>(ws + pl.off_srec);
     a.sout = nullptr;
     a.g_row = 0;
+    a.tree = tree ? 1 : 0;
+    a.parents = tree ? tree->parents : nullptr;
+    a.out_path = tree ? tree->out_path : nullptr;
+    a.wchain = reinterpret_cast<double*>(ws + pl.off_wchain);
+    a.tlist = reinterpret_cast<int32_t*>(ws + pl.off_tlist);
+    a.tcount = reinterpret_cast<int32_t*>(ws + pl.off_tcount);
+    a.nscr = reinterpret_cast<int32_t*>(ws + pl.off_nscr);
+    a.max_depth = tree ? tree->max_depth : K;
+    a.max_kids = tree ? tree->max_kids : 1;
 
     const size_t esz = (dt == SV_F32) ? 4 : 2;
     const bool aligned = reinterpret_cast<uintptr_t>(target_logits) % 16 == 0 &&
@@ -327,6 +383,13 @@ static int verify_impl(const void* target_logits, const void* draft_logits,
                          (K == 0 || (reinterpret_cast<uintptr_t>(draft_logits) % 16 == 0 &&
                                      ((size_t)ds * esz) % 16 == 0));
     hipStream_t st = static_cast<hipStream_t>(cfg->stream);
+    if (tree) {
+        if (dt == SV_F32)
+            return aligned ? launch_tree<SV_F32, true>(draft_len, sampler_params, a, st)
+                           : launch_tree<SV_F32, false>(draft_len, sampler_params, a, st);
+        return aligned ? launch_tree<SV_BF16, true>(draft_len, sampler_params, a, st)
+                       : launch_tree<SV_BF16, false>(draft_len, sampler_params, a, st);
+    }
     if (dt == SV_F32)
         return aligned ? launch_all<SV_F32, true>(draft_len, sampler_params, a, st, ev)
                        : launch_all<SV_F32, false>(draft_len, sampler_params, a, st, ev);
@@ -390,6 +453,26 @@ extern "C" int sv_verify_noalloc(const void* target_logits, const void* draft_lo
 }
 
 extern "C" size_t sv_noalloc_scratch_bytes(void) { return kNoAllocBytes; }
+
+extern "C" int sv_verify_tree(const void* target_logits, const void* draft_logits,
+                              const int32_t* node_tokens, const int32_t* node_parents,
+                              const int32_t* n_cand, const sv_sampler_params* sampler_params,
+                              const float* uniforms, int32_t* out_tokens, int32_t* out_accept_len,
+                              int32_t* out_path, int32_t max_depth, int32_t max_children,
+                              const sv_config* cfg) {
+    if (!cfg) return SV_EINVAL;
+    const int K = cfg->max_draft;
+    if (K > 0 && !node_parents) return SV_EINVAL;
+    if (max_depth < 0 || max_depth > K) return SV_EINVAL;
+    if (K > 0 && (max_children < 1 || max_children > kMaxKids)) return SV_EINVAL;
+    TreeIn t;
+    t.parents = node_parents;
+    t.out_path = out_path;
+    t.max_depth = max_depth;
+    t.max_kids = K > 0 ? max_children : 1;
+    return verify_impl(target_logits, draft_logits, node_tokens, n_cand, sampler_params, uniforms,
+                       out_tokens, out_accept_len, cfg, nullptr, &t);
+}
 
 extern "C" int sv_verify_profiled(const void* target_logits, const void* draft_logits,
                                   const int32_t* draft_tokens, const int32_t* draft_len,
@@ -473,6 +556,15 @@ extern "C" int sv_accept_stats(const void* target_logits, const void* draft_logi
     a.srec = reinterpret_cast<double*>(ws + pl.off_srec);
     a.sout = out;
     a.g_row = 0;
+    a.tree = 0;
+    a.parents = nullptr;
+    a.out_path = nullptr;
+    a.wchain = reinterpret_cast<double*>(ws + pl.off_wchain);
+    a.tlist = reinterpret_cast<int32_t*>(ws + pl.off_tlist);
+    a.tcount = reinterpret_cast<int32_t*>(ws + pl.off_tcount);
+    a.nscr = reinterpret_cast<int32_t*>(ws + pl.off_nscr);
+    a.max_depth = 1;
+    a.max_kids = 1;
     const size_t esz = (dt == SV_F32) ? 4 : 2;
     const bool aligned = reinterpret_cast<uintptr_t>(target_logits) % 16 == 0 &&
                          reinterpret_cast<uintptr_t>(draft_logits) % 16 == 0 &&

@@ -113,3 +113,24 @@ def test_accept_stats_rejects_bad_arguments_on_host(lib):
     assert lib.sv_accept_stats(*args, ctypes.byref(cfg)) == -2
     cfg.dtype = 7
     assert lib.sv_accept_stats(*args, ctypes.byref(cfg)) == -1
+
+
+def test_verify_tree_rejects_bad_arguments_on_host(lib):
+    from rejection_sampling_verify_sv_amd import _lib
+    cfg = _lib.SvConfig()
+    cfg.batch, cfg.max_draft, cfg.vocab, cfg.dtype = 2, 4, 100, 0
+    d = ctypes.c_void_p(0x1000)
+    args = [d] * 10
+    assert lib.sv_verify_tree(*args, 2, 2, None) == -1          # no config
+    assert lib.sv_verify_tree(*args, 5, 2, ctypes.byref(cfg)) == -1   # max_depth > K
+    assert lib.sv_verify_tree(*args, -1, 2, ctypes.byref(cfg)) == -1  # max_depth < 0
+    assert lib.sv_verify_tree(*args, 2, 0, ctypes.byref(cfg)) == -1   # max_children < 1
+    assert lib.sv_verify_tree(*args, 2, 65, ctypes.byref(cfg)) == -1  # max_children > 64
+    bad = list(args)
+    bad[3] = None                                               # no parents with K > 0
+    assert lib.sv_verify_tree(*bad, 2, 2, ctypes.byref(cfg)) == -1
+    assert lib.sv_verify_tree(*args, 2, 2, ctypes.byref(cfg)) == -2   # no workspace
+    # sv_verify_noalloc refuses shapes beyond its static scratch before any launch
+    cfg.batch, cfg.max_draft, cfg.vocab = 4096, 3, 151936
+    assert lib.sv_workspace_bytes(4096, 3, 151936, 0) > lib.sv_noalloc_scratch_bytes()
+    assert lib.sv_verify_noalloc(*([d] * 8), ctypes.byref(cfg)) == -4
