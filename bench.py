@@ -218,7 +218,7 @@ def read_ceiling(dev, nbytes=2 << 30, reps=10):
             "ms": round(ms, 4), "kernel": "sv_stream_read (row-pass tiling, max per element)"}
 
 
-def measure(wl, dev, steps, warmup, replicas=1, ceiling=None):
+def measure(wl, dev, steps, warmup, replicas=1, ceiling=None, step_mode="auto"):
     """Time sv_verify on a workload; per-kernel times from the events the
     library records between its launches.  With replicas > 1 the step
     rotates over that many copies of the inputs in HBM."""
@@ -238,7 +238,7 @@ def measure(wl, dev, steps, warmup, replicas=1, ceiling=None):
 
     def step(i, events=None):
         sv.verify(*ins[i % replicas], workspace=ws, out_tokens=out_tok, out_accept_len=out_acc,
-                  events=events)
+                  events=events, step_mode=step_mode)
         calls[0] += 1
 
     for i in range(warmup):
@@ -254,7 +254,7 @@ def measure(wl, dev, steps, warmup, replicas=1, ceiling=None):
     ms_per_step = e0.elapsed_time(e1) / steps
 
     hip = Hip()
-    names = _lib.launch_names(K)
+    names = _lib.launch_names(B, K, step_mode)
     nl = len(names)
     per_kernel = {}
     rowpass_ms = []
@@ -312,7 +312,8 @@ def measure(wl, dev, steps, warmup, replicas=1, ceiling=None):
         "warmup": warmup,
         "dtype": "f32" if wl.dtype == "f32" else "bf16",
         "config": {"workload": wl.name, "vocab": V, "batch": B, "max_draft": K,
-                   "logits": wl.dtype, "input_replicas": replicas,
+                   "logits": wl.dtype, "input_replicas": replicas, "step_mode": step_mode,
+                   "launches": len(names),
                    "rows_unsupported": int((acc == -2).sum())},
         "roofline": {
             "bound": "hbm", "kernel": "rowpass", "achieved": round(achieved, 1),

@@ -88,7 +88,16 @@ typedef struct {
                      the final distribution, lower CDF edge, upper CDF edge,
                      margin of u to the nearer edge).  NaN where not evaluated
                      and on greedy rows. */
+    int32_t step_mode; /* SV_STEP_AUTO (0): a dense step for small batches
+                          (2 B (K+1) <= 1024 rows to stream), position by
+                          position otherwise; SV_STEP_POSITIONS (1): always
+                          position by position; SV_STEP_DENSE (2): dense
+                          (SV_EINVAL when the batch is not small).  The
+                          results are the same in every mode. */
+    int32_t reserved;  /* 0 */
 } sv_config;
+
+enum { SV_STEP_AUTO = 0, SV_STEP_POSITIONS = 1, SV_STEP_DENSE = 2 };
 
 /* Bytes of device workspace sv_verify needs for this shape.  Pure function
  * of its arguments; 0 on invalid arguments. */
@@ -129,8 +138,9 @@ int sv_verify(const void* target_logits, const void* draft_logits, const int32_t
 /*
  * Same as sv_verify, and additionally records events[i] (hipEvent_t, created
  * by the caller) on cfg->stream just before kernel launch i of the step and
- * events[sv_launch_count(K)] after the last one, so the caller can time each
- * kernel with hipEventElapsedTime.  n_events must be >= sv_launch_count(K)+1.
+ * events[sv_launch_count(B, K, step_mode)] after the last one, so the caller
+ * can time each kernel with hipEventElapsedTime.  n_events must be
+ * >= sv_launch_count(B, K, step_mode) + 1.
  * For measuring kernels against the sustainable read rate of the part, the
  * method of "Apple Silikon İçin Cihaz Üstü Çıkarımı Optimize Etme", section
  * "Daha fazla optimizasyonun sınırları".
@@ -290,12 +300,14 @@ int sv_accept_stats(const void* target_logits, const void* draft_logits,
  */
 int sv_stream_read(const void* data, size_t bytes, uint32_t* out, void* stream);
 
-/* Number of kernel launches in one step for max_draft K (0 if K is outside
- * [0, 1024]), and
- * the name of launch i ("plan", "rowpass", "cut_decide", ...; NULL if out of
- * range).  Static strings, host only. */
-int32_t sv_launch_count(int32_t max_draft);
-const char* sv_launch_name(int32_t max_draft, int32_t i);
+/* Number of kernel launches in one sv_verify step of B rows and max_draft K
+ * in step mode `step_mode` (0 if B < 1, K is outside [0, 1024] or the mode is
+ * not served for the shape), and the name of launch i ("plan", "rowpass",
+ * "cut_decide", ...; NULL if out of range).  A dense step has one row pass
+ * over every drafted position and one decision launch that walks the
+ * positions.  Static strings, host only. */
+int32_t sv_launch_count(int32_t batch, int32_t max_draft, int32_t step_mode);
+const char* sv_launch_name(int32_t batch, int32_t max_draft, int32_t step_mode, int32_t i);
 
 /* Static description of an error code (the last HIP error for SV_EHIP). */
 const char* sv_strerror(int code);

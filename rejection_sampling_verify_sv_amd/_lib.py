@@ -36,6 +36,8 @@ class SvConfig(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("diag", ctypes.c_void_p),
+        ("step_mode", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -64,7 +66,7 @@ def load() -> ctypes.CDLL:
         lib.sv_strerror.restype = ctypes.c_char_p
         lib.sv_strerror.argtypes = [ctypes.c_int]
         lib.sv_launch_count.restype = ctypes.c_int32
-        lib.sv_launch_count.argtypes = [ctypes.c_int32]
+        lib.sv_launch_count.argtypes = [ctypes.c_int32] * 3
         lib.sv_verify_tree.restype = ctypes.c_int
         lib.sv_verify_tree.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int32, ctypes.c_int32]
                                        + [ctypes.POINTER(SvConfig)])
@@ -75,7 +77,7 @@ def load() -> ctypes.CDLL:
         lib.sv_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                        ctypes.c_void_p]
         lib.sv_launch_name.restype = ctypes.c_char_p
-        lib.sv_launch_name.argtypes = [ctypes.c_int32, ctypes.c_int32]
+        lib.sv_launch_name.argtypes = [ctypes.c_int32] * 4
         _lib = lib
     return _lib
 
@@ -84,10 +86,15 @@ def workspace_bytes(batch: int, max_draft: int, vocab: int, dtype: int) -> int:
     return int(load().sv_workspace_bytes(batch, max_draft, vocab, dtype))
 
 
-def launch_names(max_draft: int) -> list:
+SV_STEP_AUTO, SV_STEP_POSITIONS, SV_STEP_DENSE = 0, 1, 2
+STEP_MODES = {"auto": SV_STEP_AUTO, "positions": SV_STEP_POSITIONS, "dense": SV_STEP_DENSE}
+
+
+def launch_names(batch: int, max_draft: int, step_mode: str = "auto") -> list:
     lib = load()
-    return [lib.sv_launch_name(max_draft, i).decode()
-            for i in range(lib.sv_launch_count(max_draft))]
+    m = STEP_MODES[step_mode]
+    return [lib.sv_launch_name(batch, max_draft, m, i).decode()
+            for i in range(lib.sv_launch_count(batch, max_draft, m))]
 
 
 def stream_read(data: torch.Tensor, out: torch.Tensor, stream: torch.cuda.Stream | None = None):
@@ -132,13 +139,14 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
            draft_len: torch.Tensor | None, params, uniforms: torch.Tensor, *,
            diag: bool = False, workspace: torch.Tensor | None = None,
            out_tokens: torch.Tensor | None = None, out_accept_len: torch.Tensor | None = None,
-           stream: torch.cuda.Stream | None = None, events=None):
+           stream: torch.cuda.Stream | None = None, events=None, step_mode: str = "auto"):
     """Enqueue one verify step; returns (out_tokens, out_accept_len, diag|None).
 
     target [B, K+1, V], draft [B, K, V]: float32 or bfloat16 CUDA tensors.
     draft_tokens [B, K] int32; draft_len [B] int32 or None; params as in
     params_tensor(); uniforms [B, K+1] float32.  With K = 0, draft and
-    draft_tokens may be None.  Nothing is synchronised.
+    draft_tokens may be None.  step_mode: "auto", "positions" or "dense"
+    (see sv_config.step_mode).  Nothing is synchronised.
     """
     lib = load()
     if not target.is_cuda:
@@ -199,6 +207,7 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
     cfg.workspace = wptr + pad
     cfg.workspace_bytes = workspace.numel() * workspace.element_size() - pad
     cfg.diag = dg.data_ptr() if dg is not None else None
+    cfg.step_mode = STEP_MODES[step_mode]
     args = (target.data_ptr(), draft.data_ptr() if draft is not None else None,
             tok.data_ptr() if tok is not None else None,
             dl.data_ptr() if dl is not None else None, prm.data_ptr(), uni.data_ptr(),

@@ -108,6 +108,15 @@ __device__ __forceinline__ uint64_t unit_top(const PartSlot* parts, RecRange r) 
     return acc;
 }
 
+// Record slots of unit (b, position k, side) of row class cls: in the list of
+// position k's launch, or of the one launch of a dense step.
+__device__ __forceinline__ RecRange unit_rec(const StepArgs& a, const RowInfo& ri, int cls, int b,
+                                             int k, int side) {
+    const PosDesc& P = a.pos[a.dense ? 0 : k];
+    const int li = a.dense ? a.dli[unit_code(a, b, k, side)] : (side ? ri.li_d : ri.li_t);
+    return unit_records(P, unit_index(P, cls, li), a.ntiles, a.g_row);
+}
+
 // Truncated distribution over a ranked list (lane j = j-th ranked token):
 // temperature, top_k (first k_eff lanes), renormalise, keep while the mass
 // before the token is < top_p, renormalise.  Returns false when the best
@@ -296,23 +305,22 @@ __device__ void topk_draw(const StepArgs& a, int b, int k, double p, bool keep_p
     }
 }
 
-__device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, TopkScratch& ts,
+// Returns true (in every lane) when the row accepted and goes on to the next
+// position; the same for the other classes below.
+__device__ bool decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, TopkScratch& ts,
                             DecideIntent& it) {
     const int k_eff = ri.k_eff;
     const double T = (double)ri.T, top_p = (double)ri.top_p;
     const int child = first_child(a, b, k, ri);
     const bool has_draft = child >= 0;
-    const PosDesc P = a.pos[k];
     const float* u = a.uniforms + (int64_t)b * (a.K + 1);
     // every load first, so that their latencies overlap
-    const uint64_t kt =
-        unit_top(a.parts, unit_records(P, unit_index(P, CLS_TOPK, ri.li_t), a.ntiles, a.g_row));
+    const uint64_t kt = unit_top(a.parts, unit_rec(a, ri, CLS_TOPK, b, k, 0));
     uint64_t kd = 0ull;
     int x = 0;
     double uk = 0.0;
     if (has_draft) {
-        kd = unit_top(a.parts,
-                      unit_records(P, unit_index(P, CLS_TOPK, ri.li_d), a.ntiles, a.g_row));
+        kd = unit_top(a.parts, unit_rec(a, ri, CLS_TOPK, b, k, 1));
         x = a.tokens[(int64_t)b * a.K + child - 1];
         uk = (double)u[child - 1];
     }
@@ -321,18 +329,18 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
     bool keep_p;
     if (!topk_dist_wave(kt, k_eff, T, top_p, &p, &keep_p)) {
         close_row_invalid(a, b, -1);
-        return;
+        return false;
     }
     const int id_p = (int)key_id(kt);
     if (!has_draft) {  // bonus token from p
         topk_draw(a, b, k, p, keep_p, id_p, p, false, uf, ts);
-        return;
+        return false;
     }
     double q;
     bool keep_q;
     if (!topk_dist_wave(kd, k_eff, T, top_p, &q, &keep_q)) {
         close_row_invalid(a, b, -1);
-        return;
+        return false;
     }
     const int id_q = (int)key_id(kd);
     if (!a.tree) {
@@ -342,12 +350,12 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
         write_accept_diag(a, b, k, px, qx, acc, uk);
         if (uk < acc) {
             continue_row(a, b, k, ri, it);
-            return;
+            return true;
         }
         // the residual (p - q)+ over p's kept tokens
         const double d = p - q_of_lane(id_p, id_q, q, keep_q);
         topk_draw(a, b, k, p, keep_p, id_p, d > 0.0 ? d : 0.0, true, uf, ts);
-        return;
+        return false;
     }
     // Tree verify: the node's children in turn against r, which starts as p
     // and becomes the normalised residual (r - q)+ after each rejection
@@ -365,7 +373,7 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
         if (uk < acc) {
             const bool kids = next_child(a, b, c, c, ri.L) >= 0;
             if (lane_id() == 0) tree_continue(a, b, k, c, x, kids, ri, it);
-            return;
+            return true;
         }
         const double d = keep_p ? r - qj : 0.0;
         const double w = d > 0.0 ? d : 0.0;
@@ -380,13 +388,13 @@ __device__ void decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
         uk = (double)u[c - 1];
     }
     topk_draw(a, b, k, p, keep_p, id_p, fw, true, uf, ts);
+    return false;
 }
 
-__device__ void decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri,
+__device__ bool decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri,
                               DecideIntent& it) {
     const int lane = lane_id();
-    const RecRange r =
-        unit_records(a.pos[k], unit_index(a.pos[k], CLS_GREEDY, ri.li_t), a.ntiles, a.g_row);
+    const RecRange r = unit_rec(a, ri, CLS_GREEDY, b, k, 0);
     const PartSlot* s = a.parts + r.first;
     uint64_t best = 0ull;
     for (int i = lane; i < r.count; i += kWave) best = s[i].keys[0] > best ? s[i].keys[0] : best;
@@ -397,13 +405,14 @@ __device__ void decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri
         if (c >= 0) {
             const bool kids = next_child(a, b, c, c, ri.L) >= 0;
             if (lane == 0) tree_continue(a, b, k, c, g, kids, ri, it);
-            return;
+            return true;
         }
     } else if (k < ri.L && a.tokens[(int64_t)b * a.K + k] == g) {
         continue_row(a, b, k, ri, it);
-        return;
+        return true;
     }
     if (lane == 0) emit_row(a, b, k, g);
+    return false;
 }
 
 // {max, sum-exp} of one full-vocab unit from its n per-(tile, wave) records
@@ -438,7 +447,7 @@ __device__ inline void tree_to_round(const StepArgs& a, int b, int v, int nxt, D
 }
 
 template <int DT>
-__device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri, DecideIntent& it) {
+__device__ bool decide_full(const StepArgs& a, int b, int k, const RowInfo& ri, DecideIntent& it) {
     const double T = (double)ri.T, invT = 1.0 / T;
     double mt, zt, md = 0.0, zd = 0.0;
     const int nrec = a.ntiles * kWaves;
@@ -455,10 +464,10 @@ __device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri, 
         }
         ukf = a.uniforms[(int64_t)b * (a.K + 1) + child - 1];
     }
-    full_stats(a.tstat + (int64_t)(2 * b) * nrec, nrec, invT, &mt, &zt);
+    full_stats(a.tstat + (int64_t)unit_code(a, b, k, 0) * nrec, nrec, invT, &mt, &zt);
     if (!(mt > -INFINITY)) {
         close_row_invalid(a, b, -1);
-        return;
+        return false;
     }
     if (child < 0) {
         if (lane_id() == 0) {
@@ -469,24 +478,27 @@ __device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri, 
             w.zt = zt;
             queue_draw(it);
         }
-        return;
+        return false;
     }
-    full_stats(a.tstat + (int64_t)(2 * b + 1) * nrec, nrec, invT, &md, &zd);
+    full_stats(a.tstat + (int64_t)unit_code(a, b, k, 1) * nrec, nrec, invT, &md, &zd);
     if (!(md > -INFINITY)) {
         close_row_invalid(a, b, -1);
-        return;
+        return false;
     }
     // tree verify: whether the child has children, the node's next child
     const bool kids = a.tree && next_child(a, b, child, child, ri.L) >= 0;
     const int nxt = a.tree ? next_child(a, b, v, child, ri.L) : -1;
-    if (lane_id() != 0) return;
+    // every lane holds the same statistics and logits: the decision is the
+    // same in all of them, lane 0 writes it
     const double px = exp(((double)lx - mt) / T) / zt;
     const double qx = exp(((double)ld - md) / T) / zd;
     const double acc = accept_prob(px, qx);
     const double uk = (double)ukf;
+    const bool cont = uk < acc;
     write_accept_diag(a, b, child - 1, px, qx, acc, uk);
+    if (lane_id() != 0) return cont;
     RowInfo& w = a.rows[b];
-    if (uk < acc) {
+    if (cont) {
         if (a.tree)
             tree_continue(a, b, k, child, x, kids, ri, it);
         else
@@ -498,21 +510,22 @@ __device__ void decide_full(const StepArgs& a, int b, int k, const RowInfo& ri, 
         w.zd = zd;
         if (nxt >= 0) {
             tree_to_round(a, b, v, nxt, it);
-            return;
+            return cont;
         }
         w.need = NEED_RESID;
         w.kpos = v;
         queue_draw(it);
     }
+    return cont;
 }
 
 // Nucleus rows: p(x) = [key(x) >= tau] exp(t(x) / 64) / S with the anchor
 // coordinate t and the kept mass S of the cut computed by the nucleus kernels
 // for this position.
 template <int DT>
-__device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& ri,
+__device__ bool decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& ri,
                                DecideIntent& it) {
-    const FnUnit ut = fn_unit_load(a.fn_unit + b * 2);
+    const FnUnit ut = fn_unit_load(a.fn_unit + unit_code(a, b, k, 0));
     const int v = row_at(a, b, k);
     const int child = first_child(a, b, k, ri);
     const bool has_draft = child >= 0;
@@ -521,7 +534,7 @@ __device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& r
     float lx = 0.f, ld = 0.f, ukf = 0.f;
     int x = 0;
     if (has_draft) {  // loaded together with the cut states
-        ud = fn_unit_load(a.fn_unit + b * 2 + 1);
+        ud = fn_unit_load(a.fn_unit + unit_code(a, b, k, 1));
         x = a.tokens[(int64_t)b * a.K + child - 1];
         if (x >= 0 && x < a.V) {  // validated by the plan; kept in range here regardless
             lx = load_one<DT>(unit_row<DT>(a, b, 0, v), x);
@@ -532,21 +545,24 @@ __device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& r
     const int st = ut.status != 0 ? ut.status : (has_draft ? ud.status : 0);
     if (st != 0) {
         close_row_invalid(a, b, st == 1 ? -2 : -1);
-        return;
+        return false;
     }
     const bool kids = a.tree && has_draft && next_child(a, b, child, child, ri.L) >= 0;
     const int nxt = (a.tree && has_draft) ? next_child(a, b, v, child, ri.L) : -1;
-    if (lane_id() != 0) return;
-    RowInfo& w = a.rows[b];
     if (!has_draft) {
-        w.need = NEED_BONUS;
-        w.kpos = v;
-        w.mt = (double)ut.la;
-        w.zt = ut.S;
-        w.tau_t = ut.tau;
-        queue_draw(it);
-        return;
+        if (lane_id() == 0) {
+            RowInfo& w = a.rows[b];
+            w.need = NEED_BONUS;
+            w.kpos = v;
+            w.mt = (double)ut.la;
+            w.zt = ut.S;
+            w.tau_t = ut.tau;
+            queue_draw(it);
+        }
+        return false;
     }
+    // the same cut states and logits in every lane: one decision, lane 0
+    // writes it
     const float cb = bucket_coef(ri.T);
     const double px = (make_key(lx, (uint32_t)x) >= ut.tau)
                           ? exp((double)nuc_t(lx, ut.la, cb) * (1.0 / 64.0)) / ut.S
@@ -556,8 +572,11 @@ __device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& r
                           : 0.0;
     const double acc = accept_prob(px, qx);
     const double uk = (double)ukf;
+    const bool cont = uk < acc;
     write_accept_diag(a, b, child - 1, px, qx, acc, uk);
-    if (uk < acc) {
+    if (lane_id() != 0) return cont;
+    RowInfo& w = a.rows[b];
+    if (cont) {
         if (a.tree)
             tree_continue(a, b, k, child, x, kids, ri, it);
         else
@@ -571,12 +590,13 @@ __device__ void decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& r
         w.tau_d = ud.tau;
         if (nxt >= 0) {
             tree_to_round(a, b, v, nxt, it);
-            return;
+            return cont;
         }
         w.need = NEED_RESID;
         w.kpos = v;
         queue_draw(it);
     }
+    return cont;
 }
 
 // One row per wave (b_w < 0: none; rows not live at position k, and
@@ -603,7 +623,10 @@ __device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, int k,
     if (b_w >= 0) {
         const int b = b_w;
         const RowInfo ri = a.rows[b];
-        if (ri.status == ST_LIVE && k <= ri.L && !(skip_nucleus && ri.cls == CLS_NUCLEUS)) {
+        // a dense step decides position k of the rows that accepted every
+        // position before it (the caller walks the positions)
+        if (ri.status == ST_LIVE && k <= ri.L && !(skip_nucleus && ri.cls == CLS_NUCLEUS) &&
+            (!a.dense || ri.acc == k)) {
             DecideIntent& it = s_it[w];
             if (ri.cls == CLS_GREEDY)
                 decide_greedy(a, b, k, ri, it);
@@ -613,6 +636,8 @@ __device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, int k,
                 decide_nucleus<DT>(a, b, k, ri, it);
             else
                 decide_full<DT>(a, b, k, ri, it);
+            // no unit lists to extend: every position was in this launch
+            if (a.dense && lane == 0) it.nu = 0;
         }
     }
     __syncthreads();
@@ -638,7 +663,7 @@ __device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, int k,
     if (lane == 0 && it.nu > 0) {
         int li = s_base[it.cls];
         for (int j = 0; j < w; j++) li += s_it[j].cls == it.cls ? s_it[j].nu : 0;
-        int32_t* ul = a.ulist + ((int64_t)(k + 1) * kNumCls + it.cls) * 2 * a.B;
+        int32_t* ul = a.ulist + ((int64_t)(k + 1) * kNumCls + it.cls) * a.ustride;
         ul[li] = b * 2;
         RowInfo& r = a.rows[b];
         r.li_t = li;
@@ -747,12 +772,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
         ri.li_t = ri.li_d = -1;
         ri.mt = ri.zt = ri.md = ri.zd = 0.0;
         ri.tau_t = ri.tau_d = 0ull;
-        if (cls >= 0) {
+        if (cls >= 0 && a.dense) {
+            // a dense step: the units of every position, target then draft
+            const bool drafts = cls != CLS_GREEDY && 0 < L;
+            const int nu = (L + 1) + (drafts ? L : 0);
+            int li = atomicAdd(&s_nc[cls], nu);
+            int32_t* ul = a.ulist + (int64_t)cls * a.ustride;
+            for (int k = 0; k <= L; k++) {
+                for (int side = 0; side < ((drafts && k < L) ? 2 : 1); side++) {
+                    const int code = unit_code(a, b, k, side);
+                    ul[li] = code;
+                    a.dli[code] = li++;
+                    if (cls == CLS_NUCLEUS) a.fn_unit[code].rehist = 0;
+                }
+            }
+        } else if (cls >= 0) {
             // position-0 units (the layout the decisions use, LDS counters)
             const bool draft = (cls != CLS_GREEDY || a.stats) && 0 < L;
             const int nu = draft ? 2 : 1;
             const int li = atomicAdd(&s_nc[cls], nu);
-            int32_t* ul = a.ulist + (int64_t)cls * 2 * a.B;
+            int32_t* ul = a.ulist + (int64_t)cls * a.ustride;
             ul[li] = b * 2;
             ri.li_t = li;
             if (draft) {

@@ -1007,7 +1007,43 @@ struct StepArgs {
     int32_t* tcount;       // [K+1][kMaxKids] their numbers, per level and round
     int32_t* nscr;         // [B][K+1] per-node scratch of the plan (depths, child counts)
     int max_depth, max_kids;  // the tree's bounds: levels after 0, children per node
+    // dense step (dense = 1): one row pass streams every drafted position of
+    // every row, and the decisions walk the positions in order; a unit's code
+    // then carries its position, (b (K+1) + k) 2 + side
+    int dense;
+    int ustride;           // entries per class region of a position's unit list
+    int32_t* dli;          // dense: [B][K+1][2] index of each unit in its class region
 };
+
+// A dense step serves batches whose units over all positions number at most
+// kDenseUnits: there the K launch pairs a position-by-position step needs
+// cost more than the rows it need not read (section on small batches in the
+// design notes: the launches of a position take tens of microseconds, a row
+// a fraction of one).
+constexpr int kDenseUnits = 1024;
+__host__ __device__ __forceinline__ bool dense_eligible(int64_t B, int64_t K) {
+    return 2 * B * (K + 1) <= kDenseUnits;
+}
+
+// Unit codes: b 2 + side in a position-by-position step (the position is the
+// launch's), (b (K+1) + k) 2 + side in a dense step.  Per-unit state (the
+// untruncated records, the nucleus cut) is indexed by the code.
+__device__ __forceinline__ int unit_code(const StepArgs& a, int b, int k, int side) {
+    return a.dense ? (b * (a.K + 1) + k) * 2 + side : b * 2 + side;
+}
+__device__ __forceinline__ int unit_b(const StepArgs& a, int u) {
+    return a.dense ? (u >> 1) / (a.K + 1) : u >> 1;
+}
+// Position of unit u, launched at position k.
+__device__ __forceinline__ int unit_pos(const StepArgs& a, int u, int k) {
+    return a.dense ? (u >> 1) % (a.K + 1) : k;
+}
+// Row index (within its batch entry's rows) that unit u of row b streams when
+// launched at position / level k.
+__device__ __forceinline__ int unit_rowidx(const StepArgs& a, int u, int b, int k) {
+    if (a.dense) return (u >> 1) % (a.K + 1);
+    return a.tree ? a.rows[b].node : k;
+}
 
 // Row index (within batch entry b's rows) read at position / level k: the
 // position itself in a verify step, the row's current node in a tree verify.
@@ -1026,14 +1062,14 @@ __device__ __forceinline__ const void* unit_row(const StepArgs& a, int b, int si
 
 // The nucleus units of position k (their class region) and their number.
 __device__ __forceinline__ const int32_t* nuc_list(const StepArgs& a, int k) {
-    return a.ulist + ((int64_t)k * kNumCls + CLS_NUCLEUS) * 2 * a.B;
+    return a.ulist + ((int64_t)k * kNumCls + CLS_NUCLEUS) * a.ustride;
 }
 
 // Unit at index li of position k's concatenated list.
 __device__ __forceinline__ int32_t unit_at(const StepArgs& a, int k, const PosDesc& p, int li) {
     int c = 0;
     while (c < kNumCls - 1 && li >= p.n_cls[c]) li -= p.n_cls[c++];
-    return a.ulist[((int64_t)k * kNumCls + c) * 2 * a.B + li];
+    return a.ulist[((int64_t)k * kNumCls + c) * a.ustride + li];
 }
 
 }  // namespace sv

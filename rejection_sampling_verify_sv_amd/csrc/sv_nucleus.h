@@ -361,10 +361,10 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
     // completes the unit's cut
     auto cut_unit = [&](int li, int sl) -> bool {
         const int u = list[li];
-        const int b = u >> 1, side = u & 1;
+        const int b = unit_b(a, u), side = u & 1;
         const RowInfo& ri = a.rows[b];
         FnUnit* fu = a.fn_unit + u;
-        const void* row = unit_row<DT>(a, b, side, row_at(a, b, k));
+        const void* row = unit_row<DT>(a, b, side, unit_rowidx(a, u, b, k));
         const float cb = bucket_coef(ri.T);
         const RecRange rr =
             unit_records(P, unit_index(P, CLS_NUCLEUS, li), a.ntiles, a.g_row);
@@ -635,12 +635,16 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
     R = (R + kDecideRows - 1) / kDecideRows * kDecideRows;
     const int n_groups = a.stats ? 0 : (a.B + R - 1) / R;  // the statistics decide nothing
     TopkScratch* const s_ts = reinterpret_cast<TopkScratch*>(s_key);  // free between units
+    // positions a decision walks: its own, or every one in a dense step
+    const int k_last = a.dense ? a.K : k;
     auto decide_pending = [&]() {
         const int np = s_npend;
         for (int i = 0; i < np; i += kWaves) {
             const int j = i + wave_id();
-            decide_rows<DT>(a.self, k, j < np ? s_pend[j] : -1, false, s_it, s_dbase, s_ts);
-            __syncthreads();
+            for (int kk = k; kk <= k_last; kk++) {
+                decide_rows<DT>(a.self, kk, j < np ? s_pend[j] : -1, false, s_it, s_dbase, s_ts);
+                __syncthreads();
+            }
         }
         if (threadIdx.x == 0) s_npend = 0;
         __syncthreads();
@@ -652,21 +656,29 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
             const int r0 = (wi - n_work) * R;
             for (int r = r0; r < r0 + R && r < a.B; r += kDecideRows) {
                 const int bw = r + wave_id();
-                decide_rows<DT>(a.self, k, bw < a.B ? bw : -1, true, s_it, s_dbase, s_ts);
-                __syncthreads();  // LDS is reused by the next rows
+                for (int kk = k; kk <= k_last; kk++) {
+                    decide_rows<DT>(a.self, kk, bw < a.B ? bw : -1, true, s_it, s_dbase, s_ts);
+                    __syncthreads();  // LDS is reused by the next rows
+                }
             }
             continue;
         }
         const int li = wi / S, sl = wi - li * S;
         if (!cut_unit(li, sl) || a.stats) continue;
         if (threadIdx.x == 0) {
-            const int b = list[li] >> 1;
+            const int b = unit_b(a, list[li]);
+            // the row's nucleus units in this launch: the target and the
+            // draft unit of the position (the target alone at its last one);
+            // every drafted position's in a dense step.  The last unit to
+            // finish decides the row.
+            const int L = a.rows[b].L;
+            const int need = a.dense ? 2 * L + 1
+                                     : ((a.tree ? a.rows[b].kids != 0 : k < L) ? 2 : 1);
             bool last = true;
-            // a target and a draft unit: the second to finish decides
-            if (a.tree ? a.rows[b].kids != 0 : k < a.rows[b].L) {
+            if (need > 1) {
                 dev_stores_done();  // this unit's FnUnit stores, before the count
                 last = __hip_atomic_fetch_add(&a.fn_row[b], 1, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT) == 1;
+                                              __HIP_MEMORY_SCOPE_AGENT) == need - 1;
                 if (last) a.fn_row[b] = 0;  // ready for the next position's launch
             }
             if (last) s_pend[s_npend++] = b;

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void tree_round_kernel(StepArgs a, int k,
             tree_continue(a, b, k, c, x, kids, ri, it);
             // the child's units join level k + 1's lists
             const int li = atomicAdd(&a.pos[k + 1].n_cls[it.cls], it.nu);
-            int32_t* ul = a.ulist + ((int64_t)(k + 1) * kNumCls + it.cls) * 2 * a.B;
+            int32_t* ul = a.ulist + ((int64_t)(k + 1) * kNumCls + it.cls) * a.ustride;
             ul[li] = b * 2;
             w.li_t = li;
             if (it.nu == 2) {

@@ -42,7 +42,7 @@ struct Plan {
     int tile, ntiles;
     size_t off_rows, off_pos, off_ulist, off_slist, off_parts, off_tstat, off_chunks,
         off_fnu, off_hist, off_fnkeys, off_fnsync, off_fnrow, off_self, off_sdesc, off_srec, off_status,
-        off_wchain, off_tlist, off_tcount, off_nscr, bytes;
+        off_wchain, off_tlist, off_tcount, off_nscr, off_dli, bytes;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -53,7 +53,9 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
         return false;
     p->tile = (dtype == SV_F32) ? TileShape<SV_F32>::kTile : TileShape<SV_BF16>::kTile;
     p->ntiles = (V + p->tile - 1) / p->tile;
-    const size_t units = (size_t)B * 2;
+    // units streamed by one launch: two per row, or every position's in a
+    // dense step (small batches)
+    const size_t units = dense_eligible(B, K) ? (size_t)B * 2 * (K + 1) : (size_t)B * 2;
     const size_t slots = units + kGrid;  // record slot u + w of a (unit, workgroup) piece
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -63,7 +65,7 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
     };
     p->off_rows = take(sizeof(RowInfo) * (size_t)B);
     p->off_pos = take(sizeof(PosDesc) * (size_t)(K + 2));
-    p->off_ulist = take(sizeof(int32_t) * units * kNumCls * (size_t)(K + 1));
+    p->off_ulist = take(sizeof(int32_t) * (size_t)B * 2 * kNumCls * (size_t)(K + 1));
     p->off_slist = take(sizeof(int32_t) * (size_t)B);
     p->off_parts = take(sizeof(PartSlot) * slots);
     p->off_tstat = take(sizeof(FullStat) * units * p->ntiles * kWaves);
@@ -86,6 +88,7 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
     p->off_tlist = take(sizeof(int32_t) * (size_t)kMaxKids * B);
     p->off_tcount = take(sizeof(int32_t) * (size_t)(K + 1) * kMaxKids);
     p->off_nscr = take(sizeof(int32_t) * (size_t)B * (K + 1));
+    p->off_dli = take(sizeof(int32_t) * units);  // dense step: list index of each unit
     p->bytes = off;
     return true;
 }
@@ -98,17 +101,31 @@ int hip_fail(hipError_t e) {
 }
 
 // Launch order of one step; sv_launch_count / sv_launch_name describe it.
+// A dense step (small batches) has one position launch pair for all
+// positions.
 constexpr int kPre = 1;
 constexpr int kPerPos = 2;
 const char* const kPreNames[kPre] = {"plan"};
 const char* const kPosNames[kPerPos] = {"rowpass", "cut_decide"};
-int launch_count(int K) { return kPre + kPerPos * (K + 1) + 2; }
+// Whether a step of this shape in this mode is dense; -1 when the mode is not
+// served for the shape.
+int step_dense(int B, int K, int mode) {
+    if (mode == SV_STEP_POSITIONS) return 0;
+    if (mode == SV_STEP_DENSE) return dense_eligible(B, K) ? 1 : -1;
+    if (mode == SV_STEP_AUTO) return dense_eligible(B, K) ? 1 : 0;
+    return -1;
+}
+int launch_count(int B, int K, int mode) {
+    const int d = step_dense(B, K, mode);
+    return d < 0 ? 0 : kPre + kPerPos * (d ? 1 : K + 1) + 2;
+}
 
-const char* launch_name(int K, int i) {
-    if (i < 0 || i >= launch_count(K)) return nullptr;
+const char* launch_name(int B, int K, int mode, int i) {
+    if (i < 0 || i >= launch_count(B, K, mode)) return nullptr;
     if (i < kPre) return kPreNames[i];
-    if (i < kPre + kPerPos * (K + 1)) return kPosNames[(i - kPre) % kPerPos];
-    return (i == kPre + kPerPos * (K + 1)) ? "sample_sums" : "sample_pick";
+    const int np = step_dense(B, K, mode) ? 1 : K + 1;
+    if (i < kPre + kPerPos * np) return kPosNames[(i - kPre) % kPerPos];
+    return (i == kPre + kPerPos * np) ? "sample_sums" : "sample_pick";
 }
 
 // The streaming kernels split their tiles evenly over the grid, so the grid
@@ -184,7 +201,7 @@ int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepAr
     const unsigned row_grid = (unsigned)(B < kGrid ? B : kGrid);
     mark();
     plan_kernel<<<1, kPlanThreads, 0, st>>>(a, draft_len, params);
-    for (int k = 0; k <= a.K; k++) {
+    for (int k = 0; k <= (a.dense ? 0 : a.K); k++) {
         mark();
         rowpass_kernel<DT, kAligned><<<g.rowpass, kThreads, 0, st>>>(a, k);
         mark();
@@ -376,6 +393,11 @@ static int verify_impl(const void* target_logits, const void* draft_logits,
     a.nscr = reinterpret_cast<int32_t*>(ws + pl.off_nscr);
     a.max_depth = tree ? tree->max_depth : K;
     a.max_kids = tree ? tree->max_kids : 1;
+    const int dense = tree ? 0 : step_dense(B, K, cfg->step_mode);
+    if (dense < 0) return SV_EINVAL;
+    a.dense = dense;
+    a.ustride = a.dense ? 2 * B * (K + 1) : 2 * B;
+    a.dli = reinterpret_cast<int32_t*>(ws + pl.off_dli);
 
     const size_t esz = (dt == SV_F32) ? 4 : 2;
     const bool aligned = reinterpret_cast<uintptr_t>(target_logits) % 16 == 0 &&
@@ -479,10 +501,11 @@ extern "C" int sv_verify_profiled(const void* target_logits, const void* draft_l
                                   const sv_sampler_params* sampler_params, const float* uniforms,
                                   int32_t* out_tokens, int32_t* out_accept_len,
                                   const sv_config* cfg, void* const* events, int32_t n_events) {
-    if (!cfg || !events || cfg->max_draft < 0 || cfg->max_draft > kMaxDraft ||
-        n_events < launch_count(cfg->max_draft) + 1)
+    if (!cfg || !events || cfg->batch <= 0 || cfg->max_draft < 0 || cfg->max_draft > kMaxDraft)
         return SV_EINVAL;
-    for (int i = 0; i <= launch_count(cfg->max_draft); i++)
+    const int nl = launch_count(cfg->batch, cfg->max_draft, cfg->step_mode);
+    if (nl == 0 || n_events < nl + 1) return SV_EINVAL;
+    for (int i = 0; i <= nl; i++)
         if (!events[i]) return SV_EINVAL;
     return verify_impl(target_logits, draft_logits, draft_tokens, draft_len, sampler_params,
                        uniforms, out_tokens, out_accept_len, cfg,
@@ -565,6 +588,9 @@ extern "C" int sv_accept_stats(const void* target_logits, const void* draft_logi
     a.nscr = reinterpret_cast<int32_t*>(ws + pl.off_nscr);
     a.max_depth = 1;
     a.max_kids = 1;
+    a.dense = 0;
+    a.ustride = 2 * B;
+    a.dli = reinterpret_cast<int32_t*>(ws + pl.off_dli);
     const size_t esz = (dt == SV_F32) ? 4 : 2;
     const bool aligned = reinterpret_cast<uintptr_t>(target_logits) % 16 == 0 &&
                          reinterpret_cast<uintptr_t>(draft_logits) % 16 == 0 &&
@@ -577,12 +603,17 @@ extern "C" int sv_accept_stats(const void* target_logits, const void* draft_logi
                    : launch_stats<SV_BF16, false>(sampler_params, a, st);
 }
 
-extern "C" int32_t sv_launch_count(int32_t max_draft) {
-    return (max_draft >= 0 && max_draft <= kMaxDraft) ? launch_count(max_draft) : 0;
+extern "C" int32_t sv_launch_count(int32_t batch, int32_t max_draft, int32_t step_mode) {
+    return (batch > 0 && max_draft >= 0 && max_draft <= kMaxDraft)
+               ? launch_count(batch, max_draft, step_mode)
+               : 0;
 }
 
-extern "C" const char* sv_launch_name(int32_t max_draft, int32_t i) {
-    return (max_draft >= 0 && max_draft <= kMaxDraft) ? launch_name(max_draft, i) : nullptr;
+extern "C" const char* sv_launch_name(int32_t batch, int32_t max_draft, int32_t step_mode,
+                                      int32_t i) {
+    return (batch > 0 && max_draft >= 0 && max_draft <= kMaxDraft)
+               ? launch_name(batch, max_draft, step_mode, i)
+               : nullptr;
 }
 
 extern "C" const char* sv_strerror(int code) {

@@ -87,9 +87,20 @@ def test_sample_and_k0_reject_bad_arguments_on_host(lib):
     assert lib.sv_sample(*s_bad, ctypes.byref(cfg)) == -2
     cfg.batch = 0
     assert lib.sv_sample(*s_args, ctypes.byref(cfg)) == -1
-    per_position = lib.sv_launch_count(2) - lib.sv_launch_count(1)
-    assert per_position > 0 and lib.sv_launch_count(0) == lib.sv_launch_count(1) - per_position
-    assert lib.sv_launch_count(-1) == 0 and lib.sv_launch_count(1025) == 0
+    # a position-by-position step: one launch pair per position
+    per_position = lib.sv_launch_count(1024, 2, 0) - lib.sv_launch_count(1024, 1, 0)
+    assert per_position == 2
+    assert lib.sv_launch_count(1024, 0, 0) == lib.sv_launch_count(1024, 1, 0) - per_position
+    # small batches take the dense step: one pair for every position
+    assert lib.sv_launch_count(64, 4, 0) == lib.sv_launch_count(64, 0, 0) == 5
+    assert lib.sv_launch_count(64, 4, 1) == 13 and lib.sv_launch_count(64, 4, 2) == 5
+    assert lib.sv_launch_count(513, 0, 0) == 5 and lib.sv_launch_count(513, 1, 0) == 7
+    assert lib.sv_launch_count(513, 1, 2) == 0  # dense is not served for that batch
+    assert lib.sv_launch_count(4, 1, 7) == 0    # no such mode
+    assert [lib.sv_launch_name(1, 1, 0, i) for i in range(5)] == [
+        b"plan", b"rowpass", b"cut_decide", b"sample_sums", b"sample_pick"]
+    assert lib.sv_launch_count(1, -1, 0) == 0 and lib.sv_launch_count(1, 1025, 0) == 0
+    assert lib.sv_launch_count(0, 1, 0) == 0
 
 
 def test_accept_stats_rejects_bad_arguments_on_host(lib):

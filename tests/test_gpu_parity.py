@@ -36,12 +36,18 @@ def dev():
     return torch.device("cuda:0")
 
 
-def run_gpu(wl, dev, diag=True):
+def modes_for(B, K):
+    """Step modes a batch shape is served in: position by position always,
+    the dense step when 2 B (K+1) <= 1024."""
+    return ["positions", "dense"] if 2 * B * (K + 1) <= 1024 else ["positions"]
+
+
+def run_gpu(wl, dev, diag=True, step_mode="auto"):
     import torch
 
     import rejection_sampling_verify_sv_amd as sv
 
-    tok, acc, dg = sv.verify(*workloads.to_torch(wl, dev), diag=diag)
+    tok, acc, dg = sv.verify(*workloads.to_torch(wl, dev), diag=diag, step_mode=step_mode)
     torch.cuda.synchronize()
     return (tok.cpu().numpy(), acc.cpu().numpy(),
             dg.cpu().numpy() if dg is not None else None)
@@ -57,13 +63,14 @@ def run_oracle(oracle_mod, wl, rows=None):
                              dtype=wl.dtype)
 
 
-def check(oracle_mod, wl, dev, rows=None, label=""):
-    _say(f"[gpu] {label or wl.name}: B={wl.B} K={wl.K} V={wl.V} {wl.dtype}")
-    g_tok, g_acc, g_diag = run_gpu(wl, dev)
+def check(oracle_mod, wl, dev, rows=None, label="", step_mode="auto"):
+    label = f"{label or wl.name}[{step_mode}]"
+    _say(f"[gpu] {label}: B={wl.B} K={wl.K} V={wl.V} {wl.dtype}")
+    g_tok, g_acc, g_diag = run_gpu(wl, dev, step_mode=step_mode)
     ref = run_oracle(oracle_mod, wl, rows)
     rep = compare(g_tok, g_acc, g_diag, ref, rows,
                   inputs=wl if rows is None else subset(wl, rows), oracle_mod=oracle_mod)
-    _say(f"[gpu] {label or wl.name}: {rep.describe()}")
+    _say(f"[gpu] {label}: {rep.describe()}")
     assert rep.ok, rep.describe()
     # greedy and top-k rows decide in fp64 from exact selections: no outcome
     # may differ there, in band or not
@@ -77,11 +84,36 @@ RECIPES = ["tiny_v1000", "decode_b1", "mixed_greedy_b64", "fullvocab_ragged_b256
 
 @pytest.mark.parametrize("name", RECIPES)
 def test_recipe_parity(oracle_mod, dev, name):
-    # every row of each recipe at its full size (tiny_v1000: 10,000 steps)
+    # every row of each recipe at its full size (tiny_v1000: 10,000 steps), in
+    # the mode the library picks (dense for the two small batches)
     wl = workloads.make(name, poison=(name == "fullvocab_ragged_b256"))
     rep, _, _ = check(oracle_mod, wl, dev)
     assert rep.compared == wl.B
     assert rep.unsupported == 0
+
+
+@pytest.mark.parametrize("name", ["decode_b1", "mixed_greedy_b64"])
+def test_small_recipes_position_by_position(oracle_mod, dev, name):
+    wl = workloads.make(name)
+    rep, _, _ = check(oracle_mod, wl, dev, step_mode="positions")
+    assert rep.compared == wl.B
+
+
+@pytest.mark.parametrize("name,batch,vocab", [("mixed_samplers_b1024", 120, 30011),
+                                              ("fullvocab_ragged_b256", 100, 20011),
+                                              ("mixed_greedy_b64", None, None),
+                                              ("decode_b1", None, None)])
+def test_dense_matches_positions(dev, name, batch, vocab):
+    """The dense step and the position-by-position step give bitwise the same
+    outputs and diagnostics (the records they merge are the same: per (tile,
+    wave) for untruncated rows, exact keys and fixed-point histograms
+    otherwise)."""
+    wl = workloads.make(name, batch=batch, vocab=vocab)
+    a = run_gpu(wl, dev, step_mode="positions")
+    b = run_gpu(wl, dev, step_mode="dense")
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y, equal_nan=True)
+    _say(f"[gpu] dense == positions on {name} B={wl.B} V={wl.V}")
 
 
 @pytest.mark.parametrize("name", ["mixed_greedy_b64", "fullvocab_ragged_b256",
@@ -146,22 +178,31 @@ EDGE = [
 ]
 
 
-@pytest.mark.parametrize("label,B,K,V,dtype,T,top_k,top_p,extra", EDGE, ids=[e[0] for e in EDGE])
-def test_edge_cases(oracle_mod, dev, label, B, K, V, dtype, T, top_k, top_p, extra):
+EDGE_MODES = [e + (m,) for e in EDGE for m in modes_for(e[1], e[2])]
+
+
+@pytest.mark.parametrize("label,B,K,V,dtype,T,top_k,top_p,extra,mode", EDGE_MODES,
+                         ids=[f"{e[0]}-{e[-1]}" for e in EDGE_MODES])
+def test_edge_cases(oracle_mod, dev, label, B, K, V, dtype, T, top_k, top_p, extra, mode):
     rng = np.random.default_rng(zlib.crc32(label.encode()))
     wl = _random_case(rng, B, K, V, dtype, T, top_k, top_p, **extra)
-    rep, _, _ = check(oracle_mod, wl, dev, label=label)
+    rep, _, _ = check(oracle_mod, wl, dev, label=label, step_mode=mode)
     assert rep.unsupported == 0 and rep.compared == B
 
 
-def test_ragged_draft_len_and_zero(oracle_mod, dev):
+@pytest.mark.parametrize("mode", ["positions", "dense"])
+def test_ragged_draft_len_and_zero(oracle_mod, dev, mode):
     rng = np.random.default_rng(5)
     L = rng.integers(0, 4, 80).astype(np.int32)
     wl = _random_case(rng, 80, 3, 20000, "bf16", 1.0, 20, 0.9, draft_len=L)
-    check(oracle_mod, wl, dev, label="ragged_draft_len")
+    wl.params["top_k"][::3] = 0   # and nucleus rows
+    wl.params["top_p"][1::6] = 1.0
+    wl.params["temperature"][2::5] = 0.0
+    check(oracle_mod, wl, dev, label="ragged_draft_len", step_mode=mode)
 
 
-def test_invalid_rows(oracle_mod, dev):
+@pytest.mark.parametrize("mode", ["positions", "dense"])
+def test_invalid_rows(oracle_mod, dev, mode):
     rng = np.random.default_rng(6)
     wl = _random_case(rng, 12, 2, 3000, "f32", 1.0, 20, 0.9)
     wl.params["temperature"][1] = -1.0
@@ -172,7 +213,7 @@ def test_invalid_rows(oracle_mod, dev):
     wl.tokens[6, 0] = -4
     wl.draft_len[7] = -1
     wl.target[8, :, :] = -np.inf
-    rep, g_tok, g_acc = check(oracle_mod, wl, dev, label="invalid_rows")
+    rep, g_tok, g_acc = check(oracle_mod, wl, dev, label="invalid_rows", step_mode=mode)
     assert g_acc[1:9].tolist() == [-1] * 8
     assert (g_tok[1:9] == -1).all()
 
@@ -204,7 +245,8 @@ def _to_padded(x, pad, offset, fill):
     ("bf16", 50000, 16, 0),
     ("bf16", 20011, 5, 3),
 ], ids=["f32_aligned", "f32_unaligned", "bf16_aligned", "bf16_unaligned"])
-def test_strided_rows(oracle_mod, dev, dtype, V, pad, offset):
+@pytest.mark.parametrize("mode", ["positions", "dense"])
+def test_strided_rows(oracle_mod, dev, dtype, V, pad, offset, mode):
     import torch
 
     import rejection_sampling_verify_sv_amd as sv
@@ -222,7 +264,7 @@ def test_strided_rows(oracle_mod, dev, dtype, V, pad, offset):
     dp = _to_padded(d, pad, offset, float("inf"))
     assert tp.stride(1) == V + pad and tp.data_ptr() % 16 == (offset * tp.element_size()) % 16
     _say(f"[gpu] strided rows {dtype} V={V} stride={V + pad} offset={offset}")
-    g_tok, g_acc, g_dg = sv.verify(tp, dp, tok, dl, pt, uni, diag=True)
+    g_tok, g_acc, g_dg = sv.verify(tp, dp, tok, dl, pt, uni, diag=True, step_mode=mode)
     torch.cuda.synchronize()
     rep = compare(g_tok.cpu().numpy(), g_acc.cpu().numpy(), g_dg.cpu().numpy(),
                   run_oracle(oracle_mod, wl), inputs=wl, oracle_mod=oracle_mod)
@@ -230,7 +272,7 @@ def test_strided_rows(oracle_mod, dev, dtype, V, pad, offset):
     assert rep.ok, rep.describe()
     assert rep.unsupported == 0 and rep.error_rows == 0
     # the same inputs packed densely give the same bits
-    c_tok, c_acc, c_dg = run_gpu(wl, dev)
+    c_tok, c_acc, c_dg = run_gpu(wl, dev, step_mode=mode)
     assert np.array_equal(c_tok, g_tok.cpu().numpy())
     assert np.array_equal(c_acc, g_acc.cpu().numpy())
     assert np.array_equal(c_dg, g_dg.cpu().numpy(), equal_nan=True)
@@ -253,7 +295,8 @@ def test_side_stream(dev):
         assert np.array_equal(x, y, equal_nan=True)
 
 
-def test_top_k_above_limit_unsupported(oracle_mod, dev):
+@pytest.mark.parametrize("mode", ["positions", "dense"])
+def test_top_k_above_limit_unsupported(oracle_mod, dev, mode):
     import rejection_sampling_verify_sv_amd as sv
 
     rng = np.random.default_rng(11)
@@ -262,19 +305,20 @@ def test_top_k_above_limit_unsupported(oracle_mod, dev):
     bad = [1, 4, 9, 17]
     wl.params["top_k"][bad] = [sv.SV_MAX_TOP_K + 1, 100, V - 1, 2 * sv.SV_MAX_TOP_K]
     wl.params["top_k"][[2, 3]] = [sv.SV_MAX_TOP_K, V]   # served: the limit itself, and top_k = V
-    rep, g_tok, g_acc = check(oracle_mod, wl, dev, label="top_k_above_limit")
+    rep, g_tok, g_acc = check(oracle_mod, wl, dev, label="top_k_above_limit", step_mode=mode)
     assert g_acc[bad].tolist() == [-2] * len(bad)
     assert (g_tok[bad] == -1).all()
     assert rep.unsupported == len(bad)
     assert rep.compared == wl.B - len(bad)
 
 
+@pytest.mark.parametrize("mode", ["positions", "dense"])
 @pytest.mark.parametrize("dtype,K,top_k,top_p", [
     ("bf16", 8, 20, 0.9),
     ("f32", 7, 0, 0.8),
     ("bf16", 8, 0, 1.0),
 ], ids=["topk_K8", "nucleus_K7", "untruncated_K8"])
-def test_long_drafts(oracle_mod, dev, dtype, K, top_k, top_p):
+def test_long_drafts(oracle_mod, dev, dtype, K, top_k, top_p, mode):
     rng = np.random.default_rng(K * 100 + top_k)
     B, V = 40, 20011
     L = rng.integers(K - 2, K + 1, B).astype(np.int32)
@@ -282,7 +326,8 @@ def test_long_drafts(oracle_mod, dev, dtype, K, top_k, top_p):
     # drafts close to the target so that acceptance runs deep into the draft
     wl_close = _random_case(rng, B, K, V, dtype, 1.0, top_k, top_p, draft_len=L, noise=0.1)
     for case, lab in ((wl, "random"), (wl_close, "close")):
-        rep, _, g_acc = check(oracle_mod, case, dev, label=f"long_drafts_{lab}_{dtype}_K{K}")
+        rep, _, g_acc = check(oracle_mod, case, dev, label=f"long_drafts_{lab}_{dtype}_K{K}",
+                              step_mode=mode)
         assert rep.unsupported == 0
 
 
@@ -299,16 +344,18 @@ EXTREME_T = [
 ]
 
 
+@pytest.mark.parametrize("mode", ["positions", "dense"])
 @pytest.mark.parametrize("label,V,dtype,T,top_k,top_p,scale", EXTREME_T,
                          ids=[e[0] for e in EXTREME_T])
-def test_extreme_temperature(oracle_mod, dev, label, V, dtype, T, top_k, top_p, scale):
+def test_extreme_temperature(oracle_mod, dev, label, V, dtype, T, top_k, top_p, scale, mode):
     rng = np.random.default_rng(zlib.crc32(label.encode()))
     wl = _random_case(rng, 32, 2, V, dtype, T, top_k, top_p, scale=scale)
-    rep, _, _ = check(oracle_mod, wl, dev, label=label)
+    rep, _, _ = check(oracle_mod, wl, dev, label=label, step_mode=mode)
     assert rep.unsupported == 0 and rep.error_rows == 0
 
 
-def test_nucleus_anchor_cases(oracle_mod, dev):
+@pytest.mark.parametrize("mode", ["positions", "dense"])
+def test_nucleus_anchor_cases(oracle_mod, dev, mode):
     """Nucleus rows measured against the anchor window: rows whose max lies
     far above the largest of the first 64 vectors (second histogram pass),
     rows whose first vectors are all -inf, and ordinary rows, in one batch."""
@@ -326,12 +373,13 @@ def test_nucleus_anchor_cases(oracle_mod, dev):
     for b in range(1, B, 3):       # the anchor's vectors hold no finite logit
         wl.target[b, :, :512] = -np.inf
         wl.draft[b, :, :512] = -np.inf
-    rep, _, g_acc = check(oracle_mod, wl, dev, label="nucleus_anchor_cases")
+    rep, _, g_acc = check(oracle_mod, wl, dev, label="nucleus_anchor_cases", step_mode=mode)
     assert rep.unsupported == 0 and rep.error_rows == 0 and rep.compared == B
 
 
+@pytest.mark.parametrize("mode", ["positions", "dense"])
 @pytest.mark.parametrize("B", [8, 80], ids=["split_units", "one_workgroup_per_unit"])
-def test_nucleus_boundary_in_one_wave(oracle_mod, dev, B):
+def test_nucleus_boundary_in_one_wave(oracle_mod, dev, B, mode):
     """A boundary bucket of 2000 equal logits, all at offsets that one wave
     of a 4096-element tile reads: with one workgroup per unit (80 rows, 160
     nucleus units) that wave's share of the collect buffer overflows and the
@@ -356,5 +404,6 @@ def test_nucleus_boundary_in_one_wave(oracle_mod, dev, B):
             tok[b, k] = int(np.argmax(d[b, k] + rng.gumbel(size=V)))
     u = rng.random((B, K + 1), dtype=np.float32)
     wl = workloads.custom(t, d, tok, np.full(B, K, np.int32), prm, u, dtype="f32")
-    rep, _, _ = check(oracle_mod, wl, dev, label=f"nucleus_boundary_in_one_wave_B{B}")
+    rep, _, _ = check(oracle_mod, wl, dev, label=f"nucleus_boundary_in_one_wave_B{B}",
+                      step_mode=mode)
     assert rep.unsupported == 0 and rep.error_rows == 0 and rep.compared == B
