@@ -258,6 +258,7 @@ def measure(wl, dev, steps, warmup, replicas=1, ceiling=None, step_mode="auto"):
     nl = len(names)
     per_kernel = {}
     rowpass_ms = []
+    cut_ms = []
     evsets = [hip.events(nl + 1) for _ in range(steps)]
     torch.cuda.synchronize()
     for s in range(steps):
@@ -269,10 +270,13 @@ def measure(wl, dev, steps, warmup, replicas=1, ceiling=None, step_mode="auto"):
             per_kernel[n] = per_kernel.get(n, 0.0) + ms / steps
             if n == "rowpass":
                 rowpass_ms.append(ms)
+            elif n == "cut_decide":
+                cut_ms.append(ms)
         hip.destroy(evsets[s])
     rowpass_launches = names.count("rowpass")
     rowpass_mean_ms = float(np.mean(rowpass_ms))
     by_pos_ms = np.mean(np.asarray(rowpass_ms).reshape(steps, rowpass_launches), axis=0)
+    cut_by_pos_ms = np.mean(np.asarray(cut_ms).reshape(steps, -1), axis=0)
     kernel_ms_step = float(sum(per_kernel.values()))
 
     acc = out_acc.cpu().numpy()
@@ -325,6 +329,7 @@ def measure(wl, dev, steps, warmup, replicas=1, ceiling=None, step_mode="auto"):
         "kernels_ms_per_step": {k: round(v, 4) for k, v in per_kernel.items()},
         "rowpass_by_position": [{"ms": round(float(m), 4), "GBps": round(b / (m * 1e-3) / 1e9, 1)}
                                 for m, b in zip(by_pos_ms, pos_bytes)],
+        "cut_decide_ms_by_launch": [round(float(m), 4) for m in cut_by_pos_ms],
         "acceptance_rate": round(float(acc[served].sum() / max(1, L[served].sum())), 4),
         "verify_calls": calls[0],
     }
@@ -498,6 +503,7 @@ def main():
         "read_ceiling": ceil,
         "kernels_ms_per_step": res["kernels_ms_per_step"],
         "rowpass_by_position": res["rowpass_by_position"],
+        "cut_decide_ms_by_launch": res["cut_decide_ms_by_launch"],
         "acceptance_rate": res["acceptance_rate"],
         "verify_calls": res["verify_calls"],
     }

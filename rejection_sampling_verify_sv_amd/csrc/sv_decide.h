@@ -100,21 +100,62 @@ __device__ __forceinline__ int first_lane(bool pred) {
     return m ? __ffsll((unsigned long long)m) - 1 : -1;
 }
 
-// Top-64 keys (descending, lane j = j-th) of one unit from its records.
+// Top-64 keys (descending, lane j = j-th) of one or two units from their
+// records, merged in record order.  The first kPreRec records of both units
+// are loaded before the first merge: the decision then waits about one memory
+// round trip for them, not one per record.
+constexpr int kPreRec = 8;
+__device__ __forceinline__ void unit_tops(const PartSlot* parts, RecRange ra, RecRange rb,
+                                          bool two, uint64_t* ta, uint64_t* tb) {
+    const int lane = lane_id();
+    uint64_t xa[kPreRec], xb[kPreRec];
+#pragma unroll
+    for (int j = 0; j < kPreRec; j++) {
+        xa[j] = j < ra.count ? parts[ra.first + j].keys[lane] : 0ull;
+        xb[j] = (two && j < rb.count) ? parts[rb.first + j].keys[lane] : 0ull;
+    }
+    uint64_t x = xa[0], y = xb[0];
+#pragma unroll
+    for (int j = 1; j < kPreRec; j++) {
+        if (j < ra.count) x = wave_merge_top(x, xa[j]);
+        if (two && j < rb.count) y = wave_merge_top(y, xb[j]);
+    }
+    for (int i = kPreRec; i < ra.count; i++) x = wave_merge_top(x, parts[ra.first + i].keys[lane]);
+    if (two)
+        for (int i = kPreRec; i < rb.count; i++) y = wave_merge_top(y, parts[rb.first + i].keys[lane]);
+    *ta = x;
+    *tb = y;
+}
 __device__ __forceinline__ uint64_t unit_top(const PartSlot* parts, RecRange r) {
-    const PartSlot* s = parts + r.first;
-    uint64_t acc = s[0].keys[lane_id()];
-    for (int i = 1; i < r.count; i++) acc = wave_merge_top(acc, s[i].keys[lane_id()]);
-    return acc;
+    uint64_t x, y;
+    unit_tops(parts, r, r, false, &x, &y);
+    return x;
 }
 
 // Record slots of unit (b, position k, side) of row class cls: in the list of
 // position k's launch, or of the one launch of a dense step.
-__device__ __forceinline__ RecRange unit_rec(const StepArgs& a, const RowInfo& ri, int cls, int b,
-                                             int k, int side) {
-    const PosDesc& P = a.pos[a.dense ? 0 : k];
-    const int li = a.dense ? a.dli[unit_code(a, b, k, side)] : (side ? ri.li_d : ri.li_t);
+// P: the descriptor of the launch that streamed the unit (position k's, or
+// the dense step's one launch), held in LDS by the caller.
+__device__ __forceinline__ RecRange unit_rec(const StepArgs& a, const PosDesc& P, int cls, int li) {
     return unit_records(P, unit_index(P, cls, li), a.ntiles, a.g_row);
+}
+// Index of unit (b, position k, side) in its class region: kept in the row's
+// info, or, in a dense step, in dli (loaded with the row's info).
+struct UnitIdx {
+    int t, d;
+};
+__device__ __forceinline__ UnitIdx unit_idx_prefetch(const StepArgs& a, int b, int k) {
+    UnitIdx u;
+    u.t = a.dense ? a.dli[unit_code(a, b, k, 0)] : -1;
+    u.d = a.dense ? a.dli[unit_code(a, b, k, 1)] : -1;
+    return u;
+}
+__device__ __forceinline__ UnitIdx unit_idx(const StepArgs& a, const RowInfo& ri, UnitIdx pre) {
+    if (a.dense) return pre;
+    UnitIdx u;
+    u.t = ri.li_t;
+    u.d = ri.li_d;
+    return u;
 }
 
 // Truncated distribution over a ranked list (lane j = j-th ranked token):
@@ -307,23 +348,23 @@ __device__ void topk_draw(const StepArgs& a, int b, int k, double p, bool keep_p
 
 // Returns true (in every lane) when the row accepted and goes on to the next
 // position; the same for the other classes below.
-__device__ bool decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, TopkScratch& ts,
-                            DecideIntent& it) {
+__device__ bool decide_topk(const StepArgs& a, const PosDesc& P, int b, int k, const RowInfo& ri,
+                            UnitIdx ui, TopkScratch& ts, DecideIntent& it) {
     const int k_eff = ri.k_eff;
     const double T = (double)ri.T, top_p = (double)ri.top_p;
     const int child = first_child(a, b, k, ri);
     const bool has_draft = child >= 0;
     const float* u = a.uniforms + (int64_t)b * (a.K + 1);
     // every load first, so that their latencies overlap
-    const uint64_t kt = unit_top(a.parts, unit_rec(a, ri, CLS_TOPK, b, k, 0));
-    uint64_t kd = 0ull;
     int x = 0;
     double uk = 0.0;
     if (has_draft) {
-        kd = unit_top(a.parts, unit_rec(a, ri, CLS_TOPK, b, k, 1));
         x = a.tokens[(int64_t)b * a.K + child - 1];
         uk = (double)u[child - 1];
     }
+    uint64_t kt, kd;
+    unit_tops(a.parts, unit_rec(a, P, CLS_TOPK, ui.t), unit_rec(a, P, CLS_TOPK, ui.d), has_draft,
+              &kt, &kd);
     const double uf = (double)u[a.K];
     double p;
     bool keep_p;
@@ -391,10 +432,12 @@ __device__ bool decide_topk(const StepArgs& a, int b, int k, const RowInfo& ri, 
     return false;
 }
 
-__device__ bool decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri,
-                              DecideIntent& it) {
+__device__ bool decide_greedy(const StepArgs& a, const PosDesc& P, int b, int k,
+                              const RowInfo& ri, UnitIdx ui, DecideIntent& it) {
     const int lane = lane_id();
-    const RecRange r = unit_rec(a, ri, CLS_GREEDY, b, k, 0);
+    // the drafted token, loaded with the records
+    const int tok = (!a.tree && k < ri.L) ? a.tokens[(int64_t)b * a.K + k] : -1;
+    const RecRange r = unit_rec(a, P, CLS_GREEDY, ui.t);
     const PartSlot* s = a.parts + r.first;
     uint64_t best = 0ull;
     for (int i = lane; i < r.count; i += kWave) best = s[i].keys[0] > best ? s[i].keys[0] : best;
@@ -407,7 +450,7 @@ __device__ bool decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri
             if (lane == 0) tree_continue(a, b, k, c, g, kids, ri, it);
             return true;
         }
-    } else if (k < ri.L && a.tokens[(int64_t)b * a.K + k] == g) {
+    } else if (k < ri.L && tok == g) {
         continue_row(a, b, k, ri, it);
         return true;
     }
@@ -419,20 +462,60 @@ __device__ bool decide_greedy(const StepArgs& a, int b, int k, const RowInfo& ri
 // {m_i, s_i}: M = max m_i, Z = sum s_i exp((m_i - M) / T), each lane summing
 // its records in index order and the lanes in the fixed DPP tree, so every
 // lane gets the same bits.  One exp per record, none along the tree.
-__device__ inline void full_stats(const FullStat* rec, int n, double invT, double* m, double* z) {
+// Two units at once (rb may be null): the first kPreStat records of each lane
+// of both are loaded before any is used.
+constexpr int kPreStat = 4;
+__device__ inline void full_stats2(const FullStat* ra, const FullStat* rb, int n, double invT,
+                                   double* ma, double* za, double* mb, double* zb) {
     const int lane = lane_id();
-    float mm = -INFINITY;
-    for (int i = lane; i < n; i += kWave) mm = fmaxf(mm, rec[i].m);
-    const float M = wave_max_f32(mm);
-    double ss = 0.0;
-    if (M > -INFINITY) {
-        for (int i = lane; i < n; i += kWave) {
-            const FullStat r = rec[i];
-            if (r.m > -INFINITY) ss += r.s * exp(((double)r.m - (double)M) * invT);
+    FullStat xa[kPreStat], xb[kPreStat];
+#pragma unroll
+    for (int j = 0; j < kPreStat; j++) {
+        const int i = lane + j * kWave;
+        xa[j].m = -INFINITY;
+        xa[j].s = 0.0;
+        xb[j] = xa[j];
+        if (i < n) {
+            xa[j] = ra[i];
+            if (rb) xb[j] = rb[i];
         }
     }
-    *m = (double)M;
-    *z = wave_sum(ss);
+    float mx = -INFINITY, my = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kPreStat; j++) {
+        mx = fmaxf(mx, xa[j].m);
+        my = fmaxf(my, xb[j].m);
+    }
+    for (int i = lane + kPreStat * kWave; i < n; i += kWave) {
+        mx = fmaxf(mx, ra[i].m);
+        if (rb) my = fmaxf(my, rb[i].m);
+    }
+    const float MX = wave_max_f32(mx), MY = wave_max_f32(my);
+    double sx = 0.0, sy = 0.0;
+#pragma unroll
+    for (int j = 0; j < kPreStat; j++) {
+        if (MX > -INFINITY && xa[j].m > -INFINITY)
+            sx += xa[j].s * exp(((double)xa[j].m - (double)MX) * invT);
+        if (MY > -INFINITY && xb[j].m > -INFINITY)
+            sy += xb[j].s * exp(((double)xb[j].m - (double)MY) * invT);
+    }
+    for (int i = lane + kPreStat * kWave; i < n; i += kWave) {
+        const FullStat r = ra[i];
+        if (MX > -INFINITY && r.m > -INFINITY) sx += r.s * exp(((double)r.m - (double)MX) * invT);
+        if (rb) {
+            const FullStat q = rb[i];
+            if (MY > -INFINITY && q.m > -INFINITY)
+                sy += q.s * exp(((double)q.m - (double)MY) * invT);
+        }
+    }
+    *ma = (double)MX;
+    *za = wave_sum(sx);
+    *mb = (double)MY;
+    *zb = wave_sum(sy);
+}
+__device__ inline void full_stats(const FullStat* rec, int n, double invT, double* m, double* z) {
+    double m2, z2;
+    full_stats2(rec, nullptr, n, invT, m, z, &m2, &z2);
 }
 
 // Tree verify, full-vocab rows: the row rejected child `c` of its node and the
@@ -464,7 +547,9 @@ __device__ bool decide_full(const StepArgs& a, int b, int k, const RowInfo& ri, 
         }
         ukf = a.uniforms[(int64_t)b * (a.K + 1) + child - 1];
     }
-    full_stats(a.tstat + (int64_t)unit_code(a, b, k, 0) * nrec, nrec, invT, &mt, &zt);
+    full_stats2(a.tstat + (int64_t)unit_code(a, b, k, 0) * nrec,
+                child >= 0 ? a.tstat + (int64_t)unit_code(a, b, k, 1) * nrec : nullptr, nrec, invT,
+                &mt, &zt, &md, &zd);
     if (!(mt > -INFINITY)) {
         close_row_invalid(a, b, -1);
         return false;
@@ -480,7 +565,6 @@ __device__ bool decide_full(const StepArgs& a, int b, int k, const RowInfo& ri, 
         }
         return false;
     }
-    full_stats(a.tstat + (int64_t)unit_code(a, b, k, 1) * nrec, nrec, invT, &md, &zd);
     if (!(md > -INFINITY)) {
         close_row_invalid(a, b, -1);
         return false;
@@ -609,7 +693,8 @@ __device__ bool decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& r
 // around it; the arguments come from their copy in device memory (a kernel
 // argument passed by reference would be copied to private memory first).
 template <int DT>
-__device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, int k, int b_w,
+__device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, const PosDesc* sP, int k,
+                                                      int b_w,
                                                       bool skip_nucleus, DecideIntent* s_it,
                                                       int* s_base, TopkScratch* s_ts) {
     const StepArgs& a = *ga;
@@ -622,16 +707,18 @@ __device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, int k,
     }
     if (b_w >= 0) {
         const int b = b_w;
+        const UnitIdx pre = unit_idx_prefetch(a, b, k);  // loaded with the row's info
         const RowInfo ri = a.rows[b];
+        const UnitIdx ui = unit_idx(a, ri, pre);
         // a dense step decides position k of the rows that accepted every
         // position before it (the caller walks the positions)
         if (ri.status == ST_LIVE && k <= ri.L && !(skip_nucleus && ri.cls == CLS_NUCLEUS) &&
             (!a.dense || ri.acc == k)) {
             DecideIntent& it = s_it[w];
             if (ri.cls == CLS_GREEDY)
-                decide_greedy(a, b, k, ri, it);
+                decide_greedy(a, *sP, b, k, ri, ui, it);
             else if (ri.cls == CLS_TOPK)
-                decide_topk(a, b, k, ri, s_ts[w], it);
+                decide_topk(a, *sP, b, k, ri, ui, s_ts[w], it);
             else if (ri.cls == CLS_NUCLEUS)
                 decide_nucleus<DT>(a, b, k, ri, it);
             else

@@ -132,6 +132,10 @@ constexpr int kHalf = kNW / 2;
 constexpr float kBucketScale = 64.0f;
 constexpr float kLog2e64 = 0.022542110013490055f;  // log2(e) / 64
 constexpr int kCollectCap = 4096;   // boundary-bucket tokens resolved in LDS per unit
+// A row-pass piece writes out the buckets from its max's bucket down to 2048
+// below it (the lower ones weigh under e^-32 of the piece max), starting at an
+// even bucket: at most 2050 of them, stored from the slot's start.
+constexpr int kHistSlot = 2056;
 constexpr double kUnfix = 1.0 / 2147483648.0;    // 2^-31, the weights' fixed-point unit
 
 // Bucket scale 64 / T, clamped finite like exp2_coef.
@@ -989,7 +993,7 @@ struct StepArgs {
     int32_t* ulist;        // [K+1][kNumCls][2B] units to stream per position and class
     int32_t* slist;        // [B] rows that draw over the full vocabulary at the end
     FnUnit* fn_unit;       // [2B] nucleus cut of the current position
-    uint64_t* hist;        // [2B + kGrid][kNW] nucleus histograms of the row pass, slot u + w
+    uint64_t* hist;        // [units + kGrid][kHistSlot] nucleus histograms of the row pass, slot u + w
     uint64_t* fn_keys;     // [kGrid / 2][kCollectCap] boundary keys of a unit whose cut is split
     int32_t* fn_sync;      // [kGrid / 2][2] per split unit: workgroups arrived, keys reserved
     int32_t* fn_row;       // [B] nucleus units of the row whose cut is complete

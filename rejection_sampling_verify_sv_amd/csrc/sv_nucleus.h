@@ -346,9 +346,11 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
     __shared__ int s_dbase[kNumCls + 2];
     constexpr int kPend = 32;  // completed nucleus rows awaiting their decision
     __shared__ int s_pend[kPend], s_npend;
+    __shared__ PosDesc s_P;  // this launch's lists, for the decisions
     static_assert(sizeof(TopkScratch) * kWaves <= sizeof(uint64_t) * kCollectCap,
                   "the decisions' scratch lies over s_key");
     const PosDesc P = a.pos[k];
+    if (threadIdx.x == 0) s_P = P;  // read after the barriers below
     const int n_units = P.n_cls[CLS_NUCLEUS];
     const int32_t* list = nuc_list(a, k);
     // Few units: each is split over S workgroups, which all find the same
@@ -386,9 +388,9 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
             });
         } else {
             // thread t sums buckets t + q kThreads over the pieces in
-            // registers; a piece holds the buckets [lo, hi] of its slot's
-            // range (the rest are stale and masked off), so its loads go out
-            // together with that of its range
+            // registers; a piece's slot holds its buckets [lo, hi] from the
+            // slot's start (every load is clamped into the slot and the
+            // buckets outside the range masked off)
             constexpr int kPer = kNW / kThreads;
             la = fu->la;
             uint64_t acc[kPer];
@@ -396,11 +398,15 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
             for (int q = 0; q < kPer; q++) acc[q] = 0ull;
             for (int p = 0; p < rr.count; p++) {
                 const uint64_t rg = a.parts[rr.first + p].keys[1];
-                const uint64_t* h = a.hist + (int64_t)(rr.first + p) * kNW + threadIdx.x;
+                const uint64_t* h = a.hist + (int64_t)(rr.first + p) * kHistSlot;
+                const int lo = (int)(uint32_t)(rg >> 32), hi = (int)(uint32_t)rg;
                 uint64_t x[kPer];
 #pragma unroll
-                for (int q = 0; q < kPer; q++) x[q] = h[q * kThreads];
-                const int lo = (int)(uint32_t)(rg >> 32), hi = (int)(uint32_t)rg;
+                for (int q = 0; q < kPer; q++) {
+                    int i = q * kThreads + (int)threadIdx.x - lo;
+                    i = i < 0 ? 0 : (i > kHistSlot - 1 ? kHistSlot - 1 : i);
+                    x[q] = h[i];
+                }
 #pragma unroll
                 for (int q = 0; q < kPer; q++) {
                     const int j = q * kThreads + (int)threadIdx.x;
@@ -467,15 +473,14 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
                 filled += __popcll(m);
             }
         };
-        // a split unit's workgroup streams a short slice alone: keep more
-        // tiles in flight; one workgroup per unit means many units, which
-        // share HBM evenly with the plain double buffer
-        if (S > 1) {
+        // kRing tiles in flight: the cuts run at two workgroups per compute
+        // unit at most (registers, LDS), often fewer, and the double buffer
+        // of the row pass left the re-read latency-bound (about 4 TB/s over
+        // a few hundred units on the 1024-row mix)
+        {
             TileRing<DT, kAligned, kRing> ring;
             ring.start(row, e_lo, e_hi);
             ring.run(row, e_lo, e_hi, cbody);
-        } else {
-            stream_range<DT, kAligned>(row, e_lo, e_hi, cbody);
         }
         if (lane_id() == 0) s_wcnt[wave_id()] = filled;
         __syncthreads();
@@ -642,7 +647,8 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
         for (int i = 0; i < np; i += kWaves) {
             const int j = i + wave_id();
             for (int kk = k; kk <= k_last; kk++) {
-                decide_rows<DT>(a.self, kk, j < np ? s_pend[j] : -1, false, s_it, s_dbase, s_ts);
+                decide_rows<DT>(a.self, &s_P, kk, j < np ? s_pend[j] : -1, false, s_it, s_dbase,
+                                s_ts);
                 __syncthreads();
             }
         }
@@ -657,7 +663,8 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
             for (int r = r0; r < r0 + R && r < a.B; r += kDecideRows) {
                 const int bw = r + wave_id();
                 for (int kk = k; kk <= k_last; kk++) {
-                    decide_rows<DT>(a.self, kk, bw < a.B ? bw : -1, true, s_it, s_dbase, s_ts);
+                    decide_rows<DT>(a.self, &s_P, kk, bw < a.B ? bw : -1, true, s_it, s_dbase,
+                                    s_ts);
                     __syncthreads();  // LDS is reused by the next rows
                 }
             }

@@ -283,9 +283,10 @@ __device__ __forceinline__ void seg_full(const void* row, int64_t start, int64_t
 // gets the same value; the loads go out before the first tile's and are
 // reduced once that tile has arrived.  Written out: the buckets from the
 // piece max's bucket down to 2048 below it (lower ones weigh under e^-32 of
-// the piece max), their range in keys[1] of the slot and the piece max in
-// keys[0] (float bits).  A piece max above the window marks the unit for the
-// second histogram pass.
+// the piece max), from an even bucket lo on, at the start of the slot; their
+// range [lo, hi] in keys[1] of the record and the piece max in keys[0] (float
+// bits).  A piece max above the window marks the unit for the second
+// histogram pass.
 template <int DT, bool kAligned>
 __device__ __forceinline__ void seg_nuc(const void* row, int64_t start, int64_t end, int64_t V,
                                         float T, uint64_t* s_h, RowpassSmem& sm, PartSlot* out,
@@ -326,9 +327,10 @@ __device__ __forceinline__ void seg_nuc(const void* row, int64_t start, int64_t 
     const float pm = block_max_f32(lmax, sm.red);  // barriers
     const float tm = nuc_t(pm, la, cb);
     const int hi = nuc_in(tm) ? nuc_bin(tm) : (tm >= (float)kHalf ? kNW - 1 : -1);
-    const int lo = hi - 2048 > 0 ? hi - 2048 : 0;
+    const int lo = (hi - 2048 > 0 ? hi - 2048 : 0) & ~1;  // even: pairs of buckets per store
     u32x4* o4 = reinterpret_cast<u32x4*>(hout);
-    for (int i = (lo >> 1) + (int)threadIdx.x; i <= (hi >> 1); i += kThreads) o4[i] = h4[i];
+    for (int i = (lo >> 1) + (int)threadIdx.x; i <= (hi >> 1); i += kThreads)
+        o4[i - (lo >> 1)] = h4[i];
     if (threadIdx.x == 0) {
         out->keys[0] = (uint64_t)__float_as_uint(pm);
         out->keys[1] = ((uint64_t)(uint32_t)lo << 32) | (uint64_t)(uint32_t)hi;
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void rowpass_kernel(StepArgs a, int k) {
             seg_topk<DT, kAligned>(row, start, end, a.rows[b].k_eff, sm, out);
         else if (cls == CLS_NUCLEUS)
             seg_nuc<DT, kAligned>(row, start, end, a.V, a.rows[b].T, s_h, sm, out, a.fn_unit + u,
-                                  a.hist + (int64_t)(li + w) * kNW);
+                                  a.hist + (int64_t)(li + w) * kHistSlot);
         else
             seg_full<DT, kAligned>(row, start, end, a.rows[b].T,
                                    a.tstat + (int64_t)u * a.ntiles * kWaves);

@@ -71,7 +71,7 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
     p->off_tstat = take(sizeof(FullStat) * units * p->ntiles * kWaves);
     p->off_chunks = take(sizeof(double2) * (size_t)B * p->ntiles * kWaves);
     p->off_fnu = take(sizeof(FnUnit) * units);
-    p->off_hist = take(sizeof(uint64_t) * slots * kNW);
+    p->off_hist = take(sizeof(uint64_t) * slots * kHistSlot);
     // split nucleus units: their index in the position's list is below
     // min(2B, kGrid / 2)
     const size_t split_rows = units < (size_t)kGrid / 2 ? units : (size_t)kGrid / 2;
@@ -180,6 +180,15 @@ int grids_for_device(Grids* out) {
     return SV_OK;
 }
 
+// The streaming launches take at most one workgroup per tile of their largest
+// possible list: workgroups past that find no work, and a small batch would
+// otherwise start hundreds of them, all reading the same list descriptor
+// (which delays the few that work by several microseconds).
+unsigned stream_grid(unsigned resident, int64_t units, int ntiles) {
+    const int64_t t = units * (int64_t)ntiles;
+    return (unsigned)(t < (int64_t)resident ? (t > 0 ? t : 1) : (int64_t)resident);
+}
+
 // ev (optional, launch_count+1 events): ev[i] is recorded just before launch
 // i and ev[launch_count] after the last launch.
 template <int DT, bool kAligned>
@@ -188,7 +197,11 @@ int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepAr
     Grids g;
     const int rc = grids_for_device<DT, kAligned>(&g);
     if (rc != SV_OK) return rc;
-    a.g_row = (int)g.rowpass;
+    // units of one row-pass launch: every position's in a dense step
+    const unsigned grow =
+        stream_grid(g.rowpass, (int64_t)2 * a.B * (a.dense ? a.K + 1 : 1), a.ntiles);
+    const unsigned gsums = stream_grid(g.sums, a.B, a.ntiles);
+    a.g_row = (int)grow;
     int n = 0;
     auto mark = [&]() {
         if (ev) (void)hipEventRecord(ev[n], st);
@@ -203,13 +216,13 @@ int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepAr
     plan_kernel<<<1, kPlanThreads, 0, st>>>(a, draft_len, params);
     for (int k = 0; k <= (a.dense ? 0 : a.K); k++) {
         mark();
-        rowpass_kernel<DT, kAligned><<<g.rowpass, kThreads, 0, st>>>(a, k);
+        rowpass_kernel<DT, kAligned><<<grow, kThreads, 0, st>>>(a, k);
         mark();
         cut_decide_kernel<DT, kAligned><<<cut_grid, kThreads, 0, st>>>(a, k);
     }
     mark();
-    sample_sums_kernel<DT, kAligned><<<g.sums, kThreads, 0, st>>>(a, a.slist,
-                                                                 &a.pos[a.K + 1].n_sample);
+    sample_sums_kernel<DT, kAligned><<<gsums, kThreads, 0, st>>>(a, a.slist,
+                                                                &a.pos[a.K + 1].n_sample);
     mark();
     sample_pick_kernel<DT><<<row_grid, kThreads, 0, st>>>(a);
     mark();
@@ -225,7 +238,9 @@ int launch_tree(const int32_t* n_cand, const sv_sampler_params* params, StepArgs
     Grids g;
     const int rc = grids_for_device<DT, kAligned>(&g);
     if (rc != SV_OK) return rc;
-    a.g_row = (int)g.rowpass;
+    const unsigned grow = stream_grid(g.rowpass, (int64_t)2 * a.B, a.ntiles);
+    const unsigned gsums = stream_grid(g.sums, a.B, a.ntiles);
+    a.g_row = (int)grow;
     const int B = a.B;
     const unsigned cut_cap = (unsigned)(2 * B * kMaxSplit < kGrid ? 2 * B * kMaxSplit : kGrid);
     const unsigned cut_grid = g.cut < cut_cap ? g.cut : cut_cap;
@@ -233,16 +248,16 @@ int launch_tree(const int32_t* n_cand, const sv_sampler_params* params, StepArgs
     const unsigned wave_grid = (unsigned)((B + kWaves - 1) / kWaves);
     plan_kernel<<<1, kPlanThreads, 0, st>>>(a, n_cand, params);
     for (int k = 0; k <= a.max_depth; k++) {
-        rowpass_kernel<DT, kAligned><<<g.rowpass, kThreads, 0, st>>>(a, k);
+        rowpass_kernel<DT, kAligned><<<grow, kThreads, 0, st>>>(a, k);
         cut_decide_kernel<DT, kAligned><<<cut_grid, kThreads, 0, st>>>(a, k);
         for (int j = 1; j < a.max_kids; j++) {
-            sample_sums_kernel<DT, kAligned><<<g.sums, kThreads, 0, st>>>(
+            sample_sums_kernel<DT, kAligned><<<gsums, kThreads, 0, st>>>(
                 a, a.tlist + (int64_t)j * B, a.tcount + k * kMaxKids + j);
             tree_round_kernel<DT><<<wave_grid, kThreads, 0, st>>>(a, k, j);
         }
     }
-    sample_sums_kernel<DT, kAligned><<<g.sums, kThreads, 0, st>>>(a, a.slist,
-                                                                 &a.pos[a.K + 1].n_sample);
+    sample_sums_kernel<DT, kAligned><<<gsums, kThreads, 0, st>>>(a, a.slist,
+                                                                &a.pos[a.K + 1].n_sample);
     sample_pick_kernel<DT><<<row_grid, kThreads, 0, st>>>(a);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? SV_OK : hip_fail(e);
