@@ -280,8 +280,8 @@ __device__ __forceinline__ void seg_full(const void* row, int64_t start, int64_t
 // added in LDS one token at a time (fixed-point, so exact in any order).
 // The anchor is the largest of the row's first 64 vectors (64 kVec elements,
 // fewer when V is smaller): every wave of every piece reads the same ones and
-// gets the same value; the loads go out before the first tile's and are
-// reduced once that tile has arrived.  Written out: the buckets from the
+// gets the same value; the loads go out with the first tile's and are reduced
+// once that tile has arrived.  Written out: the buckets from the
 // piece max's bucket down to 2048 below it (lower ones weigh under e^-32 of
 // the piece max), from an even bucket lo on, at the start of the slot; their
 // range [lo, hi] in keys[1] of the record and the piece max in keys[0] (float
@@ -293,36 +293,73 @@ __device__ __forceinline__ void seg_nuc(const void* row, int64_t start, int64_t 
                                         FnUnit* fu, uint64_t* hout) {
     using TS = TileShape<DT>;
     constexpr int kVec = Elt<DT>::kVec;
-    float av[kVec];
-#pragma unroll
-    for (int e = 0; e < kVec; e++) {
-        const int64_t i = (int64_t)lane_id() * kVec + e;
-        av[e] = i < V ? load_one<DT>(row, i) : -INFINITY;
-    }
     const float cb = bucket_coef(T);
     u32x4* h4 = reinterpret_cast<u32x4*>(s_h);
     for (int i = threadIdx.x; i < kNW / 2; i += kThreads) h4[i] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
+    // The anchor's vectors: one range-checked 16-byte load per lane (vector
+    // `lane`), issued after the barrier above (whose fence would wait for
+    // it) and used once the first tile has arrived.
+    const int n_av = V < (int64_t)kWave * kVec ? (int)V : kWave * kVec;
+    const int nvec_av = n_av / kVec;
+    u32x4 q_av = u32x4{0u, 0u, 0u, 0u};
+    if constexpr (kAligned)
+        q_av = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(row, (uint32_t)nvec_av * 16u),
+                                                     lane_id() * 16, 0, 2 /* nt */);
     float lmax = -INFINITY, la = 0.f;
     bool first = true;
     stream_range<DT, kAligned>(row, start, end, [&](float (&v)[TS::kE], int64_t, bool)
                                                     __attribute__((always_inline)) {
         if (first) {
             first = false;
+            const int lane = lane_id();
+            float av[kVec];
+            if constexpr (kAligned) {
+                const uint32_t d[4] = {q_av.x, q_av.y, q_av.z, q_av.w};
+#pragma unroll
+                for (int e = 0; e < kVec; e++) {
+                    float x;
+                    if constexpr (DT == SV_F32)
+                        x = __uint_as_float(d[e]);
+                    else
+                        x = (e & 1) ? bf16_hi(d[e >> 1]) : bf16_lo(d[e >> 1]);
+                    av[e] = lane * kVec + e < n_av ? x : -INFINITY;
+                }
+                if (nvec_av * kVec < n_av) {  // wave-uniform: a vector straddles a short row's end
+#pragma unroll
+                    for (int e = 0; e < kVec; e++)
+                        if (lane == nvec_av && nvec_av * kVec + e < n_av)
+                            av[e] = load_one<DT>(row, nvec_av * kVec + e);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < kVec; e++) {
+                    const int i = lane * kVec + e;
+                    av[e] = i < n_av ? load_one<DT>(row, i) : -INFINITY;
+                }
+            }
             float m = av[0];
 #pragma unroll
             for (int e = 1; e < kVec; e++) m = fmaxf(m, av[e]);
             la = wave_max_f32(m);
         }
-        // elements past `end` read as -inf: t = -inf, outside the window
+        // elements past `end` read as -inf: t = -inf, outside the window.
+        // Tokens outside it add 0 to the spare slot s_h[kNW] (no branch per
+        // element).
 #pragma unroll
         for (int i = 0; i < TS::kE; i++) {
             lmax = fmaxf(lmax, v[i]);
             const float t = nuc_t(v[i], la, cb);
             int bin;
             const uint64_t w = nuc_wfix_t(t, &bin);
-            if (nuc_in(t)) atomicAdd((unsigned long long*)&s_h[bin], (unsigned long long)w);
+            const bool in = nuc_in(t);
+            atomicAdd((unsigned long long*)&s_h[in ? bin : kNW], (unsigned long long)(in ? w : 0ull));
         }
+        // The running max is formed here, before the next tile's loads reuse
+        // this tile's registers: left to the scheduler it was sunk to the end
+        // of the loop, the next loads went to other registers, and the loop
+        // copied them back after waiting for every outstanding load.
+        asm volatile("" : "+v"(lmax));
     });
     const float pm = block_max_f32(lmax, sm.red);  // barriers
     const float tm = nuc_t(pm, la, cb);
@@ -348,7 +385,7 @@ template <int DT, bool kAligned>
 __global__ __launch_bounds__(kThreads) void rowpass_kernel(StepArgs a, int k) {
     using TS = TileShape<DT>;
     __shared__ RowpassSmem sm;
-    __shared__ uint64_t s_h[kNW];  // nucleus pieces
+    __shared__ uint64_t s_h[kNW + 1];  // nucleus pieces (and a spare slot)
     const PosDesc P = a.pos[k];
     const int n = pos_units(P);
     const int64_t T = (int64_t)n * a.ntiles;
