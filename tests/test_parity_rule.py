@@ -82,6 +82,8 @@ def test_outcome_within_band_passes(oracle_mod):
     rep = compare(tok, acc, dg, ref2, inputs=wl, oracle_mod=oracle_mod)
     assert rep.ok, rep.describe()
     assert rep.mismatch_in_band == 1 and rep.mismatch_in_band_rows == [b]
+    # half a band is more than the GPU's arithmetic can move a CDF value
+    assert not rep.tight_ok and rep.mismatch_beyond_tight == [b]
     # wrong diagnostics on that row are caught
     dg[b, K, 0] += 1e-3
     rep = compare(tok, acc, dg, ref2, inputs=wl, oracle_mod=oracle_mod)
@@ -203,3 +205,25 @@ def test_tree_rule(oracle_mod):
     g[0][gb, g[1][gb]] = (g[0][gb, g[1][gb]] + 1) % inp.target.shape[-1]
     rep = compare_tree(*g, ref, inputs=inp, oracle_mod=oracle_mod)
     assert gb in rep.mismatch_out_of_band and not rep.ok
+
+
+def test_outcome_within_tight_band(oracle_mod):
+    from tests.parity import TIGHT_BAND
+
+    wl, ref = _case(oracle_mod, seed=2)
+    K = wl.K
+    # as above, with the final uniform moved only 0.5 TIGHT_BAND past the
+    # drawn token's bin: a difference the GPU's arithmetic can produce
+    b = next(b for b in range(wl.B) if wl.params["temperature"][b] > 0
+             and ref[2][b, K, 2] < 0.99 and ref[2][b, K, 2] - ref[2][b, K, 1] > 4 * TIGHT_BAND)
+    hi = ref[2][b, K, 2]
+    wl.uniforms[b, K] = np.float32(hi + 0.5 * TIGHT_BAND)
+    if wl.uniforms[b, K] < hi:  # float32 rounding put it back inside the bin
+        wl.uniforms[b, K] = np.nextafter(np.float32(hi), np.float32(1.0))
+    ref2 = oracle_mod.verify(wl.target, wl.draft, wl.tokens, wl.draft_len, wl.params,
+                             wl.uniforms)
+    assert ref2[0][b, ref2[1][b]] != ref[0][b, ref[1][b]]
+    tok, acc, dg = ref2[0].copy(), ref2[1].copy(), ref2[2].copy()
+    tok[b], acc[b], dg[b] = ref[0][b], ref[1][b], ref[2][b]
+    rep = compare(tok, acc, dg, ref2, inputs=wl, oracle_mod=oracle_mod)
+    assert rep.tight_ok and rep.mismatch_in_band_rows == [b], rep.describe()
