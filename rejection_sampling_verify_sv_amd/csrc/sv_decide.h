@@ -140,18 +140,19 @@ __device__ __forceinline__ RecRange unit_rec(const StepArgs& a, const PosDesc& P
     return unit_records(P, unit_index(P, cls, li), a.ntiles, a.g_row);
 }
 // Index of unit (b, position k, side) in its class region: kept in the row's
-// info, or, in a dense step, in dli (loaded with the row's info).
+// info, or, in the merged launch, in dli (loaded with the row's info).
 struct UnitIdx {
     int t, d;
 };
 __device__ __forceinline__ UnitIdx unit_idx_prefetch(const StepArgs& a, int b, int k) {
     UnitIdx u;
-    u.t = a.dense ? a.dli[unit_code(a, b, k, 0)] : -1;
-    u.d = a.dense ? a.dli[unit_code(a, b, k, 1)] : -1;
+    u.t = k >= a.d0 ? a.dli[unit_code(a, b, k, 0)] : -1;
+    u.d = k >= a.d0 ? a.dli[unit_code(a, b, k, 1)] : -1;
     return u;
 }
-__device__ __forceinline__ UnitIdx unit_idx(const StepArgs& a, const RowInfo& ri, UnitIdx pre) {
-    if (a.dense) return pre;
+__device__ __forceinline__ UnitIdx unit_idx(const StepArgs& a, const RowInfo& ri, UnitIdx pre,
+                                            int k) {
+    if (k >= a.d0) return pre;
     UnitIdx u;
     u.t = ri.li_t;
     u.d = ri.li_d;
@@ -259,10 +260,17 @@ __device__ inline void tree_continue(const StepArgs& a, int b, int k, int c, int
 
 // Row b accepted the draft at position k: its units go to position k+1's
 // lists (one lane calls this).
+// Units of row ri at positions k0..L, target then draft at each (the draft
+// unit up to L - 1, none for greedy rows).
+__device__ __forceinline__ int units_from(const RowInfo& ri, int k0) {
+    return ri.cls == CLS_GREEDY ? ri.L - k0 + 1 : 2 * (ri.L - k0) + 1;
+}
 __device__ inline void note_continue(const StepArgs& a, int b, int k, const RowInfo& ri,
                                      DecideIntent& it) {
     a.rows[b].acc = k + 1;
-    it.nu = (ri.cls != CLS_GREEDY && k + 1 < ri.L) ? 2 : 1;
+    // the merged launch streams every remaining position of the row
+    it.nu = (k + 1 == a.d0) ? units_from(ri, k + 1)
+                            : ((ri.cls != CLS_GREEDY && k + 1 < ri.L) ? 2 : 1);
     it.cls = ri.cls;
 }
 __device__ inline void continue_row(const StepArgs& a, int b, int k, const RowInfo& ri,
@@ -709,11 +717,11 @@ __device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, const 
         const int b = b_w;
         const UnitIdx pre = unit_idx_prefetch(a, b, k);  // loaded with the row's info
         const RowInfo ri = a.rows[b];
-        const UnitIdx ui = unit_idx(a, ri, pre);
+        const UnitIdx ui = unit_idx(a, ri, pre, k);
         // a dense step decides position k of the rows that accepted every
         // position before it (the caller walks the positions)
         if (ri.status == ST_LIVE && k <= ri.L && !(skip_nucleus && ri.cls == CLS_NUCLEUS) &&
-            (!a.dense || ri.acc == k)) {
+            (k < a.d0 || ri.acc == k)) {
             DecideIntent& it = s_it[w];
             if (ri.cls == CLS_GREEDY)
                 decide_greedy(a, *sP, b, k, ri, ui, it);
@@ -724,7 +732,7 @@ __device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, const 
             else
                 decide_full<DT>(a, b, k, ri, it);
             // no unit lists to extend: every position was in this launch
-            if (a.dense && lane == 0) it.nu = 0;
+            if (k >= a.d0 && lane == 0) it.nu = 0;
         }
     }
     __syncthreads();
@@ -751,16 +759,31 @@ __device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, const 
         int li = s_base[it.cls];
         for (int j = 0; j < w; j++) li += s_it[j].cls == it.cls ? s_it[j].nu : 0;
         int32_t* ul = a.ulist + ((int64_t)(k + 1) * kNumCls + it.cls) * a.ustride;
-        ul[li] = b * 2;
-        RowInfo& r = a.rows[b];
-        r.li_t = li;
-        if (it.nu == 2) {
-            ul[li + 1] = b * 2 + 1;
-            r.li_d = li + 1;
-        }
-        if (it.cls == CLS_NUCLEUS) {
-            a.fn_unit[b * 2].rehist = 0;
-            if (it.nu == 2) a.fn_unit[b * 2 + 1].rehist = 0;
+        if (k + 1 == a.d0) {
+            // the merged launch: every remaining position's units, target
+            // then draft, their list indices in dli
+            const int L = a.rows[b].L;
+            for (int kk = k + 1; kk <= L; kk++) {
+                const int sides = (it.cls != CLS_GREEDY && kk < L) ? 2 : 1;
+                for (int side = 0; side < sides; side++) {
+                    const int code = unit_code(a, b, kk, side);
+                    ul[li] = code;
+                    a.dli[code] = li++;
+                    if (it.cls == CLS_NUCLEUS) a.fn_unit[code].rehist = 0;
+                }
+            }
+        } else {
+            ul[li] = b * 2;
+            RowInfo& r = a.rows[b];
+            r.li_t = li;
+            if (it.nu == 2) {
+                ul[li + 1] = b * 2 + 1;
+                r.li_d = li + 1;
+            }
+            if (it.cls == CLS_NUCLEUS) {
+                a.fn_unit[b * 2].rehist = 0;
+                if (it.nu == 2) a.fn_unit[b * 2 + 1].rehist = 0;
+            }
         }
     }
     if (lane == 0 && it.draw) {
@@ -859,7 +882,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
         ri.li_t = ri.li_d = -1;
         ri.mt = ri.zt = ri.md = ri.zd = 0.0;
         ri.tau_t = ri.tau_d = 0ull;
-        if (cls >= 0 && a.dense) {
+        if (cls >= 0 && a.d0 == 0) {
             // a dense step: the units of every position, target then draft
             const bool drafts = cls != CLS_GREEDY && 0 < L;
             const int nu = (L + 1) + (drafts ? L : 0);

@@ -1011,10 +1011,12 @@ struct StepArgs {
     int32_t* tcount;       // [K+1][kMaxKids] their numbers, per level and round
     int32_t* nscr;         // [B][K+1] per-node scratch of the plan (depths, child counts)
     int max_depth, max_kids;  // the tree's bounds: levels after 0, children per node
-    // dense step (dense = 1): one row pass streams every drafted position of
-    // every row, and the decisions walk the positions in order; a unit's code
-    // then carries its position, (b (K+1) + k) 2 + side
-    int dense;
+    // merged launch: the positions d0..K of the rows still live are streamed
+    // by one row pass and decided by one cut/decide launch that walks them in
+    // order (d0 = 0: the whole step, a dense step; d0 = K + 1: none, one
+    // launch pair per position); a unit's code there carries its position,
+    // (b (K + 1 - d0) + k - d0) 2 + side
+    int d0;
     int ustride;           // entries per class region of a position's unit list
     int32_t* dli;          // dense: [B][K+1][2] index of each unit in its class region
 };
@@ -1028,24 +1030,42 @@ constexpr int kDenseUnits = 1024;
 __host__ __device__ __forceinline__ bool dense_eligible(int64_t B, int64_t K) {
     return 2 * B * (K + 1) <= kDenseUnits;
 }
+// Larger batches merge their last positions: the launch pair of each position
+// before d0, then one pair for positions d0..K of the rows still live, with d0
+// the earliest position (from 1, leaving at least two positions to merge)
+// whose largest possible list, B (2 (K - d0) + 1) units, fits kMergeUnits.
+// The merged launch also streams the later positions of rows that reject at
+// an earlier one of them; a launch pair costs about as much as streaming a
+// few hundred rows, and rows that reach the last positions are the fewer the
+// lower the acceptance, so the budget keeps that waste small against the
+// launches it saves.  K + 1: no merged launch.
+constexpr int kMergeUnits = 3072;
+__host__ __device__ __forceinline__ int merge_start(int64_t B, int64_t K) {
+    if (dense_eligible(B, K)) return 0;
+    for (int64_t d0 = 1; d0 < K; d0++)
+        if (B * (2 * (K - d0) + 1) <= kMergeUnits) return (int)d0;
+    return (int)K + 1;
+}
 
-// Unit codes: b 2 + side in a position-by-position step (the position is the
-// launch's), (b (K+1) + k) 2 + side in a dense step.  Per-unit state (the
-// untruncated records, the nucleus cut) is indexed by the code.
+// Unit codes: b 2 + side in the launch of a position before d0 (the position
+// is the launch's), (b (K + 1 - d0) + k - d0) 2 + side in the merged launch.
+// Per-unit state (the untruncated records, the nucleus cut) is indexed by the
+// code.
 __device__ __forceinline__ int unit_code(const StepArgs& a, int b, int k, int side) {
-    return a.dense ? (b * (a.K + 1) + k) * 2 + side : b * 2 + side;
+    return k >= a.d0 ? (b * (a.K + 1 - a.d0) + (k - a.d0)) * 2 + side : b * 2 + side;
 }
-__device__ __forceinline__ int unit_b(const StepArgs& a, int u) {
-    return a.dense ? (u >> 1) / (a.K + 1) : u >> 1;
+// Row of unit u in the launch of position k.
+__device__ __forceinline__ int unit_b(const StepArgs& a, int u, int k) {
+    return k >= a.d0 ? (u >> 1) / (a.K + 1 - a.d0) : u >> 1;
 }
-// Position of unit u, launched at position k.
+// Position of unit u in the launch of position k.
 __device__ __forceinline__ int unit_pos(const StepArgs& a, int u, int k) {
-    return a.dense ? (u >> 1) % (a.K + 1) : k;
+    return k >= a.d0 ? a.d0 + (u >> 1) % (a.K + 1 - a.d0) : k;
 }
-// Row index (within its batch entry's rows) that unit u of row b streams when
-// launched at position / level k.
+// Row index (within its batch entry's rows) that unit u of row b streams in
+// the launch of position / level k.
 __device__ __forceinline__ int unit_rowidx(const StepArgs& a, int u, int b, int k) {
-    if (a.dense) return (u >> 1) % (a.K + 1);
+    if (k >= a.d0) return unit_pos(a, u, k);
     return a.tree ? a.rows[b].node : k;
 }
 

@@ -363,7 +363,7 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
     // completes the unit's cut
     auto cut_unit = [&](int li, int sl) -> bool {
         const int u = list[li];
-        const int b = unit_b(a, u), side = u & 1;
+        const int b = unit_b(a, u, k), side = u & 1;
         const RowInfo& ri = a.rows[b];
         FnUnit* fu = a.fn_unit + u;
         const void* row = unit_row<DT>(a, b, side, unit_rowidx(a, u, b, k));
@@ -641,7 +641,7 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
     const int n_groups = a.stats ? 0 : (a.B + R - 1) / R;  // the statistics decide nothing
     TopkScratch* const s_ts = reinterpret_cast<TopkScratch*>(s_key);  // free between units
     // positions a decision walks: its own, or every one in a dense step
-    const int k_last = a.dense ? a.K : k;
+    const int k_last = k >= a.d0 ? a.K : k;
     auto decide_pending = [&]() {
         const int np = s_npend;
         for (int i = 0; i < np; i += kWaves) {
@@ -673,13 +673,13 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
         const int li = wi / S, sl = wi - li * S;
         if (!cut_unit(li, sl) || a.stats) continue;
         if (threadIdx.x == 0) {
-            const int b = unit_b(a, list[li]);
+            const int b = unit_b(a, list[li], k);
             // the row's nucleus units in this launch: the target and the
             // draft unit of the position (the target alone at its last one);
             // every drafted position's in a dense step.  The last unit to
             // finish decides the row.
             const int L = a.rows[b].L;
-            const int need = a.dense ? 2 * L + 1
+            const int need = k >= a.d0 ? 2 * (L - a.d0) + 1
                                      : ((a.tree ? a.rows[b].kids != 0 : k < L) ? 2 : 1);
             bool last = true;
             if (need > 1) {

@@ -399,7 +399,7 @@ __global__ __launch_bounds__(kThreads) void rowpass_kernel(StepArgs a, int k) {
         int64_t tu1 = tu0 + (t_end - t);
         if (tu1 > a.ntiles) tu1 = a.ntiles;
         const int u = unit_at(a, k, P, li);
-        const int b = unit_b(a, u), side = u & 1;
+        const int b = unit_b(a, u, k), side = u & 1;
         const int cls = a.force_full ? (int)CLS_FULL : a.rows[b].cls;
         const void* row = unit_row<DT>(a, b, side, unit_rowidx(a, u, b, k));
         const int64_t start = tu0 * TS::kTile;

@@ -39,7 +39,7 @@ using namespace sv;
 constexpr int kMaxDraft = 1024;
 
 struct Plan {
-    int tile, ntiles;
+    int tile, ntiles, ustride;
     size_t off_rows, off_pos, off_ulist, off_slist, off_parts, off_tstat, off_chunks,
         off_fnu, off_hist, off_fnkeys, off_fnsync, off_fnrow, off_self, off_sdesc, off_srec, off_status,
         off_wchain, off_tlist, off_tcount, off_nscr, off_dli, bytes;
@@ -53,9 +53,10 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
         return false;
     p->tile = (dtype == SV_F32) ? TileShape<SV_F32>::kTile : TileShape<SV_BF16>::kTile;
     p->ntiles = (V + p->tile - 1) / p->tile;
-    // units streamed by one launch: two per row, or every position's in a
-    // dense step (small batches)
-    const size_t units = dense_eligible(B, K) ? (size_t)B * 2 * (K + 1) : (size_t)B * 2;
+    // unit codes of one launch: two per row, or two per row and position in
+    // the merged launch (the automatic mode's, which needs the most)
+    const int d0 = merge_start(B, K);
+    const size_t units = (size_t)B * 2 * (size_t)(d0 <= K ? K + 1 - d0 : 1);
     const size_t slots = units + kGrid;  // record slot u + w of a (unit, workgroup) piece
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -65,7 +66,8 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
     };
     p->off_rows = take(sizeof(RowInfo) * (size_t)B);
     p->off_pos = take(sizeof(PosDesc) * (size_t)(K + 2));
-    p->off_ulist = take(sizeof(int32_t) * (size_t)B * 2 * kNumCls * (size_t)(K + 1));
+    p->ustride = (int)units;  // entries per class region of a position's list
+    p->off_ulist = take(sizeof(int32_t) * units * kNumCls * (size_t)(K + 1));
     p->off_slist = take(sizeof(int32_t) * (size_t)B);
     p->off_parts = take(sizeof(PartSlot) * slots);
     p->off_tstat = take(sizeof(FullStat) * units * p->ntiles * kWaves);
@@ -88,7 +90,7 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
     p->off_tlist = take(sizeof(int32_t) * (size_t)kMaxKids * B);
     p->off_tcount = take(sizeof(int32_t) * (size_t)(K + 1) * kMaxKids);
     p->off_nscr = take(sizeof(int32_t) * (size_t)B * (K + 1));
-    p->off_dli = take(sizeof(int32_t) * units);  // dense step: list index of each unit
+    p->off_dli = take(sizeof(int32_t) * units);  // merged launch: list index of each unit
     p->bytes = off;
     return true;
 }
@@ -100,30 +102,32 @@ int hip_fail(hipError_t e) {
     return SV_EHIP;
 }
 
-// Launch order of one step; sv_launch_count / sv_launch_name describe it.
-// A dense step (small batches) has one position launch pair for all
-// positions.
+// Launch order of one step; sv_launch_count / sv_launch_name describe it:
+// the plan, a launch pair per position before the merge start d0 and one for
+// the merged positions (a dense step: d0 = 0, one pair in all), the draws.
 constexpr int kPre = 1;
 constexpr int kPerPos = 2;
 const char* const kPreNames[kPre] = {"plan"};
 const char* const kPosNames[kPerPos] = {"rowpass", "cut_decide"};
-// Whether a step of this shape in this mode is dense; -1 when the mode is not
-// served for the shape.
-int step_dense(int B, int K, int mode) {
-    if (mode == SV_STEP_POSITIONS) return 0;
-    if (mode == SV_STEP_DENSE) return dense_eligible(B, K) ? 1 : -1;
-    if (mode == SV_STEP_AUTO) return dense_eligible(B, K) ? 1 : 0;
+// The merge start of a step of this shape in this mode (K + 1: none); -1
+// when the mode is not served for the shape.
+int step_d0(int B, int K, int mode) {
+    if (mode == SV_STEP_POSITIONS) return K + 1;
+    if (mode == SV_STEP_DENSE) return dense_eligible(B, K) ? 0 : -1;
+    if (mode == SV_STEP_AUTO) return merge_start(B, K);
     return -1;
 }
+// Launch pairs of a step with merge start d0.
+int pairs(int K, int d0) { return (d0 < K ? d0 : K) + 1; }
 int launch_count(int B, int K, int mode) {
-    const int d = step_dense(B, K, mode);
-    return d < 0 ? 0 : kPre + kPerPos * (d ? 1 : K + 1) + 2;
+    const int d0 = step_d0(B, K, mode);
+    return d0 < 0 ? 0 : kPre + kPerPos * pairs(K, d0) + 2;
 }
 
 const char* launch_name(int B, int K, int mode, int i) {
     if (i < 0 || i >= launch_count(B, K, mode)) return nullptr;
     if (i < kPre) return kPreNames[i];
-    const int np = step_dense(B, K, mode) ? 1 : K + 1;
+    const int np = pairs(K, step_d0(B, K, mode));
     if (i < kPre + kPerPos * np) return kPosNames[(i - kPre) % kPerPos];
     return (i == kPre + kPerPos * np) ? "sample_sums" : "sample_pick";
 }
@@ -197,9 +201,9 @@ int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepAr
     Grids g;
     const int rc = grids_for_device<DT, kAligned>(&g);
     if (rc != SV_OK) return rc;
-    // units of one row-pass launch: every position's in a dense step
-    const unsigned grow =
-        stream_grid(g.rowpass, (int64_t)2 * a.B * (a.dense ? a.K + 1 : 1), a.ntiles);
+    // units of one row-pass launch: two per row and position in the merged one
+    const unsigned grow = stream_grid(
+        g.rowpass, (int64_t)2 * a.B * (a.d0 <= a.K ? a.K + 1 - a.d0 : 1), a.ntiles);
     const unsigned gsums = stream_grid(g.sums, a.B, a.ntiles);
     a.g_row = (int)grow;
     int n = 0;
@@ -214,7 +218,7 @@ int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepAr
     const unsigned row_grid = (unsigned)(B < kGrid ? B : kGrid);
     mark();
     plan_kernel<<<1, kPlanThreads, 0, st>>>(a, draft_len, params);
-    for (int k = 0; k <= (a.dense ? 0 : a.K); k++) {
+    for (int k = 0; k <= (a.d0 < a.K ? a.d0 : a.K); k++) {
         mark();
         rowpass_kernel<DT, kAligned><<<grow, kThreads, 0, st>>>(a, k);
         mark();
@@ -408,10 +412,10 @@ static int verify_impl(const void* target_logits, const void* draft_logits,
     a.nscr = reinterpret_cast<int32_t*>(ws + pl.off_nscr);
     a.max_depth = tree ? tree->max_depth : K;
     a.max_kids = tree ? tree->max_kids : 1;
-    const int dense = tree ? 0 : step_dense(B, K, cfg->step_mode);
-    if (dense < 0) return SV_EINVAL;
-    a.dense = dense;
-    a.ustride = a.dense ? 2 * B * (K + 1) : 2 * B;
+    const int d0 = tree ? K + 1 : step_d0(B, K, cfg->step_mode);
+    if (d0 < 0) return SV_EINVAL;
+    a.d0 = d0;
+    a.ustride = pl.ustride;
     a.dli = reinterpret_cast<int32_t*>(ws + pl.off_dli);
 
     const size_t esz = (dt == SV_F32) ? 4 : 2;
@@ -603,8 +607,8 @@ extern "C" int sv_accept_stats(const void* target_logits, const void* draft_logi
     a.nscr = reinterpret_cast<int32_t*>(ws + pl.off_nscr);
     a.max_depth = 1;
     a.max_kids = 1;
-    a.dense = 0;
-    a.ustride = 2 * B;
+    a.d0 = a.K + 1;
+    a.ustride = pl.ustride;
     a.dli = reinterpret_cast<int32_t*>(ws + pl.off_dli);
     const size_t esz = (dt == SV_F32) ? 4 : 2;
     const bool aligned = reinterpret_cast<uintptr_t>(target_logits) % 16 == 0 &&

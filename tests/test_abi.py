@@ -88,9 +88,17 @@ def test_sample_and_k0_reject_bad_arguments_on_host(lib):
     cfg.batch = 0
     assert lib.sv_sample(*s_args, ctypes.byref(cfg)) == -1
     # a position-by-position step: one launch pair per position
-    per_position = lib.sv_launch_count(1024, 2, 0) - lib.sv_launch_count(1024, 1, 0)
+    per_position = lib.sv_launch_count(1024, 2, 1) - lib.sv_launch_count(1024, 1, 1)
     assert per_position == 2
-    assert lib.sv_launch_count(1024, 0, 0) == lib.sv_launch_count(1024, 1, 0) - per_position
+    assert lib.sv_launch_count(1024, 0, 1) == lib.sv_launch_count(1024, 1, 1) - per_position
+    # the automatic mode merges the last positions of a large batch: one pair
+    # per position before the merge start, one for the rest (B (2 (K - d0) + 1)
+    # units at most 3072): 1024 rows, K = 3 merge from position 2, 256 rows,
+    # K = 4 from position 1; 1024 rows, K = 1 and 2048 rows, K = 2 do not merge
+    assert lib.sv_launch_count(1024, 3, 0) == lib.sv_launch_count(1024, 3, 1) - per_position
+    assert lib.sv_launch_count(256, 4, 0) == lib.sv_launch_count(256, 4, 1) - 3 * per_position
+    assert lib.sv_launch_count(1024, 1, 0) == lib.sv_launch_count(1024, 1, 1)
+    assert lib.sv_launch_count(2048, 2, 0) == lib.sv_launch_count(2048, 2, 1)
     # small batches take the dense step: one pair for every position
     assert lib.sv_launch_count(64, 4, 0) == lib.sv_launch_count(64, 0, 0) == 5
     assert lib.sv_launch_count(64, 4, 1) == 13 and lib.sv_launch_count(64, 4, 2) == 5

@@ -13,7 +13,7 @@ import zlib
 import numpy as np
 import pytest
 
-from rejection_sampling_verify_sv_amd import workloads
+from rejection_sampling_verify_sv_amd import _lib, workloads
 from rejection_sampling_verify_sv_amd.workloads import PARAMS_DTYPE
 from tests.parity import compare, subset
 
@@ -114,6 +114,22 @@ def test_dense_matches_positions(dev, name, batch, vocab):
     for x, y in zip(a, b):
         assert np.array_equal(x, y, equal_nan=True)
     _say(f"[gpu] dense == positions on {name} B={wl.B} V={wl.V}")
+
+
+@pytest.mark.parametrize("name,batch,vocab,d0", [("mixed_samplers_b1024", 700, 4099, 2),
+                                                 ("fullvocab_ragged_b256", 300, 5003, 1)])
+def test_merged_matches_positions(dev, name, batch, vocab, d0):
+    """Larger batches merge their last positions into one launch pair (from
+    position d0 on); that step and the position-by-position one give bitwise
+    the same outputs and diagnostics, like the dense step."""
+    wl = workloads.make(name, batch=batch, vocab=vocab)
+    auto = _lib.launch_names(wl.B, wl.K, "auto")
+    assert auto.count("rowpass") == d0 + 1  # the merge applies at this shape
+    a = run_gpu(wl, dev, step_mode="positions")
+    b = run_gpu(wl, dev, step_mode="auto")
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y, equal_nan=True)
+    _say(f"[gpu] merged from {d0} == positions on {name} B={wl.B} V={wl.V}")
 
 
 @pytest.mark.parametrize("name", ["mixed_greedy_b64", "fullvocab_ragged_b256",
