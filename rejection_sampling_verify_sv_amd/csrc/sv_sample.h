@@ -117,11 +117,59 @@ __device__ __forceinline__ void draw_weights(const DrawCtx& x, float lt, float l
     }
 }
 
+// One piece of a row's draw masses: per (tile, wave) the sums of the
+// residual weights and of the target weights that w(lt, ld, id, &wr, &wp)
+// gives, fp64, in element order then the fixed DPP tree.  kTwo false: the
+// target row alone (a bonus draw; w gets -inf for ld).
+template <int DT, bool kAligned, bool kTwo, class W>
+__device__ __forceinline__ void draw_sums(const void* trow, const void* drow, int64_t start,
+                                          int64_t end, double2* out, W&& w) {
+    using TS = TileShape<DT>;
+    auto tile = [&](float (&vt)[TS::kE], const float* vd, int64_t t0)
+                    __attribute__((always_inline)) {
+        // elements past `end` read as -inf and weigh 0
+        double sr = 0.0, sp = 0.0;
+        uint32_t id0 = (uint32_t)elem_id<DT>(t0, 0);
+        asm volatile("" : "+v"(id0));  // keeps 16-32 ids from being hoisted
+#pragma unroll
+        for (int i = 0; i < TS::kE; i++) {
+            constexpr int kVec = Elt<DT>::kVec;
+            const uint32_t id = id0 + (uint32_t)((i / kVec) * kThreads * kVec + i % kVec);
+            double wr, wp;
+            w(vt[i], kTwo ? vd[i] : -INFINITY, id, &wr, &wp);
+            sr += wr;
+            sp += wp;
+            // four elements at a time: the fp64 terms of all of them would
+            // otherwise be live at once
+            if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+        sr = wave_sum(sr);
+        sp = wave_sum(sp);
+        if (lane_id() == 0) {
+            double2 r;
+            r.x = sr;
+            r.y = sp;
+            out[(t0 / TS::kTile) * kWaves + wave_id()] = r;
+        }
+    };
+    if constexpr (kTwo)
+        stream_range2<DT, kAligned>(trow, drow, start, end,
+                                    [&](float (&vt)[TS::kE], float (&vd)[TS::kE], int64_t t0, bool)
+                                        __attribute__((always_inline)) { tile(vt, vd, t0); });
+    else
+        stream_range<DT, kAligned>(trow, start, end,
+                                   [&](float (&vt)[TS::kE], int64_t t0, bool)
+                                       __attribute__((always_inline)) { tile(vt, nullptr, t0); });
+}
+
 // The workgroups split the tiles of the listed rows evenly; every wave leaves
 // its partial masses of each tile at chunks[(b*ntiles + tile)*kWaves + wave].
 // The rows: those that draw over the full vocabulary at the end (list slist,
 // count pos[K+1].n_sample), or, in a tree verify, those that need the mass of
-// a residual before testing their node's next child (round lists).
+// a residual before testing their node's next child (round lists).  Each
+// kind of draw streams through a loop of its own (the weights of
+// draw_weights, specialised): a bonus draw reads the target row alone, and no
+// element branches on the kind.
 template <int DT, bool kAligned>
 __global__ __launch_bounds__(kThreads) void sample_sums_kernel(StepArgs a, const int32_t* list,
                                                                const int32_t* count) {
@@ -146,34 +194,62 @@ __global__ __launch_bounds__(kThreads) void sample_sums_kernel(StepArgs a, const
         int64_t end = tu1 * TS::kTile;
         if (end > a.V) end = a.V;
         double2* out = a.chunks + (int64_t)b * a.ntiles * kWaves;
-        stream_range2<DT, kAligned>(trow, drow, start, end,
-                                    [&](float (&vt)[TS::kE], float (&vd)[TS::kE], int64_t t0,
-                                        bool) __attribute__((always_inline)) {
-            // elements past `end` read as -inf on both rows and weigh 0
-            double sr = 0.0, sp = 0.0;
-            uint32_t id0 = (uint32_t)elem_id<DT>(t0, 0);
-            asm volatile("" : "+v"(id0));  // keeps 16-32 ids from being hoisted
-#pragma unroll
-            for (int i = 0; i < TS::kE; i++) {
-                constexpr int kVec = Elt<DT>::kVec;
-                const uint32_t id = id0 + (uint32_t)((i / kVec) * kThreads * kVec + i % kVec);
-                double wr, wp;
-                draw_weights(x, vt[i], vd[i], id, &wr, &wp);
-                sr += wr;
-                sp += wp;
-                // four elements at a time: the fp64 terms of all of them would
-                // otherwise be live at once
-                if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-            }
-            sr = wave_sum(sr);
-            sp = wave_sum(sp);
-            if (lane_id() == 0) {
-                double2 r;
-                r.x = sr;
-                r.y = sp;
-                out[(t0 / TS::kTile) * kWaves + wave_id()] = r;
-            }
-        });
+        if (x.rounds > 0) {  // a tree verify's residual chain
+            draw_sums<DT, kAligned, true>(trow, x.resid ? drow : trow, start, end, out,
+                                          [&](float lt, float ld, uint32_t id, double* wr,
+                                              double* wp) __attribute__((always_inline)) {
+                draw_weights(x, lt, ld, id, wr, wp);
+            });
+        } else if (x.nucleus) {
+            const float mt = x.mt, md = x.md, cb = x.cb;
+            const double izt = x.izt, izd = x.izd;
+            const uint64_t tau_t = x.tau_t, tau_d = x.tau_d;
+            auto pw = [&](float lt, uint32_t id) __attribute__((always_inline)) {
+                return make_key(lt, id) >= tau_t
+                           ? (double)fast_exp2(nuc_t(lt, mt, cb) * kLog2e64) * izt
+                           : 0.0;
+            };
+            if (x.resid)
+                draw_sums<DT, kAligned, true>(trow, drow, start, end, out,
+                                              [&](float lt, float ld, uint32_t id, double* wr,
+                                                  double* wp) __attribute__((always_inline)) {
+                    // only tokens kept on the target side carry mass
+                    const double p = pw(lt, id);
+                    const double q = (p > 0.0 && make_key(ld, id) >= tau_d)
+                                         ? (double)fast_exp2(nuc_t(ld, md, cb) * kLog2e64) * izd
+                                         : 0.0;
+                    const double d = p - q;
+                    *wp = p;
+                    *wr = d > 0.0 ? d : 0.0;
+                });
+            else
+                draw_sums<DT, kAligned, false>(trow, nullptr, start, end, out,
+                                               [&](float lt, float, uint32_t id, double* wr,
+                                                   double* wp) __attribute__((always_inline)) {
+                    *wp = pw(lt, id);
+                    *wr = 0.0;
+                });
+        } else {
+            const float mt = x.mt, md = x.md, c = x.c;
+            const double izt = x.izt, izd = x.izd;
+            if (x.resid)
+                draw_sums<DT, kAligned, true>(trow, drow, start, end, out,
+                                              [&](float lt, float ld, uint32_t, double* wr,
+                                                  double* wp) __attribute__((always_inline)) {
+                    const float ep = fast_exp2((lt - mt) * c);
+                    const float eq = fast_exp2((ld - md) * c);
+                    const double d = fma((double)ep, izt, -((double)eq * izd));
+                    *wp = (double)ep;
+                    *wr = d > 0.0 ? d : 0.0;
+                });
+            else
+                draw_sums<DT, kAligned, false>(trow, nullptr, start, end, out,
+                                               [&](float lt, float, uint32_t, double* wr,
+                                                   double* wp) __attribute__((always_inline)) {
+                    *wp = (double)fast_exp2((lt - mt) * c);
+                    *wr = 0.0;
+                });
+        }
     }
 }
 
