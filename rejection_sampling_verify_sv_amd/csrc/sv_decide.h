@@ -299,9 +299,11 @@ __device__ __forceinline__ double q_of_lane(int id_p, int id_q, double q, bool k
 // Final draw of a top-k row over p's kept tokens in ascending id order, with
 // weight fw in the lane of each kept token: the residual after a rejection
 // (resid; p itself when the residual has no mass), p for the bonus token.
-// Writes the final diagnostics and closes the row at accept length k.
-__device__ void topk_draw(const StepArgs& a, int b, int k, double p, bool keep_p, int id_p,
-                          double fw, bool resid, double uf, TopkScratch& ts) {
+// Every lane gets the token and its diagnostics (the drawn token's
+// final-distribution probability, its CDF bin [lo, hi) and the uniform's
+// margin to it).
+__device__ int topk_draw_calc(double p, bool keep_p, int id_p, double fw, bool resid, double uf,
+                              TopkScratch& ts, double (&dg)[4]) {
     double* s_w = ts.w;
     double* s_p = ts.p;
     int* s_id = ts.id;
@@ -341,15 +343,27 @@ __device__ void topk_draw(const StepArgs& a, int b, int k, double p, bool keep_p
     const double hi = (margin_scale == 0.0) ? 1.0 : lane_value(incl, j) / W;
     const double wy = lane_value(wr, j);
     const double py = lane_value(pr, j);
-    if (lane == 0) {
-        if (a.diag) {
-            double* dg = a.diag + (int64_t)b * 4 * (a.K + 1) + 4 * a.K;
-            const double d1 = uf - lo, d2 = hi - uf;
-            dg[0] = resid ? wy / W : py;
-            dg[1] = lo;
-            dg[2] = hi;
-            dg[3] = margin_scale * (d1 < d2 ? d1 : d2);
-        }
+    const double d1 = uf - lo, d2 = hi - uf;
+    dg[0] = resid ? wy / W : py;
+    dg[1] = lo;
+    dg[2] = hi;
+    dg[3] = margin_scale * (d1 < d2 ? d1 : d2);
+    return y;
+}
+// The final draw's diagnostics (slot K) of row b.
+__device__ __forceinline__ void write_final_diag(const StepArgs& a, int b, const double (&dg)[4]) {
+    if (a.diag) {
+        double* d = a.diag + (int64_t)b * 4 * (a.K + 1) + 4 * a.K;
+        for (int i = 0; i < 4; i++) d[i] = dg[i];
+    }
+}
+// The draw, written out: the row ends at accept length k with the drawn token.
+__device__ void topk_draw(const StepArgs& a, int b, int k, double p, bool keep_p, int id_p,
+                          double fw, bool resid, double uf, TopkScratch& ts) {
+    double dg[4];
+    const int y = topk_draw_calc(p, keep_p, id_p, fw, resid, uf, ts, dg);
+    if (lane_id() == 0) {
+        write_final_diag(a, b, dg);
         emit_row(a, b, k, y);
     }
 }
@@ -691,6 +705,219 @@ __device__ bool decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& r
     return cont;
 }
 
+// ---- the merged launch with few rows: a row's positions side by side --------
+// When every row of a merged (or dense) launch can have a workgroup of its
+// own, the workgroup's waves decide positions base .. base + kWaves - 1 of
+// its row at once, each into a slot, and wave 0 then walks the slots in
+// order: it writes what the walk reaches (accept diagnostics, then the
+// first rejection's token or full-vocab draw, or the invalid row) and stops
+// there.  Each position's decision depends only on that position's records,
+// token and uniform, so the outcome is the one the position-by-position walk
+// gives; the positions past the row's end are computed and dropped.
+enum SpecKind : int32_t { SP_ACCEPT = 0, SP_EMIT = 1, SP_DRAW = 2, SP_INVALID = 3 };
+struct SpecSlot {
+    double px, qx, acc, u;   // the accept test, when one ran (tested)
+    double dy[4];            // an emitted top-k draw's final diagnostics (has_dy)
+    double mt, zt, md, zd;   // a full-vocab draw's statistics (SP_DRAW)
+    uint64_t tau_t, tau_d;
+    int32_t kind, y, code, need, tested, has_dy, pad[2];
+};
+
+// The decision at position kk of row b, side effects left out, into slot
+// `out` (LDS, written by lane 0 as the values are known); every lane of the
+// wave calls it.
+template <int DT>
+__device__ void spec_position(const StepArgs& a, const PosDesc& P, int b, int kk, const RowInfo& ri,
+                              UnitIdx ui, TopkScratch& ts, SpecSlot* out) {
+    const bool l0 = lane_id() == 0;
+    if (l0) {
+        out->kind = SP_ACCEPT;
+        out->tested = 0;
+        out->has_dy = 0;
+    }
+    const int L = ri.L;
+    const bool has_draft = kk < L;
+    const float* u = a.uniforms + (int64_t)b * (a.K + 1);
+    const int x = has_draft ? a.tokens[(int64_t)b * a.K + kk] : 0;
+    const double uk = has_draft ? (double)u[kk] : 0.0;
+    auto tested = [&](double px, double qx, double acc) __attribute__((always_inline)) {
+        if (l0) {
+            out->px = px;
+            out->qx = qx;
+            out->acc = acc;
+            out->u = uk;
+            out->tested = 1;
+        }
+    };
+    auto invalid = [&](int code) __attribute__((always_inline)) {
+        if (l0) {
+            out->kind = SP_INVALID;
+            out->code = code;
+        }
+    };
+    if (ri.cls == CLS_GREEDY) {
+        const RecRange rr = unit_rec(a, P, CLS_GREEDY, ui.t);
+        const PartSlot* s = a.parts + rr.first;
+        uint64_t best = 0ull;
+        for (int i = lane_id(); i < rr.count; i += kWave)
+            best = s[i].keys[0] > best ? s[i].keys[0] : best;
+        best = wave_max_u64(best);
+        const int g = (int)key_id(best);
+        if (l0 && !(has_draft && x == g)) {
+            out->kind = SP_EMIT;
+            out->y = g;
+        }
+    } else if (ri.cls == CLS_TOPK) {
+        const double T = (double)ri.T, top_p = (double)ri.top_p;
+        const double uf = (double)u[a.K];
+        uint64_t kt, kd;
+        unit_tops(a.parts, unit_rec(a, P, CLS_TOPK, ui.t), unit_rec(a, P, CLS_TOPK, ui.d), has_draft,
+                  &kt, &kd);
+        double p, q;
+        bool keep_p, keep_q;
+        if (!topk_dist_wave(kt, ri.k_eff, T, top_p, &p, &keep_p)) {
+            invalid(-1);
+            return;
+        }
+        const int id_p = (int)key_id(kt);
+        double dg[4];
+        int y;
+        if (!has_draft) {  // the bonus token from p
+            y = topk_draw_calc(p, keep_p, id_p, p, false, uf, ts, dg);
+        } else {
+            if (!topk_dist_wave(kd, ri.k_eff, T, top_p, &q, &keep_q)) {
+                invalid(-1);
+                return;
+            }
+            const int id_q = (int)key_id(kd);
+            const double px = lookup_lane(keep_p, id_p, p, x);
+            const double qx = lookup_lane(keep_q, id_q, q, x);
+            const double acc = accept_prob(px, qx);
+            tested(px, qx, acc);
+            if (uk < acc) return;
+            // the residual (p - q)+ over p's kept tokens
+            const double d = p - q_of_lane(id_p, id_q, q, keep_q);
+            y = topk_draw_calc(p, keep_p, id_p, d > 0.0 ? d : 0.0, true, uf, ts, dg);
+        }
+        if (l0) {
+            out->kind = SP_EMIT;
+            out->y = y;
+            out->has_dy = 1;
+            for (int i = 0; i < 4; i++) out->dy[i] = dg[i];
+        }
+    } else if (ri.cls == CLS_NUCLEUS) {
+        const FnUnit ut = fn_unit_load(a.fn_unit + unit_code(a, b, kk, 0));
+        FnUnit ud;
+        ud.status = 0;
+        float lx = 0.f, ld = 0.f;
+        if (has_draft) {
+            ud = fn_unit_load(a.fn_unit + unit_code(a, b, kk, 1));
+            if (x >= 0 && x < a.V) {
+                lx = load_one<DT>(unit_row<DT>(a, b, 0, kk), x);
+                ld = load_one<DT>(unit_row<DT>(a, b, 1, kk), x);
+            }
+        }
+        const int st = ut.status != 0 ? ut.status : (has_draft ? ud.status : 0);
+        if (st != 0) {
+            invalid(st == 1 ? -2 : -1);
+            return;
+        }
+        bool draw = !has_draft;
+        if (has_draft) {
+            const float cb = bucket_coef(ri.T);
+            const double px = (make_key(lx, (uint32_t)x) >= ut.tau)
+                                  ? exp((double)nuc_t(lx, ut.la, cb) * (1.0 / 64.0)) / ut.S
+                                  : 0.0;
+            const double qx = (make_key(ld, (uint32_t)x) >= ud.tau)
+                                  ? exp((double)nuc_t(ld, ud.la, cb) * (1.0 / 64.0)) / ud.S
+                                  : 0.0;
+            const double acc = accept_prob(px, qx);
+            tested(px, qx, acc);
+            draw = !(uk < acc);
+        }
+        if (l0 && draw) {
+            out->kind = SP_DRAW;
+            out->need = has_draft ? NEED_RESID : NEED_BONUS;
+            out->mt = (double)ut.la;
+            out->zt = ut.S;
+            out->tau_t = ut.tau;
+            out->md = (double)ud.la;
+            out->zd = ud.S;
+            out->tau_d = ud.tau;
+        }
+    } else {  // untruncated
+        const double T = (double)ri.T, invT = 1.0 / T;
+        const int nrec = a.ntiles * kWaves;
+        float lx = 0.f, ld = 0.f;
+        if (has_draft && x >= 0 && x < a.V) {
+            lx = load_one<DT>(unit_row<DT>(a, b, 0, kk), x);
+            ld = load_one<DT>(unit_row<DT>(a, b, 1, kk), x);
+        }
+        double mt, zt, md = 0.0, zd = 0.0;
+        full_stats2(a.tstat + (int64_t)unit_code(a, b, kk, 0) * nrec,
+                    has_draft ? a.tstat + (int64_t)unit_code(a, b, kk, 1) * nrec : nullptr, nrec,
+                    invT, &mt, &zt, &md, &zd);
+        if (!(mt > -INFINITY) || (has_draft && !(md > -INFINITY))) {
+            invalid(-1);
+            return;
+        }
+        bool draw = !has_draft;
+        if (has_draft) {
+            const double px = exp(((double)lx - mt) / T) / zt;
+            const double qx = exp(((double)ld - md) / T) / zd;
+            const double acc = accept_prob(px, qx);
+            tested(px, qx, acc);
+            draw = !(uk < acc);
+        }
+        if (l0 && draw) {
+            out->kind = SP_DRAW;
+            out->need = has_draft ? NEED_RESID : NEED_BONUS;
+            out->mt = mt;
+            out->zt = zt;
+            out->md = md;
+            out->zd = zd;
+        }
+    }
+}
+
+// Wave 0: the walk over slots base .. last of row b; true when the row ended.
+__device__ bool spec_commit(const StepArgs& a, int b, int base, int last, const SpecSlot* slots) {
+    for (int kk = base; kk <= last; kk++) {
+        const SpecSlot& r = slots[kk - base];
+        if (r.kind == SP_INVALID) {
+            close_row_invalid(a, b, r.code);
+            return true;
+        }
+        if (r.tested) write_accept_diag(a, b, kk, r.px, r.qx, r.acc, r.u);
+        if (lane_id() != 0) {
+            if (r.kind != SP_ACCEPT) return true;
+            continue;
+        }
+        RowInfo& w = a.rows[b];
+        if (r.kind == SP_ACCEPT) {
+            w.acc = kk + 1;
+            continue;
+        }
+        if (r.kind == SP_EMIT) {
+            if (r.has_dy) write_final_diag(a, b, r.dy);
+            emit_row(a, b, kk, r.y);
+            return true;
+        }
+        w.need = r.need;  // SP_DRAW: the full-vocabulary draw at kk
+        w.kpos = kk;
+        w.mt = r.mt;
+        w.zt = r.zt;
+        w.md = r.md;
+        w.zd = r.zd;
+        w.tau_t = r.tau_t;
+        w.tau_d = r.tau_d;
+        a.slist[atomicAdd(&a.pos[a.K + 1].n_sample, 1)] = b;
+        w.status = ST_SAMPLE;
+        return true;
+    }
+    return false;
+}
+
 // One row per wave (b_w < 0: none; rows not live at position k, and
 // nucleus rows when skip_nucleus is set, do nothing), then the workgroup's
 // list updates: per class region, for the draw list and for a tree verify's
@@ -700,13 +927,36 @@ __device__ bool decide_nucleus(const StepArgs& a, int b, int k, const RowInfo& r
 // Not inlined, so that its registers are not added to those of the cut
 // around it; the arguments come from their copy in device memory (a kernel
 // argument passed by reference would be copied to private memory first).
+// With s_slot set it decides positions k .. k + kWaves - 1 of the one row
+// b_w side by side instead (wave w: position k + w; see spec_position), and
+// s_base[0] tells every thread afterwards whether the row ended there (or
+// was not live); a row that goes on has accepted all of them.
 template <int DT>
 __device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, const PosDesc* sP, int k,
                                                       int b_w,
                                                       bool skip_nucleus, DecideIntent* s_it,
-                                                      int* s_base, TopkScratch* s_ts) {
+                                                      int* s_base, TopkScratch* s_ts,
+                                                      SpecSlot* s_slot) {
     const StepArgs& a = *ga;
     const int w = wave_id(), lane = lane_id();
+    if (s_slot) {
+        const int b = b_w;
+        const RowInfo ri = a.rows[b];
+        const bool go = ri.status == ST_LIVE && k <= ri.L && !(skip_nucleus && ri.cls == CLS_NUCLEUS);
+        const int kk = k + w;
+        if (go && kk <= ri.L) {
+            const UnitIdx ui = unit_idx(a, ri, unit_idx_prefetch(a, b, kk), kk);
+            spec_position<DT>(a, *sP, b, kk, ri, ui, s_ts[w], &s_slot[w]);
+        }
+        __syncthreads();
+        if (w == 0) {
+            const int last = k + kWaves - 1 < ri.L ? k + kWaves - 1 : ri.L;
+            const bool ended = !go || spec_commit(a, b, k, last, s_slot);
+            if (lane == 0) s_base[0] = ended ? 1 : 0;
+        }
+        __syncthreads();
+        return;
+    }
     if (lane == 0) {
         s_it[w].nu = 0;
         s_it[w].cls = 0;

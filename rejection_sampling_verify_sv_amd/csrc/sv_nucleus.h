@@ -636,10 +636,15 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
     // rows per decision item: enough that the items fit in the workgroups the
     // cuts leave free, so that no workgroup runs a cut and a group in turn
     const int n_free = (int)gridDim.x - n_work;
+    // the merged launch with a workgroup free for every row: each row's
+    // positions are decided side by side, kWaves at a time
+    const bool walk = k >= a.d0 && !a.stats && n_free >= a.B;
     int R = n_free > 0 ? (a.B + n_free - 1) / n_free : kDecideRows;
-    R = (R + kDecideRows - 1) / kDecideRows * kDecideRows;
+    R = walk ? 1 : (R + kDecideRows - 1) / kDecideRows * kDecideRows;
     const int n_groups = a.stats ? 0 : (a.B + R - 1) / R;  // the statistics decide nothing
     TopkScratch* const s_ts = reinterpret_cast<TopkScratch*>(s_key);  // free between units
+    static_assert(sizeof(SpecSlot) * kWaves <= sizeof(uint64_t) * kSub, "slots lie over s_sub");
+    SpecSlot* const s_slot = reinterpret_cast<SpecSlot*>(s_sub);  // free between units
     // positions a decision walks: its own, or every one in a dense step
     const int k_last = k >= a.d0 ? a.K : k;
     auto decide_pending = [&]() {
@@ -648,7 +653,7 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
             const int j = i + wave_id();
             for (int kk = k; kk <= k_last; kk++) {
                 decide_rows<DT>(a.self, &s_P, kk, j < np ? s_pend[j] : -1, false, s_it, s_dbase,
-                                s_ts);
+                                s_ts, nullptr);
                 __syncthreads();
             }
         }
@@ -660,11 +665,18 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
     for (int wi = blockIdx.x; wi < n_work + n_groups; wi += gridDim.x) {
         if (wi >= n_work) {
             const int r0 = (wi - n_work) * R;
+            if (walk) {  // row r0's positions, kWaves at a time
+                for (int kk = k; kk <= a.K; kk += kWaves) {
+                    decide_rows<DT>(a.self, &s_P, kk, r0, true, s_it, s_dbase, s_ts, s_slot);
+                    if (s_dbase[0]) break;  // read before the next call writes it
+                }
+                continue;
+            }
             for (int r = r0; r < r0 + R && r < a.B; r += kDecideRows) {
                 const int bw = r + wave_id();
                 for (int kk = k; kk <= k_last; kk++) {
                     decide_rows<DT>(a.self, &s_P, kk, bw < a.B ? bw : -1, true, s_it, s_dbase,
-                                    s_ts);
+                                    s_ts, nullptr);
                     __syncthreads();  // LDS is reused by the next rows
                 }
             }

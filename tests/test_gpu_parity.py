@@ -107,7 +107,10 @@ def test_dense_matches_positions(dev, name, batch, vocab):
     """The dense step and the position-by-position step give bitwise the same
     outputs and diagnostics (the records they merge are the same: per (tile,
     wave) for untruncated rows, exact keys and fixed-point histograms
-    otherwise)."""
+    otherwise).  At these batches the decision launch has a workgroup for
+    every row, so the dense step decides each row's positions side by side
+    and walks them in order afterwards; the position-by-position step never
+    does."""
     wl = workloads.make(name, batch=batch, vocab=vocab)
     a = run_gpu(wl, dev, step_mode="positions")
     b = run_gpu(wl, dev, step_mode="dense")
