@@ -733,6 +733,18 @@ __device__ __forceinline__ uint64_t xor_lane(uint64_t v) {
     const uint32_t lo = xor_lane<S>((uint32_t)v), hi = xor_lane<S>((uint32_t)(v >> 32));
     return ((uint64_t)hi << 32) | lo;
 }
+// Wave-wide max / min of an int; every lane gets the result.
+__device__ __forceinline__ int wave_max_i32(int v) {
+    int w;
+    w = (int)xor_lane<1>((uint32_t)v);  v = w > v ? w : v;
+    w = (int)xor_lane<2>((uint32_t)v);  v = w > v ? w : v;
+    w = (int)xor_lane<4>((uint32_t)v);  v = w > v ? w : v;
+    w = (int)xor_lane<8>((uint32_t)v);  v = w > v ? w : v;
+    w = (int)xor_lane<16>((uint32_t)v); v = w > v ? w : v;
+    w = (int)xor_lane<32>((uint32_t)v); v = w > v ? w : v;
+    return v;
+}
+__device__ __forceinline__ int wave_min_i32(int v) { return -wave_max_i32(-v); }
 // v of lane 63 - lane: mirror inside rows (row_mirror), then swap rows and halves.
 __device__ __forceinline__ uint64_t wave_reverse(uint64_t v) {
     const int lo = __builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xf, 0xf, false);
@@ -933,6 +945,33 @@ __device__ inline T block_exclusive_scan(T v, T* tmp /* kWaves */, T* total) {
     }
     *total = tot;
     return off + incl - v;
+}
+
+// N block-wide exclusive prefix sums at once over a block of kW waves (one
+// barrier pair): excl[j] and tot[j] are what block_exclusive_scan gives for
+// v[j], bit for bit, at kW = kWaves.
+template <int N, int kW = kWaves>
+__device__ inline void block_exclusive_scan_n(const double (&v)[N], double* tmp /* N * kW */,
+                                              double (&excl)[N], double (&tot)[N]) {
+    const int lane = lane_id(), w = wave_id();
+    double incl[N];
+#pragma unroll
+    for (int j = 0; j < N; j++) incl[j] = wave_incl_scan(v[j]);
+    __syncthreads();
+    if (lane == kWave - 1)
+#pragma unroll
+        for (int j = 0; j < N; j++) tmp[j * kW + w] = incl[j];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < N; j++) {
+        double off = 0, t = 0;
+        for (int i = 0; i < kW; i++) {
+            if (i < w) off += tmp[j * kW + i];
+            t += tmp[j * kW + i];
+        }
+        tot[j] = t;
+        excl[j] = off + incl[j] - v[j];
+    }
 }
 
 // Bitonic sort (descending) of n = power of two u64 keys in LDS.

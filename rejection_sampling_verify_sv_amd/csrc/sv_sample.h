@@ -12,7 +12,8 @@
 //                       reduction trees (one partial per wave);
 //   sample_pick_kernel  one workgroup per row: running sum over the chunk
 //                       masses, then a block-wide fp64 prefix scan inside the
-//                       chosen chunk to find the token.
+//                       chosen chunk (one 16-byte vector per thread) to find
+//                       the token.
 // Untruncated rows use the same exp2 terms as the row pass that produced
 // their normalisers; nucleus rows the anchor-relative weights of their cut.
 #pragma once
@@ -253,14 +254,53 @@ __global__ __launch_bounds__(kThreads) void sample_sums_kernel(StepArgs a, const
     }
 }
 
-// One workgroup: the drawn token of row b from its chunk masses.
-template <int DT>
+// The pick runs one thread per 16-byte vector of the chosen chunk (a tile),
+// so that each thread weighs and walks kVec tokens only.
+constexpr int kPickThreads = kThreads * kLoads;
+constexpr int kPickWaves = kPickThreads / kWave;
+
+// The kVec elements from i0 of a row; elements at or past end read as -inf.
+template <int DT, bool kAligned>
+__device__ __forceinline__ void load_vec(const void* row, int64_t i0, int64_t end,
+                                         float (&v)[Elt<DT>::kVec]) {
+    constexpr int kVec = Elt<DT>::kVec;
+    if (kAligned && i0 + kVec <= end) {
+        const u32x4 q = *reinterpret_cast<const u32x4*>(static_cast<const char*>(row) +
+                                                        i0 * Elt<DT>::kSize);
+        if constexpr (DT == SV_F32) {
+            v[0] = __uint_as_float(q.x);
+            v[1] = __uint_as_float(q.y);
+            v[2] = __uint_as_float(q.z);
+            v[3] = __uint_as_float(q.w);
+        } else {
+            v[0] = bf16_lo(q.x);
+            v[1] = bf16_hi(q.x);
+            v[2] = bf16_lo(q.y);
+            v[3] = bf16_hi(q.y);
+            v[4] = bf16_lo(q.z);
+            v[5] = bf16_hi(q.z);
+            v[6] = bf16_lo(q.w);
+            v[7] = bf16_hi(q.w);
+        }
+    } else {  // the vector that straddles end, or a row that is not aligned
+#pragma unroll
+        for (int e = 0; e < kVec; e++) {
+            const int64_t i = i0 + e;
+            const float x = load_one<DT>(row, i < end ? i : end - 1);
+            v[e] = i < end ? x : -INFINITY;
+        }
+    }
+}
+
+// One workgroup (kPickThreads): the drawn token of row b from its chunk masses.
+template <int DT, bool kAligned>
 __device__ __forceinline__ void pick_row(const StepArgs& a, int b) {
     using TS = TileShape<DT>;
-    constexpr int kE = TS::kE;
+    constexpr int kVec = Elt<DT>::kVec;
+    static_assert(kPickThreads * kVec == TS::kTile, "one vector per thread covers a chunk");
     __shared__ int s_chunk, s_lastc, s_best, s_last;
     __shared__ double s_base, s_lbase;
-    __shared__ double s_tmp[kWaves];
+    __shared__ double s_tmp[2 * kPickWaves];
     __shared__ double s_lo, s_hi, s_wy;
     const RowInfo ri = a.rows[b];
     const bool resid = ri.need == NEED_RESID;
@@ -268,26 +308,28 @@ __device__ __forceinline__ void pick_row(const StepArgs& a, int b) {
     // chunk masses: thread t sums the tiles [c0, c1), one chunk = one tile
     // (its kWaves partials in wave order); block scans give the running sums
     const double2* cs = a.chunks + (int64_t)b * a.ntiles * kWaves;
-    const int per = (a.ntiles + kThreads - 1) / kThreads;
+    const int per = (a.ntiles + kPickThreads - 1) / kPickThreads;
     const int c0 = min(a.ntiles, (int)threadIdx.x * per), c1 = min(a.ntiles, c0 + per);
-    double my_r = 0.0, my_p = 0.0;
+    double mine2[2] = {0.0, 0.0};  // residual, target
+    double r0 = 0.0, p0 = 0.0;      // the first tile's masses, kept (later ones are read again)
     for (int c = c0; c < c1; c++) {
         double wr = 0.0, wp = 0.0;
         for (int q = 0; q < kWaves; q++) {
             wr += cs[c * kWaves + q].x;
             wp += cs[c * kWaves + q].y;
         }
-        my_r += wr;
-        my_p += wp;
+        if (c == c0) {
+            r0 = wr;
+            p0 = wp;
+        }
+        mine2[0] += wr;
+        mine2[1] += wp;
     }
-    double Wr, Wp;
-    (void)block_exclusive_scan(my_r, s_tmp, &Wr);
-    (void)block_exclusive_scan(my_p, s_tmp, &Wp);
-    const bool use_r = resid && Wr > 0.0;
-    const double W = use_r ? Wr : Wp;
+    double ex2[2], tot2[2];
+    block_exclusive_scan_n<2, kPickWaves>(mine2, s_tmp, ex2, tot2);
+    const bool use_r = resid && tot2[0] > 0.0;
+    const double W = use_r ? tot2[0] : tot2[1];
     const double target = u * W;
-    double tot;
-    const double excl = block_exclusive_scan(use_r ? my_r : my_p, s_tmp, &tot);
     if (threadIdx.x == 0) {
         s_chunk = 0x7FFFFFFF;
         s_lastc = -1;
@@ -296,12 +338,15 @@ __device__ __forceinline__ void pick_row(const StepArgs& a, int b) {
         s_lo = s_hi = s_wy = 0.0;
     }
     __syncthreads();
-    double S = excl, my_base = 0.0, my_lbase = 0.0;
+    double S = use_r ? ex2[0] : ex2[1], my_base = 0.0, my_lbase = 0.0;
     int my_chunk = -1, my_last = -1;
     for (int c = c0; c < c1; c++) {
-        double wc = 0.0;
-        for (int q = 0; q < kWaves; q++)
-            wc += use_r ? cs[c * kWaves + q].x : cs[c * kWaves + q].y;
+        double wc = use_r ? r0 : p0;
+        if (c != c0) {
+            wc = 0.0;
+            for (int q = 0; q < kWaves; q++)
+                wc += use_r ? cs[c * kWaves + q].x : cs[c * kWaves + q].y;
+        }
         if (!(wc > 0.0)) continue;
         const double before = S;
         S += wc;
@@ -312,8 +357,14 @@ __device__ __forceinline__ void pick_row(const StepArgs& a, int b) {
             my_base = before;
         }
     }
-    if (my_chunk >= 0) atomicMin(&s_chunk, my_chunk);
-    if (my_last >= 0) atomicMax(&s_lastc, my_last);
+    {  // one LDS atomic per wave
+        const int wc = wave_min_i32(my_chunk >= 0 ? my_chunk : 0x7FFFFFFF);
+        const int wl = wave_max_i32(my_last);
+        if (lane_id() == 0) {
+            if (wc != 0x7FFFFFFF) atomicMin(&s_chunk, wc);
+            if (wl >= 0) atomicMax(&s_lastc, wl);
+        }
+    }
     __syncthreads();
     // rounding can leave the target past every running sum: then the last
     // chunk with positive mass is used
@@ -339,63 +390,129 @@ __device__ __forceinline__ void pick_row(const StepArgs& a, int b) {
     const DrawCtx x = draw_ctx(a, b, ri, resid);
     const void* trow = unit_row<DT>(a, b, 0, kpos);
     const void* drow = x.resid ? unit_row<DT>(a, b, 1, kpos) : nullptr;
-    // thread t owns the contiguous run [start + t*kE, start + (t+1)*kE)
+    // the chosen chunk, thread t's vector at t kVec: thread order is id order
     const int64_t cstart = (int64_t)s_chunk * TS::kTile;
-    const int64_t r0 = cstart + (int64_t)threadIdx.x * kE;
-    double w[kE];
-    double mine = 0.0;
+    const int64_t cend = cstart + TS::kTile < a.V ? cstart + TS::kTile : a.V;
+    const int64_t i0 = cstart + (int64_t)threadIdx.x * kVec;
+    float lt[kVec], ld[kVec];
+    load_vec<DT, kAligned>(trow, i0, cend, lt);
+    if (x.resid) {
+        load_vec<DT, kAligned>(drow, i0, cend, ld);
+    } else {
 #pragma unroll
-    for (int i = 0; i < kE; i++) {
-        const int64_t id = r0 + i;
-        double wi = 0.0;
-        if (id < a.V && id < cstart + TS::kTile) {
-            double wr, wp;
-            draw_weights(x, load_one<DT>(trow, id), x.resid ? load_one<DT>(drow, id) : 0.f,
-                         (uint32_t)id, &wr, &wp);
-            wi = use_r ? wr : wp;
-        }
-        w[i] = wi;
-        mine += wi;
+        for (int e = 0; e < kVec; e++) ld[e] = 0.f;
     }
-    double total;
-    const double off = block_exclusive_scan(mine, s_tmp, &total);
-    S = s_base + off;
+    double w[kVec];
+    // the weights, one loop per kind of draw (the kind is the row's)
+    auto fill = [&](auto&& f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < kVec; e++) {
+            const int64_t id = i0 + e;
+            double wr, wp;
+            f(lt[e], ld[e], (uint32_t)id, &wr, &wp);
+            w[e] = id < cend ? (use_r ? wr : wp) : 0.0;
+        }
+    };
+    if (x.rounds > 0) {
+        fill([&](float lt, float ld, uint32_t id, double* wr, double* wp)
+                 __attribute__((always_inline)) { draw_weights(x, lt, ld, id, wr, wp); });
+    } else if (x.nucleus) {
+        const float mt = x.mt, md = x.md, cb = x.cb;
+        const double izt = x.izt, izd = x.izd;
+        const uint64_t tau_t = x.tau_t, tau_d = x.tau_d;
+        if (x.resid)
+            fill([&](float lt, float ld, uint32_t id, double* wr, double* wp)
+                     __attribute__((always_inline)) {
+                const double p = make_key(lt, id) >= tau_t
+                                     ? (double)fast_exp2(nuc_t(lt, mt, cb) * kLog2e64) * izt
+                                     : 0.0;
+                const double q = (p > 0.0 && make_key(ld, id) >= tau_d)
+                                     ? (double)fast_exp2(nuc_t(ld, md, cb) * kLog2e64) * izd
+                                     : 0.0;
+                const double d = p - q;
+                *wp = p;
+                *wr = d > 0.0 ? d : 0.0;
+            });
+        else
+            fill([&](float lt, float, uint32_t id, double* wr, double* wp)
+                     __attribute__((always_inline)) {
+                *wp = make_key(lt, id) >= tau_t
+                          ? (double)fast_exp2(nuc_t(lt, mt, cb) * kLog2e64) * izt
+                          : 0.0;
+                *wr = 0.0;
+            });
+    } else {
+        const float mt = x.mt, md = x.md, c = x.c;
+        const double izt = x.izt, izd = x.izd;
+        if (x.resid)
+            fill([&](float lt, float ld, uint32_t, double* wr, double* wp)
+                     __attribute__((always_inline)) {
+                const float ep = fast_exp2((lt - mt) * c);
+                const float eq = fast_exp2((ld - md) * c);
+                const double d = fma((double)ep, izt, -((double)eq * izd));
+                *wp = (double)ep;
+                *wr = d > 0.0 ? d : 0.0;
+            });
+        else
+            fill([&](float lt, float, uint32_t, double* wr, double* wp)
+                     __attribute__((always_inline)) {
+                *wp = (double)fast_exp2((lt - mt) * c);
+                *wr = 0.0;
+            });
+    }
+    // running sums: a block scan over the threads' vector sums
+    double m[1] = {0.0}, ex[1], tot[1];
+#pragma unroll
+    for (int e = 0; e < kVec; e++) m[0] += w[e];
+    block_exclusive_scan_n<1, kPickWaves>(m, s_tmp, ex, tot);
     int found = -1;
     double f_before = 0.0, f_after = 0.0, f_w = 0.0;
     int lastpos = -1;
     double l_before = 0.0, l_after = 0.0, l_w = 0.0;
+    S = s_base + ex[0];
 #pragma unroll
-    for (int i = 0; i < kE; i++) {
-        if (!(w[i] > 0.0)) continue;
+    for (int e = 0; e < kVec; e++) {
+        if (!(w[e] > 0.0)) continue;
         const double before = S;
-        S += w[i];
-        lastpos = i;
+        S += w[e];
+        lastpos = e;
         l_before = before;
         l_after = S;
-        l_w = w[i];
+        l_w = w[e];
         if (found < 0 && target < S) {
-            found = i;
+            found = e;
             f_before = before;
             f_after = S;
-            f_w = w[i];
+            f_w = w[e];
         }
     }
-    if (found >= 0) atomicMin(&s_best, (int)(r0 + found));
+    const int f_id = found >= 0 ? (int)(i0 + found) : -1;
+    const int l_id = lastpos >= 0 ? (int)(i0 + lastpos) : -1;
     // rounding can push the target past this chunk's own running sums;
     // then the chunk's last positive-weight token is taken (margin 0)
-    if (lastpos >= 0) atomicMax(&s_last, (int)(r0 + lastpos));
+    {  // one LDS atomic per wave
+        const int wf = wave_min_i32(found >= 0 ? f_id : 0x7FFFFFFF);
+        const int wl = wave_max_i32(l_id);
+        if (lane_id() == 0) {
+            if (wf != 0x7FFFFFFF) atomicMin(&s_best, wf);
+            if (wl >= 0) atomicMax(&s_last, wl);
+        }
+    }
     __syncthreads();
     const bool fallback = s_best == 0x7FFFFFFF;
     const int y = fallback ? s_last : s_best;
-    if (!fallback && found >= 0 && (int)(r0 + found) == y) {
+    if (!fallback && found >= 0 && f_id == y) {
         s_lo = f_before;
         s_hi = f_after;
         s_wy = f_w;
-    } else if (fallback && lastpos >= 0 && (int)(r0 + lastpos) == y) {
+    } else if (fallback && lastpos >= 0 && l_id == y) {
         s_lo = l_before;
         s_hi = l_after;
         s_wy = l_w;
     }
+    int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
+    if (y >= 0 && !a.tree)  // the accepted drafts, one per thread
+        for (int j = threadIdx.x; j < kpos; j += kPickThreads) o[j] = a.tokens[(int64_t)b * a.K + j];
     __syncthreads();
     if (threadIdx.x == 0) {
         if (a.diag) {
@@ -407,7 +524,6 @@ __device__ __forceinline__ void pick_row(const StepArgs& a, int b) {
             dg[2] = hi;
             dg[3] = fallback ? 0.0 : (d1 < d2 ? d1 : d2);
         }
-        int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
         if (y < 0) {
             a.out_acc[b] = -1;
             a.rows[b].status = ST_ERROR;
@@ -422,8 +538,6 @@ __device__ __forceinline__ void pick_row(const StepArgs& a, int b) {
             a.out_acc[b] = ri.acc;
             a.rows[b].status = ST_DONE;
         } else {
-            const int32_t* t = a.tokens + (int64_t)b * a.K;
-            for (int j = 0; j < kpos; j++) o[j] = t[j];
             o[kpos] = y;
             a.out_acc[b] = kpos;
             a.rows[b].acc = kpos;
@@ -433,11 +547,11 @@ __device__ __forceinline__ void pick_row(const StepArgs& a, int b) {
     __syncthreads();
 }
 // One workgroup per row that draws over the full vocabulary.
-template <int DT>
-__global__ __launch_bounds__(kThreads) void sample_pick_kernel(StepArgs a) {
+template <int DT, bool kAligned>
+__global__ __launch_bounds__(kPickThreads) void sample_pick_kernel(StepArgs a) {
     const int n = a.pos[a.K + 1].n_sample;
     for (int si = blockIdx.x; si < n; si += gridDim.x) {
-        pick_row<DT>(a, a.slist[si]);
+        pick_row<DT, kAligned>(a, a.slist[si]);
         __syncthreads();
     }
 }

@@ -228,7 +228,7 @@ int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepAr
     sample_sums_kernel<DT, kAligned><<<gsums, kThreads, 0, st>>>(a, a.slist,
                                                                 &a.pos[a.K + 1].n_sample);
     mark();
-    sample_pick_kernel<DT><<<row_grid, kThreads, 0, st>>>(a);
+    sample_pick_kernel<DT, kAligned><<<row_grid, kPickThreads, 0, st>>>(a);
     mark();
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? SV_OK : hip_fail(e);
@@ -262,7 +262,7 @@ int launch_tree(const int32_t* n_cand, const sv_sampler_params* params, StepArgs
     }
     sample_sums_kernel<DT, kAligned><<<gsums, kThreads, 0, st>>>(a, a.slist,
                                                                 &a.pos[a.K + 1].n_sample);
-    sample_pick_kernel<DT><<<row_grid, kThreads, 0, st>>>(a);
+    sample_pick_kernel<DT, kAligned><<<row_grid, kPickThreads, 0, st>>>(a);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? SV_OK : hip_fail(e);
 }
