@@ -1064,8 +1064,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
     }
     if (threadIdx.x < kNumCls) s_nc[threadIdx.x] = 0;
     if (threadIdx.x == 0) *const_cast<StepArgs*>(a.self) = a;
-    {  // counters of split nucleus units (each launch leaves them at zero)
-        const int rows = 2 * a.B < kGrid / 2 ? 2 * a.B : kGrid / 2;
+    {  // counters of split nucleus units (each launch leaves them at zero);
+        // a split unit's index is below both the list length of a launch
+        // (ustride) and kGrid / 2
+        const int rows = a.ustride < kGrid / 2 ? a.ustride : kGrid / 2;
         for (int i = threadIdx.x; i < 2 * rows; i += kPlanThreads) a.fn_sync[i] = 0;
         for (int i = threadIdx.x; i < a.B; i += kPlanThreads) a.fn_row[i] = 0;
     }

@@ -74,8 +74,8 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
     p->off_chunks = take(sizeof(double2) * (size_t)B * p->ntiles * kWaves);
     p->off_fnu = take(sizeof(FnUnit) * units);
     p->off_hist = take(sizeof(uint64_t) * slots * kHistSlot);
-    // split nucleus units: their index in the position's list is below
-    // min(2B, kGrid / 2)
+    // split nucleus units: their index in a launch's list is below
+    // min(units, kGrid / 2)
     const size_t split_rows = units < (size_t)kGrid / 2 ? units : (size_t)kGrid / 2;
     p->off_fnkeys = take(sizeof(uint64_t) * split_rows * kCollectCap);
     p->off_fnsync = take(sizeof(int32_t) * 2 * split_rows);

@@ -171,6 +171,36 @@ def _random_case(rng, B, K, V, dtype, T, top_k, top_p, scale=2.0, quant=None, dr
     return workloads.custom(t, d, tok, L, prm, u, dtype=dtype)
 
 
+def test_split_units_on_a_dirty_workspace(oracle_mod, dev):
+    """A dense step of 8 nucleus rows at K = 7 holds 120 nucleus units in one
+    launch; each is cut by several workgroups, which count their arrivals in
+    per-unit counters indexed by the unit's place in the list (up to 119, past
+    2 B).  The workspace comes in filled with a byte pattern: the plan clears
+    every counter a launch can use, so the outputs match the oracle and, bit
+    for bit, a run on a zeroed workspace."""
+    import torch
+
+    import rejection_sampling_verify_sv_amd as sv
+
+    rng = np.random.default_rng(8107)
+    wl = _random_case(rng, 8, 7, 20011, "f32", 1.0, 0, 0.9)
+    code = sv.SV_F32
+    need = sv.workspace_bytes(wl.B, wl.K, wl.V, code) + 256
+    outs = []
+    for fill in (1, 0):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device=dev)
+        tok, acc, dg = sv.verify(*workloads.to_torch(wl, dev), diag=True, workspace=ws,
+                                 step_mode="dense")
+        torch.cuda.synchronize()
+        outs.append((tok.cpu().numpy(), acc.cpu().numpy(), dg.cpu().numpy()))
+    for x, y in zip(*outs):
+        assert np.array_equal(x, y, equal_nan=True)
+    rep = compare(*outs[0], run_oracle(oracle_mod, wl), None, inputs=wl, oracle_mod=oracle_mod)
+    _say(f"[gpu] dirty workspace, 120 split nucleus units: {rep.describe()}")
+    assert rep.tight_ok, rep.describe()
+    assert rep.compared == wl.B
+
+
 EDGE = [
     # label, B, K, V, dtype, T, top_k, top_p, extra
     ("tiny_vocab_topk", 64, 2, 7, "f32", 1.0, 3, 0.9, {}),
