@@ -310,6 +310,8 @@ __device__ inline void select_boundary(const uint64_t* s_h, float top_p, float l
 // A split unit's index in the nucleus list is below gridDim.x / 4 < kGrid / 2,
 // the rows of fn_sync and fn_keys.
 constexpr int kMaxSplit = 8;
+constexpr int kDenseSplit = 3;   // workgroups of a unit expected to keep many boundary keys
+constexpr int kDenseKeys = 128;  // boundary keys from which a collect counts as such
 __host__ __device__ inline int fn_split(int n_units, int grid, int ntiles) {
     if (n_units <= 0) return 1;
     int s = (grid / 2) / n_units;
@@ -358,10 +360,37 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
     // the row each; the last of them to finish ranks the keys.  Many units:
     // one workgroup per unit.
     const int S = fn_split(n_units, (int)gridDim.x, a.ntiles);
-    const int n_work = n_units * S;
-    // one unit, or one slice of a split unit; true for the workgroup that
-    // completes the unit's cut
-    auto cut_unit = [&](int li, int sl) -> bool {
+    int n_work = n_units * S;
+    // A unit whose row kept many boundary keys at its last cut (a bit per
+    // side in RowInfo.pad) will likely do so again, and such a collect is
+    // bound by its workgroup's instruction issue.  When the even split gives
+    // one workgroup per unit, those units get up to kDenseSplit workgroups
+    // each, as many as keep all work items one per compute unit; s_wpre[li]
+    // is then the first work item of unit li.
+    __shared__ uint16_t s_wpre[kThreads + 1];
+    bool var = false;
+    if (S == 1 && n_units > 0 && n_units <= kThreads && !a.stats) {
+        uint64_t dn = 0;
+        if ((int)threadIdx.x < n_units) {
+            const int b = unit_b(a, list[threadIdx.x], k);
+            dn = (a.rows[b].pad & 3) ? 1ull : 0ull;
+        }
+        uint64_t nd;
+        const uint64_t ex = block_exclusive_scan(dn, s_tmp, &nd);  // barriers
+        int sd = min(kDenseSplit, a.ntiles);
+        while (sd > 1 && n_units + (sd - 1) * (int)nd > (int)gridDim.x / 2) sd--;
+        var = nd > 0 && sd > 1;
+        if (var) {
+            if ((int)threadIdx.x < n_units)
+                s_wpre[threadIdx.x] = (uint16_t)(threadIdx.x + (sd - 1) * (int)ex);
+            if (threadIdx.x == 0) s_wpre[n_units] = (uint16_t)(n_units + (sd - 1) * (int)nd);
+            n_work = n_units + (sd - 1) * (int)nd;
+        }
+        __syncthreads();
+    }
+    // one unit, or one slice of a unit split over Su workgroups; true for the
+    // workgroup that completes the unit's cut
+    auto cut_unit = [&](int li, int sl, int Su) -> bool {
         const int u = list[li];
         const int b = unit_b(a, u, k), side = u & 1;
         const RowInfo& ri = a.rows[b];
@@ -430,8 +459,8 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
         //    boundary is known) with a wave-uniform count: no atomics and no
         //    scans on the way
         const float l_lo = so.l_lo, l_hi = so.l_hi;
-        const int64_t e_lo = ((int64_t)sl * a.ntiles / S) * TS::kTile;
-        const int64_t e_hi = min(((int64_t)(sl + 1) * a.ntiles / S) * TS::kTile, (int64_t)a.V);
+        const int64_t e_lo = ((int64_t)sl * a.ntiles / Su) * TS::kTile;
+        const int64_t e_hi = min(((int64_t)(sl + 1) * a.ntiles / Su) * TS::kTile, (int64_t)a.V);
         uint64_t* const s_mine = s_h + wave_id() * kWaveCap;
         int filled = 0;  // wave-uniform
         auto cbody = [&](float (&v)[TS::kE], int64_t t0, bool)
@@ -503,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
                 s_key[i] = s_h[w * kWaveCap + (i - off)];
             }
         }
-        if (S > 1) {
+        if (Su > 1) {
             // Publish the slice's keys (device-scope stores, see dev_store);
             // only the unit's last workgroup goes on, and reads them all.
             int32_t* const sync = a.fn_sync + 2 * li;  // [0] arrived, [1] keys reserved
@@ -519,7 +548,7 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
             __syncthreads();
             if (threadIdx.x == 0)
                 s_last = __hip_atomic_fetch_add(&sync[0], 1, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+                                                __HIP_MEMORY_SCOPE_AGENT) == Su - 1;
             __syncthreads();
             if (!s_last) return false;
             n = dev_load(&sync[1]);
@@ -535,6 +564,13 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
         }
         __syncthreads();
         if (over) n = kCollectCap + 1;
+        if (threadIdx.x == 0) {  // the hint for the row's next cut
+            const int bit = 1 << side;
+            if (n > kDenseKeys)
+                atomicOr(&a.rows[b].pad, bit);
+            else
+                atomicAnd(&a.rows[b].pad, ~bit);
+        }
         const double target = (double)ri.top_p * so.Z;
         const double sc = nuc_scale(so.beta) * kUnfix;
         const double A = so.A;
@@ -682,8 +718,24 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
             }
             continue;
         }
-        const int li = wi / S, sl = wi - li * S;
-        if (!cut_unit(li, sl) || a.stats) continue;
+        int li, Su;
+        if (var) {  // the last unit whose first work item is at most wi
+            int lo = 0, hi = n_units - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if ((int)s_wpre[mid] <= wi)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            li = lo;
+            Su = (int)s_wpre[li + 1] - (int)s_wpre[li];
+        } else {
+            li = wi / S;
+            Su = S;
+        }
+        const int sl = wi - (var ? (int)s_wpre[li] : li * S);
+        if (!cut_unit(li, sl, Su) || a.stats) continue;
         if (threadIdx.x == 0) {
             const int b = unit_b(a, list[li], k);
             // the row's nucleus units in this launch: the target and the
