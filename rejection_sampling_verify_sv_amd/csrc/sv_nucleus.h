@@ -466,22 +466,14 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
         auto cbody = [&](float (&v)[TS::kE], int64_t t0, bool)
                                       __attribute__((always_inline)) {
             // v lies in [l_lo, l_hi] iff clamping it to that range leaves it
-            // unchanged (never for -inf past `end`); the wave-wide test costs
-            // two vector instructions per element, the per-lane bits are only
-            // formed for tiles with a hit
-            bool any = false;
-#pragma unroll
-            for (int i = 0; i < TS::kE; i++) any |= __builtin_amdgcn_fmed3f(v[i], l_lo, l_hi) == v[i];
-            if (__ballot(any) == 0ull) return;
-            // per-lane bits: the same clamp test again, on copies of the range
-            // the compiler cannot see through (merged with the one above, its
-            // per-element masks would stay live in scalar registers)
-            float lo2 = l_lo, hi2 = l_hi;
-            asm volatile("" : "+v"(lo2), "+v"(hi2));
+            // unchanged (never for -inf past `end`); the lane's bits are
+            // formed on every tile (a compare and a select per element),
+            // which the tiles with hits then use as they are
             uint32_t hit = 0u;
 #pragma unroll
             for (int i = 0; i < TS::kE; i++)
-                hit |= (__builtin_amdgcn_fmed3f(v[i], lo2, hi2) == v[i] ? 1u : 0u) << i;
+                hit |= (__builtin_amdgcn_fmed3f(v[i], l_lo, l_hi) == v[i] ? 1u : 0u) << i;
+            if (__ballot(hit != 0u) == 0ull) return;
             uint32_t id0 = (uint32_t)elem_id<DT>(t0, 0);
             asm volatile("" : "+v"(id0));
             // round r stores the r-th hit of every lane that has one; the
