@@ -118,6 +118,91 @@ __device__ __forceinline__ void draw_weights(const DrawCtx& x, float lt, float l
     }
 }
 
+// Element i of a raw tile (i = j kVec + e: element e of the thread's vector j).
+template <int DT>
+__device__ __forceinline__ float raw_elem(const RawTile& r, int i) {
+    constexpr int kVec = Elt<DT>::kVec;
+    const u32x4& q = r.q[i / kVec];
+    if constexpr (DT == SV_F32) {
+        const int e = i % kVec;
+        return __uint_as_float(e == 0 ? q.x : e == 1 ? q.y : e == 2 ? q.z : q.w);
+    } else {
+        const int e = (i % kVec) >> 1;
+        const uint32_t w = e == 0 ? q.x : e == 1 ? q.y : e == 2 ? q.z : q.w;
+        return (i & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
+}
+
+// The tiles [start, end) of a row, or of two rows in lockstep (kTwo), for the
+// draw masses: full tiles are double-buffered as in stream_range and reach
+// the body as their raw loads, each element converted where the body uses it,
+// so no unpacked copy of a tile sits beside the loads in flight (that copy
+// held the kernel to two or three workgroups per compute unit); the ragged
+// tail comes as floats, -inf past end.  body(gt, gd, t0): gt(i), gd(i) are
+// element i of the tile at t0 in the two rows (gd gives -inf without kTwo).
+template <int DT, bool kAligned, bool kTwo, class Body>
+__device__ __forceinline__ void stream_draw(const void* ra, const void* rb, int64_t start,
+                                            int64_t end, Body&& body) {
+    using TS = TileShape<DT>;
+    int64_t t0 = start;
+    if constexpr (kAligned) {
+        const int64_t full_end = start + ((end - start) / TS::kTile) * TS::kTile;
+        if (t0 < full_end) {
+            const int64_t nt = (full_end - t0) / TS::kTile;
+            const int64_t last = full_end - TS::kTile;
+            RawTile A, A2, B, B2;
+            auto run = [&](const RawTile& X, const RawTile& X2, int64_t at)
+                           __attribute__((always_inline)) {
+                body([&](int i) __attribute__((always_inline)) { return raw_elem<DT>(X, i); },
+                     [&](int i) __attribute__((always_inline)) {
+                         if constexpr (kTwo)
+                             return raw_elem<DT>(X2, i);
+                         else
+                             return -INFINITY;
+                     },
+                     at);
+            };
+            issue_tile<DT>(ra, t0, A);
+            if constexpr (kTwo) issue_tile<DT>(rb, t0, A2);
+            for (int64_t p = nt >> 1; p > 0; --p) {
+                issue_tile<DT>(ra, t0 + TS::kTile, B);
+                if constexpr (kTwo) issue_tile<DT>(rb, t0 + TS::kTile, B2);
+                __builtin_amdgcn_sched_barrier(0);
+                run(A, A2, t0);
+                const int64_t tn = t0 + 2 * TS::kTile;
+                issue_tile<DT>(ra, tn <= last ? tn : last, A);
+                if constexpr (kTwo) issue_tile<DT>(rb, tn <= last ? tn : last, A2);
+                __builtin_amdgcn_sched_barrier(0);
+                run(B, B2, t0 + TS::kTile);
+                t0 += 2 * TS::kTile;
+            }
+            if (nt & 1) {
+                run(A, A2, t0);
+                t0 += TS::kTile;
+            }
+        }
+    }
+    float va[TS::kE], vb[TS::kE];
+    while (t0 < end) {
+        if constexpr (kAligned) {
+            load_tile_tail<DT>(ra, t0, end, va);
+            if constexpr (kTwo) load_tile_tail<DT>(rb, t0, end, vb);
+        } else {
+            load_tile_partial<DT>(ra, t0, end, va);
+            if constexpr (kTwo) load_tile_partial<DT>(rb, t0, end, vb);
+        }
+        body([&](int i) __attribute__((always_inline)) { return va[i]; },
+             [&](int i) __attribute__((always_inline)) {
+                 if constexpr (kTwo)
+                     return vb[i];
+                 else
+                     return -INFINITY;
+             },
+             t0);
+        t0 += TS::kTile;
+    }
+}
+
 // One piece of a row's draw masses: per (tile, wave) the sums of the
 // residual weights and of the target weights that w(lt, ld, id, &wr, &wp)
 // gives, fp64, in element order then the fixed DPP tree.  kTwo false: the
@@ -126,8 +211,9 @@ template <int DT, bool kAligned, bool kTwo, class W>
 __device__ __forceinline__ void draw_sums(const void* trow, const void* drow, int64_t start,
                                           int64_t end, double2* out, W&& w) {
     using TS = TileShape<DT>;
-    auto tile = [&](float (&vt)[TS::kE], const float* vd, int64_t t0)
-                    __attribute__((always_inline)) {
+    stream_draw<DT, kAligned, kTwo>(trow, drow, start, end,
+                                    [&](auto&& gt, auto&& gd, int64_t t0)
+                                        __attribute__((always_inline)) {
         // elements past `end` read as -inf and weigh 0
         double sr = 0.0, sp = 0.0;
         uint32_t id0 = (uint32_t)elem_id<DT>(t0, 0);
@@ -137,7 +223,7 @@ __device__ __forceinline__ void draw_sums(const void* trow, const void* drow, in
             constexpr int kVec = Elt<DT>::kVec;
             const uint32_t id = id0 + (uint32_t)((i / kVec) * kThreads * kVec + i % kVec);
             double wr, wp;
-            w(vt[i], kTwo ? vd[i] : -INFINITY, id, &wr, &wp);
+            w(gt(i), gd(i), id, &wr, &wp);
             sr += wr;
             sp += wp;
             // four elements at a time: the fp64 terms of all of them would
@@ -152,15 +238,7 @@ __device__ __forceinline__ void draw_sums(const void* trow, const void* drow, in
             r.y = sp;
             out[(t0 / TS::kTile) * kWaves + wave_id()] = r;
         }
-    };
-    if constexpr (kTwo)
-        stream_range2<DT, kAligned>(trow, drow, start, end,
-                                    [&](float (&vt)[TS::kE], float (&vd)[TS::kE], int64_t t0, bool)
-                                        __attribute__((always_inline)) { tile(vt, vd, t0); });
-    else
-        stream_range<DT, kAligned>(trow, start, end,
-                                   [&](float (&vt)[TS::kE], int64_t t0, bool)
-                                       __attribute__((always_inline)) { tile(vt, nullptr, t0); });
+    });
 }
 
 // The workgroups split the tiles of the listed rows evenly; every wave leaves
