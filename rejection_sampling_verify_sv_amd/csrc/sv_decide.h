@@ -37,6 +37,7 @@ struct DecideIntent {
     int32_t cls;   // their class region
     int32_t draw;  // 1: the row draws over the full vocabulary at the end
     int32_t rnd;   // 1: tree verify, the row tests its node's next child after a pass
+    int32_t pick;  // 1: that draw is an untruncated bonus draw (no second pass)
 };
 
 // Per-wave LDS of the top-k draw, passed in by the kernel (which lays it over
@@ -280,6 +281,11 @@ __device__ inline void continue_row(const StepArgs& a, int b, int k, const RowIn
 
 // Row b ends at position k with a draw over the full vocabulary (one lane).
 __device__ inline void queue_draw(DecideIntent& it) { it.draw = 1; }
+// An untruncated bonus draw: its chunk masses are the row pass's (tile, wave)
+// records rescaled, so only the chosen chunk is read again (the draw list's
+// far end).  In a tree verify the bonus node was reached by an accepted child
+// (no residual chain), and the row pass of its level left its records.
+__device__ inline void queue_bonus(DecideIntent& it) { it.pick = 1; }
 
 // q of each lane's kept p token (0 when q drops it): the kept q tokens are a
 // prefix of the lanes, broadcast one at a time by scalar lane reads.
@@ -583,7 +589,7 @@ __device__ bool decide_full(const StepArgs& a, int b, int k, const RowInfo& ri, 
             w.kpos = v;
             w.mt = mt;
             w.zt = zt;
-            queue_draw(it);
+            queue_bonus(it);
         }
         return false;
     }
@@ -720,7 +726,7 @@ struct SpecSlot {
     double dy[4];            // an emitted top-k draw's final diagnostics (has_dy)
     double mt, zt, md, zd;   // a full-vocab draw's statistics (SP_DRAW)
     uint64_t tau_t, tau_d;
-    int32_t kind, y, code, need, tested, has_dy, pad[2];
+    int32_t kind, y, code, need, tested, has_dy, pick, pad;
 };
 
 // The decision at position kk of row b, side effects left out, into slot
@@ -734,6 +740,7 @@ __device__ void spec_position(const StepArgs& a, const PosDesc& P, int b, int kk
         out->kind = SP_ACCEPT;
         out->tested = 0;
         out->has_dy = 0;
+        out->pick = 0;
     }
     const int L = ri.L;
     const bool has_draft = kk < L;
@@ -872,6 +879,7 @@ __device__ void spec_position(const StepArgs& a, const PosDesc& P, int b, int kk
         if (l0 && draw) {
             out->kind = SP_DRAW;
             out->need = has_draft ? NEED_RESID : NEED_BONUS;
+            out->pick = has_draft ? 0 : 1;
             out->mt = mt;
             out->zt = zt;
             out->md = md;
@@ -911,7 +919,10 @@ __device__ bool spec_commit(const StepArgs& a, int b, int base, int last, const 
         w.zd = r.zd;
         w.tau_t = r.tau_t;
         w.tau_d = r.tau_d;
-        a.slist[atomicAdd(&a.pos[a.K + 1].n_sample, 1)] = b;
+        if (r.pick)
+            a.slist[a.B - 1 - atomicAdd(&a.pos[a.K + 1].n_pick, 1)] = b;
+        else
+            a.slist[atomicAdd(&a.pos[a.K + 1].n_sample, 1)] = b;
         w.status = ST_SAMPLE;
         return true;
     }
@@ -962,6 +973,7 @@ __device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, const 
         s_it[w].cls = 0;
         s_it[w].draw = 0;
         s_it[w].rnd = 0;
+        s_it[w].pick = 0;
     }
     if (b_w >= 0) {
         const int b = b_w;
@@ -987,18 +999,21 @@ __device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, const 
     }
     __syncthreads();
     // thread c < kNumCls: class region c; kNumCls: draws; kNumCls + 1: the
-    // first child round of a tree verify
-    if (threadIdx.x <= kNumCls + 1) {
+    // first child round of a tree verify; kNumCls + 2: draws without a pass
+    if (threadIdx.x <= kNumCls + 2) {
         const int c = threadIdx.x;
         int cnt = 0;
         for (int j = 0; j < kWaves; j++)
-            cnt += (c < kNumCls) ? (s_it[j].cls == c ? s_it[j].nu : 0)
-                                 : (c == kNumCls ? s_it[j].draw : s_it[j].rnd);
+            cnt += (c < kNumCls)       ? (s_it[j].cls == c ? s_it[j].nu : 0)
+                   : c == kNumCls     ? s_it[j].draw
+                   : c == kNumCls + 1 ? s_it[j].rnd
+                                      : s_it[j].pick;
         int base = 0;
         if (cnt > 0)
-            base = atomicAdd(c < kNumCls    ? &a.pos[k + 1].n_cls[c]
-                             : c == kNumCls ? &a.pos[a.K + 1].n_sample
-                                            : &a.tcount[k * kMaxKids + 1],
+            base = atomicAdd(c < kNumCls        ? &a.pos[k + 1].n_cls[c]
+                             : c == kNumCls     ? &a.pos[a.K + 1].n_sample
+                             : c == kNumCls + 1 ? &a.tcount[k * kMaxKids + 1]
+                                                : &a.pos[a.K + 1].n_pick,
                              cnt);
         s_base[c] = base;
     }
@@ -1042,6 +1057,12 @@ __device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, const 
         a.slist[i] = b;
         a.rows[b].status = ST_SAMPLE;
     }
+    if (lane == 0 && it.pick) {
+        int i = s_base[kNumCls + 2];
+        for (int j = 0; j < w; j++) i += s_it[j].pick;
+        a.slist[a.B - 1 - i] = b;
+        a.rows[b].status = ST_SAMPLE;
+    }
     if (lane == 0 && it.rnd) {
         int i = s_base[kNumCls + 1];
         for (int j = 0; j < w; j++) i += s_it[j].rnd;
@@ -1061,6 +1082,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
     for (int i = threadIdx.x; i < a.K + 2; i += kPlanThreads) {
         for (int c = 0; c < kNumCls; c++) a.pos[i].n_cls[c] = 0;
         a.pos[i].n_sample = 0;
+        a.pos[i].n_pick = 0;
     }
     if (threadIdx.x < kNumCls) s_nc[threadIdx.x] = 0;
     if (threadIdx.x == 0) *const_cast<StepArgs*>(a.self) = a;

@@ -73,8 +73,10 @@ static_assert(CLS_GREEDY == 0 && CLS_TOPK == 1 && CLS_FULL == 2 && CLS_NUCLEUS =
               "row classes index the unit regions");
 struct PosDesc {
     int32_t n_cls[kNumCls];  // units listed per class region
-    int32_t n_sample;        // rows to draw from at the end (final slot only)
-    int32_t pad[3];
+    int32_t n_sample;        // rows whose final draw streams their rows (final slot only)
+    int32_t n_pick;          // rows whose final draw takes its masses from the row pass's
+                             // records (untruncated bonus draws; final slot only)
+    int32_t pad[2];
 };
 __host__ __device__ __forceinline__ int pos_units(const PosDesc& p) {
     return p.n_cls[0] + p.n_cls[1] + p.n_cls[2] + p.n_cls[3];

@@ -345,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
     __shared__ int s_star, s_nsel, s_wcnt[kWaves], s_base, s_last;
     __shared__ uint64_t s_before;
     __shared__ DecideIntent s_it[kWaves];
-    __shared__ int s_dbase[kNumCls + 2];
+    __shared__ int s_dbase[kNumCls + 3];
     constexpr int kPend = 32;  // completed nucleus rows awaiting their decision
     __shared__ int s_pend[kPend], s_npend;
     __shared__ PosDesc s_P;  // this launch's lists, for the decisions

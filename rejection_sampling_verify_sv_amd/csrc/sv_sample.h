@@ -370,8 +370,14 @@ __device__ __forceinline__ void load_vec(const void* row, int64_t i0, int64_t en
     }
 }
 
-// One workgroup (kPickThreads): the drawn token of row b from its chunk masses.
-template <int DT, bool kAligned>
+// One workgroup (kPickThreads): the drawn token of row b from its chunk masses,
+// or, for an untruncated bonus draw (stats), from the row pass's records of
+// the row: the target mass of a (tile, wave) is its sum of exp2((t - m_w) c)
+// rescaled by exp2((m_w - mt) c), the same terms the sums kernel would add up
+// one by one (each term rounded apart, so the chunk's own running sums below
+// may end a little off its record; the fallback to the chunk's last token
+// covers that).
+template <int DT, bool kAligned, bool stats>
 __device__ __forceinline__ void pick_row(const StepArgs& a, int b) {
     using TS = TileShape<DT>;
     constexpr int kVec = Elt<DT>::kVec;
@@ -386,6 +392,16 @@ __device__ __forceinline__ void pick_row(const StepArgs& a, int b) {
     // chunk masses: thread t sums the tiles [c0, c1), one chunk = one tile
     // (its kWaves partials in wave order); block scans give the running sums
     const double2* cs = a.chunks + (int64_t)b * a.ntiles * kWaves;
+    auto chunk_pair = [&](int c, int q) __attribute__((always_inline)) {
+        if constexpr (!stats) return cs[c * kWaves + q];
+        const FullStat r =
+            a.tstat[((int64_t)unit_code(a, b, ri.kpos, 0) * a.ntiles + c) * kWaves + q];
+        double2 m;
+        m.x = 0.0;
+        m.y = r.m > -INFINITY ? r.s * (double)fast_exp2((r.m - (float)ri.mt) * exp2_coef(ri.T))
+                              : 0.0;
+        return m;
+    };
     const int per = (a.ntiles + kPickThreads - 1) / kPickThreads;
     const int c0 = min(a.ntiles, (int)threadIdx.x * per), c1 = min(a.ntiles, c0 + per);
     double mine2[2] = {0.0, 0.0};  // residual, target
@@ -393,8 +409,9 @@ __device__ __forceinline__ void pick_row(const StepArgs& a, int b) {
     for (int c = c0; c < c1; c++) {
         double wr = 0.0, wp = 0.0;
         for (int q = 0; q < kWaves; q++) {
-            wr += cs[c * kWaves + q].x;
-            wp += cs[c * kWaves + q].y;
+            const double2 m = chunk_pair(c, q);
+            wr += m.x;
+            wp += m.y;
         }
         if (c == c0) {
             r0 = wr;
@@ -422,8 +439,10 @@ __device__ __forceinline__ void pick_row(const StepArgs& a, int b) {
         double wc = use_r ? r0 : p0;
         if (c != c0) {
             wc = 0.0;
-            for (int q = 0; q < kWaves; q++)
-                wc += use_r ? cs[c * kWaves + q].x : cs[c * kWaves + q].y;
+            for (int q = 0; q < kWaves; q++) {
+                const double2 m = chunk_pair(c, q);
+                wc += use_r ? m.x : m.y;
+            }
         }
         if (!(wc > 0.0)) continue;
         const double before = S;
@@ -491,7 +510,14 @@ __device__ __forceinline__ void pick_row(const StepArgs& a, int b) {
             w[e] = id < cend ? (use_r ? wr : wp) : 0.0;
         }
     };
-    if (x.rounds > 0) {
+    if (stats) {  // an untruncated bonus draw
+        const float mt = x.mt, c = x.c;
+        fill([&](float lt, float, uint32_t, double* wr, double* wp)
+                 __attribute__((always_inline)) {
+            *wp = (double)fast_exp2((lt - mt) * c);
+            *wr = 0.0;
+        });
+    } else if (x.rounds > 0) {
         fill([&](float lt, float ld, uint32_t id, double* wr, double* wp)
                  __attribute__((always_inline)) { draw_weights(x, lt, ld, id, wr, wp); });
     } else if (x.nucleus) {
@@ -627,9 +653,16 @@ __device__ __forceinline__ void pick_row(const StepArgs& a, int b) {
 // One workgroup per row that draws over the full vocabulary.
 template <int DT, bool kAligned>
 __global__ __launch_bounds__(kPickThreads) void sample_pick_kernel(StepArgs a) {
-    const int n = a.pos[a.K + 1].n_sample;
-    for (int si = blockIdx.x; si < n; si += gridDim.x) {
-        pick_row<DT, kAligned>(a, a.slist[si]);
+    // the rows whose masses the sums kernel wrote, then (from the list's far
+    // end) the untruncated bonus draws, whose masses come from the row pass
+    const int ns = a.pos[a.K + 1].n_sample, n = ns + a.pos[a.K + 1].n_pick;
+    int si = blockIdx.x;
+    for (; si < ns; si += gridDim.x) {
+        pick_row<DT, kAligned, false>(a, a.slist[si]);
+        __syncthreads();
+    }
+    for (; si < n; si += gridDim.x) {
+        pick_row<DT, kAligned, true>(a, a.slist[a.B - 1 - (si - ns)]);
         __syncthreads();
     }
 }

@@ -88,6 +88,7 @@ __global__ __launch_bounds__(kThreads) void tree_round_kernel(StepArgs a, int k,
             it.cls = 0;
             it.draw = 0;
             it.rnd = 0;
+            it.pick = 0;
             tree_continue(a, b, k, c, x, kids, ri, it);
             // the child's units join level k + 1's lists
             const int li = atomicAdd(&a.pos[k + 1].n_cls[it.cls], it.nu);
