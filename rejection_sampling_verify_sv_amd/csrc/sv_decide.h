@@ -283,8 +283,10 @@ __device__ inline void continue_row(const StepArgs& a, int b, int k, const RowIn
 __device__ inline void queue_draw(DecideIntent& it) { it.draw = 1; }
 // An untruncated bonus draw: its chunk masses are the row pass's (tile, wave)
 // records rescaled, so only the chosen chunk is read again (the draw list's
-// far end).  In a tree verify the bonus node was reached by an accepted child
-// (no residual chain), and the row pass of its level left its records.
+// far end).  The records outlive the later launches: a row that stopped is
+// not streamed again, and the merged launch's unit codes lie past the others.
+// In a tree verify the bonus node was reached by an accepted child (no
+// residual chain), and the row pass of its level left its records.
 __device__ inline void queue_bonus(DecideIntent& it) { it.pick = 1; }
 
 // q of each lane's kept p token (0 when q drops it): the kept q tokens are a

@@ -1089,19 +1089,25 @@ __host__ __device__ __forceinline__ int merge_start(int64_t B, int64_t K) {
 }
 
 // Unit codes: b 2 + side in the launch of a position before d0 (the position
-// is the launch's), (b (K + 1 - d0) + k - d0) 2 + side in the merged launch.
-// Per-unit state (the untruncated records, the nucleus cut) is indexed by the
-// code.
+// is the launch's), 2B + (b (K + 1 - d0) + k - d0) 2 + side in the merged
+// launch after such launches (no 2B in a dense step).  Per-unit state (the
+// untruncated records, the nucleus cut) is indexed by the code, so the merged
+// launch's codes lie past those of the earlier launches: the records of a row
+// that stopped before d0 outlive the merged launch, and the merged units that
+// the decisions before d0 list (clearing their state) touch no unit those
+// decisions' launch is still cutting.
+__device__ __forceinline__ int merged_base(const StepArgs& a) { return a.d0 > 0 ? 2 * a.B : 0; }
 __device__ __forceinline__ int unit_code(const StepArgs& a, int b, int k, int side) {
-    return k >= a.d0 ? (b * (a.K + 1 - a.d0) + (k - a.d0)) * 2 + side : b * 2 + side;
+    return k >= a.d0 ? merged_base(a) + (b * (a.K + 1 - a.d0) + (k - a.d0)) * 2 + side
+                     : b * 2 + side;
 }
 // Row of unit u in the launch of position k.
 __device__ __forceinline__ int unit_b(const StepArgs& a, int u, int k) {
-    return k >= a.d0 ? (u >> 1) / (a.K + 1 - a.d0) : u >> 1;
+    return k >= a.d0 ? ((u - merged_base(a)) >> 1) / (a.K + 1 - a.d0) : u >> 1;
 }
 // Position of unit u in the launch of position k.
 __device__ __forceinline__ int unit_pos(const StepArgs& a, int u, int k) {
-    return k >= a.d0 ? a.d0 + (u >> 1) % (a.K + 1 - a.d0) : k;
+    return k >= a.d0 ? a.d0 + ((u - merged_base(a)) >> 1) % (a.K + 1 - a.d0) : k;
 }
 // Row index (within its batch entry's rows) that unit u of row b streams in
 // the launch of position / level k.

@@ -53,10 +53,12 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
         return false;
     p->tile = (dtype == SV_F32) ? TileShape<SV_F32>::kTile : TileShape<SV_BF16>::kTile;
     p->ntiles = (V + p->tile - 1) / p->tile;
-    // unit codes of one launch: two per row, or two per row and position in
-    // the merged launch (the automatic mode's, which needs the most)
+    // units one launch lists: two per row, or two per row and position in
+    // the merged launch (the automatic mode's, which needs the most); unit
+    // codes: those, and the 2B of the launches before a merged one
     const int d0 = merge_start(B, K);
     const size_t units = (size_t)B * 2 * (size_t)(d0 <= K ? K + 1 - d0 : 1);
+    const size_t codes = units + (d0 >= 1 && d0 <= K ? (size_t)B * 2 : 0);
     const size_t slots = units + kGrid;  // record slot u + w of a (unit, workgroup) piece
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -70,9 +72,9 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
     p->off_ulist = take(sizeof(int32_t) * units * kNumCls * (size_t)(K + 1));
     p->off_slist = take(sizeof(int32_t) * (size_t)B);
     p->off_parts = take(sizeof(PartSlot) * slots);
-    p->off_tstat = take(sizeof(FullStat) * units * p->ntiles * kWaves);
+    p->off_tstat = take(sizeof(FullStat) * codes * p->ntiles * kWaves);
     p->off_chunks = take(sizeof(double2) * (size_t)B * p->ntiles * kWaves);
-    p->off_fnu = take(sizeof(FnUnit) * units);
+    p->off_fnu = take(sizeof(FnUnit) * codes);
     p->off_hist = take(sizeof(uint64_t) * slots * kHistSlot);
     // split nucleus units: their index in a launch's list is below
     // min(units, kGrid / 2)
@@ -90,7 +92,7 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* p) {
     p->off_tlist = take(sizeof(int32_t) * (size_t)kMaxKids * B);
     p->off_tcount = take(sizeof(int32_t) * (size_t)(K + 1) * kMaxKids);
     p->off_nscr = take(sizeof(int32_t) * (size_t)B * (K + 1));
-    p->off_dli = take(sizeof(int32_t) * units);  // merged launch: list index of each unit
+    p->off_dli = take(sizeof(int32_t) * codes);  // merged launch: list index of each unit
     p->bytes = off;
     return true;
 }

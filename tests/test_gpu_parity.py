@@ -201,6 +201,55 @@ def test_split_units_on_a_dirty_workspace(oracle_mod, dev):
     assert rep.compared == wl.B
 
 
+def _mixed_case(seed):
+    """A seeded batch whose rows each draw their own sampler (greedy, top-k up
+    to 64, top-k above 64 (not served), untruncated, nucleus), temperature,
+    draft length and logit scale; drafts are sampled from the untruncated
+    tempered draft, so some fall outside q."""
+    rng = np.random.default_rng(5150 + seed)
+    B = int(rng.choice([5, 37, 90, 150, 260], p=[0.15, 0.25, 0.2, 0.2, 0.2]))
+    K = int(rng.integers(1, 7))
+    V = int(rng.choice([3001, 9000, 20011]))
+    dtype = "bf16" if rng.random() < 0.5 else "f32"
+    scale = float(rng.choice([1.0, 3.0]))
+    t = rng.normal(0, scale, (B, K + 1, V))
+    d = t[:, :K] * 0.8 + rng.normal(0, scale * 0.6, (B, K, V))
+    prm = np.zeros(B, PARAMS_DTYPE)
+    kind = rng.choice(5, size=B, p=[0.2, 0.3, 0.05, 0.2, 0.25])
+    for b in range(B):
+        T = float(rng.uniform(0.3, 1.6))
+        if kind[b] == 0:
+            prm[b] = (0.0, 0, 1.0, 0)
+        elif kind[b] == 1:
+            prm[b] = (T, int(rng.integers(1, 65)), float(rng.choice([1.0, 0.9, 0.6])), 0)
+        elif kind[b] == 2:
+            prm[b] = (T, int(rng.integers(65, V)), 1.0, 0)
+        elif kind[b] == 3:
+            prm[b] = (T, int(rng.choice([0, V])), 1.0, 0)
+        else:
+            prm[b] = (T, 0, float(rng.uniform(0.5, 0.99)), 0)
+    L = rng.integers(0, K + 1, size=B).astype(np.int32)
+    tok = np.zeros((B, K), np.int32)
+    for b in range(B):
+        T = max(float(prm["temperature"][b]), 1e-3)
+        for k in range(K):
+            tok[b, k] = int(np.argmax(d[b, k] / T + rng.gumbel(size=V)))
+    u = rng.random((B, K + 1), dtype=np.float32)
+    return workloads.custom(t, d, tok, L, prm, u, dtype=dtype, name=f"mixed_sweep_{seed}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_mixed_rows_sweep(oracle_mod, dev, seed):
+    """Every sampler class, draft length and temperature mixed in one batch,
+    at batch shapes that take the dense, merged and position-by-position
+    steps; every row against the oracle in the library's own mode and
+    position by position."""
+    wl = _mixed_case(seed)
+    for mode in ("auto", "positions"):
+        rep, _, _ = check(oracle_mod, wl, dev, label=wl.name, step_mode=mode)
+        assert rep.compared + rep.unsupported == wl.B
+
+
 EDGE = [
     # label, B, K, V, dtype, T, top_k, top_p, extra
     ("tiny_vocab_topk", 64, 2, 7, "f32", 1.0, 3, 0.9, {}),
