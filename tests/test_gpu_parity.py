@@ -201,21 +201,34 @@ def test_split_units_on_a_dirty_workspace(oracle_mod, dev):
     assert rep.compared == wl.B
 
 
-def _mixed_case(seed):
+def _mixed_case(seed, wide=False):
     """A seeded batch whose rows each draw their own sampler (greedy, top-k up
     to 64, top-k above 64 (not served), untruncated, nucleus), temperature,
     draft length and logit scale; drafts are sampled from the untruncated
-    tempered draft, so some fall outside q."""
-    rng = np.random.default_rng(5150 + seed)
-    B = int(rng.choice([5, 37, 90, 150, 260], p=[0.15, 0.25, 0.2, 0.2, 0.2]))
-    K = int(rng.integers(1, 7))
-    V = int(rng.choice([3001, 9000, 20011]))
+    tempered draft, so some fall outside q.  wide: larger batches, drafts
+    and vocabularies, more nucleus rows, and logits rounded to a grid on some
+    batches (many ties)."""
+    rng = np.random.default_rng((9001 if wide else 5150) + seed)
+    if wide:
+        B = int(rng.choice([3, 64, 130, 300, 600], p=[0.1, 0.2, 0.25, 0.25, 0.2]))
+        K = int(rng.integers(1, 8))
+        V = int(rng.choice([2048, 30011, 65543]))
+        while B * (K + 1) * V > 40_000_000:
+            V = 2048 if V == 30011 else 30011
+        probs = [0.1, 0.2, 0.05, 0.2, 0.45]
+    else:
+        B = int(rng.choice([5, 37, 90, 150, 260], p=[0.15, 0.25, 0.2, 0.2, 0.2]))
+        K = int(rng.integers(1, 7))
+        V = int(rng.choice([3001, 9000, 20011]))
+        probs = [0.2, 0.3, 0.05, 0.2, 0.25]
     dtype = "bf16" if rng.random() < 0.5 else "f32"
     scale = float(rng.choice([1.0, 3.0]))
     t = rng.normal(0, scale, (B, K + 1, V))
     d = t[:, :K] * 0.8 + rng.normal(0, scale * 0.6, (B, K, V))
+    if wide and rng.random() < 0.3:
+        t, d = np.round(t * 4) / 4, np.round(d * 4) / 4
     prm = np.zeros(B, PARAMS_DTYPE)
-    kind = rng.choice(5, size=B, p=[0.2, 0.3, 0.05, 0.2, 0.25])
+    kind = rng.choice(5, size=B, p=probs)
     for b in range(B):
         T = float(rng.uniform(0.3, 1.6))
         if kind[b] == 0:
@@ -235,7 +248,8 @@ def _mixed_case(seed):
         for k in range(K):
             tok[b, k] = int(np.argmax(d[b, k] / T + rng.gumbel(size=V)))
     u = rng.random((B, K + 1), dtype=np.float32)
-    return workloads.custom(t, d, tok, L, prm, u, dtype=dtype, name=f"mixed_sweep_{seed}")
+    return workloads.custom(t, d, tok, L, prm, u, dtype=dtype,
+                            name=f"mixed_sweep_{'wide_' if wide else ''}{seed}")
 
 
 @pytest.mark.parametrize("seed", range(12))
@@ -246,6 +260,17 @@ def test_mixed_rows_sweep(oracle_mod, dev, seed):
     position by position."""
     wl = _mixed_case(seed)
     for mode in ("auto", "positions"):
+        rep, _, _ = check(oracle_mod, wl, dev, label=wl.name, step_mode=mode)
+        assert rep.compared + rep.unsupported == wl.B
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_mixed_rows_sweep_wide(oracle_mod, dev, seed):
+    """The same at up to 600 rows, seven drafts and V = 65543, with more
+    nucleus rows and, on some batches, logits on a grid of 1/4 (ties)."""
+    wl = _mixed_case(seed, wide=True)
+    modes = ["auto", "positions"] + (["dense"] if 2 * wl.B * (wl.K + 1) <= 1024 else [])
+    for mode in modes:
         rep, _, _ = check(oracle_mod, wl, dev, label=wl.name, step_mode=mode)
         assert rep.compared + rep.unsupported == wl.B
 
