@@ -171,6 +171,28 @@ def test_tree_mixed_classes_ragged(oracle_mod, dev):
     assert rep.compared == B and rep.error_rows == 0
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_tree_sweep(oracle_mod, dev, seed):
+    """Seeded trees: shape (random, wide, medusa, path), size, candidate
+    counts, dtype, and each row's sampler class and temperature drawn at
+    random; every row against the oracle."""
+    rng = np.random.default_rng(7300 + seed)
+    B = int(rng.choice([7, 64, 200]))
+    shape = str(rng.choice(["random", "wide", "medusa", "path"]))
+    K = int(rng.integers(2, 13)) if shape != "medusa" else 12
+    V = int(rng.choice([4099, 20011]))
+    dtype = "bf16" if rng.random() < 0.5 else "f32"
+    nc = rng.integers(0, K + 1, B).astype(np.int32)
+    wl, par = tree_case(rng, B, K, V, dtype, 1.0, 20, 0.95, shape, float(rng.uniform(0.2, 0.7)),
+                        n_cand=nc)
+    P = wl.params
+    P["temperature"] = rng.choice([0.0, 0.5, 1.0, 1.4], B)
+    P["top_k"] = rng.choice([0, 1, 20, 64, V], B)
+    P["top_p"] = rng.choice([0.7, 0.95, 1.0], B)
+    rep, g_len = check_tree(oracle_mod, wl, par, dev, f"sweep_{seed}_{shape}")
+    assert rep.compared == B and rep.error_rows == 0
+
+
 def test_tree_full_vocab_many_rejections(oracle_mod, dev):
     """Candidates the target dislikes (drawn from the draft's tail), so that
     full-vocab rows reject child after child and the residual of residuals is
