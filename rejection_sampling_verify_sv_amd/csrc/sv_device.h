@@ -1136,10 +1136,13 @@ __device__ __forceinline__ const int32_t* nuc_list(const StepArgs& a, int k) {
     return a.ulist + ((int64_t)k * kNumCls + CLS_NUCLEUS) * a.ustride;
 }
 
-// Unit at index li of position k's concatenated list.
-__device__ __forceinline__ int32_t unit_at(const StepArgs& a, int k, const PosDesc& p, int li) {
+// Unit at index li of position k's concatenated list; *cls: its class
+// region, which is the class of the unit's row.
+__device__ __forceinline__ int32_t unit_at(const StepArgs& a, int k, const PosDesc& p, int li,
+                                           int* cls) {
     int c = 0;
     while (c < kNumCls - 1 && li >= p.n_cls[c]) li -= p.n_cls[c++];
+    *cls = c;
     return a.ulist[((int64_t)k * kNumCls + c) * a.ustride + li];
 }
 

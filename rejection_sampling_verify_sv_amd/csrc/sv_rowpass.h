@@ -398,9 +398,12 @@ __global__ __launch_bounds__(kThreads) void rowpass_kernel(StepArgs a, int k) {
         const int64_t tu0 = t - (int64_t)li * a.ntiles;
         int64_t tu1 = tu0 + (t_end - t);
         if (tu1 > a.ntiles) tu1 = a.ntiles;
-        const int u = unit_at(a, k, P, li);
+        // the class comes with the list region, so the first tile's loads
+        // need not wait for the row's info
+        int region;
+        const int u = unit_at(a, k, P, li, &region);
         const int b = unit_b(a, u, k), side = u & 1;
-        const int cls = a.force_full ? (int)CLS_FULL : a.rows[b].cls;
+        const int cls = a.force_full ? (int)CLS_FULL : region;
         const void* row = unit_row<DT>(a, b, side, unit_rowidx(a, u, b, k));
         const int64_t start = tu0 * TS::kTile;
         int64_t end = tu1 * TS::kTile;
