@@ -335,6 +335,18 @@ def measure(wl, dev, steps, warmup, replicas=1, ceiling=None, step_mode="auto"):
     }
     if ceiling:
         res["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling, 4)
+    if c is not None:
+        # every kernel of the step: its counted HBM bytes per step (rocprofv3
+        # FETCH_SIZE + WRITE_SIZE, calibrated) over its time per step (events)
+        kh = {}
+        for n, ms in per_kernel.items():
+            e = c["kernels"].get(n + "_kernel")
+            if not e or ms <= 0:
+                continue
+            b = e["bytes_per_dispatch"] * e["dispatches_per_step"]
+            kh[n] = {"bytes_per_step": int(b), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                     "frac": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+        res["kernels_hbm"] = kh
     del ins, ws
     torch.cuda.empty_cache()
     return res, acc, tok
