@@ -302,13 +302,14 @@ __device__ inline void select_boundary(const uint64_t* s_h, float top_p, float l
     __syncthreads();
 }
 
-// Workgroups per unit in the cut.  One workgroup alone reads a row far below
-// its share of HBM (its collect step is bound by instruction issue), so when
-// the units are few each gets several, up to one per compute unit in all
-// (the grid holds two per compute unit; two on one compute unit only halve
-// each other's issue rate), at most kMaxSplit and one per tile of the row.
-// A split unit's index in the nucleus list is below gridDim.x / 4 < kGrid / 2,
-// the rows of fn_sync and fn_keys.
+// Workgroups per unit in the cut.  One workgroup alone collects a row at
+// about 40 GB/s, far below its share of HBM, so when the units are few each
+// gets several, up to one per compute unit in all (the grid holds two per
+// compute unit; two on one compute unit slow each other down), at most
+// kMaxSplit and one per tile of the row.  A split unit's index in the nucleus
+// list is below gridDim.x / 4 here, and below kThreads with the split by
+// density in the kernel: either way below kGrid / 2, the rows of fn_sync and
+// fn_keys.
 constexpr int kMaxSplit = 8;
 constexpr int kDenseSplit = 3;   // workgroups of a unit expected to keep many boundary keys
 constexpr int kDenseKeys = 128;  // boundary keys from which a collect counts as such
