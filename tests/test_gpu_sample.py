@@ -96,6 +96,32 @@ def test_sample_parity(oracle_mod, dev, name, vocab, k):
     assert np.array_equal(dg0.cpu().numpy(), g_dg, equal_nan=True)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_sample_sweep(oracle_mod, dev, seed):
+    """Seeded batches of up to 700 rows (beyond 512 the draw runs position by
+    position), each row with its own sampler class and temperature, both
+    dtypes, every row against the oracle."""
+    rng = np.random.default_rng(6100 + seed)
+    B = int(rng.choice([3, 300, 700]))
+    V = int(rng.choice([2048, 20011, 65543]))
+    dtype = "bf16" if rng.random() < 0.5 else "f32"
+    rows = rng.normal(0, float(rng.choice([1.0, 3.0])), (B, V)).astype(np.float32)
+    prm = np.zeros(B, workloads.PARAMS_DTYPE)
+    prm["temperature"] = rng.choice([0.0, 0.5, 1.0, 1.5], B)
+    prm["top_k"] = rng.choice([0, 1, 20, 64, 100, V], B)
+    prm["top_p"] = rng.choice([0.5, 0.9, 1.0], B)
+    u = rng.random(B, dtype=np.float32)
+    stored = rows if dtype == "f32" else workloads.f32_to_bf16_bits(rows)
+    g_tok, g_st, g_dg = _gpu_sample(stored, prm, u, dtype, dev)
+    ref = _oracle_draw(oracle_mod, stored, prm, u, dtype)
+    rep = compare(g_tok[:, None], g_st, g_dg, ref, inputs=draws(stored, prm, u, dtype),
+                  oracle_mod=oracle_mod)
+    _say(f"[gpu] sample sweep {seed} B={B} V={V} {dtype}: {rep.describe()}")
+    assert rep.mismatch_in_band_by_class.get("top_k", 0) == 0, rep.describe()
+    assert rep.tight_ok, rep.describe()
+    assert rep.compared + rep.unsupported == B
+
+
 def test_sample_edge_rows(oracle_mod, dev):
     rng = np.random.default_rng(zlib.crc32(b"sample_edges"))
     B, V = 12, 5003
