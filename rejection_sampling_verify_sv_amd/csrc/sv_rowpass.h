@@ -378,6 +378,209 @@ __device__ __forceinline__ void seg_nuc(const void* row, int64_t start, int64_t 
     }
 }
 
+// ---- units no longer than one wave's share of a tile ----------------------
+// A row of at most kWave kE tokens fits in one wave's loads.  A workgroup then
+// works its units four at a time, one per wave, and each wave's record is its
+// unit's whole record: no workgroup barrier and no merge of the waves' lists
+// per unit (worked one at a time by the whole workgroup, such a unit left
+// three waves with a quarter of the loads each and paid the barriers and the
+// merge of four lists for a few kilobytes).  Nucleus units keep the
+// workgroup-wide histogram.
+
+// Lane l's vector j is vector j kWave + l of the row, so the lane's elements
+// ascend in id; tokens at or past V read as -inf.
+template <int DT>
+__device__ __forceinline__ uint32_t wave_elem_id(int idx) {
+    constexpr int kVec = Elt<DT>::kVec;
+    int lane = lane_id();
+    asm volatile("" : "+v"(lane));  // recomputed where used, not kept live
+    return (uint32_t)(((idx / kVec) * kWave + lane) * kVec + idx % kVec);
+}
+
+template <int DT, bool kAligned>
+__device__ __forceinline__ void load_wave_unit(const void* row, int V,
+                                               float (&v)[TileShape<DT>::kE]) {
+    constexpr int kVec = Elt<DT>::kVec;
+    const int lane = lane_id();
+    if constexpr (kAligned) {
+        // whole vectors through range-checked buffer loads, the vector that
+        // straddles V token by token
+        const int nvec = V / kVec;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(row, (uint32_t)nvec * 16u);
+        RawTile r;
+#pragma unroll
+        for (int j = 0; j < kLoads; j++)
+            r.q[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (j * kWave + lane) * 16, 0, 2 /* nt */);
+        unpack_tile<DT>(r, v);
+#pragma unroll
+        for (int j = 0; j < kLoads; j++) {
+            const int vi = j * kWave + lane;
+#pragma unroll
+            for (int e = 0; e < kVec; e++)
+                if (vi * kVec + e >= V) v[j * kVec + e] = -INFINITY;
+            if (vi == nvec && nvec * kVec < V) {
+#pragma unroll
+                for (int e = 0; e < kVec; e++)
+                    if (vi * kVec + e < V) v[j * kVec + e] = load_one<DT>(row, vi * kVec + e);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kLoads; j++) {
+#pragma unroll
+            for (int e = 0; e < kVec; e++) {
+                const int i = (j * kWave + lane) * kVec + e;
+                const float x = load_one<DT>(row, i < V ? i : V - 1);
+                v[j * kVec + e] = i < V ? x : -INFINITY;
+            }
+        }
+    }
+}
+
+// Greedy unit: the best (logit, lowest id) key.
+template <int DT, bool kAligned>
+__device__ __forceinline__ void wave_greedy(const void* row, int V, PartSlot* out) {
+    using TS = TileShape<DT>;
+    float v[TS::kE];
+    load_wave_unit<DT, kAligned>(row, V, v);
+    float vmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < TS::kE; i++) vmax = fmaxf(vmax, v[i]);
+    uint64_t best = 0ull;
+#pragma unroll
+    for (int i = 0; i < TS::kE; i++) {
+        const uint32_t id = wave_elem_id<DT>(i);
+        if (best == 0ull && (int)id < V && v[i] == vmax) best = make_key(v[i], id);
+    }
+    const uint64_t r = wave_max_u64(best);
+    if (lane_id() == 0) out->keys[0] = r;
+}
+
+// Top-k unit: the wave's top-64 list (seg_topk's selection on one tile, with
+// no thresholds shared between waves: each wave has a unit of its own).
+template <int DT, bool kAligned>
+__device__ __forceinline__ void wave_topk(const void* row, int V, int k_eff, RowpassSmem& sm,
+                                          PartSlot* out) {
+    using TS = TileShape<DT>;
+    static_assert(TS::kE <= 32, "candidate mask is 32 bits");
+    const int lane = lane_id();
+    uint64_t* cbuf = sm.cbuf[wave_id()];
+    float v[TS::kE];
+    load_wave_unit<DT, kAligned>(row, V, v);
+    WaveTopk st;
+    st.lst = 0ull;
+    st.thr = 0ull;
+    st.cnt = 0;
+    {  // the k-th largest of the lanes' best keys bounds the unit's k-th key
+        float vmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < TS::kE; i++) vmax = fmaxf(vmax, v[i]);
+        uint64_t best = 0ull;
+#pragma unroll
+        for (int i = 0; i < TS::kE; i++) {
+            const uint32_t id = wave_elem_id<DT>(i);
+            if (best == 0ull && (int)id < V && v[i] == vmax) best = make_key(v[i], id);
+        }
+        const uint64_t th = lane_value(wave_sort_desc(best), k_eff - 1);
+        if (th > 0ull) st.thr = th - 1ull;
+    }
+    float fl = thr_floor(st.thr);
+    uint32_t bits = 0u;
+#pragma unroll
+    for (int i = TS::kE - 1; i >= 0; i--)
+        bits = (bits << 1) | (((int)wave_elem_id<DT>(i) < V && v[i] >= fl) ? 1u : 0u);
+    while (__ballot(bits != 0u) != 0ull) {
+        int total;
+        const uint32_t c = (uint32_t)__popc(bits);
+        const int excl = wave_excl_count(c, &total);
+        int room = kCandBuf - (st.cnt + excl);
+        room = room < 0 ? 0 : room;
+        const int nw = (int)c < room ? (int)c : room;
+        const int pos = st.cnt + excl;
+        for (int j = 0; j < nw; j++) {
+            const int i = __builtin_ctz(bits);
+            bits &= bits - 1u;
+            cbuf[pos + j] = make_raw(pick_elem(v, i), wave_elem_id<DT>(i));
+        }
+        st.cnt = st.cnt + total < kCandBuf ? st.cnt + total : kCandBuf;
+        if (st.cnt >= kWave) {
+            wt_flush(st, cbuf, k_eff, sm);
+            fl = thr_floor(st.thr);
+            uint32_t keep = 0u;
+#pragma unroll
+            for (int i = TS::kE - 1; i >= 0; i--) keep = (keep << 1) | (v[i] >= fl ? 1u : 0u);
+            bits &= keep;
+        }
+    }
+    if (st.cnt > 0) wt_flush(st, cbuf, k_eff, sm);
+    out->keys[lane] = st.lst;
+}
+
+// Untruncated unit: {max, sum of exp2((l - max) c)} in the record of wave 0 of
+// its one tile; the other waves' records are empty.
+template <int DT, bool kAligned>
+__device__ __forceinline__ void wave_full(const void* row, int V, float T, FullStat* rec) {
+    using TS = TileShape<DT>;
+    const float c = exp2_coef(T);
+    float v[TS::kE];
+    load_wave_unit<DT, kAligned>(row, V, v);
+    float lm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < TS::kE; i++) lm = fmaxf(lm, v[i]);
+    const float m = wave_max_f32(lm);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    if (m > -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < TS::kE; i++) acc[i & 3] += fast_exp2((v[i] - m) * c);
+    }
+    const double s = wave_sum((double)((acc[0] + acc[1]) + (acc[2] + acc[3])));
+    const int lane = lane_id();
+    if (lane < kWaves) {
+        FullStat r;
+        r.m = lane == 0 ? m : -INFINITY;
+        r.pad = 0.f;
+        r.s = lane == 0 ? s : 0.0;
+        rec[lane] = r;
+    }
+}
+
+// Units [l0, l1) of position k (each one tile): four at a time, one per wave,
+// then the nucleus units one at a time with the whole workgroup.
+template <int DT, bool kAligned>
+__device__ __forceinline__ void rowpass_short(const StepArgs& a, int k, const PosDesc& P, int l0,
+                                              int l1, RowpassSmem& sm, uint64_t* s_h) {
+    const int w = blockIdx.x;
+    const int V = (int)a.V;
+    for (int base = l0; base < l1; base += kWaves) {
+        const int li = base + wave_id();
+        if (li >= l1) break;
+        int region;
+        const int u = unit_at(a, k, P, li, &region);
+        const int cls = a.force_full ? (int)CLS_FULL : region;
+        if (cls == CLS_NUCLEUS) continue;
+        const int b = unit_b(a, u, k), side = u & 1;
+        const void* row = unit_row<DT>(a, b, side, unit_rowidx(a, u, b, k));
+        PartSlot* out = a.parts + li + w;
+        if (cls == CLS_GREEDY)
+            wave_greedy<DT, kAligned>(row, V, out);
+        else if (cls == CLS_TOPK)
+            wave_topk<DT, kAligned>(row, V, a.rows[b].k_eff, sm, out);
+        else
+            wave_full<DT, kAligned>(row, V, a.rows[b].T, a.tstat + (int64_t)u * kWaves);
+    }
+    if (a.force_full || P.n_cls[CLS_NUCLEUS] == 0) return;
+    for (int li = l0; li < l1; li++) {
+        int region;
+        const int u = unit_at(a, k, P, li, &region);
+        if (region != CLS_NUCLEUS) continue;
+        const int b = unit_b(a, u, k), side = u & 1;
+        const void* row = unit_row<DT>(a, b, side, unit_rowidx(a, u, b, k));
+        __syncthreads();  // LDS is reused from the previous unit
+        seg_nuc<DT, kAligned>(row, 0, a.V, a.V, a.rows[b].T, s_h, sm, a.parts + li + w,
+                              a.fn_unit + u, a.hist + (int64_t)(li + w) * kHistSlot);
+    }
+}
+
 // The workgroups split the tiles of position k's units evenly (see
 // flat_begin); each (unit, workgroup) piece leaves its record at slot
 // li + blockIdx.x.
@@ -393,6 +596,10 @@ __global__ __launch_bounds__(kThreads) void rowpass_kernel(StepArgs a, int k) {
     const int Gr = row_grid(P, T, (int)gridDim.x);  // the workgroups taking part
     int64_t t = flat_begin(T, Gr, w);
     const int64_t t_end = flat_begin(T, Gr, w + 1);
+    if (a.V <= (int64_t)kWave * TS::kE) {  // one tile per unit: t counts units
+        rowpass_short<DT, kAligned>(a, k, P, (int)t, (int)t_end, sm, s_h);
+        return;
+    }
     while (t < t_end) {
         const int li = (int)(t / a.ntiles);
         const int64_t tu0 = t - (int64_t)li * a.ntiles;

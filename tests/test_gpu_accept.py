@@ -102,7 +102,8 @@ def _mixed(seed, B, V, dtype):
     return bf(t), bf(d), prm
 
 
-@pytest.mark.parametrize("dtype,V", [("f32", 30011), ("bf16", 20011), ("f32", 4096)])
+@pytest.mark.parametrize("dtype,V", [("f32", 30011), ("bf16", 20011), ("f32", 4096),
+                                     ("f32", 1000), ("bf16", 2048), ("f32", 61)])
 def test_mixed_samplers(oracle_mod, dev, dtype, V):
     B = 96
     t, d, prm = _mixed(zlib.crc32(f"acc{dtype}{V}".encode()), B, V, dtype)

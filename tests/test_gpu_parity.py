@@ -201,15 +201,24 @@ def test_split_units_on_a_dirty_workspace(oracle_mod, dev):
     assert rep.compared == wl.B
 
 
-def _mixed_case(seed, wide=False):
+def _mixed_case(seed, wide=False, short=False):
     """A seeded batch whose rows each draw their own sampler (greedy, top-k up
     to 64, top-k above 64 (not served), untruncated, nucleus), temperature,
     draft length and logit scale; drafts are sampled from the untruncated
     tempered draft, so some fall outside q.  wide: larger batches, drafts
     and vocabularies, more nucleus rows, and logits rounded to a grid on some
-    batches (many ties)."""
-    rng = np.random.default_rng((9001 if wide else 5150) + seed)
-    if wide:
+    batches (many ties).  short: rows that fit one wave's loads (up to 1024
+    fp32 or 2048 bf16 tokens) and a token past either limit, batches from
+    one row to 1100."""
+    rng = np.random.default_rng((9001 if wide else 7707 if short else 5150) + seed)
+    if short:
+        B = int(rng.choice([1, 9, 64, 300, 1100], p=[0.15, 0.2, 0.2, 0.25, 0.2]))
+        K = int(rng.integers(1, 5))
+        dtype = "bf16" if rng.random() < 0.5 else "f32"
+        V = int(rng.choice([2, 7, 64, 333, 1000, 1021, 1024, 1025] if dtype == "f32"
+                           else [5, 64, 999, 2047, 2048, 2049]))
+        probs = [0.2, 0.3, 0.05, 0.2, 0.25]
+    elif wide:
         B = int(rng.choice([3, 64, 130, 300, 600], p=[0.1, 0.2, 0.25, 0.25, 0.2]))
         K = int(rng.integers(1, 8))
         V = int(rng.choice([2048, 30011, 65543]))
@@ -221,7 +230,8 @@ def _mixed_case(seed, wide=False):
         K = int(rng.integers(1, 7))
         V = int(rng.choice([3001, 9000, 20011]))
         probs = [0.2, 0.3, 0.05, 0.2, 0.25]
-    dtype = "bf16" if rng.random() < 0.5 else "f32"
+    if not short:
+        dtype = "bf16" if rng.random() < 0.5 else "f32"
     scale = float(rng.choice([1.0, 3.0]))
     t = rng.normal(0, scale, (B, K + 1, V))
     d = t[:, :K] * 0.8 + rng.normal(0, scale * 0.6, (B, K, V))
@@ -235,8 +245,10 @@ def _mixed_case(seed, wide=False):
             prm[b] = (0.0, 0, 1.0, 0)
         elif kind[b] == 1:
             prm[b] = (T, int(rng.integers(1, 65)), float(rng.choice([1.0, 0.9, 0.6])), 0)
-        elif kind[b] == 2:
+        elif kind[b] == 2 and V > 66:
             prm[b] = (T, int(rng.integers(65, V)), 1.0, 0)
+        elif kind[b] == 2:
+            prm[b] = (T, int(rng.integers(1, V + 1)), 1.0, 0)
         elif kind[b] == 3:
             prm[b] = (T, int(rng.choice([0, V])), 1.0, 0)
         else:
@@ -248,8 +260,8 @@ def _mixed_case(seed, wide=False):
         for k in range(K):
             tok[b, k] = int(np.argmax(d[b, k] / T + rng.gumbel(size=V)))
     u = rng.random((B, K + 1), dtype=np.float32)
-    return workloads.custom(t, d, tok, L, prm, u, dtype=dtype,
-                            name=f"mixed_sweep_{'wide_' if wide else ''}{seed}")
+    tag = "wide_" if wide else "short_" if short else ""
+    return workloads.custom(t, d, tok, L, prm, u, dtype=dtype, name=f"mixed_sweep_{tag}{seed}")
 
 
 @pytest.mark.parametrize("seed", range(12))
@@ -272,6 +284,19 @@ def test_mixed_rows_sweep_wide(oracle_mod, dev, seed):
     modes = ["auto", "positions"] + (["dense"] if 2 * wl.B * (wl.K + 1) <= 1024 else [])
     for mode in modes:
         rep, _, _ = check(oracle_mod, wl, dev, label=wl.name, step_mode=mode)
+        assert rep.compared + rep.unsupported == wl.B
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_short_rows_sweep(oracle_mod, dev, seed):
+    """Rows short enough for one wave's loads, where the row pass gives each
+    wave a unit of its own (nucleus units keep the whole workgroup), with
+    every sampler class mixed in, in every step mode the batch takes."""
+    wl = _mixed_case(seed, short=True)
+    modes = ["auto", "positions"] + (["dense"] if 2 * wl.B * (wl.K + 1) <= 1024 else [])
+    for mode in modes:
+        rep, _, _ = check(oracle_mod, wl, dev, label=f"{wl.name} V={wl.V} {wl.dtype}",
+                          step_mode=mode)
         assert rep.compared + rep.unsupported == wl.B
 
 
