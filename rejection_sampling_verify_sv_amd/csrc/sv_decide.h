@@ -1072,14 +1072,39 @@ __device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, const 
     }
 }
 
-// One workgroup: zero the work counters, then classify every row, initialise
-// its outputs and list its position-0 units.  A row is invalid when T is
+// Workgroup 0 zeroes the work counters, then classifies every row, sets its
+// accept length and lists its position-0 units; workgroups 1.. (plan_grid)
+// fill the token, path and diagnostic outputs.  A row is invalid when T is
 // negative, NaN or infinite, top_p is not > 0, draft_len is outside [0, K] or
 // a read draft token is outside [0, V).
 constexpr int kPlanThreads = 1024;
+// Workgroups of the plan launch: one that classifies, and enough to fill the
+// outputs of B rows of K + 1 positions (about 32 tokens per thread, at most
+// 64 workgroups).
+__host__ __device__ __forceinline__ unsigned plan_grid(int64_t B, int64_t K) {
+    const int64_t per = (int64_t)kPlanThreads * 32;
+    const int64_t n = (B * (K + 1) + per - 1) / per;
+    return 1u + (unsigned)(n < 64 ? n : 64);
+}
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const int32_t* draft_len,
                                                             const sv_sampler_params* params) {
+    if (blockIdx.x > 0) {
+        // the other workgroups fill the outputs every row starts from (-1
+        // tokens and path nodes, NaN diagnostics) as flat arrays, so that
+        // their stores are coalesced and run beside the classification
+        if (a.stats) return;  // no verify outputs
+        const int64_t stride = (int64_t)(gridDim.x - 1) * kPlanThreads;
+        const int64_t i0 = (int64_t)(blockIdx.x - 1) * kPlanThreads + threadIdx.x;
+        const int64_t nt = (int64_t)a.B * (a.K + 1);
+        for (int64_t i = i0; i < nt; i += stride) a.out_tokens[i] = -1;
+        if (a.out_path)
+            for (int64_t i = i0; i < nt; i += stride) a.out_path[i] = -1;
+        if (a.diag)
+            for (int64_t i = i0; i < 4 * nt; i += stride)
+                a.diag[i] = __longlong_as_double(0x7FF8000000000000ll);
+        return;
+    }
     __shared__ int s_nc[kNumCls];  // position-0 region lengths (LDS counters)
     for (int i = threadIdx.x; i < a.K + 2; i += kPlanThreads) {
         for (int c = 0; c < kNumCls; c++) a.pos[i].n_cls[c] = 0;
@@ -1191,16 +1216,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
         }
         a.rows[b] = ri;
         if (a.stats) continue;  // no verify outputs
-        int32_t* o = a.out_tokens + (int64_t)b * (a.K + 1);
-        for (int j = 0; j <= a.K; j++) o[j] = -1;
-        if (a.out_path)
-            for (int j = 0; j <= a.K; j++) a.out_path[(int64_t)b * (a.K + 1) + j] = -1;
         a.out_acc[b] = (cls == CLS_ERROR) ? -1 : (cls == CLS_UNSUP ? -2 : 0);
-        if (a.diag) {
-            double* d = a.diag + (int64_t)b * 4 * (a.K + 1);
-            for (int j = 0; j < 4 * (a.K + 1); j++)
-                d[j] = __longlong_as_double(0x7FF8000000000000ll);
-        }
     }
     __syncthreads();
     if (threadIdx.x < kNumCls) a.pos[0].n_cls[threadIdx.x] = s_nc[threadIdx.x];
