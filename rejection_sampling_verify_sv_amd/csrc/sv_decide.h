@@ -1072,30 +1072,92 @@ __device__ __attribute__((noinline)) void decide_rows(const StepArgs* ga, const 
     }
 }
 
-// Workgroup 0 zeroes the work counters, then classifies every row, sets its
-// accept length and lists its position-0 units; workgroups 1.. (plan_grid)
-// fill the token, path and diagnostic outputs.  A row is invalid when T is
-// negative, NaN or infinite, top_p is not > 0, draft_len is outside [0, K] or
-// a read draft token is outside [0, V).
+// The classifying workgroups (plan_groups) each take a contiguous share of
+// the rows: classify them, set their accept lengths and list their
+// position-0 units after those of the rows before (counted again by each);
+// workgroup 0 also zeroes the work counters.  The other workgroups fill the
+// token, path and diagnostic outputs.  A row is invalid when T is negative,
+// NaN or infinite, top_p is not > 0, draft_len is outside [0, K] or a read
+// draft token is outside [0, V).
 constexpr int kPlanThreads = 1024;
-// Workgroups of the plan launch: one that classifies, and enough to fill the
-// outputs of B rows of K + 1 positions (about 32 tokens per thread, at most
-// 64 workgroups).
-__host__ __device__ __forceinline__ unsigned plan_grid(int64_t B, int64_t K) {
+// Workgroups of the plan that classify: one per kPlanThreads rows (at most
+// kPlanGroups) on a step whose position-0 list holds at most two units per
+// row; one for a dense step or a tree verify (their rows list more units,
+// or check a tree), which then works through every row.
+constexpr int kPlanGroups = 16;
+constexpr int kPlanRows = 4;  // rows per thread whose loads go out together
+__host__ __device__ __forceinline__ int plan_groups(int64_t B, int tree, int d0) {
+    if (tree || d0 == 0 || B <= kPlanThreads) return 1;
+    const int64_t g = (B + kPlanThreads - 1) / kPlanThreads;
+    return (int)(g < kPlanGroups ? g : kPlanGroups);
+}
+// The whole plan launch: those, and enough workgroups to fill the outputs of
+// B rows of K + 1 positions (about 32 tokens per thread, at most 64).
+__host__ __device__ __forceinline__ unsigned plan_grid(int64_t B, int64_t K, int tree, int d0) {
     const int64_t per = (int64_t)kPlanThreads * 32;
     const int64_t n = (B * (K + 1) + per - 1) / per;
-    return 1u + (unsigned)(n < 64 ? n : 64);
+    return (unsigned)plan_groups(B, tree, d0) + (unsigned)(n < 64 ? n : 64);
+}
+
+// Class of row b (CLS_ERROR when invalid; see the plan), with its draft
+// length.  check_tree: also the tree checks of a tree verify (which use the
+// row's scratch in nscr).
+__device__ __forceinline__ int plan_class(const StepArgs& a, const int32_t* draft_len,
+                                          const sv_sampler_params& prm, int b, int* L_out) {
+    const int L = draft_len ? draft_len[b] : a.K;
+    *L_out = L;
+    const float T = prm.temperature, tp = prm.top_p;
+    const int tk = prm.top_k;
+    bool bad = !(T >= 0.f) || !(T < INFINITY) || !(tp > 0.f) || L < 0 || L > a.K;
+    if (!bad && !a.stats) {  // the statistics read no draft tokens
+        for (int j = 0; j < L; j++) {
+            const int t = a.tokens[(int64_t)b * a.K + j];
+            if (t < 0 || t >= a.V) bad = true;
+        }
+    }
+    if (!bad && a.tree) {
+        // nodes 1..L: parent in [0, c), depth at most max_depth, at most
+        // max_kids children per node (the host loops over that many levels
+        // and child rounds)
+        const int32_t* par = a.parents + (int64_t)b * a.K;
+        int32_t* ns = a.nscr + (int64_t)b * (a.K + 1);
+        ns[0] = 0;
+        for (int c = 1; c <= L && !bad; c++) {
+            const int pc = par[c - 1];
+            if (pc < 0 || pc >= c) {
+                bad = true;
+            } else {
+                ns[c] = ns[pc] + 1;
+                bad = ns[c] > a.max_depth;
+            }
+        }
+        if (!bad) {
+            for (int c = 0; c <= L; c++) ns[c] = 0;
+            for (int c = 1; c <= L; c++) bad |= ++ns[par[c - 1]] > a.max_kids;
+        }
+    }
+    if (bad) return CLS_ERROR;
+    if (T == 0.f) return CLS_GREEDY;
+    if (tk > 0 && tk < a.V) return (tk <= kMaxTopK) ? CLS_TOPK : CLS_UNSUP;
+    return (tp < 1.f) ? CLS_NUCLEUS : CLS_FULL;
+}
+// Position-0 units of a row of class cls (>= 0) and draft length L: the
+// target, and the draft unless the row is greedy (the statistics read both).
+__device__ __forceinline__ int plan_units0(const StepArgs& a, int cls, int L) {
+    return ((cls != CLS_GREEDY || a.stats) && 0 < L) ? 2 : 1;
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const int32_t* draft_len,
                                                             const sv_sampler_params* params) {
-    if (blockIdx.x > 0) {
+    const int n_cls_groups = plan_groups(a.B, a.tree, a.d0);
+    if ((int)blockIdx.x >= n_cls_groups) {
         // the other workgroups fill the outputs every row starts from (-1
         // tokens and path nodes, NaN diagnostics) as flat arrays, so that
         // their stores are coalesced and run beside the classification
         if (a.stats) return;  // no verify outputs
-        const int64_t stride = (int64_t)(gridDim.x - 1) * kPlanThreads;
-        const int64_t i0 = (int64_t)(blockIdx.x - 1) * kPlanThreads + threadIdx.x;
+        const int nf = (int)gridDim.x - n_cls_groups, f = (int)blockIdx.x - n_cls_groups;
+        const int64_t stride = (int64_t)nf * kPlanThreads;
+        const int64_t i0 = (int64_t)f * kPlanThreads + threadIdx.x;
         const int64_t nt = (int64_t)a.B * (a.K + 1);
         for (int64_t i = i0; i < nt; i += stride) a.out_tokens[i] = -1;
         if (a.out_path)
@@ -1105,66 +1167,68 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
                 a.diag[i] = __longlong_as_double(0x7FF8000000000000ll);
         return;
     }
-    __shared__ int s_nc[kNumCls];  // position-0 region lengths (LDS counters)
-    for (int i = threadIdx.x; i < a.K + 2; i += kPlanThreads) {
-        for (int c = 0; c < kNumCls; c++) a.pos[i].n_cls[c] = 0;
-        a.pos[i].n_sample = 0;
-        a.pos[i].n_pick = 0;
-    }
-    if (threadIdx.x < kNumCls) s_nc[threadIdx.x] = 0;
-    if (threadIdx.x == 0) *const_cast<StepArgs*>(a.self) = a;
-    {  // counters of split nucleus units (each launch leaves them at zero);
+    __shared__ int s_nc[kNumCls];    // this workgroup's region lengths (LDS counters)
+    __shared__ int s_base[kNumCls];  // units the rows before this workgroup's list
+    const int G = plan_groups(a.B, a.tree, a.d0), w = blockIdx.x;
+    const int chunk = (a.B + G - 1) / G;
+    const int r0 = w * chunk, r1 = r0 + chunk < a.B ? r0 + chunk : a.B;
+    if (w == 0) {
+        for (int i = threadIdx.x; i < a.K + 2; i += kPlanThreads) {
+            // pos[0].n_cls is written at the end, by the last workgroup
+            if (i > 0)
+                for (int c = 0; c < kNumCls; c++) a.pos[i].n_cls[c] = 0;
+            a.pos[i].n_sample = 0;
+            a.pos[i].n_pick = 0;
+        }
+        if (threadIdx.x == 0) *const_cast<StepArgs*>(a.self) = a;
+        // counters of split nucleus units (each launch leaves them at zero);
         // a split unit's index is below both the list length of a launch
         // (ustride) and kGrid / 2
         const int rows = a.ustride < kGrid / 2 ? a.ustride : kGrid / 2;
         for (int i = threadIdx.x; i < 2 * rows; i += kPlanThreads) a.fn_sync[i] = 0;
-        for (int i = threadIdx.x; i < a.B; i += kPlanThreads) a.fn_row[i] = 0;
+        if (a.tree)  // rows per (level, child round) of a tree verify
+            for (int i = threadIdx.x; i < (a.K + 1) * kMaxKids; i += kPlanThreads) a.tcount[i] = 0;
     }
-    if (a.tree)  // rows per (level, child round) of a tree verify
-        for (int i = threadIdx.x; i < (a.K + 1) * kMaxKids; i += kPlanThreads) a.tcount[i] = 0;
-    __syncthreads();
-    for (int b = threadIdx.x; b < a.B; b += kPlanThreads) {
-        const sv_sampler_params prm = params[b];
-        const int L = draft_len ? draft_len[b] : a.K;
-        const float T = prm.temperature, tp = prm.top_p;
-        const int tk = prm.top_k;
-        bool bad = !(T >= 0.f) || !(T < INFINITY) || !(tp > 0.f) || L < 0 || L > a.K;
-        if (!bad && !a.stats) {  // the statistics read no draft tokens
-            for (int j = 0; j < L; j++) {
-                const int t = a.tokens[(int64_t)b * a.K + j];
-                if (t < 0 || t >= a.V) bad = true;
-            }
-        }
-        if (!bad && a.tree) {
-            // nodes 1..L: parent in [0, c), depth at most max_depth, at most
-            // max_kids children per node (the host loops over that many
-            // levels and child rounds)
-            const int32_t* par = a.parents + (int64_t)b * a.K;
-            int32_t* ns = a.nscr + (int64_t)b * (a.K + 1);
-            ns[0] = 0;
-            for (int c = 1; c <= L && !bad; c++) {
-                const int pc = par[c - 1];
-                if (pc < 0 || pc >= c) {
-                    bad = true;
-                } else {
-                    ns[c] = ns[pc] + 1;
-                    bad = ns[c] > a.max_depth;
+    for (int i = r0 + threadIdx.x; i < r1; i += kPlanThreads) a.fn_row[i] = 0;
+    if (threadIdx.x < kNumCls) s_nc[threadIdx.x] = s_base[threadIdx.x] = 0;
+    // The units of the rows before r0, per class, counted here again (no
+    // workgroup waits for another): kPlanRows rows per thread at a time, so
+    // that their loads go out together.
+    if (r0 > 0) {  // (the same threads clear and then set s_base)
+        int cnt[kNumCls] = {0, 0, 0, 0};
+        for (int b0 = threadIdx.x; b0 < r0; b0 += kPlanThreads * kPlanRows) {
+#pragma unroll
+            for (int r = 0; r < kPlanRows; r++) {
+                const int b = b0 + r * kPlanThreads;
+                if (b < r0) {
+                    int L;
+                    const int cls = plan_class(a, draft_len, params[b], b, &L);
+#pragma unroll
+                    for (int c = 0; c < kNumCls; c++)
+                        cnt[c] += (cls == c) ? plan_units0(a, cls, L) : 0;
                 }
             }
-            if (!bad) {
-                for (int c = 0; c <= L; c++) ns[c] = 0;
-                for (int c = 1; c <= L; c++) bad |= ++ns[par[c - 1]] > a.max_kids;
-            }
         }
-        int cls;
-        if (bad)
-            cls = CLS_ERROR;
-        else if (T == 0.f)
-            cls = CLS_GREEDY;
-        else if (tk > 0 && tk < a.V)
-            cls = (tk <= kMaxTopK) ? CLS_TOPK : CLS_UNSUP;
-        else
-            cls = (tp < 1.f) ? CLS_NUCLEUS : CLS_FULL;
+        __shared__ int s_red[kNumCls][kPlanThreads / kWave];
+#pragma unroll
+        for (int c = 0; c < kNumCls; c++) {
+            const int t = (int)wave_sum((double)cnt[c]);  // exact: integers below 2^53
+            if (lane_id() == 0) s_red[c][wave_id()] = t;
+        }
+        __syncthreads();
+        if (threadIdx.x < kNumCls) {
+            int t = 0;
+            for (int j = 0; j < kPlanThreads / kWave; j++) t += s_red[threadIdx.x][j];
+            s_base[threadIdx.x] = t;
+        }
+    }
+    __syncthreads();
+    for (int b = r0 + threadIdx.x; b < r1; b += kPlanThreads) {
+        const sv_sampler_params prm = params[b];
+        int L;
+        const int cls = plan_class(a, draft_len, prm, b, &L);
+        const float T = prm.temperature, tp = prm.top_p;
+        const int tk = prm.top_k;
         RowInfo ri;
         ri.cls = cls;
         ri.L = L;
@@ -1184,7 +1248,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
         ri.mt = ri.zt = ri.md = ri.zd = 0.0;
         ri.tau_t = ri.tau_d = 0ull;
         if (cls >= 0 && a.d0 == 0) {
-            // a dense step: the units of every position, target then draft
+            // a dense step (one workgroup): the units of every position,
+            // target then draft
             const bool drafts = cls != CLS_GREEDY && 0 < L;
             const int nu = (L + 1) + (drafts ? L : 0);
             int li = atomicAdd(&s_nc[cls], nu);
@@ -1198,20 +1263,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
                 }
             }
         } else if (cls >= 0) {
-            // position-0 units (the layout the decisions use, LDS counters)
-            const bool draft = (cls != CLS_GREEDY || a.stats) && 0 < L;
-            const int nu = draft ? 2 : 1;
-            const int li = atomicAdd(&s_nc[cls], nu);
+            // position-0 units (the layout the decisions use, LDS counters
+            // after the rows of the workgroups before)
+            const int nu = plan_units0(a, cls, L);
+            const int li = s_base[cls] + atomicAdd(&s_nc[cls], nu);
             int32_t* ul = a.ulist + (int64_t)cls * a.ustride;
             ul[li] = b * 2;
             ri.li_t = li;
-            if (draft) {
+            if (nu == 2) {
                 ul[li + 1] = b * 2 + 1;
                 ri.li_d = li + 1;
             }
             if (cls == CLS_NUCLEUS) {
                 a.fn_unit[b * 2].rehist = 0;
-                if (draft) a.fn_unit[b * 2 + 1].rehist = 0;
+                if (nu == 2) a.fn_unit[b * 2 + 1].rehist = 0;
             }
         }
         a.rows[b] = ri;
@@ -1219,7 +1284,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StepArgs a, const in
         a.out_acc[b] = (cls == CLS_ERROR) ? -1 : (cls == CLS_UNSUP ? -2 : 0);
     }
     __syncthreads();
-    if (threadIdx.x < kNumCls) a.pos[0].n_cls[threadIdx.x] = s_nc[threadIdx.x];
+    if (w == G - 1 && threadIdx.x < kNumCls)
+        a.pos[0].n_cls[threadIdx.x] = s_base[threadIdx.x] + s_nc[threadIdx.x];
 }
 
 }  // namespace sv

@@ -219,7 +219,7 @@ int launch_all(const int32_t* draft_len, const sv_sampler_params* params, StepAr
     const unsigned cut_grid = g.cut < cut_cap ? g.cut : cut_cap;
     const unsigned row_grid = (unsigned)(B < kGrid ? B : kGrid);
     mark();
-    plan_kernel<<<plan_grid(a.B, a.K), kPlanThreads, 0, st>>>(a, draft_len, params);
+    plan_kernel<<<plan_grid(a.B, a.K, a.tree, a.d0), kPlanThreads, 0, st>>>(a, draft_len, params);
     for (int k = 0; k <= (a.d0 < a.K ? a.d0 : a.K); k++) {
         mark();
         rowpass_kernel<DT, kAligned><<<grow, kThreads, 0, st>>>(a, k);
@@ -252,7 +252,7 @@ int launch_tree(const int32_t* n_cand, const sv_sampler_params* params, StepArgs
     const unsigned cut_grid = g.cut < cut_cap ? g.cut : cut_cap;
     const unsigned row_grid = (unsigned)(B < kGrid ? B : kGrid);
     const unsigned wave_grid = (unsigned)((B + kWaves - 1) / kWaves);
-    plan_kernel<<<plan_grid(a.B, a.K), kPlanThreads, 0, st>>>(a, n_cand, params);
+    plan_kernel<<<plan_grid(a.B, a.K, a.tree, a.d0), kPlanThreads, 0, st>>>(a, n_cand, params);
     for (int k = 0; k <= a.max_depth; k++) {
         rowpass_kernel<DT, kAligned><<<grow, kThreads, 0, st>>>(a, k);
         cut_decide_kernel<DT, kAligned><<<cut_grid, kThreads, 0, st>>>(a, k);
@@ -282,7 +282,7 @@ int launch_stats(const sv_sampler_params* params, StepArgs a, hipStream_t st) {
     const unsigned cut_cap = (unsigned)(2 * B * kMaxSplit < kGrid ? 2 * B * kMaxSplit : kGrid);
     const unsigned cut_grid = g.cut < cut_cap ? g.cut : cut_cap;
     const unsigned row_groups = (unsigned)((B + kWaves - 1) / kWaves);
-    plan_kernel<<<plan_grid(a.B, a.K), kPlanThreads, 0, st>>>(a, nullptr, params);
+    plan_kernel<<<plan_grid(a.B, a.K, a.tree, a.d0), kPlanThreads, 0, st>>>(a, nullptr, params);
     rowpass_kernel<DT, kAligned><<<g.rowpass, kThreads, 0, st>>>(a, 0);
     cut_decide_kernel<DT, kAligned><<<cut_grid, kThreads, 0, st>>>(a, 0);
     StepArgs full = a;

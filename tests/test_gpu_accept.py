@@ -113,6 +113,15 @@ def test_mixed_samplers(oracle_mod, dev, dtype, V):
     assert _check(g, ref, margin, prm, f"mixed_{dtype}_V{V}", V) > B // 2
 
 
+def test_many_rows(oracle_mod, dev):
+    """2500 rows: the plan splits them over three classifying workgroups."""
+    B, V = 2500, 257
+    t, d, prm = _mixed(zlib.crc32(b"acc_many_rows"), B, V, "f32")
+    g = _gpu(_t(t, "f32", dev), _t(d, "f32", dev), prm, dev)
+    ref, margin = oracle_mod.accept_stats(t, d, prm, dtype="f32")
+    assert _check(g, ref, margin, prm, "many_rows_f32", V) > B // 2
+
+
 def test_one_workgroup_per_unit(oracle_mod, dev):
     """160 nucleus rows (320 units): the cut runs one workgroup per unit."""
     B, V = 160, 8192

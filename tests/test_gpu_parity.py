@@ -366,6 +366,43 @@ def test_invalid_rows(oracle_mod, dev, mode):
     assert (g_tok[1:9] == -1).all()
 
 
+@pytest.mark.parametrize("mode", ["auto", "positions"])
+def test_plan_of_several_workgroups(oracle_mod, dev, mode):
+    """3000 rows (the plan's rows split over three classifying workgroups,
+    each counting the units of the rows before its own): every sampler
+    class, unsupported rows and invalid rows spread over the batch, each
+    row's list position checked through its outcome against the oracle."""
+    rng = np.random.default_rng(61)
+    B, K, V = 3000, 2, 333
+    t = rng.normal(0, 2.0, (B, K + 1, V))
+    d = t[:, :K] * 0.8 + rng.normal(0, 1.2, (B, K, V))
+    prm = np.zeros(B, PARAMS_DTYPE)
+    kind = rng.integers(0, 5, B)
+    for b in range(B):
+        T = float(rng.uniform(0.4, 1.4))
+        prm[b] = [(0.0, 0, 1.0, 0), (T, int(rng.integers(1, 65)), 0.9, 0), (T, 100, 1.0, 0),
+                  (T, 0, 1.0, 0), (T, 0, float(rng.uniform(0.5, 0.99)), 0)][kind[b]]
+    L = rng.integers(0, K + 1, size=B).astype(np.int32)
+    tok = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    bad = rng.choice(B, size=60, replace=False)
+    for i, b in enumerate(bad):  # invalid rows, in every workgroup's share
+        if i % 4 == 0:
+            prm[b]["temperature"] = -1.0
+        elif i % 4 == 1:
+            prm[b]["top_p"] = 0.0
+        elif i % 4 == 2:
+            L[b] = K + 1
+        else:
+            L[b] = K
+            tok[b, K - 1] = V
+    u = rng.random((B, K + 1), dtype=np.float32)
+    wl = workloads.custom(t, d, tok, L, prm, u, dtype="f32", name="plan_3000_rows")
+    rep, g_tok, g_acc = check(oracle_mod, wl, dev, label="plan_3000_rows", step_mode=mode)
+    assert rep.compared + rep.unsupported == B
+    assert (g_acc[bad] == -1).all()
+    assert (g_acc[kind == 2] == -2).sum() == int(((kind == 2) & ~np.isin(np.arange(B), bad)).sum())
+
+
 def test_deterministic(dev):
     wl = workloads.make("mixed_samplers_b1024", batch=128, vocab=30011)
     a = run_gpu(wl, dev)
