@@ -82,8 +82,31 @@ def load() -> ctypes.CDLL:
     return _lib
 
 
+_WS_BYTES = {}
+
+
 def workspace_bytes(batch: int, max_draft: int, vocab: int, dtype: int) -> int:
-    return int(load().sv_workspace_bytes(batch, max_draft, vocab, dtype))
+    key = (batch, max_draft, vocab, dtype)
+    n = _WS_BYTES.get(key)
+    if n is None:
+        n = _WS_BYTES[key] = int(load().sv_workspace_bytes(batch, max_draft, vocab, dtype))
+    return n
+
+
+def _as(t: torch.Tensor, dev, dtype) -> torch.Tensor:
+    """t on dev as a contiguous tensor of dtype, without a copy (or a call
+    into torch) when it already is one."""
+    if t.dtype != dtype or t.device != dev:
+        t = t.to(dev, dtype)
+    return t if t.is_contiguous() else t.contiguous()
+
+
+def _raw_stream(dev) -> int:
+    """Handle of the current stream of device dev."""
+    get = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if get is not None:
+        return get(dev.index if dev.index is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream(dev).cuda_stream
 
 
 SV_STEP_AUTO, SV_STEP_POSITIONS, SV_STEP_DENSE = 0, 1, 2
@@ -120,7 +143,7 @@ def params_tensor(params, device) -> torch.Tensor:
     if isinstance(params, torch.Tensor):
         if params.dtype != torch.int32 or params.dim() != 2 or params.shape[1] != 4:
             raise TypeError("params tensor must be [B, 4] int32")
-        return params.to(device).contiguous()
+        return _as(params, device, torch.int32)
     arr = np.ascontiguousarray(params)
     if arr.dtype.itemsize != 16:
         raise TypeError("params must be 16-byte records")
@@ -171,20 +194,20 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
         draft, ds = _rows_layout(draft, B * K) if K > 0 else (None, 0)
     tok = None
     if K > 0 or draft_tokens is not None:
-        tok = draft_tokens.to(dev, torch.int32).contiguous()
+        tok = _as(draft_tokens, dev, torch.int32)
         if tuple(tok.shape) != (B, K):
             raise ValueError("draft_tokens must be [B, K]")
         if K == 0:
             tok = None
     dl = None
     if draft_len is not None:
-        dl = draft_len.to(dev, torch.int32).contiguous()
+        dl = _as(draft_len, dev, torch.int32)
         if tuple(dl.shape) != (B,):
             raise ValueError("draft_len must be [B]")
     prm = params_tensor(params, dev)
     if prm.shape[0] != B:
         raise ValueError("params must have B rows")
-    uni = uniforms.to(dev, torch.float32).contiguous()
+    uni = _as(uniforms, dev, torch.float32)
     if tuple(uni.shape) != (B, K1):
         raise ValueError("uniforms must be [B, K+1]")
     if out_tokens is None:
@@ -202,8 +225,7 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
     cfg = SvConfig()
     cfg.batch, cfg.max_draft, cfg.vocab, cfg.dtype = B, K, V, code
     cfg.target_row_stride, cfg.draft_row_stride = ts, ds
-    st = stream if stream is not None else torch.cuda.current_stream(dev)
-    cfg.stream = st.cuda_stream
+    cfg.stream = stream.cuda_stream if stream is not None else _raw_stream(dev)
     cfg.workspace = wptr + pad
     cfg.workspace_bytes = workspace.numel() * workspace.element_size() - pad
     cfg.diag = dg.data_ptr() if dg is not None else None
@@ -224,7 +246,7 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
         # until the work enqueued on `stream` has finished
         for t in (target, draft, tok, dl, prm, uni, workspace, out_tokens, out_accept_len, dg):
             if t is not None:
-                t.record_stream(st)
+                t.record_stream(stream)
     return out_tokens, out_accept_len, dg
 
 
@@ -294,8 +316,7 @@ def verify_tree(target: torch.Tensor, draft: torch.Tensor | None, node_tokens: t
     cfg = SvConfig()
     cfg.batch, cfg.max_draft, cfg.vocab, cfg.dtype = B, K, V, code
     cfg.target_row_stride, cfg.draft_row_stride = ts, ds
-    st = stream if stream is not None else torch.cuda.current_stream(dev)
-    cfg.stream = st.cuda_stream
+    cfg.stream = stream.cuda_stream if stream is not None else _raw_stream(dev)
     cfg.workspace = wptr + pad
     cfg.workspace_bytes = workspace.numel() * workspace.element_size() - pad
     cfg.diag = dg.data_ptr() if dg is not None else None
@@ -361,8 +382,7 @@ def sample(logits: torch.Tensor, params, uniforms: torch.Tensor, *, diag: bool =
     cfg = SvConfig()
     cfg.batch, cfg.max_draft, cfg.vocab, cfg.dtype = B, 0, V, code
     cfg.target_row_stride = logits.stride(0)
-    st = stream if stream is not None else torch.cuda.current_stream(dev)
-    cfg.stream = st.cuda_stream
+    cfg.stream = stream.cuda_stream if stream is not None else _raw_stream(dev)
     cfg.workspace = wptr + pad
     cfg.workspace_bytes = workspace.numel() * workspace.element_size() - pad
     cfg.diag = dg.data_ptr() if dg is not None else None
@@ -420,8 +440,7 @@ def accept_stats(target: torch.Tensor, draft: torch.Tensor, params, *,
     cfg = SvConfig()
     cfg.batch, cfg.max_draft, cfg.vocab, cfg.dtype = B, 1, V, code
     cfg.target_row_stride, cfg.draft_row_stride = target.stride(0), draft.stride(0)
-    st = stream if stream is not None else torch.cuda.current_stream(dev)
-    cfg.stream = st.cuda_stream
+    cfg.stream = stream.cuda_stream if stream is not None else _raw_stream(dev)
     cfg.workspace = wptr + pad
     cfg.workspace_bytes = workspace.numel() * workspace.element_size() - pad
     cfg.diag = None
