@@ -63,9 +63,12 @@ def test_noalloc_matches_verify_twice(lib):
     import torch
 
     dev = torch.device("cuda:0")
-    # a large call (every sampler class, nucleus rows included), then a
-    # smaller one of another shape and dtype on the same scratch
+    # a large call (every sampler class, nucleus rows included), then smaller
+    # ones of other shapes on the same scratch: 1500 short rows (the plan's
+    # rows over several workgroups, one unit per wave in the row pass), and
+    # a small bf16 batch
     cases = [workloads.make("mixed_samplers_b1024", batch=256, vocab=60013),
+             workloads.make("tiny_v1000", batch=1500),
              workloads.make("mixed_greedy_b64", batch=24, vocab=20011)]
     for wl in cases:
         print(f"[gpu] noalloc {wl.name} B={wl.B} K={wl.K} V={wl.V} {wl.dtype}", flush=True)
