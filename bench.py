@@ -457,6 +457,146 @@ EXTRAS = [
 ]
 
 
+def _timed(fn, steps, warmup):
+    """Mean ms per call of fn over `steps` calls after `warmup`, torch events
+    on the current stream around the timed calls."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def _op_line(args, metric, value, ms, dtype, config, alg_bytes, kernel_note):
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    return {
+        "metric": metric, "value": round(value, 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic", "config": config,
+        "roofline": {"bound": "hbm", "kernel": kernel_note, "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "alg_bytes_per_call": int(alg_bytes)},
+    }
+
+
+def bench_sample(args, wl, dev):
+    """The plain sampler (sv_sample) over position 0's target rows of a
+    recipe: one draw per row from its truncated distribution.  Algorithmic
+    bytes: each row read once (the draw's second pass over a full-vocabulary
+    row is not counted)."""
+    import torch
+
+    import rejection_sampling_verify_sv_amd as sv
+    from rejection_sampling_verify_sv_amd import workloads
+
+    B, V = wl.B, wl.V
+    t, _, _, _, prm, uni = workloads.to_torch(wl, dev)
+    rows, u = t[:, 0, :], uni[:, 0].contiguous()
+    out = sv.sample(rows, prm, u)
+    code = sv.SV_F32 if wl.dtype == "f32" else sv.SV_BF16
+    ws = torch.empty(sv.workspace_bytes(B, 0, V, code) + 256, dtype=torch.uint8, device=dev)
+    ms = _timed(lambda: sv.sample(rows, prm, u, out_tokens=out[0], out_status=out[1],
+                                  workspace=ws), args.steps, args.warmup)
+    line = _op_line(args, "sampled rows/s, V=%d" % V, B / (ms * 1e-3), ms,
+                    "f32" if wl.dtype == "f32" else "bf16",
+                    {"workload": args.workload + " position 0 targets", "vocab": V, "batch": B,
+                     "logits": wl.dtype},
+                    B * V * wl.elem_size, "whole call (sv_sample)")
+    g_tok = out[0].cpu().numpy()
+    if not args.no_cpu_baseline:
+        import oracle
+
+        oracle.build(force=False)
+        sel = np.arange(0, B, 16)
+        tc = time.perf_counter()
+        ref, _, _ = oracle.sample(wl.target[sel, 0], wl.params[sel], wl.uniforms[sel, 0],
+                                  dtype=wl.dtype, nthreads=1)
+        dt = time.perf_counter() - tc
+        line["cpu_baseline"] = {"value": round(len(sel) / dt, 2), "unit": "rows/s", "cores": 1,
+                                "kind": "oracle",
+                                "sample": f"{len(sel)} rows (every 16th), one thread, {dt:.2f} s"}
+        line["oracle_agreement"] = {"rows": int(len(sel)),
+                                    "identical_tokens": int((ref == g_tok[sel]).sum())}
+    print(json.dumps(line), flush=True)
+
+
+def bench_tree(args, dev):
+    """The tree / multi-candidate verify (sv_verify_tree) on the tree recipe:
+    256 rows, a Medusa-shaped tree of 12 candidates each.  Algorithmic bytes:
+    each needed row read once, i.e. the target row of every node the walk
+    reaches, and the draft row of every reached node with children on a
+    sampling row."""
+    import torch
+
+    import rejection_sampling_verify_sv_amd as sv
+    from rejection_sampling_verify_sv_amd import workloads
+
+    log("[bench] generating the tree recipe")
+    wl, par = workloads.make_tree()
+    B, K, V = wl.B, wl.K, wl.V
+    t, d, tok, nc, prm, uni = workloads.to_torch(wl, dev)
+    par_t = torch.from_numpy(np.ascontiguousarray(par)).to(dev)
+    depth = np.zeros(K + 1, np.int64)
+    for c in range(1, K + 1):
+        depth[c] = depth[par[0, c - 1]] + 1
+    max_depth = int(depth.max())
+    max_kids = int(np.bincount(par[0], minlength=K + 1).max())
+    out = sv.verify_tree(t, d, tok, par_t, nc, prm, uni, max_depth=max_depth,
+                         max_children=max_kids)
+    code = sv.SV_F32 if wl.dtype == "f32" else sv.SV_BF16
+    ws = torch.empty(sv.workspace_bytes(B, K, V, code) + 256, dtype=torch.uint8, device=dev)
+    ms = _timed(lambda: sv.verify_tree(t, d, tok, par_t, nc, prm, uni, max_depth=max_depth,
+                                       max_children=max_kids, workspace=ws, out_tokens=out[0],
+                                       out_accept_len=out[1], out_path=out[2]),
+                args.steps, args.warmup)
+    g_tok, g_len, g_path = (x.cpu().numpy() for x in out[:3])
+    has_kids = np.bincount(par[0], minlength=K + 1) > 0
+    greedy = wl.params["temperature"] == 0
+    n_tgt = n_drf = 0
+    for b in range(B):
+        if g_len[b] < 0:
+            continue
+        nodes = [0] + [int(v) for v in g_path[b, :g_len[b]]]
+        n_tgt += len(nodes)
+        if not greedy[b]:
+            n_drf += sum(1 for v in nodes if v < K and has_kids[v])
+    alg = (n_tgt + n_drf) * V * wl.elem_size
+    line = _op_line(args, "tree-verified rows/s, V=%d" % V, B / (ms * 1e-3), ms,
+                    "f32" if wl.dtype == "f32" else "bf16",
+                    {"workload": wl.name, "vocab": V, "batch": B, "candidates": K,
+                     "tree": "medusa 3-2-1", "logits": wl.dtype, "max_depth": max_depth,
+                     "max_children": max_kids},
+                    alg, "whole call (sv_verify_tree)")
+    line["mean_accepted"] = round(float(g_len[g_len >= 0].mean()), 3)
+    line["rows_read"] = {"target": int(n_tgt), "draft": int(n_drf)}
+    if not args.no_cpu_baseline:
+        import oracle
+
+        oracle.build(force=False)
+        sel = np.arange(0, B, 16)
+        tc = time.perf_counter()
+        r_tok, r_len, r_path, _, used = oracle.verify_tree(
+            wl.target[sel], wl.draft[sel], wl.tokens[sel], par[sel], wl.draft_len[sel],
+            wl.params[sel], wl.uniforms[sel], dtype=wl.dtype, nthreads=1)
+        dt = time.perf_counter() - tc
+        line["cpu_baseline"] = {"value": round(len(sel) / dt, 2), "unit": "rows/s",
+                                "cores": int(used), "kind": "oracle",
+                                "sample": f"{len(sel)} rows (every 16th), one thread, {dt:.2f} s"}
+        same = (r_len == g_len[sel]) & (r_tok == g_tok[sel]).all(axis=1)
+        line["oracle_agreement"] = {"rows": int(len(sel)), "identical": int(same.sum())}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -467,7 +607,7 @@ def main():
                     help="copies of the headline inputs to rotate over")
     ap.add_argument("--no-extras", action="store_true", help="measure the headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", default="verify", choices=["verify", "accept_stats"])
+    ap.add_argument("--op", default="verify", choices=["verify", "accept_stats", "sample", "tree"])
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the measurement, run 5 device-to-device copies of MIB MiB "
                          "(the reference kernel for scaling HBM counters)")
@@ -485,10 +625,16 @@ def main():
 
     dev = torch.device("cuda:0")
     sv.load()
+    if args.op == "tree":
+        bench_tree(args, dev)
+        return
     log(f"[bench] generating {args.workload}")
     wl = workloads.make(args.workload)
     if args.op == "accept_stats":
         bench_accept_stats(args, wl, dev)
+        return
+    if args.op == "sample":
+        bench_sample(args, wl, dev)
         return
     log("[bench] streaming-read ceiling")
     ceil = read_ceiling(dev)

@@ -334,7 +334,7 @@ def verify_tree(target: torch.Tensor, draft: torch.Tensor | None, node_tokens: t
         for t in (target, draft, tok, par, nc, prm, uni, workspace, out_tokens, out_accept_len,
                   out_path, dg):
             if t is not None:
-                t.record_stream(st)
+                t.record_stream(stream)
     return out_tokens, out_accept_len, out_path, dg
 
 
@@ -394,7 +394,7 @@ def sample(logits: torch.Tensor, params, uniforms: torch.Tensor, *, diag: bool =
     if stream is not None:
         for t in (logits, prm, uni, workspace, out_tokens, out_status, dg):
             if t is not None:
-                t.record_stream(st)
+                t.record_stream(stream)
     return out_tokens, out_status, dg
 
 
@@ -451,5 +451,5 @@ def accept_stats(target: torch.Tensor, draft: torch.Tensor, params, *,
                            f"{lib.sv_strerror(rc).decode()}")
     if stream is not None:
         for t in (target, draft, prm, workspace, out):
-            t.record_stream(st)
+            t.record_stream(stream)
     return out

@@ -23,6 +23,13 @@ Recipes (the pages print no dataset; these stand in for model logits):
   per-row rho ~ U[0.5, 0.95].  Per row T in {0, 0.6, 1.0}, top_k in
   {0, 20, 50}, top_p in {0.8, 0.95, 1.0}, each drawn independently.
 
+Tree recipe (``make_tree``, for the tree / multi-candidate verify): the
+mixed-sampler recipe over the nodes of a candidate tree, B=256, V=151936,
+bf16, a Medusa-shaped tree of 12 candidates (3 children at the root, 2 under
+each of them, then 1 under each of those) per row: node v's target row is
+the target after v's path and its draft row the draft there (rho per row as
+above), and candidate c's token is drawn from q at its parent's draft row.
+
 Zipf recipe: t_i = log Zipf_{s=1.1}(rank_i) + N(0, 0.5^2) with a fresh random
 permutation of the ranks for every (row, position); the draft of a Zipf
 workload mixes the target with an independent copy of the same recipe,
@@ -300,6 +307,53 @@ def make(name: str, *, batch: int | None = None, poison: bool = False,
     else:
         raise KeyError(name)
     return _finish(name, V, B, K, dtype, t32, d32, draft_len, params, seeds, rngs, poison)
+
+
+def tree_parents(K: int, shape: str = "medusa") -> np.ndarray:
+    """Parents of candidates 1..K: "medusa" (3 at the root, 2 under each of
+    them, then 1 under each of those; K <= 12), "wide" (all at the root) or
+    "path" (a chain)."""
+    if shape == "path":
+        return np.arange(K, dtype=np.int32)
+    if shape == "wide":
+        return np.zeros(K, np.int32)
+    if shape != "medusa" or K > 12:
+        raise ValueError(shape)
+    par = [0 if c <= 3 else ((c - 4) // 2 + 1 if c <= 9 else c - 6) for c in range(1, K + 1)]
+    return np.array(par, np.int32)
+
+
+def make_tree(*, batch: int = 256, vocab: int = 151936, K: int = 12, shape: str = "medusa",
+              dtype: str = "bf16"):
+    """The tree recipe (see the module docstring): (Workload, parents [B, K])
+    for sv_verify_tree, every row offering all K candidates."""
+    B, V = batch, vocab
+    seeds = np.random.SeedSequence(20261202 + 6).spawn(4)
+    rngs = [np.random.Generator(np.random.PCG64(s)) for s in seeds]
+    g_par = rngs[3]
+    base = _zipf_base(V)
+    s_t, s_d = seeds[0].spawn(2)
+    t32 = _zipf_rows(s_t, base, B * (K + 1)).reshape(B, K + 1, V)
+    d32 = _zipf_rows(s_d, base, B * K).reshape(B, K, V)
+    rho = g_par.uniform(0.5, 0.95, size=B).astype(np.float32)
+    d32 *= (1 - rho)[:, None, None]
+    d32 += rho[:, None, None] * t32[:, :K]
+    params = _params(B, 0.0, 0, 1.0)
+    params["temperature"] = g_par.choice(np.array([0.0, 0.6, 1.0], np.float32), B)
+    params["top_k"] = g_par.choice(np.array([0, 20, 50], np.int32), B)
+    params["top_p"] = g_par.choice(np.array([0.8, 0.95, 1.0], np.float32), B)
+    par = np.tile(tree_parents(K, shape), (B, 1))
+    # candidate c is drawn at its parent: the chain generator over the
+    # parents' draft rows gives each candidate a draw from q there
+    tok = _draft_tokens(seeds[1], d32[:, par[0]], params, np.full(B, K, np.int32))
+    uniforms = rngs[2].random((B, K + 1), dtype=np.float32)
+    if dtype == "bf16":
+        target, draft = f32_to_bf16_bits(t32), f32_to_bf16_bits(d32)
+    else:
+        target, draft = t32, d32
+    wl = Workload(f"tree_{shape}_b{B}", V, B, K, dtype, target, draft, tok,
+                  np.full(B, K, np.int32), params, uniforms)
+    return wl, par
 
 
 def custom(target_f32: np.ndarray, draft_f32: np.ndarray, tokens, draft_len, params,

@@ -480,6 +480,34 @@ def test_side_stream(dev):
         assert np.array_equal(x, y, equal_nan=True)
 
 
+def test_side_stream_other_entry_points(dev):
+    """The sampler, the tree verify and the acceptance statistics on a side
+    stream give what they give on the current one."""
+    import torch
+
+    import rejection_sampling_verify_sv_amd as sv
+
+    wl, par = workloads.make_tree(batch=24, vocab=4099, K=6, shape="wide", dtype="f32")
+    ins = workloads.to_torch(wl, dev)
+    t, d, tok, nc, prm, uni = ins
+    par_t = torch.from_numpy(np.ascontiguousarray(par)).to(dev)
+    runs = [
+        lambda **kw: sv.sample(t[:, 0, :], prm, uni[:, 0], diag=True, **kw),
+        lambda **kw: sv.verify_tree(t, d, tok, par_t, nc, prm, uni, max_depth=1, max_children=6,
+                                    diag=True, **kw),
+        lambda **kw: (sv.accept_stats(t[:, 0, :], d[:, 0, :], prm, **kw),),
+    ]
+    for run in runs:
+        ref = [x.cpu().numpy() for x in run() if x is not None]
+        s = torch.cuda.Stream(device=dev)  # default priority
+        s.wait_stream(torch.cuda.current_stream(dev))
+        out = run(stream=s)
+        s.synchronize()
+        got = [x.cpu().numpy() for x in out if x is not None]
+        for x, y in zip(ref, got):
+            assert np.array_equal(x, y, equal_nan=True)
+
+
 @pytest.mark.parametrize("mode", ["positions", "dense"])
 def test_top_k_above_limit_unsupported(oracle_mod, dev, mode):
     import rejection_sampling_verify_sv_amd as sv
