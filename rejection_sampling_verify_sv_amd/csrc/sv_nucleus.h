@@ -330,6 +330,7 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
     using TS = TileShape<DT>;
     static_assert(TS::kE <= 32, "hit mask is 32 bits");
     constexpr int kOwn = 4;  // boundary tokens a thread ranks per pass
+    constexpr int kSortSel = 512;  // above: the boundary sub-bucket is ranked by a sort
     constexpr int kRing = DT == SV_BF16 ? 3 : 4;  // tiles in flight while collecting a slice
     constexpr int kWaveCap = kCollectCap / kWaves;  // boundary keys a wave can hold
     static_assert(kNW <= kCollectCap && kBins <= kCollectCap && kBins + kThreads <= kCollectCap,
@@ -622,7 +623,110 @@ __global__ __launch_bounds__(kThreads) void cut_decide_kernel(StepArgs a, int k)
         __syncthreads();
         const int nsel = s_nsel;
         const uint64_t before = s_before;
-        for (int base = 0; base < nsel; base += kThreads * kOwn) {
+        // Many tokens in the boundary sub-bucket: rounded logits (bf16) put
+        // every token of one value there, and counting, for each token, the
+        // mass of those ranked ahead of it costs nsel^2.
+        bool one_value = false;
+        if (nsel > kSortSel) {
+            // all of one logit?  (the high halves of their keys)
+            uint64_t hi = 0ull, nlo = 0ull;
+            for (int i = threadIdx.x; i < nsel; i += kThreads) {
+                const uint64_t h = s_key[s_sel[i]] >> 32;
+                hi = h > hi ? h : hi;
+                nlo = (~h & 0xFFFFFFFFull) > nlo ? (~h & 0xFFFFFFFFull) : nlo;
+            }
+            hi = block_max_u64(hi, s_red);    // barriers
+            nlo = block_max_u64(nlo, s_red);  // barriers
+            one_value = hi == (~nlo & 0xFFFFFFFFull);
+        }
+        if (one_value) {
+            // One value, one weight w: the token of rank r (ascending id)
+            // has r w ahead of it, so the kept ones are the m smallest ids
+            // with m the count of r where A + sc (before + r w) < target
+            // (the per-token test, monotone in r), and tau is the key of the
+            // m-th smallest id, found by a radix select over the ids.
+            const uint64_t key0 = s_key[s_sel[0]];
+            const float l0 = key_logit(key0);
+            const float t0 = nuc_t(l0, la, cb);
+            const uint64_t w = nuc_wrel(t0 - floorf(t0));
+            if (threadIdx.x == 0) {
+                int lo = 0, hi = nsel;  // kept(r) holds for r < m
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (A + sc * (double)(before + (uint64_t)mid * w) < target)
+                        lo = mid + 1;
+                    else
+                        hi = mid;
+                }
+                s_nsel = lo;  // m (>= 1: the sub-bucket's first token qualifies)
+            }
+            __syncthreads();
+            const int m = s_nsel;
+            // the (m - 1)-th smallest id, 8 bits at a time from the top (none
+            // kept, m = 0, leaves tau and the kept mass as they are)
+            uint32_t prefix = 0u;
+            int rank = m - 1;
+            uint32_t* const s_cnt = reinterpret_cast<uint32_t*>(s_sub);  // kSub words, free now
+            for (int shift = 24; m > 0 && shift >= 0; shift -= 8) {
+                s_cnt[threadIdx.x] = 0u;
+                __syncthreads();
+                const uint32_t mask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+                for (int i = threadIdx.x; i < nsel; i += kThreads) {
+                    const uint32_t id = key_id(s_key[s_sel[i]]);
+                    if ((id & mask) == prefix) atomicAdd(&s_cnt[(id >> shift) & 0xFFu], 1u);
+                }
+                __syncthreads();
+                uint64_t tot;
+                const uint64_t c = s_cnt[threadIdx.x];
+                const uint64_t ex = block_exclusive_scan(c, s_tmp, &tot);  // barriers
+                if ((uint64_t)rank >= ex && (uint64_t)rank < ex + c) {
+                    s_star = (int)threadIdx.x;
+                    s_before = ex;
+                }
+                __syncthreads();
+                prefix |= (uint32_t)s_star << shift;
+                rank -= (int)s_before;
+                __syncthreads();
+            }
+            if (threadIdx.x == 0 && m > 0) {
+                s_tau = make_key(l0, prefix);
+                s_kept = (unsigned long long)m * w;
+            }
+        } else if (nsel > kSortSel) {
+            // Sorted (descending keys) instead, the mass ahead of a token is
+            // the prefix before it: the same integers, so the same cut.
+            int np = kThreads;
+            while (np < nsel) np <<= 1;  // <= kCollectCap: nsel <= n
+            for (int i = threadIdx.x; i < np; i += kThreads)
+                s_h[i] = i < nsel ? s_key[s_sel[i]] : 0ull;  // key 0: below every token
+            __syncthreads();
+            block_sort_desc(s_h, np);  // barriers
+            // a token's weight, as the sub-buckets above computed it
+            auto wkey = [&](uint64_t key) __attribute__((always_inline)) {
+                const float t = nuc_t(key_logit(key), la, cb);
+                return nuc_wrel(t - floorf(t));
+            };
+            constexpr int kPerT = kCollectCap / kThreads;
+            const int per = np / kThreads, i0 = (int)threadIdx.x * per;
+            uint64_t mine = 0ull;
+#pragma unroll
+            for (int q = 0; q < kPerT; q++)
+                if (q < per && i0 + q < nsel) mine += wkey(s_h[i0 + q]);
+            uint64_t tot;
+            uint64_t pre = before + block_exclusive_scan(mine, s_tmp, &tot);  // barriers
+#pragma unroll
+            for (int q = 0; q < kPerT; q++) {
+                if (q < per && i0 + q < nsel) {
+                    const uint64_t key = s_h[i0 + q], w = wkey(key);
+                    if (A + sc * (double)pre < target) {
+                        atomicMin(&s_tau, (unsigned long long)key);
+                        atomicAdd(&s_kept, (unsigned long long)w);
+                    }
+                    pre += w;
+                }
+            }
+        }
+        for (int base = 0; nsel <= kSortSel && base < nsel; base += kThreads * kOwn) {
             uint64_t key[kOwn], pre[kOwn];
 #pragma unroll
             for (int q = 0; q < kOwn; q++) {

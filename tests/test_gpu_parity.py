@@ -403,6 +403,41 @@ def test_plan_of_several_workgroups(oracle_mod, dev, mode):
     assert (g_acc[kind == 2] == -2).sum() == int(((kind == 2) & ~np.isin(np.arange(B), bad)).sum())
 
 
+@pytest.mark.parametrize("case", ["bf16_zipf", "f32_grid_jitter"])
+def test_boundary_sub_bucket_crowded(oracle_mod, dev, case):
+    """Nucleus rows whose boundary sub-bucket holds hundreds to thousands of
+    tokens: of one rounded value (bf16 Zipf rows; the cut ranks them by a
+    radix select over their ids), or of many nearly equal values (fp32
+    logits on a grid of 1/4 plus a jitter of 1e-6; ranked by a sort)."""
+    rng = np.random.default_rng(zlib.crc32(case.encode()))
+    B, K = 40, 2
+    if case == "bf16_zipf":
+        wl0 = workloads.make("mixed_samplers_b1024", batch=B)
+        t, d = wl0.target[:, :K + 1], wl0.draft[:, :K]
+        dtype = "bf16"
+    else:
+        V = 30011
+        t = np.round(rng.normal(0, 1.0, (B, K + 1, V)) * 4) / 4
+        d = np.round((0.8 * t[:, :K] + rng.normal(0, 0.6, (B, K, V))) * 4) / 4
+        t = t + rng.uniform(0, 1e-6, t.shape)
+        d = d + rng.uniform(0, 1e-6, d.shape)
+        dtype = "f32"
+    V = t.shape[-1]
+    prm = np.zeros(B, PARAMS_DTYPE)
+    for b in range(B):
+        prm[b] = (float(rng.choice([0.6, 1.0, 1.3])), 0, float(rng.choice([0.8, 0.9, 0.95])), 0)
+    tok = np.zeros((B, K), np.int32)
+    for b in range(B):
+        for k in range(K):
+            tok[b, k] = int(np.argmax(d[b, k] / prm["temperature"][b] + rng.gumbel(size=V)))
+    u = rng.random((B, K + 1), dtype=np.float32)
+    wl = workloads.custom(t, d, tok, np.full(B, K, np.int32), prm, u, dtype=dtype,
+                          name=f"crowded_{case}")
+    for mode in ("auto", "positions"):
+        rep, _, _ = check(oracle_mod, wl, dev, label=wl.name, step_mode=mode)
+        assert rep.compared == B and rep.error_rows == 0
+
+
 def test_deterministic(dev):
     wl = workloads.make("mixed_samplers_b1024", batch=128, vocab=30011)
     a = run_gpu(wl, dev)
