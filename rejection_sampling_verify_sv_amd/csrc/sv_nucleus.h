@@ -148,13 +148,21 @@ __device__ void resolve_wide(const void* row, int64_t V, FnUnit* fu, float la, f
         __syncthreads();
         stream_range<DT, kAligned>(row, 0, V, [&](float (&v)[TS::kE], int64_t t0, bool)
                                                   __attribute__((always_inline)) {
+            // the bucket's logits first, as one bit mask per lane (its keys
+            // form [lo, hi] inside them): keys are built for those tokens only
+            uint32_t bits = 0u;
 #pragma unroll
-            for (int i = 0; i < TS::kE; i++) {
-                const uint64_t key = make_key(v[i], (uint32_t)elem_id<DT>(t0, i));
+            for (int i = TS::kE - 1; i >= 0; i--)
+                bits = (bits << 1) | ((v[i] >= l_lo && v[i] <= l_hi) ? 1u : 0u);
+            while (bits != 0u) {
+                const int i = __builtin_ctz(bits);
+                bits &= bits - 1u;
+                const float vi = pick_elem(v, i);
+                const uint64_t key = make_key(vi, (uint32_t)elem_id<DT>(t0, i));
                 if (key >= rlo && key <= rhi) {  // in the bucket (its keys form [lo, hi])
                     const int bin = (int)((key - rlo) >> s);
                     int bk;
-                    const uint64_t w = nuc_wfix_t(nuc_t(v[i], la, cb), &bk);
+                    const uint64_t w = nuc_wfix_t(nuc_t(vi, la, cb), &bk);
                     atomicAdd((unsigned long long*)&s_mass[bin], (unsigned long long)w);
                     atomicAdd(&s_cnt[bin], 1u);
                 }
@@ -210,15 +218,21 @@ __device__ void resolve_wide(const void* row, int64_t V, FnUnit* fu, float la, f
     __syncthreads();
     stream_range<DT, kAligned>(row, 0, V, [&](float (&v)[TS::kE], int64_t t0, bool)
                                               __attribute__((always_inline)) {
+        uint32_t bits = 0u;
 #pragma unroll
-        for (int i = 0; i < TS::kE; i++) {
-            const uint64_t key = make_key(v[i], (uint32_t)elem_id<DT>(t0, i));
+        for (int i = TS::kE - 1; i >= 0; i--)
+            bits = (bits << 1) | ((v[i] >= l_lo && v[i] <= l_hi) ? 1u : 0u);
+        while (bits != 0u) {
+            const int i = __builtin_ctz(bits);
+            bits &= bits - 1u;
+            const float vi = pick_elem(v, i);
+            const uint64_t key = make_key(vi, (uint32_t)elem_id<DT>(t0, i));
             if (key >= rlo && key <= rhi) {
                 const int slot = atomicAdd(&s_n, 1);
                 if (slot < kThreads) {
                     int bk;
                     s_key[slot] = key;
-                    s_w[slot] = nuc_wfix_t(nuc_t(v[i], la, cb), &bk);
+                    s_w[slot] = nuc_wfix_t(nuc_t(vi, la, cb), &bk);
                 }
             }
         }
