@@ -511,8 +511,16 @@ def test_side_stream(dev):
     _say("[gpu] verify on a side stream")
     tok, acc, dg = sv.verify(*ins, diag=True, stream=s)
     s.synchronize()
-    for x, y in zip(ref, (tok.cpu().numpy(), acc.cpu().numpy(), dg.cpu().numpy())):
-        assert np.array_equal(x, y, equal_nan=True)
+    got = (tok.cpu().numpy(), acc.cpu().numpy(), dg.cpu().numpy())
+    for x, y in zip(ref, got):
+        if not np.array_equal(x, y, equal_nan=True):
+            same = (x == y) | (np.isnan(x) & np.isnan(y)) if x.dtype.kind == "f" else x == y
+            rows = np.unique(np.nonzero(~same.reshape(len(x), -1))[0])
+            detail = [(int(b), ref[0][b].tolist(), int(ref[1][b]), got[0][b].tolist(), int(got[1][b]),
+                       wl.params[b].tolist(), int(wl.draft_len[b])) for b in rows[:6]]
+            raise AssertionError(f"current and side stream differ in rows {rows.tolist()}: "
+                                 f"(row, tokens, accept length on the current stream, on the side "
+                                 f"stream, params, draft length) {detail}")
 
 
 def test_side_stream_other_entry_points(dev):
