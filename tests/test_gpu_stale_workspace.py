@@ -144,3 +144,28 @@ def test_sample_on_a_stale_workspace(dev):
     _same(run(wl, ws), fresh, "sample first run")
     _same(run(other, ws), fresh_o, "sample rolled batch")
     _same(run(wl, ws), fresh, "sample first batch again")
+
+
+def test_accept_stats_on_a_stale_workspace(dev):
+    import torch
+
+    import rejection_sampling_verify_sv_amd as sv
+
+    wl = workloads.make("mixed_samplers_b1024", batch=150, vocab=20011)
+    other = _rolled(wl, 11)
+    code = sv.SV_F32 if wl.dtype == "f32" else sv.SV_BF16
+    need = sv.workspace_bytes(wl.B, 1, wl.V, code) + 256
+
+    def run(w, ws):
+        t, d, _, _, prm, _ = workloads.to_torch(w, dev)
+        out = sv.accept_stats(t[:, 0], d[:, 0], prm, workspace=ws)
+        torch.cuda.synchronize()
+        return (out.cpu().numpy(),)
+
+    _say(f"[gpu] stale workspace: accept_stats B={wl.B} V={wl.V}")
+    fresh = run(wl, torch.zeros(need, dtype=torch.uint8, device=dev))
+    fresh_o = run(other, torch.zeros(need, dtype=torch.uint8, device=dev))
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    _same(run(wl, ws), fresh, "accept_stats first run")
+    _same(run(other, ws), fresh_o, "accept_stats rolled batch")
+    _same(run(wl, ws), fresh, "accept_stats first batch again")
